@@ -1,0 +1,448 @@
+/*
+ * kvc_oracle.c -- plain, single-threaded CPU oracle for KV-cache token scoring,
+ * eviction/compaction and hybrid low-rank compression.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Only the test suite, the smoke check and the
+ * CPU-baseline leg of the benchmark may load this library.  The product path
+ * (the HIP library) shares no source, header, table or helper with this file.
+ *
+ * Conventions
+ *   - Every floating-point quantity is carried in double precision.  bf16
+ *     inputs are widened exactly (a bf16 value is the top half of an IEEE
+ *     binary32), fp32 inputs are widened exactly.  Nothing is rounded inside;
+ *     the caller decides whether and where to round to fp32.
+ *   - Tensors are dense row-major.  A "slice" is one (layer, batch, kv head);
+ *     per-token tensors of a slice are [S][D] with a slice stride of
+ *     `s_stride` tokens (s_stride >= S).
+ *   - Return value: 0 on success, a negative number on invalid arguments or a
+ *     non-finite input (the pages define nothing for NaN or Inf).
+ *
+ * Sources (pages the method is described on):
+ *   [MKV]  "ManifoldKV: Training-Free KV Cache Compression via Euclidean
+ *          Outlier Detection" (ICML 2026 poster page), abstract and lay summary.
+ *   [OJA]  "OjaKV: Context-Aware Online Low-Rank KV Cache Compression"
+ *          (papercache deep-notes page): the "how it works" display equations
+ *          for e_t and the Oja rule, "background / low-rank attention",
+ *          "method details", and appendix A.1 (Algorithm 1), A.4, A.9.
+ *
+ * Parity status: every function here is pinned by CPU tests against closed
+ * forms, invariants, exact-rational brute force or a library routine, except
+ * the decode-time re-projection reading used by the full-loop driver, which
+ * lives in the Python wrapper and is marked "parity unpinned" there.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORA_OK 0
+#define ORA_EINVAL (-1)
+#define ORA_ENONFINITE (-2)
+#define ORA_ENOMEM (-3)
+
+/* ---------------------------------------------------------------- codecs */
+
+/* bf16 is the upper 16 bits of an IEEE-754 binary32; widening is exact. */
+static double bf16_to_double(uint16_t h) {
+    uint32_t bits = ((uint32_t)h) << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return (double)f;
+}
+
+double ora_bf16_to_f64(uint16_t h) { return bf16_to_double(h); }
+
+/* ------------------------------------------------------- ManifoldKV score */
+
+/* Mean of keys t in [t0, t1) of one slice, per channel ([MKV] "the key
+ * centroid").  Plain summation in double, then one division. */
+static void centroid_range(const uint16_t *Kslice, int64_t D, int64_t t0, int64_t t1,
+                           double *mu) {
+    for (int64_t c = 0; c < D; ++c) mu[c] = 0.0;
+    for (int64_t t = t0; t < t1; ++t)
+        for (int64_t c = 0; c < D; ++c) mu[c] += bf16_to_double(Kslice[t * D + c]);
+    double n = (double)(t1 - t0);
+    for (int64_t c = 0; c < D; ++c) mu[c] /= n;
+}
+
+/* Euclidean distance of key t to a centroid ([MKV] "Euclidean distance to the
+ * key centroid", capturing angular and radial deviation). */
+static double l2_distance(const uint16_t *krow, const double *mu, int64_t D) {
+    double acc = 0.0;
+    for (int64_t c = 0; c < D; ++c) {
+        double diff = bf16_to_double(krow[c]) - mu[c];
+        acc += diff * diff;
+    }
+    return sqrt(acc);
+}
+
+static int all_finite_bf16(const uint16_t *x, int64_t n) {
+    for (int64_t i = 0; i < n; ++i)
+        if ((x[i] & 0x7f80u) == 0x7f80u) return 0;
+    return 1;
+}
+
+/* WindowedManifoldKV ([MKV] abstract): each key is scored against the centroid
+ * of its own contiguous window [jW, min((j+1)W, S)).  The last window may be
+ * short; its mean is over the keys it actually holds.  W >= S is the global
+ * scorer.  scores: [G][S]; centroids (nullable): [G][ceil(S/W)][D]. */
+int ora_score_l2_windowed(const uint16_t *K, int64_t G, int64_t S, int64_t D, int64_t W,
+                          double *scores, double *centroids) {
+    if (G < 0 || S < 0 || D <= 0 || W <= 0 || (S > 0 && G > 0 && (!K || !scores)))
+        return ORA_EINVAL;
+    if (!all_finite_bf16(K, G * S * D)) return ORA_ENONFINITE;
+    int64_t nwin = (S + W - 1) / W;
+    double *mu = (double *)malloc(sizeof(double) * (size_t)D);
+    if (!mu) return ORA_ENOMEM;
+    for (int64_t g = 0; g < G; ++g) {
+        const uint16_t *Kg = K + g * S * D;
+        for (int64_t j = 0; j < nwin; ++j) {
+            int64_t t0 = j * W;
+            int64_t t1 = t0 + W < S ? t0 + W : S;
+            centroid_range(Kg, D, t0, t1, mu);
+            if (centroids) memcpy(centroids + (g * nwin + j) * D, mu, sizeof(double) * (size_t)D);
+            for (int64_t t = t0; t < t1; ++t) scores[g * S + t] = l2_distance(Kg + t * D, mu, D);
+        }
+    }
+    free(mu);
+    return ORA_OK;
+}
+
+/* Global ManifoldKV score: one centroid over all S keys of the slice. */
+int ora_score_l2(const uint16_t *K, int64_t G, int64_t S, int64_t D, double *scores,
+                 double *centroid) {
+    if (G < 0 || S < 0 || D <= 0 || (S > 0 && G > 0 && (!K || !scores))) return ORA_EINVAL;
+    if (!all_finite_bf16(K, G * S * D)) return ORA_ENONFINITE;
+    double *mu = (double *)malloc(sizeof(double) * (size_t)D);
+    if (!mu) return ORA_ENOMEM;
+    for (int64_t g = 0; g < G; ++g) {
+        const uint16_t *Kg = K + g * S * D;
+        if (S > 0) {
+            centroid_range(Kg, D, 0, S, mu);
+        } else {
+            for (int64_t c = 0; c < D; ++c) mu[c] = 0.0; /* no keys: no centroid */
+        }
+        if (centroid) memcpy(centroid + g * D, mu, sizeof(double) * (size_t)D);
+        for (int64_t t = 0; t < S; ++t) scores[g * S + t] = l2_distance(Kg + t * D, mu, D);
+    }
+    free(mu);
+    return ORA_OK;
+}
+
+/* --------------------------------------------------------------- top-k */
+
+typedef struct {
+    float value;
+    int32_t index;
+} scored_t;
+
+/* Order for retention: larger score first; equal scores -> lower index first.
+ * +0.0 and -0.0 compare equal, as they do in IEEE arithmetic. */
+static int cmp_retain(const void *a, const void *b) {
+    const scored_t *x = (const scored_t *)a, *y = (const scored_t *)b;
+    if (x->value > y->value) return -1;
+    if (x->value < y->value) return 1;
+    return (x->index > y->index) - (x->index < y->index);
+}
+
+static int cmp_int32(const void *a, const void *b) {
+    int32_t x = *(const int32_t *)a, y = *(const int32_t *)b;
+    return (x > y) - (x < y);
+}
+
+/* Keep the k largest scores of each slice ([MKV]: keys far from the centroid
+ * are the ones retained; [OJA] method details: the top-k error scores become
+ * full-rank anchors).  Output: [G][k] indices in ascending (temporal) order.
+ * The decision is taken on the fp32 scores given. */
+int ora_topk(const float *scores, int64_t G, int64_t S, int64_t s_stride, int64_t k,
+             int32_t *idx) {
+    if (G < 0 || S < 0 || k < 0 || k > S || s_stride < S || S > INT32_MAX) return ORA_EINVAL;
+    if (G == 0 || k == 0) return ORA_OK;
+    scored_t *buf = (scored_t *)malloc(sizeof(scored_t) * (size_t)S);
+    if (!buf) return ORA_ENOMEM;
+    for (int64_t g = 0; g < G; ++g) {
+        for (int64_t t = 0; t < S; ++t) {
+            float v = scores[g * s_stride + t];
+            if (!isfinite(v)) {
+                free(buf);
+                return ORA_ENONFINITE;
+            }
+            buf[t].value = v;
+            buf[t].index = (int32_t)t;
+        }
+        qsort(buf, (size_t)S, sizeof(scored_t), cmp_retain);
+        int32_t *out = idx + g * k;
+        for (int64_t i = 0; i < k; ++i) out[i] = buf[i].index;
+        qsort(out, (size_t)k, sizeof(int32_t), cmp_int32);
+    }
+    free(buf);
+    return ORA_OK;
+}
+
+/* Compaction: out[g][i][:] = X[g][idx[g][i]][:] (bytes copied as they are). */
+int ora_gather(const uint16_t *X, int64_t G, int64_t S, int64_t s_stride, int64_t D,
+               const int32_t *idx, int64_t k, uint16_t *out) {
+    if (G < 0 || S < 0 || D <= 0 || k < 0 || k > S || s_stride < S) return ORA_EINVAL;
+    for (int64_t g = 0; g < G; ++g)
+        for (int64_t i = 0; i < k; ++i) {
+            int32_t t = idx[g * k + i];
+            if (t < 0 || t >= S) return ORA_EINVAL;
+            memcpy(out + (g * k + i) * D, X + (g * s_stride + (int64_t)t) * D,
+                   sizeof(uint16_t) * (size_t)D);
+        }
+    return ORA_OK;
+}
+
+/* ------------------------------------------------------- OjaKV low rank */
+
+/* Low-rank projection, residual and query-weighted error score for every
+ * token of every slice ([OJA] background: K~ = K U_k, V~ = V U_v; method
+ * details: r_t = k_t - U_k U_k^T k_t and
+ *   e_t = 1/|W_t| * sum_{h, q in W_t} | q_{h,q}^T r_t / sqrt(d_h) | ).
+ * The query window of kv head h is the H_q/H_kv query heads of its group
+ * (heads h*g .. h*g+g-1), each with its W_q most recent queries, so that
+ * |W_t| = g * W_q.
+ *   K, V     : [L][B][H_kv][s_stride][D] bf16   (V nullable)
+ *   Q        : [L][B][H_q][W_q][D] bf16          (nullable: no error score)
+ *   Uk, Uv   : [L][H_kv][D][R] fp32, one basis per (layer, kv head)
+ *   Kt, Vt   : [L][B][H_kv][s_stride][R]         (Vt nullable iff V is)
+ *   err      : [L][B][H_kv][s_stride]            (nullable iff Q is)
+ */
+int ora_lowrank_compress(int64_t L, int64_t B, int64_t Hkv, int64_t Hq, int64_t S,
+                         int64_t s_stride, int64_t D, int64_t R, int64_t Wq,
+                         const uint16_t *K, const uint16_t *V, const uint16_t *Q,
+                         const float *Uk, const float *Uv, double *Kt, double *Vt,
+                         double *err) {
+    if (L < 0 || B < 0 || Hkv <= 0 || D <= 0 || R <= 0 || R > D || S < 0 || s_stride < S)
+        return ORA_EINVAL;
+    if (!K || !Uk || !Kt) return ORA_EINVAL;
+    if ((V == NULL) != (Vt == NULL) || (V && !Uv)) return ORA_EINVAL;
+    if ((Q == NULL) != (err == NULL)) return ORA_EINVAL;
+    if (Q && (Hq <= 0 || Hq % Hkv != 0 || Wq <= 0)) return ORA_EINVAL;
+    int64_t grp = Q ? Hq / Hkv : 0;
+    double *k = (double *)malloc(sizeof(double) * (size_t)(3 * D + R));
+    if (!k) return ORA_ENOMEM;
+    double *khat = k + D, *r = khat + D, *kt = r + D;
+    double inv_sqrt_d = 1.0 / sqrt((double)D);
+
+    for (int64_t l = 0; l < L; ++l)
+        for (int64_t b = 0; b < B; ++b)
+            for (int64_t h = 0; h < Hkv; ++h) {
+                int64_t slice = (l * B + b) * Hkv + h;
+                const float *U = Uk + (l * Hkv + h) * D * R;
+                for (int64_t t = 0; t < S; ++t) {
+                    const uint16_t *krow = K + (slice * s_stride + t) * D;
+                    if (!all_finite_bf16(krow, D)) {
+                        free(k);
+                        return ORA_ENONFINITE;
+                    }
+                    for (int64_t c = 0; c < D; ++c) k[c] = bf16_to_double(krow[c]);
+                    /* projection onto the basis: k~_j = sum_c k_c U[c][j] */
+                    for (int64_t j = 0; j < R; ++j) {
+                        double acc = 0.0;
+                        for (int64_t c = 0; c < D; ++c) acc += k[c] * (double)U[c * R + j];
+                        kt[j] = acc;
+                        Kt[(slice * s_stride + t) * R + j] = acc;
+                    }
+                    if (!Q) continue;
+                    /* reconstruction inside the residual, from the unrounded k~ */
+                    for (int64_t c = 0; c < D; ++c) {
+                        double acc = 0.0;
+                        for (int64_t j = 0; j < R; ++j) acc += kt[j] * (double)U[c * R + j];
+                        khat[c] = acc;
+                        r[c] = k[c] - khat[c];
+                    }
+                    /* query-weighted error over the group's recent-query window */
+                    double e = 0.0;
+                    for (int64_t hq = h * grp; hq < (h + 1) * grp; ++hq)
+                        for (int64_t q = 0; q < Wq; ++q) {
+                            const uint16_t *qrow = Q + (((l * B + b) * Hq + hq) * Wq + q) * D;
+                            double dot = 0.0;
+                            for (int64_t c = 0; c < D; ++c) dot += bf16_to_double(qrow[c]) * r[c];
+                            e += fabs(dot * inv_sqrt_d);
+                        }
+                    err[slice * s_stride + t] = e / (double)(grp * Wq);
+                }
+                if (V) {
+                    const float *Uvh = Uv + (l * Hkv + h) * D * R;
+                    for (int64_t t = 0; t < S; ++t) {
+                        const uint16_t *vrow = V + (slice * s_stride + t) * D;
+                        if (!all_finite_bf16(vrow, D)) {
+                            free(k);
+                            return ORA_ENONFINITE;
+                        }
+                        for (int64_t j = 0; j < R; ++j) {
+                            double acc = 0.0;
+                            for (int64_t c = 0; c < D; ++c)
+                                acc += bf16_to_double(vrow[c]) * (double)Uvh[c * R + j];
+                            Vt[(slice * s_stride + t) * R + j] = acc;
+                        }
+                    }
+                }
+            }
+    free(k);
+    return ORA_OK;
+}
+
+/* Reconstruction before attention ([OJA] background: K^ = K~ U_k^T), with the
+ * hybrid cache's full-rank anchors put back as they were stored ([OJA] method
+ * details: top-k tokens kept at full rank).
+ *   Xt   : [L][B][H_kv][s_stride][R] (double: the caller widens fp32 exactly)
+ *   U    : [L][H_kv][D][R] fp32
+ *   idx  : [L][B][H_kv][k] anchor token indices; rows: [..][k][D] bf16
+ *   Xhat : [L][B][H_kv][s_stride][D]                                        */
+int ora_reconstruct(int64_t L, int64_t B, int64_t Hkv, int64_t S, int64_t s_stride, int64_t D,
+                    int64_t R, const double *Xt, const float *U, const int32_t *idx,
+                    const uint16_t *rows, int64_t k, double *Xhat) {
+    if (L < 0 || B < 0 || Hkv <= 0 || D <= 0 || R <= 0 || R > D || S < 0 || s_stride < S ||
+        k < 0 || k > S)
+        return ORA_EINVAL;
+    if (!Xt || !U || !Xhat || (k > 0 && (!idx || !rows))) return ORA_EINVAL;
+    for (int64_t l = 0; l < L; ++l)
+        for (int64_t b = 0; b < B; ++b)
+            for (int64_t h = 0; h < Hkv; ++h) {
+                int64_t slice = (l * B + b) * Hkv + h;
+                const float *Uh = U + (l * Hkv + h) * D * R;
+                for (int64_t t = 0; t < S; ++t)
+                    for (int64_t c = 0; c < D; ++c) {
+                        double acc = 0.0;
+                        for (int64_t j = 0; j < R; ++j)
+                            acc += Xt[(slice * s_stride + t) * R + j] * (double)Uh[c * R + j];
+                        Xhat[(slice * s_stride + t) * D + c] = acc;
+                    }
+                for (int64_t i = 0; i < k; ++i) {
+                    int32_t t = idx[slice * k + i];
+                    if (t < 0 || t >= S) return ORA_EINVAL;
+                    for (int64_t c = 0; c < D; ++c)
+                        Xhat[(slice * s_stride + t) * D + c] =
+                            bf16_to_double(rows[(slice * k + i) * D + c]);
+                }
+            }
+    return ORA_OK;
+}
+
+/* --------------------------------------------------------- Oja + QR */
+
+/* Local average pooling along tokens ([OJA] method details:
+ * X_pooled = AvgPool(X, b); Algorithm 1 prefill step 1).  Windows are
+ * [i*p, min((i+1)p, N)) with kernel = stride = p; a short tail window is
+ * averaged over the tokens it holds.  X: [N][D] bf16 (one slice),
+ * out: [ceil(N/p)][D]. */
+int ora_avgpool(const uint16_t *X, int64_t N, int64_t D, int64_t p, double *out) {
+    if (N < 0 || D <= 0 || p <= 0) return ORA_EINVAL;
+    int64_t np = (N + p - 1) / p;
+    for (int64_t i = 0; i < np; ++i) {
+        int64_t t0 = i * p, t1 = t0 + p < N ? t0 + p : N;
+        for (int64_t c = 0; c < D; ++c) {
+            double acc = 0.0;
+            for (int64_t t = t0; t < t1; ++t) acc += bf16_to_double(X[t * D + c]);
+            out[i * D + c] = acc / (double)(t1 - t0);
+        }
+    }
+    return ORA_OK;
+}
+
+/* One Oja step on a batch ([OJA] how-it-works display equation and method
+ * details):  C = (1/n) X^T X  (the empirical, uncentred second moment of the
+ * n feature rows), U' = U + eta (C U - U U^T C U).  No re-orthonormalisation
+ * here.  X: [n][D] (rows are tokens), U, Unew: [D][R]. */
+int ora_oja_step(const double *X, int64_t n, int64_t D, int64_t R, const double *U, double eta,
+                 double *Unew) {
+    if (n <= 0 || D <= 0 || R <= 0 || R > D) return ORA_EINVAL;
+    double *C = (double *)malloc(sizeof(double) * (size_t)(D * D + D * R + R * R));
+    if (!C) return ORA_ENOMEM;
+    double *CU = C + D * D, *UtCU = CU + D * R;
+    for (int64_t a = 0; a < D; ++a)
+        for (int64_t c = 0; c < D; ++c) {
+            double acc = 0.0;
+            for (int64_t i = 0; i < n; ++i) acc += X[i * D + a] * X[i * D + c];
+            C[a * D + c] = acc / (double)n;
+        }
+    for (int64_t a = 0; a < D; ++a)
+        for (int64_t j = 0; j < R; ++j) {
+            double acc = 0.0;
+            for (int64_t c = 0; c < D; ++c) acc += C[a * D + c] * U[c * R + j];
+            CU[a * R + j] = acc;
+        }
+    for (int64_t i = 0; i < R; ++i)
+        for (int64_t j = 0; j < R; ++j) {
+            double acc = 0.0;
+            for (int64_t a = 0; a < D; ++a) acc += U[a * R + i] * CU[a * R + j];
+            UtCU[i * R + j] = acc;
+        }
+    for (int64_t a = 0; a < D; ++a)
+        for (int64_t j = 0; j < R; ++j) {
+            double acc = 0.0;
+            for (int64_t i = 0; i < R; ++i) acc += U[a * R + i] * UtCU[i * R + j];
+            Unew[a * R + j] = U[a * R + j] + eta * (CU[a * R + j] - acc);
+        }
+    free(C);
+    return ORA_OK;
+}
+
+/* Thin QR by Gram-Schmidt, each column orthogonalised twice against the
+ * columns before it ([OJA] method details: re-orthonormalise by QR after
+ * every update).  Q: [D][R] with orthonormal columns spanning those of A,
+ * taken with a positive diagonal of R, which makes Q unique. */
+int ora_qr(const double *A, int64_t D, int64_t R, double *Q) {
+    if (D <= 0 || R <= 0 || R > D) return ORA_EINVAL;
+    double *v = (double *)malloc(sizeof(double) * (size_t)D);
+    if (!v) return ORA_ENOMEM;
+    for (int64_t j = 0; j < R; ++j) {
+        for (int64_t a = 0; a < D; ++a) v[a] = A[a * R + j];
+        for (int pass = 0; pass < 2; ++pass)
+            for (int64_t i = 0; i < j; ++i) {
+                double dot = 0.0;
+                for (int64_t a = 0; a < D; ++a) dot += Q[a * R + i] * v[a];
+                for (int64_t a = 0; a < D; ++a) v[a] -= dot * Q[a * R + i];
+            }
+        double nrm = 0.0;
+        for (int64_t a = 0; a < D; ++a) nrm += v[a] * v[a];
+        nrm = sqrt(nrm);
+        if (!(nrm > 0.0)) {
+            free(v);
+            return ORA_EINVAL; /* rank deficient */
+        }
+        for (int64_t a = 0; a < D; ++a) Q[a * R + j] = v[a] / nrm;
+    }
+    free(v);
+    return ORA_OK;
+}
+
+/* Basis update for every (layer, kv head) ([OJA] method details, two-phase
+ * online update; Algorithm 1): pool each batch row's N tokens with window p,
+ * stack the pooled rows of all B sequences (n = B * ceil(N/p) rows), take one
+ * Oja step with the empirical second moment, then re-orthonormalise by QR.
+ *   U_in : [L][H_kv][D][R] fp32,  U_out : [L][H_kv][D][R] double
+ *   X    : [L][B][H_kv][n_stride][D] bf16, first N tokens of each slice used */
+int ora_oja_update(int64_t L, int64_t B, int64_t Hkv, int64_t N, int64_t n_stride, int64_t D,
+                   int64_t R, const float *U_in, const uint16_t *X, int64_t p, double eta,
+                   double *U_out) {
+    if (L < 0 || B <= 0 || Hkv <= 0 || N <= 0 || n_stride < N || D <= 0 || R <= 0 || R > D ||
+        p <= 0)
+        return ORA_EINVAL;
+    if (!isfinite(eta)) return ORA_EINVAL;
+    int64_t np = (N + p - 1) / p;
+    double *Xp = (double *)malloc(sizeof(double) * (size_t)(B * np * D + 2 * D * R));
+    if (!Xp) return ORA_ENOMEM;
+    double *U = Xp + B * np * D, *Un = U + D * R;
+    int rc = ORA_OK;
+    for (int64_t l = 0; l < L && rc == ORA_OK; ++l)
+        for (int64_t h = 0; h < Hkv && rc == ORA_OK; ++h) {
+            for (int64_t b = 0; b < B; ++b) {
+                const uint16_t *Xs = X + ((l * B + b) * Hkv + h) * n_stride * D;
+                if (!all_finite_bf16(Xs, N * D)) {
+                    rc = ORA_ENONFINITE;
+                    break;
+                }
+                ora_avgpool(Xs, N, D, p, Xp + b * np * D);
+            }
+            if (rc != ORA_OK) break;
+            const float *Uh = U_in + (l * Hkv + h) * D * R;
+            for (int64_t i = 0; i < D * R; ++i) U[i] = (double)Uh[i];
+            rc = ora_oja_step(Xp, B * np, D, R, U, eta, Un);
+            if (rc == ORA_OK) rc = ora_qr(Un, D, R, U_out + (l * Hkv + h) * D * R);
+        }
+    free(Xp);
+    return rc;
+}
