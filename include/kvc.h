@@ -1,0 +1,172 @@
+/*
+ * kvc.h -- C ABI of libkvc: KV-cache token scoring, eviction/compaction and
+ * hybrid low-rank compression on AMD Instinct MI355X (gfx950).
+ *
+ * Methods (cited by page title and section):
+ *   [MKV] "ManifoldKV: Training-Free KV Cache Compression via Euclidean
+ *         Outlier Detection" (ICML 2026 poster page), abstract.
+ *   [OJA] "OjaKV: Context-Aware Online Low-Rank KV Cache Compression"
+ *         (papercache deep-notes page): "how it works" equations, background
+ *         on low-rank attention, method details, appendix A.1 (Algorithm 1).
+ *
+ * Common conventions
+ *   - Every tensor pointer is a DEVICE pointer to dense row-major memory.
+ *     bf16 tensors are passed as uint16_t bit patterns.  Pointers to bf16 and
+ *     fp32 tensors must be 16-byte aligned.
+ *   - A "slice" is one (layer, batch, kv head).  Per-token tensors are laid
+ *     out [slice][token][...]; G = number of slices.  Where a `s_stride`
+ *     appears, consecutive slices are s_stride tokens apart (s_stride >= S)
+ *     so that a cache with spare capacity can be processed in place.
+ *   - Ownership: the caller allocates every buffer, including the workspace
+ *     `ws` of at least kvc_workspace_bytes(...) bytes (256-byte aligned).  The
+ *     library never allocates or frees device memory and keeps no pointer
+ *     after the call returns.  Buffers must stay valid until the work queued
+ *     on `stream` has completed.  Inputs and outputs must not overlap, except
+ *     where a parameter is documented in/out.
+ *   - Execution: arguments are validated synchronously; on any error nothing
+ *     is launched and the status is returned.  Otherwise the work is queued on
+ *     `stream` (0 = the null stream) and the call returns without waiting.
+ *     Results are deterministic: the same inputs give the same bits on every
+ *     run.  Two calls that share a workspace must not run concurrently.
+ *   - Inputs must be finite; results for NaN/Inf inputs are unspecified.
+ *   - Supported shapes: head dimension D = 128; low rank R in {32, 64, 96,
+ *     128}; at most 128 queries per error-score window (g * W_q <= 128);
+ *     S, k and window counts below 2^31.
+ */
+#ifndef KVC_H
+#define KVC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVC_ABI_VERSION 1
+
+typedef enum kvc_status {
+    KVC_OK = 0,
+    KVC_ERR_INVALID_ARGUMENT = 1,   /* null/misaligned pointer, negative or inconsistent size */
+    KVC_ERR_UNSUPPORTED = 2,        /* valid but not built: D != 128, R not in {32,64,96,128}, ... */
+    KVC_ERR_WORKSPACE_TOO_SMALL = 3,/* ws_bytes < kvc_workspace_bytes(...) */
+    KVC_ERR_HIP = 4                 /* a HIP runtime call or kernel launch failed */
+} kvc_status;
+
+typedef enum kvc_op {
+    KVC_OP_SCORE_L2 = 0,
+    KVC_OP_SCORE_L2_WINDOWED = 1,
+    KVC_OP_TOPK_COMPACT = 2,
+    KVC_OP_LOWRANK_COMPRESS = 3,
+    KVC_OP_OJA_UPDATE = 4,
+    KVC_OP_RECONSTRUCT = 5
+} kvc_op;
+
+/* Shapes of a multi-layer KV cache.
+ *   L layers, B sequences, H_kv key/value heads, H_q query heads (a multiple of
+ *   H_kv; kv head h serves query heads h*g .. h*g+g-1 with g = H_q/H_kv),
+ *   S valid tokens per slice, S_stride allocated tokens per slice (0 -> S),
+ *   D head dimension, R low rank, W_q recent queries per query head. */
+typedef struct kvc_dims {
+    int64_t L, B, H_kv, H_q, S, S_stride, D, R, W_q;
+} kvc_dims;
+
+/* ABI version of the loaded library (KVC_ABI_VERSION). */
+int kvc_abi_version(void);
+
+/* Static, human-readable text for a status code. */
+const char *kvc_status_str(kvc_status s);
+
+/* Workspace bytes needed by one call of `op`.
+ *   SCORE_L2, SCORE_L2_WINDOWED: G = L*B*H_kv slices of S tokens; W = window
+ *     (ignored for SCORE_L2).
+ *   TOPK_COMPACT: G = L*B*H_kv slices of S tokens; k = tokens kept.
+ *   LOWRANK_COMPRESS, OJA_UPDATE, RECONSTRUCT: shapes from `d`; for OJA_UPDATE
+ *     d->S is the token count N and W is the pooling window.
+ * 0 means the call needs no workspace (ws may then be NULL); invalid shapes
+ * also give 0 and are reported by the call itself. */
+size_t kvc_workspace_bytes(kvc_op op, const kvc_dims *d, int64_t k, int64_t W);
+
+/* Global ManifoldKV score ([MKV] abstract): for every slice g and token t,
+ *   mu_g       = (1/S) sum_t K[g][t][:]           (the key centroid)
+ *   scores[g][t] = || K[g][t][:] - mu_g ||_2      (Euclidean distance)
+ * K: bf16 [G][S][D].  scores: fp32 [G][S].  centroid: fp32 [G][D] or NULL.
+ * Accumulation is fp32.  G >= 0, S >= 1 (G = 0 is a no-op). */
+kvc_status kvc_score_l2(const uint16_t *K, int64_t G, int64_t S, int32_t D, float *scores,
+                        float *centroid, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* WindowedManifoldKV score ([MKV] abstract): as kvc_score_l2, but token t is
+ * scored against the centroid of its contiguous window j = floor(t/W), the
+ * mean over tokens [jW, min((j+1)W, S)) (a short last window is averaged over
+ * the tokens it holds).  W >= S reproduces kvc_score_l2.
+ * centroids: fp32 [G][ceil(S/W)][D] or NULL.  W >= 1. */
+kvc_status kvc_score_l2_windowed(const uint16_t *K, int64_t G, int64_t S, int32_t D, int64_t W,
+                                 float *scores, float *centroids, void *ws, size_t ws_bytes,
+                                 hipStream_t stream);
+
+/* Retention and compaction ([MKV] abstract: the keys farthest from the
+ * centroid are retained; [OJA] method details: the top-k error scores are kept
+ * at full rank).  For each slice g, selects the k largest scores[g][0..S)
+ * (equal scores: the lower token index wins; +0.0 == -0.0), writes their token
+ * indices in ascending order to idx_out[g][0..k), and, when K / V are given,
+ * copies the selected rows bit for bit: K_out[g][i][:] = K[g][idx_out[g][i]][:].
+ *   scores: fp32, slice stride s_stride floats (s_stride >= S)
+ *   K, V:   bf16, slice stride s_stride rows of D, or NULL
+ *   idx_out: int32 [G][k];  K_out, V_out: bf16 [G][k][D] (NULL iff K / V NULL)
+ * 0 <= k <= S. */
+kvc_status kvc_topk_compact(const float *scores, int64_t G, int64_t S, int64_t s_stride, int64_t k,
+                            const uint16_t *K, const uint16_t *V, int32_t D, int32_t *idx_out,
+                            uint16_t *K_out, uint16_t *V_out, void *ws, size_t ws_bytes,
+                            hipStream_t stream);
+
+/* Hybrid low-rank compression ([OJA] background: K~ = K U_k, V~ = V U_v;
+ * method details: residual r_t = k_t - U_k U_k^T k_t and query-weighted error
+ *   err_t = 1/|W_t| sum_{h, q in W_t} | q_{h,q}^T r_t / sqrt(D) |,
+ * the window W_t being the W_q recent queries of the g query heads of the
+ * slice's kv head, |W_t| = g*W_q).
+ *   K, V:   bf16 [L][B][H_kv][S_stride][D]     (V may be NULL)
+ *   Q_win:  bf16 [L][B][H_q][W_q][D]           (NULL: no error score)
+ *   U_k, U_v: fp32 [L][H_kv][D][R], one basis per (layer, kv head), shared by
+ *           the batch; any matrix is accepted (orthonormality is not checked)
+ *   K_tilde, V_tilde: fp32 [L][B][H_kv][S_stride][R]  (V_tilde NULL iff V NULL)
+ *   err:    fp32 [L][B][H_kv][S_stride]        (NULL iff Q_win NULL)
+ * Rows t >= S of the outputs are not written. */
+kvc_status kvc_lowrank_compress(const kvc_dims *d, const uint16_t *K, const uint16_t *V,
+                                const uint16_t *Q_win, const float *U_k, const float *U_v,
+                                float *K_tilde, float *V_tilde, float *err, void *ws,
+                                size_t ws_bytes, hipStream_t stream);
+
+/* Oja basis update with pooling and QR ([OJA] how it works: the Oja rule;
+ * method details: prefill update on AvgPool(X, pool) with the empirical
+ * covariance, decode update on the buffered tokens, re-orthonormalisation by
+ * QR; appendix A.1).  For each (layer, kv head):
+ *   X_p = rows of AvgPool(X[l][b][h][0..N), pool) for b = 0..B-1 (windows
+ *         [i*pool, min((i+1)*pool, N)), a short tail averaged over its rows),
+ *   n   = B * ceil(N/pool),  C = X_p^T X_p / n,
+ *   U  <- Q factor of  U + eta (C U - U U^T C U)  (positive diagonal of R).
+ *   U: fp32 [L][H_kv][D][R], IN/OUT (updated in place)
+ *   X: bf16 [L][B][H_kv][S_stride][D], the first N = d->S tokens are used
+ * pool >= 1 (1 = no pooling); eta finite.  The update is computed in fp64
+ * after an fp32 accumulation of C. */
+kvc_status kvc_oja_update(const kvc_dims *d, float *U, const uint16_t *X, int32_t pool, float eta,
+                          void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Reconstruction before attention ([OJA] background: K^ = K~ U_k^T) with the
+ * hybrid cache's full-rank anchors put back ([OJA] method details):
+ *   X_hat[g][t][:] = X_tilde[g][t][:] U^T              for non-anchor t,
+ *   X_hat[g][idx[g][i]][:] = anchor_rows[g][i][:] (bf16 widened exactly).
+ *   X_tilde: fp32 [L][B][H_kv][S_stride][R];  U: fp32 [L][H_kv][D][R]
+ *   anchor_idx: int32 [L*B*H_kv][k] (indices < S, unique); anchor_rows: bf16
+ *   [L*B*H_kv][k][D]; both NULL iff k == 0
+ *   X_hat: fp32 [L][B][H_kv][S_stride][D] (rows t >= S not written) */
+kvc_status kvc_reconstruct(const kvc_dims *d, const float *X_tilde, const float *U,
+                           const int32_t *anchor_idx, const uint16_t *anchor_rows, int64_t k,
+                           float *X_hat, void *ws, size_t ws_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVC_H */

@@ -1,0 +1,139 @@
+"""GPU parity of the OjaKV hybrid low-rank path against the CPU oracle, through
+the C ABI: projection K~/V~ and reconstruction within rel 2e-3 of
+(|oracle| + rms(slice)); the error score e_t (an fp32 score) within rel 1e-4;
+Oja/QR bases within rel 2e-3 and orthonormal to 1e-5; anchors by the
+threshold-band rule; anchor rows exact."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests.helpers import index_sets_agree, lowrank_close, score_close
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _compress_check(gpu_lib, inp, slices=None, S=None):
+    S = inp.S if S is None else S
+    Kt, Vt, err = gpu_lib.kvc_lowrank_compress(inp.K, inp.V, inp.Q, inp.Uk, inp.Uv, inp.L, inp.B,
+                                               inp.Hkv, S=S)
+    torch.cuda.synchronize()
+    G = inp.L * inp.B * inp.Hkv
+    slices = range(G) if slices is None else slices
+    Uk = inp.Uk.cpu().numpy()
+    Uv = inp.Uv.cpu().numpy()
+    for g in slices:
+        l = g // (inp.B * inp.Hkv)
+        b = (g // inp.Hkv) % inp.B
+        h = g % inp.Hkv
+        grp = inp.Hq // inp.Hkv
+        Q = synth.bf16_bits(inp.Q[l:l + 1, b:b + 1, h * grp:(h + 1) * grp])
+        okt, ovt, oerr = oracle.lowrank_compress(
+            synth.bf16_bits(inp.K[g:g + 1, :S]), synth.bf16_bits(inp.V[g:g + 1, :S]), Q,
+            Uk[l:l + 1, h:h + 1], Uv[l:l + 1, h:h + 1], 1, 1, 1, grp)
+        ok, rel = lowrank_close(Kt[g:g + 1, :S].cpu().numpy(), okt)
+        assert ok, "K~ slice %d: max rel %.3g" % (g, rel)
+        ok, rel = lowrank_close(Vt[g:g + 1, :S].cpu().numpy(), ovt)
+        assert ok, "V~ slice %d: max rel %.3g" % (g, rel)
+        ok, rel, nbad = score_close(err[g:g + 1, :S].cpu().numpy(), oerr)
+        assert ok, "err slice %d: %d off, max rel %.3g" % (g, nbad, rel)
+    return Kt, Vt, err
+
+
+@pytest.mark.parametrize("R", [32, 64, 96, 128])
+def test_compress_small(gpu_lib, R):
+    inp = synth.oja_inputs(2, 2, 2, 8, 700, R=R, Wq=32, seed=R, device=DEV)
+    _compress_check(gpu_lib, inp)
+
+
+@pytest.mark.parametrize("Hq,Wq", [(2, 1), (4, 7), (16, 8)])
+def test_compress_window_shapes(gpu_lib, Hq, Wq):
+    # |W| = g*Wq from 1 to 64 queries; ragged token tail; strided cache (S < S_stride)
+    inp = synth.oja_inputs(1, 1, 2, Hq, 333, R=64, Wq=Wq, S_cap=400, seed=Hq * 100 + Wq, device=DEV)
+    _compress_check(gpu_lib, inp, S=333)
+
+
+def test_compress_without_query_or_values(gpu_lib):
+    inp = synth.oja_inputs(1, 1, 2, 8, 300, R=64, Wq=4, device=DEV)
+    Kt, Vt, err = gpu_lib.kvc_lowrank_compress(inp.K, None, None, inp.Uk, None, 1, 1, 2)
+    torch.cuda.synchronize()
+    assert Vt is None and err is None
+    okt, _, _ = oracle.lowrank_compress(synth.bf16_bits(inp.K), None, None, inp.Uk.cpu().numpy(), None,
+                                        1, 1, 2, 0)
+    ok, rel = lowrank_close(Kt.cpu().numpy(), okt)
+    assert ok, rel
+
+
+def test_config3_sampled(gpu_lib):
+    # 32 layers x batch 4 x 8 kv heads x 32 query heads, S=32768, r=64, 32-query window, 5% anchors
+    inp = synth.oja_inputs(32, 4, 8, 32, 32768, R=64, Wq=32, device=DEV)
+    Kt, Vt, err = _compress_check(gpu_lib, inp, slices=[0, 517])
+    k = oracle.n_anchors(32768)
+    idx, Ka, Va = gpu_lib.kvc_topk_compact(err, k, inp.K, inp.V)
+    torch.cuda.synchronize()
+    for g in [0, 517]:
+        l, b, h = g // 32, (g // 8) % 4, g % 8
+        Q = synth.bf16_bits(inp.Q[l:l + 1, b:b + 1, 4 * h:4 * h + 4])
+        _, _, oerr = oracle.lowrank_compress(synth.bf16_bits(inp.K[g:g + 1]), None, Q,
+                                             inp.Uk[l:l + 1, h:h + 1].cpu().numpy(), None, 1, 1, 1, 4)
+        e32 = oerr.astype(np.float32)
+        ok, nb = index_sets_agree(idx[g:g + 1].cpu().numpy(), oracle.topk(e32, k), e32, k)
+        assert ok
+        sel = idx[g].cpu().numpy().astype(np.int64)
+        np.testing.assert_array_equal(synth.bf16_bits(Ka[g]), synth.bf16_bits(inp.K[g])[sel])
+
+
+@pytest.mark.parametrize("R,k", [(32, 0), (64, 17), (128, 5)])
+def test_reconstruct_small(gpu_lib, R, k):
+    L, B, Hkv, S = 2, 1, 3, 517
+    G = L * B * Hkv
+    Xt = synth.random_lowrank(G, S, R, seed=R).to(DEV)
+    U = torch.from_numpy(np.stack([[synth.orthonormal_basis(128, R, 3, l, h) for h in range(Hkv)]
+                                   for l in range(L)])).to(DEV)
+    rng = np.random.default_rng(R + k)
+    idx = np.sort(np.stack([rng.choice(S, k, replace=False) for _ in range(G)]), 1).astype(np.int32)
+    rows = synth.bf16_bits(torch.randn((G, k, 128)).to(torch.bfloat16))
+    idx_t = torch.from_numpy(idx).to(DEV) if k else None
+    rows_t = synth.from_bits(rows, DEV) if k else None
+    Xh = gpu_lib.kvc_reconstruct(Xt, U, idx_t, rows_t, L, B, Hkv)
+    torch.cuda.synchronize()
+    ora = oracle.reconstruct(Xt.cpu().numpy(), U.cpu().numpy(), idx if k else None, rows if k else None,
+                             L, B, Hkv)
+    ok, rel = lowrank_close(Xh.cpu().numpy(), ora)
+    assert ok, rel
+    for g in range(G):  # anchors exact
+        np.testing.assert_array_equal(Xh[g].cpu().numpy()[idx[g]], ora[g][idx[g]])
+
+
+@pytest.mark.parametrize("B,N,pool,eta", [(1, 4096, 32, 1e-3), (2, 700, 7, 0.05), (1, 32, 1, 1e-3),
+                                          (3, 64, 1, 0.1)])
+def test_oja_update_small(gpu_lib, B, N, pool, eta):
+    L, Hkv, R = 2, 2, 64
+    inp = synth.oja_inputs(L, B, Hkv, 4, N, R=R, Wq=1, seed=N + B, device=DEV)
+    U0 = inp.Uk.clone()
+    U = inp.Uk.clone()
+    gpu_lib.kvc_oja_update(U, inp.K, pool, eta, L, B, Hkv)
+    torch.cuda.synchronize()
+    ora = oracle.oja_update(U0.cpu().numpy(), synth.bf16_bits(inp.K), pool, eta, L, B, Hkv)
+    Ug = U.cpu().numpy().astype(np.float64)
+    ok, rel = lowrank_close(Ug.reshape(L * Hkv, -1), ora.reshape(L * Hkv, -1))
+    assert ok, rel
+    # the step itself (U' - U) is also matched, so the check is not carried by U alone
+    d_gpu = Ug - U0.cpu().numpy()
+    d_ora = ora - U0.cpu().numpy()
+    ok, rel = lowrank_close(d_gpu.reshape(L * Hkv, -1), d_ora.reshape(L * Hkv, -1), rel=2e-3)
+    assert ok, rel
+    for l in range(L):
+        for h in range(Hkv):
+            assert np.abs(Ug[l, h].T @ Ug[l, h] - np.eye(R)).max() < 1e-5
+
+
+def test_compress_determinism(gpu_lib):
+    inp = synth.oja_inputs(1, 2, 4, 16, 3000, R=64, Wq=32, device=DEV)
+    a = [t.clone() for t in gpu_lib.kvc_lowrank_compress(inp.K, inp.V, inp.Q, inp.Uk, inp.Uv, 1, 2, 4)]
+    b = gpu_lib.kvc_lowrank_compress(inp.K, inp.V, inp.Q, inp.Uk, inp.Uv, 1, 2, 4)
+    torch.cuda.synchronize()
+    for x, y in zip(a, b):
+        assert torch.equal(x, y)

@@ -1,0 +1,129 @@
+"""GPU parity of ManifoldKV scoring (global and windowed), retention and
+compaction against the CPU oracle, through the C ABI.  Rules: fp32 scores
+within rel 1e-4 (+1e-6 rms); top-k on identical fp32 scores bit-exact;
+end-to-end retained sets identical except for tokens within rel 1e-4 of the
+k-th score; gathered rows bit-exact."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests.helpers import index_sets_agree, score_close
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _scores_vs_oracle(K, gpu_scores, W=None):
+    bits = synth.bf16_bits(K)
+    ora, mu = oracle.score_l2(bits) if W is None else oracle.score_l2_windowed(bits, W)
+    ok, rel, nbad = score_close(gpu_scores.cpu().numpy(), ora)
+    assert ok, "scores: %d outside tolerance, max rel %.3g" % (nbad, rel)
+    return ora, mu
+
+
+@pytest.mark.parametrize("G,S", [(1, 1), (3, 257), (2, 1000), (4, 4096), (1, 16384 + 77)])
+def test_score_l2_small(gpu_lib, G, S):
+    K, _, _ = synth.manifold_global(1, 1, G, S, planted=min(4, S), seed=S, device=DEV)
+    mu_gpu = torch.empty((G, 128), dtype=torch.float32, device=DEV)
+    s = gpu_lib.kvc_score_l2(K, centroid=mu_gpu)
+    torch.cuda.synchronize()
+    _, mu = _scores_vs_oracle(K, s)
+    np.testing.assert_allclose(mu_gpu.cpu().numpy(), mu, rtol=1e-5, atol=1e-5)
+
+
+@pytest.mark.parametrize("S,W", [(1000, 1), (1000, 1000), (1000, 5000), (1000, 300), (4096 * 3 + 5, 4096),
+                                 (8192, 512)])
+def test_score_l2_windowed_small(gpu_lib, S, W):
+    K, _ = synth.manifold_drifting(1, 1, 2, S, segment=max(1, S // 3), seed=W, device=DEV)
+    nwin = -(-S // W)
+    mu_gpu = torch.empty((2, nwin, 128), dtype=torch.float32, device=DEV)
+    s = gpu_lib.kvc_score_l2_windowed(K, W, centroids=mu_gpu)
+    torch.cuda.synchronize()
+    _, mu = _scores_vs_oracle(K, s, W)
+    np.testing.assert_allclose(mu_gpu.cpu().numpy(), mu, rtol=1e-5, atol=1e-5)
+    if W == 1:
+        assert torch.all(s == 0)
+
+
+@pytest.mark.parametrize("kind", ["normal", "ties", "signed"])
+@pytest.mark.parametrize("G,S", [(1, 1), (3, 100), (2, 4096), (2, 4097), (5, 20000)])
+def test_topk_bit_exact_on_same_scores(gpu_lib, kind, G, S):
+    s = synth.random_scores(G, S, seed=S * 7 + G, kind=kind, device="cpu")
+    s_gpu = s.to(DEV)
+    for k in sorted({0, 1, S // 3, S // 2, S - 1, S}):
+        if k < 0:
+            continue
+        idx, _, _ = gpu_lib.kvc_topk_compact(s_gpu, k)
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(idx.cpu().numpy(), oracle.topk(s.numpy(), k))
+
+
+def test_topk_strided_and_gather_bit_exact(gpu_lib):
+    G, S, stride, k = 3, 5000, 5123, 1234
+    K = torch.randint(-32768, 32767, (G, stride, 128), dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    V = torch.randint(-32768, 32767, (G, stride, 128), dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    s = synth.random_scores(G, stride, seed=5, device="cpu")
+    idx, Ko, Vo = gpu_lib.kvc_topk_compact(s.to(DEV), k, K, V, S=S)
+    torch.cuda.synchronize()
+    ref_idx = oracle.topk(s.numpy(), k, S=S)
+    np.testing.assert_array_equal(idx.cpu().numpy(), ref_idx)
+    np.testing.assert_array_equal(synth.bf16_bits(Ko), oracle.gather(synth.bf16_bits(K), ref_idx, S=S))
+    np.testing.assert_array_equal(synth.bf16_bits(Vo), oracle.gather(synth.bf16_bits(V), ref_idx, S=S))
+
+
+def _evict_and_check(gpu_lib, K, V, keep, W=None, slices=None):
+    s = gpu_lib.kvc_score_l2(K) if W is None else gpu_lib.kvc_score_l2_windowed(K, W)
+    idx, Ko, Vo = gpu_lib.kvc_topk_compact(s, keep, K, V)
+    torch.cuda.synchronize()
+    slices = range(K.shape[0]) if slices is None else slices
+    nb_total = 0
+    for g in slices:
+        kb = synth.bf16_bits(K[g:g + 1])
+        vb = synth.bf16_bits(V[g:g + 1])
+        ora, _ = oracle.score_l2(kb) if W is None else oracle.score_l2_windowed(kb, W)
+        ok, rel, nbad = score_close(s[g:g + 1].cpu().numpy(), ora)
+        assert ok, "slice %d: %d scores off (max rel %.3g)" % (g, nbad, rel)
+        ora32 = ora.astype(np.float32)
+        ora_idx = oracle.topk(ora32, keep)
+        gi = idx[g:g + 1].cpu().numpy()
+        ok, nb = index_sets_agree(gi, ora_idx, ora32, keep)
+        assert ok, "slice %d: retained set differs beyond the threshold band" % g
+        nb_total += nb
+        # gathered rows are the input rows at the GPU's indices, bit for bit
+        # (a plain index_select on the host; the oracle never takes GPU output)
+        sel = gi[0].astype(np.int64)
+        np.testing.assert_array_equal(synth.bf16_bits(Ko[g]), kb[0][sel])
+        np.testing.assert_array_equal(synth.bf16_bits(Vo[g]), vb[0][sel])
+    return idx, nb_total
+
+
+def test_config0_global_full(gpu_lib):
+    # 1 layer x 8 kv heads, S=4096, drop 20% -> keep 3277; every slice checked
+    K, V, plant = synth.manifold_global(1, 1, 8, 4096, planted=16, device=DEV)
+    idx, _ = _evict_and_check(gpu_lib, K, V, oracle.keep_count(4096, 20))
+    for g in range(8):  # the planted x4 tokens survive
+        assert set(plant[g].tolist()) <= set(idx[g].cpu().tolist())
+
+
+def test_config1_global_sampled(gpu_lib):
+    # 32 layers x 8 kv heads, S=16384, keep 8192; launch at full size, check sampled slices
+    K, V, plant = synth.manifold_global(32, 1, 8, 16384, planted=64, device=DEV)
+    _evict_and_check(gpu_lib, K, V, 8192, slices=[0, 101, 255])
+
+
+def test_config2_windowed_sampled(gpu_lib):
+    # 32 layers x 8 kv heads, S=65536, W=4096, keep 49152; sampled slices
+    K, V = synth.manifold_drifting(32, 1, 8, 65536, device=DEV)
+    _evict_and_check(gpu_lib, K, V, 49152, W=4096, slices=[0, 200])
+
+
+def test_determinism(gpu_lib):
+    K, V, _ = synth.manifold_global(2, 1, 8, 8192, planted=8, device=DEV)
+    a = gpu_lib.kvc_score_l2(K).clone()
+    ia, Ka, _ = gpu_lib.kvc_topk_compact(a, 3000, K, V)
+    b = gpu_lib.kvc_score_l2(K)
+    ib, Kb, _ = gpu_lib.kvc_topk_compact(b, 3000, K, V)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b) and torch.equal(ia, ib) and torch.equal(Ka.view(torch.int16), Kb.view(torch.int16))

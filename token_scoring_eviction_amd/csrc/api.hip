@@ -1,0 +1,37 @@
+// Library-level entry points of libkvc: version, status text, workspace sizing.
+#include "kvc_internal.h"
+
+namespace kvc {
+size_t score_workspace_bytes(int64_t G, int64_t S, int64_t W);
+size_t topk_workspace_bytes(int64_t G, int64_t S, int64_t k);
+size_t compress_workspace_bytes(const kvc_dims *d);
+size_t oja_workspace_bytes(const kvc_dims *d, int64_t pool);
+size_t reconstruct_workspace_bytes(const kvc_dims *d);
+}  // namespace kvc
+
+extern "C" int kvc_abi_version(void) { return KVC_ABI_VERSION; }
+
+extern "C" const char *kvc_status_str(kvc_status s) {
+    switch (s) {
+        case KVC_OK: return "ok";
+        case KVC_ERR_INVALID_ARGUMENT: return "invalid argument";
+        case KVC_ERR_UNSUPPORTED: return "unsupported shape or parameter";
+        case KVC_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+        case KVC_ERR_HIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+extern "C" size_t kvc_workspace_bytes(kvc_op op, const kvc_dims *d, int64_t k, int64_t W) {
+    if (!d) return 0;
+    const int64_t G = d->L * d->B * d->H_kv;
+    switch (op) {
+        case KVC_OP_SCORE_L2: return kvc::score_workspace_bytes(G, d->S, d->S);
+        case KVC_OP_SCORE_L2_WINDOWED: return kvc::score_workspace_bytes(G, d->S, W);
+        case KVC_OP_TOPK_COMPACT: return kvc::topk_workspace_bytes(G, d->S, k);
+        case KVC_OP_LOWRANK_COMPRESS: return kvc::compress_workspace_bytes(d);
+        case KVC_OP_OJA_UPDATE: return kvc::oja_workspace_bytes(d, W);
+        case KVC_OP_RECONSTRUCT: return kvc::reconstruct_workspace_bytes(d);
+    }
+    return 0;
+}

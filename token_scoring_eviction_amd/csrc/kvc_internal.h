@@ -1,0 +1,67 @@
+// Internal helpers shared by the libkvc HIP sources (not part of the ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kvc.h"
+
+namespace kvc {
+
+constexpr int kHeadDim = 128;        // the only head dimension built
+constexpr size_t kWsAlign = 256;     // sub-buffer alignment inside a workspace
+
+inline size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+inline bool aligned(const void *p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Carves consecutive aligned sub-buffers out of a caller-provided workspace.
+struct WsCursor {
+    char *base;
+    size_t off = 0;
+    explicit WsCursor(void *p) : base(static_cast<char *>(p)) {}
+    template <class T>
+    T *take(size_t count) {
+        off = align_up(off, kWsAlign);
+        T *p = reinterpret_cast<T *>(base + off);
+        off += count * sizeof(T);
+        return p;
+    }
+};
+
+// Same layout arithmetic without a base pointer, for kvc_workspace_bytes.
+struct WsSizer {
+    size_t off = 0;
+    template <class T>
+    void take(size_t count) {
+        off = align_up(off, kWsAlign);
+        off += count * sizeof(T);
+    }
+    size_t bytes() const { return off; }
+};
+
+inline kvc_status launch_status() {
+    return hipGetLastError() == hipSuccess ? KVC_OK : KVC_ERR_HIP;
+}
+
+// ------------------------------------------------------------ device helpers
+
+// Exact bf16 -> fp32 widening of the two halves of a packed 32-bit word.
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// fp32 -> bf16 bits, round to nearest even (inputs are finite).
+__device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+// Order-preserving map of an fp32 value to an unsigned key: a > b <=> key(a) > key(b).
+// -0.0 is folded onto +0.0 so that the two compare equal, as in IEEE arithmetic.
+__device__ __forceinline__ uint32_t order_key(float f) {
+    uint32_t u = __float_as_uint(f);
+    if (u == 0x80000000u) u = 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+}  // namespace kvc

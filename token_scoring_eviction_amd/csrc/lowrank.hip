@@ -1,0 +1,535 @@
+// OjaKV hybrid low-rank path on MFMA ("OjaKV: Context-Aware Online Low-Rank KV
+// Cache Compression", background on low-rank attention and method details):
+//   compress:     K~ = K U_k, V~ = V U_v, and the query-weighted error score
+//                 err_t = 1/|W| sum_q |q^T r_t| / sqrt(D), r_t = k_t - U U^T k_t;
+//   reconstruct:  X^ = X~ U^T, then the full-rank anchor rows put back.
+//
+// Precision.  K, V and Q are bf16 and enter the bf16 MFMA exactly.  fp32
+// operands (U, X~, the folded query matrix) are split as x = hi + lo with hi,
+// lo bf16 (|x - hi - lo| <= 2^-17 |x|) and every product is accumulated in
+// fp32 by v_mfma_f32_32x32x16_bf16, so the result carries ~2^-16 relative
+// error instead of the 2^-8 of a plain bf16 rounding.
+//
+// Error score without materialising r_t.  Because (I - U U^T) is symmetric,
+// q^T r_t = ((I - U U^T) q)^T k_t for any U.  A per-slice prep kernel forms
+// Q'' = (Q_win (I - U U^T)) / (|W| sqrt(D)) once in fp64 and stores its hi/lo
+// MFMA fragments; the streaming kernel then needs one contraction per token,
+// err_t = sum_q |Q''_q . k_t|, fused with the projection on the same key tile.
+//
+// MFMA tiling (32x32x16, wave64): a wave owns 64 tokens (two 32-token column
+// blocks) per step.  Key rows are the B operand: lane i loads 16 bytes of token
+// (i % 32) at channel 16s + 8(i / 32) for k-step s, so each lane reads whole
+// 256-byte rows over the 8 k-steps.  The A operands (U^T and Q'' fragments,
+// hi and lo) sit in LDS as [fragment][lane][16 bytes], read conflict-free.
+// Accumulator lane i, register r holds row 8(r/4) + 4(i/32) + r%4, column i%32,
+// so four consecutive output features go out as one 16-byte store.
+#include "kvc_internal.h"
+
+namespace kvc {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kFragBytes = 64 * 16;  // one MFMA operand fragment: 64 lanes x 8 bf16
+
+__device__ __forceinline__ f32x16 mfma32x32x16(u32x4 a, u32x4 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// x (8 fp32) -> hi, lo (8 bf16 each, packed little-endian in 4 dwords)
+__device__ __forceinline__ void split8(const float *x, u32x4 &hi, u32x4 &lo) {
+    uint32_t h[8], l[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        h[e] = f32_to_bf16_rne(x[e]);
+        l[e] = f32_to_bf16_rne(x[e] - __uint_as_float(h[e] << 16));
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        hi[q] = h[2 * q] | (h[2 * q + 1] << 16);
+        lo[q] = l[2 * q] | (l[2 * q + 1] << 16);
+    }
+}
+
+__device__ __forceinline__ void split8_f64(const double *x, u32x4 &hi, u32x4 &lo) {
+    uint32_t h[8], l[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        h[e] = f32_to_bf16_rne(static_cast<float>(x[e]));
+        const double rest = x[e] - static_cast<double>(__uint_as_float(h[e] << 16));
+        l[e] = f32_to_bf16_rne(static_cast<float>(rest));
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        hi[q] = h[2 * q] | (h[2 * q + 1] << 16);
+        lo[q] = l[2 * q] | (l[2 * q + 1] << 16);
+    }
+}
+
+struct Slices {
+    int64_t B, Hkv, S, S_stride;
+    int64_t nsplit;     // blocks per slice
+    int64_t per_split;  // tokens per block (multiple of 64)
+};
+
+// ------------------------------------------------------------ compress prep
+
+// Folded, scaled query fragments of one slice:
+//   Q''[q][c] = scale * (Q[q][c] - sum_j (sum_c' Q[q][c'] U[c'][j]) U[c][j])
+// in fp64, split hi/lo into A-operand fragments [qb][s][hi|lo][lane].
+__global__ __launch_bounds__(256) void prep_query_kernel(const uint16_t *__restrict__ Q,
+                                                         const float *__restrict__ Uk, int64_t B,
+                                                         int64_t Hkv, int64_t Hq, int64_t Wq,
+                                                         int R, int nq, int nqb, double scale,
+                                                         u32x4 *__restrict__ qfrag) {
+    extern __shared__ double T[];  // [128][R]: T = Q U
+    const int64_t slice = blockIdx.x;
+    const int64_t h = slice % Hkv;
+    const int64_t lb = slice / Hkv;  // l*B + b
+    const int64_t l = lb / B;
+    const int64_t grp = Hq / Hkv;
+    const float *U = Uk + (l * Hkv + h) * kHeadDim * R;
+    auto qrow = [&](int q) {
+        const int64_t hq = h * grp + q / Wq;
+        return Q + ((lb * Hq + hq) * Wq + q % Wq) * kHeadDim;
+    };
+    for (int o = threadIdx.x; o < nq * R; o += blockDim.x) {
+        const int q = o / R, j = o % R;
+        const uint16_t *qr = qrow(q);
+        double acc = 0.0;
+        for (int c = 0; c < kHeadDim; ++c)
+            acc += static_cast<double>(__uint_as_float(static_cast<uint32_t>(qr[c]) << 16)) *
+                   static_cast<double>(U[c * R + j]);
+        T[q * R + j] = acc;
+    }
+    __syncthreads();
+    u32x4 *out = qfrag + slice * static_cast<int64_t>(nqb) * 16 * 64;
+    for (int p = threadIdx.x; p < nqb * 8 * 64; p += blockDim.x) {
+        const int lane = p & 63, fs = p >> 6, s = fs & 7, qb = fs >> 3;
+        const int q = qb * 32 + (lane & 31);
+        const int c0 = 16 * s + (lane >> 5) * 8;
+        double x[8];
+        if (q < nq) {
+            const uint16_t *qr = qrow(q);
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const int c = c0 + e;
+                double proj = 0.0;
+                for (int j = 0; j < R; ++j) proj += T[q * R + j] * static_cast<double>(U[c * R + j]);
+                const double qc = static_cast<double>(__uint_as_float(static_cast<uint32_t>(qr[c]) << 16));
+                x[e] = scale * (qc - proj);
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = 0.0;
+        }
+        u32x4 hi, lo;
+        split8_f64(x, hi, lo);
+        out[((qb * 8 + s) * 2 + 0) * 64 + lane] = hi;
+        out[((qb * 8 + s) * 2 + 1) * 64 + lane] = lo;
+    }
+}
+
+// --------------------------------------------------------------- compress
+
+// One block per (slice, token range); 8 waves; each wave 64 tokens per step.
+// LDS: U^T fragments [rb][s][hi|lo] (NRB*16 KB), then Q'' fragments (nqb*16 KB).
+template <int NRB>
+__global__ __launch_bounds__(512) void project_kernel(const uint16_t *__restrict__ X,
+                                                      const float *__restrict__ Ubase,
+                                                      const u32x4 *__restrict__ qfrag, int nqb,
+                                                      Slices sl, float *__restrict__ Xt,
+                                                      float *__restrict__ err) {
+    constexpr int R = 32 * NRB;
+    extern __shared__ u32x4 lds[];
+    u32x4 *ufr = lds;
+    u32x4 *qfr = lds + NRB * 16 * 64;
+
+    const int64_t slice = blockIdx.x / sl.nsplit;
+    const int64_t split = blockIdx.x % sl.nsplit;
+    const int64_t h = slice % sl.Hkv;
+    const int64_t l = slice / (sl.Hkv * sl.B);
+    const float *U = Ubase + (l * sl.Hkv + h) * kHeadDim * R;
+
+    for (int p = threadIdx.x; p < NRB * 8 * 64; p += blockDim.x) {
+        const int lane = p & 63, fs = p >> 6, s = fs & 7, rb = fs >> 3;
+        const int j = rb * 32 + (lane & 31);
+        const int c0 = 16 * s + (lane >> 5) * 8;
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = U[(c0 + e) * R + j];
+        u32x4 hi, lo;
+        split8(x, hi, lo);
+        ufr[((rb * 8 + s) * 2 + 0) * 64 + lane] = hi;
+        ufr[((rb * 8 + s) * 2 + 1) * 64 + lane] = lo;
+    }
+    if (nqb > 0) {
+        const u32x4 *src = qfrag + slice * static_cast<int64_t>(nqb) * 16 * 64;
+        for (int p = threadIdx.x; p < nqb * 16 * 64; p += blockDim.x) qfr[p] = src[p];
+    }
+    __syncthreads();
+
+    const int64_t t_begin = split * sl.per_split;
+    const int64_t t_end = min(sl.S, t_begin + sl.per_split);
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int col = lane & 31, khalf = lane >> 5;
+    const u32x4 *xrows = reinterpret_cast<const u32x4 *>(X + slice * sl.S_stride * kHeadDim);
+    float *xt = Xt + slice * sl.S_stride * R;
+
+    for (int64_t t0 = t_begin + wave * 64; t0 < t_end; t0 += (blockDim.x / 64) * 64) {
+        u32x4 b[2][8];
+#pragma unroll
+        for (int hb = 0; hb < 2; ++hb) {
+            const int64_t tok = t0 + hb * 32 + col;
+            const bool ok = tok < t_end;
+            const u32x4 *row = xrows + (ok ? tok : 0) * 16;
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+                b[hb][s] = row[2 * s + khalf];
+                if (!ok) b[hb][s] = u32x4{0u, 0u, 0u, 0u};
+            }
+        }
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb) {
+            f32x16 a0 = {}, a1 = {};
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+                const u32x4 fh = ufr[((rb * 8 + s) * 2 + 0) * 64 + lane];
+                const u32x4 fl = ufr[((rb * 8 + s) * 2 + 1) * 64 + lane];
+                a0 = mfma32x32x16(fh, b[0][s], a0);
+                a1 = mfma32x32x16(fh, b[1][s], a1);
+                a0 = mfma32x32x16(fl, b[0][s], a0);
+                a1 = mfma32x32x16(fl, b[1][s], a1);
+            }
+#pragma unroll
+            for (int hb = 0; hb < 2; ++hb) {
+                const int64_t tok = t0 + hb * 32 + col;
+                if (tok < t_end) {
+                    const f32x16 &a = hb ? a1 : a0;
+                    float *dst = xt + tok * R + rb * 32 + khalf * 4;
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        *reinterpret_cast<float4 *>(dst + q * 8) =
+                            make_float4(a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]);
+                }
+            }
+        }
+        if (nqb > 0) {
+            float e0 = 0.f, e1 = 0.f;
+            for (int qb = 0; qb < nqb; ++qb) {
+                f32x16 a0 = {}, a1 = {};
+#pragma unroll
+                for (int s = 0; s < 8; ++s) {
+                    const u32x4 fh = qfr[((qb * 8 + s) * 2 + 0) * 64 + lane];
+                    const u32x4 fl = qfr[((qb * 8 + s) * 2 + 1) * 64 + lane];
+                    a0 = mfma32x32x16(fh, b[0][s], a0);
+                    a1 = mfma32x32x16(fh, b[1][s], a1);
+                    a0 = mfma32x32x16(fl, b[0][s], a0);
+                    a1 = mfma32x32x16(fl, b[1][s], a1);
+                }
+#pragma unroll
+                for (int r = 0; r < 16; ++r) {
+                    e0 += fabsf(a0[r]);
+                    e1 += fabsf(a1[r]);
+                }
+            }
+            e0 += __shfl_xor(e0, 32);
+            e1 += __shfl_xor(e1, 32);
+            if (khalf == 0) {
+                float *er = err + slice * sl.S_stride;
+                if (t0 + col < t_end) er[t0 + col] = e0;
+                if (t0 + 32 + col < t_end) er[t0 + 32 + col] = e1;
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------- reconstruct
+
+// One block per (slice, token range); 4 waves; each wave 32 tokens per step.
+// X^^T[c][t] = sum_j U[c][j] X~[t][j]: A = U (channel rows, hi/lo in LDS),
+// B = X~^T split hi/lo in registers; hi*hi + lo*hi + hi*lo.
+template <int NRB>
+__global__ __launch_bounds__(256) void reconstruct_kernel(const float *__restrict__ Xt,
+                                                          const float *__restrict__ Ubase,
+                                                          Slices sl, float *__restrict__ Xh) {
+    constexpr int R = 32 * NRB;
+    constexpr int KS = R / 16;  // k-steps
+    __shared__ u32x4 ufr[4 * KS * 2 * 64];
+
+    const int64_t slice = blockIdx.x / sl.nsplit;
+    const int64_t split = blockIdx.x % sl.nsplit;
+    const int64_t h = slice % sl.Hkv;
+    const int64_t l = slice / (sl.Hkv * sl.B);
+    const float *U = Ubase + (l * sl.Hkv + h) * kHeadDim * R;
+
+    for (int p = threadIdx.x; p < 4 * KS * 64; p += blockDim.x) {
+        const int lane = p & 63, fs = p >> 6, s = fs % KS, cb = fs / KS;
+        const int c = cb * 32 + (lane & 31);
+        const int j0 = 16 * s + (lane >> 5) * 8;
+        float x[8];
+        const float4 *src = reinterpret_cast<const float4 *>(U + c * R + j0);
+        const float4 u0 = src[0], u1 = src[1];
+        x[0] = u0.x; x[1] = u0.y; x[2] = u0.z; x[3] = u0.w;
+        x[4] = u1.x; x[5] = u1.y; x[6] = u1.z; x[7] = u1.w;
+        u32x4 hi, lo;
+        split8(x, hi, lo);
+        ufr[((cb * KS + s) * 2 + 0) * 64 + lane] = hi;
+        ufr[((cb * KS + s) * 2 + 1) * 64 + lane] = lo;
+    }
+    __syncthreads();
+
+    const int64_t t_begin = split * sl.per_split;
+    const int64_t t_end = min(sl.S, t_begin + sl.per_split);
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int col = lane & 31, khalf = lane >> 5;
+    const float *xt = Xt + slice * sl.S_stride * R;
+    float *xh = Xh + slice * sl.S_stride * kHeadDim;
+
+    for (int64_t t0 = t_begin + wave * 32; t0 < t_end; t0 += (blockDim.x / 64) * 32) {
+        const int64_t tok = t0 + col;
+        const bool ok = tok < t_end;
+        u32x4 bh[KS], bl[KS];
+#pragma unroll
+        for (int s = 0; s < KS; ++s) {
+            float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+            if (ok) {
+                const float4 *src = reinterpret_cast<const float4 *>(xt + tok * R + 16 * s + khalf * 8);
+                const float4 v0 = src[0], v1 = src[1];
+                x[0] = v0.x; x[1] = v0.y; x[2] = v0.z; x[3] = v0.w;
+                x[4] = v1.x; x[5] = v1.y; x[6] = v1.z; x[7] = v1.w;
+            }
+            split8(x, bh[s], bl[s]);
+        }
+#pragma unroll
+        for (int cb = 0; cb < 4; ++cb) {
+            f32x16 acc = {};
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                const u32x4 ah = ufr[((cb * KS + s) * 2 + 0) * 64 + lane];
+                const u32x4 al = ufr[((cb * KS + s) * 2 + 1) * 64 + lane];
+                acc = mfma32x32x16(ah, bh[s], acc);
+                acc = mfma32x32x16(al, bh[s], acc);
+                acc = mfma32x32x16(ah, bl[s], acc);
+            }
+            if (ok) {
+                float *dst = xh + tok * kHeadDim + cb * 32 + khalf * 4;
+#pragma unroll
+                for (int q = 0; q < 4; ++q)
+                    *reinterpret_cast<float4 *>(dst + q * 8) =
+                        make_float4(acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]);
+            }
+        }
+    }
+}
+
+// Anchor rows back into X^: 16 lanes per row, bf16 widened exactly.
+__global__ __launch_bounds__(256) void anchor_scatter_kernel(const int32_t *__restrict__ idx,
+                                                             const uint16_t *__restrict__ rows,
+                                                             int64_t k, int64_t blocks_per_slice,
+                                                             int64_t S, int64_t S_stride,
+                                                             float *__restrict__ Xh) {
+    const int64_t g = blockIdx.x / blocks_per_slice;
+    const int64_t i = (blockIdx.x % blocks_per_slice) * 16 + (threadIdx.x >> 4);
+    const int lane16 = threadIdx.x & 15;
+    if (i >= k) return;
+    const int64_t t = idx[g * k + i];
+    if (t < 0 || t >= S) return;  // documented precondition; never write outside the slice
+    const uint4 v = reinterpret_cast<const uint4 *>(rows + (g * k + i) * kHeadDim)[lane16];
+    float4 *dst = reinterpret_cast<float4 *>(Xh + (g * S_stride + t) * kHeadDim + lane16 * 8);
+    dst[0] = make_float4(bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y));
+    dst[1] = make_float4(bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w));
+}
+
+// ------------------------------------------------------------------- host
+
+bool rank_ok(int64_t R) { return R == 32 || R == 64 || R == 96 || R == 128; }
+
+kvc_status check_dims(const kvc_dims *d, bool need_q) {
+    if (!d) return KVC_ERR_INVALID_ARGUMENT;
+    if (d->L < 0 || d->B < 0 || d->H_kv <= 0 || d->S < 0 || d->D <= 0 || d->R <= 0)
+        return KVC_ERR_INVALID_ARGUMENT;
+    if (d->S_stride != 0 && d->S_stride < d->S) return KVC_ERR_INVALID_ARGUMENT;
+    if (need_q && (d->H_q <= 0 || d->W_q <= 0 || d->H_q % d->H_kv != 0))
+        return KVC_ERR_INVALID_ARGUMENT;
+    if (d->R > d->D) return KVC_ERR_INVALID_ARGUMENT;
+    if (d->D != kHeadDim || !rank_ok(d->R)) return KVC_ERR_UNSUPPORTED;
+    if (need_q && (d->H_q / d->H_kv) * d->W_q > 128) return KVC_ERR_UNSUPPORTED;
+    if (d->S > INT32_MAX) return KVC_ERR_UNSUPPORTED;
+    return KVC_OK;
+}
+
+int64_t stride_of(const kvc_dims *d) { return d->S_stride ? d->S_stride : d->S; }
+
+Slices make_slices(const kvc_dims *d, int64_t tokens_per_step) {
+    Slices sl;
+    sl.B = d->B;
+    sl.Hkv = d->H_kv;
+    sl.S = d->S;
+    sl.S_stride = stride_of(d);
+    const int64_t G = d->L * d->B * d->H_kv;
+    // aim at >= 1024 blocks in flight, never below one step of tokens per block
+    int64_t nsplit = G > 0 ? (1024 + G - 1) / G : 1;
+    const int64_t max_split = (d->S + tokens_per_step - 1) / tokens_per_step;
+    if (nsplit > max_split) nsplit = max_split;
+    if (nsplit < 1) nsplit = 1;
+    int64_t per = (d->S + nsplit - 1) / nsplit;
+    per = (per + 63) / 64 * 64;
+    sl.nsplit = nsplit;
+    sl.per_split = per > 0 ? per : 64;
+    return sl;
+}
+
+template <class Ws>
+void compress_ws_layout(Ws &ws, const kvc_dims *d, bool with_q) {
+    if (with_q) {
+        const int64_t G = d->L * d->B * d->H_kv;
+        const int64_t nq = (d->H_q / d->H_kv) * d->W_q;
+        const int64_t nqb = (nq + 31) / 32;
+        ws.template take<u32x4>(static_cast<size_t>(G * nqb * 16 * 64));
+    }
+}
+
+template <int NRB>
+kvc_status launch_project(const uint16_t *X, const float *U, const u32x4 *qfrag, int nqb,
+                          const Slices &sl, int64_t G, float *Xt, float *err, hipStream_t stream) {
+    const size_t lds = static_cast<size_t>(NRB + nqb) * 16 * kFragBytes;
+    static bool attr_set = false;
+    if (!attr_set) {
+        if (hipFuncSetAttribute(reinterpret_cast<const void *>(&project_kernel<NRB>),
+                                hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) != hipSuccess)
+            return KVC_ERR_HIP;
+        attr_set = true;
+    }
+    const int64_t blocks = G * sl.nsplit;
+    if (blocks > INT32_MAX) return KVC_ERR_UNSUPPORTED;
+    hipLaunchKernelGGL(project_kernel<NRB>, dim3(static_cast<unsigned>(blocks)), dim3(512), lds,
+                       stream, X, U, qfrag, nqb, sl, Xt, err);
+    return launch_status();
+}
+
+kvc_status project_dispatch(int64_t R, const uint16_t *X, const float *U, const u32x4 *qfrag,
+                            int nqb, const Slices &sl, int64_t G, float *Xt, float *err,
+                            hipStream_t stream) {
+    switch (R) {
+        case 32: return launch_project<1>(X, U, qfrag, nqb, sl, G, Xt, err, stream);
+        case 64: return launch_project<2>(X, U, qfrag, nqb, sl, G, Xt, err, stream);
+        case 96: return launch_project<3>(X, U, qfrag, nqb, sl, G, Xt, err, stream);
+        case 128: return launch_project<4>(X, U, qfrag, nqb, sl, G, Xt, err, stream);
+    }
+    return KVC_ERR_UNSUPPORTED;
+}
+
+template <int NRB>
+kvc_status launch_reconstruct(const float *Xt, const float *U, const Slices &sl, int64_t G,
+                              float *Xh, hipStream_t stream) {
+    const int64_t blocks = G * sl.nsplit;
+    if (blocks > INT32_MAX) return KVC_ERR_UNSUPPORTED;
+    hipLaunchKernelGGL(reconstruct_kernel<NRB>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
+                       stream, Xt, U, sl, Xh);
+    return launch_status();
+}
+
+}  // namespace
+
+size_t compress_workspace_bytes(const kvc_dims *d) {
+    if (!d || check_dims(d, false) != KVC_OK) return 0;
+    const bool with_q = d->H_q > 0 && d->W_q > 0 && d->H_q % d->H_kv == 0 &&
+                        (d->H_q / d->H_kv) * d->W_q <= 128;
+    WsSizer sz;
+    compress_ws_layout(sz, d, with_q);
+    return sz.bytes();
+}
+
+size_t reconstruct_workspace_bytes(const kvc_dims *) { return 0; }
+
+}  // namespace kvc
+
+extern "C" kvc_status kvc_lowrank_compress(const kvc_dims *d, const uint16_t *K, const uint16_t *V,
+                                           const uint16_t *Q_win, const float *U_k,
+                                           const float *U_v, float *K_tilde, float *V_tilde,
+                                           float *err, void *ws, size_t ws_bytes,
+                                           hipStream_t stream) {
+    using namespace kvc;
+    const bool with_q = Q_win != nullptr;
+    kvc_status st = check_dims(d, with_q);
+    if (st != KVC_OK) return st;
+    if ((Q_win == nullptr) != (err == nullptr)) return KVC_ERR_INVALID_ARGUMENT;
+    if ((V == nullptr) != (V_tilde == nullptr) || (V && !U_v)) return KVC_ERR_INVALID_ARGUMENT;
+    const int64_t G = d->L * d->B * d->H_kv;
+    if (G == 0 || d->S == 0) return KVC_OK;
+    if (!K || !U_k || !K_tilde) return KVC_ERR_INVALID_ARGUMENT;
+    if (!aligned(K, 16) || !aligned(U_k, 16) || !aligned(K_tilde, 16) ||
+        (V && (!aligned(V, 16) || !aligned(U_v, 16) || !aligned(V_tilde, 16))) ||
+        (with_q && (!aligned(Q_win, 16) || !aligned(err, 4))))
+        return KVC_ERR_INVALID_ARGUMENT;
+    WsSizer sz;
+    compress_ws_layout(sz, d, with_q);
+    if (sz.bytes() > 0 && (!ws || !aligned(ws, kWsAlign))) return KVC_ERR_INVALID_ARGUMENT;
+    if (ws_bytes < sz.bytes()) return KVC_ERR_WORKSPACE_TOO_SMALL;
+
+    const Slices sl = make_slices(d, 512);
+    int nqb = 0;
+    u32x4 *qfrag = nullptr;
+    if (with_q) {
+        WsCursor cur(ws);
+        const int64_t nq = (d->H_q / d->H_kv) * d->W_q;
+        nqb = static_cast<int>((nq + 31) / 32);
+        qfrag = cur.take<u32x4>(static_cast<size_t>(G * nqb * 16 * 64));
+        const double scale = 1.0 / (static_cast<double>(nq) * sqrt(static_cast<double>(d->D)));
+        static bool attr_set = false;
+        if (!attr_set) {
+            if (hipFuncSetAttribute(reinterpret_cast<const void *>(&prep_query_kernel),
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) !=
+                hipSuccess)
+                return KVC_ERR_HIP;
+            attr_set = true;
+        }
+        if (G > INT32_MAX) return KVC_ERR_UNSUPPORTED;
+        hipLaunchKernelGGL(prep_query_kernel, dim3(static_cast<unsigned>(G)), dim3(256),
+                           static_cast<size_t>(128 * d->R) * sizeof(double), stream, Q_win, U_k,
+                           d->B, d->H_kv, d->H_q, d->W_q, static_cast<int>(d->R),
+                           static_cast<int>(nq), nqb, scale, qfrag);
+        if ((st = launch_status()) != KVC_OK) return st;
+    }
+    st = project_dispatch(d->R, K, U_k, qfrag, nqb, sl, G, K_tilde, err, stream);
+    if (st != KVC_OK) return st;
+    if (V) st = project_dispatch(d->R, V, U_v, nullptr, 0, sl, G, V_tilde, nullptr, stream);
+    return st;
+}
+
+extern "C" kvc_status kvc_reconstruct(const kvc_dims *d, const float *X_tilde, const float *U,
+                                      const int32_t *anchor_idx, const uint16_t *anchor_rows,
+                                      int64_t k, float *X_hat, void *ws, size_t ws_bytes,
+                                      hipStream_t stream) {
+    using namespace kvc;
+    (void)ws;
+    (void)ws_bytes;
+    kvc_status st = check_dims(d, false);
+    if (st != KVC_OK) return st;
+    if (k < 0 || k > d->S) return KVC_ERR_INVALID_ARGUMENT;
+    if ((k > 0) && (!anchor_idx || !anchor_rows)) return KVC_ERR_INVALID_ARGUMENT;
+    const int64_t G = d->L * d->B * d->H_kv;
+    if (G == 0 || d->S == 0) return KVC_OK;
+    if (!X_tilde || !U || !X_hat || !aligned(X_tilde, 16) || !aligned(U, 16) || !aligned(X_hat, 16))
+        return KVC_ERR_INVALID_ARGUMENT;
+    if (k > 0 && (!aligned(anchor_idx, 4) || !aligned(anchor_rows, 16)))
+        return KVC_ERR_INVALID_ARGUMENT;
+    const Slices sl = make_slices(d, 128);
+    switch (d->R) {
+        case 32: st = launch_reconstruct<1>(X_tilde, U, sl, G, X_hat, stream); break;
+        case 64: st = launch_reconstruct<2>(X_tilde, U, sl, G, X_hat, stream); break;
+        case 96: st = launch_reconstruct<3>(X_tilde, U, sl, G, X_hat, stream); break;
+        case 128: st = launch_reconstruct<4>(X_tilde, U, sl, G, X_hat, stream); break;
+        default: return KVC_ERR_UNSUPPORTED;
+    }
+    if (st != KVC_OK || k == 0) return st;
+    const int64_t bps = (k + 15) / 16;
+    if (G * bps > INT32_MAX) return KVC_ERR_UNSUPPORTED;
+    hipLaunchKernelGGL(anchor_scatter_kernel, dim3(static_cast<unsigned>(G * bps)), dim3(256), 0,
+                       stream, anchor_idx, anchor_rows, k, bps, d->S, sl.S_stride, X_hat);
+    return launch_status();
+}

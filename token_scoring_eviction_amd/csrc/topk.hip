@@ -1,0 +1,216 @@
+// Retention and compaction: per slice, the k largest fp32 scores (equal
+// scores: lower token index first), their indices in ascending order, and a
+// bit-exact gather of the retained K and V rows.  ManifoldKV keeps the keys
+// farthest from the centroid ("ManifoldKV ...", abstract and lay summary);
+// OjaKV keeps the top-k error-score tokens at full rank ("OjaKV ...", method
+// details).
+//
+// select_compact: one 1024-thread workgroup per slice.
+//   - scores are mapped to order-preserving 32-bit keys;
+//   - radix select, 8 bits per pass from the top: per-wave LDS histograms of
+//     the keys that still match the prefix, then a 256-bin suffix scan finds
+//     the digit holding the k-th largest key; after 4 passes the threshold
+//     key T is exact and `need` = how many keys equal to T are kept;
+//   - one ordered pass in 4096-key tiles: a packed (greater, equal) count
+//     scan gives every kept key its output slot, equal keys taken lowest
+//     index first until `need` are taken.
+// gather_rows: 16 lanes per 256-byte row, 16-byte loads and stores.
+#include "kvc_internal.h"
+
+namespace kvc {
+namespace {
+
+constexpr int kSelThreads = 1024;
+constexpr int kSelWaves = kSelThreads / 64;
+constexpr int kPerThread = 4;
+constexpr int kTile = kSelThreads * kPerThread;
+
+// Inclusive scan over the 1024 threads of the block; returns the exclusive
+// prefix and writes the block total to *total.  `wtot` holds kSelWaves words.
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *wtot,
+                                                         uint32_t *total) {
+    const int lane = threadIdx.x & 63;
+    const int wave = threadIdx.x >> 6;
+    uint32_t x = v;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+        uint32_t y = __shfl_up(x, d, 64);
+        if (lane >= d) x += y;
+    }
+    if (lane == 63) wtot[wave] = x;
+    __syncthreads();
+    if (wave == 0) {
+        uint32_t w = lane < kSelWaves ? wtot[lane] : 0u;
+#pragma unroll
+        for (int d = 1; d < kSelWaves; d <<= 1) {
+            uint32_t y = __shfl_up(w, d, 64);
+            if (lane >= d) w += y;
+        }
+        if (lane < kSelWaves) wtot[kSelWaves + lane] = w;  // inclusive wave prefix
+    }
+    __syncthreads();
+    const uint32_t wave_excl = wave ? wtot[kSelWaves + wave - 1] : 0u;
+    *total = wtot[2 * kSelWaves - 1];
+    const uint32_t excl = wave_excl + x - v;
+    __syncthreads();  // wtot may be reused by the caller's next scan
+    return excl;
+}
+
+__global__ __launch_bounds__(kSelThreads) void select_compact(const float *__restrict__ scores,
+                                                              int64_t S, int64_t s_stride,
+                                                              int64_t k,
+                                                              int32_t *__restrict__ idx_out) {
+    const int64_t g = blockIdx.x;
+    const float *s = scores + g * s_stride;
+    int32_t *out = idx_out + g * k;
+
+    __shared__ uint32_t hist[kSelWaves][256];
+    __shared__ uint32_t suffix[257];
+    __shared__ uint32_t sel[2];
+    __shared__ uint32_t wtot[2 * kSelWaves];
+
+    const int wave = threadIdx.x >> 6;
+    uint32_t prefix = 0, mask = 0;
+    uint32_t remaining = static_cast<uint32_t>(k);
+
+    for (int pass = 0; pass < 4; ++pass) {
+        const int shift = 24 - 8 * pass;
+        for (int i = threadIdx.x; i < kSelWaves * 256; i += kSelThreads) (&hist[0][0])[i] = 0u;
+        __syncthreads();
+        for (int64_t i = threadIdx.x; i < S; i += kSelThreads) {
+            const uint32_t key = order_key(s[i]);
+            if ((key & mask) == prefix) atomicAdd(&hist[wave][(key >> shift) & 255u], 1u);
+        }
+        __syncthreads();
+        if (threadIdx.x < 256) {
+            uint32_t c = 0;
+#pragma unroll
+            for (int w = 0; w < kSelWaves; ++w) c += hist[w][threadIdx.x];
+            suffix[threadIdx.x] = c;
+        }
+        if (threadIdx.x == 0) suffix[256] = 0u;
+        __syncthreads();
+        // suffix sums over bins: suffix[b] = count of matching keys with digit >= b
+        for (int d = 1; d < 256; d <<= 1) {
+            uint32_t add = 0;
+            if (threadIdx.x < 256 && threadIdx.x + d < 256) add = suffix[threadIdx.x + d];
+            __syncthreads();
+            if (threadIdx.x < 256) suffix[threadIdx.x] += add;
+            __syncthreads();
+        }
+        if (threadIdx.x < 256) {
+            const uint32_t here = suffix[threadIdx.x], above = suffix[threadIdx.x + 1];
+            if (here >= remaining && above < remaining) {
+                sel[0] = threadIdx.x;
+                sel[1] = above;
+            }
+        }
+        __syncthreads();
+        const uint32_t digit = sel[0];
+        remaining -= sel[1];
+        prefix |= digit << shift;
+        mask |= 255u << shift;
+        __syncthreads();
+    }
+    const uint32_t T = prefix;      // key of the k-th largest score
+    const uint32_t need = remaining;  // keys equal to T that are kept (>= 1)
+
+    uint32_t out_pos = 0;  // kept so far (uniform across the block)
+    uint32_t eq_seen = 0;  // keys equal to T seen so far
+    for (int64_t base = 0; base < S; base += kTile) {
+        const int64_t i0 = base + static_cast<int64_t>(threadIdx.x) * kPerThread;
+        uint32_t keys[kPerThread];
+        uint32_t n_gt = 0, n_eq = 0;
+#pragma unroll
+        for (int j = 0; j < kPerThread; ++j) {
+            const int64_t i = i0 + j;
+            keys[j] = i < S ? order_key(s[i]) : 0u;
+            n_gt += (i < S && keys[j] > T);
+            n_eq += (i < S && keys[j] == T);
+        }
+        uint32_t tot;
+        const uint32_t excl = block_exclusive_scan((n_gt << 16) | n_eq, wtot, &tot);
+        const uint32_t gt_before = excl >> 16, eq_before = excl & 0xffffu;
+        const uint32_t tile_gt = tot >> 16, tile_eq = tot & 0xffffu;
+        uint32_t pos = out_pos + gt_before + (min(eq_seen + eq_before, need) - min(eq_seen, need));
+        uint32_t eq_rank = eq_seen + eq_before;
+#pragma unroll
+        for (int j = 0; j < kPerThread; ++j) {
+            const int64_t i = i0 + j;
+            if (i >= S) break;
+            // pos < k holds by construction (exactly k keys are kept); the
+            // test only keeps a write inside the slice's output row regardless
+            if (keys[j] > T) {
+                if (pos < k) out[pos] = static_cast<int32_t>(i);
+                ++pos;
+            } else if (keys[j] == T) {
+                if (eq_rank < need) {
+                    if (pos < k) out[pos] = static_cast<int32_t>(i);
+                    ++pos;
+                }
+                ++eq_rank;
+            }
+        }
+        out_pos += tile_gt + (min(eq_seen + tile_eq, need) - min(eq_seen, need));
+        eq_seen += tile_eq;
+    }
+}
+
+constexpr int kGatherThreads = 256;
+constexpr int kGatherRows = 64;  // rows per block
+
+__global__ __launch_bounds__(kGatherThreads) void gather_rows(
+    const uint16_t *__restrict__ K, const uint16_t *__restrict__ V, int64_t S, int64_t s_stride,
+    const int32_t *__restrict__ idx, int64_t k, int64_t blocks_per_slice,
+    uint16_t *__restrict__ K_out, uint16_t *__restrict__ V_out) {
+    const int64_t g = blockIdx.x / blocks_per_slice;
+    const int64_t r0 = (blockIdx.x % blocks_per_slice) * kGatherRows;
+    const int lane16 = threadIdx.x & 15;
+    const int rsub = threadIdx.x >> 4;  // 0..15
+#pragma unroll
+    for (int r = 0; r < kGatherRows / 16; ++r) {
+        const int64_t i = r0 + r * 16 + rsub;
+        if (i < k) {
+            const int64_t t = idx[g * k + i];
+            if (t < 0 || t >= S) continue;  // indices come from select_compact; never read outside
+            const int64_t src = (g * s_stride + t) * (kHeadDim / 8) + lane16;
+            const int64_t dst = (g * k + i) * (kHeadDim / 8) + lane16;
+            if (K) reinterpret_cast<uint4 *>(K_out)[dst] = reinterpret_cast<const uint4 *>(K)[src];
+            if (V) reinterpret_cast<uint4 *>(V_out)[dst] = reinterpret_cast<const uint4 *>(V)[src];
+        }
+    }
+}
+
+}  // namespace
+
+size_t topk_workspace_bytes(int64_t, int64_t, int64_t) { return 0; }
+
+}  // namespace kvc
+
+extern "C" kvc_status kvc_topk_compact(const float *scores, int64_t G, int64_t S, int64_t s_stride,
+                                       int64_t k, const uint16_t *K, const uint16_t *V, int32_t D,
+                                       int32_t *idx_out, uint16_t *K_out, uint16_t *V_out,
+                                       void *ws, size_t ws_bytes, hipStream_t stream) {
+    using namespace kvc;
+    (void)ws;
+    (void)ws_bytes;
+    if (G < 0 || S < 0 || k < 0 || k > S || s_stride < S) return KVC_ERR_INVALID_ARGUMENT;
+    if ((K == nullptr) != (K_out == nullptr) || (V == nullptr) != (V_out == nullptr))
+        return KVC_ERR_INVALID_ARGUMENT;
+    if ((K || V) && D != kHeadDim) return D <= 0 ? KVC_ERR_INVALID_ARGUMENT : KVC_ERR_UNSUPPORTED;
+    if (S > INT32_MAX || G > INT32_MAX) return KVC_ERR_UNSUPPORTED;
+    if (G == 0 || k == 0) return KVC_OK;
+    if (!scores || !idx_out || !aligned(scores, 4) || !aligned(idx_out, 4))
+        return KVC_ERR_INVALID_ARGUMENT;
+    if ((K && (!aligned(K, 16) || !aligned(K_out, 16))) || (V && (!aligned(V, 16) || !aligned(V_out, 16))))
+        return KVC_ERR_INVALID_ARGUMENT;
+    hipLaunchKernelGGL(select_compact, dim3(static_cast<unsigned>(G)), dim3(kSelThreads), 0, stream,
+                       scores, S, s_stride, k, idx_out);
+    if (K || V) {
+        const int64_t bps = (k + kGatherRows - 1) / kGatherRows;
+        if (G * bps > INT32_MAX) return KVC_ERR_UNSUPPORTED;
+        hipLaunchKernelGGL(gather_rows, dim3(static_cast<unsigned>(G * bps)), dim3(kGatherThreads), 0,
+                           stream, K, V, S, s_stride, idx_out, k, bps, K_out, V_out);
+    }
+    return launch_status();
+}

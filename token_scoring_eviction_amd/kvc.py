@@ -1,0 +1,220 @@
+"""ctypes binding of libkvc's C ABI (include/kvc.h), one Python function per
+entry point, same names.  Only argument marshalling happens here: shapes are
+read off torch tensors, the workspace is sized with kvc_workspace_bytes and
+taken from a per-device cache, and the current torch stream is passed down.
+Every step of the computation runs in the HIP library; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libkvc.so")
+
+OK, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_WORKSPACE_TOO_SMALL, ERR_HIP = range(5)
+OP_SCORE_L2, OP_SCORE_L2_WINDOWED, OP_TOPK_COMPACT, OP_LOWRANK_COMPRESS, OP_OJA_UPDATE, \
+    OP_RECONSTRUCT = range(6)
+
+EXPORTED = ("kvc_abi_version", "kvc_status_str", "kvc_workspace_bytes", "kvc_score_l2",
+            "kvc_score_l2_windowed", "kvc_topk_compact", "kvc_lowrank_compress", "kvc_oja_update",
+            "kvc_reconstruct")
+
+
+class KvcError(RuntimeError):
+    def __init__(self, fn, status, text):
+        super().__init__("%s failed: %s (status %d)" % (fn, text, status))
+        self.status = status
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int64) for n in ("L", "B", "H_kv", "H_q", "S", "S_stride", "D", "R", "W_q")]
+
+
+_lib = None
+_lock = threading.Lock()
+_ws = {}
+
+
+def load(path: str = LIB_PATH):
+    """Load libkvc.so (built by token_scoring_eviction_amd.build); raises if absent."""
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(path):
+                raise RuntimeError("libkvc.so not built: run `python -m token_scoring_eviction_amd.build`")
+            lib = ctypes.CDLL(path)
+            P, I64, I32, SZ = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+            DP = ctypes.POINTER(Dims)
+            lib.kvc_abi_version.argtypes, lib.kvc_abi_version.restype = [], ctypes.c_int
+            lib.kvc_status_str.argtypes, lib.kvc_status_str.restype = [ctypes.c_int], ctypes.c_char_p
+            lib.kvc_workspace_bytes.argtypes, lib.kvc_workspace_bytes.restype = [ctypes.c_int, DP, I64, I64], SZ
+            sigs = {
+                "kvc_score_l2": [P, I64, I64, I32, P, P, P, SZ, P],
+                "kvc_score_l2_windowed": [P, I64, I64, I32, I64, P, P, P, SZ, P],
+                "kvc_topk_compact": [P, I64, I64, I64, I64, P, P, I32, P, P, P, P, SZ, P],
+                "kvc_lowrank_compress": [DP, P, P, P, P, P, P, P, P, P, SZ, P],
+                "kvc_oja_update": [DP, P, P, I32, ctypes.c_float, P, SZ, P],
+                "kvc_reconstruct": [DP, P, P, P, P, I64, P, P, SZ, P],
+            }
+            for name, a in sigs.items():
+                fn = getattr(lib, name)
+                fn.argtypes, fn.restype = a, ctypes.c_int
+            _lib = lib
+    return _lib
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _check(name, st):
+    if st != OK:
+        raise KvcError(name, st, load().kvc_status_str(st).decode())
+
+
+def workspace(nbytes: int, device=None):
+    """A cached uint8 device buffer of at least nbytes (None when nbytes == 0)."""
+    if nbytes == 0:
+        return None
+    dev = torch.device("cuda", torch.cuda.current_device() if device is None else device)
+    buf = _ws.get(dev)
+    if buf is None or buf.numel() < nbytes:
+        buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+        _ws[dev] = buf
+    return buf
+
+
+def workspace_bytes(op, dims: Dims, k=0, W=0) -> int:
+    return int(load().kvc_workspace_bytes(op, ctypes.byref(dims), k, W))
+
+
+def _bits(t):
+    if t.dtype != torch.bfloat16:
+        raise TypeError("expected a bfloat16 tensor, got %s" % t.dtype)
+    return t
+
+
+def _dims(L, B, H_kv, H_q, S, S_stride, D, R, W_q):
+    return Dims(L, B, H_kv, H_q, S, S_stride, D, R, W_q)
+
+
+# ---------------------------------------------------------------- entry points
+
+def kvc_score_l2(K, scores=None, centroid=None):
+    """K: bf16 [G, S, D] -> scores fp32 [G, S] (and centroid fp32 [G, D] if given)."""
+    lib = load()
+    G, S, D = K.shape
+    if scores is None:
+        scores = torch.empty((G, S), dtype=torch.float32, device=K.device)
+    nb = workspace_bytes(OP_SCORE_L2, _dims(1, 1, G, 0, S, 0, D, 0, 0))
+    ws = workspace(nb, K.device.index)
+    _check("kvc_score_l2", lib.kvc_score_l2(_ptr(_bits(K)), G, S, D, _ptr(scores), _ptr(centroid),
+                                            _ptr(ws), nb, _stream()))
+    return scores
+
+
+def kvc_score_l2_windowed(K, W, scores=None, centroids=None):
+    """K: bf16 [G, S, D], window W -> scores fp32 [G, S]."""
+    lib = load()
+    G, S, D = K.shape
+    if scores is None:
+        scores = torch.empty((G, S), dtype=torch.float32, device=K.device)
+    nb = workspace_bytes(OP_SCORE_L2_WINDOWED, _dims(1, 1, G, 0, S, 0, D, 0, 0), 0, W)
+    ws = workspace(nb, K.device.index)
+    _check("kvc_score_l2_windowed",
+           lib.kvc_score_l2_windowed(_ptr(_bits(K)), G, S, D, W, _ptr(scores), _ptr(centroids),
+                                     _ptr(ws), nb, _stream()))
+    return scores
+
+
+def kvc_topk_compact(scores, k, K=None, V=None, S=None, idx_out=None, K_out=None, V_out=None):
+    """scores: fp32 [G, S_stride]; keeps the k largest of the first S per slice.
+    Returns (idx int32 [G, k], K_out, V_out) (bf16 [G, k, D] or None)."""
+    lib = load()
+    G, stride = scores.shape
+    S = stride if S is None else S
+    dev = scores.device
+    if idx_out is None:
+        idx_out = torch.empty((G, k), dtype=torch.int32, device=dev)
+    D = 0
+    if K is not None:
+        D = K.shape[-1]
+        if K_out is None:
+            K_out = torch.empty((G, k, D), dtype=torch.bfloat16, device=dev)
+    if V is not None:
+        D = V.shape[-1]
+        if V_out is None:
+            V_out = torch.empty((G, k, D), dtype=torch.bfloat16, device=dev)
+    nb = workspace_bytes(OP_TOPK_COMPACT, _dims(1, 1, G, 0, S, 0, D, 0, 0), k)
+    ws = workspace(nb, dev.index)
+    _check("kvc_topk_compact",
+           lib.kvc_topk_compact(_ptr(scores), G, S, stride, k, _ptr(K), _ptr(V), D, _ptr(idx_out),
+                                _ptr(K_out), _ptr(V_out), _ptr(ws), nb, _stream()))
+    return idx_out, K_out, V_out
+
+
+def kvc_lowrank_compress(K, V, Q_win, U_k, U_v, L, B, H_kv, S=None, K_tilde=None, V_tilde=None,
+                         err=None):
+    """K, V: bf16 [L*B*H_kv, S_stride, D]; Q_win: bf16 [L, B, H_q, W_q, D] or None;
+    U_k, U_v: fp32 [L, H_kv, D, R].  Returns (K_tilde, V_tilde, err)."""
+    lib = load()
+    G, stride, D = K.shape
+    S = stride if S is None else S
+    R = U_k.shape[-1]
+    H_q, W_q = (Q_win.shape[2], Q_win.shape[3]) if Q_win is not None else (0, 0)
+    dev = K.device
+    if K_tilde is None:
+        K_tilde = torch.empty((G, stride, R), dtype=torch.float32, device=dev)
+    if V is not None and V_tilde is None:
+        V_tilde = torch.empty((G, stride, R), dtype=torch.float32, device=dev)
+    if Q_win is not None and err is None:
+        err = torch.empty((G, stride), dtype=torch.float32, device=dev)
+    d = _dims(L, B, H_kv, H_q, S, stride, D, R, W_q)
+    nb = workspace_bytes(OP_LOWRANK_COMPRESS, d)
+    ws = workspace(nb, dev.index)
+    _check("kvc_lowrank_compress",
+           lib.kvc_lowrank_compress(ctypes.byref(d), _ptr(K), _ptr(V), _ptr(Q_win), _ptr(U_k),
+                                    _ptr(U_v), _ptr(K_tilde), _ptr(V_tilde), _ptr(err), _ptr(ws),
+                                    nb, _stream()))
+    return K_tilde, V_tilde, err
+
+
+def kvc_oja_update(U, X, pool, eta, L, B, H_kv, N=None):
+    """U: fp32 [L, H_kv, D, R] updated in place; X: bf16 [L*B*H_kv, S_stride, D]."""
+    lib = load()
+    G, stride, D = X.shape
+    N = stride if N is None else N
+    R = U.shape[-1]
+    d = _dims(L, B, H_kv, 0, N, stride, D, R, 0)
+    nb = workspace_bytes(OP_OJA_UPDATE, d, 0, pool)
+    ws = workspace(nb, X.device.index)
+    _check("kvc_oja_update", lib.kvc_oja_update(ctypes.byref(d), _ptr(U), _ptr(X), pool, float(eta),
+                                                _ptr(ws), nb, _stream()))
+    return U
+
+
+def kvc_reconstruct(X_tilde, U, anchor_idx, anchor_rows, L, B, H_kv, S=None, X_hat=None):
+    """X_tilde: fp32 [L*B*H_kv, S_stride, R]; U: fp32 [L, H_kv, D, R];
+    anchor_idx int32 [G, k] / anchor_rows bf16 [G, k, D] or None -> X_hat fp32 [G, S_stride, D]."""
+    lib = load()
+    G, stride, R = X_tilde.shape
+    S = stride if S is None else S
+    D = U.shape[-2]
+    k = 0 if anchor_idx is None else anchor_idx.shape[1]
+    if X_hat is None:
+        X_hat = torch.empty((G, stride, D), dtype=torch.float32, device=X_tilde.device)
+    d = _dims(L, B, H_kv, 0, S, stride, D, R, 0)
+    nb = workspace_bytes(OP_RECONSTRUCT, d, k)
+    ws = workspace(nb, X_tilde.device.index)
+    _check("kvc_reconstruct",
+           lib.kvc_reconstruct(ctypes.byref(d), _ptr(X_tilde), _ptr(U), _ptr(anchor_idx),
+                               _ptr(anchor_rows), k, _ptr(X_hat), _ptr(ws), nb, _stream()))
+    return X_hat

@@ -1,0 +1,102 @@
+"""Host orchestration of the C-ABI calls into the two hot paths (no arithmetic
+here: every step runs in libkvc's HIP kernels).
+
+* ManifoldKV eviction ("ManifoldKV: Training-Free KV Cache Compression via
+  Euclidean Outlier Detection", abstract): score every key by its distance to
+  the (global or windowed) key centroid, keep the `keep` farthest per slice,
+  compact K and V to the kept rows.
+* OjaKV hybrid low-rank loop ("OjaKV: Context-Aware Online Low-Rank KV Cache
+  Compression", method details and appendix A.1): prefill pooled Oja update +
+  QR, projection, error score, top-k full-rank anchors, reconstruction; then
+  decode steps buffered T at a time, each full buffer triggering an unpooled
+  update, re-projection of the whole cache, re-scoring, re-selection of
+  anchors and reconstruction.
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import torch
+
+from . import kvc
+
+
+@dataclass
+class EvictionBuffers:
+    scores: torch.Tensor
+    idx: torch.Tensor
+    K_out: torch.Tensor
+    V_out: torch.Tensor
+
+
+def alloc_eviction(G, S, keep, D=128, device="cuda"):
+    return EvictionBuffers(
+        scores=torch.empty((G, S), dtype=torch.float32, device=device),
+        idx=torch.empty((G, keep), dtype=torch.int32, device=device),
+        K_out=torch.empty((G, keep, D), dtype=torch.bfloat16, device=device),
+        V_out=torch.empty((G, keep, D), dtype=torch.bfloat16, device=device))
+
+
+def manifold_evict(K, V, keep, W=None, buf: EvictionBuffers | None = None):
+    """One ManifoldKV eviction pass over K, V (bf16 [G, S, 128]).  W=None: global
+    centroid; otherwise contiguous windows of W tokens.  Returns the buffers."""
+    G, S, D = K.shape
+    buf = buf or alloc_eviction(G, S, keep, D, K.device)
+    if W is None:
+        kvc.kvc_score_l2(K, scores=buf.scores)
+    else:
+        kvc.kvc_score_l2_windowed(K, W, scores=buf.scores)
+    kvc.kvc_topk_compact(buf.scores, keep, K, V, idx_out=buf.idx, K_out=buf.K_out, V_out=buf.V_out)
+    return buf
+
+
+def anchor_count(S, percent=5):
+    """ceil(percent * S / 100) full-rank anchors."""
+    return -(-percent * S // 100)
+
+
+@dataclass
+class HybridState:
+    """Hybrid cache of one OjaKV pass: K~/V~ for every token, the anchors'
+    indices and full-rank rows, the error scores and the reconstruction."""
+    Kt: torch.Tensor
+    Vt: torch.Tensor
+    err: torch.Tensor
+    idx: torch.Tensor
+    K_anchor: torch.Tensor
+    V_anchor: torch.Tensor
+    Khat: torch.Tensor
+    Vhat: torch.Tensor
+
+
+def alloc_hybrid(G, S_cap, R, D=128, device="cuda", max_anchor=None, with_hat=True):
+    max_anchor = anchor_count(S_cap) if max_anchor is None else max_anchor
+    f32 = dict(dtype=torch.float32, device=device)
+    return HybridState(
+        Kt=torch.empty((G, S_cap, R), **f32), Vt=torch.empty((G, S_cap, R), **f32),
+        err=torch.empty((G, S_cap), **f32),
+        idx=torch.empty((G, max_anchor), dtype=torch.int32, device=device),
+        K_anchor=torch.empty((G, max_anchor, D), dtype=torch.bfloat16, device=device),
+        V_anchor=torch.empty((G, max_anchor, D), dtype=torch.bfloat16, device=device),
+        Khat=torch.empty((G, S_cap, D), **f32) if with_hat else None,
+        Vhat=torch.empty((G, S_cap, D), **f32) if with_hat else None)
+
+
+def hybrid_pass(K, V, Q_win, U_k, U_v, L, B, H_kv, S, st: HybridState, anchor_percent=5,
+                reconstruct=True):
+    """Compress all S tokens, score them, keep ceil(p%) anchors at full rank and
+    (optionally) rebuild K^, V^.  K, V: bf16 [G, S_cap, 128] caches (S <= S_cap)."""
+    G = K.shape[0]
+    k = anchor_count(S, anchor_percent)
+    kvc.kvc_lowrank_compress(K, V, Q_win, U_k, U_v, L, B, H_kv, S=S, K_tilde=st.Kt, V_tilde=st.Vt,
+                             err=st.err)
+    idx = st.idx[:, :k] if k == st.idx.shape[1] else torch.empty((G, k), dtype=torch.int32,
+                                                                   device=K.device)
+    Ka = st.K_anchor[:, :k] if k == st.K_anchor.shape[1] else torch.empty(
+        (G, k, K.shape[2]), dtype=torch.bfloat16, device=K.device)
+    Va = st.V_anchor[:, :k] if k == st.V_anchor.shape[1] else torch.empty_like(Ka)
+    kvc.kvc_topk_compact(st.err, k, K, V, S=S, idx_out=idx, K_out=Ka, V_out=Va)
+    if reconstruct:
+        kvc.kvc_reconstruct(st.Kt, U_k, idx, Ka, L, B, H_kv, S=S, X_hat=st.Khat)
+        kvc.kvc_reconstruct(st.Vt, U_v, idx, Va, L, B, H_kv, S=S, X_hat=st.Vhat)
+    return idx, Ka, Va
