@@ -50,7 +50,7 @@ def test_workspace_sizing():
     assert 0 < a < b
     # compress needs folded query fragments only when a window is given
     assert kvc.workspace_bytes(kvc.OP_LOWRANK_COMPRESS, D(32, 4, 8, 32, 32768, 0, 128, 64, 32)) == \
-        1024 * 4 * 16 * 64 * 16
+        1024 * 4 * 8 * 3 * 64 * 16
     assert kvc.workspace_bytes(kvc.OP_LOWRANK_COMPRESS, D(32, 4, 8, 0, 32768, 0, 128, 64, 0)) == 0
     # invalid or unsupported shapes report 0
     assert kvc.workspace_bytes(kvc.OP_LOWRANK_COMPRESS, D(1, 1, 1, 0, 10, 0, 64, 32, 0)) == 0

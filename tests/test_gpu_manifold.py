@@ -127,3 +127,18 @@ def test_determinism(gpu_lib):
     ib, Kb, _ = gpu_lib.kvc_topk_compact(b, 3000, K, V)
     torch.cuda.synchronize()
     assert torch.equal(a, b) and torch.equal(ia, ib) and torch.equal(Ka.view(torch.int16), Kb.view(torch.int16))
+
+
+@pytest.mark.parametrize("W", [None, 4096, 1000])
+def test_fused_and_three_launch_paths_agree(gpu_lib, monkeypatch, W):
+    # the cooperative single-read path and the three-launch path compute the same scores
+    K, _, _ = synth.manifold_global(4, 1, 8, 12288 + 100, planted=8, seed=3, device=DEV)
+    f = gpu_lib.kvc_score_l2(K) if W is None else gpu_lib.kvc_score_l2_windowed(K, W)
+    f = f.clone()
+    monkeypatch.setenv("KVC_SCORE_UNFUSED", "1")
+    u = gpu_lib.kvc_score_l2(K) if W is None else gpu_lib.kvc_score_l2_windowed(K, W)
+    torch.cuda.synchronize()
+    ora, _ = oracle.score_l2(synth.bf16_bits(K)) if W is None else oracle.score_l2_windowed(synth.bf16_bits(K), W)
+    for x in (f, u):
+        ok, rel, nbad = score_close(x.cpu().numpy(), ora)
+        assert ok, (rel, nbad)

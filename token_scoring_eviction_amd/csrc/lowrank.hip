@@ -54,19 +54,22 @@ __device__ __forceinline__ void split8(const float *x, u32x4 &hi, u32x4 &lo) {
     }
 }
 
-__device__ __forceinline__ void split8_f64(const double *x, u32x4 &hi, u32x4 &lo) {
-    uint32_t h[8], l[8];
+// x (8 fp64) -> three bf16 terms x = t0 + t1 + t2 + O(2^-25 |x|)
+__device__ __forceinline__ void split8x3_f64(const double *x, u32x4 *part) {
+    uint32_t t[3][8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-        h[e] = f32_to_bf16_rne(static_cast<float>(x[e]));
-        const double rest = x[e] - static_cast<double>(__uint_as_float(h[e] << 16));
-        l[e] = f32_to_bf16_rne(static_cast<float>(rest));
+        double rest = x[e];
+#pragma unroll
+        for (int p = 0; p < 3; ++p) {
+            t[p][e] = f32_to_bf16_rne(static_cast<float>(rest));
+            rest -= static_cast<double>(__uint_as_float(t[p][e] << 16));
+        }
     }
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-        hi[q] = h[2 * q] | (h[2 * q + 1] << 16);
-        lo[q] = l[2 * q] | (l[2 * q + 1] << 16);
-    }
+    for (int p = 0; p < 3; ++p)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) part[p][q] = t[p][2 * q] | (t[p][2 * q + 1] << 16);
 }
 
 struct Slices {
@@ -77,9 +80,13 @@ struct Slices {
 
 // ------------------------------------------------------------ compress prep
 
+constexpr int kQParts = 3;  // bf16 terms per folded-query element
+
 // Folded, scaled query fragments of one slice:
 //   Q''[q][c] = scale * (Q[q][c] - sum_j (sum_c' Q[q][c'] U[c'][j]) U[c][j])
-// in fp64, split hi/lo into A-operand fragments [qb][s][hi|lo][lane].
+// in fp64, split into three bf16 terms, as A-operand fragments
+// [qb][s][term][lane].  Three terms keep the score's error at the level of
+// the fp32 accumulation even when |q . r_t| cancels far below ||q|| ||r_t||.
 __global__ __launch_bounds__(256) void prep_query_kernel(const uint16_t *__restrict__ Q,
                                                          const float *__restrict__ Uk, int64_t B,
                                                          int64_t Hkv, int64_t Hq, int64_t Wq,
@@ -106,7 +113,7 @@ __global__ __launch_bounds__(256) void prep_query_kernel(const uint16_t *__restr
         T[q * R + j] = acc;
     }
     __syncthreads();
-    u32x4 *out = qfrag + slice * static_cast<int64_t>(nqb) * 16 * 64;
+    u32x4 *out = qfrag + slice * static_cast<int64_t>(nqb) * 8 * kQParts * 64;
     for (int p = threadIdx.x; p < nqb * 8 * 64; p += blockDim.x) {
         const int lane = p & 63, fs = p >> 6, s = fs & 7, qb = fs >> 3;
         const int q = qb * 32 + (lane & 31);
@@ -126,17 +133,18 @@ __global__ __launch_bounds__(256) void prep_query_kernel(const uint16_t *__restr
 #pragma unroll
             for (int e = 0; e < 8; ++e) x[e] = 0.0;
         }
-        u32x4 hi, lo;
-        split8_f64(x, hi, lo);
-        out[((qb * 8 + s) * 2 + 0) * 64 + lane] = hi;
-        out[((qb * 8 + s) * 2 + 1) * 64 + lane] = lo;
+        u32x4 part[kQParts];
+        split8x3_f64(x, part);
+#pragma unroll
+        for (int t = 0; t < kQParts; ++t) out[((qb * 8 + s) * kQParts + t) * 64 + lane] = part[t];
     }
 }
 
 // --------------------------------------------------------------- compress
 
 // One block per (slice, token range); 8 waves; each wave 64 tokens per step.
-// LDS: U^T fragments [rb][s][hi|lo] (NRB*16 KB), then Q'' fragments (nqb*16 KB).
+// LDS: U^T fragments [rb][s][hi|lo] (NRB*16 KB), then Q'' fragments
+// [qb][s][term] (nqb*24 KB).
 template <int NRB>
 __global__ __launch_bounds__(512) void project_kernel(const uint16_t *__restrict__ X,
                                                       const float *__restrict__ Ubase,
@@ -146,7 +154,7 @@ __global__ __launch_bounds__(512) void project_kernel(const uint16_t *__restrict
     constexpr int R = 32 * NRB;
     extern __shared__ u32x4 lds[];
     u32x4 *ufr = lds;
-    u32x4 *qfr = lds + NRB * 16 * 64;
+    u32x4 *qfr = lds + NRB * 16 * 64;  // after the U^T fragments
 
     const int64_t slice = blockIdx.x / sl.nsplit;
     const int64_t split = blockIdx.x % sl.nsplit;
@@ -167,8 +175,9 @@ __global__ __launch_bounds__(512) void project_kernel(const uint16_t *__restrict
         ufr[((rb * 8 + s) * 2 + 1) * 64 + lane] = lo;
     }
     if (nqb > 0) {
-        const u32x4 *src = qfrag + slice * static_cast<int64_t>(nqb) * 16 * 64;
-        for (int p = threadIdx.x; p < nqb * 16 * 64; p += blockDim.x) qfr[p] = src[p];
+        const int nq4 = nqb * 8 * kQParts * 64;
+        const u32x4 *src = qfrag + slice * static_cast<int64_t>(nq4);
+        for (int p = threadIdx.x; p < nq4; p += blockDim.x) qfr[p] = src[p];
     }
     __syncthreads();
 
@@ -223,12 +232,12 @@ __global__ __launch_bounds__(512) void project_kernel(const uint16_t *__restrict
                 f32x16 a0 = {}, a1 = {};
 #pragma unroll
                 for (int s = 0; s < 8; ++s) {
-                    const u32x4 fh = qfr[((qb * 8 + s) * 2 + 0) * 64 + lane];
-                    const u32x4 fl = qfr[((qb * 8 + s) * 2 + 1) * 64 + lane];
-                    a0 = mfma32x32x16(fh, b[0][s], a0);
-                    a1 = mfma32x32x16(fh, b[1][s], a1);
-                    a0 = mfma32x32x16(fl, b[0][s], a0);
-                    a1 = mfma32x32x16(fl, b[1][s], a1);
+#pragma unroll
+                    for (int t = 0; t < kQParts; ++t) {
+                        const u32x4 f = qfr[((qb * 8 + s) * kQParts + t) * 64 + lane];
+                        a0 = mfma32x32x16(f, b[0][s], a0);
+                        a1 = mfma32x32x16(f, b[1][s], a1);
+                    }
                 }
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
@@ -389,14 +398,14 @@ void compress_ws_layout(Ws &ws, const kvc_dims *d, bool with_q) {
         const int64_t G = d->L * d->B * d->H_kv;
         const int64_t nq = (d->H_q / d->H_kv) * d->W_q;
         const int64_t nqb = (nq + 31) / 32;
-        ws.template take<u32x4>(static_cast<size_t>(G * nqb * 16 * 64));
+        ws.template take<u32x4>(static_cast<size_t>(G * nqb * 8 * kQParts * 64));
     }
 }
 
 template <int NRB>
 kvc_status launch_project(const uint16_t *X, const float *U, const u32x4 *qfrag, int nqb,
                           const Slices &sl, int64_t G, float *Xt, float *err, hipStream_t stream) {
-    const size_t lds = static_cast<size_t>(NRB + nqb) * 16 * kFragBytes;
+    const size_t lds = static_cast<size_t>(NRB * 16 + nqb * 8 * kQParts) * kFragBytes;
     static bool attr_set = false;
     if (!attr_set) {
         if (hipFuncSetAttribute(reinterpret_cast<const void *>(&project_kernel<NRB>),
@@ -478,7 +487,7 @@ extern "C" kvc_status kvc_lowrank_compress(const kvc_dims *d, const uint16_t *K,
         WsCursor cur(ws);
         const int64_t nq = (d->H_q / d->H_kv) * d->W_q;
         nqb = static_cast<int>((nq + 31) / 32);
-        qfrag = cur.take<u32x4>(static_cast<size_t>(G * nqb * 16 * 64));
+        qfrag = cur.take<u32x4>(static_cast<size_t>(G * nqb * 8 * kQParts * 64));
         const double scale = 1.0 / (static_cast<double>(nq) * sqrt(static_cast<double>(d->D)));
         static bool attr_set = false;
         if (!attr_set) {

@@ -3,13 +3,31 @@
 // Detection", abstract) or of its contiguous window (WindowedManifoldKV, same
 // abstract).  The global score is the windowed score with one window.
 //
-// Three launches on the caller's stream:
+// Fused path (used whenever a window's tiles fit on the GPU at once): one
+// cooperative launch of a persistent grid reads every key exactly once.
+//   - A window (the whole slice for the global score) is a team of 256-token
+//     tiles; the grid is a multiple of the team size and all its workgroups
+//     are co-resident (cooperative launch), so a team's tiles run in the same
+//     round.  Each workgroup keeps its tile in registers (16 rows x 8 channels
+//     per thread, 16-byte coalesced loads).
+//   - Each workgroup publishes its tile's fp32 column sums; the last one to
+//     arrive (device-scope counter) adds the team's partials in tile order --
+//     deterministic whichever arrives last -- divides by the window length and
+//     publishes the centroid and a flag; the others poll the flag (bounded:
+//     past the limit a status bit is set and the kernel still ends).
+//   - Every workgroup then scores its rows from registers.  Two tiles are in
+//     flight per workgroup: the next tile is loaded and its partial published
+//     before the workgroup waits for the current tile's centroid.
+//
+// Fallback path, three launches on the caller's stream:
 //   1. centroid_partial: column sums of bf16 keys over fixed 256-token chunks
 //      (coalesced 16-byte loads, fp32 accumulation, one LDS reduction);
 //   2. centroid_final: per window, the chunk partials added in chunk order
 //      (deterministic, no float atomics) and divided by the window's length;
 //   3. l2_distance: 16 lanes per key row, each lane 8 channels, a 16-lane
 //      butterfly for the squared norm, fp32 sqrt.
+#include <stdlib.h>
+
 #include "kvc_internal.h"
 
 namespace kvc {
@@ -110,6 +128,279 @@ __global__ __launch_bounds__(kThreads) void l2_distance(const uint16_t *__restri
     if (valid && lane16 == 0) scores[tok] = sqrtf(part);
 }
 
+// ----------------------------------------------------------- fused path
+
+#ifndef KVC_FUSE_ROWS
+#define KVC_FUSE_ROWS 16
+#endif
+constexpr int kFuseThreads = 256;
+constexpr int kFuseRows = KVC_FUSE_ROWS;                      // rows per thread (8 or 16)
+constexpr int kFuseTile = (kFuseThreads / 16) * kFuseRows;    // 256 tokens per tile
+constexpr uint32_t kSpinLimit = 1u << 16;  // ~0.1 s of polling: far above any real wait
+
+struct FuseGeom {
+    int64_t G, S, W, nwin;
+    int64_t members;  // tiles per window
+    int64_t teams;    // G * nwin
+    int64_t tiles;    // teams * members
+};
+
+__device__ __forceinline__ void widen8(const uint4 &v, float *x) {
+    x[0] = bf16_lo(v.x); x[1] = bf16_hi(v.x);
+    x[2] = bf16_lo(v.y); x[3] = bf16_hi(v.y);
+    x[4] = bf16_lo(v.z); x[5] = bf16_hi(v.z);
+    x[6] = bf16_lo(v.w); x[7] = bf16_hi(v.w);
+}
+
+// DPP lane exchanges inside a row of 16 lanes (gfx9 encodings): partner = lane ^ m
+// for m = 15 (row_mirror), 7 (row_half_mirror), 3 and 1 (quad_perm).
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kCtrl, 0xf, 0xf, false));
+}
+constexpr int kDppXor15 = 0x140, kDppXor7 = 0x141, kDppXor3 = 0x1b, kDppXor1 = 0xb1;
+
+// One butterfly step over n values: pairs (v[j], v[j + n/2]); the lane whose
+// `bit` is set keeps the upper half.  After it, v[0..n/2) hold the kept rows
+// summed over the lane and its partner.
+template <int kCtrl, int n>
+__device__ __forceinline__ void fold_step(float *v, bool upper) {
+#pragma unroll
+    for (int j = 0; j < n / 2; ++j) {
+        const float send = upper ? v[j] : v[j + n / 2];
+        const float keep = upper ? v[j + n / 2] : v[j];
+        v[j] = keep + dpp_f<kCtrl>(send);
+    }
+}
+
+// Transpose-reduce across the 16 lanes of a row group: on entry lane i holds
+// n per-row partials v[0..n); on exit v[0] holds the 16-lane total of row
+// i (n = 16) or of row i >> 1 (n = 8; lanes i and i ^ 1 hold the same total).
+template <int n>
+__device__ __forceinline__ void row_transpose_reduce(float *v, int lane16) {
+    if (n == 16) {
+        fold_step<kDppXor15, 16>(v, lane16 & 8);
+        fold_step<kDppXor7, 8>(v, lane16 & 4);
+        fold_step<kDppXor3, 4>(v, lane16 & 2);
+        fold_step<kDppXor1, 2>(v, lane16 & 1);
+    } else {
+        fold_step<kDppXor15, 8>(v, lane16 & 8);
+        fold_step<kDppXor7, 4>(v, lane16 & 4);
+        fold_step<kDppXor3, 2>(v, lane16 & 2);
+        v[0] += dpp_f<kDppXor1>(v[0]);
+    }
+}
+
+__global__ __launch_bounds__(kFuseThreads) void zero_words(uint32_t *p, int64_t n) {
+    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
+         i += static_cast<int64_t>(gridDim.x) * blockDim.x)
+        p[i] = 0u;
+}
+
+__global__ __launch_bounds__(kFuseThreads) void l2_fused(const uint16_t *__restrict__ K, FuseGeom geo,
+                                                         float *partial, float *mu_pub,
+                                                         uint32_t *counters, uint32_t *flags,
+                                                         uint32_t *status, float *__restrict__ scores,
+                                                         float *__restrict__ mu_user) {
+    const int tid = threadIdx.x;
+    const int lane16 = tid & 15;
+    const int rowg = tid >> 4;  // 0..15
+    __shared__ float red[16][kHeadDim + 4];
+    __shared__ float mu_s[kHeadDim];
+    __shared__ uint32_t last_s;
+
+    struct TileGeo {
+        int64_t team, member, g, w0, w1, t0;
+    };
+    auto geo_of = [&](int64_t tile) {
+        TileGeo t;
+        t.team = tile / geo.members;
+        t.member = tile - t.team * geo.members;
+        t.g = t.team / geo.nwin;
+        const int64_t w = t.team - t.g * geo.nwin;
+        t.w0 = w * geo.W;
+        t.w1 = min(t.w0 + geo.W, geo.S);
+        t.t0 = t.w0 + t.member * kFuseTile + rowg;  // this thread's first row
+        return t;
+    };
+    auto load_tile = [&](const TileGeo &t, uint4 *v) {
+        const uint4 *base = reinterpret_cast<const uint4 *>(K + t.g * geo.S * kHeadDim) + lane16;
+#pragma unroll
+        for (int r = 0; r < kFuseRows; ++r) {
+            const int64_t row = t.t0 + 16 * r;
+            v[r] = row < t.w1 ? base[row * (kHeadDim / 8)] : make_uint4(0u, 0u, 0u, 0u);
+        }
+    };
+    // Column sums of the tile -> the team's partial slot; the last arrival of
+    // the team adds the team's partials in tile order and publishes the centroid.
+    auto publish = [&](int64_t tile, const TileGeo &t, const uint4 *v) {
+        float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int r = 0; r < kFuseRows; ++r) {
+            float x[8];
+            widen8(v[r], x);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) acc[j] += x[j];
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) red[rowg][lane16 * 8 + j] = acc[j];
+        __syncthreads();
+        if (tid < kHeadDim) {
+            float sum = 0.f;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) sum += red[r][tid];
+            __hip_atomic_store(partial + tile * kHeadDim + tid, sum, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (tid == 0)
+            last_s = atomicAdd(&counters[t.team], 1u) == static_cast<uint32_t>(geo.members - 1);
+        __syncthreads();
+        if (!last_s) return;
+        // 32 channel groups of 4 x 8 member groups; each thread sums its members
+        // (float4 loads, all in flight), then member groups are added in order
+        {
+            const int cg = tid & 31, mg = tid >> 5;
+            const int64_t per = (geo.members + 7) / 8;
+            const int64_t m0 = mg * per, m1 = min(geo.members, m0 + per);
+            const float *p = partial + t.team * geo.members * kHeadDim + cg * 4;
+            float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
+            int64_t m = m0;
+            for (; m + 8 <= m1; m += 8) {
+                float4 x[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    const float *q = p + (m + u) * kHeadDim;
+                    x[u].x = __hip_atomic_load(q + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    x[u].y = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    x[u].z = __hip_atomic_load(q + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                    x[u].w = __hip_atomic_load(q + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                }
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    sum.x += x[u].x; sum.y += x[u].y; sum.z += x[u].z; sum.w += x[u].w;
+                }
+            }
+            for (; m < m1; ++m) {
+                const float *q = p + m * kHeadDim;
+                sum.x += __hip_atomic_load(q + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                sum.y += __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                sum.z += __hip_atomic_load(q + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                sum.w += __hip_atomic_load(q + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            }
+            red[mg][cg * 4 + 0] = sum.x;
+            red[mg][cg * 4 + 1] = sum.y;
+            red[mg][cg * 4 + 2] = sum.z;
+            red[mg][cg * 4 + 3] = sum.w;
+        }
+        __syncthreads();
+        if (tid < kHeadDim) {
+            float sum = 0.f;
+#pragma unroll
+            for (int q = 0; q < 8; ++q) sum += red[q][tid];
+            const float mu = sum / static_cast<float>(t.w1 - t.w0);
+            __hip_atomic_store(mu_pub + t.team * kHeadDim + tid, mu, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+            if (mu_user) mu_user[t.team * kHeadDim + tid] = mu;
+        }
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (tid == 0) __hip_atomic_store(&flags[t.team], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    };
+
+    uint4 v[kFuseRows], vn[kFuseRows];
+    int64_t tile = blockIdx.x;
+    if (tile < geo.tiles) {
+        const TileGeo t = geo_of(tile);
+        load_tile(t, v);
+        publish(tile, t, v);
+    }
+    // Two tiles in flight per workgroup: tile `next` is loaded and its partial
+    // published before this workgroup waits for tile `tile`'s centroid, so the
+    // exchange of one team overlaps the HBM traffic of the next.
+    for (; tile < geo.tiles; tile += gridDim.x) {
+        const TileGeo t = geo_of(tile);
+        const int64_t next = tile + gridDim.x;
+        if (next < geo.tiles) {
+            const TileGeo tn = geo_of(next);
+            load_tile(tn, vn);
+            publish(next, tn, vn);
+        }
+        if (tid == 0) {
+            uint32_t spins = 0;
+            while (__hip_atomic_load(&flags[t.team], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
+                __builtin_amdgcn_s_sleep(1);
+                if (++spins > kSpinLimit) {
+                    atomicOr(status, 1u);
+                    break;
+                }
+            }
+        }
+        __syncthreads();
+        if (tid < kHeadDim)
+            mu_s[tid] = __hip_atomic_load(mu_pub + t.team * kHeadDim + tid, __ATOMIC_RELAXED,
+                                          __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();
+        float m[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) m[j] = mu_s[lane16 * 8 + j];
+        float *sc = scores + t.g * geo.S;
+        float d2[kFuseRows];
+#pragma unroll
+        for (int r = 0; r < kFuseRows; ++r) {
+            float x[8];
+            widen8(v[r], x);
+            float acc = 0.f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float d = x[j] - m[j];
+                acc += d * d;
+            }
+            d2[r] = acc;
+        }
+        row_transpose_reduce<kFuseRows>(d2, lane16);
+        {
+            const int r = kFuseRows == 16 ? lane16 : (lane16 >> 1);
+            const int64_t row = t.t0 + 16 * r;
+            if ((kFuseRows == 16 || (lane16 & 1) == 0) && row < t.w1) sc[row] = sqrtf(d2[0]);
+        }
+#pragma unroll
+        for (int r = 0; r < kFuseRows; ++r) v[r] = vn[r];
+    }
+}
+
+FuseGeom make_fuse_geom(int64_t G, int64_t S, int64_t W) {
+    FuseGeom f;
+    f.G = G;
+    f.S = S;
+    f.W = W < S ? W : S;
+    f.nwin = (S + f.W - 1) / f.W;
+    f.members = (f.W + kFuseTile - 1) / kFuseTile;
+    f.teams = G * f.nwin;
+    f.tiles = f.teams * f.members;
+    return f;
+}
+
+template <class Ws>
+void fused_ws_layout(Ws &ws, const FuseGeom &f) {
+    ws.template take<float>(static_cast<size_t>(f.tiles) * kHeadDim);   // tile partials
+    ws.template take<float>(static_cast<size_t>(f.teams) * kHeadDim);   // published centroids
+    ws.template take<uint32_t>(static_cast<size_t>(2 * f.teams + 1));   // counters, flags, status
+}
+
+// Co-resident workgroups of l2_fused on the current device (0 if unknown).
+int64_t fused_capacity() {
+    int dev = 0, cus = 0, per_cu = 0, coop = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+    if (hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) != hipSuccess || !coop) return 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(&l2_fused),
+                                                     kFuseThreads, 0) != hipSuccess)
+        return 0;
+    return static_cast<int64_t>(cus) * per_cu;
+}
+
 WinGeom make_geom(int64_t G, int64_t S, int64_t W) {
     WinGeom geo;
     geo.G = G;
@@ -126,6 +417,20 @@ void score_ws_layout(Ws &ws, const WinGeom &geo) {
     ws.template take<float>(static_cast<size_t>(geo.G * geo.nwin) * kHeadDim);
 }
 
+size_t score_bytes(int64_t G, int64_t S, int64_t W) {
+    WsSizer a, b;
+    score_ws_layout(a, make_geom(G, S, W));
+    fused_ws_layout(b, make_fuse_geom(G, S, W));
+    return a.bytes() > b.bytes() ? a.bytes() : b.bytes();
+}
+
+// KVC_SCORE_UNFUSED=1 in the environment selects the three-launch path
+// (read at every call, so a process can compare both paths).
+bool force_unfused() {
+    const char *e = getenv("KVC_SCORE_UNFUSED");
+    return e && e[0] == '1';
+}
+
 kvc_status score_windowed_impl(const uint16_t *K, int64_t G, int64_t S, int32_t D, int64_t W,
                                float *scores, float *centroids, void *ws, size_t ws_bytes,
                                hipStream_t stream) {
@@ -137,10 +442,41 @@ kvc_status score_windowed_impl(const uint16_t *K, int64_t G, int64_t S, int32_t 
     if (!aligned(K, 16) || !aligned(scores, 4) || !aligned(ws, kWsAlign) ||
         (centroids && !aligned(centroids, 4)))
         return KVC_ERR_INVALID_ARGUMENT;
+    if (ws_bytes < score_bytes(G, S, W)) return KVC_ERR_WORKSPACE_TOO_SMALL;
+
+    const FuseGeom f = make_fuse_geom(G, S, W);
+    static int64_t capacity_by_dev[64];
+    static bool known[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return KVC_ERR_HIP;
+    if (!known[dev]) {
+        capacity_by_dev[dev] = fused_capacity();
+        known[dev] = true;
+    }
+    const int64_t capacity = capacity_by_dev[dev];
+    if (capacity >= f.members && f.tiles <= INT32_MAX && !force_unfused()) {
+        WsCursor cur(ws);
+        float *partial = cur.take<float>(static_cast<size_t>(f.tiles) * kHeadDim);
+        float *mu_pub = cur.take<float>(static_cast<size_t>(f.teams) * kHeadDim);
+        uint32_t *words = cur.take<uint32_t>(static_cast<size_t>(2 * f.teams + 1));
+        uint32_t *counters = words, *flags = words + f.teams, *status = words + 2 * f.teams;
+        const int64_t nw = 2 * f.teams + 1;
+        const int64_t zb = nw < 256 * 1024 ? (nw + kFuseThreads - 1) / kFuseThreads : 1024;
+        hipLaunchKernelGGL(zero_words, dim3(static_cast<unsigned>(zb)), dim3(kFuseThreads), 0, stream,
+                           words, nw);
+        FuseGeom fa = f;
+        float *mu_user = centroids;
+        int64_t grid = capacity / f.members * f.members;
+        if (grid > f.tiles) grid = f.tiles;
+        void *args[] = {&K, &fa, &partial, &mu_pub, &counters, &flags, &status, &scores, &mu_user};
+        if (hipLaunchCooperativeKernel(reinterpret_cast<const void *>(&l2_fused),
+                                       dim3(static_cast<unsigned>(grid)), dim3(kFuseThreads), args, 0,
+                                       stream) != hipSuccess)
+            return KVC_ERR_HIP;
+        return launch_status();
+    }
+
     const WinGeom geo = make_geom(G, S, W);
-    WsSizer sz;
-    score_ws_layout(sz, geo);
-    if (ws_bytes < sz.bytes()) return KVC_ERR_WORKSPACE_TOO_SMALL;
     WsCursor cur(ws);
     float *partial = cur.take<float>(static_cast<size_t>(geo.G * geo.nwin * geo.nchunk) * kHeadDim);
     float *mu = cur.take<float>(static_cast<size_t>(geo.G * geo.nwin) * kHeadDim);
@@ -162,9 +498,7 @@ kvc_status score_windowed_impl(const uint16_t *K, int64_t G, int64_t S, int32_t 
 
 size_t score_workspace_bytes(int64_t G, int64_t S, int64_t W) {
     if (G < 0 || S < 1 || W < 1) return 0;
-    WsSizer sz;
-    score_ws_layout(sz, make_geom(G, S, W));
-    return sz.bytes();
+    return score_bytes(G, S, W);
 }
 
 }  // namespace kvc
