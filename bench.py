@@ -1,16 +1,20 @@
-"""Benchmark of the ManifoldKV eviction hot path on one MI355X.
+"""Benchmark of the KV-cache scoring / compaction hot path on one MI355X.
 
-Workload (default): a Llama-3.1-8B-shaped KV cache, 32 layers x 8 KV heads
-(256 slices), head dim 128, batch 1, S = 16384 tokens, bf16 K/V drawn with
-per-channel offsets, lognormal norm scales and 64 planted x4 outliers per
-head; global-centroid L2 scoring, 50% eviction (keep 8192 per head) and
-compaction of K and V.  One step = score every key + select + compact.
+Default workload (the headline): ManifoldKV eviction of a Llama-3.1-8B-shaped
+KV cache -- 32 layers x 8 KV heads (256 slices), head dim 128, batch 1,
+S = 16384 tokens, bf16 K/V drawn with per-channel offsets, lognormal norm
+scales and 64 planted x4 outliers per head -- scored against the global key
+centroid, 50% evicted (keep 8192 per head), K and V compacted.  One step =
+score every key + select + compact.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config N] [--no-cpu-baseline]
 
-Prints one JSON line: head-tokens scored+compacted per second, the roofline
-of the dominant kernel (algorithmic bytes / its average launch time, from HIP
-events on the launch stream) and the CPU oracle timed on a bounded sample.
+--config 0..4 measures the other synthetic workloads instead (0: 8 slices at
+S=4096 keep 3277; 2: windowed W=4096 at S=65536 keep 49152; 3: OjaKV prefill
+compression B=4, S=32768, r=64 with 5% anchors; 4: the OjaKV prefill + 256
+decode-step loop at S=131072).  Prints one JSON line: head-tokens/s, the
+roofline of the dominant entry point (algorithmic bytes / its average time,
+HIP events on the launch stream), and the CPU oracle on a bounded sample.
 """
 from __future__ import annotations
 
@@ -23,7 +27,8 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, 8 TB/s
+HBM_PEAK_GBS = 8000.0    # MI355X HBM3E
+MFMA_BF16_PEAK_TFLOPS = 2500.0
 
 
 def parse():
@@ -31,9 +36,209 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", type=int, default=1, choices=[0, 1, 2, 3, 4])
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--copy-ref", type=int, default=0, metavar="MIB",
+                    help="only time a plain device-to-device copy of MIB MiB (the reference "
+                         "kernel for scaling HBM traffic counters) and exit")
     return ap.parse_args()
+
+
+def copy_reference(mib, reps):
+    import torch
+    n = mib << 20
+    a = torch.ones(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(reps):
+        b.copy_(a)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / reps
+    print(json.dumps({"copy_bytes": n, "ms": ms, "GBs_read_plus_write": 2 * n / ms / 1e6}), flush=True)
+
+
+class Op:
+    """An entry-point call inside a step, with its algorithmic bytes and flops."""
+
+    def __init__(self, name, fn, nbytes, flops=0, kernel=None):
+        self.name, self.fn, self.nbytes, self.flops = name, fn, nbytes, flops
+        self.kernel = kernel or name
+        self.ms = []
+
+
+def manifold_workload(cfg, dev):
+    import synth
+    from token_scoring_eviction_amd import kvc, pipeline
+    if cfg == 0:
+        L, H, S, keep, W = 1, 8, 4096, 3277, None
+        K, V, _ = synth.manifold_global(L, 1, H, S, planted=16, device=dev)
+        desc = "ManifoldKV global-L2 eviction, 1 layer x 8 KV heads x d_h 128, S=4096, keep 3277 (drop 20%)"
+    elif cfg == 1:
+        L, H, S, keep, W = 32, 8, 16384, 8192, None
+        K, V, _ = synth.manifold_global(L, 1, H, S, planted=64, device=dev)
+        desc = ("ManifoldKV global-L2 eviction, 32 layers x 8 KV heads x d_h 128, batch 1, "
+                "S=16384, keep 8192 (50%)")
+    else:
+        L, H, S, keep, W = 32, 8, 65536, 49152, 4096
+        K, V = synth.manifold_drifting(L, 1, H, S, device=dev)
+        desc = ("Windowed ManifoldKV eviction, 32 layers x 8 KV heads x d_h 128, batch 1, "
+                "S=65536, W=4096, keep 49152 (25% evicted)")
+    G = L * H
+    buf = pipeline.alloc_eviction(G, S, keep, device=dev)
+    score = (lambda: kvc.kvc_score_l2(K, scores=buf.scores)) if W is None else \
+        (lambda: kvc.kvc_score_l2_windowed(K, W, scores=buf.scores))
+    ops = [
+        Op("kvc_score_l2" if W is None else "kvc_score_l2_windowed", score, G * S * (256 + 4),
+           kernel="l2_fused"),
+        Op("kvc_topk_compact",
+           lambda: kvc.kvc_topk_compact(buf.scores, keep, K, V, idx_out=buf.idx, K_out=buf.K_out,
+                                        V_out=buf.V_out),
+           G * S * 4 + G * keep * (2 * 256 * 2 + 4), kernel="select_compact+gather_rows"),
+    ]
+    algo = G * S * 256 + G * keep * 256 + 2 * G * keep * 256 + G * S * 4 + G * keep * 4
+    config = {"workload": desc, "slices": G, "seq_len": S, "keep": keep, "head_dim": 128,
+              "window": W}
+
+    def cpu(budget):
+        import numpy as np
+        import oracle
+        done, t = 0, 0.0
+        while done < G and t < budget:
+            kb = synth.bf16_bits(K[done:done + 1])
+            vb = synth.bf16_bits(V[done:done + 1])
+            t0 = time.perf_counter()
+            sc, _ = oracle.score_l2(kb) if W is None else oracle.score_l2_windowed(kb, W)
+            idx = oracle.topk(sc.astype(np.float32), keep)
+            oracle.gather(kb, idx)
+            oracle.gather(vb, idx)
+            t += time.perf_counter() - t0
+            done += 1
+        return done * S, t, "%d of %d slices (S=%d each) of the same workload" % (done, G, S)
+
+    return ops, G * S, algo, config, cpu
+
+
+def oja_workload(dev):
+    import synth
+    from token_scoring_eviction_amd import kvc, pipeline
+    L, B, Hkv, Hq, S, R, Wq = 32, 4, 8, 32, 32768, 64, 32
+    inp = synth.oja_inputs(L, B, Hkv, Hq, S, R=R, Wq=Wq, device=dev)
+    G = L * B * Hkv
+    k = pipeline.anchor_count(S)
+    st = pipeline.alloc_hybrid(G, S, R, device=dev, max_anchor=k, with_hat=False)
+    ops = [
+        Op("kvc_lowrank_compress",
+           lambda: kvc.kvc_lowrank_compress(inp.K, inp.V, inp.Q, inp.Uk, inp.Uv, L, B, Hkv,
+                                            K_tilde=st.Kt, V_tilde=st.Vt, err=st.err),
+           G * S * (2 * 256 + 2 * R * 4 + 4),
+           flops=G * S * (2 * 2 * 128 * R + 3 * 2 * 128 * (Hq // Hkv) * Wq + 2 * 2 * 128 * R),
+           kernel="project_kernel"),
+        Op("kvc_topk_compact",
+           lambda: kvc.kvc_topk_compact(st.err, k, inp.K, inp.V, idx_out=st.idx, K_out=st.K_anchor,
+                                        V_out=st.V_anchor),
+           G * S * 4 + G * k * (2 * 256 * 2 + 4), kernel="select_compact+gather_rows"),
+    ]
+    algo = G * S * (2 * 256 + 2 * R * 4 + 4) + G * k * (2 * 256 * 2 + 4)
+    config = {"workload": "OjaKV hybrid low-rank prefill compression, 32 layers x batch 4 x 8 KV heads "
+                          "(32 query heads), d_h 128, S=32768, r=64, 32-query window, 5% anchors",
+              "slices": G, "seq_len": S, "rank": R, "anchors": k}
+
+    def cpu(budget):
+        import numpy as np
+        import oracle
+        done, t = 0, 0.0
+        Uk, Uv = inp.Uk.cpu().numpy(), inp.Uv.cpu().numpy()
+        while done < G and t < budget:
+            g = done
+            l, b, h = g // (B * Hkv), (g // Hkv) % B, g % Hkv
+            kb, vb = synth.bf16_bits(inp.K[g:g + 1]), synth.bf16_bits(inp.V[g:g + 1])
+            q = synth.bf16_bits(inp.Q[l:l + 1, b:b + 1, 4 * h:4 * h + 4])
+            t0 = time.perf_counter()
+            _, _, e = oracle.lowrank_compress(kb, vb, q, Uk[l:l + 1, h:h + 1], Uv[l:l + 1, h:h + 1],
+                                              1, 1, 1, 4)
+            idx = oracle.topk(e.astype(np.float32), k)
+            oracle.gather(kb, idx)
+            oracle.gather(vb, idx)
+            t += time.perf_counter() - t0
+            done += 1
+        return done * S, t, "%d of %d slices (S=%d each) of the same workload" % (done, G, S)
+
+    return ops, G * S, algo, config, cpu
+
+
+def run_loop_config(args, dev):
+    """Config 4: one step = the whole OjaKV loop (prefill + 256 decode steps, 8 updates)."""
+    import torch
+
+    import synth
+    from token_scoring_eviction_amd import pipeline
+    L, B, Hkv, Hq, S0, R, Wq, steps, T = 32, 1, 8, 32, 131072, 64, 32, 256, 32
+    inp = synth.oja_inputs(L, B, Hkv, Hq, S0, R=R, Wq=Wq, S_cap=S0 + steps, device=dev)
+    G = L * B * Hkv
+    toks = [synth.decode_token(inp, s) for s in range(steps)]
+    Uk0, Uv0 = inp.Uk.clone(), inp.Uv.clone()
+
+    def loop(times=None):
+        Uk, Uv = Uk0.clone(), Uv0.clone()
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        e[0].record()
+        st = pipeline.ojakv_prefill(inp.K, inp.V, inp.Q, Uk, Uv, L, B, Hkv, S0, T=T, pool=32, eta=1e-3)
+        e[1].record()
+        upd = []
+        for s in range(steps):
+            k, v, q = toks[s]
+            if (s + 1) % T == 0:
+                a = torch.cuda.Event(enable_timing=True)
+                a.record()
+            if pipeline.ojakv_decode_step(st, inp.K, inp.V, k, v, q, L, B, Hkv, T=T, eta=1e-3):
+                b = torch.cuda.Event(enable_timing=True)
+                b.record()
+                upd.append((a, b))
+        if times is not None:
+            times.append((e, upd))
+        return st
+
+    for _ in range(max(1, args.warmup // 5)):
+        st = loop()
+    torch.cuda.synchronize()
+    reps = max(1, args.steps // 25)
+    times = []
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    t0.record()
+    for _ in range(reps):
+        st = loop(times)
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / reps
+    pre = sum(e[0].elapsed_time(e[1]) for e, _ in times) / reps
+    upd = sum(sum(a.elapsed_time(b) for a, b in u) for _, u in times) / reps / 8
+    scorings = G * sum(S0 + T * j for j in range(9))
+    per_pass = lambda S: G * S * (2 * 256 + 2 * R * 4 + 4 + 2 * 512) + G * pipeline.anchor_count(S) * 1028
+    algo = G * S0 * 256 * 2 + sum(per_pass(S0 + T * j) for j in range(9))
+    line = base_line(args, "KV head-tokens scored+compacted/s", scorings / (ms / 1e3), ms, reps,
+                     {"workload": "OjaKV full loop: 32 layers x batch 1 x 8 KV heads (32 query heads), "
+                                  "d_h 128, S=131072 prefill pooled by 32 + 256 decode steps, update "
+                                  "every 32 (eta 1e-3, r=64, 5% anchors, K^/V^ rebuilt per update)",
+                      "slices": G, "seq_len": S0, "decode_steps": steps, "updates": 8})
+    line["phases_ms"] = {"prefill": pre, "per_update": upd, "whole_loop": ms}
+    line["step_hbm"] = {"algorithmic_bytes": algo, "GBs": algo / ms / 1e6,
+                        "frac": algo / ms / 1e6 / HBM_PEAK_GBS}
+    line["roofline"] = None
+    print(json.dumps(line), flush=True)
+
+
+def base_line(args, metric, value, ms_step, steps, config):
+    return {"metric": metric, "value": value, "unit": "head-tokens/s", "n_gpus": 1, "steps": steps,
+            "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
+            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "config": config}
 
 
 def main():
@@ -44,115 +249,71 @@ def main():
         sys.exit(2)
     import torch
 
-    import synth
-    from token_scoring_eviction_amd import kvc, pipeline
+    from token_scoring_eviction_amd import kvc
 
+    if args.copy_ref:
+        return copy_reference(args.copy_ref, args.steps)
     kvc.load()
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
-    L, H, S, keep = 32, 8, 16384, 8192
-    G = L * H
-    K, V, _ = synth.manifold_global(L, 1, H, S, planted=64, device=dev)
-    buf = pipeline.alloc_eviction(G, S, keep, device=dev)
+    if args.config == 4:
+        return run_loop_config(args, dev)
+    if args.config == 3:
+        ops, head_tokens, algo, config, cpu = oja_workload(dev)
+    else:
+        ops, head_tokens, algo, config, cpu = manifold_workload(args.config, dev)
     torch.cuda.synchronize()
 
-    def step(ev=None):
-        if ev is not None:
-            ev[0].record()
-        kvc.kvc_score_l2(K, scores=buf.scores)
-        if ev is not None:
-            ev[1].record()
-        kvc.kvc_topk_compact(buf.scores, keep, K, V, idx_out=buf.idx, K_out=buf.K_out, V_out=buf.V_out)
-        if ev is not None:
-            ev[2].record()
+    def step(record=False):
+        for op in ops:
+            if record:
+                a = torch.cuda.Event(enable_timing=True)
+                b = torch.cuda.Event(enable_timing=True)
+                a.record()
+                op.fn()
+                b.record()
+                op.ms.append((a, b))
+            else:
+                op.fn()
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-
-    # whole-step timing: K steps between two synchronizations
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
     t0.record()
     for _ in range(args.steps):
         step()
     t1.record()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    ms_total = t0.elapsed_time(t1)
-    ms_step = ms_total / args.steps
-
-    # per-entry-point timing with events on the launch stream
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
-    for e in evs:
-        step(e)
+    ms_step = t0.elapsed_time(t1) / args.steps
+    for _ in range(args.steps):
+        step(record=True)
     torch.cuda.synchronize()
-    score_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / args.steps
-    topk_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / args.steps
-
-    head_tokens = G * S
-    # algorithmic (compulsory) bytes
-    by_score = G * S * (128 * 2 + 4)                       # K read once, fp32 score written
-    by_topk = G * S * 4 + 2 * G * keep * 128 * 2 * 2 + G * keep * 4  # scores, kept K/V rows r+w, idx
-    by_step = G * S * 128 * 2 + G * keep * 128 * 2 + 2 * G * keep * 128 * 2 + G * S * 4 + G * keep * 4
-    ops = {
-        "kvc_score_l2": {"ms": score_ms, "bytes": by_score, "GBs": by_score / score_ms / 1e6},
-        "kvc_topk_compact": {"ms": topk_ms, "bytes": by_topk, "GBs": by_topk / topk_ms / 1e6},
-    }
-    dom = max(ops, key=lambda n: ops[n]["ms"])
-    achieved = ops[dom]["GBs"]
-    line = {
-        "metric": "KV head-tokens scored+compacted/s",
-        "value": head_tokens / (ms_step / 1e3),
-        "unit": "head-tokens/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": ms_step,
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic",
-        "config": {"workload": "ManifoldKV global-L2 eviction, 32 layers x 8 KV heads x d_h 128, "
-                               "batch 1, S=16384, keep 8192 (50%)",
-                   "slices": G, "seq_len": S, "keep": keep, "head_dim": 128},
-        "roofline": {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None},
-        "step_hbm": {"algorithmic_bytes": by_step, "GBs": by_step / ms_step / 1e6,
-                     "frac": by_step / ms_step / 1e6 / HBM_PEAK_GBS},
-        "ops": ops,
-        "wall_s": wall,
-    }
+    per_op = {}
+    for op in ops:
+        ms = sum(a.elapsed_time(b) for a, b in op.ms) / len(op.ms)
+        per_op[op.name] = {"ms": ms, "bytes": op.nbytes, "GBs": op.nbytes / ms / 1e6,
+                           "kernel": op.kernel}
+        if op.flops:
+            per_op[op.name]["TFLOPs"] = op.flops / ms / 1e9
+    dom = max(per_op, key=lambda n: per_op[n]["ms"])
+    achieved = per_op[dom]["GBs"]
+    line = base_line(args, "KV head-tokens scored+compacted/s", head_tokens / (ms_step / 1e3),
+                     ms_step, args.steps, config)
+    line["roofline"] = {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
+                        "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None}
+    if "TFLOPs" in per_op[dom]:
+        line["roofline"]["mfma_TFLOPs"] = per_op[dom]["TFLOPs"]
+        line["roofline"]["mfma_frac"] = per_op[dom]["TFLOPs"] / MFMA_BF16_PEAK_TFLOPS
+    line["step_hbm"] = {"algorithmic_bytes": algo, "GBs": algo / ms_step / 1e6,
+                        "frac": algo / ms_step / 1e6 / HBM_PEAK_GBS}
+    line["ops"] = per_op
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(K, V, keep, args.cpu_seconds)
+        n, t, sample = cpu(args.cpu_seconds)
+        line["cpu_baseline"] = {"value": n / t, "unit": "head-tokens/s", "cores": 1, "kind": "oracle",
+                                "sample": "%s, %.1f s" % (sample, t)}
     print(json.dumps(line), flush=True)
-
-
-def cpu_baseline(K, V, keep, budget_s):
-    """The oracle (single-threaded C, fp64) on the first slices of the same
-    workload, as many as fit in about budget_s seconds."""
-    import numpy as np
-
-    import oracle
-    import synth
-    G, S, _ = K.shape
-    done = 0
-    t = 0.0
-    while done < G and t < budget_s:
-        kb = synth.bf16_bits(K[done:done + 1])
-        vb = synth.bf16_bits(V[done:done + 1])
-        t0 = time.perf_counter()
-        sc, _ = oracle.score_l2(kb)
-        idx = oracle.topk(sc.astype(np.float32), keep)
-        oracle.gather(kb, idx)
-        oracle.gather(vb, idx)
-        t += time.perf_counter() - t0
-        done += 1
-    return {"value": done * S / t, "unit": "head-tokens/s", "cores": 1, "kind": "oracle",
-            "sample": "%d of %d slices (S=%d each) of the same workload, %.1f s" % (done, G, S, t)}
 
 
 if __name__ == "__main__":

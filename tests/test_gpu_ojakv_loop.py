@@ -1,0 +1,132 @@
+"""GPU parity of the OjaKV prefill + decode loop (appendix A.1 of the OjaKV
+deep-notes page) against the oracle's loop, run independently on the same
+inputs: after the prefill and after every decode update the bases (rel 2e-3,
+orthonormal to 1e-5), error scores (rel 1e-4), anchor sets (threshold band)
+and reconstructions (rel 2e-3, anchor rows exact) agree.
+
+The loop's decode-time re-projection and re-selection over the whole cache is
+this build's reading of the full-loop workload (parity unpinned relative to
+the pages); both sides implement that same reading."""
+import threading
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests.helpers import index_sets_agree, lowrank_close, score_close
+from token_scoring_eviction_amd import pipeline
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _run_gpu_loop(inp, steps, T, pool, eta, slices, token_sample=None):
+    """Runs the loop on the GPU; snapshots the sampled slices after the prefill
+    and each update.  Returns (snapshots, decode queries per step on host)."""
+    L, B, Hkv = inp.L, inp.B, inp.Hkv
+    Uk, Uv = inp.Uk.clone(), inp.Uv.clone()
+    snaps = []
+    qdec = []
+
+    def snap(st):
+        torch.cuda.synchronize()
+        S = st.S
+        k = pipeline.anchor_count(S)
+        G = inp.L * inp.B * inp.Hkv
+        idx = st.hybrid.idx.view(-1)[:G * k].view(G, k)
+        out = {"S": S}
+        for g in slices:
+            l, h = g // (B * Hkv), g % Hkv
+            rows = np.arange(S) if token_sample is None else np.unique(
+                np.concatenate([token_sample(S), idx[g].cpu().numpy()]))
+            rt = torch.from_numpy(rows).to(DEV)
+            out[g] = dict(Uk=st.U_k[l, h].cpu().numpy(), Uv=st.U_v[l, h].cpu().numpy(),
+                          err=st.hybrid.err[g, :S].cpu().numpy(), idx=idx[g].cpu().numpy(),
+                          rows=rows, Khat=st.hybrid.Khat[g][rt].cpu().numpy(),
+                          Vhat=st.hybrid.Vhat[g][rt].cpu().numpy())
+        snaps.append(out)
+
+    st = pipeline.ojakv_prefill(inp.K, inp.V, inp.Q, Uk, Uv, L, B, Hkv, inp.S, T=T, pool=pool, eta=eta)
+    snap(st)
+    for step in range(steps):
+        k, v, q = synth.decode_token(inp, step)
+        qdec.append(q.cpu())
+        if pipeline.ojakv_decode_step(st, inp.K, inp.V, k, v, q, L, B, Hkv, T=T, eta=eta):
+            snap(st)
+    torch.cuda.synchronize()
+    return snaps, torch.stack(qdec) if qdec else None
+
+
+def _oracle_loop(inp, g, steps, T, pool, eta, qdec):
+    l, b, h = g // (inp.B * inp.Hkv), (g // inp.Hkv) % inp.B, g % inp.Hkv
+    grp = inp.Hq // inp.Hkv
+    S_end = inp.S + steps
+    K = synth.bf16_bits(inp.K[g, :S_end])
+    V = synth.bf16_bits(inp.V[g, :S_end])
+    Qp = synth.bf16_bits(inp.Q[l, b, h * grp:(h + 1) * grp])
+    Qd = synth.bf16_bits(qdec[:, l, b, h * grp:(h + 1) * grp].to(torch.bfloat16)) if steps else \
+        np.zeros((0, grp, inp.D), np.uint16)
+    return oracle.full_loop_slice(K, V, Qp, Qd, inp.Uk[l, h].cpu().numpy(), inp.Uv[l, h].cpu().numpy(),
+                                  inp.S, steps, T, pool, eta)
+
+
+def _compare(snap_g, ora, S):
+    for key in ("Uk", "Uv"):
+        ok, rel = lowrank_close(snap_g[key][None], ora[key][None].astype(np.float64))
+        assert ok, "%s rel %.3g" % (key, rel)
+        U = snap_g[key].astype(np.float64)
+        assert np.abs(U.T @ U - np.eye(U.shape[1])).max() < 1e-5
+    ok, rel, nbad = score_close(snap_g["err"][None], ora["err"])
+    assert ok, "err: %d off, max rel %.3g" % (nbad, rel)
+    k = pipeline.anchor_count(S)
+    e32 = ora["err"].astype(np.float32)
+    ok, nb = index_sets_agree(snap_g["idx"][None], ora["idx"], e32, k)
+    assert ok, "anchor sets differ beyond the threshold band"
+    both = np.intersect1d(snap_g["idx"], ora["idx"][0])
+    gpu_anchor = np.isin(snap_g["rows"], snap_g["idx"])
+    ora_anchor = np.isin(snap_g["rows"], ora["idx"][0])
+    same = gpu_anchor == ora_anchor
+    for key in ("Khat", "Vhat"):
+        ref = ora[key][0][snap_g["rows"]]
+        ok, rel = lowrank_close(snap_g[key][same][None], ref[same][None])
+        assert ok, "%s rel %.3g" % (key, rel)
+    assert both.size >= k - nb
+
+
+def test_loop_small_all_slices(gpu_lib):
+    # 1 layer, 2 kv heads / 8 query heads, 4096-token prompt, 256 decode steps, T=32 -> 8 updates
+    inp = synth.oja_inputs(1, 1, 2, 8, 4096, R=64, Wq=32, S_cap=4096 + 256, seed=41, device=DEV)
+    snaps, qdec = _run_gpu_loop(inp, 256, 32, 32, 1e-3, slices=[0, 1])
+    assert [s["S"] for s in snaps] == [4096 + 32 * j for j in range(9)]
+    for g in (0, 1):
+        res = _oracle_loop(inp, g, 256, 32, 32, 1e-3, qdec)
+        for j, ora in enumerate(res):
+            _compare(snaps[j][g], ora, ora["S"])
+
+
+def test_loop_config4_sampled(gpu_lib):
+    # 32 layers x batch 1 x 8 kv heads (32 query heads), 131072-token prompt pooled by 32 for
+    # the prefill update, eta 1e-3, 256 decode steps with an update every 32, all at full
+    # size on the GPU.  Two slices are checked against independent oracle runs (one thread
+    # each) after the prefill and the first two updates; every update of the loop is
+    # checked on all slices at a 4096-token prompt by test_loop_small_all_slices.
+    S0, steps, checked = 131072, 256, 2
+    inp = synth.oja_inputs(32, 1, 8, 32, S0, R=64, Wq=32, S_cap=S0 + steps, device=DEV)
+    sl = [137, 250]
+    rng = np.random.default_rng(0)
+    snaps, qdec = _run_gpu_loop(inp, steps, 32, 32, 1e-3, slices=sl,
+                                token_sample=lambda S: np.sort(rng.choice(S, 4096, replace=False)))
+    assert len(snaps) == 9 and snaps[-1]["S"] == S0 + steps
+    result = {}
+    threads = [threading.Thread(target=lambda g=g: result.__setitem__(
+        g, _oracle_loop(inp, g, 32 * checked, 32, 32, 1e-3, qdec))) for g in sl]
+    for th in threads:
+        th.start()
+    for th in threads:
+        th.join()
+    for g in sl:
+        assert len(result[g]) == checked + 1
+        for j, ora in enumerate(result[g]):
+            _compare(snaps[j][g], ora, ora["S"])

@@ -88,15 +88,78 @@ def hybrid_pass(K, V, Q_win, U_k, U_v, L, B, H_kv, S, st: HybridState, anchor_pe
     (optionally) rebuild K^, V^.  K, V: bf16 [G, S_cap, 128] caches (S <= S_cap)."""
     G = K.shape[0]
     k = anchor_count(S, anchor_percent)
+    if k > st.idx.shape[1]:
+        raise ValueError("anchor buffers hold %d rows, %d needed" % (st.idx.shape[1], k))
     kvc.kvc_lowrank_compress(K, V, Q_win, U_k, U_v, L, B, H_kv, S=S, K_tilde=st.Kt, V_tilde=st.Vt,
                              err=st.err)
-    idx = st.idx[:, :k] if k == st.idx.shape[1] else torch.empty((G, k), dtype=torch.int32,
-                                                                   device=K.device)
-    Ka = st.K_anchor[:, :k] if k == st.K_anchor.shape[1] else torch.empty(
-        (G, k, K.shape[2]), dtype=torch.bfloat16, device=K.device)
-    Va = st.V_anchor[:, :k] if k == st.V_anchor.shape[1] else torch.empty_like(Ka)
+    # anchors of this pass: the first k rows of the (contiguous) anchor buffers
+    idx = st.idx.view(-1)[:G * k].view(G, k)
+    Ka = st.K_anchor.view(-1)[:G * k * K.shape[2]].view(G, k, K.shape[2])
+    Va = st.V_anchor.view(-1)[:G * k * K.shape[2]].view(G, k, K.shape[2])
     kvc.kvc_topk_compact(st.err, k, K, V, S=S, idx_out=idx, K_out=Ka, V_out=Va)
     if reconstruct:
         kvc.kvc_reconstruct(st.Kt, U_k, idx, Ka, L, B, H_kv, S=S, X_hat=st.Khat)
         kvc.kvc_reconstruct(st.Vt, U_v, idx, Va, L, B, H_kv, S=S, X_hat=st.Vhat)
     return idx, Ka, Va
+
+
+@dataclass
+class OjaLoopState:
+    U_k: torch.Tensor
+    U_v: torch.Tensor
+    hybrid: HybridState
+    K_buf: torch.Tensor      # [G, T, D] tokens since the last update
+    V_buf: torch.Tensor
+    Q_dec: torch.Tensor      # [L, B, H_q, T, D] decode queries since the last update
+    S: int                   # tokens in the cache
+    step: int = 0
+    updates: int = 0
+
+
+def ojakv_prefill(K, V, Q_prompt, U_k, U_v, L, B, H_kv, S0, T=32, pool=32, eta=1e-3,
+                  anchor_percent=5, S_cap=None, reconstruct=True):
+    """Prefill phase (appendix A.1): pooled Oja update of U_k (on K) and U_v (on V)
+    with QR, then projection, error score with the prompt's query window,
+    top-k anchors and (optionally) reconstruction.  U_k, U_v are updated in place.
+    K, V: bf16 [L*B*H_kv, S_cap, 128] caches holding S0 prompt tokens."""
+    G, cap, D = K.shape
+    S_cap = cap if S_cap is None else S_cap
+    kvc.kvc_oja_update(U_k, K, pool, eta, L, B, H_kv, N=S0)
+    kvc.kvc_oja_update(U_v, V, pool, eta, L, B, H_kv, N=S0)
+    R = U_k.shape[-1]
+    st = alloc_hybrid(G, S_cap, R, D, K.device, max_anchor=anchor_count(S_cap, anchor_percent),
+                      with_hat=reconstruct)
+    hybrid_pass(K, V, Q_prompt, U_k, U_v, L, B, H_kv, S0, st, anchor_percent, reconstruct)
+    H_q = Q_prompt.shape[2]
+    return OjaLoopState(
+        U_k=U_k, U_v=U_v, hybrid=st,
+        K_buf=torch.empty((G, T, D), dtype=torch.bfloat16, device=K.device),
+        V_buf=torch.empty((G, T, D), dtype=torch.bfloat16, device=K.device),
+        Q_dec=torch.empty((L, B, H_q, T, D), dtype=torch.bfloat16, device=K.device),
+        S=S0)
+
+
+def ojakv_decode_step(state: OjaLoopState, K, V, k_new, v_new, q_new, L, B, H_kv, T=32,
+                      eta=1e-3, anchor_percent=5, reconstruct=True):
+    """One decode step (appendix A.1): the new (k, v) are appended to the cache
+    and to the update buffer, the new queries to the decode query window; when
+    T tokens are buffered the bases take an unpooled Oja step + QR, and the
+    whole cache is re-projected, re-scored with the T decode queries, its
+    anchors re-selected and K^, V^ rebuilt.  Returns True on an update step.
+    k_new, v_new: bf16 [G, 128]; q_new: bf16 [L, B, H_q, 128]."""
+    slot = state.step % T
+    K[:, state.S] = k_new
+    V[:, state.S] = v_new
+    state.K_buf[:, slot] = k_new
+    state.V_buf[:, slot] = v_new
+    state.Q_dec[:, :, :, slot] = q_new
+    state.S += 1
+    state.step += 1
+    if state.step % T:
+        return False
+    kvc.kvc_oja_update(state.U_k, state.K_buf, 1, eta, L, B, H_kv)
+    kvc.kvc_oja_update(state.U_v, state.V_buf, 1, eta, L, B, H_kv)
+    hybrid_pass(K, V, state.Q_dec, state.U_k, state.U_v, L, B, H_kv, state.S, state.hybrid,
+                anchor_percent, reconstruct)
+    state.updates += 1
+    return True
