@@ -197,10 +197,18 @@ __global__ __launch_bounds__(kFuseThreads) void zero_words(uint32_t *p, int64_t 
         p[i] = 0u;
 }
 
-__global__ __launch_bounds__(kFuseThreads) void l2_fused(const uint16_t *__restrict__ K, FuseGeom geo,
-                                                         float *partial, float *mu_pub,
-                                                         uint32_t *counters, uint32_t *flags,
-                                                         uint32_t *status, float *__restrict__ scores,
+// Centroid words are published as 64-bit {fp32 bits, ready tag}, so a reader
+// learns availability and value in one coherent load.
+constexpr uint32_t kReady = 1u;
+
+__device__ __forceinline__ uint64_t tagged(float mu) {
+    return (static_cast<uint64_t>(kReady) << 32) | __float_as_uint(mu);
+}
+
+__global__ __launch_bounds__(kFuseThreads, 3) void l2_fused(const uint16_t *__restrict__ K, FuseGeom geo,
+                                                         float *partial, uint64_t *mu_pub,
+                                                         uint32_t *counters, uint32_t *status,
+                                                         float *__restrict__ scores,
                                                          float *__restrict__ mu_user) {
     const int tid = threadIdx.x;
     const int lane16 = tid & 15;
@@ -252,47 +260,45 @@ __global__ __launch_bounds__(kFuseThreads) void l2_fused(const uint16_t *__restr
             __hip_atomic_store(partial + tile * kHeadDim + tid, sum, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
         }
-        __builtin_amdgcn_s_waitcnt(0);
+        __builtin_amdgcn_s_waitcnt(0);  // partial stored at the coherence point
         __syncthreads();
         if (tid == 0)
             last_s = atomicAdd(&counters[t.team], 1u) == static_cast<uint32_t>(geo.members - 1);
         __syncthreads();
         if (!last_s) return;
         // 32 channel groups of 4 x 8 member groups; each thread sums its members
-        // (float4 loads, all in flight), then member groups are added in order
+        // (all loads in flight), then member groups are added in order
         {
             const int cg = tid & 31, mg = tid >> 5;
             const int64_t per = (geo.members + 7) / 8;
             const int64_t m0 = mg * per, m1 = min(geo.members, m0 + per);
             const float *p = partial + t.team * geo.members * kHeadDim + cg * 4;
-            float4 sum = make_float4(0.f, 0.f, 0.f, 0.f);
+            float sx = 0.f, sy = 0.f, sz = 0.f, sw = 0.f;
             int64_t m = m0;
             for (; m + 8 <= m1; m += 8) {
-                float4 x[8];
+                float x[8][4];
+#pragma unroll
+                for (int u = 0; u < 8; ++u)
+#pragma unroll
+                    for (int c = 0; c < 4; ++c)
+                        x[u][c] = __hip_atomic_load(p + (m + u) * kHeadDim + c, __ATOMIC_RELAXED,
+                                                    __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
                 for (int u = 0; u < 8; ++u) {
-                    const float *q = p + (m + u) * kHeadDim;
-                    x[u].x = __hip_atomic_load(q + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    x[u].y = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    x[u].z = __hip_atomic_load(q + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                    x[u].w = __hip_atomic_load(q + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                }
-#pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    sum.x += x[u].x; sum.y += x[u].y; sum.z += x[u].z; sum.w += x[u].w;
+                    sx += x[u][0]; sy += x[u][1]; sz += x[u][2]; sw += x[u][3];
                 }
             }
             for (; m < m1; ++m) {
                 const float *q = p + m * kHeadDim;
-                sum.x += __hip_atomic_load(q + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                sum.y += __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                sum.z += __hip_atomic_load(q + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                sum.w += __hip_atomic_load(q + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                sx += __hip_atomic_load(q + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                sy += __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                sz += __hip_atomic_load(q + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                sw += __hip_atomic_load(q + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             }
-            red[mg][cg * 4 + 0] = sum.x;
-            red[mg][cg * 4 + 1] = sum.y;
-            red[mg][cg * 4 + 2] = sum.z;
-            red[mg][cg * 4 + 3] = sum.w;
+            red[mg][cg * 4 + 0] = sx;
+            red[mg][cg * 4 + 1] = sy;
+            red[mg][cg * 4 + 2] = sz;
+            red[mg][cg * 4 + 3] = sw;
         }
         __syncthreads();
         if (tid < kHeadDim) {
@@ -300,13 +306,31 @@ __global__ __launch_bounds__(kFuseThreads) void l2_fused(const uint16_t *__restr
 #pragma unroll
             for (int q = 0; q < 8; ++q) sum += red[q][tid];
             const float mu = sum / static_cast<float>(t.w1 - t.w0);
-            __hip_atomic_store(mu_pub + t.team * kHeadDim + tid, mu, __ATOMIC_RELAXED,
+            __hip_atomic_store(mu_pub + t.team * kHeadDim + tid, tagged(mu), __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
             if (mu_user) mu_user[t.team * kHeadDim + tid] = mu;
         }
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-        if (tid == 0) __hip_atomic_store(&flags[t.team], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __syncthreads();  // red is reused by the caller
+    };
+    // The team's centroid into mu_s: each channel's tagged word is polled
+    // until ready (bounded; past the limit a status bit is set).
+    auto fetch_mu = [&](const TileGeo &t) {
+        uint32_t spins = 0;
+        for (;;) {
+            bool ready = true;
+            if (tid < kHeadDim) {
+                const uint64_t w = __hip_atomic_load(mu_pub + t.team * kHeadDim + tid, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
+                ready = (w >> 32) == kReady;
+                mu_s[tid] = __uint_as_float(static_cast<uint32_t>(w));
+            }
+            if (__syncthreads_and(ready)) break;
+            if (++spins > kSpinLimit) {
+                if (tid == 0) atomicOr(status, 1u);
+                break;
+            }
+            __builtin_amdgcn_s_sleep(1);
+        }
     };
 
     uint4 v[kFuseRows], vn[kFuseRows];
@@ -316,36 +340,21 @@ __global__ __launch_bounds__(kFuseThreads) void l2_fused(const uint16_t *__restr
         load_tile(t, v);
         publish(tile, t, v);
     }
-    // Two tiles in flight per workgroup: tile `next` is loaded and its partial
-    // published before this workgroup waits for tile `tile`'s centroid, so the
-    // exchange of one team overlaps the HBM traffic of the next.
+    // Two tiles per workgroup: while tile `tile` waits for its team's centroid
+    // and is scored, the next tile's loads are already in flight; its partial
+    // is published right after.
     for (; tile < geo.tiles; tile += gridDim.x) {
         const TileGeo t = geo_of(tile);
         const int64_t next = tile + gridDim.x;
+        TileGeo tn;
         if (next < geo.tiles) {
-            const TileGeo tn = geo_of(next);
+            tn = geo_of(next);
             load_tile(tn, vn);
-            publish(next, tn, vn);
         }
-        if (tid == 0) {
-            uint32_t spins = 0;
-            while (__hip_atomic_load(&flags[t.team], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == 0u) {
-                __builtin_amdgcn_s_sleep(1);
-                if (++spins > kSpinLimit) {
-                    atomicOr(status, 1u);
-                    break;
-                }
-            }
-        }
-        __syncthreads();
-        if (tid < kHeadDim)
-            mu_s[tid] = __hip_atomic_load(mu_pub + t.team * kHeadDim + tid, __ATOMIC_RELAXED,
-                                          __HIP_MEMORY_SCOPE_AGENT);
-        __syncthreads();
+        fetch_mu(t);
         float m[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) m[j] = mu_s[lane16 * 8 + j];
-        float *sc = scores + t.g * geo.S;
         float d2[kFuseRows];
 #pragma unroll
         for (int r = 0; r < kFuseRows; ++r) {
@@ -363,8 +372,11 @@ __global__ __launch_bounds__(kFuseThreads) void l2_fused(const uint16_t *__restr
         {
             const int r = kFuseRows == 16 ? lane16 : (lane16 >> 1);
             const int64_t row = t.t0 + 16 * r;
-            if ((kFuseRows == 16 || (lane16 & 1) == 0) && row < t.w1) sc[row] = sqrtf(d2[0]);
+            if ((kFuseRows == 16 || (lane16 & 1) == 0) && row < t.w1)
+                scores[t.g * geo.S + row] = sqrtf(d2[0]);
         }
+        __syncthreads();  // mu_s is rewritten by the next fetch
+        if (next < geo.tiles) publish(next, tn, vn);
 #pragma unroll
         for (int r = 0; r < kFuseRows; ++r) v[r] = vn[r];
     }
@@ -384,9 +396,9 @@ FuseGeom make_fuse_geom(int64_t G, int64_t S, int64_t W) {
 
 template <class Ws>
 void fused_ws_layout(Ws &ws, const FuseGeom &f) {
-    ws.template take<float>(static_cast<size_t>(f.tiles) * kHeadDim);   // tile partials
-    ws.template take<float>(static_cast<size_t>(f.teams) * kHeadDim);   // published centroids
-    ws.template take<uint32_t>(static_cast<size_t>(2 * f.teams + 1));   // counters, flags, status
+    ws.template take<float>(static_cast<size_t>(f.tiles) * kHeadDim);      // tile partials
+    ws.template take<uint64_t>(static_cast<size_t>(f.teams) * kHeadDim);   // tagged centroids
+    ws.template take<uint32_t>(static_cast<size_t>(f.teams + 1));          // counters, status
 }
 
 // Co-resident workgroups of l2_fused on the current device (0 if unknown).
@@ -457,18 +469,24 @@ kvc_status score_windowed_impl(const uint16_t *K, int64_t G, int64_t S, int32_t 
     if (capacity >= f.members && f.tiles <= INT32_MAX && !force_unfused()) {
         WsCursor cur(ws);
         float *partial = cur.take<float>(static_cast<size_t>(f.tiles) * kHeadDim);
-        float *mu_pub = cur.take<float>(static_cast<size_t>(f.teams) * kHeadDim);
-        uint32_t *words = cur.take<uint32_t>(static_cast<size_t>(2 * f.teams + 1));
-        uint32_t *counters = words, *flags = words + f.teams, *status = words + 2 * f.teams;
-        const int64_t nw = 2 * f.teams + 1;
-        const int64_t zb = nw < 256 * 1024 ? (nw + kFuseThreads - 1) / kFuseThreads : 1024;
-        hipLaunchKernelGGL(zero_words, dim3(static_cast<unsigned>(zb)), dim3(kFuseThreads), 0, stream,
-                           words, nw);
+        uint64_t *mu_pub = cur.take<uint64_t>(static_cast<size_t>(f.teams) * kHeadDim);
+        uint32_t *words = cur.take<uint32_t>(static_cast<size_t>(f.teams + 1));
+        uint32_t *counters = words, *status = words + f.teams;
+        // clear the centroid tags, the counters and the status word (a kernel,
+        // not a memset, so the sequence can be captured in a graph)
+        const int64_t n_mu = f.teams * kHeadDim * 2, n_w = f.teams + 1;
+        auto zero_blocks = [](int64_t n) {
+            const int64_t b = (n + kFuseThreads - 1) / kFuseThreads;
+            return static_cast<unsigned>(b < 1024 ? b : 1024);
+        };
+        hipLaunchKernelGGL(zero_words, dim3(zero_blocks(n_mu)), dim3(kFuseThreads), 0, stream,
+                           reinterpret_cast<uint32_t *>(mu_pub), n_mu);
+        hipLaunchKernelGGL(zero_words, dim3(zero_blocks(n_w)), dim3(kFuseThreads), 0, stream, words, n_w);
         FuseGeom fa = f;
         float *mu_user = centroids;
         int64_t grid = capacity / f.members * f.members;
         if (grid > f.tiles) grid = f.tiles;
-        void *args[] = {&K, &fa, &partial, &mu_pub, &counters, &flags, &status, &scores, &mu_user};
+        void *args[] = {&K, &fa, &partial, &mu_pub, &counters, &status, &scores, &mu_user};
         if (hipLaunchCooperativeKernel(reinterpret_cast<const void *>(&l2_fused),
                                        dim3(static_cast<unsigned>(grid)), dim3(kFuseThreads), args, 0,
                                        stream) != hipSuccess)
