@@ -107,10 +107,13 @@ def test_reconstruct_small(gpu_lib, R, k):
         np.testing.assert_array_equal(Xh[g].cpu().numpy()[idx[g]], ora[g][idx[g]])
 
 
-@pytest.mark.parametrize("B,N,pool,eta", [(1, 4096, 32, 1e-3), (2, 700, 7, 0.05), (1, 32, 1, 1e-3),
-                                          (3, 64, 1, 0.1)])
-def test_oja_update_small(gpu_lib, B, N, pool, eta):
-    L, Hkv, R = 2, 2, 64
+@pytest.mark.parametrize("B,N,pool,eta,R", [(1, 4096, 32, 1e-3, 64), (2, 700, 7, 0.05, 64),
+                                            (1, 32, 1, 1e-3, 64), (3, 64, 1, 0.1, 64),
+                                            (1, 500, 4, 0.02, 32), (2, 300, 3, 0.02, 96),
+                                            (1, 256, 1, 0.02, 128)])
+def test_oja_update_small(gpu_lib, B, N, pool, eta, R):
+    # R <= 64 runs the LDS-resident step + QR, larger R the workspace-backed one
+    L, Hkv = 2, 2
     inp = synth.oja_inputs(L, B, Hkv, 4, N, R=R, Wq=1, seed=N + B, device=DEV)
     U0 = inp.Uk.clone()
     U = inp.Uk.clone()

@@ -83,7 +83,7 @@ struct Slices {
 constexpr int kQParts = 3;  // bf16 terms per folded-query element
 
 // Folded, scaled query fragments of one slice:
-//   Q''[q][c] = scale * (Q[q][c] - sum_j (sum_c' Q[q][c'] U[c'][j]) U[c][j])
+//   Q''[q][c] = scale * (Q[q][c] - sum_j T[q][j] U[c][j]),  T = Q U
 // in fp64, split into three bf16 terms, as A-operand fragments
 // [qb][s][term][lane].  Three terms keep the score's error at the level of
 // the fp32 accumulation even when |q . r_t| cancels far below ||q|| ||r_t||.
@@ -92,25 +92,38 @@ __global__ __launch_bounds__(256) void prep_query_kernel(const uint16_t *__restr
                                                          int64_t Hkv, int64_t Hq, int64_t Wq,
                                                          int R, int nq, int nqb, double scale,
                                                          u32x4 *__restrict__ qfrag) {
-    extern __shared__ double T[];  // [128][R]: T = Q U
+    // LDS: Q window rows (bf16 bits, [128][128]), T = Q U ([128][R] fp64: when U is
+    // close to a full orthonormal basis the residual is a tiny difference that
+    // an fp32 T would lose), U ([128][R] fp32, staged only when R <= 64, else
+    // read from global memory).  At most 160 KB.
+    extern __shared__ uint32_t lds_q[];
+    const bool u_lds = R <= 64;
+    uint16_t *Qs = reinterpret_cast<uint16_t *>(lds_q);
+    double *Ts = reinterpret_cast<double *>(lds_q + 128 * kHeadDim / 2);
+    float *Ul = reinterpret_cast<float *>(Ts + kHeadDim * R);
     const int64_t slice = blockIdx.x;
     const int64_t h = slice % Hkv;
     const int64_t lb = slice / Hkv;  // l*B + b
     const int64_t l = lb / B;
     const int64_t grp = Hq / Hkv;
     const float *U = Uk + (l * Hkv + h) * kHeadDim * R;
-    auto qrow = [&](int q) {
-        const int64_t hq = h * grp + q / Wq;
-        return Q + ((lb * Hq + hq) * Wq + q % Wq) * kHeadDim;
-    };
+    const float *Us = u_lds ? Ul : U;
+    // window rows q = (group head) * Wq + (query); the group's heads are contiguous in Q
+    const uint16_t *Qg = Q + ((lb * Hq + h * grp) * Wq) * kHeadDim;
+    for (int i = threadIdx.x; i < nq * kHeadDim / 8; i += blockDim.x)
+        reinterpret_cast<uint4 *>(Qs)[i] = reinterpret_cast<const uint4 *>(Qg)[i];
+    if (u_lds)
+        for (int i = threadIdx.x; i < kHeadDim * R / 4; i += blockDim.x)
+            reinterpret_cast<float4 *>(Ul)[i] = reinterpret_cast<const float4 *>(U)[i];
+    __syncthreads();
     for (int o = threadIdx.x; o < nq * R; o += blockDim.x) {
         const int q = o / R, j = o % R;
-        const uint16_t *qr = qrow(q);
         double acc = 0.0;
+#pragma unroll 8
         for (int c = 0; c < kHeadDim; ++c)
-            acc += static_cast<double>(__uint_as_float(static_cast<uint32_t>(qr[c]) << 16)) *
-                   static_cast<double>(U[c * R + j]);
-        T[q * R + j] = acc;
+            acc += static_cast<double>(__uint_as_float(static_cast<uint32_t>(Qs[q * kHeadDim + c]) << 16)) *
+                   static_cast<double>(Us[c * R + j]);
+        Ts[q * R + j] = acc;
     }
     __syncthreads();
     u32x4 *out = qfrag + slice * static_cast<int64_t>(nqb) * 8 * kQParts * 64;
@@ -118,20 +131,20 @@ __global__ __launch_bounds__(256) void prep_query_kernel(const uint16_t *__restr
         const int lane = p & 63, fs = p >> 6, s = fs & 7, qb = fs >> 3;
         const int q = qb * 32 + (lane & 31);
         const int c0 = 16 * s + (lane >> 5) * 8;
-        double x[8];
+        double x[8] = {0., 0., 0., 0., 0., 0., 0., 0.};
         if (q < nq) {
-            const uint16_t *qr = qrow(q);
+            double proj[8] = {0., 0., 0., 0., 0., 0., 0., 0.};
+            for (int j = 0; j < R; ++j) {
+                const double t = Ts[q * R + j];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) proj[e] += t * static_cast<double>(Us[(c0 + e) * R + j]);
+            }
 #pragma unroll
             for (int e = 0; e < 8; ++e) {
-                const int c = c0 + e;
-                double proj = 0.0;
-                for (int j = 0; j < R; ++j) proj += T[q * R + j] * static_cast<double>(U[c * R + j]);
-                const double qc = static_cast<double>(__uint_as_float(static_cast<uint32_t>(qr[c]) << 16));
-                x[e] = scale * (qc - proj);
+                const double qc = static_cast<double>(
+                    __uint_as_float(static_cast<uint32_t>(Qs[q * kHeadDim + c0 + e]) << 16));
+                x[e] = scale * (qc - proj[e]);
             }
-        } else {
-#pragma unroll
-            for (int e = 0; e < 8; ++e) x[e] = 0.0;
         }
         u32x4 part[kQParts];
         split8x3_f64(x, part);
@@ -498,8 +511,11 @@ extern "C" kvc_status kvc_lowrank_compress(const kvc_dims *d, const uint16_t *K,
             attr_set = true;
         }
         if (G > INT32_MAX) return KVC_ERR_UNSUPPORTED;
-        hipLaunchKernelGGL(prep_query_kernel, dim3(static_cast<unsigned>(G)), dim3(256),
-                           static_cast<size_t>(128 * d->R) * sizeof(double), stream, Q_win, U_k,
+        const size_t prep_lds = static_cast<size_t>(128) * kHeadDim * 2 +
+                                static_cast<size_t>(kHeadDim * d->R) * sizeof(double) +
+                                (d->R <= 64 ? static_cast<size_t>(kHeadDim * d->R) * sizeof(float) : 0);
+        hipLaunchKernelGGL(prep_query_kernel, dim3(static_cast<unsigned>(G)), dim3(256), prep_lds, stream,
+                           Q_win, U_k,
                            d->B, d->H_kv, d->H_q, d->W_q, static_cast<int>(d->R),
                            static_cast<int>(nq), nqb, scale, qfrag);
         if ((st = launch_status()) != KVC_OK) return st;

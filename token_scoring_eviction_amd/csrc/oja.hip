@@ -8,10 +8,12 @@
 //   cov_partial_kernel per (layer, kv head) and chunk of pooled rows (rows of
 //                      all sequences of the batch): sum of x x^T in fp32,
 //                      8x8 register tiles over LDS-staged rows
-//   oja_step_qr_kernel per (layer, kv head), fp64: C = sum of partials / n in
-//                      chunk order; CU = C U; M = U^T CU; U' = U + eta (CU - U M);
-//                      classical Gram-Schmidt applied twice per column (a
-//                      reorthogonalised QR, positive diagonal); U <- fp32(Q)
+//   oja_step_qr_*      per (layer, kv head), fp64 arithmetic: C = sum of
+//                      partials / n in chunk order; CU = C U; M = U^T CU;
+//                      U' = U + eta (CU - U M); classical Gram-Schmidt applied
+//                      twice per column (a reorthogonalised QR, positive
+//                      diagonal); U <- fp32(Q).  R <= 64 runs entirely in LDS
+//                      (M stored in fp32); larger R keeps C, CU, M in the workspace.
 #include <cmath>
 
 #include "kvc_internal.h"
@@ -184,6 +186,110 @@ __global__ __launch_bounds__(256) void oja_step_qr_kernel(float *__restrict__ U,
     for (int e = tid; e < kHeadDim * R; e += blockDim.x) Ug[e] = static_cast<float>(Ul[(e / R) * ld + e % R]);
 }
 
+// Fast path for R <= 64: everything per head stays in LDS.
+//   Ud [128][R+1] fp64: U, later Q;  Wd [128][R] fp64: C column chunks, then CU,
+//   then U';  Mf [R][R+1] fp32: U^T C U;  vs/ds: Gram-Schmidt scratch.
+// Each thread owns row a = tid / 2 and half of the columns of CU and U'.
+constexpr int kCChunk = 16;  // C columns staged per step
+
+__global__ __launch_bounds__(256) void oja_step_qr_lds_kernel(float *__restrict__ U,
+                                                              const float *__restrict__ Cpart,
+                                                              int64_t nchunk, int64_t n, int R,
+                                                              double eta) {
+    extern __shared__ double lds[];
+    const int ld = R + 1;
+    double *Ud = lds;                                  // [128][R+1]
+    double *Wd = Ud + kHeadDim * ld;                   // [128][R] (>= [128][kCChunk])
+    float *Mf = reinterpret_cast<float *>(Wd + kHeadDim * R);  // [R][R+1]
+    double *vs = reinterpret_cast<double *>(Mf + R * ld + (R * ld) % 2);  // [128]
+    double *ds = vs + kHeadDim;                        // [128]
+    double *red = ds + kHeadDim;                       // [2]
+    const int64_t lh = blockIdx.x;
+    const int tid = threadIdx.x;
+    float *Ug = U + lh * kHeadDim * R;
+    const int DD = kHeadDim * kHeadDim;
+    const double inv_n = 1.0 / static_cast<double>(n);
+    const int a = tid >> 1, jh = (tid & 1) * (R / 2), nj = R / 2;
+
+    for (int e = tid; e < kHeadDim * R; e += blockDim.x) Ud[(e / R) * ld + e % R] = static_cast<double>(Ug[e]);
+    // CU = C U, C staged kCChunk columns at a time (chunk partials added in order)
+    double acc[32];
+#pragma unroll
+    for (int q = 0; q < 32; ++q) acc[q] = 0.0;
+    for (int c0 = 0; c0 < kHeadDim; c0 += kCChunk) {
+        __syncthreads();
+        for (int e = tid; e < kHeadDim * kCChunk; e += blockDim.x) {
+            const int r = e / kCChunk, c = c0 + e % kCChunk;
+            double sum = 0.0;
+            for (int64_t ch = 0; ch < nchunk; ++ch)
+                sum += static_cast<double>(Cpart[(lh * nchunk + ch) * DD + r * kHeadDim + c]);
+            Wd[r * kCChunk + e % kCChunk] = sum * inv_n;
+        }
+        __syncthreads();
+        for (int c = 0; c < kCChunk; ++c) {
+            const double cv = Wd[a * kCChunk + c];
+#pragma unroll
+            for (int q = 0; q < 32; ++q)
+                if (q < nj) acc[q] += cv * Ud[(c0 + c) * ld + jh + q];
+        }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int q = 0; q < 32; ++q)
+        if (q < nj) Wd[a * R + jh + q] = acc[q];
+    __syncthreads();
+    // M = U^T (C U)
+    for (int e = tid; e < R * R; e += blockDim.x) {
+        const int i = e / R, j = e % R;
+        double sum = 0.0;
+        for (int r = 0; r < kHeadDim; ++r) sum += Ud[r * ld + i] * Wd[r * R + j];
+        Mf[i * ld + j] = static_cast<float>(sum);
+    }
+    __syncthreads();
+    // U' = U + eta (CU - U M), each thread on its own entries of Wd
+#pragma unroll
+    for (int q = 0; q < 32; ++q) {
+        if (q < nj) {
+            const int j = jh + q;
+            double um = 0.0;
+            for (int i = 0; i < R; ++i) um += Ud[a * ld + i] * static_cast<double>(Mf[i * ld + j]);
+            Wd[a * R + j] = Ud[a * ld + j] + eta * (Wd[a * R + j] - um);
+        }
+    }
+    __syncthreads();
+    // QR of U' (columns of Wd) by Gram-Schmidt twice per column; Q replaces U in Ud
+    for (int j = 0; j < R; ++j) {
+        double v = tid < kHeadDim ? Wd[tid * R + j] : 0.0;
+        for (int pass = 0; pass < 2; ++pass) {
+            if (tid < kHeadDim) vs[tid] = v;
+            __syncthreads();
+            if (tid < j) {
+                double d = 0.0;
+                for (int r = 0; r < kHeadDim; ++r) d += Ud[r * ld + tid] * vs[r];
+                ds[tid] = d;
+            }
+            __syncthreads();
+            if (tid < kHeadDim) {
+                double sum = 0.0;
+                for (int i = 0; i < j; ++i) sum += ds[i] * Ud[tid * ld + i];
+                v -= sum;
+            }
+            __syncthreads();
+        }
+        const double nrm2 = block_sum_128(tid < kHeadDim ? v * v : 0.0, red);
+        if (tid < kHeadDim) Ud[tid * ld + j] = v / sqrt(nrm2);
+        __syncthreads();
+    }
+    for (int e = tid; e < kHeadDim * R; e += blockDim.x) Ug[e] = static_cast<float>(Ud[(e / R) * ld + e % R]);
+}
+
+size_t oja_lds_bytes(int R) {
+    const size_t ld = R + 1;
+    size_t b = (kHeadDim * ld + kHeadDim * R) * sizeof(double) + R * ld * sizeof(float);
+    b = (b + 7) / 8 * 8 + (2 * kHeadDim + 2) * sizeof(double);
+    return b;
+}
+
 struct OjaGeom {
     int64_t G, LH, N, S_stride, np, n, nchunk, rows_per_chunk;
 };
@@ -264,6 +370,19 @@ extern "C" kvc_status kvc_oja_update(const kvc_dims *d, float *U, const uint16_t
                        o.N, o.S_stride, pool, o.np, Xp);
     hipLaunchKernelGGL(cov_partial_kernel, dim3(static_cast<unsigned>(o.LH * o.nchunk)), dim3(256), 0,
                        stream, Xp, d->B, d->H_kv, o.np, o.rows_per_chunk, o.nchunk, Cpart);
+    if (d->R <= 64) {
+        static bool attr_fast = false;
+        if (!attr_fast) {
+            if (hipFuncSetAttribute(reinterpret_cast<const void *>(&oja_step_qr_lds_kernel),
+                                    hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) != hipSuccess)
+                return KVC_ERR_HIP;
+            attr_fast = true;
+        }
+        hipLaunchKernelGGL(oja_step_qr_lds_kernel, dim3(static_cast<unsigned>(o.LH)), dim3(256),
+                           oja_lds_bytes(static_cast<int>(d->R)), stream, U, Cpart, o.nchunk, o.n,
+                           static_cast<int>(d->R), static_cast<double>(eta));
+        return launch_status();
+    }
     const size_t lds = (static_cast<size_t>(kHeadDim) * (d->R + 1) + 2 * kHeadDim + 2) * sizeof(double);
     static bool attr_set = false;
     if (!attr_set) {
