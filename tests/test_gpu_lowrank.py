@@ -123,11 +123,13 @@ def test_oja_update_small(gpu_lib, B, N, pool, eta, R):
     Ug = U.cpu().numpy().astype(np.float64)
     ok, rel = lowrank_close(Ug.reshape(L * Hkv, -1), ora.reshape(L * Hkv, -1))
     assert ok, rel
-    # the step itself (U' - U) is also matched, so the check is not carried by U alone
-    d_gpu = Ug - U0.cpu().numpy()
-    d_ora = ora - U0.cpu().numpy()
-    ok, rel = lowrank_close(d_gpu.reshape(L * Hkv, -1), d_ora.reshape(L * Hkv, -1), rel=2e-3)
-    assert ok, rel
+    # the step itself (U' - U) is also matched, so the check is not carried by U alone;
+    # at r = d the basis spans everything, C U - U U^T C U = 0 and the step is rounding noise
+    if R < 128:
+        d_gpu = Ug - U0.cpu().numpy()
+        d_ora = ora - U0.cpu().numpy()
+        ok, rel = lowrank_close(d_gpu.reshape(L * Hkv, -1), d_ora.reshape(L * Hkv, -1), rel=2e-3)
+        assert ok, rel
     for l in range(L):
         for h in range(Hkv):
             assert np.abs(Ug[l, h].T @ Ug[l, h] - np.eye(R)).max() < 1e-5
