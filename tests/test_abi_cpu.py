@@ -48,9 +48,12 @@ def test_workspace_sizing():
     a = kvc.workspace_bytes(kvc.OP_SCORE_L2, D(1, 1, 8, 0, 4096, 0, 128, 0, 0))
     b = kvc.workspace_bytes(kvc.OP_SCORE_L2, D(1, 1, 16, 0, 4096, 0, 128, 0, 0))
     assert 0 < a < b
-    # compress needs folded query fragments only when a window is given
+    # compress needs folded query fragments only when a window is given (two bf16 terms
+    # per element for a 128-query window, three below 32 queries)
     assert kvc.workspace_bytes(kvc.OP_LOWRANK_COMPRESS, D(32, 4, 8, 32, 32768, 0, 128, 64, 32)) == \
-        1024 * 4 * 8 * 3 * 64 * 16
+        1024 * 4 * 8 * 2 * 64 * 16
+    assert kvc.workspace_bytes(kvc.OP_LOWRANK_COMPRESS, D(1, 1, 2, 2, 100, 0, 128, 64, 1)) == \
+        2 * 1 * 8 * 3 * 64 * 16
     assert kvc.workspace_bytes(kvc.OP_LOWRANK_COMPRESS, D(32, 4, 8, 0, 32768, 0, 128, 64, 0)) == 0
     # invalid or unsupported shapes report 0
     assert kvc.workspace_bytes(kvc.OP_LOWRANK_COMPRESS, D(1, 1, 1, 0, 10, 0, 64, 32, 0)) == 0

@@ -80,7 +80,12 @@ struct Slices {
 
 // ------------------------------------------------------------ compress prep
 
-constexpr int kQParts = 3;  // bf16 terms per folded-query element
+constexpr int kQParts = 3;  // bf16 terms per folded-query element (at most)
+
+// Terms used for the folded query: three for small windows (a single |q . r_t|
+// can cancel far below ||q|| ||r_t||: two terms missed the score tolerance at a
+// one-query window), two once the score averages >= 32 products.
+inline int query_terms(int64_t nq) { return nq < 32 ? 3 : 2; }
 
 // Folded, scaled query fragments of one slice:
 //   Q''[q][c] = scale * (Q[q][c] - sum_j T[q][j] U[c][j]),  T = Q U
@@ -90,8 +95,8 @@ constexpr int kQParts = 3;  // bf16 terms per folded-query element
 __global__ __launch_bounds__(256) void prep_query_kernel(const uint16_t *__restrict__ Q,
                                                          const float *__restrict__ Uk, int64_t B,
                                                          int64_t Hkv, int64_t Hq, int64_t Wq,
-                                                         int R, int nq, int nqb, double scale,
-                                                         u32x4 *__restrict__ qfrag) {
+                                                         int R, int nq, int nqb, int nterm,
+                                                         double scale, u32x4 *__restrict__ qfrag) {
     // LDS: Q window rows (bf16 bits, [128][128]), T = Q U ([128][R] fp64: when U is
     // close to a full orthonormal basis the residual is a tiny difference that
     // an fp32 T would lose), U ([128][R] fp32, staged only when R <= 64, else
@@ -126,7 +131,7 @@ __global__ __launch_bounds__(256) void prep_query_kernel(const uint16_t *__restr
         Ts[q * R + j] = acc;
     }
     __syncthreads();
-    u32x4 *out = qfrag + slice * static_cast<int64_t>(nqb) * 8 * kQParts * 64;
+    u32x4 *out = qfrag + slice * static_cast<int64_t>(nqb) * 8 * nterm * 64;
     for (int p = threadIdx.x; p < nqb * 8 * 64; p += blockDim.x) {
         const int lane = p & 63, fs = p >> 6, s = fs & 7, qb = fs >> 3;
         const int q = qb * 32 + (lane & 31);
@@ -148,23 +153,23 @@ __global__ __launch_bounds__(256) void prep_query_kernel(const uint16_t *__restr
         }
         u32x4 part[kQParts];
         split8x3_f64(x, part);
-#pragma unroll
-        for (int t = 0; t < kQParts; ++t) out[((qb * 8 + s) * kQParts + t) * 64 + lane] = part[t];
+        for (int t = 0; t < nterm; ++t) out[((qb * 8 + s) * nterm + t) * 64 + lane] = part[t];
     }
 }
 
 // --------------------------------------------------------------- compress
 
-// One block per (slice, token range); 8 waves; each wave 64 tokens per step.
+// One block per (slice, token range).  Each wave takes 32*HB tokens per step
+// (HB column blocks of 32 tokens share every A fragment read from LDS).
 // LDS: U^T fragments [rb][s][hi|lo] (NRB*16 KB), then Q'' fragments
-// [qb][s][term] (nqb*24 KB).
-template <int NRB>
-__global__ __launch_bounds__(512) void project_kernel(const uint16_t *__restrict__ X,
-                                                      const float *__restrict__ Ubase,
-                                                      const u32x4 *__restrict__ qfrag, int nqb,
-                                                      Slices sl, float *__restrict__ Xt,
-                                                      float *__restrict__ err) {
+// [qb][s][term] (nqb*8*nterm KB).  HB = 1 runs 16 waves per block (4 per SIMD),
+// HB = 2 runs 8 waves with twice the reuse of each fragment.
+template <int NRB, int HB>
+__global__ __launch_bounds__(HB == 1 ? 1024 : 512) void project_kernel(
+    const uint16_t *__restrict__ X, const float *__restrict__ Ubase, const u32x4 *__restrict__ qfrag,
+    int nqb, int nterm, Slices sl, float *__restrict__ Xt, float *__restrict__ err) {
     constexpr int R = 32 * NRB;
+    constexpr int TOK = 32 * HB;
     extern __shared__ u32x4 lds[];
     u32x4 *ufr = lds;
     u32x4 *qfr = lds + NRB * 16 * 64;  // after the U^T fragments
@@ -188,7 +193,7 @@ __global__ __launch_bounds__(512) void project_kernel(const uint16_t *__restrict
         ufr[((rb * 8 + s) * 2 + 1) * 64 + lane] = lo;
     }
     if (nqb > 0) {
-        const int nq4 = nqb * 8 * kQParts * 64;
+        const int nq4 = nqb * 8 * nterm * 64;
         const u32x4 *src = qfrag + slice * static_cast<int64_t>(nq4);
         for (int p = threadIdx.x; p < nq4; p += blockDim.x) qfr[p] = src[p];
     }
@@ -201,10 +206,11 @@ __global__ __launch_bounds__(512) void project_kernel(const uint16_t *__restrict
     const u32x4 *xrows = reinterpret_cast<const u32x4 *>(X + slice * sl.S_stride * kHeadDim);
     float *xt = Xt + slice * sl.S_stride * R;
 
-    for (int64_t t0 = t_begin + wave * 64; t0 < t_end; t0 += (blockDim.x / 64) * 64) {
-        u32x4 b[2][8];
+    // key tile of a wave step: lane (col, khalf) holds 16 bytes of token t0+32hb+col
+    // at channel 16s + 8khalf, s = 0..7 (B operand of the k-steps)
+    auto load_b = [&](int64_t t0, u32x4 (&b)[HB][8]) {
 #pragma unroll
-        for (int hb = 0; hb < 2; ++hb) {
+        for (int hb = 0; hb < HB; ++hb) {
             const int64_t tok = t0 + hb * 32 + col;
             const bool ok = tok < t_end;
             const u32x4 *row = xrows + (ok ? tok : 0) * 16;
@@ -214,58 +220,72 @@ __global__ __launch_bounds__(512) void project_kernel(const uint16_t *__restrict
                 if (!ok) b[hb][s] = u32x4{0u, 0u, 0u, 0u};
             }
         }
-#pragma unroll
+    };
+    const int64_t wstep = (blockDim.x / 64) * TOK;
+    u32x4 b[HB][8], bn[HB][8];
+    if (t_begin + wave * TOK < t_end) load_b(t_begin + wave * TOK, b);
+    for (int64_t t0 = t_begin + wave * TOK; t0 < t_end; t0 += wstep) {
+        // the next step's keys are requested before this step's contractions
+        if (t0 + wstep < t_end) load_b(t0 + wstep, bn);
+#pragma unroll 1
         for (int rb = 0; rb < NRB; ++rb) {
-            f32x16 a0 = {}, a1 = {};
+            f32x16 a[HB];
+#pragma unroll
+            for (int hb = 0; hb < HB; ++hb) a[hb] = f32x16{};
 #pragma unroll
             for (int s = 0; s < 8; ++s) {
                 const u32x4 fh = ufr[((rb * 8 + s) * 2 + 0) * 64 + lane];
                 const u32x4 fl = ufr[((rb * 8 + s) * 2 + 1) * 64 + lane];
-                a0 = mfma32x32x16(fh, b[0][s], a0);
-                a1 = mfma32x32x16(fh, b[1][s], a1);
-                a0 = mfma32x32x16(fl, b[0][s], a0);
-                a1 = mfma32x32x16(fl, b[1][s], a1);
+#pragma unroll
+                for (int hb = 0; hb < HB; ++hb) a[hb] = mfma32x32x16(fh, b[hb][s], a[hb]);
+#pragma unroll
+                for (int hb = 0; hb < HB; ++hb) a[hb] = mfma32x32x16(fl, b[hb][s], a[hb]);
             }
 #pragma unroll
-            for (int hb = 0; hb < 2; ++hb) {
+            for (int hb = 0; hb < HB; ++hb) {
                 const int64_t tok = t0 + hb * 32 + col;
                 if (tok < t_end) {
-                    const f32x16 &a = hb ? a1 : a0;
                     float *dst = xt + tok * R + rb * 32 + khalf * 4;
 #pragma unroll
                     for (int q = 0; q < 4; ++q)
                         *reinterpret_cast<float4 *>(dst + q * 8) =
-                            make_float4(a[4 * q], a[4 * q + 1], a[4 * q + 2], a[4 * q + 3]);
+                            make_float4(a[hb][4 * q], a[hb][4 * q + 1], a[hb][4 * q + 2], a[hb][4 * q + 3]);
                 }
             }
         }
         if (nqb > 0) {
-            float e0 = 0.f, e1 = 0.f;
+            float e[HB];
+#pragma unroll
+            for (int hb = 0; hb < HB; ++hb) e[hb] = 0.f;
+#pragma unroll 1
             for (int qb = 0; qb < nqb; ++qb) {
-                f32x16 a0 = {}, a1 = {};
+                f32x16 a[HB];
+#pragma unroll
+                for (int hb = 0; hb < HB; ++hb) a[hb] = f32x16{};
 #pragma unroll
                 for (int s = 0; s < 8; ++s) {
+                    for (int t = 0; t < nterm; ++t) {
+                        const u32x4 f = qfr[((qb * 8 + s) * nterm + t) * 64 + lane];
 #pragma unroll
-                    for (int t = 0; t < kQParts; ++t) {
-                        const u32x4 f = qfr[((qb * 8 + s) * kQParts + t) * 64 + lane];
-                        a0 = mfma32x32x16(f, b[0][s], a0);
-                        a1 = mfma32x32x16(f, b[1][s], a1);
+                        for (int hb = 0; hb < HB; ++hb) a[hb] = mfma32x32x16(f, b[hb][s], a[hb]);
                     }
                 }
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    e0 += fabsf(a0[r]);
-                    e1 += fabsf(a1[r]);
-                }
+                for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+                    for (int r = 0; r < 16; ++r) e[hb] += fabsf(a[hb][r]);
             }
-            e0 += __shfl_xor(e0, 32);
-            e1 += __shfl_xor(e1, 32);
-            if (khalf == 0) {
-                float *er = err + slice * sl.S_stride;
-                if (t0 + col < t_end) er[t0 + col] = e0;
-                if (t0 + 32 + col < t_end) er[t0 + 32 + col] = e1;
+            float *er = err + slice * sl.S_stride;
+#pragma unroll
+            for (int hb = 0; hb < HB; ++hb) {
+                e[hb] += __shfl_xor(e[hb], 32);
+                if (khalf == 0 && t0 + hb * 32 + col < t_end) er[t0 + hb * 32 + col] = e[hb];
             }
         }
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+            for (int s = 0; s < 8; ++s) b[hb][s] = bn[hb][s];
     }
 }
 
@@ -311,22 +331,34 @@ __global__ __launch_bounds__(256) void reconstruct_kernel(const float *__restric
     const float *xt = Xt + slice * sl.S_stride * R;
     float *xh = Xh + slice * sl.S_stride * kHeadDim;
 
-    for (int64_t t0 = t_begin + wave * 32; t0 < t_end; t0 += (blockDim.x / 64) * 32) {
+    // X~ rows of a wave step: lane (col, khalf) holds ranks 16s + 8khalf .. +8 of
+    // token t0 + col (B operand), split hi/lo once the step's data is in hand
+    const int64_t wstep = (blockDim.x / 64) * 32;
+    float4 xc[2 * KS], xn[2 * KS];
+#define KVC_LOAD_X(T0, DST)                                                                      \
+    do {                                                                                          \
+        const int64_t tok_ = (T0) + col;                                                          \
+        const bool ok_ = tok_ < t_end;                                                            \
+        const float4 *src_ = reinterpret_cast<const float4 *>(xt + (ok_ ? tok_ : 0) * R + khalf * 8); \
+        _Pragma("unroll") for (int s_ = 0; s_ < 2 * KS; ++s_) {                                   \
+            DST[s_] = src_[(s_ >> 1) * 4 + (s_ & 1)];                                             \
+            if (!ok_) DST[s_] = make_float4(0.f, 0.f, 0.f, 0.f);                                  \
+        }                                                                                         \
+    } while (0)
+    if (t_begin + wave * 32 < t_end) KVC_LOAD_X(t_begin + wave * 32, xc);
+    for (int64_t t0 = t_begin + wave * 32; t0 < t_end; t0 += wstep) {
+        if (t0 + wstep < t_end) KVC_LOAD_X(t0 + wstep, xn);  // next step in flight
         const int64_t tok = t0 + col;
         const bool ok = tok < t_end;
         u32x4 bh[KS], bl[KS];
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
-            float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-            if (ok) {
-                const float4 *src = reinterpret_cast<const float4 *>(xt + tok * R + 16 * s + khalf * 8);
-                const float4 v0 = src[0], v1 = src[1];
-                x[0] = v0.x; x[1] = v0.y; x[2] = v0.z; x[3] = v0.w;
-                x[4] = v1.x; x[5] = v1.y; x[6] = v1.z; x[7] = v1.w;
-            }
+            float x[8];
+            x[0] = xc[2 * s].x; x[1] = xc[2 * s].y; x[2] = xc[2 * s].z; x[3] = xc[2 * s].w;
+            x[4] = xc[2 * s + 1].x; x[5] = xc[2 * s + 1].y; x[6] = xc[2 * s + 1].z; x[7] = xc[2 * s + 1].w;
             split8(x, bh[s], bl[s]);
         }
-#pragma unroll
+#pragma unroll 1
         for (int cb = 0; cb < 4; ++cb) {
             f32x16 acc = {};
 #pragma unroll
@@ -345,7 +377,10 @@ __global__ __launch_bounds__(256) void reconstruct_kernel(const float *__restric
                         make_float4(acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]);
             }
         }
+#pragma unroll
+        for (int s = 0; s < 2 * KS; ++s) xc[s] = xn[s];
     }
+#undef KVC_LOAD_X
 }
 
 // Anchor rows back into X^: 16 lanes per row, bf16 widened exactly.
@@ -411,36 +446,41 @@ void compress_ws_layout(Ws &ws, const kvc_dims *d, bool with_q) {
         const int64_t G = d->L * d->B * d->H_kv;
         const int64_t nq = (d->H_q / d->H_kv) * d->W_q;
         const int64_t nqb = (nq + 31) / 32;
-        ws.template take<u32x4>(static_cast<size_t>(G * nqb * 8 * kQParts * 64));
+        ws.template take<u32x4>(static_cast<size_t>(G * nqb * 8 * query_terms(nq) * 64));
     }
 }
 
+#ifndef KVC_PROJECT_HB
+#define KVC_PROJECT_HB 2
+#endif
 template <int NRB>
 kvc_status launch_project(const uint16_t *X, const float *U, const u32x4 *qfrag, int nqb,
-                          const Slices &sl, int64_t G, float *Xt, float *err, hipStream_t stream) {
-    const size_t lds = static_cast<size_t>(NRB * 16 + nqb * 8 * kQParts) * kFragBytes;
+                          int nterm, const Slices &sl, int64_t G, float *Xt, float *err,
+                          hipStream_t stream) {
+    constexpr int HB = KVC_PROJECT_HB;
+    const size_t lds = static_cast<size_t>(NRB * 16 + nqb * 8 * nterm) * kFragBytes;
     static bool attr_set = false;
     if (!attr_set) {
-        if (hipFuncSetAttribute(reinterpret_cast<const void *>(&project_kernel<NRB>),
+        if (hipFuncSetAttribute(reinterpret_cast<const void *>(&project_kernel<NRB, HB>),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) != hipSuccess)
             return KVC_ERR_HIP;
         attr_set = true;
     }
     const int64_t blocks = G * sl.nsplit;
     if (blocks > INT32_MAX) return KVC_ERR_UNSUPPORTED;
-    hipLaunchKernelGGL(project_kernel<NRB>, dim3(static_cast<unsigned>(blocks)), dim3(512), lds,
-                       stream, X, U, qfrag, nqb, sl, Xt, err);
+    hipLaunchKernelGGL((project_kernel<NRB, HB>), dim3(static_cast<unsigned>(blocks)),
+                       dim3(HB == 1 ? 1024 : 512), lds, stream, X, U, qfrag, nqb, nterm, sl, Xt, err);
     return launch_status();
 }
 
 kvc_status project_dispatch(int64_t R, const uint16_t *X, const float *U, const u32x4 *qfrag,
-                            int nqb, const Slices &sl, int64_t G, float *Xt, float *err,
+                            int nqb, int nterm, const Slices &sl, int64_t G, float *Xt, float *err,
                             hipStream_t stream) {
     switch (R) {
-        case 32: return launch_project<1>(X, U, qfrag, nqb, sl, G, Xt, err, stream);
-        case 64: return launch_project<2>(X, U, qfrag, nqb, sl, G, Xt, err, stream);
-        case 96: return launch_project<3>(X, U, qfrag, nqb, sl, G, Xt, err, stream);
-        case 128: return launch_project<4>(X, U, qfrag, nqb, sl, G, Xt, err, stream);
+        case 32: return launch_project<1>(X, U, qfrag, nqb, nterm, sl, G, Xt, err, stream);
+        case 64: return launch_project<2>(X, U, qfrag, nqb, nterm, sl, G, Xt, err, stream);
+        case 96: return launch_project<3>(X, U, qfrag, nqb, nterm, sl, G, Xt, err, stream);
+        case 128: return launch_project<4>(X, U, qfrag, nqb, nterm, sl, G, Xt, err, stream);
     }
     return KVC_ERR_UNSUPPORTED;
 }
@@ -494,13 +534,14 @@ extern "C" kvc_status kvc_lowrank_compress(const kvc_dims *d, const uint16_t *K,
     if (ws_bytes < sz.bytes()) return KVC_ERR_WORKSPACE_TOO_SMALL;
 
     const Slices sl = make_slices(d, 512);
-    int nqb = 0;
+    int nqb = 0, nterm = 0;
     u32x4 *qfrag = nullptr;
     if (with_q) {
         WsCursor cur(ws);
         const int64_t nq = (d->H_q / d->H_kv) * d->W_q;
         nqb = static_cast<int>((nq + 31) / 32);
-        qfrag = cur.take<u32x4>(static_cast<size_t>(G * nqb * 8 * kQParts * 64));
+        nterm = query_terms(nq);
+        qfrag = cur.take<u32x4>(static_cast<size_t>(G * nqb * 8 * nterm * 64));
         const double scale = 1.0 / (static_cast<double>(nq) * sqrt(static_cast<double>(d->D)));
         static bool attr_set = false;
         if (!attr_set) {
@@ -517,12 +558,12 @@ extern "C" kvc_status kvc_lowrank_compress(const kvc_dims *d, const uint16_t *K,
         hipLaunchKernelGGL(prep_query_kernel, dim3(static_cast<unsigned>(G)), dim3(256), prep_lds, stream,
                            Q_win, U_k,
                            d->B, d->H_kv, d->H_q, d->W_q, static_cast<int>(d->R),
-                           static_cast<int>(nq), nqb, scale, qfrag);
+                           static_cast<int>(nq), nqb, nterm, scale, qfrag);
         if ((st = launch_status()) != KVC_OK) return st;
     }
-    st = project_dispatch(d->R, K, U_k, qfrag, nqb, sl, G, K_tilde, err, stream);
+    st = project_dispatch(d->R, K, U_k, qfrag, nqb, nterm, sl, G, K_tilde, err, stream);
     if (st != KVC_OK) return st;
-    if (V) st = project_dispatch(d->R, V, U_v, nullptr, 0, sl, G, V_tilde, nullptr, stream);
+    if (V) st = project_dispatch(d->R, V, U_v, nullptr, 0, 0, sl, G, V_tilde, nullptr, stream);
     return st;
 }
 
