@@ -133,6 +133,12 @@ __global__ __launch_bounds__(kThreads) void l2_distance(const uint16_t *__restri
 #ifndef KVC_FUSE_ROWS
 #define KVC_FUSE_ROWS 16
 #endif
+#ifndef KVC_FUSE_DEPTH
+#define KVC_FUSE_DEPTH 2
+#endif
+#ifndef KVC_FUSE_MINBLOCKS
+#define KVC_FUSE_MINBLOCKS 3
+#endif
 constexpr int kFuseThreads = 256;
 constexpr int kFuseRows = KVC_FUSE_ROWS;                      // rows per thread (8 or 16)
 constexpr int kFuseTile = (kFuseThreads / 16) * kFuseRows;    // 256 tokens per tile
@@ -205,7 +211,7 @@ __device__ __forceinline__ uint64_t tagged(float mu) {
     return (static_cast<uint64_t>(kReady) << 32) | __float_as_uint(mu);
 }
 
-__global__ __launch_bounds__(kFuseThreads, 3) void l2_fused(const uint16_t *__restrict__ K, FuseGeom geo,
+__global__ __launch_bounds__(kFuseThreads, KVC_FUSE_MINBLOCKS) void l2_fused(const uint16_t *__restrict__ K, FuseGeom geo,
                                                          float *partial, uint64_t *mu_pub,
                                                          uint32_t *counters, uint32_t *status,
                                                          float *__restrict__ scores,
@@ -333,6 +339,56 @@ __global__ __launch_bounds__(kFuseThreads, 3) void l2_fused(const uint16_t *__re
         }
     };
 
+#if KVC_FUSE_DEPTH == 3
+    // Three tiles per workgroup: tile i is scored while tile i+1 (published one
+    // iteration earlier) waits for its centroid and tile i+2 is loading, so a
+    // team's centroid is fetched a full iteration after its partials went out.
+    uint4 v0[kFuseRows], v1[kFuseRows], v2[kFuseRows];
+    const int64_t step = gridDim.x;
+    int64_t tile = blockIdx.x;
+    if (tile < geo.tiles) {
+        const TileGeo t = geo_of(tile);
+        load_tile(t, v0);
+        publish(tile, t, v0);
+    }
+    if (tile + step < geo.tiles) load_tile(geo_of(tile + step), v1);
+    for (; tile < geo.tiles; tile += step) {
+        const TileGeo t = geo_of(tile);
+        const int64_t n1 = tile + step, n2 = tile + 2 * step;
+        if (n2 < geo.tiles) load_tile(geo_of(n2), v2);
+        if (n1 < geo.tiles) publish(n1, geo_of(n1), v1);
+        fetch_mu(t);
+        float m[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) m[j] = mu_s[lane16 * 8 + j];
+        float d2[kFuseRows];
+#pragma unroll
+        for (int r = 0; r < kFuseRows; ++r) {
+            float x[8];
+            widen8(v0[r], x);
+            float acc = 0.f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float d = x[j] - m[j];
+                acc += d * d;
+            }
+            d2[r] = acc;
+        }
+        row_transpose_reduce<kFuseRows>(d2, lane16);
+        {
+            const int r = kFuseRows == 16 ? lane16 : (lane16 >> 1);
+            const int64_t row = t.t0 + 16 * r;
+            if ((kFuseRows == 16 || (lane16 & 1) == 0) && row < t.w1)
+                scores[t.g * geo.S + row] = sqrtf(d2[0]);
+        }
+        __syncthreads();  // mu_s is rewritten by the next fetch
+#pragma unroll
+        for (int r = 0; r < kFuseRows; ++r) {
+            v0[r] = v1[r];
+            v1[r] = v2[r];
+        }
+    }
+#else
     uint4 v[kFuseRows], vn[kFuseRows];
     int64_t tile = blockIdx.x;
     if (tile < geo.tiles) {
@@ -380,6 +436,7 @@ __global__ __launch_bounds__(kFuseThreads, 3) void l2_fused(const uint16_t *__re
 #pragma unroll
         for (int r = 0; r < kFuseRows; ++r) v[r] = vn[r];
     }
+#endif
 }
 
 FuseGeom make_fuse_geom(int64_t G, int64_t S, int64_t W) {
