@@ -133,9 +133,6 @@ __global__ __launch_bounds__(kThreads) void l2_distance(const uint16_t *__restri
 #ifndef KVC_FUSE_ROWS
 #define KVC_FUSE_ROWS 16
 #endif
-#ifndef KVC_FUSE_DEPTH
-#define KVC_FUSE_DEPTH 2
-#endif
 #ifndef KVC_FUSE_MINBLOCKS
 #define KVC_FUSE_MINBLOCKS 3
 #endif
@@ -319,9 +316,10 @@ __global__ __launch_bounds__(kFuseThreads, KVC_FUSE_MINBLOCKS) void l2_fused(con
         __syncthreads();  // red is reused by the caller
     };
     // The team's centroid into mu_s: each channel's tagged word is polled
-    // until ready (bounded; past the limit a status bit is set).
+    // until ready, with back-off (bounded; past the limit a status bit is set).
     auto fetch_mu = [&](const TileGeo &t) {
         uint32_t spins = 0;
+        int nap = 1;
         for (;;) {
             bool ready = true;
             if (tid < kHeadDim) {
@@ -335,60 +333,15 @@ __global__ __launch_bounds__(kFuseThreads, KVC_FUSE_MINBLOCKS) void l2_fused(con
                 if (tid == 0) atomicOr(status, 1u);
                 break;
             }
-            __builtin_amdgcn_s_sleep(1);
+            // back-off: a team polls the same few lines; hammering them costs
+            // the data loads bandwidth on those memory channels
+            if (nap <= 1) __builtin_amdgcn_s_sleep(1);
+            else if (nap <= 4) __builtin_amdgcn_s_sleep(4);
+            else __builtin_amdgcn_s_sleep(16);
+            nap = nap < 16 ? nap * 2 : 16;
         }
     };
 
-#if KVC_FUSE_DEPTH == 3
-    // Three tiles per workgroup: tile i is scored while tile i+1 (published one
-    // iteration earlier) waits for its centroid and tile i+2 is loading, so a
-    // team's centroid is fetched a full iteration after its partials went out.
-    uint4 v0[kFuseRows], v1[kFuseRows], v2[kFuseRows];
-    const int64_t step = gridDim.x;
-    int64_t tile = blockIdx.x;
-    if (tile < geo.tiles) {
-        const TileGeo t = geo_of(tile);
-        load_tile(t, v0);
-        publish(tile, t, v0);
-    }
-    if (tile + step < geo.tiles) load_tile(geo_of(tile + step), v1);
-    for (; tile < geo.tiles; tile += step) {
-        const TileGeo t = geo_of(tile);
-        const int64_t n1 = tile + step, n2 = tile + 2 * step;
-        if (n2 < geo.tiles) load_tile(geo_of(n2), v2);
-        if (n1 < geo.tiles) publish(n1, geo_of(n1), v1);
-        fetch_mu(t);
-        float m[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) m[j] = mu_s[lane16 * 8 + j];
-        float d2[kFuseRows];
-#pragma unroll
-        for (int r = 0; r < kFuseRows; ++r) {
-            float x[8];
-            widen8(v0[r], x);
-            float acc = 0.f;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const float d = x[j] - m[j];
-                acc += d * d;
-            }
-            d2[r] = acc;
-        }
-        row_transpose_reduce<kFuseRows>(d2, lane16);
-        {
-            const int r = kFuseRows == 16 ? lane16 : (lane16 >> 1);
-            const int64_t row = t.t0 + 16 * r;
-            if ((kFuseRows == 16 || (lane16 & 1) == 0) && row < t.w1)
-                scores[t.g * geo.S + row] = sqrtf(d2[0]);
-        }
-        __syncthreads();  // mu_s is rewritten by the next fetch
-#pragma unroll
-        for (int r = 0; r < kFuseRows; ++r) {
-            v0[r] = v1[r];
-            v1[r] = v2[r];
-        }
-    }
-#else
     uint4 v[kFuseRows], vn[kFuseRows];
     int64_t tile = blockIdx.x;
     if (tile < geo.tiles) {
@@ -436,7 +389,6 @@ __global__ __launch_bounds__(kFuseThreads, KVC_FUSE_MINBLOCKS) void l2_fused(con
 #pragma unroll
         for (int r = 0; r < kFuseRows; ++r) v[r] = vn[r];
     }
-#endif
 }
 
 FuseGeom make_fuse_geom(int64_t G, int64_t S, int64_t W) {

@@ -15,6 +15,8 @@
 //     scan gives every kept key its output slot, equal keys taken lowest
 //     index first until `need` are taken.
 // gather_rows: 16 lanes per 256-byte row, 16-byte loads and stores.
+#include <stdlib.h>
+
 #include "kvc_internal.h"
 
 namespace kvc {
@@ -59,7 +61,11 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *w
 __global__ __launch_bounds__(kSelThreads) void select_compact(const float *__restrict__ scores,
                                                               int64_t S, int64_t s_stride,
                                                               int64_t k,
-                                                              int32_t *__restrict__ idx_out) {
+                                                              int32_t *__restrict__ idx_out,
+                                                              const uint16_t *__restrict__ K,
+                                                              const uint16_t *__restrict__ V,
+                                                              uint16_t *__restrict__ K_out,
+                                                              uint16_t *__restrict__ V_out) {
     const int64_t g = blockIdx.x;
     const float *s = scores + g * s_stride;
     int32_t *out = idx_out + g * k;
@@ -154,6 +160,48 @@ __global__ __launch_bounds__(kSelThreads) void select_compact(const float *__res
         out_pos += tile_gt + (min(eq_seen + tile_eq, need) - min(eq_seen, need));
         eq_seen += tile_eq;
     }
+    if (!K && !V) return;
+    // Compaction of the slice's rows by the same workgroup, as soon as its
+    // indices exist: 16 lanes per 256-byte row, 4 rows per thread in flight.
+    __syncthreads();  // this workgroup's index writes are visible to it
+    const int lane16 = threadIdx.x & 15;
+    const int rsub = threadIdx.x >> 4;  // 0..63
+    const uint4 *Ks = K ? reinterpret_cast<const uint4 *>(K + g * s_stride * kHeadDim) : nullptr;
+    const uint4 *Vs = V ? reinterpret_cast<const uint4 *>(V + g * s_stride * kHeadDim) : nullptr;
+    uint4 *Ko = K_out ? reinterpret_cast<uint4 *>(K_out + g * k * kHeadDim) : nullptr;
+    uint4 *Vo = V_out ? reinterpret_cast<uint4 *>(V_out + g * k * kHeadDim) : nullptr;
+    constexpr int kRowsPerPass = kSelThreads / 16;  // 64
+    constexpr int kUnroll = 4;  // rows per thread in flight (fetch(0..3) below)
+    for (int64_t i0 = 0; i0 < k; i0 += kRowsPerPass * kUnroll) {
+        int64_t src0, src1, src2, src3;
+        bool ok0, ok1, ok2, ok3;
+        auto fetch = [&](int u, int64_t &src, bool &ok) {
+            const int64_t i = i0 + u * kRowsPerPass + rsub;
+            const int64_t t = i < k ? out[i] : -1;
+            ok = t >= 0 && t < S;  // never read outside the slice
+            src = ok ? t : 0;
+        };
+        fetch(0, src0, ok0);
+        fetch(1, src1, ok1);
+        fetch(2, src2, ok2);
+        fetch(3, src3, ok3);
+        if (Ks) {
+            const uint4 a0 = Ks[src0 * 16 + lane16], a1 = Ks[src1 * 16 + lane16];
+            const uint4 a2 = Ks[src2 * 16 + lane16], a3 = Ks[src3 * 16 + lane16];
+            if (ok0) Ko[(i0 + 0 * kRowsPerPass + rsub) * 16 + lane16] = a0;
+            if (ok1) Ko[(i0 + 1 * kRowsPerPass + rsub) * 16 + lane16] = a1;
+            if (ok2) Ko[(i0 + 2 * kRowsPerPass + rsub) * 16 + lane16] = a2;
+            if (ok3) Ko[(i0 + 3 * kRowsPerPass + rsub) * 16 + lane16] = a3;
+        }
+        if (Vs) {
+            const uint4 b0 = Vs[src0 * 16 + lane16], b1 = Vs[src1 * 16 + lane16];
+            const uint4 b2 = Vs[src2 * 16 + lane16], b3 = Vs[src3 * 16 + lane16];
+            if (ok0) Vo[(i0 + 0 * kRowsPerPass + rsub) * 16 + lane16] = b0;
+            if (ok1) Vo[(i0 + 1 * kRowsPerPass + rsub) * 16 + lane16] = b1;
+            if (ok2) Vo[(i0 + 2 * kRowsPerPass + rsub) * 16 + lane16] = b2;
+            if (ok3) Vo[(i0 + 3 * kRowsPerPass + rsub) * 16 + lane16] = b3;
+        }
+    }
 }
 
 constexpr int kGatherThreads = 256;
@@ -181,6 +229,12 @@ __global__ __launch_bounds__(kGatherThreads) void gather_rows(
     }
 }
 
+// KVC_GATHER_SEPARATE=1 in the environment selects the separate gather launch.
+bool fused_gather() {
+    const char *e = getenv("KVC_GATHER_SEPARATE");
+    return !(e && e[0] == '1');
+}
+
 }  // namespace
 
 size_t topk_workspace_bytes(int64_t, int64_t, int64_t) { return 0; }
@@ -204,8 +258,15 @@ extern "C" kvc_status kvc_topk_compact(const float *scores, int64_t G, int64_t S
         return KVC_ERR_INVALID_ARGUMENT;
     if ((K && (!aligned(K, 16) || !aligned(K_out, 16))) || (V && (!aligned(V, 16) || !aligned(V_out, 16))))
         return KVC_ERR_INVALID_ARGUMENT;
+    // the selecting workgroup also copies its slice's rows when the copy is
+    // small (k <= 8192 rows per slice); larger copies go to a wide gather launch
+    if ((K || V) && k <= 8192 && fused_gather()) {
+        hipLaunchKernelGGL(select_compact, dim3(static_cast<unsigned>(G)), dim3(kSelThreads), 0, stream,
+                           scores, S, s_stride, k, idx_out, K, V, K_out, V_out);
+        return launch_status();
+    }
     hipLaunchKernelGGL(select_compact, dim3(static_cast<unsigned>(G)), dim3(kSelThreads), 0, stream,
-                       scores, S, s_stride, k, idx_out);
+                       scores, S, s_stride, k, idx_out, nullptr, nullptr, nullptr, nullptr);
     if (K || V) {
         const int64_t bps = (k + kGatherRows - 1) / kGatherRows;
         if (G * bps > INT32_MAX) return KVC_ERR_UNSUPPORTED;
