@@ -34,6 +34,7 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kFragBytes = 64 * 16;  // one MFMA operand fragment: 64 lanes x 8 bf16
 
+
 __device__ __forceinline__ f32x16 mfma32x32x16(u32x4 a, u32x4 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
                                                    __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
@@ -164,7 +165,7 @@ __global__ __launch_bounds__(256) void prep_query_kernel(const uint16_t *__restr
 // LDS: U^T fragments [rb][s][hi|lo] (NRB*16 KB), then Q'' fragments
 // [qb][s][term] (nqb*8*nterm KB).  HB = 1 runs 16 waves per block (4 per SIMD),
 // HB = 2 runs 8 waves with twice the reuse of each fragment.
-template <int NRB, int HB>
+template <int NRB, int HB, bool kRowStores>
 __global__ __launch_bounds__(HB == 1 ? 1024 : 512) void project_kernel(
     const uint16_t *__restrict__ X, const float *__restrict__ Ubase, const u32x4 *__restrict__ qfrag,
     int nqb, int nterm, Slices sl, float *__restrict__ Xt, float *__restrict__ err) {
@@ -205,6 +206,9 @@ __global__ __launch_bounds__(HB == 1 ? 1024 : 512) void project_kernel(
     const int col = lane & 31, khalf = lane >> 5;
     const u32x4 *xrows = reinterpret_cast<const u32x4 *>(X + slice * sl.S_stride * kHeadDim);
     float *xt = Xt + slice * sl.S_stride * R;
+    // Projection-only launches (no error score) write K~ rows in full 128-byte
+    // segments; with the score fused, register pressure favours 16-byte pieces.
+    constexpr bool row_stores = kRowStores;
 
     // key tile of a wave step: lane (col, khalf) holds 16 bytes of token t0+32hb+col
     // at channel 16s + 8khalf, s = 0..7 (B operand of the k-steps)
@@ -236,20 +240,41 @@ __global__ __launch_bounds__(HB == 1 ? 1024 : 512) void project_kernel(
             for (int s = 0; s < 8; ++s) {
                 const u32x4 fh = ufr[((rb * 8 + s) * 2 + 0) * 64 + lane];
                 const u32x4 fl = ufr[((rb * 8 + s) * 2 + 1) * 64 + lane];
+                if constexpr (row_stores) {
+                    // keys as the A operand (same registers): D[token][rank]
 #pragma unroll
-                for (int hb = 0; hb < HB; ++hb) a[hb] = mfma32x32x16(fh, b[hb][s], a[hb]);
+                    for (int hb = 0; hb < HB; ++hb) a[hb] = mfma32x32x16(b[hb][s], fh, a[hb]);
 #pragma unroll
-                for (int hb = 0; hb < HB; ++hb) a[hb] = mfma32x32x16(fl, b[hb][s], a[hb]);
+                    for (int hb = 0; hb < HB; ++hb) a[hb] = mfma32x32x16(b[hb][s], fl, a[hb]);
+                } else {
+#pragma unroll
+                    for (int hb = 0; hb < HB; ++hb) a[hb] = mfma32x32x16(fh, b[hb][s], a[hb]);
+#pragma unroll
+                    for (int hb = 0; hb < HB; ++hb) a[hb] = mfma32x32x16(fl, b[hb][s], a[hb]);
+                }
             }
+            if constexpr (row_stores) {
+                // lane (col, khalf) holds rank rb*32+col of tokens 8(j/4) + 4khalf + j%4:
+                // each store writes two 128-byte row segments
 #pragma unroll
-            for (int hb = 0; hb < HB; ++hb) {
-                const int64_t tok = t0 + hb * 32 + col;
-                if (tok < t_end) {
-                    float *dst = xt + tok * R + rb * 32 + khalf * 4;
+                for (int hb = 0; hb < HB; ++hb)
 #pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        *reinterpret_cast<float4 *>(dst + q * 8) =
-                            make_float4(a[hb][4 * q], a[hb][4 * q + 1], a[hb][4 * q + 2], a[hb][4 * q + 3]);
+                    for (int j = 0; j < 16; ++j) {
+                        const int64_t tok = t0 + hb * 32 + (j >> 2) * 8 + khalf * 4 + (j & 3);
+                        if (tok < t_end) xt[tok * R + rb * 32 + col] = a[hb][j];
+                    }
+            } else {
+                // lane (col, khalf) holds ranks rb*32 + 8q + 4khalf .. +4 of token col
+#pragma unroll
+                for (int hb = 0; hb < HB; ++hb) {
+                    const int64_t tok = t0 + hb * 32 + col;
+                    if (tok < t_end) {
+                        float *dst = xt + tok * R + rb * 32 + khalf * 4;
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            *reinterpret_cast<float4 *>(dst + q * 8) =
+                                make_float4(a[hb][4 * q], a[hb][4 * q + 1], a[hb][4 * q + 2], a[hb][4 * q + 3]);
+                    }
                 }
             }
         }
@@ -365,16 +390,17 @@ __global__ __launch_bounds__(256) void reconstruct_kernel(const float *__restric
             for (int s = 0; s < KS; ++s) {
                 const u32x4 ah = ufr[((cb * KS + s) * 2 + 0) * 64 + lane];
                 const u32x4 al = ufr[((cb * KS + s) * 2 + 1) * 64 + lane];
-                acc = mfma32x32x16(ah, bh[s], acc);
-                acc = mfma32x32x16(al, bh[s], acc);
-                acc = mfma32x32x16(ah, bl[s], acc);
+                // X~ as the A operand (its registers are laid out as B's): D[token][channel]
+                acc = mfma32x32x16(bh[s], ah, acc);
+                acc = mfma32x32x16(bh[s], al, acc);
+                acc = mfma32x32x16(bl[s], ah, acc);
             }
-            if (ok) {
-                float *dst = xh + tok * kHeadDim + cb * 32 + khalf * 4;
+            // lane (col, khalf) holds channel cb*32+col of tokens 8(j/4) + 4khalf + j%4:
+            // each store writes two 128-byte row segments
 #pragma unroll
-                for (int q = 0; q < 4; ++q)
-                    *reinterpret_cast<float4 *>(dst + q * 8) =
-                        make_float4(acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]);
+            for (int j = 0; j < 16; ++j) {
+                const int64_t tj = t0 + (j >> 2) * 8 + khalf * 4 + (j & 3);
+                if (tj < t_end) xh[tj * kHeadDim + cb * 32 + col] = acc[j];
             }
         }
 #pragma unroll
@@ -453,24 +479,32 @@ void compress_ws_layout(Ws &ws, const kvc_dims *d, bool with_q) {
 #ifndef KVC_PROJECT_HB
 #define KVC_PROJECT_HB 2
 #endif
-template <int NRB>
-kvc_status launch_project(const uint16_t *X, const float *U, const u32x4 *qfrag, int nqb,
-                          int nterm, const Slices &sl, int64_t G, float *Xt, float *err,
-                          hipStream_t stream) {
+template <int NRB, bool kRowStores>
+kvc_status launch_project_variant(const uint16_t *X, const float *U, const u32x4 *qfrag, int nqb,
+                                  int nterm, const Slices &sl, int64_t G, float *Xt, float *err,
+                                  hipStream_t stream) {
     constexpr int HB = KVC_PROJECT_HB;
     const size_t lds = static_cast<size_t>(NRB * 16 + nqb * 8 * nterm) * kFragBytes;
     static bool attr_set = false;
     if (!attr_set) {
-        if (hipFuncSetAttribute(reinterpret_cast<const void *>(&project_kernel<NRB, HB>),
+        if (hipFuncSetAttribute(reinterpret_cast<const void *>(&project_kernel<NRB, HB, kRowStores>),
                                 hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) != hipSuccess)
             return KVC_ERR_HIP;
         attr_set = true;
     }
     const int64_t blocks = G * sl.nsplit;
     if (blocks > INT32_MAX) return KVC_ERR_UNSUPPORTED;
-    hipLaunchKernelGGL((project_kernel<NRB, HB>), dim3(static_cast<unsigned>(blocks)),
+    hipLaunchKernelGGL((project_kernel<NRB, HB, kRowStores>), dim3(static_cast<unsigned>(blocks)),
                        dim3(HB == 1 ? 1024 : 512), lds, stream, X, U, qfrag, nqb, nterm, sl, Xt, err);
     return launch_status();
+}
+
+template <int NRB>
+kvc_status launch_project(const uint16_t *X, const float *U, const u32x4 *qfrag, int nqb,
+                          int nterm, const Slices &sl, int64_t G, float *Xt, float *err,
+                          hipStream_t stream) {
+    return nqb > 0 ? launch_project_variant<NRB, false>(X, U, qfrag, nqb, nterm, sl, G, Xt, err, stream)
+                   : launch_project_variant<NRB, true>(X, U, qfrag, nqb, nterm, sl, G, Xt, err, stream);
 }
 
 kvc_status project_dispatch(int64_t R, const uint16_t *X, const float *U, const u32x4 *qfrag,
