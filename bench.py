@@ -29,6 +29,27 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0    # MI355X HBM3E
 MFMA_BF16_PEAK_TFLOPS = 2500.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+
+
+def source_digest(path):
+    import hashlib
+    with open(os.path.join(ROOT, path), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def measured_traffic(entry_point, config):
+    """Scaled FETCH_SIZE + WRITE_SIZE bytes per launch of an entry point, as
+    recorded from rocprofv3 counter runs (profiles/hbm_traffic.json); None when
+    absent or when the kernel source changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            rec = json.load(f)["entries"]["%s/config%d" % (entry_point, config)]
+    except (OSError, KeyError, ValueError):
+        return None
+    if any(source_digest(p) != h for p, h in rec["sources"].items()):
+        return None
+    return rec["bytes_per_launch"]
 
 
 def parse():
@@ -99,7 +120,8 @@ def manifold_workload(cfg, dev):
         Op("kvc_topk_compact",
            lambda: kvc.kvc_topk_compact(buf.scores, keep, K, V, idx_out=buf.idx, K_out=buf.K_out,
                                         V_out=buf.V_out),
-           G * S * 4 + G * keep * (2 * 256 * 2 + 4), kernel="select_compact+gather_rows"),
+           G * S * 4 + G * keep * (2 * 256 * 2 + 4),
+           kernel="select_compact" if keep <= 8192 and G >= 256 else "select_compact+gather_rows"),
     ]
     algo = G * S * 256 + G * keep * 256 + 2 * G * keep * 256 + G * S * 4 + G * keep * 4
     config = {"workload": desc, "slices": G, "seq_len": S, "keep": keep, "head_dim": 128,
@@ -109,9 +131,10 @@ def manifold_workload(cfg, dev):
         import numpy as np
         import oracle
         done, t = 0, 0.0
-        while done < G and t < budget:
-            kb = synth.bf16_bits(K[done:done + 1])
-            vb = synth.bf16_bits(V[done:done + 1])
+        while t < budget and done < 64 * G:
+            g = done % G
+            kb = synth.bf16_bits(K[g:g + 1])
+            vb = synth.bf16_bits(V[g:g + 1])
             t0 = time.perf_counter()
             sc, _ = oracle.score_l2(kb) if W is None else oracle.score_l2_windowed(kb, W)
             idx = oracle.topk(sc.astype(np.float32), keep)
@@ -119,7 +142,8 @@ def manifold_workload(cfg, dev):
             oracle.gather(vb, idx)
             t += time.perf_counter() - t0
             done += 1
-        return done * S, t, "%d of %d slices (S=%d each) of the same workload" % (done, G, S)
+        return done * S, t, "%d slice passes (S=%d each; the workload has %d slices, taken in order)" % (
+            done, S, G)
 
     return ops, G * S, algo, config, cpu
 
@@ -142,7 +166,7 @@ def oja_workload(dev):
         Op("kvc_topk_compact",
            lambda: kvc.kvc_topk_compact(st.err, k, inp.K, inp.V, idx_out=st.idx, K_out=st.K_anchor,
                                         V_out=st.V_anchor),
-           G * S * 4 + G * k * (2 * 256 * 2 + 4), kernel="select_compact+gather_rows"),
+           G * S * 4 + G * k * (2 * 256 * 2 + 4), kernel="select_compact"),
     ]
     algo = G * S * (2 * 256 + 2 * R * 4 + 4) + G * k * (2 * 256 * 2 + 4)
     config = {"workload": "OjaKV hybrid low-rank prefill compression, 32 layers x batch 4 x 8 KV heads "
@@ -264,35 +288,31 @@ def main():
         ops, head_tokens, algo, config, cpu = manifold_workload(args.config, dev)
     torch.cuda.synchronize()
 
-    def step(record=False):
-        for op in ops:
-            if record:
-                a = torch.cuda.Event(enable_timing=True)
-                b = torch.cuda.Event(enable_timing=True)
-                a.record()
-                op.fn()
-                b.record()
-                op.ms.append((a, b))
-            else:
-                op.fn()
-
     for _ in range(args.warmup):
-        step()
+        for op in ops:
+            op.fn()
     torch.cuda.synchronize()
+    # every entry point is bracketed by events on the stream its kernels are launched on
+    # (torch's current stream, which the binding passes to libkvc), inside the timed region
+    ev = [[(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in ops] for _ in range(args.steps)]
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     t0.record()
-    for _ in range(args.steps):
-        step()
+    for i in range(args.steps):
+        for op, (a, b) in zip(ops, ev[i]):
+            a.record()
+            op.fn()
+            b.record()
     t1.record()
     torch.cuda.synchronize()
     ms_step = t0.elapsed_time(t1) / args.steps
-    for _ in range(args.steps):
-        step(record=True)
-    torch.cuda.synchronize()
+    for i in range(args.steps):
+        for op, (a, b) in zip(ops, ev[i]):
+            op.ms.append(a.elapsed_time(b))
     per_op = {}
     for op in ops:
-        ms = sum(a.elapsed_time(b) for a, b in op.ms) / len(op.ms)
+        ms = sum(op.ms) / len(op.ms)
         per_op[op.name] = {"ms": ms, "bytes": op.nbytes, "GBs": op.nbytes / ms / 1e6,
                            "kernel": op.kernel}
         if op.flops:
@@ -301,8 +321,10 @@ def main():
     achieved = per_op[dom]["GBs"]
     line = base_line(args, "KV head-tokens scored+compacted/s", head_tokens / (ms_step / 1e3),
                      ms_step, args.steps, config)
-    line["roofline"] = {"bound": "hbm", "kernel": dom, "achieved": achieved, "peak": HBM_PEAK_GBS,
-                        "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": None}
+    line["roofline"] = {"bound": "hbm", "entry_point": dom, "kernel": per_op[dom]["kernel"],
+                        "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                        "traffic": measured_traffic(dom, args.config),
+                        "algorithmic_bytes": per_op[dom]["bytes"]}
     if "TFLOPs" in per_op[dom]:
         line["roofline"]["mfma_TFLOPs"] = per_op[dom]["TFLOPs"]
         line["roofline"]["mfma_frac"] = per_op[dom]["TFLOPs"] / MFMA_BF16_PEAK_TFLOPS

@@ -73,6 +73,27 @@ def test_topk_strided_and_gather_bit_exact(gpu_lib):
     np.testing.assert_array_equal(synth.bf16_bits(Vo), oracle.gather(synth.bf16_bits(V), ref_idx, S=S))
 
 
+@pytest.mark.parametrize("separate", [False, True])
+def test_gather_paths_bit_exact(gpu_lib, monkeypatch, separate):
+    # 300 slices (more than one per compute unit, so the selecting workgroup copies the
+    # rows itself unless the separate launch is forced), ragged S, strided cache,
+    # k from 1 to S including the 8192-row boundary of the in-workgroup copy
+    G, S, stride = 300, 8197, 8200
+    if separate:
+        monkeypatch.setenv("KVC_GATHER_SEPARATE", "1")
+    K = torch.randint(-32768, 32767, (G, stride, 128), dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    V = torch.randint(-32768, 32767, (G, stride, 128), dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    s = synth.random_scores(G, stride, seed=11, kind="ties", device="cpu")
+    Kb, Vb = synth.bf16_bits(K), synth.bf16_bits(V)
+    for k in (1, 777, 8192, 8193, S):
+        idx, Ko, Vo = gpu_lib.kvc_topk_compact(s.to(DEV), k, K, V, S=S)
+        torch.cuda.synchronize()
+        ref_idx = oracle.topk(s.numpy(), k, S=S)
+        np.testing.assert_array_equal(idx.cpu().numpy(), ref_idx)
+        np.testing.assert_array_equal(synth.bf16_bits(Ko), oracle.gather(Kb, ref_idx, S=S))
+        np.testing.assert_array_equal(synth.bf16_bits(Vo), oracle.gather(Vb, ref_idx, S=S))
+
+
 def _evict_and_check(gpu_lib, K, V, keep, W=None, slices=None):
     s = gpu_lib.kvc_score_l2(K) if W is None else gpu_lib.kvc_score_l2_windowed(K, W)
     idx, Ko, Vo = gpu_lib.kvc_topk_compact(s, keep, K, V)

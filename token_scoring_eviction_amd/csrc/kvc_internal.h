@@ -43,6 +43,20 @@ inline kvc_status launch_status() {
     return hipGetLastError() == hipSuccess ? KVC_OK : KVC_ERR_HIP;
 }
 
+// Compute units of the current device (cached per device; 0 if it cannot be queried).
+inline int device_cu_count() {
+    static int cus_by_dev[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+    if (cus_by_dev[dev] == 0) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            return 0;
+        cus_by_dev[dev] = cus;
+    }
+    return cus_by_dev[dev];
+}
+
 // ------------------------------------------------------------ device helpers
 
 // Exact bf16 -> fp32 widening of the two halves of a packed 32-bit word.

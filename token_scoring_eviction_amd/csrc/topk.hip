@@ -258,9 +258,10 @@ extern "C" kvc_status kvc_topk_compact(const float *scores, int64_t G, int64_t S
         return KVC_ERR_INVALID_ARGUMENT;
     if ((K && (!aligned(K, 16) || !aligned(K_out, 16))) || (V && (!aligned(V, 16) || !aligned(V_out, 16))))
         return KVC_ERR_INVALID_ARGUMENT;
-    // the selecting workgroup also copies its slice's rows when the copy is
-    // small (k <= 8192 rows per slice); larger copies go to a wide gather launch
-    if ((K || V) && k <= 8192 && fused_gather()) {
+    // the selecting workgroup also copies its slice's rows when the copy is small
+    // (k <= 8192 rows per slice) and there are enough slices to occupy every compute
+    // unit; otherwise the copy goes to a wide gather launch
+    if ((K || V) && k <= 8192 && G >= device_cu_count() && fused_gather()) {
         hipLaunchKernelGGL(select_compact, dim3(static_cast<unsigned>(G)), dim3(kSelThreads), 0, stream,
                            scores, S, s_stride, k, idx_out, K, V, K_out, V_out);
         return launch_status();
