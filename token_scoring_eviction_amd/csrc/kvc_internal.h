@@ -43,6 +43,19 @@ inline kvc_status launch_status() {
     return hipGetLastError() == hipSuccess ? KVC_OK : KVC_ERR_HIP;
 }
 
+// Lets `kernel` take up to 160 KB of dynamic LDS on the current device (the
+// default cap is 64 KB); done once per device, `done` is the caller's per-kernel flag array.
+inline kvc_status allow_large_lds(const void *kernel, bool (&done)[64]) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return KVC_ERR_HIP;
+    if (!done[dev]) {
+        if (hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) != hipSuccess)
+            return KVC_ERR_HIP;
+        done[dev] = true;
+    }
+    return KVC_OK;
+}
+
 // Compute units of the current device (cached per device; 0 if it cannot be queried).
 inline int device_cu_count() {
     static int cus_by_dev[64];

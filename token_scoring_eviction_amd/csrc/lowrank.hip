@@ -93,68 +93,123 @@ inline int query_terms(int64_t nq) { return nq < 32 ? 3 : 2; }
 // in fp64, split into three bf16 terms, as A-operand fragments
 // [qb][s][term][lane].  Three terms keep the score's error at the level of
 // the fp32 accumulation even when |q . r_t| cancels far below ||q|| ||r_t||.
+constexpr int kPrepJ = 64;                  // basis columns per chunk of the prep
+constexpr int kPrepQStride = kHeadDim + 2;  // bf16 row stride of the staged window
+constexpr int kPrepStride = kPrepJ + 1;     // row stride of T and of the U chunk (in elements)
+constexpr size_t kPrepLds = static_cast<size_t>(kHeadDim) * kPrepStride * sizeof(double) +
+                            static_cast<size_t>(kHeadDim) * kPrepStride * sizeof(float) +
+                            static_cast<size_t>(kHeadDim) * kPrepQStride * sizeof(uint16_t);
+
+// One workgroup per slice, U taken in chunks of 64 columns:
+//   phase 1  T[q][j] = sum_c Q[q][c] U[c][j]        (thread tile 4 queries x 8 columns)
+//   phase 2  P[q][c] += sum_j T[q][j] U[c][j]       (thread tile 4 queries x 16 channels,
+//                                                    accumulated in registers over chunks)
+// then Q''[q][c] = scale * (Q[q][c] - P[q][c]).  Everything is fp64 (bf16 x fp32
+// products are exact in fp64).  LDS strides are padded so that the rows a wave
+// reads at one column fall in distinct banks.
 __global__ __launch_bounds__(256) void prep_query_kernel(const uint16_t *__restrict__ Q,
                                                          const float *__restrict__ Uk, int64_t B,
                                                          int64_t Hkv, int64_t Hq, int64_t Wq,
                                                          int R, int nq, int nqb, int nterm,
                                                          double scale, u32x4 *__restrict__ qfrag) {
-    // LDS: Q window rows (bf16 bits, [128][128]), T = Q U ([128][R] fp64: when U is
-    // close to a full orthonormal basis the residual is a tiny difference that
-    // an fp32 T would lose), U ([128][R] fp32, staged only when R <= 64, else
-    // read from global memory).  At most 160 KB.
-    extern __shared__ uint32_t lds_q[];
-    const bool u_lds = R <= 64;
-    uint16_t *Qs = reinterpret_cast<uint16_t *>(lds_q);
-    double *Ts = reinterpret_cast<double *>(lds_q + 128 * kHeadDim / 2);
-    float *Ul = reinterpret_cast<float *>(Ts + kHeadDim * R);
+    extern __shared__ double lds_prep[];
+    double *Ts = lds_prep;                                                     // [128][65]
+    float *Uc = reinterpret_cast<float *>(Ts + kHeadDim * kPrepStride);        // [128][65]
+    uint16_t *Qs = reinterpret_cast<uint16_t *>(Uc + kHeadDim * kPrepStride);  // [128][130]
+    const int tid = threadIdx.x;
     const int64_t slice = blockIdx.x;
     const int64_t h = slice % Hkv;
     const int64_t lb = slice / Hkv;  // l*B + b
     const int64_t l = lb / B;
     const int64_t grp = Hq / Hkv;
     const float *U = Uk + (l * Hkv + h) * kHeadDim * R;
-    const float *Us = u_lds ? Ul : U;
     // window rows q = (group head) * Wq + (query); the group's heads are contiguous in Q
     const uint16_t *Qg = Q + ((lb * Hq + h * grp) * Wq) * kHeadDim;
-    for (int i = threadIdx.x; i < nq * kHeadDim / 8; i += blockDim.x)
-        reinterpret_cast<uint4 *>(Qs)[i] = reinterpret_cast<const uint4 *>(Qg)[i];
-    if (u_lds)
-        for (int i = threadIdx.x; i < kHeadDim * R / 4; i += blockDim.x)
-            reinterpret_cast<float4 *>(Ul)[i] = reinterpret_cast<const float4 *>(U)[i];
-    __syncthreads();
-    for (int o = threadIdx.x; o < nq * R; o += blockDim.x) {
-        const int q = o / R, j = o % R;
-        double acc = 0.0;
-#pragma unroll 8
-        for (int c = 0; c < kHeadDim; ++c)
-            acc += static_cast<double>(__uint_as_float(static_cast<uint32_t>(Qs[q * kHeadDim + c]) << 16)) *
-                   static_cast<double>(Us[c * R + j]);
-        Ts[q * R + j] = acc;
+    for (int i = tid; i < kHeadDim * (kHeadDim / 2); i += blockDim.x) {
+        const int q = i / (kHeadDim / 2), c2 = i % (kHeadDim / 2);  // rows past nq are zero
+        reinterpret_cast<uint32_t *>(Qs + q * kPrepQStride)[c2] =
+            q < nq ? reinterpret_cast<const uint32_t *>(Qg + q * kHeadDim)[c2] : 0u;
     }
-    __syncthreads();
-    u32x4 *out = qfrag + slice * static_cast<int64_t>(nqb) * 8 * nterm * 64;
-    for (int p = threadIdx.x; p < nqb * 8 * 64; p += blockDim.x) {
-        const int lane = p & 63, fs = p >> 6, s = fs & 7, qb = fs >> 3;
-        const int q = qb * 32 + (lane & 31);
-        const int c0 = 16 * s + (lane >> 5) * 8;
-        double x[8] = {0., 0., 0., 0., 0., 0., 0., 0.};
-        if (q < nq) {
-            double proj[8] = {0., 0., 0., 0., 0., 0., 0., 0.};
-            for (int j = 0; j < R; ++j) {
-                const double t = Ts[q * R + j];
+    auto qval = [&](int q, int c) {
+        return static_cast<double>(__uint_as_float(static_cast<uint32_t>(Qs[q * kPrepQStride + c]) << 16));
+    };
+    // phase-1 tile: columns j = jg + 8 jj, queries 4 qg .. 4 qg + 3
+    const int jg = tid & 7, qg1 = tid >> 3;
+    // phase-2 tile: channels 16 cg .. 16 cg + 15, queries 4 qg .. 4 qg + 3
+    const int cg = tid & 7, qg2 = tid >> 3;
+    double P[4][16];
 #pragma unroll
-                for (int e = 0; e < 8; ++e) proj[e] += t * static_cast<double>(Us[(c0 + e) * R + j]);
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) P[a][e] = 0.0;
+
+    for (int j0 = 0; j0 < R; j0 += kPrepJ) {
+        const int jn = min(kPrepJ, R - j0);  // 32 or 64
+        __syncthreads();                     // previous chunk's readers are done
+        for (int i = tid; i < kHeadDim * jn; i += blockDim.x) {
+            const int c = i / jn, jj = i % jn;
+            Uc[c * kPrepStride + jj] = U[c * R + j0 + jj];
+        }
+        __syncthreads();
+        if (4 * qg1 < nq) {
+            // columns jg + 8 jj for jj < jn / 8
+            double t[4][8];
+#pragma unroll
+            for (int a = 0; a < 4; ++a)
+#pragma unroll
+                for (int jj = 0; jj < 8; ++jj) t[a][jj] = 0.0;
+            const int nj = jn / 8;
+            for (int c = 0; c < kHeadDim; ++c) {
+                double qv[4], uv[8];
+#pragma unroll
+                for (int a = 0; a < 4; ++a) qv[a] = qval(4 * qg1 + a, c);
+#pragma unroll
+                for (int jj = 0; jj < 8; ++jj)
+                    uv[jj] = jj < nj ? static_cast<double>(Uc[c * kPrepStride + jg + 8 * jj]) : 0.0;
+#pragma unroll
+                for (int a = 0; a < 4; ++a)
+#pragma unroll
+                    for (int jj = 0; jj < 8; ++jj) t[a][jj] = fma(qv[a], uv[jj], t[a][jj]);
             }
 #pragma unroll
-            for (int e = 0; e < 8; ++e) {
-                const double qc = static_cast<double>(
-                    __uint_as_float(static_cast<uint32_t>(Qs[q * kHeadDim + c0 + e]) << 16));
-                x[e] = scale * (qc - proj[e]);
+            for (int a = 0; a < 4; ++a)
+#pragma unroll
+                for (int jj = 0; jj < 8; ++jj)
+                    if (jj < nj) Ts[(4 * qg1 + a) * kPrepStride + jg + 8 * jj] = t[a][jj];
+        }
+        __syncthreads();
+        if (4 * qg2 < nq) {
+            for (int j = 0; j < jn; ++j) {
+                double tv[4], uv[16];
+#pragma unroll
+                for (int a = 0; a < 4; ++a) tv[a] = Ts[(4 * qg2 + a) * kPrepStride + j];
+#pragma unroll
+                for (int e = 0; e < 16; ++e) uv[e] = static_cast<double>(Uc[(16 * cg + e) * kPrepStride + j]);
+#pragma unroll
+                for (int a = 0; a < 4; ++a)
+#pragma unroll
+                    for (int e = 0; e < 16; ++e) P[a][e] = fma(tv[a], uv[e], P[a][e]);
             }
         }
-        u32x4 part[kQParts];
-        split8x3_f64(x, part);
-        for (int t = 0; t < nterm; ++t) out[((qb * 8 + s) * nterm + t) * 64 + lane] = part[t];
+    }
+    // Q'' in fragment order: lane (q % 32) + 32 * ((c0 / 8) % 2) of fragment (q / 32, c0 / 16)
+    // holds channels c0 .. c0 + 7 of query q; queries nq .. 32 nqb - 1 are zero
+    u32x4 *out = qfrag + slice * static_cast<int64_t>(nqb) * 8 * nterm * 64;
+#pragma unroll
+    for (int a = 0; a < 4; ++a) {
+        const int q = 4 * qg2 + a;
+        if (q >= 32 * nqb) continue;
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+            const int c0 = 16 * cg + 8 * half;
+            double x[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e) x[e] = q < nq ? scale * (qval(q, c0 + e) - P[a][8 * half + e]) : 0.0;
+            u32x4 part[kQParts];
+            split8x3_f64(x, part);
+            const int lane = (q & 31) + 32 * half, s = cg;
+            for (int t = 0; t < nterm; ++t) out[(((q >> 5) * 8 + s) * nterm + t) * 64 + lane] = part[t];
+        }
     }
 }
 
@@ -485,13 +540,9 @@ kvc_status launch_project_variant(const uint16_t *X, const float *U, const u32x4
                                   hipStream_t stream) {
     constexpr int HB = KVC_PROJECT_HB;
     const size_t lds = static_cast<size_t>(NRB * 16 + nqb * 8 * nterm) * kFragBytes;
-    static bool attr_set = false;
-    if (!attr_set) {
-        if (hipFuncSetAttribute(reinterpret_cast<const void *>(&project_kernel<NRB, HB, kRowStores>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) != hipSuccess)
-            return KVC_ERR_HIP;
-        attr_set = true;
-    }
+    static bool lds_ok[64];
+    if (allow_large_lds(reinterpret_cast<const void *>(&project_kernel<NRB, HB, kRowStores>), lds_ok) != KVC_OK)
+        return KVC_ERR_HIP;
     const int64_t blocks = G * sl.nsplit;
     if (blocks > INT32_MAX) return KVC_ERR_UNSUPPORTED;
     hipLaunchKernelGGL((project_kernel<NRB, HB, kRowStores>), dim3(static_cast<unsigned>(blocks)),
@@ -577,18 +628,11 @@ extern "C" kvc_status kvc_lowrank_compress(const kvc_dims *d, const uint16_t *K,
         nterm = query_terms(nq);
         qfrag = cur.take<u32x4>(static_cast<size_t>(G * nqb * 8 * nterm * 64));
         const double scale = 1.0 / (static_cast<double>(nq) * sqrt(static_cast<double>(d->D)));
-        static bool attr_set = false;
-        if (!attr_set) {
-            if (hipFuncSetAttribute(reinterpret_cast<const void *>(&prep_query_kernel),
-                                    hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) !=
-                hipSuccess)
-                return KVC_ERR_HIP;
-            attr_set = true;
-        }
+        static bool lds_ok[64];
+        if (allow_large_lds(reinterpret_cast<const void *>(&prep_query_kernel), lds_ok) != KVC_OK)
+            return KVC_ERR_HIP;
         if (G > INT32_MAX) return KVC_ERR_UNSUPPORTED;
-        const size_t prep_lds = static_cast<size_t>(128) * kHeadDim * 2 +
-                                static_cast<size_t>(kHeadDim * d->R) * sizeof(double) +
-                                (d->R <= 64 ? static_cast<size_t>(kHeadDim * d->R) * sizeof(float) : 0);
+        const size_t prep_lds = kPrepLds;
         hipLaunchKernelGGL(prep_query_kernel, dim3(static_cast<unsigned>(G)), dim3(256), prep_lds, stream,
                            Q_win, U_k,
                            d->B, d->H_kv, d->H_q, d->W_q, static_cast<int>(d->R),

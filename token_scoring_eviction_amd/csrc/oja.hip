@@ -371,26 +371,18 @@ extern "C" kvc_status kvc_oja_update(const kvc_dims *d, float *U, const uint16_t
     hipLaunchKernelGGL(cov_partial_kernel, dim3(static_cast<unsigned>(o.LH * o.nchunk)), dim3(256), 0,
                        stream, Xp, d->B, d->H_kv, o.np, o.rows_per_chunk, o.nchunk, Cpart);
     if (d->R <= 64) {
-        static bool attr_fast = false;
-        if (!attr_fast) {
-            if (hipFuncSetAttribute(reinterpret_cast<const void *>(&oja_step_qr_lds_kernel),
-                                    hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) != hipSuccess)
-                return KVC_ERR_HIP;
-            attr_fast = true;
-        }
+        static bool lds_ok[64];
+        if (allow_large_lds(reinterpret_cast<const void *>(&oja_step_qr_lds_kernel), lds_ok) != KVC_OK)
+            return KVC_ERR_HIP;
         hipLaunchKernelGGL(oja_step_qr_lds_kernel, dim3(static_cast<unsigned>(o.LH)), dim3(256),
                            oja_lds_bytes(static_cast<int>(d->R)), stream, U, Cpart, o.nchunk, o.n,
                            static_cast<int>(d->R), static_cast<double>(eta));
         return launch_status();
     }
     const size_t lds = (static_cast<size_t>(kHeadDim) * (d->R + 1) + 2 * kHeadDim + 2) * sizeof(double);
-    static bool attr_set = false;
-    if (!attr_set) {
-        if (hipFuncSetAttribute(reinterpret_cast<const void *>(&oja_step_qr_kernel),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) != hipSuccess)
-            return KVC_ERR_HIP;
-        attr_set = true;
-    }
+    static bool lds_ok[64];
+    if (allow_large_lds(reinterpret_cast<const void *>(&oja_step_qr_kernel), lds_ok) != KVC_OK)
+        return KVC_ERR_HIP;
     hipLaunchKernelGGL(oja_step_qr_kernel, dim3(static_cast<unsigned>(o.LH)), dim3(256), lds, stream, U,
                        Cpart, o.nchunk, o.n, static_cast<int>(d->R), static_cast<double>(eta), C64,
                        CU64, M64);

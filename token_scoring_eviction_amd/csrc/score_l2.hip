@@ -342,24 +342,8 @@ __global__ __launch_bounds__(kFuseThreads, KVC_FUSE_MINBLOCKS) void l2_fused(con
         }
     };
 
-    uint4 v[kFuseRows], vn[kFuseRows];
-    int64_t tile = blockIdx.x;
-    if (tile < geo.tiles) {
-        const TileGeo t = geo_of(tile);
-        load_tile(t, v);
-        publish(tile, t, v);
-    }
-    // Two tiles per workgroup: while tile `tile` waits for its team's centroid
-    // and is scored, the next tile's loads are already in flight; its partial
-    // is published right after.
-    for (; tile < geo.tiles; tile += gridDim.x) {
-        const TileGeo t = geo_of(tile);
-        const int64_t next = tile + gridDim.x;
-        TileGeo tn;
-        if (next < geo.tiles) {
-            tn = geo_of(next);
-            load_tile(tn, vn);
-        }
+    // Scores tile `t` (held in v) once its team's centroid is published.
+    auto score_tile = [&](const TileGeo &t, const uint4 *v) {
         fetch_mu(t);
         float m[8];
 #pragma unroll
@@ -385,6 +369,28 @@ __global__ __launch_bounds__(kFuseThreads, KVC_FUSE_MINBLOCKS) void l2_fused(con
                 scores[t.g * geo.S + row] = sqrtf(d2[0]);
         }
         __syncthreads();  // mu_s is rewritten by the next fetch
+    };
+
+    const int64_t step = gridDim.x;
+    int64_t tile = blockIdx.x;
+    // Two tiles per workgroup: while tile `tile` waits for its team's centroid
+    // and is scored, the next tile's loads are already in flight; its partial
+    // is published right after.
+    uint4 v[kFuseRows], vn[kFuseRows];
+    if (tile < geo.tiles) {
+        const TileGeo t = geo_of(tile);
+        load_tile(t, v);
+        publish(tile, t, v);
+    }
+    for (; tile < geo.tiles; tile += step) {
+        const TileGeo t = geo_of(tile);
+        const int64_t next = tile + step;
+        TileGeo tn;
+        if (next < geo.tiles) {
+            tn = geo_of(next);
+            load_tile(tn, vn);
+        }
+        score_tile(t, v);
         if (next < geo.tiles) publish(next, tn, vn);
 #pragma unroll
         for (int r = 0; r < kFuseRows; ++r) v[r] = vn[r];
