@@ -3,6 +3,8 @@ compaction against the CPU oracle, through the C ABI.  Rules: fp32 scores
 within rel 1e-4 (+1e-6 rms); top-k on identical fp32 scores bit-exact;
 end-to-end retained sets identical except for tokens within rel 1e-4 of the
 k-th score; gathered rows bit-exact."""
+from concurrent.futures import ThreadPoolExecutor
+
 import numpy as np
 import pytest
 import torch
@@ -94,29 +96,36 @@ def test_gather_paths_bit_exact(gpu_lib, monkeypatch, separate):
         np.testing.assert_array_equal(synth.bf16_bits(Vo), oracle.gather(Vb, ref_idx, S=S))
 
 
-def _evict_and_check(gpu_lib, K, V, keep, W=None, slices=None):
+def _evict_and_check(gpu_lib, K, V, keep, W=None, slices=None, threads=8):
     s = gpu_lib.kvc_score_l2(K) if W is None else gpu_lib.kvc_score_l2_windowed(K, W)
     idx, Ko, Vo = gpu_lib.kvc_topk_compact(s, keep, K, V)
     torch.cuda.synchronize()
-    slices = range(K.shape[0]) if slices is None else slices
-    nb_total = 0
-    for g in slices:
-        kb = synth.bf16_bits(K[g:g + 1])
-        vb = synth.bf16_bits(V[g:g + 1])
+    slices = list(range(K.shape[0]) if slices is None else slices)
+    kb_all, vb_all = synth.bf16_bits(K), synth.bf16_bits(V)
+    s_all, idx_all = s.cpu().numpy(), idx.cpu().numpy()
+    ko_all, vo_all = synth.bf16_bits(Ko), synth.bf16_bits(Vo)
+
+    def check(g):
+        kb = kb_all[g:g + 1]
         ora, _ = oracle.score_l2(kb) if W is None else oracle.score_l2_windowed(kb, W)
-        ok, rel, nbad = score_close(s[g:g + 1].cpu().numpy(), ora)
+        ok, rel, nbad = score_close(s_all[g:g + 1], ora)
         assert ok, "slice %d: %d scores off (max rel %.3g)" % (g, nbad, rel)
         ora32 = ora.astype(np.float32)
         ora_idx = oracle.topk(ora32, keep)
-        gi = idx[g:g + 1].cpu().numpy()
+        gi = idx_all[g:g + 1]
         ok, nb = index_sets_agree(gi, ora_idx, ora32, keep)
         assert ok, "slice %d: retained set differs beyond the threshold band" % g
-        nb_total += nb
         # gathered rows are the input rows at the GPU's indices, bit for bit
         # (a plain index_select on the host; the oracle never takes GPU output)
         sel = gi[0].astype(np.int64)
-        np.testing.assert_array_equal(synth.bf16_bits(Ko[g]), kb[0][sel])
-        np.testing.assert_array_equal(synth.bf16_bits(Vo[g]), vb[0][sel])
+        np.testing.assert_array_equal(ko_all[g], kb[0][sel])
+        np.testing.assert_array_equal(vo_all[g], vb_all[g][sel])
+        return nb
+
+    # the oracle is single-threaded C called through ctypes (the GIL is released),
+    # so independent slices are checked concurrently
+    with ThreadPoolExecutor(max_workers=threads) as ex:
+        nb_total = sum(ex.map(check, slices))
     return idx, nb_total
 
 
@@ -128,16 +137,19 @@ def test_config0_global_full(gpu_lib):
         assert set(plant[g].tolist()) <= set(idx[g].cpu().tolist())
 
 
-def test_config1_global_sampled(gpu_lib):
-    # 32 layers x 8 kv heads, S=16384, keep 8192; launch at full size, check sampled slices
+def test_config1_global_full(gpu_lib):
+    # 32 layers x 8 kv heads, S=16384, keep 8192, in the launch configuration the
+    # benchmark times; every one of the 256 slices checked against the oracle
     K, V, plant = synth.manifold_global(32, 1, 8, 16384, planted=64, device=DEV)
-    _evict_and_check(gpu_lib, K, V, 8192, slices=[0, 101, 255])
+    idx, _ = _evict_and_check(gpu_lib, K, V, 8192)
+    for g in (0, 101, 255):  # the planted x4 tokens survive
+        assert set(plant[g].tolist()) <= set(idx[g].cpu().tolist())
 
 
-def test_config2_windowed_sampled(gpu_lib):
-    # 32 layers x 8 kv heads, S=65536, W=4096, keep 49152; sampled slices
+def test_config2_windowed_full(gpu_lib):
+    # 32 layers x 8 kv heads, S=65536, W=4096, keep 49152; every slice checked
     K, V = synth.manifold_drifting(32, 1, 8, 65536, device=DEV)
-    _evict_and_check(gpu_lib, K, V, 49152, W=4096, slices=[0, 200])
+    _evict_and_check(gpu_lib, K, V, 49152, W=4096)
 
 
 def test_determinism(gpu_lib):

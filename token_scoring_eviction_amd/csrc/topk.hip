@@ -76,34 +76,58 @@ __global__ __launch_bounds__(kSelThreads) void select_compact(const float *__res
     __shared__ uint32_t wtot[2 * kSelWaves];
 
     const int wave = threadIdx.x >> 6;
+    const int lane = threadIdx.x & 63;
     uint32_t prefix = 0, mask = 0;
     uint32_t remaining = static_cast<uint32_t>(k);
+    // 16-byte loads when the slice's scores are 16-byte aligned (uniform per block)
+    const bool vec = (reinterpret_cast<uintptr_t>(s) & 15u) == 0;
+    const int64_t S4 = vec ? S / 4 * 4 : 0;
 
     for (int pass = 0; pass < 4; ++pass) {
         const int shift = 24 - 8 * pass;
         for (int i = threadIdx.x; i < kSelWaves * 256; i += kSelThreads) (&hist[0][0])[i] = 0u;
         __syncthreads();
-        for (int64_t i = threadIdx.x; i < S; i += kSelThreads) {
-            const uint32_t key = order_key(s[i]);
+        auto count = [&](uint32_t key) {
             if ((key & mask) == prefix) atomicAdd(&hist[wave][(key >> shift) & 255u], 1u);
+        };
+        // four 16-byte loads per thread in flight per step
+        constexpr int64_t kStep = static_cast<int64_t>(kSelThreads) * 4;
+        for (int64_t i = static_cast<int64_t>(threadIdx.x) * 4; i < S4; i += 4 * kStep) {
+            float4 x[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                if (i + u * kStep < S4) x[u] = *reinterpret_cast<const float4 *>(s + i + u * kStep);
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                if (i + u * kStep < S4) {
+                    count(order_key(x[u].x));
+                    count(order_key(x[u].y));
+                    count(order_key(x[u].z));
+                    count(order_key(x[u].w));
+                }
+        }
+        for (int64_t i = S4 + threadIdx.x; i < S; i += kSelThreads) count(order_key(s[i]));
+        __syncthreads();
+        // suffix sums over bins, suffix[b] = count of matching keys with digit >= b:
+        // a 64-lane suffix scan per wave over its 64 bins, then the waves above added
+        uint32_t c = 0;
+        if (threadIdx.x < 256) {
+#pragma unroll
+            for (int w = 0; w < kSelWaves; ++w) c += hist[w][threadIdx.x];
+#pragma unroll
+            for (int d = 1; d < 64; d <<= 1) {
+                const uint32_t y = __shfl_down(c, d, 64);
+                if (lane + d < 64) c += y;
+            }
+            if (lane == 0) wtot[wave] = c;  // total of the wave's 64 bins
         }
         __syncthreads();
         if (threadIdx.x < 256) {
-            uint32_t c = 0;
-#pragma unroll
-            for (int w = 0; w < kSelWaves; ++w) c += hist[w][threadIdx.x];
+            for (int w = wave + 1; w < 4; ++w) c += wtot[w];
             suffix[threadIdx.x] = c;
         }
         if (threadIdx.x == 0) suffix[256] = 0u;
         __syncthreads();
-        // suffix sums over bins: suffix[b] = count of matching keys with digit >= b
-        for (int d = 1; d < 256; d <<= 1) {
-            uint32_t add = 0;
-            if (threadIdx.x < 256 && threadIdx.x + d < 256) add = suffix[threadIdx.x + d];
-            __syncthreads();
-            if (threadIdx.x < 256) suffix[threadIdx.x] += add;
-            __syncthreads();
-        }
         if (threadIdx.x < 256) {
             const uint32_t here = suffix[threadIdx.x], above = suffix[threadIdx.x + 1];
             if (here >= remaining && above < remaining) {
@@ -127,10 +151,19 @@ __global__ __launch_bounds__(kSelThreads) void select_compact(const float *__res
         const int64_t i0 = base + static_cast<int64_t>(threadIdx.x) * kPerThread;
         uint32_t keys[kPerThread];
         uint32_t n_gt = 0, n_eq = 0;
+        if (vec && i0 + kPerThread <= S) {
+            const float4 x = *reinterpret_cast<const float4 *>(s + i0);
+            keys[0] = order_key(x.x);
+            keys[1] = order_key(x.y);
+            keys[2] = order_key(x.z);
+            keys[3] = order_key(x.w);
+        } else {
+#pragma unroll
+            for (int j = 0; j < kPerThread; ++j) keys[j] = i0 + j < S ? order_key(s[i0 + j]) : 0u;
+        }
 #pragma unroll
         for (int j = 0; j < kPerThread; ++j) {
             const int64_t i = i0 + j;
-            keys[j] = i < S ? order_key(s[i]) : 0u;
             n_gt += (i < S && keys[j] > T);
             n_eq += (i < S && keys[j] == T);
         }
