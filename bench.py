@@ -58,6 +58,9 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--config", type=int, default=1, choices=[0, 1, 2, 3, 4])
+    ap.add_argument("--metric", choices=["l2", "cosine"], default="l2",
+                    help="centroid score of configs 0-2: ManifoldKV's L2 distance (the workload) "
+                         "or the cosine-dissimilarity baseline")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-ref", type=int, default=0, metavar="MIB",
@@ -93,7 +96,7 @@ class Op:
         self.ms = []
 
 
-def manifold_workload(cfg, dev):
+def manifold_workload(cfg, dev, metric="l2"):
     import synth
     from token_scoring_eviction_amd import kvc, pipeline
     if cfg == 0:
@@ -112,11 +115,16 @@ def manifold_workload(cfg, dev):
                 "S=65536, W=4096, keep 49152 (25% evicted)")
     G = L * H
     buf = pipeline.alloc_eviction(G, S, keep, device=dev)
-    score = (lambda: kvc.kvc_score_l2(K, scores=buf.scores)) if W is None else \
-        (lambda: kvc.kvc_score_l2_windowed(K, W, scores=buf.scores))
+    if metric == "cosine":
+        score = lambda: kvc.kvc_score_centroid(K, W=W, metric="cosine", scores=buf.scores)
+        score_name = "kvc_score_centroid"
+        desc = desc.replace("ManifoldKV", "cosine-to-centroid").replace("global-L2", "global")
+    elif W is None:
+        score, score_name = (lambda: kvc.kvc_score_l2(K, scores=buf.scores)), "kvc_score_l2"
+    else:
+        score, score_name = (lambda: kvc.kvc_score_l2_windowed(K, W, scores=buf.scores)), "kvc_score_l2_windowed"
     ops = [
-        Op("kvc_score_l2" if W is None else "kvc_score_l2_windowed", score, G * S * (256 + 4),
-           kernel="l2_fused"),
+        Op(score_name, score, G * S * (256 + 4), kernel="l2_fused"),
         Op("kvc_topk_compact",
            lambda: kvc.kvc_topk_compact(buf.scores, keep, K, V, idx_out=buf.idx, K_out=buf.K_out,
                                         V_out=buf.V_out),
@@ -125,7 +133,7 @@ def manifold_workload(cfg, dev):
     ]
     algo = G * S * 256 + G * keep * 256 + 2 * G * keep * 256 + G * S * 4 + G * keep * 4
     config = {"workload": desc, "slices": G, "seq_len": S, "keep": keep, "head_dim": 128,
-              "window": W}
+              "window": W, "metric": metric}
 
     def cpu(budget):
         import numpy as np
@@ -136,7 +144,10 @@ def manifold_workload(cfg, dev):
             kb = synth.bf16_bits(K[g:g + 1])
             vb = synth.bf16_bits(V[g:g + 1])
             t0 = time.perf_counter()
-            sc, _ = oracle.score_l2(kb) if W is None else oracle.score_l2_windowed(kb, W)
+            if metric == "cosine":
+                sc, _ = oracle.score_cosine_windowed(kb, W or S)
+            else:
+                sc, _ = oracle.score_l2(kb) if W is None else oracle.score_l2_windowed(kb, W)
             idx = oracle.topk(sc.astype(np.float32), keep)
             oracle.gather(kb, idx)
             oracle.gather(vb, idx)
@@ -285,7 +296,7 @@ def main():
     if args.config == 3:
         ops, head_tokens, algo, config, cpu = oja_workload(dev)
     else:
-        ops, head_tokens, algo, config, cpu = manifold_workload(args.config, dev)
+        ops, head_tokens, algo, config, cpu = manifold_workload(args.config, dev, args.metric)
     torch.cuda.synchronize()
 
     for _ in range(args.warmup):

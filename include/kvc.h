@@ -45,7 +45,7 @@
 extern "C" {
 #endif
 
-#define KVC_ABI_VERSION 1
+#define KVC_ABI_VERSION 2
 
 typedef enum kvc_status {
     KVC_OK = 0,
@@ -61,8 +61,18 @@ typedef enum kvc_op {
     KVC_OP_TOPK_COMPACT = 2,
     KVC_OP_LOWRANK_COMPRESS = 3,
     KVC_OP_OJA_UPDATE = 4,
-    KVC_OP_RECONSTRUCT = 5
+    KVC_OP_RECONSTRUCT = 5,
+    KVC_OP_SCORE_CENTROID = 6
 } kvc_op;
+
+/* Score of a key against its (global or window) centroid mu, for
+ * kvc_score_centroid. */
+typedef enum kvc_metric {
+    KVC_METRIC_L2 = 0,     /* || k_t - mu ||_2: ManifoldKV ([MKV] abstract) */
+    KVC_METRIC_COSINE = 1  /* 1 - cos(k_t, mu): the cosine-to-centroid baseline the [MKV]
+                              abstract compares against (scale-invariant); taken as 1 where
+                              k_t or mu is the zero vector */
+} kvc_metric;
 
 /* Shapes of a multi-layer KV cache.
  *   L layers, B sequences, H_kv key/value heads, H_q query heads (a multiple of
@@ -80,8 +90,8 @@ int kvc_abi_version(void);
 const char *kvc_status_str(kvc_status s);
 
 /* Workspace bytes needed by one call of `op`.
- *   SCORE_L2, SCORE_L2_WINDOWED: G = L*B*H_kv slices of S tokens; W = window
- *     (ignored for SCORE_L2).
+ *   SCORE_L2, SCORE_L2_WINDOWED, SCORE_CENTROID: G = L*B*H_kv slices of S
+ *     tokens; W = window (ignored for SCORE_L2).
  *   TOPK_COMPACT: G = L*B*H_kv slices of S tokens; k = tokens kept.
  *   LOWRANK_COMPRESS, OJA_UPDATE, RECONSTRUCT: shapes from `d`; for OJA_UPDATE
  *     d->S is the token count N and W is the pooling window.
@@ -105,6 +115,18 @@ kvc_status kvc_score_l2(const uint16_t *K, int64_t G, int64_t S, int32_t D, floa
 kvc_status kvc_score_l2_windowed(const uint16_t *K, int64_t G, int64_t S, int32_t D, int64_t W,
                                  float *scores, float *centroids, void *ws, size_t ws_bytes,
                                  hipStream_t stream);
+
+/* Centroid score with a choice of metric: as kvc_score_l2_windowed (windows
+ * of W tokens; W >= S is the global centroid), with scores[g][t] =
+ * metric(K[g][t][:], mu) for `metric` a kvc_metric.  KVC_METRIC_L2 gives the
+ * same bits as kvc_score_l2(_windowed).  For KVC_METRIC_COSINE the score is
+ * evaluated as ||k/||k|| - mu/||mu||||^2 / 2 (equal to 1 - cos), which keeps
+ * its relative accuracy for keys nearly parallel to mu; it lies in [0, 2].
+ * centroids: fp32 [G][ceil(S/W)][D] or NULL (always the mean, not its
+ * direction).  Unknown metric: KVC_ERR_INVALID_ARGUMENT. */
+kvc_status kvc_score_centroid(const uint16_t *K, int64_t G, int64_t S, int32_t D, int64_t W,
+                              int32_t metric, float *scores, float *centroids, void *ws,
+                              size_t ws_bytes, hipStream_t stream);
 
 /* Retention and compaction ([MKV] abstract: the keys farthest from the
  * centroid are retained; [OJA] method details: the top-k error scores are kept

@@ -63,6 +63,7 @@ def _load():
             sig = {
                 "ora_score_l2": [P, I, I, I, P, P],
                 "ora_score_l2_windowed": [P, I, I, I, I, P, P],
+                "ora_score_cosine_windowed": [P, I, I, I, I, P, P],
                 "ora_topk": [P, I, I, I, I, P],
                 "ora_gather": [P, I, I, I, I, P, I, P],
                 "ora_lowrank_compress": [I, I, I, I, I, I, I, I, I, P, P, P, P, P, P, P, P],
@@ -130,6 +131,29 @@ def score_l2_windowed(K, W):
     _check(_load().ora_score_l2_windowed(_p(K), G, S, D, W, _p(scores), _p(mu)),
            "score_l2_windowed")
     return scores, mu
+
+
+def score_cosine_windowed(K, W):
+    """Cosine dissimilarity 1 - cos(k_t, mu) to the centroid of each contiguous
+    window of W keys (W >= S: the global centroid).  Returns (scores float64
+    [G, S], centroids float64 [G, ceil(S/W), D])."""
+    K = _u16(K)
+    G, S, D = K.shape
+    nwin = -(-S // W) if W > 0 else 0
+    scores = np.zeros((G, S), np.float64)
+    mu = np.zeros((G, nwin, D), np.float64)
+    _check(_load().ora_score_cosine_windowed(_p(K), G, S, D, W, _p(scores), _p(mu)),
+           "score_cosine_windowed")
+    return scores, mu
+
+
+def score_cosine(K):
+    """Cosine dissimilarity to the global key centroid.  Returns (scores float64
+    [G, S], centroid float64 [G, D])."""
+    K = _u16(K)
+    G, S, D = K.shape
+    scores, mu = score_cosine_windowed(K, max(S, 1))
+    return scores, (mu[:, 0] if S > 0 else np.zeros((G, D), np.float64))
 
 
 def topk(scores32, k, S=None):

@@ -129,6 +129,49 @@ int ora_score_l2(const uint16_t *K, int64_t G, int64_t S, int64_t D, double *sco
     return ORA_OK;
 }
 
+/* Cosine dissimilarity of key t to a centroid: 1 - cos(k_t, mu), the score of
+ * the geometry-based baseline the ManifoldKV abstract contrasts with its L2
+ * score (keys scored by cosine similarity to a global centroid; the most
+ * dissimilar kept).  Where k_t or mu is the zero vector the cosine is taken as
+ * 0 (score 1). */
+static double cosine_dissimilarity(const uint16_t *krow, const double *mu, int64_t D) {
+    double dot = 0.0, kk = 0.0, mm = 0.0;
+    for (int64_t c = 0; c < D; ++c) {
+        double x = bf16_to_double(krow[c]);
+        dot += x * mu[c];
+        kk += x * x;
+        mm += mu[c] * mu[c];
+    }
+    if (kk == 0.0 || mm == 0.0) return 1.0;
+    /* ||k|| ||mu|| as one square root of the product: for k = mu it is exactly
+     * ||k||^2, so a key equal to its centroid scores exactly 0 */
+    return 1.0 - dot / sqrt(kk * mm);
+}
+
+/* The cosine score against the centroid of each contiguous window of W keys
+ * (W >= S: one global centroid), windows as in ora_score_l2_windowed. */
+int ora_score_cosine_windowed(const uint16_t *K, int64_t G, int64_t S, int64_t D, int64_t W,
+                              double *scores, double *centroids) {
+    if (G < 0 || S < 0 || D <= 0 || W <= 0 || (S > 0 && G > 0 && (!K || !scores)))
+        return ORA_EINVAL;
+    if (!all_finite_bf16(K, G * S * D)) return ORA_ENONFINITE;
+    int64_t nwin = (S + W - 1) / W;
+    double *mu = (double *)malloc(sizeof(double) * (size_t)D);
+    if (!mu) return ORA_ENOMEM;
+    for (int64_t g = 0; g < G; ++g) {
+        const uint16_t *Kg = K + g * S * D;
+        for (int64_t j = 0; j < nwin; ++j) {
+            int64_t t0 = j * W;
+            int64_t t1 = t0 + W < S ? t0 + W : S;
+            centroid_range(Kg, D, t0, t1, mu);
+            if (centroids) memcpy(centroids + (g * nwin + j) * D, mu, sizeof(double) * (size_t)D);
+            for (int64_t t = t0; t < t1; ++t) scores[g * S + t] = cosine_dissimilarity(Kg + t * D, mu, D);
+        }
+    }
+    free(mu);
+    return ORA_OK;
+}
+
 /* --------------------------------------------------------------- top-k */
 
 typedef struct {

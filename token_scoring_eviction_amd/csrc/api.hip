@@ -27,7 +27,8 @@ extern "C" size_t kvc_workspace_bytes(kvc_op op, const kvc_dims *d, int64_t k, i
     const int64_t G = d->L * d->B * d->H_kv;
     switch (op) {
         case KVC_OP_SCORE_L2: return kvc::score_workspace_bytes(G, d->S, d->S);
-        case KVC_OP_SCORE_L2_WINDOWED: return kvc::score_workspace_bytes(G, d->S, W);
+        case KVC_OP_SCORE_L2_WINDOWED:
+        case KVC_OP_SCORE_CENTROID: return kvc::score_workspace_bytes(G, d->S, W);
         case KVC_OP_TOPK_COMPACT: return kvc::topk_workspace_bytes(G, d->S, k);
         case KVC_OP_LOWRANK_COMPRESS: return kvc::compress_workspace_bytes(d);
         case KVC_OP_OJA_UPDATE: return kvc::oja_workspace_bytes(d, W);

@@ -1,7 +1,11 @@
 // ManifoldKV scoring: Euclidean distance of every key to the centroid of the
 // slice ("ManifoldKV: Training-Free KV Cache Compression via Euclidean Outlier
 // Detection", abstract) or of its contiguous window (WindowedManifoldKV, same
-// abstract).  The global score is the windowed score with one window.
+// abstract).  The global score is the windowed score with one window.  The
+// same kernels also give the cosine dissimilarity 1 - cos(k, mu) of the
+// cosine-to-centroid baseline that abstract compares against, evaluated as
+// ||k/||k|| - mu/||mu||||^2 / 2 so that nearly parallel keys keep their
+// relative accuracy.
 //
 // Fused path (used whenever a window's tiles fit on the GPU at once): one
 // cooperative launch of a persistent grid reads every key exactly once.
@@ -36,8 +40,12 @@ namespace {
 constexpr int kChunk = 256;   // tokens per centroid partial
 constexpr int kThreads = 256;
 
+constexpr int kMetricL2 = KVC_METRIC_L2;
+constexpr int kMetricCosine = KVC_METRIC_COSINE;
+
 struct WinGeom {
     int64_t G, S, W, nwin, nchunk;  // nchunk: chunks per window
+    int metric;                     // kvc_metric
 };
 
 __global__ __launch_bounds__(kThreads) void centroid_partial(const uint16_t *__restrict__ K,
@@ -128,6 +136,64 @@ __global__ __launch_bounds__(kThreads) void l2_distance(const uint16_t *__restri
     if (valid && lane16 == 0) scores[tok] = sqrtf(part);
 }
 
+// a*b - c*d with both products rounded on their own: never contracted into a
+// fused multiply-add, so equal operands cancel exactly.
+__device__ __forceinline__ float diff_of_products(float a, float b, float c, float d) {
+#pragma clang fp contract(off)
+    return a * b - c * d;
+}
+
+// 1 - cos(k_t, mu) as ||k_t/||k_t|| - mu/||mu||||^2 / 2; 1 where k_t or mu is
+// zero.  16 lanes per key row.
+__global__ __launch_bounds__(kThreads) void cosine_distance(const uint16_t *__restrict__ K,
+                                                            const float *__restrict__ mu_dir,
+                                                            WinGeom geo, float *__restrict__ scores) {
+    const int64_t tok = static_cast<int64_t>(blockIdx.x) * (kThreads / 16) + (threadIdx.x >> 4);
+    const int lane16 = threadIdx.x & 15;
+    const bool valid = tok < geo.G * geo.S;
+    float x[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    float m[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (valid) {
+        const int64_t g = tok / geo.S;
+        const int64_t t = tok - g * geo.S;
+        const int64_t w = t / geo.W;
+        const uint4 v = reinterpret_cast<const uint4 *>(K + tok * kHeadDim)[lane16];
+        x[0] = bf16_lo(v.x); x[1] = bf16_hi(v.x); x[2] = bf16_lo(v.y); x[3] = bf16_hi(v.y);
+        x[4] = bf16_lo(v.z); x[5] = bf16_hi(v.z); x[6] = bf16_lo(v.w); x[7] = bf16_hi(v.w);
+        const float4 *m4 =
+            reinterpret_cast<const float4 *>(mu_dir + (g * geo.nwin + w) * kHeadDim + lane16 * 8);
+        const float4 ma = m4[0], mb = m4[1];
+        m[0] = ma.x; m[1] = ma.y; m[2] = ma.z; m[3] = ma.w;
+        m[4] = mb.x; m[5] = mb.y; m[6] = mb.z; m[7] = mb.w;
+    }
+    auto sum16 = [](float a) {
+        a += __shfl_xor(a, 8, 16);
+        a += __shfl_xor(a, 4, 16);
+        a += __shfl_xor(a, 2, 16);
+        a += __shfl_xor(a, 1, 16);
+        return a;
+    };
+    // both norms with the same lane split and butterfly, so k = mu scores exactly 0
+    float kk = 0.f, mm = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        kk += x[j] * x[j];
+        mm += m[j] * m[j];
+    }
+    kk = sum16(kk);
+    mm = sum16(mm);
+    const float inv = kk > 0.f ? 1.f / sqrtf(kk) : 0.f;
+    const float inv_m = mm > 0.f ? 1.f / sqrtf(mm) : 0.f;
+    float e = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const float d = diff_of_products(x[j], inv, m[j], inv_m);
+        e += d * d;
+    }
+    e = sum16(e);
+    if (valid && lane16 == 0) scores[tok] = (kk > 0.f && mm > 0.f) ? 0.5f * e : 1.f;
+}
+
 // ----------------------------------------------------------- fused path
 
 #ifndef KVC_FUSE_ROWS
@@ -143,6 +209,7 @@ constexpr uint32_t kSpinLimit = 1u << 16;  // ~0.1 s of polling: far above any r
 
 struct FuseGeom {
     int64_t G, S, W, nwin;
+    int metric;       // kvc_metric
     int64_t members;  // tiles per window
     int64_t teams;    // G * nwin
     int64_t tiles;    // teams * members
@@ -194,6 +261,16 @@ __device__ __forceinline__ void row_transpose_reduce(float *v, int lane16) {
     }
 }
 
+// Sum over the 16 lanes of a row group, the same bits in every lane (each
+// butterfly step adds a commuted pair).
+__device__ __forceinline__ float sum16(float a) {
+    a += dpp_f<kDppXor15>(a);
+    a += dpp_f<kDppXor7>(a);
+    a += dpp_f<kDppXor3>(a);
+    a += dpp_f<kDppXor1>(a);
+    return a;
+}
+
 __global__ __launch_bounds__(kFuseThreads) void zero_words(uint32_t *p, int64_t n) {
     for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
          i += static_cast<int64_t>(gridDim.x) * blockDim.x)
@@ -208,6 +285,7 @@ __device__ __forceinline__ uint64_t tagged(float mu) {
     return (static_cast<uint64_t>(kReady) << 32) | __float_as_uint(mu);
 }
 
+template <int kMetric>
 __global__ __launch_bounds__(kFuseThreads, KVC_FUSE_MINBLOCKS) void l2_fused(const uint16_t *__restrict__ K, FuseGeom geo,
                                                          float *partial, uint64_t *mu_pub,
                                                          uint32_t *counters, uint32_t *status,
@@ -304,15 +382,17 @@ __global__ __launch_bounds__(kFuseThreads, KVC_FUSE_MINBLOCKS) void l2_fused(con
             red[mg][cg * 4 + 3] = sw;
         }
         __syncthreads();
+        float mu = 0.f;
         if (tid < kHeadDim) {
             float sum = 0.f;
 #pragma unroll
             for (int q = 0; q < 8; ++q) sum += red[q][tid];
-            const float mu = sum / static_cast<float>(t.w1 - t.w0);
-            __hip_atomic_store(mu_pub + t.team * kHeadDim + tid, tagged(mu), __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
+            mu = sum / static_cast<float>(t.w1 - t.w0);
             if (mu_user) mu_user[t.team * kHeadDim + tid] = mu;
         }
+        if (tid < kHeadDim)
+            __hip_atomic_store(mu_pub + t.team * kHeadDim + tid, tagged(mu), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
         __syncthreads();  // red is reused by the caller
     };
     // The team's centroid into mu_s: each channel's tagged word is polled
@@ -348,21 +428,52 @@ __global__ __launch_bounds__(kFuseThreads, KVC_FUSE_MINBLOCKS) void l2_fused(con
         float m[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) m[j] = mu_s[lane16 * 8 + j];
-        float d2[kFuseRows];
+        if (kMetric == kMetricCosine) {
+            // ||k/||k|| - mu/||mu||||^2 / 2 per row: the 16 lanes of a row group hold its
+            // 128 channels; lane r keeps row r's score (1 where k or mu is zero)
+            // ||mu||^2 with the same lane split and butterfly as each key's ||k||^2, so a
+            // key equal to the centroid gets the same scale and scores exactly 0
+            float mm = 0.f;
 #pragma unroll
-        for (int r = 0; r < kFuseRows; ++r) {
-            float x[8];
-            widen8(v[r], x);
-            float acc = 0.f;
+            for (int j = 0; j < 8; ++j) mm += m[j] * m[j];
+            mm = sum16(mm);
+            const float inv_m = mm > 0.f ? 1.f / sqrtf(mm) : 0.f;
+            float mine = 0.f;
 #pragma unroll
-            for (int j = 0; j < 8; ++j) {
-                const float d = x[j] - m[j];
-                acc += d * d;
+            for (int r = 0; r < kFuseRows; ++r) {
+                float x[8];
+                widen8(v[r], x);
+                float kk = 0.f;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) kk += x[j] * x[j];
+                kk = sum16(kk);
+                const float inv = kk > 0.f ? 1.f / sqrtf(kk) : 0.f;
+                float e = 0.f;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const float d = diff_of_products(x[j], inv, m[j], inv_m);
+                    e += d * d;
+                }
+                e = sum16(e);
+                if (lane16 == r) mine = (kk > 0.f && mm > 0.f) ? 0.5f * e : 1.f;
             }
-            d2[r] = acc;
-        }
-        row_transpose_reduce<kFuseRows>(d2, lane16);
-        {
+            const int64_t row = t.t0 + 16 * lane16;
+            if (lane16 < kFuseRows && row < t.w1) scores[t.g * geo.S + row] = mine;
+        } else {
+            float d2[kFuseRows];
+#pragma unroll
+            for (int r = 0; r < kFuseRows; ++r) {
+                float x[8];
+                widen8(v[r], x);
+                float acc = 0.f;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const float d = x[j] - m[j];
+                    acc += d * d;
+                }
+                d2[r] = acc;
+            }
+            row_transpose_reduce<kFuseRows>(d2, lane16);
             const int r = kFuseRows == 16 ? lane16 : (lane16 >> 1);
             const int64_t row = t.t0 + 16 * r;
             if ((kFuseRows == 16 || (lane16 & 1) == 0) && row < t.w1)
@@ -397,8 +508,9 @@ __global__ __launch_bounds__(kFuseThreads, KVC_FUSE_MINBLOCKS) void l2_fused(con
     }
 }
 
-FuseGeom make_fuse_geom(int64_t G, int64_t S, int64_t W) {
+FuseGeom make_fuse_geom(int64_t G, int64_t S, int64_t W, int metric = kMetricL2) {
     FuseGeom f;
+    f.metric = metric;
     f.G = G;
     f.S = S;
     f.W = W < S ? W : S;
@@ -416,20 +528,20 @@ void fused_ws_layout(Ws &ws, const FuseGeom &f) {
     ws.template take<uint32_t>(static_cast<size_t>(f.teams + 1));          // counters, status
 }
 
-// Co-resident workgroups of l2_fused on the current device (0 if unknown).
-int64_t fused_capacity() {
+// Co-resident workgroups of a fused-kernel instance on the current device (0 if unknown).
+int64_t fused_capacity(const void *kernel) {
     int dev = 0, cus = 0, per_cu = 0, coop = 0;
     if (hipGetDevice(&dev) != hipSuccess) return 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
     if (hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) != hipSuccess || !coop) return 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(&l2_fused),
-                                                     kFuseThreads, 0) != hipSuccess)
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kFuseThreads, 0) != hipSuccess)
         return 0;
     return static_cast<int64_t>(cus) * per_cu;
 }
 
-WinGeom make_geom(int64_t G, int64_t S, int64_t W) {
+WinGeom make_geom(int64_t G, int64_t S, int64_t W, int metric = kMetricL2) {
     WinGeom geo;
+    geo.metric = metric;
     geo.G = G;
     geo.S = S;
     geo.W = W < S ? W : S;
@@ -459,9 +571,10 @@ bool force_unfused() {
 }
 
 kvc_status score_windowed_impl(const uint16_t *K, int64_t G, int64_t S, int32_t D, int64_t W,
-                               float *scores, float *centroids, void *ws, size_t ws_bytes,
-                               hipStream_t stream) {
+                               int metric, float *scores, float *centroids, void *ws,
+                               size_t ws_bytes, hipStream_t stream) {
     if (G < 0 || S < 1 || W < 1 || D <= 0) return KVC_ERR_INVALID_ARGUMENT;
+    if (metric != kMetricL2 && metric != kMetricCosine) return KVC_ERR_INVALID_ARGUMENT;
     if (D != kHeadDim) return KVC_ERR_UNSUPPORTED;
     if (S > INT32_MAX) return KVC_ERR_UNSUPPORTED;
     if (G == 0) return KVC_OK;
@@ -471,16 +584,18 @@ kvc_status score_windowed_impl(const uint16_t *K, int64_t G, int64_t S, int32_t 
         return KVC_ERR_INVALID_ARGUMENT;
     if (ws_bytes < score_bytes(G, S, W)) return KVC_ERR_WORKSPACE_TOO_SMALL;
 
-    const FuseGeom f = make_fuse_geom(G, S, W);
-    static int64_t capacity_by_dev[64];
-    static bool known[64];
+    const FuseGeom f = make_fuse_geom(G, S, W, metric);
+    const void *fused = metric == kMetricCosine ? reinterpret_cast<const void *>(&l2_fused<kMetricCosine>)
+                                                : reinterpret_cast<const void *>(&l2_fused<kMetricL2>);
+    static int64_t capacity_by_dev[2][64];
+    static bool known[2][64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return KVC_ERR_HIP;
-    if (!known[dev]) {
-        capacity_by_dev[dev] = fused_capacity();
-        known[dev] = true;
+    if (!known[metric][dev]) {
+        capacity_by_dev[metric][dev] = fused_capacity(fused);
+        known[metric][dev] = true;
     }
-    const int64_t capacity = capacity_by_dev[dev];
+    const int64_t capacity = capacity_by_dev[metric][dev];
     if (capacity >= f.members && f.tiles <= INT32_MAX && !force_unfused()) {
         WsCursor cur(ws);
         float *partial = cur.take<float>(static_cast<size_t>(f.tiles) * kHeadDim);
@@ -502,14 +617,14 @@ kvc_status score_windowed_impl(const uint16_t *K, int64_t G, int64_t S, int32_t 
         int64_t grid = capacity / f.members * f.members;
         if (grid > f.tiles) grid = f.tiles;
         void *args[] = {&K, &fa, &partial, &mu_pub, &counters, &status, &scores, &mu_user};
-        if (hipLaunchCooperativeKernel(reinterpret_cast<const void *>(&l2_fused),
+        if (hipLaunchCooperativeKernel(fused,
                                        dim3(static_cast<unsigned>(grid)), dim3(kFuseThreads), args, 0,
                                        stream) != hipSuccess)
             return KVC_ERR_HIP;
         return launch_status();
     }
 
-    const WinGeom geo = make_geom(G, S, W);
+    const WinGeom geo = make_geom(G, S, W, metric);
     WsCursor cur(ws);
     float *partial = cur.take<float>(static_cast<size_t>(geo.G * geo.nwin * geo.nchunk) * kHeadDim);
     float *mu = cur.take<float>(static_cast<size_t>(geo.G * geo.nwin) * kHeadDim);
@@ -522,8 +637,12 @@ kvc_status score_windowed_impl(const uint16_t *K, int64_t G, int64_t S, int32_t 
                        dim3(kHeadDim), 0, stream, partial, geo, mu, centroids);
     const int64_t nblk = (geo.G * geo.S + (kThreads / 16) - 1) / (kThreads / 16);
     if (nblk > INT32_MAX) return KVC_ERR_UNSUPPORTED;
-    hipLaunchKernelGGL(l2_distance, dim3(static_cast<unsigned>(nblk)), dim3(kThreads), 0, stream, K,
-                       mu, geo, scores);
+    if (metric == kMetricCosine)
+        hipLaunchKernelGGL(cosine_distance, dim3(static_cast<unsigned>(nblk)), dim3(kThreads), 0, stream,
+                           K, mu, geo, scores);
+    else
+        hipLaunchKernelGGL(l2_distance, dim3(static_cast<unsigned>(nblk)), dim3(kThreads), 0, stream, K,
+                           mu, geo, scores);
     return launch_status();
 }
 
@@ -538,11 +657,19 @@ size_t score_workspace_bytes(int64_t G, int64_t S, int64_t W) {
 
 extern "C" kvc_status kvc_score_l2(const uint16_t *K, int64_t G, int64_t S, int32_t D, float *scores,
                                    float *centroid, void *ws, size_t ws_bytes, hipStream_t stream) {
-    return kvc::score_windowed_impl(K, G, S, D, S, scores, centroid, ws, ws_bytes, stream);
+    return kvc::score_windowed_impl(K, G, S, D, S, KVC_METRIC_L2, scores, centroid, ws, ws_bytes,
+                                    stream);
 }
 
 extern "C" kvc_status kvc_score_l2_windowed(const uint16_t *K, int64_t G, int64_t S, int32_t D,
                                             int64_t W, float *scores, float *centroids, void *ws,
                                             size_t ws_bytes, hipStream_t stream) {
-    return kvc::score_windowed_impl(K, G, S, D, W, scores, centroids, ws, ws_bytes, stream);
+    return kvc::score_windowed_impl(K, G, S, D, W, KVC_METRIC_L2, scores, centroids, ws, ws_bytes,
+                                    stream);
+}
+
+extern "C" kvc_status kvc_score_centroid(const uint16_t *K, int64_t G, int64_t S, int32_t D, int64_t W,
+                                         int32_t metric, float *scores, float *centroids, void *ws,
+                                         size_t ws_bytes, hipStream_t stream) {
+    return kvc::score_windowed_impl(K, G, S, D, W, metric, scores, centroids, ws, ws_bytes, stream);
 }

@@ -17,11 +17,13 @@ LIB_PATH = os.path.join(_PKG, "libkvc.so")
 
 OK, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_WORKSPACE_TOO_SMALL, ERR_HIP = range(5)
 OP_SCORE_L2, OP_SCORE_L2_WINDOWED, OP_TOPK_COMPACT, OP_LOWRANK_COMPRESS, OP_OJA_UPDATE, \
-    OP_RECONSTRUCT = range(6)
+    OP_RECONSTRUCT, OP_SCORE_CENTROID = range(7)
+METRIC_L2, METRIC_COSINE = 0, 1
+METRICS = {"l2": METRIC_L2, "cosine": METRIC_COSINE}
 
 EXPORTED = ("kvc_abi_version", "kvc_status_str", "kvc_workspace_bytes", "kvc_score_l2",
-            "kvc_score_l2_windowed", "kvc_topk_compact", "kvc_lowrank_compress", "kvc_oja_update",
-            "kvc_reconstruct")
+            "kvc_score_l2_windowed", "kvc_score_centroid", "kvc_topk_compact", "kvc_lowrank_compress",
+            "kvc_oja_update", "kvc_reconstruct")
 
 
 class KvcError(RuntimeError):
@@ -55,6 +57,7 @@ def load(path: str = LIB_PATH):
             sigs = {
                 "kvc_score_l2": [P, I64, I64, I32, P, P, P, SZ, P],
                 "kvc_score_l2_windowed": [P, I64, I64, I32, I64, P, P, P, SZ, P],
+                "kvc_score_centroid": [P, I64, I64, I32, I64, I32, P, P, P, SZ, P],
                 "kvc_topk_compact": [P, I64, I64, I64, I64, P, P, I32, P, P, P, P, SZ, P],
                 "kvc_lowrank_compress": [DP, P, P, P, P, P, P, P, P, P, SZ, P],
                 "kvc_oja_update": [DP, P, P, I32, ctypes.c_float, P, SZ, P],
@@ -132,6 +135,23 @@ def kvc_score_l2_windowed(K, W, scores=None, centroids=None):
     _check("kvc_score_l2_windowed",
            lib.kvc_score_l2_windowed(_ptr(_bits(K)), G, S, D, W, _ptr(scores), _ptr(centroids),
                                      _ptr(ws), nb, _stream()))
+    return scores
+
+
+def kvc_score_centroid(K, W=None, metric="l2", scores=None, centroids=None):
+    """K: bf16 [G, S, D]; W: window (None: the global centroid); metric "l2" or
+    "cosine" (or a kvc_metric value) -> scores fp32 [G, S]."""
+    lib = load()
+    G, S, D = K.shape
+    W = S if W is None else W
+    m = METRICS[metric] if isinstance(metric, str) else int(metric)
+    if scores is None:
+        scores = torch.empty((G, S), dtype=torch.float32, device=K.device)
+    nb = workspace_bytes(OP_SCORE_CENTROID, _dims(1, 1, G, 0, S, 0, D, 0, 0), 0, W)
+    ws = workspace(nb, K.device.index)
+    _check("kvc_score_centroid",
+           lib.kvc_score_centroid(_ptr(_bits(K)), G, S, D, W, m, _ptr(scores), _ptr(centroids),
+                                  _ptr(ws), nb, _stream()))
     return scores
 
 

@@ -37,12 +37,16 @@ def alloc_eviction(G, S, keep, D=128, device="cuda"):
         V_out=torch.empty((G, keep, D), dtype=torch.bfloat16, device=device))
 
 
-def manifold_evict(K, V, keep, W=None, buf: EvictionBuffers | None = None):
+def manifold_evict(K, V, keep, W=None, buf: EvictionBuffers | None = None, metric="l2"):
     """One ManifoldKV eviction pass over K, V (bf16 [G, S, 128]).  W=None: global
-    centroid; otherwise contiguous windows of W tokens.  Returns the buffers."""
+    centroid; otherwise contiguous windows of W tokens.  metric "cosine" scores
+    1 - cos(k, mu) instead of ||k - mu|| (the cosine-to-centroid baseline).
+    Returns the buffers."""
     G, S, D = K.shape
     buf = buf or alloc_eviction(G, S, keep, D, K.device)
-    if W is None:
+    if metric != "l2":
+        kvc.kvc_score_centroid(K, W=W, metric=metric, scores=buf.scores)
+    elif W is None:
         kvc.kvc_score_l2(K, scores=buf.scores)
     else:
         kvc.kvc_score_l2_windowed(K, W, scores=buf.scores)
