@@ -61,6 +61,9 @@ def parse():
     ap.add_argument("--metric", choices=["l2", "cosine"], default="l2",
                     help="centroid score of configs 0-2: ManifoldKV's L2 distance (the workload) "
                          "or the cosine-dissimilarity baseline")
+    ap.add_argument("--storage", choices=["fp32", "bf16"], default="fp32",
+                    help="OjaKV configs 3-4: compressed cache (K~, V~, K^, V^) in fp32 (the "
+                         "workload) or bf16 (the memory-saving layout)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-ref", type=int, default=0, metavar="MIB",
@@ -159,19 +162,21 @@ def manifold_workload(cfg, dev, metric="l2"):
     return ops, G * S, algo, config, cpu
 
 
-def oja_workload(dev):
+def oja_workload(dev, storage="fp32"):
     import synth
     from token_scoring_eviction_amd import kvc, pipeline
     L, B, Hkv, Hq, S, R, Wq = 32, 4, 8, 32, 32768, 64, 32
     inp = synth.oja_inputs(L, B, Hkv, Hq, S, R=R, Wq=Wq, device=dev)
     G = L * B * Hkv
     k = pipeline.anchor_count(S)
-    st = pipeline.alloc_hybrid(G, S, R, device=dev, max_anchor=k, with_hat=False)
+    st = pipeline.alloc_hybrid(G, S, R, device=dev, max_anchor=k, with_hat=False, storage=storage)
+    ob = 2 if storage == "bf16" else 4  # bytes per stored K~ / V~ element
+    compress = kvc.kvc_lowrank_compress_bf16 if storage == "bf16" else kvc.kvc_lowrank_compress
     ops = [
-        Op("kvc_lowrank_compress",
-           lambda: kvc.kvc_lowrank_compress(inp.K, inp.V, inp.Q, inp.Uk, inp.Uv, L, B, Hkv,
-                                            K_tilde=st.Kt, V_tilde=st.Vt, err=st.err),
-           G * S * (2 * 256 + 2 * R * 4 + 4),
+        Op("kvc_lowrank_compress" + ("_bf16" if storage == "bf16" else ""),
+           lambda: compress(inp.K, inp.V, inp.Q, inp.Uk, inp.Uv, L, B, Hkv,
+                            K_tilde=st.Kt, V_tilde=st.Vt, err=st.err),
+           G * S * (2 * 256 + 2 * R * ob + 4),
            flops=G * S * (2 * 2 * 128 * R + 3 * 2 * 128 * (Hq // Hkv) * Wq + 2 * 2 * 128 * R),
            kernel="project_kernel"),
         Op("kvc_topk_compact",
@@ -179,10 +184,10 @@ def oja_workload(dev):
                                         V_out=st.V_anchor),
            G * S * 4 + G * k * (2 * 256 * 2 + 4), kernel="select_compact"),
     ]
-    algo = G * S * (2 * 256 + 2 * R * 4 + 4) + G * k * (2 * 256 * 2 + 4)
+    algo = G * S * (2 * 256 + 2 * R * ob + 4) + G * k * (2 * 256 * 2 + 4)
     config = {"workload": "OjaKV hybrid low-rank prefill compression, 32 layers x batch 4 x 8 KV heads "
                           "(32 query heads), d_h 128, S=32768, r=64, 32-query window, 5% anchors",
-              "slices": G, "seq_len": S, "rank": R, "anchors": k}
+              "slices": G, "seq_len": S, "rank": R, "anchors": k, "storage": storage}
 
     def cpu(budget):
         import numpy as np
@@ -223,7 +228,8 @@ def run_loop_config(args, dev):
         Uk, Uv = Uk0.clone(), Uv0.clone()
         e = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
         e[0].record()
-        st = pipeline.ojakv_prefill(inp.K, inp.V, inp.Q, Uk, Uv, L, B, Hkv, S0, T=T, pool=32, eta=1e-3)
+        st = pipeline.ojakv_prefill(inp.K, inp.V, inp.Q, Uk, Uv, L, B, Hkv, S0, T=T, pool=32, eta=1e-3,
+                                    storage=args.storage)
         e[1].record()
         upd = []
         for s in range(steps):
@@ -255,13 +261,16 @@ def run_loop_config(args, dev):
     pre = sum(e[0].elapsed_time(e[1]) for e, _ in times) / reps
     upd = sum(sum(a.elapsed_time(b) for a, b in u) for _, u in times) / reps / 8
     scorings = G * sum(S0 + T * j for j in range(9))
-    per_pass = lambda S: G * S * (2 * 256 + 2 * R * 4 + 4 + 2 * 512) + G * pipeline.anchor_count(S) * 1028
+    ob = 2 if args.storage == "bf16" else 4  # bytes per stored K~, V~, K^, V^ element
+    per_pass = lambda S: (G * S * (2 * 256 + 2 * R * ob + 4 + 2 * 128 * ob)
+                          + G * pipeline.anchor_count(S) * 1028)
     algo = G * S0 * 256 * 2 + sum(per_pass(S0 + T * j) for j in range(9))
     line = base_line(args, "KV head-tokens scored+compacted/s", scorings / (ms / 1e3), ms, reps,
                      {"workload": "OjaKV full loop: 32 layers x batch 1 x 8 KV heads (32 query heads), "
                                   "d_h 128, S=131072 prefill pooled by 32 + 256 decode steps, update "
                                   "every 32 (eta 1e-3, r=64, 5% anchors, K^/V^ rebuilt per update)",
-                      "slices": G, "seq_len": S0, "decode_steps": steps, "updates": 8})
+                      "slices": G, "seq_len": S0, "decode_steps": steps, "updates": 8,
+                      "storage": args.storage})
     line["phases_ms"] = {"prefill": pre, "per_update": upd, "whole_loop": ms}
     line["step_hbm"] = {"algorithmic_bytes": algo, "GBs": algo / ms / 1e6,
                         "frac": algo / ms / 1e6 / HBM_PEAK_GBS}
@@ -294,7 +303,7 @@ def main():
     if args.config == 4:
         return run_loop_config(args, dev)
     if args.config == 3:
-        ops, head_tokens, algo, config, cpu = oja_workload(dev)
+        ops, head_tokens, algo, config, cpu = oja_workload(dev, args.storage)
     else:
         ops, head_tokens, algo, config, cpu = manifold_workload(args.config, dev, args.metric)
     torch.cuda.synchronize()

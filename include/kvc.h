@@ -94,7 +94,8 @@ const char *kvc_status_str(kvc_status s);
  *     tokens; W = window (ignored for SCORE_L2).
  *   TOPK_COMPACT: G = L*B*H_kv slices of S tokens; k = tokens kept.
  *   LOWRANK_COMPRESS, OJA_UPDATE, RECONSTRUCT: shapes from `d`; for OJA_UPDATE
- *     d->S is the token count N and W is the pooling window.
+ *     d->S is the token count N and W is the pooling window.  The bf16-storage
+ *     variants need what LOWRANK_COMPRESS and RECONSTRUCT need.
  * 0 means the call needs no workspace (ws may then be NULL); invalid shapes
  * also give 0 and are reported by the call itself. */
 size_t kvc_workspace_bytes(kvc_op op, const kvc_dims *d, int64_t k, int64_t W);
@@ -160,6 +161,16 @@ kvc_status kvc_lowrank_compress(const kvc_dims *d, const uint16_t *K, const uint
                                 float *K_tilde, float *V_tilde, float *err, void *ws,
                                 size_t ws_bytes, hipStream_t stream);
 
+/* bf16 storage of the compressed cache ([OJA] efficiency analysis: the memory
+ * saving comes from storing K~ and V~ instead of K and V): as
+ * kvc_lowrank_compress, with K~ and V~ written as bf16, the round-to-nearest-even
+ * of the same fp32 result; err stays fp32.
+ *   K_tilde, V_tilde: bf16 [L][B][H_kv][S_stride][R] */
+kvc_status kvc_lowrank_compress_bf16(const kvc_dims *d, const uint16_t *K, const uint16_t *V,
+                                     const uint16_t *Q_win, const float *U_k, const float *U_v,
+                                     uint16_t *K_tilde, uint16_t *V_tilde, float *err, void *ws,
+                                     size_t ws_bytes, hipStream_t stream);
+
 /* Oja basis update with pooling and QR ([OJA] how it works: the Oja rule;
  * method details: prefill update on AvgPool(X, pool) with the empirical
  * covariance, decode update on the buffered tokens, re-orthonormalisation by
@@ -186,6 +197,15 @@ kvc_status kvc_oja_update(const kvc_dims *d, float *U, const uint16_t *X, int32_
 kvc_status kvc_reconstruct(const kvc_dims *d, const float *X_tilde, const float *U,
                            const int32_t *anchor_idx, const uint16_t *anchor_rows, int64_t k,
                            float *X_hat, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Reconstruction from bf16 storage: as kvc_reconstruct, with X_tilde and X_hat
+ * bf16.  X_hat = bf16(X_tilde U^T), an fp32 accumulation of the exact bf16
+ * X_tilde against U split as hi + lo, rounded to nearest even; anchor rows are
+ * copied bit for bit.
+ *   X_tilde: bf16 [L][B][H_kv][S_stride][R];  X_hat: bf16 [L][B][H_kv][S_stride][D] */
+kvc_status kvc_reconstruct_bf16(const kvc_dims *d, const uint16_t *X_tilde, const float *U,
+                                const int32_t *anchor_idx, const uint16_t *anchor_rows, int64_t k,
+                                uint16_t *X_hat, void *ws, size_t ws_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -74,3 +74,25 @@ def index_sets_agree(gpu_idx, ora_idx, ora_scores32, k, rel=1e-4):
                 return False, -1
             nb += diff.size
     return True, nb
+
+
+def bf16_close(gpu_bits, ora, ulps=1, abs_frac=2.0 ** -14):
+    """bf16 outputs: within +-ulps bf16 ulps of the oracle's value rounded to bf16
+    (nearest even), or within abs_frac * rms(slice) absolutely: for values below
+    ~2^-6 of the slice's rms a bf16 ulp is smaller than the fp32 result's own error
+    (hi/lo-split operands, fp32 accumulation: a few 2^-16 of the row scale).
+    Axis 0 = slice.  Returns (ok, worst ulp distance among failures, or overall)."""
+    gpu_bits = np.asarray(gpu_bits, np.uint16)
+    ora = np.asarray(ora, np.float64)
+    ob = bf16_bits_rne(ora)
+
+    def ordered(b):
+        b = b.astype(np.int64)
+        return np.where(b & 0x8000, -(b & 0x7FFF), b & 0x7FFF)
+
+    dist = np.abs(ordered(gpu_bits) - ordered(ob))
+    g = (gpu_bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    axes = tuple(range(1, ora.ndim))
+    rms = np.sqrt(np.mean(ora ** 2, axis=axes, keepdims=True))
+    ok = (dist <= ulps) | (np.abs(g - ora) <= abs_frac * rms)
+    return bool(ok.all()), int(dist[~ok].max()) if (~ok).any() else int(dist.max())

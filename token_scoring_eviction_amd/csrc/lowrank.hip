@@ -220,10 +220,12 @@ __global__ __launch_bounds__(256) void prep_query_kernel(const uint16_t *__restr
 // LDS: U^T fragments [rb][s][hi|lo] (NRB*16 KB), then Q'' fragments
 // [qb][s][term] (nqb*8*nterm KB).  HB = 1 runs 16 waves per block (4 per SIMD),
 // HB = 2 runs 8 waves with twice the reuse of each fragment.
-template <int NRB, int HB, bool kRowStores>
+template <int NRB, int HB, bool kRowStores, typename OutT>
 __global__ __launch_bounds__(HB == 1 ? 1024 : 512) void project_kernel(
     const uint16_t *__restrict__ X, const float *__restrict__ Ubase, const u32x4 *__restrict__ qfrag,
-    int nqb, int nterm, Slices sl, float *__restrict__ Xt, float *__restrict__ err) {
+    int nqb, int nterm, Slices sl, OutT *__restrict__ Xt, float *__restrict__ err) {
+    // OutT float: fp32 K~ rows; OutT uint16_t: bf16 K~ rows (round to nearest even)
+    constexpr bool kBf16 = sizeof(OutT) == 2;
     constexpr int R = 32 * NRB;
     constexpr int TOK = 32 * HB;
     extern __shared__ u32x4 lds[];
@@ -260,7 +262,7 @@ __global__ __launch_bounds__(HB == 1 ? 1024 : 512) void project_kernel(
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int col = lane & 31, khalf = lane >> 5;
     const u32x4 *xrows = reinterpret_cast<const u32x4 *>(X + slice * sl.S_stride * kHeadDim);
-    float *xt = Xt + slice * sl.S_stride * R;
+    OutT *xt = Xt + slice * sl.S_stride * R;
     // Projection-only launches (no error score) write K~ rows in full 128-byte
     // segments; with the score fused, register pressure favours 16-byte pieces.
     constexpr bool row_stores = kRowStores;
@@ -310,13 +312,20 @@ __global__ __launch_bounds__(HB == 1 ? 1024 : 512) void project_kernel(
             }
             if constexpr (row_stores) {
                 // lane (col, khalf) holds rank rb*32+col of tokens 8(j/4) + 4khalf + j%4:
-                // each store writes two 128-byte row segments
+                // each store writes two 128-byte (fp32) or 64-byte (bf16 pairs) row segments
 #pragma unroll
                 for (int hb = 0; hb < HB; ++hb)
 #pragma unroll
                     for (int j = 0; j < 16; ++j) {
                         const int64_t tok = t0 + hb * 32 + (j >> 2) * 8 + khalf * 4 + (j & 3);
-                        if (tok < t_end) xt[tok * R + rb * 32 + col] = a[hb][j];
+                        if constexpr (kBf16) {
+                            const float nb = __shfl_xor(a[hb][j], 1);  // rank col ^ 1, same token
+                            if (!(col & 1) && tok < t_end)
+                                *reinterpret_cast<uint32_t *>(xt + tok * R + rb * 32 + col) =
+                                    f32_to_bf16_rne(a[hb][j]) | (f32_to_bf16_rne(nb) << 16);
+                        } else {
+                            if (tok < t_end) xt[tok * R + rb * 32 + col] = a[hb][j];
+                        }
                     }
             } else {
                 // lane (col, khalf) holds ranks rb*32 + 8q + 4khalf .. +4 of token col
@@ -324,11 +333,18 @@ __global__ __launch_bounds__(HB == 1 ? 1024 : 512) void project_kernel(
                 for (int hb = 0; hb < HB; ++hb) {
                     const int64_t tok = t0 + hb * 32 + col;
                     if (tok < t_end) {
-                        float *dst = xt + tok * R + rb * 32 + khalf * 4;
+                        OutT *dst = xt + tok * R + rb * 32 + khalf * 4;
 #pragma unroll
-                        for (int q = 0; q < 4; ++q)
-                            *reinterpret_cast<float4 *>(dst + q * 8) =
-                                make_float4(a[hb][4 * q], a[hb][4 * q + 1], a[hb][4 * q + 2], a[hb][4 * q + 3]);
+                        for (int q = 0; q < 4; ++q) {
+                            if constexpr (kBf16) {
+                                *reinterpret_cast<uint2 *>(dst + q * 8) = make_uint2(
+                                    f32_to_bf16_rne(a[hb][4 * q]) | (f32_to_bf16_rne(a[hb][4 * q + 1]) << 16),
+                                    f32_to_bf16_rne(a[hb][4 * q + 2]) | (f32_to_bf16_rne(a[hb][4 * q + 3]) << 16));
+                            } else {
+                                *reinterpret_cast<float4 *>(dst + q * 8) = make_float4(
+                                    a[hb][4 * q], a[hb][4 * q + 1], a[hb][4 * q + 2], a[hb][4 * q + 3]);
+                            }
+                        }
                     }
                 }
             }
@@ -464,6 +480,105 @@ __global__ __launch_bounds__(256) void reconstruct_kernel(const float *__restric
 #undef KVC_LOAD_X
 }
 
+// bf16 storage of the compressed cache: X~ bf16 rows are the MFMA operand as they
+// are (exact, no split), A = U hi/lo from LDS (two products), X^ rounded to bf16
+// (nearest even).  Same tiling as reconstruct_kernel; lanes col and col ^ 1 hold
+// adjacent channels of one token and the even lane stores the pair.
+template <int NRB>
+__global__ __launch_bounds__(256) void reconstruct_bf16_kernel(const uint16_t *__restrict__ Xt,
+                                                               const float *__restrict__ Ubase,
+                                                               Slices sl, uint16_t *__restrict__ Xh) {
+    constexpr int R = 32 * NRB;
+    constexpr int KS = R / 16;  // k-steps
+    __shared__ u32x4 ufr[4 * KS * 2 * 64];
+
+    const int64_t slice = blockIdx.x / sl.nsplit;
+    const int64_t split = blockIdx.x % sl.nsplit;
+    const int64_t h = slice % sl.Hkv;
+    const int64_t l = slice / (sl.Hkv * sl.B);
+    const float *U = Ubase + (l * sl.Hkv + h) * kHeadDim * R;
+
+    for (int p = threadIdx.x; p < 4 * KS * 64; p += blockDim.x) {
+        const int lane = p & 63, fs = p >> 6, s = fs % KS, cb = fs / KS;
+        const int c = cb * 32 + (lane & 31);
+        const int j0 = 16 * s + (lane >> 5) * 8;
+        float x[8];
+        const float4 *src = reinterpret_cast<const float4 *>(U + c * R + j0);
+        const float4 u0 = src[0], u1 = src[1];
+        x[0] = u0.x; x[1] = u0.y; x[2] = u0.z; x[3] = u0.w;
+        x[4] = u1.x; x[5] = u1.y; x[6] = u1.z; x[7] = u1.w;
+        u32x4 hi, lo;
+        split8(x, hi, lo);
+        ufr[((cb * KS + s) * 2 + 0) * 64 + lane] = hi;
+        ufr[((cb * KS + s) * 2 + 1) * 64 + lane] = lo;
+    }
+    __syncthreads();
+
+    const int64_t t_begin = split * sl.per_split;
+    const int64_t t_end = min(sl.S, t_begin + sl.per_split);
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int col = lane & 31, khalf = lane >> 5;
+    const uint16_t *xt = Xt + slice * sl.S_stride * R;
+    uint16_t *xh = Xh + slice * sl.S_stride * kHeadDim;
+
+    // lane (col, khalf) holds ranks 16s + 8khalf .. +8 of token t0 + col: one 16-byte load per k-step
+    const int64_t wstep = (blockDim.x / 64) * 32;
+    u32x4 xc[KS], xn[KS];
+#define KVC_LOAD_XB(T0, DST)                                                                     \
+    do {                                                                                          \
+        const int64_t tok_ = (T0) + col;                                                          \
+        const bool ok_ = tok_ < t_end;                                                            \
+        const u32x4 *src_ = reinterpret_cast<const u32x4 *>(xt + (ok_ ? tok_ : 0) * R + khalf * 8); \
+        _Pragma("unroll") for (int s_ = 0; s_ < KS; ++s_) {                                       \
+            DST[s_] = src_[2 * s_];                                                               \
+            if (!ok_) DST[s_] = u32x4{0u, 0u, 0u, 0u};                                            \
+        }                                                                                         \
+    } while (0)
+    if (t_begin + wave * 32 < t_end) KVC_LOAD_XB(t_begin + wave * 32, xc);
+    for (int64_t t0 = t_begin + wave * 32; t0 < t_end; t0 += wstep) {
+        if (t0 + wstep < t_end) KVC_LOAD_XB(t0 + wstep, xn);  // next step in flight
+#pragma unroll 1
+        for (int cb = 0; cb < 4; ++cb) {
+            f32x16 acc = {};
+#pragma unroll
+            for (int s = 0; s < KS; ++s) {
+                const u32x4 ah = ufr[((cb * KS + s) * 2 + 0) * 64 + lane];
+                const u32x4 al = ufr[((cb * KS + s) * 2 + 1) * 64 + lane];
+                acc = mfma32x32x16(xc[s], ah, acc);
+                acc = mfma32x32x16(xc[s], al, acc);
+            }
+            // lane (col, khalf) holds channel cb*32+col of tokens 8(j/4) + 4khalf + j%4
+#pragma unroll
+            for (int j = 0; j < 16; ++j) {
+                const int64_t tj = t0 + (j >> 2) * 8 + khalf * 4 + (j & 3);
+                const float nb = __shfl_xor(acc[j], 1);  // channel col ^ 1, same token
+                if (!(col & 1) && tj < t_end)
+                    *reinterpret_cast<uint32_t *>(xh + tj * kHeadDim + cb * 32 + col) =
+                        f32_to_bf16_rne(acc[j]) | (f32_to_bf16_rne(nb) << 16);
+            }
+        }
+#pragma unroll
+        for (int s = 0; s < KS; ++s) xc[s] = xn[s];
+    }
+#undef KVC_LOAD_XB
+}
+
+// Anchor rows of a bf16 X^: a bit-exact copy, 16 lanes per row.
+__global__ __launch_bounds__(256) void anchor_copy_bf16_kernel(const int32_t *__restrict__ idx,
+                                                               const uint16_t *__restrict__ rows,
+                                                               int64_t k, int64_t blocks_per_slice,
+                                                               int64_t S, int64_t S_stride,
+                                                               uint16_t *__restrict__ Xh) {
+    const int64_t g = blockIdx.x / blocks_per_slice;
+    const int64_t i = (blockIdx.x % blocks_per_slice) * 16 + (threadIdx.x >> 4);
+    const int lane16 = threadIdx.x & 15;
+    if (i >= k) return;
+    const int64_t t = idx[g * k + i];
+    if (t < 0 || t >= S) return;  // documented precondition; never write outside the slice
+    reinterpret_cast<uint4 *>(Xh + (g * S_stride + t) * kHeadDim)[lane16] =
+        reinterpret_cast<const uint4 *>(rows + (g * k + i) * kHeadDim)[lane16];
+}
+
 // Anchor rows back into X^: 16 lanes per row, bf16 widened exactly.
 __global__ __launch_bounds__(256) void anchor_scatter_kernel(const int32_t *__restrict__ idx,
                                                              const uint16_t *__restrict__ rows,
@@ -534,32 +649,34 @@ void compress_ws_layout(Ws &ws, const kvc_dims *d, bool with_q) {
 #ifndef KVC_PROJECT_HB
 #define KVC_PROJECT_HB 2
 #endif
-template <int NRB, bool kRowStores>
+template <int NRB, bool kRowStores, typename OutT>
 kvc_status launch_project_variant(const uint16_t *X, const float *U, const u32x4 *qfrag, int nqb,
-                                  int nterm, const Slices &sl, int64_t G, float *Xt, float *err,
+                                  int nterm, const Slices &sl, int64_t G, OutT *Xt, float *err,
                                   hipStream_t stream) {
     constexpr int HB = KVC_PROJECT_HB;
     const size_t lds = static_cast<size_t>(NRB * 16 + nqb * 8 * nterm) * kFragBytes;
     static bool lds_ok[64];
-    if (allow_large_lds(reinterpret_cast<const void *>(&project_kernel<NRB, HB, kRowStores>), lds_ok) != KVC_OK)
+    if (allow_large_lds(reinterpret_cast<const void *>(&project_kernel<NRB, HB, kRowStores, OutT>), lds_ok) !=
+        KVC_OK)
         return KVC_ERR_HIP;
     const int64_t blocks = G * sl.nsplit;
     if (blocks > INT32_MAX) return KVC_ERR_UNSUPPORTED;
-    hipLaunchKernelGGL((project_kernel<NRB, HB, kRowStores>), dim3(static_cast<unsigned>(blocks)),
+    hipLaunchKernelGGL((project_kernel<NRB, HB, kRowStores, OutT>), dim3(static_cast<unsigned>(blocks)),
                        dim3(HB == 1 ? 1024 : 512), lds, stream, X, U, qfrag, nqb, nterm, sl, Xt, err);
     return launch_status();
 }
 
-template <int NRB>
+template <int NRB, typename OutT>
 kvc_status launch_project(const uint16_t *X, const float *U, const u32x4 *qfrag, int nqb,
-                          int nterm, const Slices &sl, int64_t G, float *Xt, float *err,
+                          int nterm, const Slices &sl, int64_t G, OutT *Xt, float *err,
                           hipStream_t stream) {
     return nqb > 0 ? launch_project_variant<NRB, false>(X, U, qfrag, nqb, nterm, sl, G, Xt, err, stream)
                    : launch_project_variant<NRB, true>(X, U, qfrag, nqb, nterm, sl, G, Xt, err, stream);
 }
 
+template <typename OutT>
 kvc_status project_dispatch(int64_t R, const uint16_t *X, const float *U, const u32x4 *qfrag,
-                            int nqb, int nterm, const Slices &sl, int64_t G, float *Xt, float *err,
+                            int nqb, int nterm, const Slices &sl, int64_t G, OutT *Xt, float *err,
                             hipStream_t stream) {
     switch (R) {
         case 32: return launch_project<1>(X, U, qfrag, nqb, nterm, sl, G, Xt, err, stream);
@@ -580,6 +697,16 @@ kvc_status launch_reconstruct(const float *Xt, const float *U, const Slices &sl,
     return launch_status();
 }
 
+template <int NRB>
+kvc_status launch_reconstruct_bf16(const uint16_t *Xt, const float *U, const Slices &sl, int64_t G,
+                                   uint16_t *Xh, hipStream_t stream) {
+    const int64_t blocks = G * sl.nsplit;
+    if (blocks > INT32_MAX) return KVC_ERR_UNSUPPORTED;
+    hipLaunchKernelGGL(reconstruct_bf16_kernel<NRB>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
+                       stream, Xt, U, sl, Xh);
+    return launch_status();
+}
+
 }  // namespace
 
 size_t compress_workspace_bytes(const kvc_dims *d) {
@@ -595,12 +722,13 @@ size_t reconstruct_workspace_bytes(const kvc_dims *) { return 0; }
 
 }  // namespace kvc
 
-extern "C" kvc_status kvc_lowrank_compress(const kvc_dims *d, const uint16_t *K, const uint16_t *V,
-                                           const uint16_t *Q_win, const float *U_k,
-                                           const float *U_v, float *K_tilde, float *V_tilde,
-                                           float *err, void *ws, size_t ws_bytes,
-                                           hipStream_t stream) {
-    using namespace kvc;
+namespace kvc {
+namespace {
+
+template <typename OutT>
+kvc_status compress_impl(const kvc_dims *d, const uint16_t *K, const uint16_t *V,
+                         const uint16_t *Q_win, const float *U_k, const float *U_v, OutT *K_tilde,
+                         OutT *V_tilde, float *err, void *ws, size_t ws_bytes, hipStream_t stream) {
     const bool with_q = Q_win != nullptr;
     kvc_status st = check_dims(d, with_q);
     if (st != KVC_OK) return st;
@@ -645,6 +773,25 @@ extern "C" kvc_status kvc_lowrank_compress(const kvc_dims *d, const uint16_t *K,
     return st;
 }
 
+}  // namespace
+}  // namespace kvc
+
+extern "C" kvc_status kvc_lowrank_compress(const kvc_dims *d, const uint16_t *K, const uint16_t *V,
+                                           const uint16_t *Q_win, const float *U_k,
+                                           const float *U_v, float *K_tilde, float *V_tilde,
+                                           float *err, void *ws, size_t ws_bytes,
+                                           hipStream_t stream) {
+    return kvc::compress_impl(d, K, V, Q_win, U_k, U_v, K_tilde, V_tilde, err, ws, ws_bytes, stream);
+}
+
+extern "C" kvc_status kvc_lowrank_compress_bf16(const kvc_dims *d, const uint16_t *K, const uint16_t *V,
+                                                const uint16_t *Q_win, const float *U_k,
+                                                const float *U_v, uint16_t *K_tilde,
+                                                uint16_t *V_tilde, float *err, void *ws,
+                                                size_t ws_bytes, hipStream_t stream) {
+    return kvc::compress_impl(d, K, V, Q_win, U_k, U_v, K_tilde, V_tilde, err, ws, ws_bytes, stream);
+}
+
 extern "C" kvc_status kvc_reconstruct(const kvc_dims *d, const float *X_tilde, const float *U,
                                       const int32_t *anchor_idx, const uint16_t *anchor_rows,
                                       int64_t k, float *X_hat, void *ws, size_t ws_bytes,
@@ -674,6 +821,39 @@ extern "C" kvc_status kvc_reconstruct(const kvc_dims *d, const float *X_tilde, c
     const int64_t bps = (k + 15) / 16;
     if (G * bps > INT32_MAX) return KVC_ERR_UNSUPPORTED;
     hipLaunchKernelGGL(anchor_scatter_kernel, dim3(static_cast<unsigned>(G * bps)), dim3(256), 0,
+                       stream, anchor_idx, anchor_rows, k, bps, d->S, sl.S_stride, X_hat);
+    return launch_status();
+}
+
+extern "C" kvc_status kvc_reconstruct_bf16(const kvc_dims *d, const uint16_t *X_tilde, const float *U,
+                                           const int32_t *anchor_idx, const uint16_t *anchor_rows,
+                                           int64_t k, uint16_t *X_hat, void *ws, size_t ws_bytes,
+                                           hipStream_t stream) {
+    using namespace kvc;
+    (void)ws;
+    (void)ws_bytes;
+    kvc_status st = check_dims(d, false);
+    if (st != KVC_OK) return st;
+    if (k < 0 || k > d->S) return KVC_ERR_INVALID_ARGUMENT;
+    if ((k > 0) && (!anchor_idx || !anchor_rows)) return KVC_ERR_INVALID_ARGUMENT;
+    const int64_t G = d->L * d->B * d->H_kv;
+    if (G == 0 || d->S == 0) return KVC_OK;
+    if (!X_tilde || !U || !X_hat || !aligned(X_tilde, 16) || !aligned(U, 16) || !aligned(X_hat, 16))
+        return KVC_ERR_INVALID_ARGUMENT;
+    if (k > 0 && (!aligned(anchor_idx, 4) || !aligned(anchor_rows, 16)))
+        return KVC_ERR_INVALID_ARGUMENT;
+    const Slices sl = make_slices(d, 128);
+    switch (d->R) {
+        case 32: st = launch_reconstruct_bf16<1>(X_tilde, U, sl, G, X_hat, stream); break;
+        case 64: st = launch_reconstruct_bf16<2>(X_tilde, U, sl, G, X_hat, stream); break;
+        case 96: st = launch_reconstruct_bf16<3>(X_tilde, U, sl, G, X_hat, stream); break;
+        case 128: st = launch_reconstruct_bf16<4>(X_tilde, U, sl, G, X_hat, stream); break;
+        default: return KVC_ERR_UNSUPPORTED;
+    }
+    if (st != KVC_OK || k == 0) return st;
+    const int64_t bps = (k + 15) / 16;
+    if (G * bps > INT32_MAX) return KVC_ERR_UNSUPPORTED;
+    hipLaunchKernelGGL(anchor_copy_bf16_kernel, dim3(static_cast<unsigned>(G * bps)), dim3(256), 0,
                        stream, anchor_idx, anchor_rows, k, bps, d->S, sl.S_stride, X_hat);
     return launch_status();
 }

@@ -23,7 +23,7 @@ METRICS = {"l2": METRIC_L2, "cosine": METRIC_COSINE}
 
 EXPORTED = ("kvc_abi_version", "kvc_status_str", "kvc_workspace_bytes", "kvc_score_l2",
             "kvc_score_l2_windowed", "kvc_score_centroid", "kvc_topk_compact", "kvc_lowrank_compress",
-            "kvc_oja_update", "kvc_reconstruct")
+            "kvc_lowrank_compress_bf16", "kvc_oja_update", "kvc_reconstruct", "kvc_reconstruct_bf16")
 
 
 class KvcError(RuntimeError):
@@ -60,8 +60,10 @@ def load(path: str = LIB_PATH):
                 "kvc_score_centroid": [P, I64, I64, I32, I64, I32, P, P, P, SZ, P],
                 "kvc_topk_compact": [P, I64, I64, I64, I64, P, P, I32, P, P, P, P, SZ, P],
                 "kvc_lowrank_compress": [DP, P, P, P, P, P, P, P, P, P, SZ, P],
+                "kvc_lowrank_compress_bf16": [DP, P, P, P, P, P, P, P, P, P, SZ, P],
                 "kvc_oja_update": [DP, P, P, I32, ctypes.c_float, P, SZ, P],
                 "kvc_reconstruct": [DP, P, P, P, P, I64, P, P, SZ, P],
+                "kvc_reconstruct_bf16": [DP, P, P, P, P, I64, P, P, SZ, P],
             }
             for name, a in sigs.items():
                 fn = getattr(lib, name)
@@ -181,10 +183,7 @@ def kvc_topk_compact(scores, k, K=None, V=None, S=None, idx_out=None, K_out=None
     return idx_out, K_out, V_out
 
 
-def kvc_lowrank_compress(K, V, Q_win, U_k, U_v, L, B, H_kv, S=None, K_tilde=None, V_tilde=None,
-                         err=None):
-    """K, V: bf16 [L*B*H_kv, S_stride, D]; Q_win: bf16 [L, B, H_q, W_q, D] or None;
-    U_k, U_v: fp32 [L, H_kv, D, R].  Returns (K_tilde, V_tilde, err)."""
+def _compress(name, dtype, K, V, Q_win, U_k, U_v, L, B, H_kv, S, K_tilde, V_tilde, err):
     lib = load()
     G, stride, D = K.shape
     S = stride if S is None else S
@@ -192,19 +191,33 @@ def kvc_lowrank_compress(K, V, Q_win, U_k, U_v, L, B, H_kv, S=None, K_tilde=None
     H_q, W_q = (Q_win.shape[2], Q_win.shape[3]) if Q_win is not None else (0, 0)
     dev = K.device
     if K_tilde is None:
-        K_tilde = torch.empty((G, stride, R), dtype=torch.float32, device=dev)
+        K_tilde = torch.empty((G, stride, R), dtype=dtype, device=dev)
     if V is not None and V_tilde is None:
-        V_tilde = torch.empty((G, stride, R), dtype=torch.float32, device=dev)
+        V_tilde = torch.empty((G, stride, R), dtype=dtype, device=dev)
     if Q_win is not None and err is None:
         err = torch.empty((G, stride), dtype=torch.float32, device=dev)
     d = _dims(L, B, H_kv, H_q, S, stride, D, R, W_q)
     nb = workspace_bytes(OP_LOWRANK_COMPRESS, d)
     ws = workspace(nb, dev.index)
-    _check("kvc_lowrank_compress",
-           lib.kvc_lowrank_compress(ctypes.byref(d), _ptr(K), _ptr(V), _ptr(Q_win), _ptr(U_k),
+    _check(name, getattr(lib, name)(ctypes.byref(d), _ptr(K), _ptr(V), _ptr(Q_win), _ptr(U_k),
                                     _ptr(U_v), _ptr(K_tilde), _ptr(V_tilde), _ptr(err), _ptr(ws),
                                     nb, _stream()))
     return K_tilde, V_tilde, err
+
+
+def kvc_lowrank_compress(K, V, Q_win, U_k, U_v, L, B, H_kv, S=None, K_tilde=None, V_tilde=None,
+                         err=None):
+    """K, V: bf16 [L*B*H_kv, S_stride, D]; Q_win: bf16 [L, B, H_q, W_q, D] or None;
+    U_k, U_v: fp32 [L, H_kv, D, R].  Returns (K_tilde, V_tilde, err), K~/V~ fp32."""
+    return _compress("kvc_lowrank_compress", torch.float32, K, V, Q_win, U_k, U_v, L, B, H_kv, S,
+                     K_tilde, V_tilde, err)
+
+
+def kvc_lowrank_compress_bf16(K, V, Q_win, U_k, U_v, L, B, H_kv, S=None, K_tilde=None, V_tilde=None,
+                              err=None):
+    """As kvc_lowrank_compress, with K~/V~ stored as bf16 [L*B*H_kv, S_stride, R]."""
+    return _compress("kvc_lowrank_compress_bf16", torch.bfloat16, K, V, Q_win, U_k, U_v, L, B, H_kv, S,
+                     K_tilde, V_tilde, err)
 
 
 def kvc_oja_update(U, X, pool, eta, L, B, H_kv, N=None):
@@ -221,20 +234,30 @@ def kvc_oja_update(U, X, pool, eta, L, B, H_kv, N=None):
     return U
 
 
-def kvc_reconstruct(X_tilde, U, anchor_idx, anchor_rows, L, B, H_kv, S=None, X_hat=None):
-    """X_tilde: fp32 [L*B*H_kv, S_stride, R]; U: fp32 [L, H_kv, D, R];
-    anchor_idx int32 [G, k] / anchor_rows bf16 [G, k, D] or None -> X_hat fp32 [G, S_stride, D]."""
+def _reconstruct(name, dtype, X_tilde, U, anchor_idx, anchor_rows, L, B, H_kv, S, X_hat):
     lib = load()
     G, stride, R = X_tilde.shape
     S = stride if S is None else S
     D = U.shape[-2]
     k = 0 if anchor_idx is None else anchor_idx.shape[1]
     if X_hat is None:
-        X_hat = torch.empty((G, stride, D), dtype=torch.float32, device=X_tilde.device)
+        X_hat = torch.empty((G, stride, D), dtype=dtype, device=X_tilde.device)
     d = _dims(L, B, H_kv, 0, S, stride, D, R, 0)
     nb = workspace_bytes(OP_RECONSTRUCT, d, k)
     ws = workspace(nb, X_tilde.device.index)
-    _check("kvc_reconstruct",
-           lib.kvc_reconstruct(ctypes.byref(d), _ptr(X_tilde), _ptr(U), _ptr(anchor_idx),
-                               _ptr(anchor_rows), k, _ptr(X_hat), _ptr(ws), nb, _stream()))
+    _check(name, getattr(lib, name)(ctypes.byref(d), _ptr(X_tilde), _ptr(U), _ptr(anchor_idx),
+                                    _ptr(anchor_rows), k, _ptr(X_hat), _ptr(ws), nb, _stream()))
     return X_hat
+
+
+def kvc_reconstruct(X_tilde, U, anchor_idx, anchor_rows, L, B, H_kv, S=None, X_hat=None):
+    """X_tilde: fp32 [L*B*H_kv, S_stride, R]; U: fp32 [L, H_kv, D, R];
+    anchor_idx int32 [G, k] / anchor_rows bf16 [G, k, D] or None -> X_hat fp32 [G, S_stride, D]."""
+    return _reconstruct("kvc_reconstruct", torch.float32, X_tilde, U, anchor_idx, anchor_rows, L, B,
+                        H_kv, S, X_hat)
+
+
+def kvc_reconstruct_bf16(X_tilde, U, anchor_idx, anchor_rows, L, B, H_kv, S=None, X_hat=None):
+    """As kvc_reconstruct with X_tilde bf16 [G, S_stride, R] -> X_hat bf16 [G, S_stride, D]."""
+    return _reconstruct("kvc_reconstruct_bf16", torch.bfloat16, X_tilde, U, anchor_idx, anchor_rows, L,
+                        B, H_kv, S, X_hat)

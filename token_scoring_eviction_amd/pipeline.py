@@ -73,17 +73,19 @@ class HybridState:
     Vhat: torch.Tensor
 
 
-def alloc_hybrid(G, S_cap, R, D=128, device="cuda", max_anchor=None, with_hat=True):
+def alloc_hybrid(G, S_cap, R, D=128, device="cuda", max_anchor=None, with_hat=True, storage="fp32"):
+    """storage "fp32": K~, V~, K^, V^ in fp32; "bf16": all four in bf16 (the
+    memory-saving layout).  Error scores are fp32 either way."""
     max_anchor = anchor_count(S_cap) if max_anchor is None else max_anchor
-    f32 = dict(dtype=torch.float32, device=device)
+    st = dict(dtype=torch.bfloat16 if storage == "bf16" else torch.float32, device=device)
     return HybridState(
-        Kt=torch.empty((G, S_cap, R), **f32), Vt=torch.empty((G, S_cap, R), **f32),
-        err=torch.empty((G, S_cap), **f32),
+        Kt=torch.empty((G, S_cap, R), **st), Vt=torch.empty((G, S_cap, R), **st),
+        err=torch.empty((G, S_cap), dtype=torch.float32, device=device),
         idx=torch.empty((G, max_anchor), dtype=torch.int32, device=device),
         K_anchor=torch.empty((G, max_anchor, D), dtype=torch.bfloat16, device=device),
         V_anchor=torch.empty((G, max_anchor, D), dtype=torch.bfloat16, device=device),
-        Khat=torch.empty((G, S_cap, D), **f32) if with_hat else None,
-        Vhat=torch.empty((G, S_cap, D), **f32) if with_hat else None)
+        Khat=torch.empty((G, S_cap, D), **st) if with_hat else None,
+        Vhat=torch.empty((G, S_cap, D), **st) if with_hat else None)
 
 
 def hybrid_pass(K, V, Q_win, U_k, U_v, L, B, H_kv, S, st: HybridState, anchor_percent=5,
@@ -94,16 +96,18 @@ def hybrid_pass(K, V, Q_win, U_k, U_v, L, B, H_kv, S, st: HybridState, anchor_pe
     k = anchor_count(S, anchor_percent)
     if k > st.idx.shape[1]:
         raise ValueError("anchor buffers hold %d rows, %d needed" % (st.idx.shape[1], k))
-    kvc.kvc_lowrank_compress(K, V, Q_win, U_k, U_v, L, B, H_kv, S=S, K_tilde=st.Kt, V_tilde=st.Vt,
-                             err=st.err)
+    bf16 = st.Kt.dtype == torch.bfloat16
+    compress = kvc.kvc_lowrank_compress_bf16 if bf16 else kvc.kvc_lowrank_compress
+    rebuild = kvc.kvc_reconstruct_bf16 if bf16 else kvc.kvc_reconstruct
+    compress(K, V, Q_win, U_k, U_v, L, B, H_kv, S=S, K_tilde=st.Kt, V_tilde=st.Vt, err=st.err)
     # anchors of this pass: the first k rows of the (contiguous) anchor buffers
     idx = st.idx.view(-1)[:G * k].view(G, k)
     Ka = st.K_anchor.view(-1)[:G * k * K.shape[2]].view(G, k, K.shape[2])
     Va = st.V_anchor.view(-1)[:G * k * K.shape[2]].view(G, k, K.shape[2])
     kvc.kvc_topk_compact(st.err, k, K, V, S=S, idx_out=idx, K_out=Ka, V_out=Va)
     if reconstruct:
-        kvc.kvc_reconstruct(st.Kt, U_k, idx, Ka, L, B, H_kv, S=S, X_hat=st.Khat)
-        kvc.kvc_reconstruct(st.Vt, U_v, idx, Va, L, B, H_kv, S=S, X_hat=st.Vhat)
+        rebuild(st.Kt, U_k, idx, Ka, L, B, H_kv, S=S, X_hat=st.Khat)
+        rebuild(st.Vt, U_v, idx, Va, L, B, H_kv, S=S, X_hat=st.Vhat)
     return idx, Ka, Va
 
 
@@ -121,7 +125,7 @@ class OjaLoopState:
 
 
 def ojakv_prefill(K, V, Q_prompt, U_k, U_v, L, B, H_kv, S0, T=32, pool=32, eta=1e-3,
-                  anchor_percent=5, S_cap=None, reconstruct=True):
+                  anchor_percent=5, S_cap=None, reconstruct=True, storage="fp32"):
     """Prefill phase (appendix A.1): pooled Oja update of U_k (on K) and U_v (on V)
     with QR, then projection, error score with the prompt's query window,
     top-k anchors and (optionally) reconstruction.  U_k, U_v are updated in place.
@@ -132,7 +136,7 @@ def ojakv_prefill(K, V, Q_prompt, U_k, U_v, L, B, H_kv, S0, T=32, pool=32, eta=1
     kvc.kvc_oja_update(U_v, V, pool, eta, L, B, H_kv, N=S0)
     R = U_k.shape[-1]
     st = alloc_hybrid(G, S_cap, R, D, K.device, max_anchor=anchor_count(S_cap, anchor_percent),
-                      with_hat=reconstruct)
+                      with_hat=reconstruct, storage=storage)
     hybrid_pass(K, V, Q_prompt, U_k, U_v, L, B, H_kv, S0, st, anchor_percent, reconstruct)
     H_q = Q_prompt.shape[2]
     return OjaLoopState(
