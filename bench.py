@@ -61,6 +61,9 @@ def parse():
     ap.add_argument("--metric", choices=["l2", "cosine"], default="l2",
                     help="centroid score of configs 0-2: ManifoldKV's L2 distance (the workload) "
                          "or the cosine-dissimilarity baseline")
+    ap.add_argument("--budgets", choices=["uniform", "ripple"], default="uniform",
+                    help="configs 0-2: every slice keeps the same k (the workload) or per-layer "
+                         "RippleKV budgets (seeded sensitivity profile, r=8, gamma=4) with the same total")
     ap.add_argument("--storage", choices=["fp32", "bf16"], default="fp32",
                     help="OjaKV configs 3-4: compressed cache (K~, V~, K^, V^) in fp32 (the "
                          "workload) or bf16 (the memory-saving layout)")
@@ -99,7 +102,9 @@ class Op:
         self.ms = []
 
 
-def manifold_workload(cfg, dev, metric="l2"):
+def manifold_workload(cfg, dev, metric="l2", budgets="uniform"):
+    import torch
+
     import synth
     from token_scoring_eviction_amd import kvc, pipeline
     if cfg == 0:
@@ -126,17 +131,32 @@ def manifold_workload(cfg, dev, metric="l2"):
         score, score_name = (lambda: kvc.kvc_score_l2(K, scores=buf.scores)), "kvc_score_l2"
     else:
         score, score_name = (lambda: kvc.kvc_score_l2_windowed(K, W, scores=buf.scores)), "kvc_score_l2_windowed"
-    ops = [
-        Op(score_name, score, G * S * (256 + 4), kernel="l2_fused"),
-        Op("kvc_topk_compact",
-           lambda: kvc.kvc_topk_compact(buf.scores, keep, K, V, idx_out=buf.idx, K_out=buf.K_out,
-                                        V_out=buf.V_out),
-           G * S * 4 + G * keep * (2 * 256 * 2 + 4),
-           kernel="select_compact" if keep <= 8192 and G >= 256 else "select_compact+gather_rows"),
-    ]
+    ops = [Op(score_name, score, G * S * (256 + 4), kernel="l2_fused")]
+    if budgets == "ripple":
+        # per-layer budgets from a seeded sensitivity profile, same total as keep per slice
+        import numpy as np
+        sens = np.random.default_rng(20261202 + cfg).gamma(2.0, 1.0, L)
+        kl = kvc.kvc_layer_budgets(sens, 8.0, 4.0, L * keep, S)
+        ks = np.repeat(kl, H)
+        total = int(ks.sum())
+        rbuf = (torch.empty(total, dtype=torch.int32, device=dev),
+                torch.empty((total, 128), dtype=torch.bfloat16, device=dev),
+                torch.empty((total, 128), dtype=torch.bfloat16, device=dev))
+        ops.append(Op("kvc_topk_compact_ragged",
+                      lambda: kvc.kvc_topk_compact_ragged(buf.scores, ks, K, V, idx_out=rbuf[0],
+                                                          K_out=rbuf[1], V_out=rbuf[2]),
+                      G * S * 4 + total * (2 * 256 * 2 + 4),
+                      kernel="select_compact" if ks.max() <= 8192 and G >= 256 else "select_compact+gather_rows"))
+        desc += "; RippleKV per-layer budgets %d..%d (r=8, gamma=4)" % (kl.min(), kl.max())
+    else:
+        ops.append(Op("kvc_topk_compact",
+                      lambda: kvc.kvc_topk_compact(buf.scores, keep, K, V, idx_out=buf.idx, K_out=buf.K_out,
+                                                   V_out=buf.V_out),
+                      G * S * 4 + G * keep * (2 * 256 * 2 + 4),
+                      kernel="select_compact" if keep <= 8192 and G >= 256 else "select_compact+gather_rows"))
     algo = G * S * 256 + G * keep * 256 + 2 * G * keep * 256 + G * S * 4 + G * keep * 4
     config = {"workload": desc, "slices": G, "seq_len": S, "keep": keep, "head_dim": 128,
-              "window": W, "metric": metric}
+              "window": W, "metric": metric, "budgets": budgets}
 
     def cpu(budget):
         import numpy as np
@@ -305,7 +325,7 @@ def main():
     if args.config == 3:
         ops, head_tokens, algo, config, cpu = oja_workload(dev, args.storage)
     else:
-        ops, head_tokens, algo, config, cpu = manifold_workload(args.config, dev, args.metric)
+        ops, head_tokens, algo, config, cpu = manifold_workload(args.config, dev, args.metric, args.budgets)
     torch.cuda.synchronize()
 
     for _ in range(args.warmup):

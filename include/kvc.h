@@ -8,6 +8,8 @@
  *   [OJA] "OjaKV: Context-Aware Online Low-Rank KV Cache Compression"
  *         (papercache deep-notes page): "how it works" equations, background
  *         on low-rank attention, method details, appendix A.1 (Algorithm 1).
+ *   [RKV] "RippleKV: Cross-Layer KV Cache Allocation via Perturbation
+ *         Propagation" (explainer page), sensitivity-guided budget allocation.
  *
  * Common conventions
  *   - Every tensor pointer is a DEVICE pointer to dense row-major memory.
@@ -62,7 +64,8 @@ typedef enum kvc_op {
     KVC_OP_LOWRANK_COMPRESS = 3,
     KVC_OP_OJA_UPDATE = 4,
     KVC_OP_RECONSTRUCT = 5,
-    KVC_OP_SCORE_CENTROID = 6
+    KVC_OP_SCORE_CENTROID = 6,
+    KVC_OP_TOPK_RAGGED = 7
 } kvc_op;
 
 /* Score of a key against its (global or window) centroid mu, for
@@ -93,6 +96,7 @@ const char *kvc_status_str(kvc_status s);
  *   SCORE_L2, SCORE_L2_WINDOWED, SCORE_CENTROID: G = L*B*H_kv slices of S
  *     tokens; W = window (ignored for SCORE_L2).
  *   TOPK_COMPACT: G = L*B*H_kv slices of S tokens; k = tokens kept.
+ *   TOPK_RAGGED: G = L*B*H_kv slices (16 bytes per slice).
  *   LOWRANK_COMPRESS, OJA_UPDATE, RECONSTRUCT: shapes from `d`; for OJA_UPDATE
  *     d->S is the token count N and W is the pooling window.  The bf16-storage
  *     variants need what LOWRANK_COMPRESS and RECONSTRUCT need.
@@ -143,6 +147,32 @@ kvc_status kvc_topk_compact(const float *scores, int64_t G, int64_t S, int64_t s
                             const uint16_t *K, const uint16_t *V, int32_t D, int32_t *idx_out,
                             uint16_t *K_out, uint16_t *V_out, void *ws, size_t ws_bytes,
                             hipStream_t stream);
+
+/* RippleKV budget allocation ([RKV] "RippleKV: Cross-Layer KV Cache Allocation
+ * via Perturbation Propagation", sensitivity-guided budget allocation).  HOST
+ * function, host pointers.  For layers l = 0..L-1 with sensitivities s_l:
+ *   s^_l = (s_l - min s) / (max s - min s)    (0 for all when they are equal),
+ *   w_l  = r^{s^_l} clipped to [1/gamma, gamma],
+ *   k_l  proportional to w_l with sum_l k_l = B.
+ * A share above S is pinned at S and the remaining budget shared again by the
+ * other layers; whole tokens are the floors plus one for the largest fractional
+ * parts (equal parts: the lower layer first).  Requires r > 0, gamma >= 1,
+ * 0 <= B <= L * S.  k_out: int64 [L]. */
+kvc_status kvc_layer_budgets(const double *sensitivity, int64_t L, double r, double gamma,
+                             int64_t B, int64_t S, int64_t *k_out);
+
+/* Retention and compaction with a budget per slice (e.g. RippleKV's layer
+ * budgets, every slice of layer l keeping k_l): as kvc_topk_compact with slice
+ * g keeping k[g] tokens, 0 <= k[g] <= S.  k is a HOST array [G], read before the
+ * call returns.  Outputs are packed in slice order: slice g's indices are
+ * idx_out[o_g .. o_g + k[g]) with o_g = k[0] + ... + k[g-1], and its rows
+ * K_out[o_g + i][:] (likewise V_out); idx_out int32 [sum k], K_out, V_out bf16
+ * [sum k][D].  The workspace holds the budgets and offsets on the device
+ * (kvc_workspace_bytes(KVC_OP_TOPK_RAGGED, ...)). */
+kvc_status kvc_topk_compact_ragged(const float *scores, int64_t G, int64_t S, int64_t s_stride,
+                                   const int64_t *k, const uint16_t *K, const uint16_t *V,
+                                   int32_t D, int32_t *idx_out, uint16_t *K_out, uint16_t *V_out,
+                                   void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* Hybrid low-rank compression ([OJA] background: K~ = K U_k, V~ = V U_v;
  * method details: residual r_t = k_t - U_k U_k^T k_t and query-weighted error

@@ -72,6 +72,7 @@ def _load():
                 "ora_oja_step": [P, I, I, I, P, D, P],
                 "ora_qr": [P, I, I, P],
                 "ora_oja_update": [I, I, I, I, I, I, I, P, P, I, D, P],
+                "ora_layer_budgets": [P, I, D, D, I, I, P],
             }
             for name, argtypes in sig.items():
                 fn = getattr(lib, name)
@@ -344,4 +345,23 @@ def bf16_to_f64(bits):
     """Exact widening of bf16 bit patterns (uint16) to float64."""
     b = np.ascontiguousarray(bits, dtype=np.uint16).astype(np.uint32) << 16
     return b.view(np.float32).astype(np.float64)
+
+
+def layer_budgets(sensitivity, r, gamma, B, S):
+    """RippleKV per-layer budgets: normalised sensitivities, multipliers r^s
+    clipped to [1/gamma, gamma], rescaled to sum to B (budgets above S capped and
+    re-spread; integers by largest remainder).  Returns int64 [L]."""
+    s = np.ascontiguousarray(sensitivity, dtype=np.float64)
+    k = np.zeros(s.shape[0], np.int64)
+    _check(_load().ora_layer_budgets(_p(s), s.shape[0], float(r), float(gamma), int(B), int(S), _p(k)),
+           "layer_budgets")
+    return k
+
+
+def topk_ragged(scores32, ks, S=None):
+    """Top-k per slice with a budget per slice (ks: int [G]); indices packed in
+    slice order: slice g's ks[g] ascending indices, then slice g+1's."""
+    s = _f32(scores32)
+    parts = [topk(s[g:g + 1], int(ks[g]), S)[0] for g in range(s.shape[0])]
+    return np.concatenate(parts).astype(np.int32) if parts else np.zeros(0, np.int32)
 

@@ -20,6 +20,10 @@
  * Sources (pages the method is described on):
  *   [MKV]  "ManifoldKV: Training-Free KV Cache Compression via Euclidean
  *          Outlier Detection" (ICML 2026 poster page), abstract and lay summary.
+ *   [RKV]  "RippleKV: Cross-Layer KV Cache Allocation via Perturbation
+ *          Propagation" (explainer page), "Sensitivity-Guided Budget
+ *          Allocation": normalised sensitivities, exponential multipliers,
+ *          clipping, rescaling to the global budget.
  *   [OJA]  "OjaKV: Context-Aware Online Low-Rank KV Cache Compression"
  *          (papercache deep-notes page): the "how it works" display equations
  *          for e_t and the Oja rule, "background / low-rank attention",
@@ -489,3 +493,93 @@ int ora_oja_update(int64_t L, int64_t B, int64_t Hkv, int64_t N, int64_t n_strid
     free(Xp);
     return rc;
 }
+
+/* ------------------------------------------------------ RippleKV budgets */
+
+/* Per-layer token budgets from per-layer sensitivities ([RKV] sensitivity-
+ * guided budget allocation):
+ *   s^_l = (s_l - min s) / (max s - min s)   (all 0 when the scores are equal)
+ *   w_l  = r^{s^_l}, clipped to [1/gamma, gamma]
+ *   b_l  = B * w_l / sum_m w_m               (real budgets summing to B)
+ * Readings where the page is silent: a budget above S (a layer cannot keep more
+ * tokens than it has) is set to S and the remaining budget is spread again over
+ * the other layers in proportion to w, until none exceeds S; integer budgets
+ * are the floors plus one for the layers with the largest fractional parts
+ * (ties: the lower layer index) until they sum to B.
+ * Requires r > 0, gamma >= 1, 0 <= B <= L * S. */
+int ora_layer_budgets(const double *s, int64_t L, double r, double gamma, int64_t B, int64_t S,
+                      int64_t *k) {
+    if (L <= 0 || !s || !k || !(r > 0.0) || !(gamma >= 1.0) || S < 0 || B < 0 || B > L * S)
+        return ORA_EINVAL;
+    for (int64_t l = 0; l < L; ++l)
+        if (!isfinite(s[l])) return ORA_ENONFINITE;
+    double *w = (double *)malloc(sizeof(double) * (size_t)L * 2);
+    int *capped = (int *)calloc((size_t)L, sizeof(int));
+    if (!w || !capped) {
+        free(w);
+        free(capped);
+        return ORA_ENOMEM;
+    }
+    double *b = w + L;
+    double lo = s[0], hi = s[0];
+    for (int64_t l = 1; l < L; ++l) {
+        if (s[l] < lo) lo = s[l];
+        if (s[l] > hi) hi = s[l];
+    }
+    for (int64_t l = 0; l < L; ++l) {
+        double sn = hi > lo ? (s[l] - lo) / (hi - lo) : 0.0;
+        double m = pow(r, sn);
+        if (m < 1.0 / gamma) m = 1.0 / gamma;
+        if (m > gamma) m = gamma;
+        w[l] = m;
+    }
+    /* spread the budget; layers whose share exceeds S are capped and the rest re-spread */
+    double left = (double)B;
+    for (;;) {
+        double wsum = 0.0;
+        for (int64_t l = 0; l < L; ++l)
+            if (!capped[l]) wsum += w[l];
+        int changed = 0;
+        for (int64_t l = 0; l < L; ++l) {
+            if (capped[l]) continue;
+            b[l] = wsum > 0.0 ? left * w[l] / wsum : 0.0;
+            if (b[l] > (double)S) {
+                capped[l] = 1;
+                changed = 1;
+            }
+        }
+        if (!changed) break;
+        left = (double)B;
+        for (int64_t l = 0; l < L; ++l)
+            if (capped[l]) {
+                b[l] = (double)S;
+                left -= (double)S;
+            }
+    }
+    /* integers: floors, then +1 by largest fractional part (ties: lower layer) */
+    int64_t assigned = 0;
+    for (int64_t l = 0; l < L; ++l) {
+        k[l] = (int64_t)floor(b[l]);
+        if (k[l] > S) k[l] = S;
+        assigned += k[l];
+    }
+    while (assigned < B) {
+        int64_t best = -1;
+        double best_frac = -1.0;
+        for (int64_t l = 0; l < L; ++l) {
+            if (k[l] >= S) continue;
+            double frac = b[l] - (double)k[l];
+            if (frac > best_frac) {
+                best_frac = frac;
+                best = l;
+            }
+        }
+        if (best < 0) break; /* cannot happen when B <= L * S */
+        k[best] += 1;
+        assigned += 1;
+    }
+    free(w);
+    free(capped);
+    return ORA_OK;
+}
+

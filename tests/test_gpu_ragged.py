@@ -1,0 +1,103 @@
+"""GPU parity of retention with a budget per slice (kvc_topk_compact_ragged) driven
+by RippleKV's layer budgets ("RippleKV: Cross-Layer KV Cache Allocation via
+Perturbation Propagation", sensitivity-guided budget allocation: every slice of
+layer l keeps k_l tokens, the token selector itself unchanged).  Index sets are
+bit-exact on identical scores; rows bit-exact; end to end with ManifoldKV scores
+the retained sets agree with the oracle's up to the threshold band."""
+from concurrent.futures import ThreadPoolExecutor
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests.helpers import index_sets_agree
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _check_packed(idx, Ko, Vo, ks, s_host, Kb, Vb, S=None):
+    ref = oracle.topk_ragged(s_host, ks, S)
+    np.testing.assert_array_equal(idx.cpu().numpy(), ref)
+    if Ko is not None:
+        off = np.concatenate([[0], np.cumsum(ks)])
+        ko, vo = synth.bf16_bits(Ko), synth.bf16_bits(Vo)
+        for g in range(len(ks)):
+            sel = ref[off[g]:off[g + 1]].astype(np.int64)
+            np.testing.assert_array_equal(ko[off[g]:off[g + 1]], Kb[g][sel])
+            np.testing.assert_array_equal(vo[off[g]:off[g + 1]], Vb[g][sel])
+
+
+@pytest.mark.parametrize("separate", [False, True])
+def test_ragged_layer_budgets_bit_exact(gpu_lib, monkeypatch, separate):
+    # 30 layers x 10 slices, S = 5000 with a ragged stride; budgets from a sensitivity
+    # profile (some layers pinned at S, none empty) and ties in the scores
+    if separate:
+        monkeypatch.setenv("KVC_GATHER_SEPARATE", "1")
+    L, per, S, stride = 30, 10, 5000, 5003
+    G = L * per
+    rng = np.random.default_rng(21)
+    kl = gpu_lib.kvc_layer_budgets(rng.exponential(1.0, L), 16.0, 4.0, L * S // 3, S)
+    ks = np.repeat(kl, per)
+    s = synth.random_scores(G, stride, seed=22, kind="ties", device="cpu")
+    K = torch.randint(-32768, 32767, (G, stride, 128), dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    V = torch.randint(-32768, 32767, (G, stride, 128), dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    idx, Ko, Vo = gpu_lib.kvc_topk_compact_ragged(s.to(DEV), ks, K, V, S=S)
+    torch.cuda.synchronize()
+    _check_packed(idx, Ko, Vo, ks, s.numpy(), synth.bf16_bits(K), synth.bf16_bits(V), S)
+
+
+def test_ragged_zero_full_and_large_budgets(gpu_lib):
+    # budgets 0, 1, S and above the in-workgroup copy limit (8192), mixed
+    G, S = 6, 20000
+    ks = np.array([0, 1, S, 9000, 0, 12345])
+    s = synth.random_scores(G, S, seed=23, device="cpu")
+    K = torch.randint(-32768, 32767, (G, S, 128), dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    V = torch.randint(-32768, 32767, (G, S, 128), dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    idx, Ko, Vo = gpu_lib.kvc_topk_compact_ragged(s.to(DEV), ks, K, V)
+    torch.cuda.synchronize()
+    _check_packed(idx, Ko, Vo, ks, s.numpy(), synth.bf16_bits(K), synth.bf16_bits(V))
+    idx2, _, _ = gpu_lib.kvc_topk_compact_ragged(s.to(DEV), ks)  # indices only
+    torch.cuda.synchronize()
+    assert torch.equal(idx, idx2)
+
+
+def test_ragged_with_uniform_budgets_equals_topk(gpu_lib):
+    G, S, k = 40, 3000, 777
+    s = synth.random_scores(G, S, seed=24, device="cpu").to(DEV)
+    a, _, _ = gpu_lib.kvc_topk_compact(s, k)
+    b, _, _ = gpu_lib.kvc_topk_compact_ragged(s, [k] * G)
+    torch.cuda.synchronize()
+    assert torch.equal(a.view(-1), b)
+
+
+def test_ripplekv_eviction_llama_shape(gpu_lib):
+    # ManifoldKV scores on the 32-layer x 8-kv-head cache (S = 16384); per-layer budgets
+    # from a seeded sensitivity profile, total 50% of the cache; every slice checked
+    L, H, S = 32, 8, 16384
+    K, V, _ = synth.manifold_global(L, 1, H, S, planted=64, device=DEV)
+    sens = np.random.default_rng(25).gamma(2.0, 1.0, L)
+    kl = gpu_lib.kvc_layer_budgets(sens, 8.0, 4.0, L * S // 2, S)
+    assert kl.sum() == L * S // 2
+    ks = np.repeat(kl, H)
+    sc = gpu_lib.kvc_score_l2(K)
+    idx, Ko, Vo = gpu_lib.kvc_topk_compact_ragged(sc, ks, K, V)
+    torch.cuda.synchronize()
+    kb, vb = synth.bf16_bits(K), synth.bf16_bits(V)
+    idx_h, ko, vo = idx.cpu().numpy(), synth.bf16_bits(Ko), synth.bf16_bits(Vo)
+    off = np.concatenate([[0], np.cumsum(ks)])
+
+    def check(g):
+        ora, _ = oracle.score_l2(kb[g:g + 1])
+        o32 = ora.astype(np.float32)
+        gi = idx_h[off[g]:off[g + 1]][None]
+        ok, _ = index_sets_agree(gi, oracle.topk(o32, int(ks[g])), o32, int(ks[g]))
+        assert ok, "slice %d" % g
+        sel = gi[0].astype(np.int64)
+        np.testing.assert_array_equal(ko[off[g]:off[g + 1]], kb[g][sel])
+        np.testing.assert_array_equal(vo[off[g]:off[g + 1]], vb[g][sel])
+
+    with ThreadPoolExecutor(max_workers=8) as ex:
+        list(ex.map(check, range(L * H)))

@@ -4,6 +4,7 @@
 namespace kvc {
 size_t score_workspace_bytes(int64_t G, int64_t S, int64_t W);
 size_t topk_workspace_bytes(int64_t G, int64_t S, int64_t k);
+size_t topk_ragged_workspace_bytes(int64_t G);
 size_t compress_workspace_bytes(const kvc_dims *d);
 size_t oja_workspace_bytes(const kvc_dims *d, int64_t pool);
 size_t reconstruct_workspace_bytes(const kvc_dims *d);
@@ -33,6 +34,7 @@ extern "C" size_t kvc_workspace_bytes(kvc_op op, const kvc_dims *d, int64_t k, i
         case KVC_OP_LOWRANK_COMPRESS: return kvc::compress_workspace_bytes(d);
         case KVC_OP_OJA_UPDATE: return kvc::oja_workspace_bytes(d, W);
         case KVC_OP_RECONSTRUCT: return kvc::reconstruct_workspace_bytes(d);
+        case KVC_OP_TOPK_RAGGED: return kvc::topk_ragged_workspace_bytes(G);
     }
     return 0;
 }

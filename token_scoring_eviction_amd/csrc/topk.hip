@@ -17,6 +17,8 @@
 // gather_rows: 16 lanes per 256-byte row, 16-byte loads and stores.
 #include <stdlib.h>
 
+#include <vector>
+
 #include "kvc_internal.h"
 
 namespace kvc {
@@ -58,17 +60,24 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *w
     return excl;
 }
 
+// kg / koff (device, nullable): per-slice budget and output offset (packed
+// outputs); otherwise every slice keeps k and its outputs start at g * k.
 __global__ __launch_bounds__(kSelThreads) void select_compact(const float *__restrict__ scores,
                                                               int64_t S, int64_t s_stride,
-                                                              int64_t k,
+                                                              int64_t k_all,
+                                                              const int64_t *__restrict__ kg,
+                                                              const int64_t *__restrict__ koff,
                                                               int32_t *__restrict__ idx_out,
                                                               const uint16_t *__restrict__ K,
                                                               const uint16_t *__restrict__ V,
                                                               uint16_t *__restrict__ K_out,
                                                               uint16_t *__restrict__ V_out) {
     const int64_t g = blockIdx.x;
+    const int64_t k = kg ? kg[g] : k_all;
+    const int64_t base = koff ? koff[g] : g * k_all;
+    if (k <= 0 || k > S) return;  // the host validated every budget; uniform per block
     const float *s = scores + g * s_stride;
-    int32_t *out = idx_out + g * k;
+    int32_t *out = idx_out + base;
 
     __shared__ uint32_t hist[kSelWaves][256];
     __shared__ uint32_t suffix[257];
@@ -201,8 +210,8 @@ __global__ __launch_bounds__(kSelThreads) void select_compact(const float *__res
     const int rsub = threadIdx.x >> 4;  // 0..63
     const uint4 *Ks = K ? reinterpret_cast<const uint4 *>(K + g * s_stride * kHeadDim) : nullptr;
     const uint4 *Vs = V ? reinterpret_cast<const uint4 *>(V + g * s_stride * kHeadDim) : nullptr;
-    uint4 *Ko = K_out ? reinterpret_cast<uint4 *>(K_out + g * k * kHeadDim) : nullptr;
-    uint4 *Vo = V_out ? reinterpret_cast<uint4 *>(V_out + g * k * kHeadDim) : nullptr;
+    uint4 *Ko = K_out ? reinterpret_cast<uint4 *>(K_out + base * kHeadDim) : nullptr;
+    uint4 *Vo = V_out ? reinterpret_cast<uint4 *>(V_out + base * kHeadDim) : nullptr;
     constexpr int kRowsPerPass = kSelThreads / 16;  // 64
     constexpr int kUnroll = 4;  // rows per thread in flight (fetch(0..3) below)
     for (int64_t i0 = 0; i0 < k; i0 += kRowsPerPass * kUnroll) {
@@ -240,22 +249,27 @@ __global__ __launch_bounds__(kSelThreads) void select_compact(const float *__res
 constexpr int kGatherThreads = 256;
 constexpr int kGatherRows = 64;  // rows per block
 
+// kg / koff as for select_compact (nullable: k_all rows per slice at g * k_all).
 __global__ __launch_bounds__(kGatherThreads) void gather_rows(
     const uint16_t *__restrict__ K, const uint16_t *__restrict__ V, int64_t S, int64_t s_stride,
-    const int32_t *__restrict__ idx, int64_t k, int64_t blocks_per_slice,
-    uint16_t *__restrict__ K_out, uint16_t *__restrict__ V_out) {
+    const int32_t *__restrict__ idx_all, int64_t k_all, const int64_t *__restrict__ kg,
+    const int64_t *__restrict__ koff, int64_t blocks_per_slice, uint16_t *__restrict__ K_out,
+    uint16_t *__restrict__ V_out) {
     const int64_t g = blockIdx.x / blocks_per_slice;
     const int64_t r0 = (blockIdx.x % blocks_per_slice) * kGatherRows;
+    const int64_t k = kg ? kg[g] : k_all;
+    const int64_t base = koff ? koff[g] : g * k_all;
+    const int32_t *idx = idx_all + base;
     const int lane16 = threadIdx.x & 15;
     const int rsub = threadIdx.x >> 4;  // 0..15
 #pragma unroll
     for (int r = 0; r < kGatherRows / 16; ++r) {
         const int64_t i = r0 + r * 16 + rsub;
         if (i < k) {
-            const int64_t t = idx[g * k + i];
+            const int64_t t = idx[i];
             if (t < 0 || t >= S) continue;  // indices come from select_compact; never read outside
             const int64_t src = (g * s_stride + t) * (kHeadDim / 8) + lane16;
-            const int64_t dst = (g * k + i) * (kHeadDim / 8) + lane16;
+            const int64_t dst = (base + i) * (kHeadDim / 8) + lane16;
             if (K) reinterpret_cast<uint4 *>(K_out)[dst] = reinterpret_cast<const uint4 *>(K)[src];
             if (V) reinterpret_cast<uint4 *>(V_out)[dst] = reinterpret_cast<const uint4 *>(V)[src];
         }
@@ -271,6 +285,11 @@ bool fused_gather() {
 }  // namespace
 
 size_t topk_workspace_bytes(int64_t, int64_t, int64_t) { return 0; }
+
+// Per-slice budgets and output offsets of kvc_topk_compact_ragged.
+size_t topk_ragged_workspace_bytes(int64_t G) {
+    return G > 0 ? align_up(static_cast<size_t>(2 * G) * sizeof(int64_t), kWsAlign) : 0;
+}
 
 }  // namespace kvc
 
@@ -296,16 +315,72 @@ extern "C" kvc_status kvc_topk_compact(const float *scores, int64_t G, int64_t S
     // unit; otherwise the copy goes to a wide gather launch
     if ((K || V) && k <= 8192 && G >= device_cu_count() && fused_gather()) {
         hipLaunchKernelGGL(select_compact, dim3(static_cast<unsigned>(G)), dim3(kSelThreads), 0, stream,
-                           scores, S, s_stride, k, idx_out, K, V, K_out, V_out);
+                           scores, S, s_stride, k, nullptr, nullptr, idx_out, K, V, K_out, V_out);
         return launch_status();
     }
     hipLaunchKernelGGL(select_compact, dim3(static_cast<unsigned>(G)), dim3(kSelThreads), 0, stream,
-                       scores, S, s_stride, k, idx_out, nullptr, nullptr, nullptr, nullptr);
+                       scores, S, s_stride, k, nullptr, nullptr, idx_out, nullptr, nullptr, nullptr,
+                       nullptr);
     if (K || V) {
         const int64_t bps = (k + kGatherRows - 1) / kGatherRows;
         if (G * bps > INT32_MAX) return KVC_ERR_UNSUPPORTED;
         hipLaunchKernelGGL(gather_rows, dim3(static_cast<unsigned>(G * bps)), dim3(kGatherThreads), 0,
-                           stream, K, V, S, s_stride, idx_out, k, bps, K_out, V_out);
+                           stream, K, V, S, s_stride, idx_out, k, nullptr, nullptr, bps, K_out, V_out);
+    }
+    return launch_status();
+}
+
+extern "C" kvc_status kvc_topk_compact_ragged(const float *scores, int64_t G, int64_t S,
+                                              int64_t s_stride, const int64_t *k, const uint16_t *K,
+                                              const uint16_t *V, int32_t D, int32_t *idx_out,
+                                              uint16_t *K_out, uint16_t *V_out, void *ws,
+                                              size_t ws_bytes, hipStream_t stream) {
+    using namespace kvc;
+    if (G < 0 || S < 0 || s_stride < S) return KVC_ERR_INVALID_ARGUMENT;
+    if ((K == nullptr) != (K_out == nullptr) || (V == nullptr) != (V_out == nullptr))
+        return KVC_ERR_INVALID_ARGUMENT;
+    if ((K || V) && D != kHeadDim) return D <= 0 ? KVC_ERR_INVALID_ARGUMENT : KVC_ERR_UNSUPPORTED;
+    if (S > INT32_MAX || G > INT32_MAX) return KVC_ERR_UNSUPPORTED;
+    if (G == 0) return KVC_OK;
+    if (!k) return KVC_ERR_INVALID_ARGUMENT;
+    // budgets (host) -> validated, packed offsets
+    int64_t total = 0, kmax = 0;
+    for (int64_t g = 0; g < G; ++g) {
+        if (k[g] < 0 || k[g] > S) return KVC_ERR_INVALID_ARGUMENT;
+        total += k[g];
+        kmax = k[g] > kmax ? k[g] : kmax;
+    }
+    if (total == 0) return KVC_OK;
+    if (!scores || !idx_out || !aligned(scores, 4) || !aligned(idx_out, 4)) return KVC_ERR_INVALID_ARGUMENT;
+    if ((K && (!aligned(K, 16) || !aligned(K_out, 16))) || (V && (!aligned(V, 16) || !aligned(V_out, 16))))
+        return KVC_ERR_INVALID_ARGUMENT;
+    if (!ws || !aligned(ws, kWsAlign)) return KVC_ERR_INVALID_ARGUMENT;
+    if (ws_bytes < topk_ragged_workspace_bytes(G)) return KVC_ERR_WORKSPACE_TOO_SMALL;
+    std::vector<int64_t> host(static_cast<size_t>(2 * G));
+    for (int64_t g = 0, off = 0; g < G; ++g) {
+        host[g] = k[g];
+        host[G + g] = off;
+        off += k[g];
+    }
+    int64_t *kg = static_cast<int64_t *>(ws);
+    int64_t *koff = kg + G;
+    // the copy is ordered before the kernels on the stream; the host vector is read
+    // before hipMemcpyAsync returns (pageable source)
+    if (hipMemcpyAsync(kg, host.data(), host.size() * sizeof(int64_t), hipMemcpyHostToDevice, stream) !=
+        hipSuccess)
+        return KVC_ERR_HIP;
+    if ((K || V) && kmax <= 8192 && G >= device_cu_count() && fused_gather()) {
+        hipLaunchKernelGGL(select_compact, dim3(static_cast<unsigned>(G)), dim3(kSelThreads), 0, stream,
+                           scores, S, s_stride, int64_t{0}, kg, koff, idx_out, K, V, K_out, V_out);
+        return launch_status();
+    }
+    hipLaunchKernelGGL(select_compact, dim3(static_cast<unsigned>(G)), dim3(kSelThreads), 0, stream,
+                       scores, S, s_stride, int64_t{0}, kg, koff, idx_out, nullptr, nullptr, nullptr, nullptr);
+    if (K || V) {
+        const int64_t bps = (kmax + kGatherRows - 1) / kGatherRows;
+        if (G * bps > INT32_MAX) return KVC_ERR_UNSUPPORTED;
+        hipLaunchKernelGGL(gather_rows, dim3(static_cast<unsigned>(G * bps)), dim3(kGatherThreads), 0,
+                           stream, K, V, S, s_stride, idx_out, int64_t{0}, kg, koff, bps, K_out, V_out);
     }
     return launch_status();
 }

@@ -17,12 +17,13 @@ LIB_PATH = os.path.join(_PKG, "libkvc.so")
 
 OK, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_WORKSPACE_TOO_SMALL, ERR_HIP = range(5)
 OP_SCORE_L2, OP_SCORE_L2_WINDOWED, OP_TOPK_COMPACT, OP_LOWRANK_COMPRESS, OP_OJA_UPDATE, \
-    OP_RECONSTRUCT, OP_SCORE_CENTROID = range(7)
+    OP_RECONSTRUCT, OP_SCORE_CENTROID, OP_TOPK_RAGGED = range(8)
 METRIC_L2, METRIC_COSINE = 0, 1
 METRICS = {"l2": METRIC_L2, "cosine": METRIC_COSINE}
 
 EXPORTED = ("kvc_abi_version", "kvc_status_str", "kvc_workspace_bytes", "kvc_score_l2",
-            "kvc_score_l2_windowed", "kvc_score_centroid", "kvc_topk_compact", "kvc_lowrank_compress",
+            "kvc_score_l2_windowed", "kvc_score_centroid", "kvc_layer_budgets", "kvc_topk_compact",
+            "kvc_topk_compact_ragged", "kvc_lowrank_compress",
             "kvc_lowrank_compress_bf16", "kvc_oja_update", "kvc_reconstruct", "kvc_reconstruct_bf16")
 
 
@@ -59,6 +60,8 @@ def load(path: str = LIB_PATH):
                 "kvc_score_l2_windowed": [P, I64, I64, I32, I64, P, P, P, SZ, P],
                 "kvc_score_centroid": [P, I64, I64, I32, I64, I32, P, P, P, SZ, P],
                 "kvc_topk_compact": [P, I64, I64, I64, I64, P, P, I32, P, P, P, P, SZ, P],
+                "kvc_topk_compact_ragged": [P, I64, I64, I64, P, P, P, I32, P, P, P, P, SZ, P],
+                "kvc_layer_budgets": [P, I64, ctypes.c_double, ctypes.c_double, I64, I64, P],
                 "kvc_lowrank_compress": [DP, P, P, P, P, P, P, P, P, P, SZ, P],
                 "kvc_lowrank_compress_bf16": [DP, P, P, P, P, P, P, P, P, P, SZ, P],
                 "kvc_oja_update": [DP, P, P, I32, ctypes.c_float, P, SZ, P],
@@ -180,6 +183,45 @@ def kvc_topk_compact(scores, k, K=None, V=None, S=None, idx_out=None, K_out=None
     _check("kvc_topk_compact",
            lib.kvc_topk_compact(_ptr(scores), G, S, stride, k, _ptr(K), _ptr(V), D, _ptr(idx_out),
                                 _ptr(K_out), _ptr(V_out), _ptr(ws), nb, _stream()))
+    return idx_out, K_out, V_out
+
+
+def kvc_layer_budgets(sensitivity, r, gamma, B, S):
+    """RippleKV per-layer budgets (host computation in libkvc): sensitivity
+    float [L] -> int64 numpy [L] summing to B."""
+    import numpy as np
+    s = np.ascontiguousarray(sensitivity, dtype=np.float64)
+    k = np.zeros(s.shape[0], np.int64)
+    _check("kvc_layer_budgets", load().kvc_layer_budgets(s.ctypes.data_as(ctypes.c_void_p), s.shape[0],
+                                                         float(r), float(gamma), int(B), int(S),
+                                                         k.ctypes.data_as(ctypes.c_void_p)))
+    return k
+
+
+def kvc_topk_compact_ragged(scores, ks, K=None, V=None, S=None, idx_out=None, K_out=None, V_out=None):
+    """scores: fp32 [G, S_stride]; ks: per-slice budgets (int sequence [G]).
+    Returns (idx int32 [sum ks], K_out, V_out bf16 [sum ks, D] or None), packed
+    in slice order."""
+    import numpy as np
+    lib = load()
+    G, stride = scores.shape
+    S = stride if S is None else S
+    k = np.ascontiguousarray(ks, dtype=np.int64)
+    total = int(k.sum())
+    D = K.shape[2] if K is not None else (V.shape[2] if V is not None else 128)
+    dev = scores.device
+    if idx_out is None:
+        idx_out = torch.empty(total, dtype=torch.int32, device=dev)
+    if K is not None and K_out is None:
+        K_out = torch.empty((total, D), dtype=torch.bfloat16, device=dev)
+    if V is not None and V_out is None:
+        V_out = torch.empty((total, D), dtype=torch.bfloat16, device=dev)
+    nb = workspace_bytes(OP_TOPK_RAGGED, _dims(1, 1, G, 0, S, stride, D, 0, 0))
+    ws = workspace(nb, dev.index)
+    _check("kvc_topk_compact_ragged",
+           lib.kvc_topk_compact_ragged(_ptr(scores), G, S, stride, k.ctypes.data_as(ctypes.c_void_p),
+                                       _ptr(K), _ptr(V), D, _ptr(idx_out), _ptr(K_out), _ptr(V_out),
+                                       _ptr(ws), nb, _stream()))
     return idx_out, K_out, V_out
 
 
