@@ -67,6 +67,9 @@ def parse():
     ap.add_argument("--storage", choices=["fp32", "bf16"], default="fp32",
                     help="OjaKV configs 3-4: compressed cache (K~, V~, K^, V^) in fp32 (the "
                          "workload) or bf16 (the memory-saving layout)")
+    ap.add_argument("--refine", action="store_true",
+                    help="time RefineKV cluster summaries (10-key clusters) and risk scores (4 queries "
+                         "per kv head) on a 32-layer x 8-kv-head cache of 131072 tokens instead")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--copy-ref", type=int, default=0, metavar="MIB",
@@ -178,6 +181,52 @@ def manifold_workload(cfg, dev, metric="l2", budgets="uniform"):
             done += 1
         return done * S, t, "%d slice passes (S=%d each; the workload has %d slices, taken in order)" % (
             done, S, G)
+
+    return ops, G * S, algo, config, cpu
+
+
+def refine_workload(dev):
+    import torch
+
+    import synth
+    from token_scoring_eviction_amd import kvc
+    L, H, S, c, nq = 32, 8, 131072, 10, 4
+    G, nC = L * H, -(-S // c)
+    K, V, _ = synth.manifold_global(L, 1, H, S, planted=64, device=dev)
+    Q = torch.randn((G, nq, 128), generator=torch.Generator().manual_seed(11)).to(torch.bfloat16).to(dev)
+    f32 = dict(dtype=torch.float32, device=dev)
+    summ = [torch.empty((G, nC, 128), **f32), torch.empty((G, nC, 128), **f32), torch.empty((G, nC), **f32),
+            torch.empty((G, nC), **f32)]
+    rc = torch.empty((G, nq, nC), **f32)
+
+    def summaries():
+        lib = kvc.load()
+        kvc._check("kvc_cluster_summaries", lib.kvc_cluster_summaries(
+            kvc._ptr(K), kvc._ptr(V), G, S, 128, c, *[kvc._ptr(t) for t in summ], kvc._stream()))
+
+    ops = [Op("kvc_cluster_summaries", summaries, G * S * 512 + G * nC * (2 * 512 + 8),
+              kernel="cluster_summary_kernel"),
+           Op("kvc_refine_risk", lambda: kvc.kvc_refine_risk(summ[0], summ[2], summ[3], S, c, Q, rc=rc),
+              G * nC * (512 + 8 + 3 * nq * 4), kernel="refine_risk_kernel")]
+    algo = G * S * 512 + G * nC * (2 * 512 + 8) + G * nC * (512 + 8 + nq * 4)
+    config = {"workload": "RefineKV cluster summaries (contiguous 10-key clusters: mean key, mean value, "
+                          "key radius, value norm) and risk scores of every cluster for the 4 query heads "
+                          "of each kv head, 32 layers x 8 KV heads x d_h 128, S=131072",
+              "slices": G, "seq_len": S, "cluster": c, "queries": nq}
+
+    def cpu(budget):
+        import numpy as np
+        import oracle
+        done, t = 0, 0.0
+        while t < budget and done < G:
+            kb, vb = synth.bf16_bits(K[done:done + 1, :16384]), synth.bf16_bits(V[done:done + 1, :16384])
+            qb = synth.bf16_bits(Q[done:done + 1])
+            t0 = time.perf_counter()
+            mk, _, rad, vn = oracle.cluster_summaries(kb, vb, c)
+            oracle.refine_risk(mk, rad, vn, 16384, c, qb)
+            t += time.perf_counter() - t0
+            done += 1
+        return done * 16384, t, "%d slices truncated to their first 16384 tokens" % done
 
     return ops, G * S, algo, config, cpu
 
@@ -320,9 +369,11 @@ def main():
     kvc.load()
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
-    if args.config == 4:
+    if args.config == 4 and not args.refine:
         return run_loop_config(args, dev)
-    if args.config == 3:
+    if args.refine:
+        ops, head_tokens, algo, config, cpu = refine_workload(dev)
+    elif args.config == 3:
         ops, head_tokens, algo, config, cpu = oja_workload(dev, args.storage)
     else:
         ops, head_tokens, algo, config, cpu = manifold_workload(args.config, dev, args.metric, args.budgets)

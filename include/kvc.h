@@ -10,6 +10,8 @@
  *         on low-rank attention, method details, appendix A.1 (Algorithm 1).
  *   [RKV] "RippleKV: Cross-Layer KV Cache Allocation via Perturbation
  *         Propagation" (explainer page), sensitivity-guided budget allocation.
+ *   [RFK] "RefineKV" (project page): "Summarize", "Select", the Figure 2 risk
+ *         formula.
  *
  * Common conventions
  *   - Every tensor pointer is a DEVICE pointer to dense row-major memory.
@@ -173,6 +175,31 @@ kvc_status kvc_topk_compact_ragged(const float *scores, int64_t G, int64_t S, in
                                    const int64_t *k, const uint16_t *K, const uint16_t *V,
                                    int32_t D, int32_t *idx_out, uint16_t *K_out, uint16_t *V_out,
                                    void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* RefineKV cluster summaries ([RFK] "Summarize": contiguous clusters with
+ * cached mean keys, mean values and metadata).  For slice g and cluster
+ * j = tokens [jc, min((j+1)c, S)), nC = ceil(S/c):
+ *   mu_k[g][j][:] = mean key, mu_v[g][j][:] = mean value   (fp32 [G][nC][D]),
+ *   radius[g][j]  = max_t ||k_t - mu_k[g][j]||_2            (fp32 [G][nC]),
+ *   vnorm[g][j]   = max_t ||v_t||_2                          (fp32 [G][nC]).
+ * K, V: bf16 [G][S][D].  fp32 accumulation in token order.  c >= 1. */
+kvc_status kvc_cluster_summaries(const uint16_t *K, const uint16_t *V, int64_t G, int64_t S,
+                                 int32_t D, int64_t c, float *mu_k, float *mu_v, float *radius,
+                                 float *vnorm, hipStream_t stream);
+
+/* RefineKV risk score of every cluster for each query ([RFK] "Select": global
+ * importance x local distortion, with the Figure 2 formula)
+ *   RC = 2 p_C Vmax [ (cosh d_C - 1) / Dn + tanh(d_C / 2) ],  Dn = sum_C' p_C' cosh d_C',
+ * where (readings: the page names these quantities without formulas)
+ *   p_C  = n_C exp(z_C) / sum_C' n_C' exp(z_C'),  z_C = q . mu_k[C] / sqrt(D),
+ *   d_C  = ||q|| radius[C] / sqrt(D)   (bounds |q.k - q.mu_C| / sqrt(D) for k in C),
+ *   Vmax = max_C vnorm[C] over the slice.
+ * Summaries as from kvc_cluster_summaries (same S and c); Q: bf16 [G][nq][D]
+ * (the queries served by slice g, nq <= 8); rc: fp32 [G][nq][nC].  A cluster
+ * with RC > tau would be expanded to its exact entries (not done here). */
+kvc_status kvc_refine_risk(const float *mu_k, const float *radius, const float *vnorm, int64_t G,
+                           int64_t S, int64_t c, int32_t D, const uint16_t *Q, int32_t nq, float *rc,
+                           hipStream_t stream);
 
 /* Hybrid low-rank compression ([OJA] background: K~ = K U_k, V~ = V U_v;
  * method details: residual r_t = k_t - U_k U_k^T k_t and query-weighted error

@@ -73,6 +73,8 @@ def _load():
                 "ora_qr": [P, I, I, P],
                 "ora_oja_update": [I, I, I, I, I, I, I, P, P, I, D, P],
                 "ora_layer_budgets": [P, I, D, D, I, I, P],
+                "ora_cluster_summaries": [P, P, I, I, I, I, P, P, P, P],
+                "ora_refine_risk": [P, P, P, I, I, I, I, P, I, P],
             }
             for name, argtypes in sig.items():
                 fn = getattr(lib, name)
@@ -364,4 +366,32 @@ def topk_ragged(scores32, ks, S=None):
     s = _f32(scores32)
     parts = [topk(s[g:g + 1], int(ks[g]), S)[0] for g in range(s.shape[0])]
     return np.concatenate(parts).astype(np.int32) if parts else np.zeros(0, np.int32)
+
+
+def cluster_summaries(K, V, c):
+    """RefineKV summaries of contiguous c-token clusters: (mu_k [G, nC, D],
+    mu_v [G, nC, D], radius [G, nC], vnorm [G, nC]) in float64."""
+    K, V = _u16(K), _u16(V)
+    G, S, D = K.shape
+    nC = -(-S // c)
+    mk, mv = np.zeros((G, nC, D)), np.zeros((G, nC, D))
+    rad, vn = np.zeros((G, nC)), np.zeros((G, nC))
+    _check(_load().ora_cluster_summaries(_p(K), _p(V), G, S, D, c, _p(mk), _p(mv), _p(rad), _p(vn)),
+           "cluster_summaries")
+    return mk, mv, rad, vn
+
+
+def refine_risk(mu_k, radius, vnorm, S, c, Q):
+    """RefineKV risk scores RC [G, nq, nC] (float64) of every cluster for each
+    query; Q: bf16 bits [G, nq, D]."""
+    mu_k = np.ascontiguousarray(mu_k, np.float64)
+    radius = np.ascontiguousarray(radius, np.float64)
+    vnorm = np.ascontiguousarray(vnorm, np.float64)
+    Q = _u16(Q)
+    G, nC, D = mu_k.shape
+    nq = Q.shape[1]
+    rc = np.zeros((G, nq, nC))
+    _check(_load().ora_refine_risk(_p(mu_k), _p(radius), _p(vnorm), G, S, c, D, _p(Q), nq, _p(rc)),
+           "refine_risk")
+    return rc
 

@@ -24,6 +24,9 @@
  *          Propagation" (explainer page), "Sensitivity-Guided Budget
  *          Allocation": normalised sensitivities, exponential multipliers,
  *          clipping, rescaling to the global budget.
+ *   [RFK]  "RefineKV" (project page): "Summarize" (contiguous clusters with
+ *          mean keys, mean values and metadata), "Select" and the Figure 2
+ *          risk-score formula.
  *   [OJA]  "OjaKV: Context-Aware Online Low-Rank KV Cache Compression"
  *          (papercache deep-notes page): the "how it works" display equations
  *          for e_t and the Oja rule, "background / low-rank attention",
@@ -580,6 +583,102 @@ int ora_layer_budgets(const double *s, int64_t L, double r, double gamma, int64_
     }
     free(w);
     free(capped);
+    return ORA_OK;
+}
+
+/* --------------------------------------------------- RefineKV summaries */
+
+/* Cluster summaries ([RFK] "Summarize": the cache is cut into contiguous
+ * clusters whose mean keys, mean values and metadata are cached).  For slice g
+ * and cluster j = tokens [jc, min((j+1)c, S)):
+ *   mu_k[g][j] = mean of its keys, mu_v[g][j] = mean of its values,
+ *   radius[g][j] = max_t ||k_t - mu_k[g][j]||_2   (metadata for the logit bound),
+ *   vnorm[g][j]  = max_t ||v_t||_2                (metadata for the value bound).
+ * Shapes: K, V [G][S][D] bf16; mu_k, mu_v [G][nC][D]; radius, vnorm [G][nC],
+ * nC = ceil(S/c). */
+int ora_cluster_summaries(const uint16_t *K, const uint16_t *V, int64_t G, int64_t S, int64_t D,
+                          int64_t c, double *mu_k, double *mu_v, double *radius, double *vnorm) {
+    if (G < 0 || S <= 0 || D <= 0 || c <= 0 || !K || !V || !mu_k || !mu_v || !radius || !vnorm)
+        return ORA_EINVAL;
+    if (!all_finite_bf16(K, G * S * D) || !all_finite_bf16(V, G * S * D)) return ORA_ENONFINITE;
+    int64_t nC = (S + c - 1) / c;
+    for (int64_t g = 0; g < G; ++g) {
+        const uint16_t *Kg = K + g * S * D, *Vg = V + g * S * D;
+        for (int64_t j = 0; j < nC; ++j) {
+            int64_t t0 = j * c, t1 = t0 + c < S ? t0 + c : S;
+            double *mk = mu_k + (g * nC + j) * D, *mv = mu_v + (g * nC + j) * D;
+            centroid_range(Kg, D, t0, t1, mk);
+            centroid_range(Vg, D, t0, t1, mv);
+            double rmax = 0.0, vmax = 0.0;
+            for (int64_t t = t0; t < t1; ++t) {
+                double dk = l2_distance(Kg + t * D, mk, D);
+                double nv = 0.0;
+                for (int64_t d = 0; d < D; ++d) {
+                    double x = bf16_to_double(Vg[t * D + d]);
+                    nv += x * x;
+                }
+                nv = sqrt(nv);
+                if (dk > rmax) rmax = dk;
+                if (nv > vmax) vmax = nv;
+            }
+            radius[g * nC + j] = rmax;
+            vnorm[g * nC + j] = vmax;
+        }
+    }
+    return ORA_OK;
+}
+
+/* Risk score of every cluster for one query ([RFK] "Select": importance x
+ * distortion, and the Figure 2 formula
+ *   RC = 2 p_C Vmax [ (cosh d_C - 1) / Dn + tanh(d_C / 2) ],  Dn = sum_C' p_C' cosh d_C').
+ * Readings where the page only names the quantities:
+ *   p_C  = n_C exp(z_C) / sum_C' n_C' exp(z_C'),  z_C = q . mu_C / sqrt(D)
+ *          (the share of attention mass if every key of C had the mean's logit),
+ *   d_C  = ||q|| radius_C / sqrt(D)
+ *          (|q.k - q.mu_C| / sqrt(D) <= ||q|| ||k - mu_C|| / sqrt(D), Cauchy-Schwarz),
+ *   Vmax = max_C vnorm_C (one value bound for the slice, as in Figure 2).
+ * mu_k [G][nC][D], radius, vnorm [G][nC]; Q [G][nq][D] bf16 (the queries served
+ * by each slice); RC [G][nq][nC]. */
+int ora_refine_risk(const double *mu_k, const double *radius, const double *vnorm, int64_t G,
+                    int64_t S, int64_t c, int64_t D, const uint16_t *Q, int64_t nq, double *RC) {
+    if (G < 0 || S <= 0 || D <= 0 || c <= 0 || nq < 0 || !mu_k || !radius || !vnorm || (nq > 0 && (!Q || !RC)))
+        return ORA_EINVAL;
+    if (!all_finite_bf16(Q, G * nq * D)) return ORA_ENONFINITE;
+    int64_t nC = (S + c - 1) / c;
+    double *z = (double *)malloc(sizeof(double) * (size_t)nC);
+    if (!z) return ORA_ENOMEM;
+    double rs = 1.0 / sqrt((double)D);
+    for (int64_t g = 0; g < G; ++g) {
+        double vmax = 0.0;
+        for (int64_t j = 0; j < nC; ++j)
+            if (vnorm[g * nC + j] > vmax) vmax = vnorm[g * nC + j];
+        for (int64_t i = 0; i < nq; ++i) {
+            const uint16_t *q = Q + (g * nq + i) * D;
+            double qn = 0.0, zmax = -INFINITY;
+            for (int64_t d = 0; d < D; ++d) qn += bf16_to_double(q[d]) * bf16_to_double(q[d]);
+            qn = sqrt(qn);
+            for (int64_t j = 0; j < nC; ++j) {
+                double dot = 0.0;
+                for (int64_t d = 0; d < D; ++d) dot += bf16_to_double(q[d]) * mu_k[(g * nC + j) * D + d];
+                z[j] = dot * rs;
+                if (z[j] > zmax) zmax = z[j];
+            }
+            double psum = 0.0;
+            for (int64_t j = 0; j < nC; ++j) {
+                double n = (double)((j + 1) * c < S ? c : S - j * c);
+                z[j] = n * exp(z[j] - zmax); /* unnormalised mass */
+                psum += z[j];
+            }
+            double Dn = 0.0;
+            for (int64_t j = 0; j < nC; ++j) Dn += (z[j] / psum) * cosh(qn * radius[g * nC + j] * rs);
+            double *out = RC + (g * nq + i) * nC;
+            for (int64_t j = 0; j < nC; ++j) {
+                double p = z[j] / psum, dl = qn * radius[g * nC + j] * rs;
+                out[j] = 2.0 * p * vmax * ((cosh(dl) - 1.0) / Dn + tanh(dl / 2.0));
+            }
+        }
+    }
+    free(z);
     return ORA_OK;
 }
 

@@ -1,0 +1,221 @@
+// RefineKV cluster summaries and risk scores ("RefineKV" project page:
+// "Summarize" -- contiguous clusters with cached mean keys, mean values and
+// metadata -- and "Select" with the Figure 2 risk formula
+//   RC = 2 p_C Vmax [ (cosh d_C - 1) / Dn + tanh(d_C / 2) ],  Dn = sum_C' p_C' cosh d_C').
+// The page names p_C (the cluster's approximate share of attention mass) and d_C
+// (a bound on the deviation of its keys' logits from the representative's) without
+// formulas; here
+//   p_C = n_C exp(z_C) / sum_C' n_C' exp(z_C'),  z_C = q . mu_C / sqrt(D),
+//   d_C = ||q|| radius_C / sqrt(D)  (Cauchy-Schwarz on q . (k - mu_C)),
+//   Vmax = the largest value norm of the slice.
+//
+// cluster_summary_kernel: one wave per cluster, 2 channels per lane (a 256-byte
+//   key row per load across the wave); sums in token order, 64-lane sums for the
+//   norms; the cluster's key rows stay in registers for the radius pass (c <= 32)
+//   or are read again.
+// refine_risk_kernel: one 1024-thread workgroup per slice and its queries; 16
+//   lanes per cluster (8 channels each) for the logits z, written into the RC
+//   buffer and read back for the normalisation passes; block reductions in a
+//   fixed order (deterministic).
+#include <math.h>
+
+#include "kvc_internal.h"
+
+namespace kvc {
+namespace {
+
+constexpr int kSumWaves = 4;       // clusters per summary workgroup
+constexpr int kKeepRows = 32;      // cluster rows kept in registers for the radius pass
+constexpr int kRiskThreads = 1024;
+constexpr int kMaxRiskQueries = 8;
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) x += __shfl_xor(x, d, 64);
+    return x;
+}
+
+__global__ __launch_bounds__(64 * kSumWaves) void cluster_summary_kernel(
+    const uint16_t *__restrict__ K, const uint16_t *__restrict__ V, int64_t G, int64_t S, int64_t c,
+    int64_t nC, float *__restrict__ mu_k, float *__restrict__ mu_v, float *__restrict__ radius,
+    float *__restrict__ vnorm) {
+    const int64_t cl = static_cast<int64_t>(blockIdx.x) * kSumWaves + (threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63;
+    if (cl >= G * nC) return;  // whole waves leave together
+    const int64_t g = cl / nC, j = cl - g * nC;
+    const int64_t t0 = j * c, t1 = min(t0 + c, S);
+    const uint32_t *kr = reinterpret_cast<const uint32_t *>(K + (g * S) * kHeadDim) + lane;
+    const uint32_t *vr = reinterpret_cast<const uint32_t *>(V + (g * S) * kHeadDim) + lane;
+    float sk0 = 0.f, sk1 = 0.f, sv0 = 0.f, sv1 = 0.f, vmax2 = 0.f;
+    uint32_t keep[kKeepRows];
+#pragma unroll
+    for (int r = 0; r < kKeepRows; ++r) keep[r] = 0u;
+    for (int64_t t = t0; t < t1; ++t) {
+        const uint32_t kw = kr[t * (kHeadDim / 2)], vw = vr[t * (kHeadDim / 2)];
+        const int r = static_cast<int>(t - t0);
+#pragma unroll
+        for (int q = 0; q < kKeepRows; ++q)
+            if (q == r) keep[q] = kw;
+        sk0 += bf16_lo(kw);
+        sk1 += bf16_hi(kw);
+        const float a = bf16_lo(vw), b = bf16_hi(vw);
+        sv0 += a;
+        sv1 += b;
+        vmax2 = fmaxf(vmax2, wave_sum(a * a + b * b));
+    }
+    const float n = static_cast<float>(t1 - t0);
+    const float m0 = sk0 / n, m1 = sk1 / n;
+    float rmax2 = 0.f;
+    for (int64_t t = t0; t < t1; ++t) {
+        const int r = static_cast<int>(t - t0);
+        uint32_t kw = 0u;
+        if (r < kKeepRows) {
+#pragma unroll
+            for (int q = 0; q < kKeepRows; ++q)
+                if (q == r) kw = keep[q];
+        } else {
+            kw = kr[t * (kHeadDim / 2)];
+        }
+        const float d0 = bf16_lo(kw) - m0, d1 = bf16_hi(kw) - m1;
+        rmax2 = fmaxf(rmax2, wave_sum(d0 * d0 + d1 * d1));
+    }
+    reinterpret_cast<float2 *>(mu_k + cl * kHeadDim)[lane] = make_float2(m0, m1);
+    reinterpret_cast<float2 *>(mu_v + cl * kHeadDim)[lane] = make_float2(sv0 / n, sv1 / n);
+    if (lane == 0) {
+        radius[cl] = sqrtf(rmax2);
+        vnorm[cl] = sqrtf(vmax2);
+    }
+}
+
+// Block-wide reduction over 1024 threads in a fixed order (op: 0 sum, 1 max).
+template <int kOp>
+__device__ __forceinline__ float block_reduce(float x, float *scratch) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) {
+        const float y = __shfl_xor(x, d, 64);
+        x = kOp == 0 ? x + y : fmaxf(x, y);
+    }
+    __syncthreads();  // scratch is free
+    if (lane == 0) scratch[wave] = x;
+    __syncthreads();
+    float r = kOp == 0 ? 0.f : -INFINITY;
+    for (int w = 0; w < kRiskThreads / 64; ++w) r = kOp == 0 ? r + scratch[w] : fmaxf(r, scratch[w]);
+    return r;
+}
+
+__global__ __launch_bounds__(kRiskThreads) void refine_risk_kernel(
+    const float *__restrict__ mu_k, const float *__restrict__ radius, const float *__restrict__ vnorm,
+    int64_t S, int64_t c, int64_t nC, const uint16_t *__restrict__ Q, int nq, float *__restrict__ rc) {
+    __shared__ float qs[kMaxRiskQueries][kHeadDim];
+    __shared__ float scratch[kRiskThreads / 64];
+    const int64_t g = blockIdx.x;
+    const int tid = threadIdx.x, lane16 = tid & 15, grp = tid >> 4;  // 64 groups of 16 lanes
+    const float rs = 1.f / sqrtf(static_cast<float>(kHeadDim));
+    for (int i = tid; i < nq * kHeadDim; i += kRiskThreads) {
+        const uint16_t h = Q[(g * nq) * kHeadDim + i];
+        qs[i / kHeadDim][i % kHeadDim] = __uint_as_float(static_cast<uint32_t>(h) << 16);
+    }
+    __syncthreads();
+    float qn[kMaxRiskQueries];
+    for (int i = 0; i < nq; ++i) {
+        float s = 0.f;
+        for (int d = 0; d < kHeadDim; ++d) s += qs[i][d] * qs[i][d];
+        qn[i] = sqrtf(s);  // the same bits in every thread
+    }
+    float *rcg = rc + g * nq * nC;
+    // pass 1: logits z into the output rows; running maxima; the slice's value bound
+    float zmax[kMaxRiskQueries], vm = 0.f;
+    for (int i = 0; i < kMaxRiskQueries; ++i) zmax[i] = -INFINITY;
+    for (int64_t j = grp; j < nC; j += kRiskThreads / 16) {
+        const float4 *m4 = reinterpret_cast<const float4 *>(mu_k + (g * nC + j) * kHeadDim + lane16 * 8);
+        const float4 a = m4[0], b = m4[1];
+        for (int i = 0; i < nq; ++i) {
+            const float *q = &qs[i][lane16 * 8];
+            float z = a.x * q[0] + a.y * q[1] + a.z * q[2] + a.w * q[3] + b.x * q[4] + b.y * q[5] +
+                      b.z * q[6] + b.w * q[7];
+            z += __shfl_xor(z, 8, 16);
+            z += __shfl_xor(z, 4, 16);
+            z += __shfl_xor(z, 2, 16);
+            z += __shfl_xor(z, 1, 16);
+            z *= rs;
+            zmax[i] = fmaxf(zmax[i], z);
+            if (lane16 == i) rcg[i * nC + j] = z;
+        }
+        vm = fmaxf(vm, vnorm[g * nC + j]);
+    }
+    const float vmax = block_reduce<1>(vm, scratch);
+    for (int i = 0; i < nq; ++i) zmax[i] = block_reduce<1>(zmax[i], scratch);
+    __syncthreads();  // the logits written by other threads are visible
+    // pass 2: masses n_C exp(z - zmax) and the sums over clusters
+    float psum[kMaxRiskQueries], dsum[kMaxRiskQueries];
+    for (int i = 0; i < nq; ++i) {
+        psum[i] = 0.f;
+        dsum[i] = 0.f;
+    }
+    for (int64_t j = tid; j < nC; j += kRiskThreads) {
+        const float n = static_cast<float>(min((j + 1) * c, S) - j * c);
+        const float r = radius[g * nC + j];
+        for (int i = 0; i < nq; ++i) {
+            const float p = n * expf(rcg[i * nC + j] - zmax[i]);
+            psum[i] += p;
+            dsum[i] += p * coshf(qn[i] * r * rs);
+        }
+    }
+    for (int i = 0; i < nq; ++i) {
+        psum[i] = block_reduce<0>(psum[i], scratch);
+        dsum[i] = block_reduce<0>(dsum[i], scratch);
+    }
+    // pass 3: RC = 2 p Vmax [ (cosh d - 1) / Dn + tanh(d / 2) ], cosh d - 1 = 2 sinh^2(d / 2)
+    for (int64_t j = tid; j < nC; j += kRiskThreads) {
+        const float n = static_cast<float>(min((j + 1) * c, S) - j * c);
+        const float r = radius[g * nC + j];
+        for (int i = 0; i < nq; ++i) {
+            const float p = n * expf(rcg[i * nC + j] - zmax[i]) / psum[i];
+            const float dl = qn[i] * r * rs;
+            const float sh = sinhf(0.5f * dl);
+            const float Dn = dsum[i] / psum[i];
+            rcg[i * nC + j] = 2.f * p * vmax * (2.f * sh * sh / Dn + tanhf(0.5f * dl));
+        }
+    }
+}
+
+}  // namespace
+}  // namespace kvc
+
+extern "C" kvc_status kvc_cluster_summaries(const uint16_t *K, const uint16_t *V, int64_t G, int64_t S,
+                                            int32_t D, int64_t c, float *mu_k, float *mu_v,
+                                            float *radius, float *vnorm, hipStream_t stream) {
+    using namespace kvc;
+    if (G < 0 || S < 1 || c < 1 || D <= 0) return KVC_ERR_INVALID_ARGUMENT;
+    if (D != kHeadDim) return KVC_ERR_UNSUPPORTED;
+    if (G == 0) return KVC_OK;
+    if (!K || !V || !mu_k || !mu_v || !radius || !vnorm) return KVC_ERR_INVALID_ARGUMENT;
+    if (!aligned(K, 16) || !aligned(V, 16) || !aligned(mu_k, 16) || !aligned(mu_v, 16) ||
+        !aligned(radius, 4) || !aligned(vnorm, 4))
+        return KVC_ERR_INVALID_ARGUMENT;
+    const int64_t nC = (S + c - 1) / c;
+    const int64_t blocks = (G * nC + kSumWaves - 1) / kSumWaves;
+    if (blocks > INT32_MAX) return KVC_ERR_UNSUPPORTED;
+    hipLaunchKernelGGL(cluster_summary_kernel, dim3(static_cast<unsigned>(blocks)), dim3(64 * kSumWaves), 0,
+                       stream, K, V, G, S, c, nC, mu_k, mu_v, radius, vnorm);
+    return launch_status();
+}
+
+extern "C" kvc_status kvc_refine_risk(const float *mu_k, const float *radius, const float *vnorm,
+                                      int64_t G, int64_t S, int64_t c, int32_t D, const uint16_t *Q,
+                                      int32_t nq, float *rc, hipStream_t stream) {
+    using namespace kvc;
+    if (G < 0 || S < 1 || c < 1 || D <= 0 || nq < 0) return KVC_ERR_INVALID_ARGUMENT;
+    if (D != kHeadDim || nq > kMaxRiskQueries) return KVC_ERR_UNSUPPORTED;
+    if (G == 0 || nq == 0) return KVC_OK;
+    if (!mu_k || !radius || !vnorm || !Q || !rc) return KVC_ERR_INVALID_ARGUMENT;
+    if (!aligned(mu_k, 16) || !aligned(radius, 4) || !aligned(vnorm, 4) || !aligned(Q, 2) ||
+        !aligned(rc, 4))
+        return KVC_ERR_INVALID_ARGUMENT;
+    if (G > INT32_MAX) return KVC_ERR_UNSUPPORTED;
+    const int64_t nC = (S + c - 1) / c;
+    hipLaunchKernelGGL(refine_risk_kernel, dim3(static_cast<unsigned>(G)), dim3(kRiskThreads), 0, stream,
+                       mu_k, radius, vnorm, S, c, nC, Q, nq, rc);
+    return launch_status();
+}

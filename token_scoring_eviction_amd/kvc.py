@@ -23,7 +23,7 @@ METRICS = {"l2": METRIC_L2, "cosine": METRIC_COSINE}
 
 EXPORTED = ("kvc_abi_version", "kvc_status_str", "kvc_workspace_bytes", "kvc_score_l2",
             "kvc_score_l2_windowed", "kvc_score_centroid", "kvc_layer_budgets", "kvc_topk_compact",
-            "kvc_topk_compact_ragged", "kvc_lowrank_compress",
+            "kvc_topk_compact_ragged", "kvc_cluster_summaries", "kvc_refine_risk", "kvc_lowrank_compress",
             "kvc_lowrank_compress_bf16", "kvc_oja_update", "kvc_reconstruct", "kvc_reconstruct_bf16")
 
 
@@ -62,6 +62,8 @@ def load(path: str = LIB_PATH):
                 "kvc_topk_compact": [P, I64, I64, I64, I64, P, P, I32, P, P, P, P, SZ, P],
                 "kvc_topk_compact_ragged": [P, I64, I64, I64, P, P, P, I32, P, P, P, P, SZ, P],
                 "kvc_layer_budgets": [P, I64, ctypes.c_double, ctypes.c_double, I64, I64, P],
+                "kvc_cluster_summaries": [P, P, I64, I64, I32, I64, P, P, P, P, P],
+                "kvc_refine_risk": [P, P, P, I64, I64, I64, I32, P, I32, P, P],
                 "kvc_lowrank_compress": [DP, P, P, P, P, P, P, P, P, P, SZ, P],
                 "kvc_lowrank_compress_bf16": [DP, P, P, P, P, P, P, P, P, P, SZ, P],
                 "kvc_oja_update": [DP, P, P, I32, ctypes.c_float, P, SZ, P],
@@ -223,6 +225,33 @@ def kvc_topk_compact_ragged(scores, ks, K=None, V=None, S=None, idx_out=None, K_
                                        _ptr(K), _ptr(V), D, _ptr(idx_out), _ptr(K_out), _ptr(V_out),
                                        _ptr(ws), nb, _stream()))
     return idx_out, K_out, V_out
+
+
+def kvc_cluster_summaries(K, V, c):
+    """K, V: bf16 [G, S, D] -> (mu_k fp32 [G, nC, D], mu_v fp32 [G, nC, D], radius fp32
+    [G, nC], vnorm fp32 [G, nC]) for contiguous clusters of c tokens."""
+    lib = load()
+    G, S, D = K.shape
+    nC = -(-S // c)
+    f32 = dict(dtype=torch.float32, device=K.device)
+    mk, mv = torch.empty((G, nC, D), **f32), torch.empty((G, nC, D), **f32)
+    rad, vn = torch.empty((G, nC), **f32), torch.empty((G, nC), **f32)
+    _check("kvc_cluster_summaries",
+           lib.kvc_cluster_summaries(_ptr(_bits(K)), _ptr(_bits(V)), G, S, D, c, _ptr(mk), _ptr(mv),
+                                     _ptr(rad), _ptr(vn), _stream()))
+    return mk, mv, rad, vn
+
+
+def kvc_refine_risk(mu_k, radius, vnorm, S, c, Q, rc=None):
+    """Risk scores fp32 [G, nq, nC] of every cluster for each query; Q bf16 [G, nq, D]."""
+    lib = load()
+    G, nC, D = mu_k.shape
+    nq = Q.shape[1]
+    if rc is None:
+        rc = torch.empty((G, nq, nC), dtype=torch.float32, device=mu_k.device)
+    _check("kvc_refine_risk", lib.kvc_refine_risk(_ptr(mu_k), _ptr(radius), _ptr(vnorm), G, S, c, D,
+                                                  _ptr(_bits(Q)), nq, _ptr(rc), _stream()))
+    return rc
 
 
 def _compress(name, dtype, K, V, Q_win, U_k, U_v, L, B, H_kv, S, K_tilde, V_tilde, err):
