@@ -10,9 +10,9 @@
 //   Vmax = the largest value norm of the slice.
 //
 // cluster_summary_kernel: one wave per cluster, 2 channels per lane (a 256-byte
-//   key row per load across the wave); sums in token order, 64-lane sums for the
-//   norms; the cluster's key rows stay in registers for the radius pass (c <= 32)
-//   or are read again.
+//   key row per load across the wave), up to 16 (c <= 16) or 32 rows of K and V in
+//   flight at once; sums in token order, 64-lane sums for the norms; the first
+//   chunk's key rows stay in registers for the radius pass, later ones are read again.
 // refine_risk_kernel: one 1024-thread workgroup per slice and its queries; 16
 //   lanes per cluster (8 channels each) for the logits z, written into the RC
 //   buffer and read back for the normalisation passes; block reductions in a
@@ -25,7 +25,6 @@ namespace kvc {
 namespace {
 
 constexpr int kSumWaves = 4;       // clusters per summary workgroup
-constexpr int kKeepRows = 32;      // cluster rows kept in registers for the radius pass
 constexpr int kRiskThreads = 1024;
 constexpr int kMaxRiskQueries = 8;
 
@@ -35,6 +34,7 @@ __device__ __forceinline__ float wave_sum(float x) {
     return x;
 }
 
+template <int kKeepRows>
 __global__ __launch_bounds__(64 * kSumWaves) void cluster_summary_kernel(
     const uint16_t *__restrict__ K, const uint16_t *__restrict__ V, int64_t G, int64_t S, int64_t c,
     int64_t nC, float *__restrict__ mu_k, float *__restrict__ mu_v, float *__restrict__ radius,
@@ -47,37 +47,48 @@ __global__ __launch_bounds__(64 * kSumWaves) void cluster_summary_kernel(
     const uint32_t *kr = reinterpret_cast<const uint32_t *>(K + (g * S) * kHeadDim) + lane;
     const uint32_t *vr = reinterpret_cast<const uint32_t *>(V + (g * S) * kHeadDim) + lane;
     float sk0 = 0.f, sk1 = 0.f, sv0 = 0.f, sv1 = 0.f, vmax2 = 0.f;
-    uint32_t keep[kKeepRows];
+    // rows in chunks of kKeepRows, every load of a chunk in flight before any use;
+    // the first chunk's key rows stay in registers for the radius pass
+    uint32_t kw[kKeepRows];
+    for (int64_t base = t0; base < t1; base += kKeepRows) {
+        uint32_t kc[kKeepRows], vc[kKeepRows];
 #pragma unroll
-    for (int r = 0; r < kKeepRows; ++r) keep[r] = 0u;
-    for (int64_t t = t0; t < t1; ++t) {
-        const uint32_t kw = kr[t * (kHeadDim / 2)], vw = vr[t * (kHeadDim / 2)];
-        const int r = static_cast<int>(t - t0);
+        for (int r = 0; r < kKeepRows; ++r) {
+            const bool ok = base + r < t1;
+            kc[r] = ok ? kr[(base + r) * (kHeadDim / 2)] : 0u;
+            vc[r] = ok ? vr[(base + r) * (kHeadDim / 2)] : 0u;
+        }
 #pragma unroll
-        for (int q = 0; q < kKeepRows; ++q)
-            if (q == r) keep[q] = kw;
-        sk0 += bf16_lo(kw);
-        sk1 += bf16_hi(kw);
-        const float a = bf16_lo(vw), b = bf16_hi(vw);
-        sv0 += a;
-        sv1 += b;
-        vmax2 = fmaxf(vmax2, wave_sum(a * a + b * b));
+        for (int r = 0; r < kKeepRows; ++r) {
+            if (base + r < t1) {  // token order
+                sk0 += bf16_lo(kc[r]);
+                sk1 += bf16_hi(kc[r]);
+                const float a = bf16_lo(vc[r]), b = bf16_hi(vc[r]);
+                sv0 += a;
+                sv1 += b;
+                vmax2 = fmaxf(vmax2, wave_sum(a * a + b * b));
+            }
+        }
+        if (base == t0) {
+#pragma unroll
+            for (int r = 0; r < kKeepRows; ++r) kw[r] = kc[r];
+        }
     }
     const float n = static_cast<float>(t1 - t0);
     const float m0 = sk0 / n, m1 = sk1 / n;
     float rmax2 = 0.f;
-    for (int64_t t = t0; t < t1; ++t) {
-        const int r = static_cast<int>(t - t0);
-        uint32_t kw = 0u;
-        if (r < kKeepRows) {
+    for (int64_t base = t0; base < t1; base += kKeepRows) {
+        uint32_t kc[kKeepRows];
 #pragma unroll
-            for (int q = 0; q < kKeepRows; ++q)
-                if (q == r) kw = keep[q];
-        } else {
-            kw = kr[t * (kHeadDim / 2)];
+        for (int r = 0; r < kKeepRows; ++r)
+            kc[r] = base == t0 ? kw[r] : (base + r < t1 ? kr[(base + r) * (kHeadDim / 2)] : 0u);
+#pragma unroll
+        for (int r = 0; r < kKeepRows; ++r) {
+            if (base + r < t1) {
+                const float d0 = bf16_lo(kc[r]) - m0, d1 = bf16_hi(kc[r]) - m1;
+                rmax2 = fmaxf(rmax2, wave_sum(d0 * d0 + d1 * d1));
+            }
         }
-        const float d0 = bf16_lo(kw) - m0, d1 = bf16_hi(kw) - m1;
-        rmax2 = fmaxf(rmax2, wave_sum(d0 * d0 + d1 * d1));
     }
     reinterpret_cast<float2 *>(mu_k + cl * kHeadDim)[lane] = make_float2(m0, m1);
     reinterpret_cast<float2 *>(mu_v + cl * kHeadDim)[lane] = make_float2(sv0 / n, sv1 / n);
@@ -197,8 +208,13 @@ extern "C" kvc_status kvc_cluster_summaries(const uint16_t *K, const uint16_t *V
     const int64_t nC = (S + c - 1) / c;
     const int64_t blocks = (G * nC + kSumWaves - 1) / kSumWaves;
     if (blocks > INT32_MAX) return KVC_ERR_UNSUPPORTED;
-    hipLaunchKernelGGL(cluster_summary_kernel, dim3(static_cast<unsigned>(blocks)), dim3(64 * kSumWaves), 0,
-                       stream, K, V, G, S, c, nC, mu_k, mu_v, radius, vnorm);
+    // rows per chunk (in flight together, the first chunk kept for the radius pass)
+    if (c <= 16)
+        hipLaunchKernelGGL(cluster_summary_kernel<16>, dim3(static_cast<unsigned>(blocks)), dim3(64 * kSumWaves),
+                           0, stream, K, V, G, S, c, nC, mu_k, mu_v, radius, vnorm);
+    else
+        hipLaunchKernelGGL(cluster_summary_kernel<32>, dim3(static_cast<unsigned>(blocks)), dim3(64 * kSumWaves),
+                           0, stream, K, V, G, S, c, nC, mu_k, mu_v, radius, vnorm);
     return launch_status();
 }
 
