@@ -255,6 +255,20 @@ kvc_status kvc_reconstruct(const kvc_dims *d, const float *X_tilde, const float 
                            const int32_t *anchor_idx, const uint16_t *anchor_rows, int64_t k,
                            float *X_hat, void *ws, size_t ws_bytes, hipStream_t stream);
 
+/* Decode-step append ([OJA] method details, appendix A.1: each decoded token
+ * joins the cache and the update buffer, its queries the scoring window):
+ *   K[g][pos][:] = k_new[g][:],  V[g][pos][:] = v_new[g][:]      (g < L*B*H_kv),
+ *   K_buf[g][slot][:] = k_new[g][:], V_buf[g][slot][:] = v_new[g][:]   (if given),
+ *   Q_buf[h][slot][:] = q_new[h][:]  for the L*B*H_q query heads h   (if q_new given).
+ * K, V: bf16 [L*B*H_kv][S_stride][D]; k_new, v_new: bf16 [L*B*H_kv][D];
+ * K_buf, V_buf: bf16 [L*B*H_kv][T][D] (both or neither); q_new: bf16
+ * [L*B*H_q][D]; Q_buf: bf16 [L*B*H_q][T][D].  0 <= pos < S_stride (d->S_stride,
+ * or d->S when 0), 0 <= slot < T.  One launch; no workspace. */
+kvc_status kvc_decode_append(const kvc_dims *d, int64_t pos, int64_t T, int64_t slot,
+                             const uint16_t *k_new, const uint16_t *v_new, const uint16_t *q_new,
+                             uint16_t *K, uint16_t *V, uint16_t *K_buf, uint16_t *V_buf,
+                             uint16_t *Q_buf, hipStream_t stream);
+
 /* Reconstruction from bf16 storage: as kvc_reconstruct, with X_tilde and X_hat
  * bf16.  X_hat = bf16(X_tilde U^T), an fp32 accumulation of the exact bf16
  * X_tilde against U split as hi + lo, rounded to nearest even; anchor rows are

@@ -130,3 +130,31 @@ def test_loop_config4_sampled(gpu_lib):
         assert len(result[g]) == checked + 1
         for j, ora in enumerate(result[g]):
             _compare(snaps[j][g], ora, ora["S"])
+
+
+def test_decode_append_places_rows(gpu_lib):
+    # one decode step's rows land bit for bit in the cache, the update buffer and the
+    # query window (method details / A.1), and nothing else changes
+    L, B, Hkv, Hq, S_cap, T, D = 2, 1, 3, 12, 50, 8, 128
+    G = L * B * Hkv
+    gen = torch.Generator().manual_seed(3)
+    K = torch.randn((G, S_cap, D), generator=gen).to(torch.bfloat16).to(DEV)
+    V = torch.randn((G, S_cap, D), generator=gen).to(torch.bfloat16).to(DEV)
+    Kb = torch.randn((G, T, D), generator=gen).to(torch.bfloat16).to(DEV)
+    Vb = torch.randn((G, T, D), generator=gen).to(torch.bfloat16).to(DEV)
+    Qb = torch.randn((L, B, Hq, T, D), generator=gen).to(torch.bfloat16).to(DEV)
+    k = torch.randn((G, D), generator=gen).to(torch.bfloat16).to(DEV)
+    v = torch.randn((G, D), generator=gen).to(torch.bfloat16).to(DEV)
+    q = torch.randn((L, B, Hq, D), generator=gen).to(torch.bfloat16).to(DEV)
+    ref = [t.clone() for t in (K, V, Kb, Vb, Qb)]
+    ref[0][:, 37] = k
+    ref[1][:, 37] = v
+    ref[2][:, 5] = k
+    ref[3][:, 5] = v
+    ref[4][:, :, :, 5] = q
+    gpu_lib.kvc_decode_append(K, V, k, v, 37, L, B, Hkv, K_buf=Kb, V_buf=Vb, slot=5, q_new=q, Q_buf=Qb)
+    torch.cuda.synchronize()
+    for got, want in zip((K, V, Kb, Vb, Qb), ref):
+        assert torch.equal(got.view(torch.int16), want.view(torch.int16))
+    with pytest.raises(gpu_lib.KvcError):
+        gpu_lib.kvc_decode_append(K, V, k, v, S_cap, L, B, Hkv)  # position past the capacity

@@ -24,7 +24,8 @@ METRICS = {"l2": METRIC_L2, "cosine": METRIC_COSINE}
 EXPORTED = ("kvc_abi_version", "kvc_status_str", "kvc_workspace_bytes", "kvc_score_l2",
             "kvc_score_l2_windowed", "kvc_score_centroid", "kvc_layer_budgets", "kvc_topk_compact",
             "kvc_topk_compact_ragged", "kvc_cluster_summaries", "kvc_refine_risk", "kvc_lowrank_compress",
-            "kvc_lowrank_compress_bf16", "kvc_oja_update", "kvc_reconstruct", "kvc_reconstruct_bf16")
+            "kvc_lowrank_compress_bf16", "kvc_oja_update", "kvc_reconstruct", "kvc_reconstruct_bf16",
+            "kvc_decode_append")
 
 
 class KvcError(RuntimeError):
@@ -69,6 +70,7 @@ def load(path: str = LIB_PATH):
                 "kvc_oja_update": [DP, P, P, I32, ctypes.c_float, P, SZ, P],
                 "kvc_reconstruct": [DP, P, P, P, P, I64, P, P, SZ, P],
                 "kvc_reconstruct_bf16": [DP, P, P, P, P, I64, P, P, SZ, P],
+                "kvc_decode_append": [DP, I64, I64, I64, P, P, P, P, P, P, P, P, P],
             }
             for name, a in sigs.items():
                 fn = getattr(lib, name)
@@ -332,3 +334,18 @@ def kvc_reconstruct_bf16(X_tilde, U, anchor_idx, anchor_rows, L, B, H_kv, S=None
     """As kvc_reconstruct with X_tilde bf16 [G, S_stride, R] -> X_hat bf16 [G, S_stride, D]."""
     return _reconstruct("kvc_reconstruct_bf16", torch.bfloat16, X_tilde, U, anchor_idx, anchor_rows, L,
                         B, H_kv, S, X_hat)
+
+
+def kvc_decode_append(K, V, k_new, v_new, pos, L, B, H_kv, K_buf=None, V_buf=None, slot=0,
+                      q_new=None, Q_buf=None):
+    """Writes k_new/v_new (bf16 [G, D]) at token pos of K, V (bf16 [G, S_stride, D]),
+    and (if given) at `slot` of K_buf/V_buf (bf16 [G, T, D]); q_new (bf16 [L, B, H_q, D])
+    at `slot` of Q_buf (bf16 [L, B, H_q, T, D])."""
+    G, stride, D = K.shape
+    H_q = q_new.shape[2] if q_new is not None else 0
+    T = K_buf.shape[1] if K_buf is not None else (Q_buf.shape[3] if Q_buf is not None else 1)
+    d = _dims(L, B, H_kv, H_q, stride, stride, D, 0, 0)
+    _check("kvc_decode_append",
+           load().kvc_decode_append(ctypes.byref(d), pos, T, slot, _ptr(k_new), _ptr(v_new), _ptr(q_new),
+                                    _ptr(K), _ptr(V), _ptr(K_buf), _ptr(V_buf), _ptr(Q_buf), _stream()))
+

@@ -156,11 +156,8 @@ def ojakv_decode_step(state: OjaLoopState, K, V, k_new, v_new, q_new, L, B, H_kv
     anchors re-selected and K^, V^ rebuilt.  Returns True on an update step.
     k_new, v_new: bf16 [G, 128]; q_new: bf16 [L, B, H_q, 128]."""
     slot = state.step % T
-    K[:, state.S] = k_new
-    V[:, state.S] = v_new
-    state.K_buf[:, slot] = k_new
-    state.V_buf[:, slot] = v_new
-    state.Q_dec[:, :, :, slot] = q_new
+    kvc.kvc_decode_append(K, V, k_new, v_new, state.S, L, B, H_kv, K_buf=state.K_buf, V_buf=state.V_buf,
+                          slot=slot, q_new=q_new, Q_buf=state.Q_dec)
     state.S += 1
     state.step += 1
     if state.step % T:
