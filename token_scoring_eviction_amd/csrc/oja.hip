@@ -186,16 +186,93 @@ __global__ __launch_bounds__(256) void oja_step_qr_kernel(float *__restrict__ U,
     for (int e = tid; e < kHeadDim * R; e += blockDim.x) Ug[e] = static_cast<float>(Ul[(e / R) * ld + e % R]);
 }
 
+// Cholesky QR of W [128][R] (fp64, LDS, row-major) applied twice: G = W^T W =
+// R_^T R_ with R_ upper triangular and a positive diagonal, then W <- W R_^{-1}.
+// One pass leaves an orthogonality error of about cond(W)^2 eps; the second
+// pass, on a W that is already orthonormal to that level, brings it to eps.  The
+// Q factor with a positive diagonal of R is unique, so this is the same Q as any
+// other QR with that convention.  256 threads; G [R][R+1] and dg [R] are scratch.
+template <int R>
+__device__ void cholesky_qr2(double *W, double *G, double *dg) {
+    constexpr int TS = R / 16;  // Gram tile per thread (16 x 16 threads)
+    constexpr int ldg = R + 1;
+    const int tid = threadIdx.x;
+    for (int pass = 0; pass < 2; ++pass) {
+        {  // G = W^T W, a TS x TS tile per thread (exactly symmetric: same products, same order)
+            const int ti = tid >> 4, tj = tid & 15;
+            double acc[TS][TS];
+#pragma unroll
+            for (int x = 0; x < TS; ++x)
+#pragma unroll
+                for (int y = 0; y < TS; ++y) acc[x][y] = 0.0;
+            for (int r = 0; r < kHeadDim; ++r) {
+                double a[TS], b[TS];
+#pragma unroll
+                for (int x = 0; x < TS; ++x) {
+                    a[x] = W[r * R + ti * TS + x];
+                    b[x] = W[r * R + tj * TS + x];
+                }
+#pragma unroll
+                for (int x = 0; x < TS; ++x)
+#pragma unroll
+                    for (int y = 0; y < TS; ++y) acc[x][y] = fma(a[x], b[y], acc[x][y]);
+            }
+#pragma unroll
+            for (int x = 0; x < TS; ++x)
+#pragma unroll
+                for (int y = 0; y < TS; ++y) G[(ti * TS + x) * ldg + tj * TS + y] = acc[x][y];
+        }
+        __syncthreads();
+        // right-looking Cholesky on the unscaled rows: step k removes row k from the
+        // trailing block; the rows are scaled by 1/sqrt(G_kk) at the end
+        for (int k = 0; k < R - 1; ++k) {
+            const int n = R - 1 - k;
+            const double inv = 1.0 / G[k * ldg + k];
+            for (int e = tid; e < n * n; e += blockDim.x) {
+                const int i = k + 1 + e / n, j = k + 1 + e % n;
+                G[i * ldg + j] -= G[k * ldg + i] * G[k * ldg + j] * inv;
+            }
+            __syncthreads();
+        }
+        if (tid < R) dg[tid] = sqrt(G[tid * ldg + tid]);
+        __syncthreads();
+        for (int e = tid; e < R * R; e += blockDim.x) {
+            const int k = e / R, j = e % R;
+            if (j >= k) G[k * ldg + j] /= dg[k];
+        }
+        __syncthreads();
+        // W <- W R_^{-1}: one row per thread, forward substitution in registers
+        if (tid < kHeadDim) {
+            double x[R];
+#pragma unroll
+            for (int j = 0; j < R; ++j) x[j] = W[tid * R + j];
+#pragma unroll
+            for (int j = 0; j < R; ++j) {
+                double s0 = x[j], s1 = 0.0;
+#pragma unroll
+                for (int i = 0; i < j; ++i) {
+                    if (i & 1) s1 = fma(-x[i], G[i * ldg + j], s1);
+                    else s0 = fma(-x[i], G[i * ldg + j], s0);
+                }
+                x[j] = (s0 + s1) / G[j * ldg + j];
+            }
+#pragma unroll
+            for (int j = 0; j < R; ++j) W[tid * R + j] = x[j];
+        }
+        __syncthreads();
+    }
+}
+
 // Fast path for R <= 64: everything per head stays in LDS.
-//   Ud [128][R+1] fp64: U, later Q;  Wd [128][R] fp64: C column chunks, then CU,
-//   then U';  Mf [R][R+1] fp32: U^T C U;  vs/ds: Gram-Schmidt scratch.
+//   Ud [128][R+1] fp64: U, later the Gram matrix of the QR;  Wd [128][R] fp64: C
+//   column chunks, then CU, then U', then Q;  Mf [R][R+1] fp32: U^T C U;  vs: scratch.
 // Each thread owns row a = tid / 2 and half of the columns of CU and U'.
 constexpr int kCChunk = 16;  // C columns staged per step
 
+template <int R>
 __global__ __launch_bounds__(256) void oja_step_qr_lds_kernel(float *__restrict__ U,
                                                               const float *__restrict__ Cpart,
-                                                              int64_t nchunk, int64_t n, int R,
-                                                              double eta) {
+                                                              int64_t nchunk, int64_t n, double eta) {
     extern __shared__ double lds[];
     const int ld = R + 1;
     double *Ud = lds;                                  // [128][R+1]
@@ -257,30 +334,10 @@ __global__ __launch_bounds__(256) void oja_step_qr_lds_kernel(float *__restrict_
         }
     }
     __syncthreads();
-    // QR of U' (columns of Wd) by Gram-Schmidt twice per column; Q replaces U in Ud
-    for (int j = 0; j < R; ++j) {
-        double v = tid < kHeadDim ? Wd[tid * R + j] : 0.0;
-        for (int pass = 0; pass < 2; ++pass) {
-            if (tid < kHeadDim) vs[tid] = v;
-            __syncthreads();
-            if (tid < j) {
-                double d = 0.0;
-                for (int r = 0; r < kHeadDim; ++r) d += Ud[r * ld + tid] * vs[r];
-                ds[tid] = d;
-            }
-            __syncthreads();
-            if (tid < kHeadDim) {
-                double sum = 0.0;
-                for (int i = 0; i < j; ++i) sum += ds[i] * Ud[tid * ld + i];
-                v -= sum;
-            }
-            __syncthreads();
-        }
-        const double nrm2 = block_sum_128(tid < kHeadDim ? v * v : 0.0, red);
-        if (tid < kHeadDim) Ud[tid * ld + j] = v / sqrt(nrm2);
-        __syncthreads();
-    }
-    for (int e = tid; e < kHeadDim * R; e += blockDim.x) Ug[e] = static_cast<float>(Ud[(e / R) * ld + e % R]);
+    // QR of U' (in Wd) by Cholesky QR twice; U is no longer needed, so its
+    // storage holds the Gram matrix
+    cholesky_qr2<R>(Wd, Ud, vs);
+    for (int e = tid; e < kHeadDim * R; e += blockDim.x) Ug[e] = static_cast<float>(Wd[e]);
 }
 
 size_t oja_lds_bytes(int R) {
@@ -371,12 +428,17 @@ extern "C" kvc_status kvc_oja_update(const kvc_dims *d, float *U, const uint16_t
     hipLaunchKernelGGL(cov_partial_kernel, dim3(static_cast<unsigned>(o.LH * o.nchunk)), dim3(256), 0,
                        stream, Xp, d->B, d->H_kv, o.np, o.rows_per_chunk, o.nchunk, Cpart);
     if (d->R <= 64) {
-        static bool lds_ok[64];
-        if (allow_large_lds(reinterpret_cast<const void *>(&oja_step_qr_lds_kernel), lds_ok) != KVC_OK)
-            return KVC_ERR_HIP;
-        hipLaunchKernelGGL(oja_step_qr_lds_kernel, dim3(static_cast<unsigned>(o.LH)), dim3(256),
-                           oja_lds_bytes(static_cast<int>(d->R)), stream, U, Cpart, o.nchunk, o.n,
-                           static_cast<int>(d->R), static_cast<double>(eta));
+        static bool lds_ok[2][64];
+        const void *fn = d->R == 32 ? reinterpret_cast<const void *>(&oja_step_qr_lds_kernel<32>)
+                                    : reinterpret_cast<const void *>(&oja_step_qr_lds_kernel<64>);
+        if (allow_large_lds(fn, lds_ok[d->R == 32 ? 0 : 1]) != KVC_OK) return KVC_ERR_HIP;
+        const size_t lds = oja_lds_bytes(static_cast<int>(d->R));
+        if (d->R == 32)
+            hipLaunchKernelGGL(oja_step_qr_lds_kernel<32>, dim3(static_cast<unsigned>(o.LH)), dim3(256), lds,
+                               stream, U, Cpart, o.nchunk, o.n, static_cast<double>(eta));
+        else
+            hipLaunchKernelGGL(oja_step_qr_lds_kernel<64>, dim3(static_cast<unsigned>(o.LH)), dim3(256), lds,
+                               stream, U, Cpart, o.nchunk, o.n, static_cast<double>(eta));
         return launch_status();
     }
     const size_t lds = (static_cast<size_t>(kHeadDim) * (d->R + 1) + 2 * kHeadDim + 2) * sizeof(double);
