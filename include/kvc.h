@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define KVC_ABI_VERSION 2
+#define KVC_ABI_VERSION 3
 
 typedef enum kvc_status {
     KVC_OK = 0,
@@ -277,6 +277,48 @@ kvc_status kvc_decode_append(const kvc_dims *d, int64_t pos, int64_t T, int64_t 
 kvc_status kvc_reconstruct_bf16(const kvc_dims *d, const uint16_t *X_tilde, const float *U,
                                 const int32_t *anchor_idx, const uint16_t *anchor_rows, int64_t k,
                                 uint16_t *X_hat, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* Compression with the reconstruction fused in ([OJA] background: K~ = K U_k
+ * and K^ = K~ U_k^T; the OjaKV pass that re-projects the cache and rebuilds
+ * K^, V^ for attention): everything kvc_lowrank_compress computes, plus
+ *   K_hat[g][t][:] = K_tilde[g][t][:] U_k^T,  V_hat[g][t][:] = V_tilde[g][t][:] U_v^T
+ * for EVERY token t < S, anchors not placed (select them from err with
+ * kvc_topk_compact, then write their rows with kvc_place_anchors).  X~ is
+ * taken from the projection's registers instead of being read back (4R fewer
+ * bytes per head-token and tensor in fp32, 2R in bf16).  The
+ * outputs equal those of kvc_lowrank_compress followed by kvc_reconstruct with
+ * k = 0, bit for bit.
+ *   K_hat: fp32 [L][B][H_kv][S_stride][D] (not NULL); V_hat: same, NULL iff V is NULL.
+ * Other arguments, workspace (KVC_OP_LOWRANK_COMPRESS) and errors as
+ * kvc_lowrank_compress. */
+kvc_status kvc_lowrank_compress_reconstruct(const kvc_dims *d, const uint16_t *K, const uint16_t *V,
+                                            const uint16_t *Q_win, const float *U_k, const float *U_v,
+                                            float *K_tilde, float *V_tilde, float *err, float *K_hat,
+                                            float *V_hat, void *ws, size_t ws_bytes, hipStream_t stream);
+
+/* bf16 storage: as kvc_lowrank_compress_reconstruct with K~, V~, K^, V^ bf16;
+ * equals kvc_lowrank_compress_bf16 followed by kvc_reconstruct_bf16 with k = 0,
+ * bit for bit. */
+kvc_status kvc_lowrank_compress_reconstruct_bf16(const kvc_dims *d, const uint16_t *K,
+                                                 const uint16_t *V, const uint16_t *Q_win,
+                                                 const float *U_k, const float *U_v, uint16_t *K_tilde,
+                                                 uint16_t *V_tilde, float *err, uint16_t *K_hat,
+                                                 uint16_t *V_hat, void *ws, size_t ws_bytes,
+                                                 hipStream_t stream);
+
+/* The hybrid cache's full-rank anchors put into a reconstruction ([OJA] method
+ * details: anchor tokens keep their exact rows):
+ *   X_hat[g][idx[g][i]][:] = anchor_rows[g][i][:]   (bf16 widened exactly), i < k.
+ * Uses d->L, B, H_kv, S, S_stride, D only.  anchor_idx: int32 [L*B*H_kv][k]
+ * (indices < S; an index outside [0, S) is skipped); anchor_rows: bf16
+ * [L*B*H_kv][k][D]; X_hat: fp32 [L][B][H_kv][S_stride][D].  k = 0 does nothing. */
+kvc_status kvc_place_anchors(const kvc_dims *d, const int32_t *anchor_idx, const uint16_t *anchor_rows,
+                             int64_t k, float *X_hat, hipStream_t stream);
+
+/* As kvc_place_anchors into a bf16 X_hat (rows copied bit for bit). */
+kvc_status kvc_place_anchors_bf16(const kvc_dims *d, const int32_t *anchor_idx,
+                                  const uint16_t *anchor_rows, int64_t k, uint16_t *X_hat,
+                                  hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -1,0 +1,137 @@
+"""GPU parity of the compression with the reconstruction fused in
+(kvc_lowrank_compress_reconstruct and its bf16 form) and of anchor placement
+(kvc_place_anchors): "OjaKV: Context-Aware Online Low-Rank KV Cache
+Compression", background (K^ = K~ U^T) and method details (anchor rows kept
+exact).  Rules: fp32 K^/V^ within rel 2e-3 of (|oracle| + rms(slice)); bf16
+K^/V^ within +-1 bf16 ulp of the oracle's reconstruction of the stored bf16 K~;
+every output bit-identical to compress followed by reconstruct; anchor rows
+exact and no other row touched."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from tests.helpers import bf16_close, lowrank_close, score_close
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def _bits(t):
+    return synth.bf16_bits(t)
+
+
+def _same(a, b):
+    if a.dtype == torch.bfloat16:
+        return torch.equal(a.view(torch.int16), b.view(torch.int16))
+    return torch.equal(a, b)
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+@pytest.mark.parametrize("R", [32, 64, 96, 128])
+def test_fused_equals_compress_then_reconstruct(gpu_lib, R, bf16):
+    # ragged token count inside a strided cache: S = 700 of 760 rows
+    S = 700
+    inp = synth.oja_inputs(2, 2, 2, 8, S, R=R, Wq=32, S_cap=760, seed=R + 11 * bf16, device=DEV)
+    args = (inp.K, inp.V, inp.Q, inp.Uk, inp.Uv, inp.L, inp.B, inp.Hkv)
+    if bf16:
+        Kt, Vt, err, Kh, Vh = gpu_lib.kvc_lowrank_compress_reconstruct_bf16(*args, S=S)
+        Kt2, Vt2, err2 = gpu_lib.kvc_lowrank_compress_bf16(*args, S=S)
+        Kh2 = gpu_lib.kvc_reconstruct_bf16(Kt2, inp.Uk, None, None, inp.L, inp.B, inp.Hkv, S=S)
+        Vh2 = gpu_lib.kvc_reconstruct_bf16(Vt2, inp.Uv, None, None, inp.L, inp.B, inp.Hkv, S=S)
+    else:
+        Kt, Vt, err, Kh, Vh = gpu_lib.kvc_lowrank_compress_reconstruct(*args, S=S)
+        Kt2, Vt2, err2 = gpu_lib.kvc_lowrank_compress(*args, S=S)
+        Kh2 = gpu_lib.kvc_reconstruct(Kt2, inp.Uk, None, None, inp.L, inp.B, inp.Hkv, S=S)
+        Vh2 = gpu_lib.kvc_reconstruct(Vt2, inp.Uv, None, None, inp.L, inp.B, inp.Hkv, S=S)
+    torch.cuda.synchronize()
+    for a, b in ((Kt, Kt2), (Vt, Vt2), (err, err2), (Kh, Kh2), (Vh, Vh2)):
+        assert _same(a[:, :S], b[:, :S])
+
+
+@pytest.mark.parametrize("R,Hq,Wq", [(64, 8, 32), (32, 8, 32), (64, 2, 1), (64, 16, 8)])
+def test_fused_vs_oracle(gpu_lib, R, Hq, Wq):
+    S = 1000
+    inp = synth.oja_inputs(1, 2, 2, Hq, S, R=R, Wq=Wq, seed=R * 7 + Hq + Wq, device=DEV)
+    Kt, Vt, err, Kh, Vh = gpu_lib.kvc_lowrank_compress_reconstruct(inp.K, inp.V, inp.Q, inp.Uk, inp.Uv,
+                                                                   inp.L, inp.B, inp.Hkv)
+    torch.cuda.synchronize()
+    G, grp = inp.L * inp.B * inp.Hkv, inp.Hq // inp.Hkv
+    Uk, Uv = inp.Uk.cpu().numpy(), inp.Uv.cpu().numpy()
+    for g in range(G):
+        l, b, h = g // (inp.B * inp.Hkv), (g // inp.Hkv) % inp.B, g % inp.Hkv
+        Q = _bits(inp.Q[l:l + 1, b:b + 1, h * grp:(h + 1) * grp])
+        okt, ovt, oerr = oracle.lowrank_compress(_bits(inp.K[g:g + 1]), _bits(inp.V[g:g + 1]), Q,
+                                                 Uk[l:l + 1, h:h + 1], Uv[l:l + 1, h:h + 1], 1, 1, 1, grp)
+        okh = oracle.reconstruct(okt, Uk[l:l + 1, h:h + 1], None, None, 1, 1, 1)
+        ovh = oracle.reconstruct(ovt, Uv[l:l + 1, h:h + 1], None, None, 1, 1, 1)
+        for gpu, ora, name in ((Kt, okt, "K~"), (Vt, ovt, "V~"), (Kh, okh, "K^"), (Vh, ovh, "V^")):
+            ok, rel = lowrank_close(gpu[g:g + 1].cpu().numpy(), ora)
+            assert ok, "%s slice %d: max rel %.3g" % (name, g, rel)
+        ok, rel, nbad = score_close(err[g:g + 1].cpu().numpy(), oerr)
+        assert ok, "err slice %d: %d off, max rel %.3g" % (g, nbad, rel)
+
+
+@pytest.mark.parametrize("R", [32, 64])
+def test_fused_bf16_vs_oracle(gpu_lib, R):
+    S = 777
+    inp = synth.oja_inputs(2, 1, 2, 8, S, R=R, Wq=16, seed=R + 3, device=DEV)
+    Kt, Vt, err, Kh, Vh = gpu_lib.kvc_lowrank_compress_reconstruct_bf16(inp.K, inp.V, inp.Q, inp.Uk, inp.Uv,
+                                                                        inp.L, inp.B, inp.Hkv)
+    torch.cuda.synchronize()
+    G, grp = inp.L * inp.B * inp.Hkv, inp.Hq // inp.Hkv
+    Uk, Uv = inp.Uk.cpu().numpy(), inp.Uv.cpu().numpy()
+    for g in range(G):
+        l, b, h = g // (inp.B * inp.Hkv), (g // inp.Hkv) % inp.B, g % inp.Hkv
+        Q = _bits(inp.Q[l:l + 1, b:b + 1, h * grp:(h + 1) * grp])
+        okt, ovt, _ = oracle.lowrank_compress(_bits(inp.K[g:g + 1]), _bits(inp.V[g:g + 1]), Q,
+                                              Uk[l:l + 1, h:h + 1], Uv[l:l + 1, h:h + 1], 1, 1, 1, grp)
+        for gt, ora, U, gh, name in ((Kt, okt, Uk, Kh, "K"), (Vt, ovt, Uv, Vh, "V")):
+            ok, ulp = bf16_close(_bits(gt[g:g + 1]), ora)
+            assert ok, "%s~ slice %d: %d ulps" % (name, g, ulp)
+            # X^ is rebuilt from the stored bf16 X~, widened exactly
+            ora_h = oracle.reconstruct(gt[g:g + 1].float().cpu().numpy(), U[l:l + 1, h:h + 1], None, None,
+                                       1, 1, 1)
+            ok, ulp = bf16_close(_bits(gh[g:g + 1]), ora_h)
+            assert ok, "%s^ slice %d: %d ulps" % (name, g, ulp)
+
+
+@pytest.mark.parametrize("bf16", [False, True])
+def test_place_anchors(gpu_lib, bf16):
+    L, B, Hkv, S, stride, k = 2, 1, 3, 517, 530, 29
+    G = L * B * Hkv
+    dt = torch.bfloat16 if bf16 else torch.float32
+    Xh = torch.full((G, stride, 128), -7.0, dtype=dt, device=DEV)
+    rng = np.random.default_rng(5 + bf16)
+    idx = np.sort(np.stack([rng.choice(S, k, replace=False) for _ in range(G)]), 1).astype(np.int32)
+    idx[1, -1] = S  # outside the slice's tokens: skipped
+    rows = _bits(torch.randn((G, k, 128)).to(torch.bfloat16))
+    place = gpu_lib.kvc_place_anchors_bf16 if bf16 else gpu_lib.kvc_place_anchors
+    place(torch.from_numpy(idx).to(DEV), synth.from_bits(rows, DEV), L, B, Hkv, Xh, S=S)
+    torch.cuda.synchronize()
+    got = Xh.float().cpu().numpy()
+    want = np.full((G, stride, 128), -7.0)
+    for g in range(G):
+        for i in range(k):
+            if idx[g, i] < S:
+                want[g, idx[g, i]] = synth.from_bits(rows[g, i], "cpu").float().numpy()
+    np.testing.assert_array_equal(got, want)
+
+
+def test_pipeline_fused_equals_unfused(gpu_lib):
+    # one hybrid pass both ways, fp32 and bf16 storage: identical caches, bit for bit
+    from token_scoring_eviction_amd import pipeline
+    inp = synth.oja_inputs(2, 1, 4, 16, 3000, R=64, Wq=32, S_cap=3100, seed=23, device=DEV)
+    G = inp.L * inp.B * inp.Hkv
+    for storage in ("fp32", "bf16"):
+        a = pipeline.alloc_hybrid(G, 3100, 64, storage=storage, device=DEV)
+        b = pipeline.alloc_hybrid(G, 3100, 64, storage=storage, device=DEV)
+        for st, fused in ((a, True), (b, False)):
+            pipeline.hybrid_pass(inp.K, inp.V, inp.Q, inp.Uk, inp.Uv, inp.L, inp.B, inp.Hkv, 3000, st,
+                                 fused=fused)
+        torch.cuda.synchronize()
+        for x, y in ((a.Kt, b.Kt), (a.Vt, b.Vt), (a.err, b.err), (a.Khat, b.Khat), (a.Vhat, b.Vhat)):
+            assert _same(x[:, :3000], y[:, :3000]), storage
+        n = G * pipeline.anchor_count(3000)  # a pass's anchors: the first G*k entries
+        assert torch.equal(a.idx.view(-1)[:n], b.idx.view(-1)[:n])

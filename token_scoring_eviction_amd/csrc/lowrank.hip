@@ -23,6 +23,14 @@
 // hi and lo) sit in LDS as [fragment][lane][16 bytes], read conflict-free.
 // Accumulator lane i, register r holds row 8(r/4) + 4(i/32) + r%4, column i%32,
 // so four consecutive output features go out as one 16-byte store.
+//
+// Rank order of the reconstruction.  A sum over the rank may take the ranks in
+// any order as long as both operands agree.  Reconstruction k-step ks gives
+// operand element e of lane half h the rank 16ks + 8(e/4) + 4h + e%4: exactly the
+// ranks that a projection accumulator lane already holds in registers 8(ks%2)..+7
+// of its rank block, so the fused kernel feeds X~ to the reconstruction straight
+// from the projection's accumulators, and the stand-alone reconstruction (which
+// loads X~ in the same order) gives bit-identical X^.
 #include "kvc_internal.h"
 
 namespace kvc {
@@ -71,6 +79,56 @@ __device__ __forceinline__ void split8x3_f64(const double *x, u32x4 *part) {
     for (int p = 0; p < 3; ++p)
 #pragma unroll
         for (int q = 0; q < 4; ++q) part[p][q] = t[p][2 * q] | (t[p][2 * q + 1] << 16);
+}
+
+// rank carried by operand element e of lane half h at reconstruction k-step ks
+__host__ __device__ constexpr int recon_rank(int ks, int h, int e) {
+    return 16 * ks + 8 * (e >> 2) + 4 * h + (e & 3);
+}
+
+// Reconstruction B operand: U[c][rank] for channel block cb, hi/lo bf16 split,
+// stored as [cb][ks][hi|lo][lane] fragments (lane = channel cb*32 + lane%32, half lane/32).
+template <int R>
+__device__ void stage_recon_u(const float *__restrict__ U, u32x4 *frag) {
+    constexpr int KS = R / 16;
+    for (int p = threadIdx.x; p < 4 * KS * 64; p += blockDim.x) {
+        const int lane = p & 63, fs = p >> 6, ks = fs % KS, cb = fs / KS;
+        const int c = cb * 32 + (lane & 31), h = lane >> 5;
+        float x[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) x[e] = U[c * R + recon_rank(ks, h, e)];
+        u32x4 hi, lo;
+        split8(x, hi, lo);
+        frag[((cb * KS + ks) * 2 + 0) * 64 + lane] = hi;
+        frag[((cb * KS + ks) * 2 + 1) * 64 + lane] = lo;
+    }
+}
+
+// One reconstruction k-step: X~ fragment x (token rows) times U fragment u
+// (channel columns), D[token][channel].
+__device__ __forceinline__ f32x16 recon_mfma(u32x4 x, u32x4 u, f32x16 c) { return mfma32x32x16(x, u, c); }
+
+// Stores a 32-token x 32-channel block of X^ (tokens t0.., channels cb*32..):
+// lane (col, khalf) holds channel cb*32 + col of tokens 8(j/4) + 4khalf + j%4, so
+// each fp32 store covers two 128-byte row segments; bf16 pairs go out from the
+// even lane.  (The transposed block, 16-byte pieces of 32 rows per store, was
+// measured 20% slower for fp32 and 36% slower for bf16.)
+template <typename OutT>
+__device__ __forceinline__ void recon_store(OutT *xh, int64_t t0, int64_t t_end, int cb, int col, int khalf,
+                                            const f32x16 &acc) {
+    constexpr bool kBf16 = sizeof(OutT) == 2;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+        const int64_t tj = t0 + (j >> 2) * 8 + khalf * 4 + (j & 3);
+        if constexpr (kBf16) {
+            const float nb = __shfl_xor(acc[j], 1);  // channel col ^ 1, same token
+            if (!(col & 1) && tj < t_end)
+                *reinterpret_cast<uint32_t *>(xh + tj * kHeadDim + cb * 32 + col) =
+                    f32_to_bf16_rne(acc[j]) | (f32_to_bf16_rne(nb) << 16);
+        } else {
+            if (tj < t_end) xh[tj * kHeadDim + cb * 32 + col] = acc[j];
+        }
+    }
 }
 
 struct Slices {
@@ -217,20 +275,34 @@ __global__ __launch_bounds__(256) void prep_query_kernel(const uint16_t *__restr
 
 // One block per (slice, token range).  Each wave takes 32*HB tokens per step
 // (HB column blocks of 32 tokens share every A fragment read from LDS).
-// LDS: U^T fragments [rb][s][hi|lo] (NRB*16 KB), then Q'' fragments
+// LDS: U^T fragments [rb][s][hi|lo] (NRB*16 KB), with kRebuild the
+// reconstruction's U fragments [cb][ks][hi|lo] (NRB*16 KB), then Q'' fragments
 // [qb][s][term] (nqb*8*nterm KB).  HB = 1 runs 16 waves per block (4 per SIMD),
 // HB = 2 runs 8 waves with twice the reuse of each fragment.
-template <int NRB, int HB, bool kRowStores, typename OutT>
+//
+// kRebuild also writes X^ = X~ U^T for every token (no anchors): the step's X~
+// accumulators, split hi/lo (fp32 storage) or rounded to the stored bf16, are the
+// A operand of the reconstruction in the rank order of recon_rank, so X~ is
+// never read back from memory.
+template <int NRB, int HB, bool kRowStores, bool kRebuild, typename OutT>
 __global__ __launch_bounds__(HB == 1 ? 1024 : 512) void project_kernel(
     const uint16_t *__restrict__ X, const float *__restrict__ Ubase, const u32x4 *__restrict__ qfrag,
-    int nqb, int nterm, Slices sl, OutT *__restrict__ Xt, float *__restrict__ err) {
+    int nqb, int nterm, Slices sl, OutT *__restrict__ Xt, float *__restrict__ err,
+    OutT *__restrict__ Xh) {
     // OutT float: fp32 K~ rows; OutT uint16_t: bf16 K~ rows (round to nearest even)
+    static_assert(!(kRowStores && kRebuild), "the fused reconstruction needs rank-major accumulators");
     constexpr bool kBf16 = sizeof(OutT) == 2;
     constexpr int R = 32 * NRB;
+    constexpr int KS = R / 16;  // reconstruction k-steps
     constexpr int TOK = 32 * HB;
+#ifndef KVC_FUSED_LATE_PREFETCH
+#define KVC_FUSED_LATE_PREFETCH 1
+#endif
+    constexpr bool kLatePrefetch = kRebuild && KVC_FUSED_LATE_PREFETCH;
     extern __shared__ u32x4 lds[];
     u32x4 *ufr = lds;
-    u32x4 *qfr = lds + NRB * 16 * 64;  // after the U^T fragments
+    u32x4 *rfr = lds + NRB * 16 * 64;                            // reconstruction fragments
+    u32x4 *qfr = lds + NRB * 16 * 64 * (kRebuild ? 2 : 1);       // after the U fragments
 
     const int64_t slice = blockIdx.x / sl.nsplit;
     const int64_t split = blockIdx.x % sl.nsplit;
@@ -250,6 +322,7 @@ __global__ __launch_bounds__(HB == 1 ? 1024 : 512) void project_kernel(
         ufr[((rb * 8 + s) * 2 + 0) * 64 + lane] = hi;
         ufr[((rb * 8 + s) * 2 + 1) * 64 + lane] = lo;
     }
+    if constexpr (kRebuild) stage_recon_u<R>(U, rfr);
     if (nqb > 0) {
         const int nq4 = nqb * 8 * nterm * 64;
         const u32x4 *src = qfrag + slice * static_cast<int64_t>(nq4);
@@ -282,12 +355,48 @@ __global__ __launch_bounds__(HB == 1 ? 1024 : 512) void project_kernel(
             }
         }
     };
+    // error score of the step's tokens: err_t = sum over the folded queries of |Q''_q . k_t|
+    auto score_step = [&](int64_t t0, const u32x4 (&b)[HB][8]) {
+        float e[HB];
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb) e[hb] = 0.f;
+#pragma unroll 1
+        for (int qb = 0; qb < nqb; ++qb) {
+            f32x16 a[HB];
+#pragma unroll
+            for (int hb = 0; hb < HB; ++hb) a[hb] = f32x16{};
+#pragma unroll
+            for (int s = 0; s < 8; ++s) {
+                for (int t = 0; t < nterm; ++t) {
+                    const u32x4 f = qfr[((qb * 8 + s) * nterm + t) * 64 + lane];
+#pragma unroll
+                    for (int hb = 0; hb < HB; ++hb) a[hb] = mfma32x32x16(f, b[hb][s], a[hb]);
+                }
+            }
+#pragma unroll
+            for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) e[hb] += fabsf(a[hb][r]);
+        }
+        float *er = err + slice * sl.S_stride;
+#pragma unroll
+        for (int hb = 0; hb < HB; ++hb) {
+            e[hb] += __shfl_xor(e[hb], 32);
+            if (khalf == 0 && t0 + hb * 32 + col < t_end) er[t0 + hb * 32 + col] = e[hb];
+        }
+    };
     const int64_t wstep = (blockDim.x / 64) * TOK;
     u32x4 b[HB][8], bn[HB][8];
+    // X~ of the step as reconstruction operands: [k-step][hb][hi|lo]
+    u32x4 xf[kRebuild ? KS : 1][HB][2];
     if (t_begin + wave * TOK < t_end) load_b(t_begin + wave * TOK, b);
     for (int64_t t0 = t_begin + wave * TOK; t0 < t_end; t0 += wstep) {
-        // the next step's keys are requested before this step's contractions
-        if (t0 + wstep < t_end) load_b(t0 + wstep, bn);
+        // the next step's keys are requested before this step's contractions (fused:
+        // once the projection is done, which keeps fewer registers live)
+        if (!kLatePrefetch && t0 + wstep < t_end) load_b(t0 + wstep, bn);
+        // fused: the score first, so that the keys are dead once the projection
+        // has built the X~ fragments (fewer registers live at once)
+        if (kRebuild && nqb > 0) score_step(t0, b);
 #pragma unroll 1
         for (int rb = 0; rb < NRB; ++rb) {
             f32x16 a[HB];
@@ -328,6 +437,27 @@ __global__ __launch_bounds__(HB == 1 ? 1024 : 512) void project_kernel(
                         }
                     }
             } else {
+                if constexpr (kRebuild) {
+                    // registers 8sp..8sp+7 hold ranks recon_rank(2rb + sp, khalf, 0..7);
+                    // the loop stays rolled (fewer live fragments), so the rank block
+                    // picks its registers by a uniform branch
+                    auto keep = [&](auto rbc) {
+                        constexpr int kb = decltype(rbc)::value;
+#pragma unroll
+                        for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+                            for (int sp = 0; sp < 2; ++sp) {
+                                float x[8];
+#pragma unroll
+                                for (int e = 0; e < 8; ++e) x[e] = a[hb][8 * sp + e];
+                                split8(x, xf[2 * kb + sp][hb][0], xf[2 * kb + sp][hb][1]);
+                            }
+                    };
+                    if (rb == 0) keep(std::integral_constant<int, 0>{});
+                    if constexpr (NRB > 1) {
+                        if (rb == 1) keep(std::integral_constant<int, 1>{});
+                    }
+                }
                 // lane (col, khalf) holds ranks rb*32 + 8q + 4khalf .. +4 of token col
 #pragma unroll
                 for (int hb = 0; hb < HB; ++hb) {
@@ -349,33 +479,30 @@ __global__ __launch_bounds__(HB == 1 ? 1024 : 512) void project_kernel(
                 }
             }
         }
-        if (nqb > 0) {
-            float e[HB];
-#pragma unroll
-            for (int hb = 0; hb < HB; ++hb) e[hb] = 0.f;
+        if (!kRebuild && nqb > 0) score_step(t0, b);
+        if (kLatePrefetch && t0 + wstep < t_end) load_b(t0 + wstep, bn);
+        if constexpr (kRebuild) {
+            // X^[t][c] for channel block cb: hi*hi + hi*lo + lo*hi (fp32 X~), or the
+            // stored bf16 X~ times U hi and lo
+            OutT *xh = Xh + slice * sl.S_stride * kHeadDim;
 #pragma unroll 1
-            for (int qb = 0; qb < nqb; ++qb) {
-                f32x16 a[HB];
+            for (int cb = 0; cb < 4; ++cb) {
+                f32x16 acc[HB];
 #pragma unroll
-                for (int hb = 0; hb < HB; ++hb) a[hb] = f32x16{};
+                for (int hb = 0; hb < HB; ++hb) acc[hb] = f32x16{};
 #pragma unroll
-                for (int s = 0; s < 8; ++s) {
-                    for (int t = 0; t < nterm; ++t) {
-                        const u32x4 f = qfr[((qb * 8 + s) * nterm + t) * 64 + lane];
+                for (int ks = 0; ks < KS; ++ks) {
+                    const u32x4 uh = rfr[((cb * KS + ks) * 2 + 0) * 64 + lane];
+                    const u32x4 ul = rfr[((cb * KS + ks) * 2 + 1) * 64 + lane];
 #pragma unroll
-                        for (int hb = 0; hb < HB; ++hb) a[hb] = mfma32x32x16(f, b[hb][s], a[hb]);
+                    for (int hb = 0; hb < HB; ++hb) {
+                        acc[hb] = recon_mfma(xf[ks][hb][0], uh, acc[hb]);
+                        acc[hb] = recon_mfma(xf[ks][hb][0], ul, acc[hb]);
+                        if constexpr (!kBf16) acc[hb] = recon_mfma(xf[ks][hb][1], uh, acc[hb]);
                     }
                 }
 #pragma unroll
-                for (int hb = 0; hb < HB; ++hb)
-#pragma unroll
-                    for (int r = 0; r < 16; ++r) e[hb] += fabsf(a[hb][r]);
-            }
-            float *er = err + slice * sl.S_stride;
-#pragma unroll
-            for (int hb = 0; hb < HB; ++hb) {
-                e[hb] += __shfl_xor(e[hb], 32);
-                if (khalf == 0 && t0 + hb * 32 + col < t_end) er[t0 + hb * 32 + col] = e[hb];
+                for (int hb = 0; hb < HB; ++hb) recon_store(xh, t0 + hb * 32, t_end, cb, col, khalf, acc[hb]);
             }
         }
 #pragma unroll
@@ -388,8 +515,9 @@ __global__ __launch_bounds__(HB == 1 ? 1024 : 512) void project_kernel(
 // ------------------------------------------------------------- reconstruct
 
 // One block per (slice, token range); 4 waves; each wave 32 tokens per step.
-// X^^T[c][t] = sum_j U[c][j] X~[t][j]: A = U (channel rows, hi/lo in LDS),
-// B = X~^T split hi/lo in registers; hi*hi + lo*hi + hi*lo.
+// X^[t][c] = sum_j X~[t][j] U[c][j]: A = X~ split hi/lo in registers, B = U
+// (channel columns, hi/lo in LDS), ranks in the reconstruction order;
+// hi*hi + hi*lo + lo*hi.
 template <int NRB>
 __global__ __launch_bounds__(256) void reconstruct_kernel(const float *__restrict__ Xt,
                                                           const float *__restrict__ Ubase,
@@ -404,20 +532,7 @@ __global__ __launch_bounds__(256) void reconstruct_kernel(const float *__restric
     const int64_t l = slice / (sl.Hkv * sl.B);
     const float *U = Ubase + (l * sl.Hkv + h) * kHeadDim * R;
 
-    for (int p = threadIdx.x; p < 4 * KS * 64; p += blockDim.x) {
-        const int lane = p & 63, fs = p >> 6, s = fs % KS, cb = fs / KS;
-        const int c = cb * 32 + (lane & 31);
-        const int j0 = 16 * s + (lane >> 5) * 8;
-        float x[8];
-        const float4 *src = reinterpret_cast<const float4 *>(U + c * R + j0);
-        const float4 u0 = src[0], u1 = src[1];
-        x[0] = u0.x; x[1] = u0.y; x[2] = u0.z; x[3] = u0.w;
-        x[4] = u1.x; x[5] = u1.y; x[6] = u1.z; x[7] = u1.w;
-        u32x4 hi, lo;
-        split8(x, hi, lo);
-        ufr[((cb * KS + s) * 2 + 0) * 64 + lane] = hi;
-        ufr[((cb * KS + s) * 2 + 1) * 64 + lane] = lo;
-    }
+    stage_recon_u<R>(U, ufr);
     __syncthreads();
 
     const int64_t t_begin = split * sl.per_split;
@@ -427,25 +542,23 @@ __global__ __launch_bounds__(256) void reconstruct_kernel(const float *__restric
     const float *xt = Xt + slice * sl.S_stride * R;
     float *xh = Xh + slice * sl.S_stride * kHeadDim;
 
-    // X~ rows of a wave step: lane (col, khalf) holds ranks 16s + 8khalf .. +8 of
-    // token t0 + col (B operand), split hi/lo once the step's data is in hand
+    // X~ rows of a wave step: lane (col, khalf) holds ranks recon_rank(s, khalf, 0..7)
+    // of token t0 + col (two 16-byte pieces), split hi/lo once the step's data is in hand
     const int64_t wstep = (blockDim.x / 64) * 32;
     float4 xc[2 * KS], xn[2 * KS];
 #define KVC_LOAD_X(T0, DST)                                                                      \
     do {                                                                                          \
         const int64_t tok_ = (T0) + col;                                                          \
         const bool ok_ = tok_ < t_end;                                                            \
-        const float4 *src_ = reinterpret_cast<const float4 *>(xt + (ok_ ? tok_ : 0) * R + khalf * 8); \
+        const float4 *src_ = reinterpret_cast<const float4 *>(xt + (ok_ ? tok_ : 0) * R + khalf * 4); \
         _Pragma("unroll") for (int s_ = 0; s_ < 2 * KS; ++s_) {                                   \
-            DST[s_] = src_[(s_ >> 1) * 4 + (s_ & 1)];                                             \
+            DST[s_] = src_[(s_ >> 1) * 4 + (s_ & 1) * 2];                                         \
             if (!ok_) DST[s_] = make_float4(0.f, 0.f, 0.f, 0.f);                                  \
         }                                                                                         \
     } while (0)
     if (t_begin + wave * 32 < t_end) KVC_LOAD_X(t_begin + wave * 32, xc);
     for (int64_t t0 = t_begin + wave * 32; t0 < t_end; t0 += wstep) {
         if (t0 + wstep < t_end) KVC_LOAD_X(t0 + wstep, xn);  // next step in flight
-        const int64_t tok = t0 + col;
-        const bool ok = tok < t_end;
         u32x4 bh[KS], bl[KS];
 #pragma unroll
         for (int s = 0; s < KS; ++s) {
@@ -461,18 +574,11 @@ __global__ __launch_bounds__(256) void reconstruct_kernel(const float *__restric
             for (int s = 0; s < KS; ++s) {
                 const u32x4 ah = ufr[((cb * KS + s) * 2 + 0) * 64 + lane];
                 const u32x4 al = ufr[((cb * KS + s) * 2 + 1) * 64 + lane];
-                // X~ as the A operand (its registers are laid out as B's): D[token][channel]
-                acc = mfma32x32x16(bh[s], ah, acc);
-                acc = mfma32x32x16(bh[s], al, acc);
-                acc = mfma32x32x16(bl[s], ah, acc);
+                acc = recon_mfma(bh[s], ah, acc);
+                acc = recon_mfma(bh[s], al, acc);
+                acc = recon_mfma(bl[s], ah, acc);
             }
-            // lane (col, khalf) holds channel cb*32+col of tokens 8(j/4) + 4khalf + j%4:
-            // each store writes two 128-byte row segments
-#pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const int64_t tj = t0 + (j >> 2) * 8 + khalf * 4 + (j & 3);
-                if (tj < t_end) xh[tj * kHeadDim + cb * 32 + col] = acc[j];
-            }
+            recon_store(xh, t0, t_end, cb, col, khalf, acc);
         }
 #pragma unroll
         for (int s = 0; s < 2 * KS; ++s) xc[s] = xn[s];
@@ -498,20 +604,7 @@ __global__ __launch_bounds__(256) void reconstruct_bf16_kernel(const uint16_t *_
     const int64_t l = slice / (sl.Hkv * sl.B);
     const float *U = Ubase + (l * sl.Hkv + h) * kHeadDim * R;
 
-    for (int p = threadIdx.x; p < 4 * KS * 64; p += blockDim.x) {
-        const int lane = p & 63, fs = p >> 6, s = fs % KS, cb = fs / KS;
-        const int c = cb * 32 + (lane & 31);
-        const int j0 = 16 * s + (lane >> 5) * 8;
-        float x[8];
-        const float4 *src = reinterpret_cast<const float4 *>(U + c * R + j0);
-        const float4 u0 = src[0], u1 = src[1];
-        x[0] = u0.x; x[1] = u0.y; x[2] = u0.z; x[3] = u0.w;
-        x[4] = u1.x; x[5] = u1.y; x[6] = u1.z; x[7] = u1.w;
-        u32x4 hi, lo;
-        split8(x, hi, lo);
-        ufr[((cb * KS + s) * 2 + 0) * 64 + lane] = hi;
-        ufr[((cb * KS + s) * 2 + 1) * 64 + lane] = lo;
-    }
+    stage_recon_u<R>(U, ufr);
     __syncthreads();
 
     const int64_t t_begin = split * sl.per_split;
@@ -521,16 +614,17 @@ __global__ __launch_bounds__(256) void reconstruct_bf16_kernel(const uint16_t *_
     const uint16_t *xt = Xt + slice * sl.S_stride * R;
     uint16_t *xh = Xh + slice * sl.S_stride * kHeadDim;
 
-    // lane (col, khalf) holds ranks 16s + 8khalf .. +8 of token t0 + col: one 16-byte load per k-step
+    // lane (col, khalf) holds ranks recon_rank(s, khalf, 0..7) of token t0 + col: two 8-byte loads per k-step
     const int64_t wstep = (blockDim.x / 64) * 32;
     u32x4 xc[KS], xn[KS];
 #define KVC_LOAD_XB(T0, DST)                                                                     \
     do {                                                                                          \
         const int64_t tok_ = (T0) + col;                                                          \
         const bool ok_ = tok_ < t_end;                                                            \
-        const u32x4 *src_ = reinterpret_cast<const u32x4 *>(xt + (ok_ ? tok_ : 0) * R + khalf * 8); \
+        const uint2 *src_ = reinterpret_cast<const uint2 *>(xt + (ok_ ? tok_ : 0) * R + khalf * 4); \
         _Pragma("unroll") for (int s_ = 0; s_ < KS; ++s_) {                                       \
-            DST[s_] = src_[2 * s_];                                                               \
+            const uint2 p0_ = src_[4 * s_], p1_ = src_[4 * s_ + 2];                               \
+            DST[s_] = u32x4{p0_.x, p0_.y, p1_.x, p1_.y};                                          \
             if (!ok_) DST[s_] = u32x4{0u, 0u, 0u, 0u};                                            \
         }                                                                                         \
     } while (0)
@@ -544,18 +638,10 @@ __global__ __launch_bounds__(256) void reconstruct_bf16_kernel(const uint16_t *_
             for (int s = 0; s < KS; ++s) {
                 const u32x4 ah = ufr[((cb * KS + s) * 2 + 0) * 64 + lane];
                 const u32x4 al = ufr[((cb * KS + s) * 2 + 1) * 64 + lane];
-                acc = mfma32x32x16(xc[s], ah, acc);
-                acc = mfma32x32x16(xc[s], al, acc);
+                acc = recon_mfma(xc[s], ah, acc);
+                acc = recon_mfma(xc[s], al, acc);
             }
-            // lane (col, khalf) holds channel cb*32+col of tokens 8(j/4) + 4khalf + j%4
-#pragma unroll
-            for (int j = 0; j < 16; ++j) {
-                const int64_t tj = t0 + (j >> 2) * 8 + khalf * 4 + (j & 3);
-                const float nb = __shfl_xor(acc[j], 1);  // channel col ^ 1, same token
-                if (!(col & 1) && tj < t_end)
-                    *reinterpret_cast<uint32_t *>(xh + tj * kHeadDim + cb * 32 + col) =
-                        f32_to_bf16_rne(acc[j]) | (f32_to_bf16_rne(nb) << 16);
-            }
+            recon_store(xh, t0, t_end, cb, col, khalf, acc);
         }
 #pragma unroll
         for (int s = 0; s < KS; ++s) xc[s] = xn[s];
@@ -649,40 +735,61 @@ void compress_ws_layout(Ws &ws, const kvc_dims *d, bool with_q) {
 #ifndef KVC_PROJECT_HB
 #define KVC_PROJECT_HB 2
 #endif
-template <int NRB, bool kRowStores, typename OutT>
+// LDS of a projection launch
+size_t project_lds(int NRB, bool rebuild, int nqb, int nterm) {
+    return static_cast<size_t>(NRB * 16 * (rebuild ? 2 : 1) + nqb * 8 * nterm) * kFragBytes;
+}
+
+// The fused reconstruction keeps all of a step's X~ fragments in registers
+// (ranks <= 64) and both U fragment sets in LDS.
+constexpr size_t kMaxLds = 160 * 1024;
+bool rebuild_fusable(int64_t R, int nqb, int nterm) {
+    return R <= 64 && project_lds(static_cast<int>(R / 32), true, nqb, nterm) <= kMaxLds;
+}
+
+template <int NRB, bool kRowStores, bool kRebuild, typename OutT>
 kvc_status launch_project_variant(const uint16_t *X, const float *U, const u32x4 *qfrag, int nqb,
                                   int nterm, const Slices &sl, int64_t G, OutT *Xt, float *err,
-                                  hipStream_t stream) {
+                                  OutT *Xh, hipStream_t stream) {
     constexpr int HB = KVC_PROJECT_HB;
-    const size_t lds = static_cast<size_t>(NRB * 16 + nqb * 8 * nterm) * kFragBytes;
+    const size_t lds = project_lds(NRB, kRebuild, nqb, nterm);
     static bool lds_ok[64];
-    if (allow_large_lds(reinterpret_cast<const void *>(&project_kernel<NRB, HB, kRowStores, OutT>), lds_ok) !=
-        KVC_OK)
+    if (allow_large_lds(reinterpret_cast<const void *>(&project_kernel<NRB, HB, kRowStores, kRebuild, OutT>),
+                        lds_ok) != KVC_OK)
         return KVC_ERR_HIP;
     const int64_t blocks = G * sl.nsplit;
     if (blocks > INT32_MAX) return KVC_ERR_UNSUPPORTED;
-    hipLaunchKernelGGL((project_kernel<NRB, HB, kRowStores, OutT>), dim3(static_cast<unsigned>(blocks)),
-                       dim3(HB == 1 ? 1024 : 512), lds, stream, X, U, qfrag, nqb, nterm, sl, Xt, err);
+    hipLaunchKernelGGL((project_kernel<NRB, HB, kRowStores, kRebuild, OutT>), dim3(static_cast<unsigned>(blocks)),
+                       dim3(HB == 1 ? 1024 : 512), lds, stream, X, U, qfrag, nqb, nterm, sl, Xt, err, Xh);
     return launch_status();
 }
 
+// Xh != nullptr: fused reconstruction (only called when rebuild_fusable)
 template <int NRB, typename OutT>
 kvc_status launch_project(const uint16_t *X, const float *U, const u32x4 *qfrag, int nqb,
                           int nterm, const Slices &sl, int64_t G, OutT *Xt, float *err,
-                          hipStream_t stream) {
-    return nqb > 0 ? launch_project_variant<NRB, false>(X, U, qfrag, nqb, nterm, sl, G, Xt, err, stream)
-                   : launch_project_variant<NRB, true>(X, U, qfrag, nqb, nterm, sl, G, Xt, err, stream);
+                          OutT *Xh, hipStream_t stream) {
+    if constexpr (NRB <= 2) {
+        if (Xh)
+            return launch_project_variant<NRB, false, true>(X, U, qfrag, nqb, nterm, sl, G, Xt, err, Xh,
+                                                            stream);
+    } else {
+        if (Xh) return KVC_ERR_UNSUPPORTED;
+    }
+    return nqb > 0
+               ? launch_project_variant<NRB, false, false>(X, U, qfrag, nqb, nterm, sl, G, Xt, err, Xh, stream)
+               : launch_project_variant<NRB, true, false>(X, U, qfrag, nqb, nterm, sl, G, Xt, err, Xh, stream);
 }
 
 template <typename OutT>
 kvc_status project_dispatch(int64_t R, const uint16_t *X, const float *U, const u32x4 *qfrag,
                             int nqb, int nterm, const Slices &sl, int64_t G, OutT *Xt, float *err,
-                            hipStream_t stream) {
+                            OutT *Xh, hipStream_t stream) {
     switch (R) {
-        case 32: return launch_project<1>(X, U, qfrag, nqb, nterm, sl, G, Xt, err, stream);
-        case 64: return launch_project<2>(X, U, qfrag, nqb, nterm, sl, G, Xt, err, stream);
-        case 96: return launch_project<3>(X, U, qfrag, nqb, nterm, sl, G, Xt, err, stream);
-        case 128: return launch_project<4>(X, U, qfrag, nqb, nterm, sl, G, Xt, err, stream);
+        case 32: return launch_project<1>(X, U, qfrag, nqb, nterm, sl, G, Xt, err, Xh, stream);
+        case 64: return launch_project<2>(X, U, qfrag, nqb, nterm, sl, G, Xt, err, Xh, stream);
+        case 96: return launch_project<3>(X, U, qfrag, nqb, nterm, sl, G, Xt, err, Xh, stream);
+        case 128: return launch_project<4>(X, U, qfrag, nqb, nterm, sl, G, Xt, err, Xh, stream);
     }
     return KVC_ERR_UNSUPPORTED;
 }
@@ -698,12 +805,46 @@ kvc_status launch_reconstruct(const float *Xt, const float *U, const Slices &sl,
 }
 
 template <int NRB>
-kvc_status launch_reconstruct_bf16(const uint16_t *Xt, const float *U, const Slices &sl, int64_t G,
-                                   uint16_t *Xh, hipStream_t stream) {
+kvc_status launch_reconstruct(const uint16_t *Xt, const float *U, const Slices &sl, int64_t G,
+                              uint16_t *Xh, hipStream_t stream) {
     const int64_t blocks = G * sl.nsplit;
     if (blocks > INT32_MAX) return KVC_ERR_UNSUPPORTED;
     hipLaunchKernelGGL(reconstruct_bf16_kernel<NRB>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
                        stream, Xt, U, sl, Xh);
+    return launch_status();
+}
+
+// X^ = X~ U^T for every token (OutT float: fp32 rows; uint16_t: bf16 rows)
+template <typename OutT>
+kvc_status reconstruct_dispatch(const kvc_dims *d, const OutT *Xt, const float *U, int64_t G, OutT *Xh,
+                                hipStream_t stream) {
+    const Slices sl = make_slices(d, 128);
+    switch (d->R) {
+        case 32: return launch_reconstruct<1>(Xt, U, sl, G, Xh, stream);
+        case 64: return launch_reconstruct<2>(Xt, U, sl, G, Xh, stream);
+        case 96: return launch_reconstruct<3>(Xt, U, sl, G, Xh, stream);
+        case 128: return launch_reconstruct<4>(Xt, U, sl, G, Xh, stream);
+    }
+    return KVC_ERR_UNSUPPORTED;
+}
+
+// Anchor rows into X^ (fp32: widened exactly; bf16: copied).  Bounds were
+// checked by the caller; out-of-slice indices are skipped by the kernels.
+kvc_status launch_anchors(const int32_t *idx, const uint16_t *rows, int64_t k, int64_t G, int64_t S,
+                          int64_t S_stride, float *Xh, hipStream_t stream) {
+    const int64_t bps = (k + 15) / 16;
+    if (G * bps > INT32_MAX) return KVC_ERR_UNSUPPORTED;
+    hipLaunchKernelGGL(anchor_scatter_kernel, dim3(static_cast<unsigned>(G * bps)), dim3(256), 0, stream,
+                       idx, rows, k, bps, S, S_stride, Xh);
+    return launch_status();
+}
+
+kvc_status launch_anchors(const int32_t *idx, const uint16_t *rows, int64_t k, int64_t G, int64_t S,
+                          int64_t S_stride, uint16_t *Xh, hipStream_t stream) {
+    const int64_t bps = (k + 15) / 16;
+    if (G * bps > INT32_MAX) return KVC_ERR_UNSUPPORTED;
+    hipLaunchKernelGGL(anchor_copy_bf16_kernel, dim3(static_cast<unsigned>(G * bps)), dim3(256), 0, stream,
+                       idx, rows, k, bps, S, S_stride, Xh);
     return launch_status();
 }
 
@@ -725,21 +866,28 @@ size_t reconstruct_workspace_bytes(const kvc_dims *) { return 0; }
 namespace kvc {
 namespace {
 
+// K_hat == nullptr: compression only.  Otherwise X^ = X~ U^T is also written for
+// every token of K (and of V when given), fused into the projection where it fits
+// (ranks <= 64), else by the stand-alone reconstruction; both give the same bits.
 template <typename OutT>
 kvc_status compress_impl(const kvc_dims *d, const uint16_t *K, const uint16_t *V,
                          const uint16_t *Q_win, const float *U_k, const float *U_v, OutT *K_tilde,
-                         OutT *V_tilde, float *err, void *ws, size_t ws_bytes, hipStream_t stream) {
+                         OutT *V_tilde, float *err, OutT *K_hat, OutT *V_hat, void *ws, size_t ws_bytes,
+                         hipStream_t stream) {
     const bool with_q = Q_win != nullptr;
     kvc_status st = check_dims(d, with_q);
     if (st != KVC_OK) return st;
     if ((Q_win == nullptr) != (err == nullptr)) return KVC_ERR_INVALID_ARGUMENT;
     if ((V == nullptr) != (V_tilde == nullptr) || (V && !U_v)) return KVC_ERR_INVALID_ARGUMENT;
+    if (!K_hat && V_hat) return KVC_ERR_INVALID_ARGUMENT;
+    if (K_hat && (V == nullptr) != (V_hat == nullptr)) return KVC_ERR_INVALID_ARGUMENT;
     const int64_t G = d->L * d->B * d->H_kv;
     if (G == 0 || d->S == 0) return KVC_OK;
     if (!K || !U_k || !K_tilde) return KVC_ERR_INVALID_ARGUMENT;
     if (!aligned(K, 16) || !aligned(U_k, 16) || !aligned(K_tilde, 16) ||
         (V && (!aligned(V, 16) || !aligned(U_v, 16) || !aligned(V_tilde, 16))) ||
-        (with_q && (!aligned(Q_win, 16) || !aligned(err, 4))))
+        (with_q && (!aligned(Q_win, 16) || !aligned(err, 4))) ||
+        (K_hat && !aligned(K_hat, 16)) || (V_hat && !aligned(V_hat, 16)))
         return KVC_ERR_INVALID_ARGUMENT;
     WsSizer sz;
     compress_ws_layout(sz, d, with_q);
@@ -767,10 +915,55 @@ kvc_status compress_impl(const kvc_dims *d, const uint16_t *K, const uint16_t *V
                            static_cast<int>(nq), nqb, nterm, scale, qfrag);
         if ((st = launch_status()) != KVC_OK) return st;
     }
-    st = project_dispatch(d->R, K, U_k, qfrag, nqb, nterm, sl, G, K_tilde, err, stream);
+    // one side (K with its error score, or V): projection, then X^ fused or separate
+    auto side = [&](const uint16_t *X, const float *U, const u32x4 *qf, int nb, int nt, OutT *Xt,
+                    float *e, OutT *Xh) -> kvc_status {
+        if (Xh && !rebuild_fusable(d->R, nb, nt)) {
+            const kvc_status s1 =
+                project_dispatch(d->R, X, U, qf, nb, nt, sl, G, Xt, e, static_cast<OutT *>(nullptr), stream);
+            if (s1 != KVC_OK) return s1;
+            return reconstruct_dispatch(d, static_cast<const OutT *>(Xt), U, G, Xh, stream);
+        }
+        return project_dispatch(d->R, X, U, qf, nb, nt, sl, G, Xt, e, Xh, stream);
+    };
+    st = side(K, U_k, qfrag, nqb, nterm, K_tilde, err, K_hat);
     if (st != KVC_OK) return st;
-    if (V) st = project_dispatch(d->R, V, U_v, nullptr, 0, 0, sl, G, V_tilde, nullptr, stream);
+    if (V) st = side(V, U_v, nullptr, 0, 0, V_tilde, nullptr, V_hat);
     return st;
+}
+
+template <typename OutT>
+kvc_status reconstruct_impl(const kvc_dims *d, const OutT *X_tilde, const float *U, const int32_t *anchor_idx,
+                            const uint16_t *anchor_rows, int64_t k, OutT *X_hat, hipStream_t stream) {
+    kvc_status st = check_dims(d, false);
+    if (st != KVC_OK) return st;
+    if (k < 0 || k > d->S) return KVC_ERR_INVALID_ARGUMENT;
+    if ((k > 0) && (!anchor_idx || !anchor_rows)) return KVC_ERR_INVALID_ARGUMENT;
+    const int64_t G = d->L * d->B * d->H_kv;
+    if (G == 0 || d->S == 0) return KVC_OK;
+    if (!X_tilde || !U || !X_hat || !aligned(X_tilde, 16) || !aligned(U, 16) || !aligned(X_hat, 16))
+        return KVC_ERR_INVALID_ARGUMENT;
+    if (k > 0 && (!aligned(anchor_idx, 4) || !aligned(anchor_rows, 16)))
+        return KVC_ERR_INVALID_ARGUMENT;
+    st = reconstruct_dispatch(d, X_tilde, U, G, X_hat, stream);
+    if (st != KVC_OK || k == 0) return st;
+    return launch_anchors(anchor_idx, anchor_rows, k, G, d->S, stride_of(d), X_hat, stream);
+}
+
+template <typename OutT>
+kvc_status place_anchors_impl(const kvc_dims *d, const int32_t *anchor_idx, const uint16_t *anchor_rows,
+                              int64_t k, OutT *X_hat, hipStream_t stream) {
+    if (!d) return KVC_ERR_INVALID_ARGUMENT;
+    if (d->L < 0 || d->B < 0 || d->H_kv <= 0 || d->S < 0 || d->D <= 0) return KVC_ERR_INVALID_ARGUMENT;
+    if (d->S_stride != 0 && d->S_stride < d->S) return KVC_ERR_INVALID_ARGUMENT;
+    if (d->D != kHeadDim) return KVC_ERR_UNSUPPORTED;
+    if (k < 0 || k > d->S) return KVC_ERR_INVALID_ARGUMENT;
+    const int64_t G = d->L * d->B * d->H_kv;
+    if (G == 0 || d->S == 0 || k == 0) return KVC_OK;
+    if (!anchor_idx || !anchor_rows || !X_hat || !aligned(anchor_idx, 4) || !aligned(anchor_rows, 16) ||
+        !aligned(X_hat, 16))
+        return KVC_ERR_INVALID_ARGUMENT;
+    return launch_anchors(anchor_idx, anchor_rows, k, G, d->S, stride_of(d), X_hat, stream);
 }
 
 }  // namespace
@@ -781,7 +974,8 @@ extern "C" kvc_status kvc_lowrank_compress(const kvc_dims *d, const uint16_t *K,
                                            const float *U_v, float *K_tilde, float *V_tilde,
                                            float *err, void *ws, size_t ws_bytes,
                                            hipStream_t stream) {
-    return kvc::compress_impl(d, K, V, Q_win, U_k, U_v, K_tilde, V_tilde, err, ws, ws_bytes, stream);
+    return kvc::compress_impl(d, K, V, Q_win, U_k, U_v, K_tilde, V_tilde, err, static_cast<float *>(nullptr),
+                              static_cast<float *>(nullptr), ws, ws_bytes, stream);
 }
 
 extern "C" kvc_status kvc_lowrank_compress_bf16(const kvc_dims *d, const uint16_t *K, const uint16_t *V,
@@ -789,71 +983,58 @@ extern "C" kvc_status kvc_lowrank_compress_bf16(const kvc_dims *d, const uint16_
                                                 const float *U_v, uint16_t *K_tilde,
                                                 uint16_t *V_tilde, float *err, void *ws,
                                                 size_t ws_bytes, hipStream_t stream) {
-    return kvc::compress_impl(d, K, V, Q_win, U_k, U_v, K_tilde, V_tilde, err, ws, ws_bytes, stream);
+    return kvc::compress_impl(d, K, V, Q_win, U_k, U_v, K_tilde, V_tilde, err, static_cast<uint16_t *>(nullptr),
+                              static_cast<uint16_t *>(nullptr), ws, ws_bytes, stream);
+}
+
+extern "C" kvc_status kvc_lowrank_compress_reconstruct(const kvc_dims *d, const uint16_t *K,
+                                                       const uint16_t *V, const uint16_t *Q_win,
+                                                       const float *U_k, const float *U_v, float *K_tilde,
+                                                       float *V_tilde, float *err, float *K_hat,
+                                                       float *V_hat, void *ws, size_t ws_bytes,
+                                                       hipStream_t stream) {
+    if (!K_hat) return KVC_ERR_INVALID_ARGUMENT;
+    return kvc::compress_impl(d, K, V, Q_win, U_k, U_v, K_tilde, V_tilde, err, K_hat, V_hat, ws, ws_bytes,
+                              stream);
+}
+
+extern "C" kvc_status kvc_lowrank_compress_reconstruct_bf16(const kvc_dims *d, const uint16_t *K,
+                                                            const uint16_t *V, const uint16_t *Q_win,
+                                                            const float *U_k, const float *U_v,
+                                                            uint16_t *K_tilde, uint16_t *V_tilde, float *err,
+                                                            uint16_t *K_hat, uint16_t *V_hat, void *ws,
+                                                            size_t ws_bytes, hipStream_t stream) {
+    if (!K_hat) return KVC_ERR_INVALID_ARGUMENT;
+    return kvc::compress_impl(d, K, V, Q_win, U_k, U_v, K_tilde, V_tilde, err, K_hat, V_hat, ws, ws_bytes,
+                              stream);
 }
 
 extern "C" kvc_status kvc_reconstruct(const kvc_dims *d, const float *X_tilde, const float *U,
                                       const int32_t *anchor_idx, const uint16_t *anchor_rows,
                                       int64_t k, float *X_hat, void *ws, size_t ws_bytes,
                                       hipStream_t stream) {
-    using namespace kvc;
     (void)ws;
     (void)ws_bytes;
-    kvc_status st = check_dims(d, false);
-    if (st != KVC_OK) return st;
-    if (k < 0 || k > d->S) return KVC_ERR_INVALID_ARGUMENT;
-    if ((k > 0) && (!anchor_idx || !anchor_rows)) return KVC_ERR_INVALID_ARGUMENT;
-    const int64_t G = d->L * d->B * d->H_kv;
-    if (G == 0 || d->S == 0) return KVC_OK;
-    if (!X_tilde || !U || !X_hat || !aligned(X_tilde, 16) || !aligned(U, 16) || !aligned(X_hat, 16))
-        return KVC_ERR_INVALID_ARGUMENT;
-    if (k > 0 && (!aligned(anchor_idx, 4) || !aligned(anchor_rows, 16)))
-        return KVC_ERR_INVALID_ARGUMENT;
-    const Slices sl = make_slices(d, 128);
-    switch (d->R) {
-        case 32: st = launch_reconstruct<1>(X_tilde, U, sl, G, X_hat, stream); break;
-        case 64: st = launch_reconstruct<2>(X_tilde, U, sl, G, X_hat, stream); break;
-        case 96: st = launch_reconstruct<3>(X_tilde, U, sl, G, X_hat, stream); break;
-        case 128: st = launch_reconstruct<4>(X_tilde, U, sl, G, X_hat, stream); break;
-        default: return KVC_ERR_UNSUPPORTED;
-    }
-    if (st != KVC_OK || k == 0) return st;
-    const int64_t bps = (k + 15) / 16;
-    if (G * bps > INT32_MAX) return KVC_ERR_UNSUPPORTED;
-    hipLaunchKernelGGL(anchor_scatter_kernel, dim3(static_cast<unsigned>(G * bps)), dim3(256), 0,
-                       stream, anchor_idx, anchor_rows, k, bps, d->S, sl.S_stride, X_hat);
-    return launch_status();
+    return kvc::reconstruct_impl(d, X_tilde, U, anchor_idx, anchor_rows, k, X_hat, stream);
 }
 
 extern "C" kvc_status kvc_reconstruct_bf16(const kvc_dims *d, const uint16_t *X_tilde, const float *U,
                                            const int32_t *anchor_idx, const uint16_t *anchor_rows,
                                            int64_t k, uint16_t *X_hat, void *ws, size_t ws_bytes,
                                            hipStream_t stream) {
-    using namespace kvc;
     (void)ws;
     (void)ws_bytes;
-    kvc_status st = check_dims(d, false);
-    if (st != KVC_OK) return st;
-    if (k < 0 || k > d->S) return KVC_ERR_INVALID_ARGUMENT;
-    if ((k > 0) && (!anchor_idx || !anchor_rows)) return KVC_ERR_INVALID_ARGUMENT;
-    const int64_t G = d->L * d->B * d->H_kv;
-    if (G == 0 || d->S == 0) return KVC_OK;
-    if (!X_tilde || !U || !X_hat || !aligned(X_tilde, 16) || !aligned(U, 16) || !aligned(X_hat, 16))
-        return KVC_ERR_INVALID_ARGUMENT;
-    if (k > 0 && (!aligned(anchor_idx, 4) || !aligned(anchor_rows, 16)))
-        return KVC_ERR_INVALID_ARGUMENT;
-    const Slices sl = make_slices(d, 128);
-    switch (d->R) {
-        case 32: st = launch_reconstruct_bf16<1>(X_tilde, U, sl, G, X_hat, stream); break;
-        case 64: st = launch_reconstruct_bf16<2>(X_tilde, U, sl, G, X_hat, stream); break;
-        case 96: st = launch_reconstruct_bf16<3>(X_tilde, U, sl, G, X_hat, stream); break;
-        case 128: st = launch_reconstruct_bf16<4>(X_tilde, U, sl, G, X_hat, stream); break;
-        default: return KVC_ERR_UNSUPPORTED;
-    }
-    if (st != KVC_OK || k == 0) return st;
-    const int64_t bps = (k + 15) / 16;
-    if (G * bps > INT32_MAX) return KVC_ERR_UNSUPPORTED;
-    hipLaunchKernelGGL(anchor_copy_bf16_kernel, dim3(static_cast<unsigned>(G * bps)), dim3(256), 0,
-                       stream, anchor_idx, anchor_rows, k, bps, d->S, sl.S_stride, X_hat);
-    return launch_status();
+    return kvc::reconstruct_impl(d, X_tilde, U, anchor_idx, anchor_rows, k, X_hat, stream);
+}
+
+extern "C" kvc_status kvc_place_anchors(const kvc_dims *d, const int32_t *anchor_idx,
+                                        const uint16_t *anchor_rows, int64_t k, float *X_hat,
+                                        hipStream_t stream) {
+    return kvc::place_anchors_impl(d, anchor_idx, anchor_rows, k, X_hat, stream);
+}
+
+extern "C" kvc_status kvc_place_anchors_bf16(const kvc_dims *d, const int32_t *anchor_idx,
+                                             const uint16_t *anchor_rows, int64_t k, uint16_t *X_hat,
+                                             hipStream_t stream) {
+    return kvc::place_anchors_impl(d, anchor_idx, anchor_rows, k, X_hat, stream);
 }

@@ -279,8 +279,6 @@ __global__ __launch_bounds__(256) void oja_step_qr_lds_kernel(float *__restrict_
     double *Wd = Ud + kHeadDim * ld;                   // [128][R] (>= [128][kCChunk])
     float *Mf = reinterpret_cast<float *>(Wd + kHeadDim * R);  // [R][R+1]
     double *vs = reinterpret_cast<double *>(Mf + R * ld + (R * ld) % 2);  // [128]
-    double *ds = vs + kHeadDim;                        // [128]
-    double *red = ds + kHeadDim;                       // [2]
     const int64_t lh = blockIdx.x;
     const int tid = threadIdx.x;
     float *Ug = U + lh * kHeadDim * R;

@@ -25,7 +25,8 @@ EXPORTED = ("kvc_abi_version", "kvc_status_str", "kvc_workspace_bytes", "kvc_sco
             "kvc_score_l2_windowed", "kvc_score_centroid", "kvc_layer_budgets", "kvc_topk_compact",
             "kvc_topk_compact_ragged", "kvc_cluster_summaries", "kvc_refine_risk", "kvc_lowrank_compress",
             "kvc_lowrank_compress_bf16", "kvc_oja_update", "kvc_reconstruct", "kvc_reconstruct_bf16",
-            "kvc_decode_append")
+            "kvc_decode_append", "kvc_lowrank_compress_reconstruct",
+            "kvc_lowrank_compress_reconstruct_bf16", "kvc_place_anchors", "kvc_place_anchors_bf16")
 
 
 class KvcError(RuntimeError):
@@ -71,6 +72,10 @@ def load(path: str = LIB_PATH):
                 "kvc_reconstruct": [DP, P, P, P, P, I64, P, P, SZ, P],
                 "kvc_reconstruct_bf16": [DP, P, P, P, P, I64, P, P, SZ, P],
                 "kvc_decode_append": [DP, I64, I64, I64, P, P, P, P, P, P, P, P, P],
+                "kvc_lowrank_compress_reconstruct": [DP, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
+                "kvc_lowrank_compress_reconstruct_bf16": [DP, P, P, P, P, P, P, P, P, P, P, P, SZ, P],
+                "kvc_place_anchors": [DP, P, P, I64, P, P],
+                "kvc_place_anchors_bf16": [DP, P, P, I64, P, P],
             }
             for name, a in sigs.items():
                 fn = getattr(lib, name)
@@ -291,6 +296,69 @@ def kvc_lowrank_compress_bf16(K, V, Q_win, U_k, U_v, L, B, H_kv, S=None, K_tilde
     """As kvc_lowrank_compress, with K~/V~ stored as bf16 [L*B*H_kv, S_stride, R]."""
     return _compress("kvc_lowrank_compress_bf16", torch.bfloat16, K, V, Q_win, U_k, U_v, L, B, H_kv, S,
                      K_tilde, V_tilde, err)
+
+
+def _compress_reconstruct(name, dtype, K, V, Q_win, U_k, U_v, L, B, H_kv, S, K_tilde, V_tilde, err,
+                          K_hat, V_hat):
+    lib = load()
+    G, stride, D = K.shape
+    S = stride if S is None else S
+    R = U_k.shape[-1]
+    H_q, W_q = (Q_win.shape[2], Q_win.shape[3]) if Q_win is not None else (0, 0)
+    dev = K.device
+    if K_tilde is None:
+        K_tilde = torch.empty((G, stride, R), dtype=dtype, device=dev)
+    if V is not None and V_tilde is None:
+        V_tilde = torch.empty((G, stride, R), dtype=dtype, device=dev)
+    if Q_win is not None and err is None:
+        err = torch.empty((G, stride), dtype=torch.float32, device=dev)
+    if K_hat is None:
+        K_hat = torch.empty((G, stride, D), dtype=dtype, device=dev)
+    if V is not None and V_hat is None:
+        V_hat = torch.empty((G, stride, D), dtype=dtype, device=dev)
+    d = _dims(L, B, H_kv, H_q, S, stride, D, R, W_q)
+    nb = workspace_bytes(OP_LOWRANK_COMPRESS, d)
+    ws = workspace(nb, dev.index)
+    _check(name, getattr(lib, name)(ctypes.byref(d), _ptr(K), _ptr(V), _ptr(Q_win), _ptr(U_k),
+                                    _ptr(U_v), _ptr(K_tilde), _ptr(V_tilde), _ptr(err), _ptr(K_hat),
+                                    _ptr(V_hat), _ptr(ws), nb, _stream()))
+    return K_tilde, V_tilde, err, K_hat, V_hat
+
+
+def kvc_lowrank_compress_reconstruct(K, V, Q_win, U_k, U_v, L, B, H_kv, S=None, K_tilde=None,
+                                     V_tilde=None, err=None, K_hat=None, V_hat=None):
+    """As kvc_lowrank_compress, plus K^ = K~ U_k^T and V^ = V~ U_v^T (fp32 [G, S_stride, D])
+    for every token, anchors not placed.  Returns (K_tilde, V_tilde, err, K_hat, V_hat)."""
+    return _compress_reconstruct("kvc_lowrank_compress_reconstruct", torch.float32, K, V, Q_win, U_k,
+                                 U_v, L, B, H_kv, S, K_tilde, V_tilde, err, K_hat, V_hat)
+
+
+def kvc_lowrank_compress_reconstruct_bf16(K, V, Q_win, U_k, U_v, L, B, H_kv, S=None, K_tilde=None,
+                                          V_tilde=None, err=None, K_hat=None, V_hat=None):
+    """bf16 storage form of kvc_lowrank_compress_reconstruct (K~, V~, K^, V^ bf16)."""
+    return _compress_reconstruct("kvc_lowrank_compress_reconstruct_bf16", torch.bfloat16, K, V, Q_win,
+                                 U_k, U_v, L, B, H_kv, S, K_tilde, V_tilde, err, K_hat, V_hat)
+
+
+def _place_anchors(name, anchor_idx, anchor_rows, L, B, H_kv, S, X_hat):
+    lib = load()
+    G, stride, D = X_hat.shape
+    S = stride if S is None else S
+    k = anchor_idx.shape[1]
+    d = _dims(L, B, H_kv, 0, S, stride, D, 0, 0)
+    _check(name, getattr(lib, name)(ctypes.byref(d), _ptr(anchor_idx), _ptr(_bits(anchor_rows)), k,
+                                    _ptr(X_hat), _stream()))
+    return X_hat
+
+
+def kvc_place_anchors(anchor_idx, anchor_rows, L, B, H_kv, X_hat, S=None):
+    """anchor_idx int32 [G, k], anchor_rows bf16 [G, k, D] -> rows of X_hat fp32 [G, S_stride, D]."""
+    return _place_anchors("kvc_place_anchors", anchor_idx, anchor_rows, L, B, H_kv, S, X_hat)
+
+
+def kvc_place_anchors_bf16(anchor_idx, anchor_rows, L, B, H_kv, X_hat, S=None):
+    """As kvc_place_anchors into a bf16 X_hat (rows copied bit for bit)."""
+    return _place_anchors("kvc_place_anchors_bf16", anchor_idx, anchor_rows, L, B, H_kv, S, X_hat)
 
 
 def kvc_oja_update(U, X, pool, eta, L, B, H_kv, N=None):

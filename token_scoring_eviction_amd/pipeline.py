@@ -89,21 +89,33 @@ def alloc_hybrid(G, S_cap, R, D=128, device="cuda", max_anchor=None, with_hat=Tr
 
 
 def hybrid_pass(K, V, Q_win, U_k, U_v, L, B, H_kv, S, st: HybridState, anchor_percent=5,
-                reconstruct=True):
+                reconstruct=True, fused=True):
     """Compress all S tokens, score them, keep ceil(p%) anchors at full rank and
-    (optionally) rebuild K^, V^.  K, V: bf16 [G, S_cap, 128] caches (S <= S_cap)."""
+    (optionally) rebuild K^, V^.  K, V: bf16 [G, S_cap, 128] caches (S <= S_cap).
+    fused: K^, V^ come out of the compression launch (X~ is not read back) and
+    only the anchor rows are written afterwards; the result is the same, bit
+    for bit, as compress -> select -> reconstruct."""
     G = K.shape[0]
     k = anchor_count(S, anchor_percent)
     if k > st.idx.shape[1]:
         raise ValueError("anchor buffers hold %d rows, %d needed" % (st.idx.shape[1], k))
     bf16 = st.Kt.dtype == torch.bfloat16
-    compress = kvc.kvc_lowrank_compress_bf16 if bf16 else kvc.kvc_lowrank_compress
-    rebuild = kvc.kvc_reconstruct_bf16 if bf16 else kvc.kvc_reconstruct
-    compress(K, V, Q_win, U_k, U_v, L, B, H_kv, S=S, K_tilde=st.Kt, V_tilde=st.Vt, err=st.err)
     # anchors of this pass: the first k rows of the (contiguous) anchor buffers
     idx = st.idx.view(-1)[:G * k].view(G, k)
     Ka = st.K_anchor.view(-1)[:G * k * K.shape[2]].view(G, k, K.shape[2])
     Va = st.V_anchor.view(-1)[:G * k * K.shape[2]].view(G, k, K.shape[2])
+    if reconstruct and fused:
+        both = kvc.kvc_lowrank_compress_reconstruct_bf16 if bf16 else kvc.kvc_lowrank_compress_reconstruct
+        place = kvc.kvc_place_anchors_bf16 if bf16 else kvc.kvc_place_anchors
+        both(K, V, Q_win, U_k, U_v, L, B, H_kv, S=S, K_tilde=st.Kt, V_tilde=st.Vt, err=st.err,
+             K_hat=st.Khat, V_hat=st.Vhat)
+        kvc.kvc_topk_compact(st.err, k, K, V, S=S, idx_out=idx, K_out=Ka, V_out=Va)
+        place(idx, Ka, L, B, H_kv, st.Khat, S=S)
+        place(idx, Va, L, B, H_kv, st.Vhat, S=S)
+        return idx, Ka, Va
+    compress = kvc.kvc_lowrank_compress_bf16 if bf16 else kvc.kvc_lowrank_compress
+    rebuild = kvc.kvc_reconstruct_bf16 if bf16 else kvc.kvc_reconstruct
+    compress(K, V, Q_win, U_k, U_v, L, B, H_kv, S=S, K_tilde=st.Kt, V_tilde=st.Vt, err=st.err)
     kvc.kvc_topk_compact(st.err, k, K, V, S=S, idx_out=idx, K_out=Ka, V_out=Va)
     if reconstruct:
         rebuild(st.Kt, U_k, idx, Ka, L, B, H_kv, S=S, X_hat=st.Khat)
