@@ -78,7 +78,8 @@ def parse():
     return ap.parse_args()
 
 
-def copy_reference(mib, reps):
+def time_device_copy(mib, reps):
+    """A plain device-to-device copy of MIB MiB: (ms per copy, GB/s read + write)."""
     import torch
     n = mib << 20
     a = torch.ones(n, dtype=torch.uint8, device="cuda")
@@ -93,7 +94,48 @@ def copy_reference(mib, reps):
     t1.record()
     torch.cuda.synchronize()
     ms = t0.elapsed_time(t1) / reps
-    print(json.dumps({"copy_bytes": n, "ms": ms, "GBs_read_plus_write": 2 * n / ms / 1e6}), flush=True)
+    del a, b
+    return ms, 2 * n / ms / 1e6
+
+
+def copy_reference(mib, reps):
+    ms, gbs = time_device_copy(mib, reps)
+    print(json.dumps({"copy_bytes": mib << 20, "ms": ms, "GBs_read_plus_write": gbs}), flush=True)
+
+
+def host_cpu():
+    """Model name of the host CPU and the threads the OS reports."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return model, os.cpu_count()
+
+
+def run_cpu_baseline(cpu, seconds):
+    """The oracle on one host core: this thread is pinned to the core it runs on
+    for the sample, then its affinity is restored."""
+    before = None
+    try:
+        before = os.sched_getaffinity(0)
+        core = sorted(before)[0]
+        os.sched_setaffinity(0, {core})
+    except (AttributeError, OSError):
+        core = None
+    try:
+        n, t, sample = cpu(seconds)
+    finally:
+        if before is not None:
+            os.sched_setaffinity(0, before)
+    model, threads = host_cpu()
+    return {"value": n / t, "unit": "head-tokens/s", "cores": 1, "kind": "oracle",
+            "sample": "%s, %.1f s" % (sample, t), "pinned_core": core, "host_cpu": model,
+            "host_threads": threads}
 
 
 class Op:
@@ -422,10 +464,11 @@ def main():
     line["step_hbm"] = {"algorithmic_bytes": algo, "GBs": algo / ms_step / 1e6,
                         "frac": algo / ms_step / 1e6 / HBM_PEAK_GBS}
     line["ops"] = per_op
+    # context for the fraction: what a plain 1 GiB device copy reaches on this GPU
+    copy_ms, copy_gbs = time_device_copy(1024, 10)
+    line["context"] = {"device_copy_GBs": copy_gbs, "device_copy_frac": copy_gbs / HBM_PEAK_GBS}
     if not args.no_cpu_baseline:
-        n, t, sample = cpu(args.cpu_seconds)
-        line["cpu_baseline"] = {"value": n / t, "unit": "head-tokens/s", "cores": 1, "kind": "oracle",
-                                "sample": "%s, %.1f s" % (sample, t)}
+        line["cpu_baseline"] = run_cpu_baseline(cpu, args.cpu_seconds)
     print(json.dumps(line), flush=True)
 
 
