@@ -158,14 +158,21 @@ constexpr size_t kPrepLds = static_cast<size_t>(kHeadDim) * kPrepStride * sizeof
                             static_cast<size_t>(kHeadDim) * kPrepStride * sizeof(float) +
                             static_cast<size_t>(kHeadDim) * kPrepQStride * sizeof(uint16_t);
 
-// One workgroup per slice, U taken in chunks of 64 columns:
-//   phase 1  T[q][j] = sum_c Q[q][c] U[c][j]        (thread tile 4 queries x 8 columns)
-//   phase 2  P[q][c] += sum_j T[q][j] U[c][j]       (thread tile 4 queries x 16 channels,
+// One workgroup of NT threads per slice, U taken in chunks of 64 columns:
+//   phase 1  T[q][j] = sum_c Q[q][c] U[c][j]        (thread tile 4 queries x JW columns)
+//   phase 2  P[q][c] += sum_j T[q][j] U[c][j]       (thread tile 4 queries x CW channels,
 //                                                    accumulated in registers over chunks)
 // then Q''[q][c] = scale * (Q[q][c] - P[q][c]).  Everything is fp64 (bf16 x fp32
 // products are exact in fp64).  LDS strides are padded so that the rows a wave
-// reads at one column fall in distinct banks.
-__global__ __launch_bounds__(256) void prep_query_kernel(const uint16_t *__restrict__ Q,
+// reads at one column fall in distinct banks.  The LDS footprint allows one
+// workgroup per CU, so NT sets the waves per SIMD: 512 threads (two per SIMD,
+// 128 VGPRs) took 0.37 ms for 1024 slices where 256 threads took 0.52 ms.
+#ifndef KVC_PREP_THREADS
+#define KVC_PREP_THREADS 512
+#endif
+constexpr int kPrepThreads = KVC_PREP_THREADS;
+template <int NT>
+__global__ __launch_bounds__(NT) void prep_query_kernel(const uint16_t *__restrict__ Q,
                                                          const float *__restrict__ Uk, int64_t B,
                                                          int64_t Hkv, int64_t Hq, int64_t Wq,
                                                          int R, int nq, int nqb, int nterm,
@@ -191,15 +198,18 @@ __global__ __launch_bounds__(256) void prep_query_kernel(const uint16_t *__restr
     auto qval = [&](int q, int c) {
         return static_cast<double>(__uint_as_float(static_cast<uint32_t>(Qs[q * kPrepQStride + c]) << 16));
     };
-    // phase-1 tile: columns j = jg + 8 jj, queries 4 qg .. 4 qg + 3
-    const int jg = tid & 7, qg1 = tid >> 3;
-    // phase-2 tile: channels 16 cg .. 16 cg + 15, queries 4 qg .. 4 qg + 3
-    const int cg = tid & 7, qg2 = tid >> 3;
-    double P[4][16];
+    constexpr int GROUPS = NT / 32;             // column / channel groups (32 query groups of 4)
+    constexpr int JW = kPrepJ / GROUPS;         // columns per thread in phase 1
+    constexpr int CW = kHeadDim / GROUPS;       // channels per thread in phase 2
+    // phase-1 tile: columns j = jg + GROUPS jj, queries 4 qg .. 4 qg + 3
+    const int jg = tid % GROUPS, qg1 = tid / GROUPS;
+    // phase-2 tile: channels CW cg .. CW cg + CW - 1, queries 4 qg .. 4 qg + 3
+    const int cg = tid % GROUPS, qg2 = tid / GROUPS;
+    double P[4][CW];
 #pragma unroll
     for (int a = 0; a < 4; ++a)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) P[a][e] = 0.0;
+        for (int e = 0; e < CW; ++e) P[a][e] = 0.0;
 
     for (int j0 = 0; j0 < R; j0 += kPrepJ) {
         const int jn = min(kPrepJ, R - j0);  // 32 or 64
@@ -210,43 +220,43 @@ __global__ __launch_bounds__(256) void prep_query_kernel(const uint16_t *__restr
         }
         __syncthreads();
         if (4 * qg1 < nq) {
-            // columns jg + 8 jj for jj < jn / 8
-            double t[4][8];
+            // columns jg + GROUPS jj for jj < jn / GROUPS
+            double t[4][JW];
 #pragma unroll
             for (int a = 0; a < 4; ++a)
 #pragma unroll
-                for (int jj = 0; jj < 8; ++jj) t[a][jj] = 0.0;
-            const int nj = jn / 8;
+                for (int jj = 0; jj < JW; ++jj) t[a][jj] = 0.0;
+            const int nj = jn / GROUPS;
             for (int c = 0; c < kHeadDim; ++c) {
-                double qv[4], uv[8];
+                double qv[4], uv[JW];
 #pragma unroll
                 for (int a = 0; a < 4; ++a) qv[a] = qval(4 * qg1 + a, c);
 #pragma unroll
-                for (int jj = 0; jj < 8; ++jj)
-                    uv[jj] = jj < nj ? static_cast<double>(Uc[c * kPrepStride + jg + 8 * jj]) : 0.0;
+                for (int jj = 0; jj < JW; ++jj)
+                    uv[jj] = jj < nj ? static_cast<double>(Uc[c * kPrepStride + jg + GROUPS * jj]) : 0.0;
 #pragma unroll
                 for (int a = 0; a < 4; ++a)
 #pragma unroll
-                    for (int jj = 0; jj < 8; ++jj) t[a][jj] = fma(qv[a], uv[jj], t[a][jj]);
+                    for (int jj = 0; jj < JW; ++jj) t[a][jj] = fma(qv[a], uv[jj], t[a][jj]);
             }
 #pragma unroll
             for (int a = 0; a < 4; ++a)
 #pragma unroll
-                for (int jj = 0; jj < 8; ++jj)
-                    if (jj < nj) Ts[(4 * qg1 + a) * kPrepStride + jg + 8 * jj] = t[a][jj];
+                for (int jj = 0; jj < JW; ++jj)
+                    if (jj < nj) Ts[(4 * qg1 + a) * kPrepStride + jg + GROUPS * jj] = t[a][jj];
         }
         __syncthreads();
         if (4 * qg2 < nq) {
             for (int j = 0; j < jn; ++j) {
-                double tv[4], uv[16];
+                double tv[4], uv[CW];
 #pragma unroll
                 for (int a = 0; a < 4; ++a) tv[a] = Ts[(4 * qg2 + a) * kPrepStride + j];
 #pragma unroll
-                for (int e = 0; e < 16; ++e) uv[e] = static_cast<double>(Uc[(16 * cg + e) * kPrepStride + j]);
+                for (int e = 0; e < CW; ++e) uv[e] = static_cast<double>(Uc[(CW * cg + e) * kPrepStride + j]);
 #pragma unroll
                 for (int a = 0; a < 4; ++a)
 #pragma unroll
-                    for (int e = 0; e < 16; ++e) P[a][e] = fma(tv[a], uv[e], P[a][e]);
+                    for (int e = 0; e < CW; ++e) P[a][e] = fma(tv[a], uv[e], P[a][e]);
             }
         }
     }
@@ -258,14 +268,14 @@ __global__ __launch_bounds__(256) void prep_query_kernel(const uint16_t *__restr
         const int q = 4 * qg2 + a;
         if (q >= 32 * nqb) continue;
 #pragma unroll
-        for (int half = 0; half < 2; ++half) {
-            const int c0 = 16 * cg + 8 * half;
+        for (int half = 0; half < CW / 8; ++half) {
+            const int c0 = CW * cg + 8 * half;
             double x[8];
 #pragma unroll
             for (int e = 0; e < 8; ++e) x[e] = q < nq ? scale * (qval(q, c0 + e) - P[a][8 * half + e]) : 0.0;
             u32x4 part[kQParts];
             split8x3_f64(x, part);
-            const int lane = (q & 31) + 32 * half, s = cg;
+            const int lane = (q & 31) + 32 * ((c0 >> 3) & 1), s = c0 >> 4;
             for (int t = 0; t < nterm; ++t) out[(((q >> 5) * 8 + s) * nterm + t) * 64 + lane] = part[t];
         }
     }
@@ -386,14 +396,24 @@ __global__ __launch_bounds__(HB == 1 ? 1024 : 512) void project_kernel(
         }
     };
     const int64_t wstep = (blockDim.x / 64) * TOK;
-    u32x4 b[HB][8], bn[HB][8];
+    // Score launches without the fused reconstruction keep two steps of keys in
+    // flight at ranks 64 and 96 (254 / 250 VGPRs, no spills; the other ranks would
+    // spill): the error-score MFMAs otherwise leave the memory pipe idle (K side
+    // 4.1-4.4 -> 3.95-4.05 ms at 1024 slices x 32768, r = 64).
+    constexpr bool kDepth2 = !kRebuild && !kRowStores && (NRB == 2 || NRB == 3);
+    u32x4 b[HB][8], bn[HB][8], bnn[kDepth2 ? HB : 1][8];
     // X~ of the step as reconstruction operands: [k-step][hb][hi|lo]
     u32x4 xf[kRebuild ? KS : 1][HB][2];
     if (t_begin + wave * TOK < t_end) load_b(t_begin + wave * TOK, b);
+    if (kDepth2 && t_begin + wave * TOK + wstep < t_end) load_b(t_begin + wave * TOK + wstep, bn);
     for (int64_t t0 = t_begin + wave * TOK; t0 < t_end; t0 += wstep) {
         // the next step's keys are requested before this step's contractions (fused:
         // once the projection is done, which keeps fewer registers live)
-        if (!kLatePrefetch && t0 + wstep < t_end) load_b(t0 + wstep, bn);
+        if constexpr (kDepth2) {
+            if (t0 + 2 * wstep < t_end) load_b(t0 + 2 * wstep, bnn);
+        } else {
+            if (!kLatePrefetch && t0 + wstep < t_end) load_b(t0 + wstep, bn);
+        }
         // fused: the score first, so that the keys are dead once the projection
         // has built the X~ fragments (fewer registers live at once)
         if (kRebuild && nqb > 0) score_step(t0, b);
@@ -508,7 +528,10 @@ __global__ __launch_bounds__(HB == 1 ? 1024 : 512) void project_kernel(
 #pragma unroll
         for (int hb = 0; hb < HB; ++hb)
 #pragma unroll
-            for (int s = 0; s < 8; ++s) b[hb][s] = bn[hb][s];
+            for (int s = 0; s < 8; ++s) {
+                b[hb][s] = bn[hb][s];
+                if constexpr (kDepth2) bn[hb][s] = bnn[hb][s];
+            }
     }
 }
 
@@ -905,11 +928,12 @@ kvc_status compress_impl(const kvc_dims *d, const uint16_t *K, const uint16_t *V
         qfrag = cur.take<u32x4>(static_cast<size_t>(G * nqb * 8 * nterm * 64));
         const double scale = 1.0 / (static_cast<double>(nq) * sqrt(static_cast<double>(d->D)));
         static bool lds_ok[64];
-        if (allow_large_lds(reinterpret_cast<const void *>(&prep_query_kernel), lds_ok) != KVC_OK)
+        if (allow_large_lds(reinterpret_cast<const void *>(&prep_query_kernel<kPrepThreads>), lds_ok) != KVC_OK)
             return KVC_ERR_HIP;
         if (G > INT32_MAX) return KVC_ERR_UNSUPPORTED;
         const size_t prep_lds = kPrepLds;
-        hipLaunchKernelGGL(prep_query_kernel, dim3(static_cast<unsigned>(G)), dim3(256), prep_lds, stream,
+        hipLaunchKernelGGL(prep_query_kernel<kPrepThreads>, dim3(static_cast<unsigned>(G)), dim3(kPrepThreads),
+                           prep_lds, stream,
                            Q_win, U_k,
                            d->B, d->H_kv, d->H_q, d->W_q, static_cast<int>(d->R),
                            static_cast<int>(nq), nqb, nterm, scale, qfrag);
