@@ -131,6 +131,48 @@ __device__ __forceinline__ void recon_store(OutT *xh, int64_t t0, int64_t t_end,
     }
 }
 
+// Whole-row stores of bf16 X^ through a per-wave LDS tile of ROWS rows x 256
+// bytes.  The reconstruction block is taken transposed, D[channel][token] (lane
+// (col, khalf) holds channels cb*32 + 8q + 4khalf .. +3 of token col), rounded to
+// bf16 quads and written into the tile; the rows then leave as 16-byte pieces, 16
+// lanes per 256-byte row and four rows per store.  Chunk c of row r sits at chunk
+// position (c ^ r) mod 16, so both the column writes and the row reads spread over
+// the banks without padding.  (Stored straight from the untransposed block, bf16
+// rows go out in 64-byte halves of a cache line: 3.8 ms instead of 2.6 ms for
+// 256 slices x 131072 tokens.)
+template <int ROWS>
+struct Bf16RowTile {
+    static constexpr int kBytes = ROWS * 256;
+    __device__ static int at(int r, int byte) { return r * 256 + ((((byte >> 4) ^ r) & 15) << 4) + (byte & 15); }
+    // tokens row0 .. row0 + ROWS - 1 of channel block cb into the tile
+    __device__ static void put(uint8_t *tile, int lane, int cb, int row0, const f32x16 &acc) {
+        const int col = lane & 31, khalf = lane >> 5;
+        const int r = col - row0;
+        if (r < 0 || r >= ROWS) return;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+            *reinterpret_cast<uint2 *>(tile + at(r, (cb * 32 + 8 * q + 4 * khalf) * 2)) =
+                make_uint2(f32_to_bf16_rne(acc[4 * q]) | (f32_to_bf16_rne(acc[4 * q + 1]) << 16),
+                           f32_to_bf16_rne(acc[4 * q + 2]) | (f32_to_bf16_rne(acc[4 * q + 3]) << 16));
+    }
+    // tile rows r -> X^ rows t0 + r (those below t_end); the wave's tile is free again after it
+    __device__ static void flush(uint16_t *xh, int64_t t0, int64_t t_end, int lane, const uint8_t *tile) {
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+        for (int part = 0; part < ROWS / 4; ++part) {
+            const int r = (lane >> 4) + 4 * part, c = lane & 15;
+            const uint4 v = *reinterpret_cast<const uint4 *>(tile + r * 256 + (((c ^ r) & 15) << 4));
+            const int64_t tok = t0 + r;
+            if (tok < t_end) *reinterpret_cast<uint4 *>(xh + tok * kHeadDim + c * 8) = v;
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    }
+};
+
 struct Slices {
     int64_t B, Hkv, S, S_stride;
     int64_t nsplit;     // blocks per slice
@@ -294,7 +336,7 @@ __global__ __launch_bounds__(NT) void prep_query_kernel(const uint16_t *__restri
 // accumulators, split hi/lo (fp32 storage) or rounded to the stored bf16, are the
 // A operand of the reconstruction in the rank order of recon_rank, so X~ is
 // never read back from memory.
-template <int NRB, int HB, bool kRowStores, bool kRebuild, typename OutT>
+template <int NRB, int HB, bool kRowStores, bool kRebuild, typename OutT, int kStageRows = 0>
 __global__ __launch_bounds__(HB == 1 ? 1024 : 512) void project_kernel(
     const uint16_t *__restrict__ X, const float *__restrict__ Ubase, const u32x4 *__restrict__ qfrag,
     int nqb, int nterm, Slices sl, OutT *__restrict__ Xt, float *__restrict__ err,
@@ -479,10 +521,11 @@ __global__ __launch_bounds__(HB == 1 ? 1024 : 512) void project_kernel(
                     }
                 }
                 // lane (col, khalf) holds ranks rb*32 + 8q + 4khalf .. +4 of token col
+                // (bf16 launches with a 32-row tile write K~ whole-row from the fragments instead)
 #pragma unroll
                 for (int hb = 0; hb < HB; ++hb) {
                     const int64_t tok = t0 + hb * 32 + col;
-                    if (tok < t_end) {
+                    if (kStageRows != 32 && tok < t_end) {
                         OutT *dst = xt + tok * R + rb * 32 + khalf * 4;
 #pragma unroll
                         for (int q = 0; q < 4; ++q) {
@@ -500,11 +543,95 @@ __global__ __launch_bounds__(HB == 1 ? 1024 : 512) void project_kernel(
             }
         }
         if (!kRebuild && nqb > 0) score_step(t0, b);
+        if constexpr (kBf16 && kStageRows == 32) {
+            // bf16 K~ of each 32-token column block from its fragments (the stored
+            // values exactly: ranks recon_rank(ks, khalf, 0..7) of token col) through
+            // the wave's tile as whole 2R-byte rows; chunk c of row r sits at c ^ r
+            constexpr int kRowB = 2 * R, kChunks = R / 8;
+            uint8_t *tile = reinterpret_cast<uint8_t *>(qfr + nqb * 8 * nterm * 64) + wave * Bf16RowTile<32>::kBytes;
+            auto at = [](int r, int byte) {
+                return r * kRowB + ((((byte >> 4) ^ r) & (kChunks - 1)) << 4) + (byte & 15);
+            };
+#pragma unroll
+            for (int hb = 0; hb < HB; ++hb) {
+#pragma unroll
+                for (int ks = 0; ks < KS; ++ks) {
+                    const u32x4 f = xf[ks][hb][0];
+                    *reinterpret_cast<uint2 *>(tile + at(col, (16 * ks + 4 * khalf) * 2)) = make_uint2(f[0], f[1]);
+                    *reinterpret_cast<uint2 *>(tile + at(col, (16 * ks + 8 + 4 * khalf) * 2)) = make_uint2(f[2], f[3]);
+                }
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+                for (int part = 0; part < 32 * kChunks / 64; ++part) {
+                    const int r = lane / kChunks + (64 / kChunks) * part, c = lane % kChunks;
+                    const uint4 v = *reinterpret_cast<const uint4 *>(tile + r * kRowB + (((c ^ r) & (kChunks - 1)) << 4));
+                    const int64_t tok = t0 + hb * 32 + r;
+                    if (tok < t_end) *reinterpret_cast<uint4 *>(xt + tok * R + c * 8) = v;
+                }
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            }
+        }
+        // (a scheduling fence keeps the prefetch's registers out of the phases above)
+        if constexpr (kLatePrefetch) __builtin_amdgcn_sched_barrier(0);
         if (kLatePrefetch && t0 + wstep < t_end) load_b(t0 + wstep, bn);
         if constexpr (kRebuild) {
             // X^[t][c] for channel block cb: hi*hi + hi*lo + lo*hi (fp32 X~), or the
             // stored bf16 X~ times U hi and lo
             OutT *xh = Xh + slice * sl.S_stride * kHeadDim;
+            if constexpr (kBf16 && kStageRows == 32) {
+                // bf16: each 32-token column block, transposed, leaves as whole rows
+                // through the wave's 32-row tile (after the Q'' fragments)
+                uint8_t *tile = reinterpret_cast<uint8_t *>(qfr + nqb * 8 * nterm * 64) +
+                                wave * Bf16RowTile<32>::kBytes;
+#pragma unroll
+                for (int hb = 0; hb < HB; ++hb) {
+#pragma unroll 1
+                    for (int cb = 0; cb < 4; ++cb) {
+                        f32x16 acc = {};
+#pragma unroll
+                        for (int ks = 0; ks < KS; ++ks) {
+                            const u32x4 uh = rfr[((cb * KS + ks) * 2 + 0) * 64 + lane];
+                            const u32x4 ul = rfr[((cb * KS + ks) * 2 + 1) * 64 + lane];
+                            acc = mfma32x32x16(uh, xf[ks][hb][0], acc);  // D[channel][token]
+                            acc = mfma32x32x16(ul, xf[ks][hb][0], acc);
+                        }
+                        Bf16RowTile<32>::put(tile, lane, cb, 0, acc);
+                    }
+                    Bf16RowTile<32>::flush(xh, t0 + hb * 32, t_end, lane, tile);
+                }
+            } else if constexpr (kBf16) {
+                // where LDS is short (the score's fragments): a 16-row tile, the four
+                // channel blocks of a column block held in registers, 16 tokens at a
+                // time (computing each block once per half instead was slower: the
+                // K side at r = 64 went 5.97 -> 6.25 ms)
+                uint8_t *tile = reinterpret_cast<uint8_t *>(qfr + nqb * 8 * nterm * 64) +
+                                wave * Bf16RowTile<16>::kBytes;
+#pragma unroll
+                for (int hb = 0; hb < HB; ++hb) {
+                    f32x16 acc[4];
+#pragma unroll
+                    for (int cb = 0; cb < 4; ++cb) {
+                        acc[cb] = f32x16{};
+#pragma unroll
+                        for (int ks = 0; ks < KS; ++ks) {
+                            const u32x4 uh = rfr[((cb * KS + ks) * 2 + 0) * 64 + lane];
+                            const u32x4 ul = rfr[((cb * KS + ks) * 2 + 1) * 64 + lane];
+                            acc[cb] = mfma32x32x16(uh, xf[ks][hb][0], acc[cb]);  // D[channel][token]
+                            acc[cb] = mfma32x32x16(ul, xf[ks][hb][0], acc[cb]);
+                        }
+                    }
+#pragma unroll
+                    for (int half = 0; half < 2; ++half) {
+#pragma unroll
+                        for (int cb = 0; cb < 4; ++cb) Bf16RowTile<16>::put(tile, lane, cb, 16 * half, acc[cb]);
+                        Bf16RowTile<16>::flush(xh, t0 + hb * 32 + 16 * half, t_end, lane, tile);
+                    }
+                }
+            } else {
 #pragma unroll 1
             for (int cb = 0; cb < 4; ++cb) {
                 f32x16 acc[HB];
@@ -523,6 +650,7 @@ __global__ __launch_bounds__(HB == 1 ? 1024 : 512) void project_kernel(
                 }
 #pragma unroll
                 for (int hb = 0; hb < HB; ++hb) recon_store(xh, t0 + hb * 32, t_end, cb, col, khalf, acc[hb]);
+            }
             }
         }
 #pragma unroll
@@ -610,9 +738,9 @@ __global__ __launch_bounds__(256) void reconstruct_kernel(const float *__restric
 }
 
 // bf16 storage of the compressed cache: X~ bf16 rows are the MFMA operand as they
-// are (exact, no split), A = U hi/lo from LDS (two products), X^ rounded to bf16
-// (nearest even).  Same tiling as reconstruct_kernel; lanes col and col ^ 1 hold
-// adjacent channels of one token and the even lane stores the pair.
+// are (exact, no split), U hi/lo from LDS (two products), X^ rounded to bf16
+// (nearest even).  Same tiling as reconstruct_kernel, with the block taken
+// transposed and a wave step's 32 rows stored whole through Bf16RowTile.
 template <int NRB>
 __global__ __launch_bounds__(256) void reconstruct_bf16_kernel(const uint16_t *__restrict__ Xt,
                                                                const float *__restrict__ Ubase,
@@ -620,6 +748,7 @@ __global__ __launch_bounds__(256) void reconstruct_bf16_kernel(const uint16_t *_
     constexpr int R = 32 * NRB;
     constexpr int KS = R / 16;  // k-steps
     __shared__ u32x4 ufr[4 * KS * 2 * 64];
+    __shared__ __attribute__((aligned(16))) uint8_t stile[4][Bf16RowTile<32>::kBytes];
 
     const int64_t slice = blockIdx.x / sl.nsplit;
     const int64_t split = blockIdx.x % sl.nsplit;
@@ -661,11 +790,12 @@ __global__ __launch_bounds__(256) void reconstruct_bf16_kernel(const uint16_t *_
             for (int s = 0; s < KS; ++s) {
                 const u32x4 ah = ufr[((cb * KS + s) * 2 + 0) * 64 + lane];
                 const u32x4 al = ufr[((cb * KS + s) * 2 + 1) * 64 + lane];
-                acc = recon_mfma(xc[s], ah, acc);
-                acc = recon_mfma(xc[s], al, acc);
+                acc = mfma32x32x16(ah, xc[s], acc);  // D[channel][token]: same products and order
+                acc = mfma32x32x16(al, xc[s], acc);
             }
-            recon_store(xh, t0, t_end, cb, col, khalf, acc);
+            Bf16RowTile<32>::put(stile[wave], lane, cb, 0, acc);
         }
+        Bf16RowTile<32>::flush(xh, t0, t_end, lane, stile[wave]);
 #pragma unroll
         for (int s = 0; s < KS; ++s) xc[s] = xn[s];
     }
@@ -758,44 +888,63 @@ void compress_ws_layout(Ws &ws, const kvc_dims *d, bool with_q) {
 #ifndef KVC_PROJECT_HB
 #define KVC_PROJECT_HB 2
 #endif
-// LDS of a projection launch
-size_t project_lds(int NRB, bool rebuild, int nqb, int nterm) {
-    return static_cast<size_t>(NRB * 16 * (rebuild ? 2 : 1) + nqb * 8 * nterm) * kFragBytes;
+// LDS of a projection launch; the fused bf16 reconstruction adds a staging tile
+// of stage_rows x 256 bytes per wave after the fragments
+constexpr int kProjectWaves = KVC_PROJECT_HB == 1 ? 16 : 8;
+size_t project_lds(int NRB, bool rebuild, int nqb, int nterm, int stage_rows) {
+    return static_cast<size_t>(NRB * 16 * (rebuild ? 2 : 1) + nqb * 8 * nterm) * kFragBytes +
+           (rebuild ? static_cast<size_t>(kProjectWaves) * stage_rows * 256 : 0);
 }
 
 // The fused reconstruction keeps all of a step's X~ fragments in registers
-// (ranks <= 64) and both U fragment sets in LDS.
+// (ranks <= 64) and both U fragment sets in LDS; bf16 also needs a staging tile
+// of at least 16 rows per wave.
 constexpr size_t kMaxLds = 160 * 1024;
-bool rebuild_fusable(int64_t R, int nqb, int nterm) {
-    return R <= 64 && project_lds(static_cast<int>(R / 32), true, nqb, nterm) <= kMaxLds;
+bool rebuild_fusable(int64_t R, int nqb, int nterm, bool bf16) {
+    return R <= 64 && project_lds(static_cast<int>(R / 32), true, nqb, nterm, bf16 ? 16 : 0) <= kMaxLds;
 }
 
-template <int NRB, bool kRowStores, bool kRebuild, typename OutT>
+template <int NRB, bool kRowStores, bool kRebuild, typename OutT, int kStageRows = 0>
 kvc_status launch_project_variant(const uint16_t *X, const float *U, const u32x4 *qfrag, int nqb,
                                   int nterm, const Slices &sl, int64_t G, OutT *Xt, float *err,
                                   OutT *Xh, hipStream_t stream) {
     constexpr int HB = KVC_PROJECT_HB;
-    const size_t lds = project_lds(NRB, kRebuild, nqb, nterm);
+    const size_t lds = project_lds(NRB, kRebuild, nqb, nterm, kStageRows);
     static bool lds_ok[64];
-    if (allow_large_lds(reinterpret_cast<const void *>(&project_kernel<NRB, HB, kRowStores, kRebuild, OutT>),
-                        lds_ok) != KVC_OK)
+    if (allow_large_lds(
+            reinterpret_cast<const void *>(&project_kernel<NRB, HB, kRowStores, kRebuild, OutT, kStageRows>),
+            lds_ok) != KVC_OK)
         return KVC_ERR_HIP;
     const int64_t blocks = G * sl.nsplit;
     if (blocks > INT32_MAX) return KVC_ERR_UNSUPPORTED;
-    hipLaunchKernelGGL((project_kernel<NRB, HB, kRowStores, kRebuild, OutT>), dim3(static_cast<unsigned>(blocks)),
-                       dim3(HB == 1 ? 1024 : 512), lds, stream, X, U, qfrag, nqb, nterm, sl, Xt, err, Xh);
+    hipLaunchKernelGGL((project_kernel<NRB, HB, kRowStores, kRebuild, OutT, kStageRows>),
+                       dim3(static_cast<unsigned>(blocks)), dim3(HB == 1 ? 1024 : 512), lds, stream, X, U, qfrag,
+                       nqb, nterm, sl, Xt, err, Xh);
     return launch_status();
 }
 
-// Xh != nullptr: fused reconstruction (only called when rebuild_fusable)
+// Xh != nullptr: fused reconstruction (only called when rebuild_fusable); bf16
+// stages whole rows through a 32-row tile per wave where LDS allows, else 16 rows
 template <int NRB, typename OutT>
 kvc_status launch_project(const uint16_t *X, const float *U, const u32x4 *qfrag, int nqb,
                           int nterm, const Slices &sl, int64_t G, OutT *Xt, float *err,
                           OutT *Xh, hipStream_t stream) {
     if constexpr (NRB <= 2) {
-        if (Xh)
-            return launch_project_variant<NRB, false, true>(X, U, qfrag, nqb, nterm, sl, G, Xt, err, Xh,
-                                                            stream);
+        if (Xh) {
+            if constexpr (sizeof(OutT) == 2) {
+                // rank 32 fits the 32-row tile at every window size (<= 160 KB)
+                if (NRB == 1 || project_lds(NRB, true, nqb, nterm, 32) <= kMaxLds)
+                    return launch_project_variant<NRB, false, true, OutT, 32>(X, U, qfrag, nqb, nterm, sl, G, Xt,
+                                                                              err, Xh, stream);
+                if constexpr (NRB == 2)
+                    return launch_project_variant<NRB, false, true, OutT, 16>(X, U, qfrag, nqb, nterm, sl, G, Xt,
+                                                                              err, Xh, stream);
+                return KVC_ERR_UNSUPPORTED;
+            } else {
+                return launch_project_variant<NRB, false, true>(X, U, qfrag, nqb, nterm, sl, G, Xt, err, Xh,
+                                                                stream);
+            }
+        }
     } else {
         if (Xh) return KVC_ERR_UNSUPPORTED;
     }
@@ -942,7 +1091,7 @@ kvc_status compress_impl(const kvc_dims *d, const uint16_t *K, const uint16_t *V
     // one side (K with its error score, or V): projection, then X^ fused or separate
     auto side = [&](const uint16_t *X, const float *U, const u32x4 *qf, int nb, int nt, OutT *Xt,
                     float *e, OutT *Xh) -> kvc_status {
-        if (Xh && !rebuild_fusable(d->R, nb, nt)) {
+        if (Xh && !rebuild_fusable(d->R, nb, nt, sizeof(OutT) == 2)) {
             const kvc_status s1 =
                 project_dispatch(d->R, X, U, qf, nb, nt, sl, G, Xt, e, static_cast<OutT *>(nullptr), stream);
             if (s1 != KVC_OK) return s1;
