@@ -442,7 +442,16 @@ __global__ __launch_bounds__(HB == 1 ? 1024 : 512) void project_kernel(
     // flight at ranks 64 and 96 (254 / 250 VGPRs, no spills; the other ranks would
     // spill): the error-score MFMAs otherwise leave the memory pipe idle (K side
     // 4.1-4.4 -> 3.95-4.05 ms at 1024 slices x 32768, r = 64).
-    constexpr bool kDepth2 = !kRebuild && !kRowStores && (NRB == 2 || NRB == 3);
+    // bf16 compression without the reconstruction: the step's 64 K~ rows go through
+    // a per-wave tile of 64 rows x 2R bytes and leave whole (16-byte chunk c of row
+    // r at position c ^ r); stored as 8-byte pieces they were 16-byte segments
+    constexpr bool kStageKt = kBf16 && !kRebuild && kStageRows == 64;
+    constexpr bool kDepth2 = !kRebuild && !kRowStores && !kStageKt && (NRB == 2 || NRB == 3);
+    constexpr int kKtRowB = 2 * R, kKtChunks = R / 8;
+    auto kt_at = [](int r, int byte) {
+        return r * kKtRowB + ((((byte >> 4) ^ r) & (kKtChunks - 1)) << 4) + (byte & 15);
+    };
+    uint8_t *kt_tile = reinterpret_cast<uint8_t *>(qfr + nqb * 8 * nterm * 64) + wave * 64 * kKtRowB;
     u32x4 b[HB][8], bn[HB][8], bnn[kDepth2 ? HB : 1][8];
     // X~ of the step as reconstruction operands: [k-step][hb][hi|lo]
     u32x4 xf[kRebuild ? KS : 1][HB][2];
@@ -499,6 +508,16 @@ __global__ __launch_bounds__(HB == 1 ? 1024 : 512) void project_kernel(
                         }
                     }
             } else {
+                if constexpr (kStageKt) {
+#pragma unroll
+                    for (int hb = 0; hb < HB; ++hb)
+#pragma unroll
+                        for (int q = 0; q < 4; ++q)
+                            *reinterpret_cast<uint2 *>(kt_tile +
+                                                       kt_at(hb * 32 + col, (rb * 32 + 8 * q + 4 * khalf) * 2)) =
+                                make_uint2(f32_to_bf16_rne(a[hb][4 * q]) | (f32_to_bf16_rne(a[hb][4 * q + 1]) << 16),
+                                           f32_to_bf16_rne(a[hb][4 * q + 2]) | (f32_to_bf16_rne(a[hb][4 * q + 3]) << 16));
+                }
                 if constexpr (kRebuild) {
                     // registers 8sp..8sp+7 hold ranks recon_rank(2rb + sp, khalf, 0..7);
                     // the loop stays rolled (fewer live fragments), so the rank block
@@ -521,11 +540,12 @@ __global__ __launch_bounds__(HB == 1 ? 1024 : 512) void project_kernel(
                     }
                 }
                 // lane (col, khalf) holds ranks rb*32 + 8q + 4khalf .. +4 of token col
-                // (bf16 launches with a 32-row tile write K~ whole-row from the fragments instead)
+                // (staged bf16 launches write whole K~ rows from a tile instead)
 #pragma unroll
                 for (int hb = 0; hb < HB; ++hb) {
                     const int64_t tok = t0 + hb * 32 + col;
-                    if (kStageRows != 32 && tok < t_end) {
+                    constexpr bool kPieces = kStageRows == 0 || (kStageRows == 16 && kRebuild);
+                    if (kPieces && tok < t_end) {
                         OutT *dst = xt + tok * R + rb * 32 + khalf * 4;
 #pragma unroll
                         for (int q = 0; q < 4; ++q) {
@@ -541,6 +561,22 @@ __global__ __launch_bounds__(HB == 1 ? 1024 : 512) void project_kernel(
                     }
                 }
             }
+        }
+        if constexpr (kStageKt) {
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+            for (int part = 0; part < kKtChunks; ++part) {
+                const int r = lane / kKtChunks + (64 / kKtChunks) * part, c = lane % kKtChunks;
+                const uint4 v =
+                    *reinterpret_cast<const uint4 *>(kt_tile + r * kKtRowB + (((c ^ r) & (kKtChunks - 1)) << 4));
+                const int64_t tok = t0 + r;  // row hb*32 + col is token t0 + hb*32 + col
+                if (tok < t_end) *reinterpret_cast<uint4 *>(xt + tok * R + c * 8) = v;
+            }
+            __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+            __builtin_amdgcn_wave_barrier();
+            __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
         }
         if (!kRebuild && nqb > 0) score_step(t0, b);
         if constexpr (kBf16 && kStageRows == 32) {
@@ -892,8 +928,12 @@ void compress_ws_layout(Ws &ws, const kvc_dims *d, bool with_q) {
 // of stage_rows x 256 bytes per wave after the fragments
 constexpr int kProjectWaves = KVC_PROJECT_HB == 1 ? 16 : 8;
 size_t project_lds(int NRB, bool rebuild, int nqb, int nterm, int stage_rows) {
+    // rebuild: stage_rows x 256-byte rows of X^; otherwise (bf16 K~ staging, 64):
+    // 64 rows x 2R bytes
+    const size_t per_wave = rebuild ? static_cast<size_t>(stage_rows) * 256
+                                    : static_cast<size_t>(stage_rows) * 2 * 32 * NRB;
     return static_cast<size_t>(NRB * 16 * (rebuild ? 2 : 1) + nqb * 8 * nterm) * kFragBytes +
-           (rebuild ? static_cast<size_t>(kProjectWaves) * stage_rows * 256 : 0);
+           static_cast<size_t>(kProjectWaves) * per_wave;
 }
 
 // The fused reconstruction keeps all of a step's X~ fragments in registers
@@ -947,6 +987,12 @@ kvc_status launch_project(const uint16_t *X, const float *U, const u32x4 *qfrag,
         }
     } else {
         if (Xh) return KVC_ERR_UNSUPPORTED;
+    }
+    if constexpr (sizeof(OutT) == 2 && NRB <= 2) {
+        // bf16 K~ rows staged whole where the tile fits (both sides at ranks <= 64)
+        if (project_lds(NRB, false, nqb, nterm, 64) <= kMaxLds)
+            return launch_project_variant<NRB, false, false, OutT, 64>(X, U, qfrag, nqb, nterm, sl, G, Xt, err, Xh,
+                                                                       stream);
     }
     return nqb > 0
                ? launch_project_variant<NRB, false, false>(X, U, qfrag, nqb, nterm, sl, G, Xt, err, Xh, stream)
