@@ -446,7 +446,12 @@ __global__ __launch_bounds__(HB == 1 ? 1024 : 512) void project_kernel(
     // a per-wave tile of 64 rows x 2R bytes and leave whole (16-byte chunk c of row
     // r at position c ^ r); stored as 8-byte pieces they were 16-byte segments
     constexpr bool kStageKt = kBf16 && !kRebuild && kStageRows == 64;
-    constexpr bool kDepth2 = !kRebuild && !kRowStores && !kStageKt && (NRB == 2 || NRB == 3);
+    // fp32 compression with the score: one 32-token column block at a time, its K~
+    // rows (4R bytes) through a per-wave tile of 32 rows and out whole
+    constexpr bool kStageKtF = !kBf16 && !kRebuild && kStageRows == 32;
+    constexpr int kFRowB = 4 * R, kFChunks = R / 4;
+    constexpr bool kDepth2 = !kRebuild && !kRowStores && !kStageKt && !kStageKtF && (NRB == 2 || NRB == 3);
+
     constexpr int kKtRowB = 2 * R, kKtChunks = R / 8;
     auto kt_at = [](int r, int byte) {
         return r * kKtRowB + ((((byte >> 4) ^ r) & (kKtChunks - 1)) << 4) + (byte & 15);
@@ -468,8 +473,46 @@ __global__ __launch_bounds__(HB == 1 ? 1024 : 512) void project_kernel(
         // fused: the score first, so that the keys are dead once the projection
         // has built the X~ fragments (fewer registers live at once)
         if (kRebuild && nqb > 0) score_step(t0, b);
+        if constexpr (kStageKtF) {
+            uint8_t *tile = reinterpret_cast<uint8_t *>(qfr + nqb * 8 * nterm * 64) + wave * 32 * kFRowB;
+#pragma unroll
+            for (int hb = 0; hb < HB; ++hb) {
 #pragma unroll 1
-        for (int rb = 0; rb < NRB; ++rb) {
+                for (int rb = 0; rb < NRB; ++rb) {
+                    f32x16 acc = {};
+#pragma unroll
+                    for (int s = 0; s < 8; ++s) {
+                        const u32x4 fh = ufr[((rb * 8 + s) * 2 + 0) * 64 + lane];
+                        const u32x4 fl = ufr[((rb * 8 + s) * 2 + 1) * 64 + lane];
+                        acc = mfma32x32x16(fh, b[hb][s], acc);  // same products and order as below
+                        acc = mfma32x32x16(fl, b[hb][s], acc);
+                    }
+                    // lane (col, khalf): ranks rb*32 + 8q + 4khalf .. +3 of token col
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) {
+                        const int byte = (rb * 32 + 8 * q + 4 * khalf) * 4;
+                        *reinterpret_cast<float4 *>(tile + col * kFRowB + ((((byte >> 4) ^ col) & (kFChunks - 1)) << 4)) =
+                            make_float4(acc[4 * q], acc[4 * q + 1], acc[4 * q + 2], acc[4 * q + 3]);
+                    }
+                }
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+                for (int part = 0; part < kFChunks / 2; ++part) {
+                    const int r = lane / kFChunks + (64 / kFChunks) * part, c = lane % kFChunks;
+                    const float4 v =
+                        *reinterpret_cast<const float4 *>(tile + r * kFRowB + (((c ^ r) & (kFChunks - 1)) << 4));
+                    const int64_t tok = t0 + hb * 32 + r;
+                    if (tok < t_end) *reinterpret_cast<float4 *>(xt + tok * R + c * 4) = v;
+                }
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            }
+        }
+#pragma unroll 1
+        for (int rb = 0; rb < (kStageKtF ? 0 : NRB); ++rb) {
             f32x16 a[HB];
 #pragma unroll
             for (int hb = 0; hb < HB; ++hb) a[hb] = f32x16{};
@@ -930,8 +973,9 @@ constexpr int kProjectWaves = KVC_PROJECT_HB == 1 ? 16 : 8;
 size_t project_lds(int NRB, bool rebuild, int nqb, int nterm, int stage_rows) {
     // rebuild: stage_rows x 256-byte rows of X^; otherwise (bf16 K~ staging, 64):
     // 64 rows x 2R bytes
+    // (bf16 K~ staging: 64 rows x 2R bytes; fp32 K~ staging: 32 rows x 4R bytes)
     const size_t per_wave = rebuild ? static_cast<size_t>(stage_rows) * 256
-                                    : static_cast<size_t>(stage_rows) * 2 * 32 * NRB;
+                                    : static_cast<size_t>(stage_rows) * (stage_rows == 64 ? 2 : 4) * 32 * NRB;
     return static_cast<size_t>(NRB * 16 * (rebuild ? 2 : 1) + nqb * 8 * nterm) * kFragBytes +
            static_cast<size_t>(kProjectWaves) * per_wave;
 }
@@ -992,6 +1036,14 @@ kvc_status launch_project(const uint16_t *X, const float *U, const u32x4 *qfrag,
         // bf16 K~ rows staged whole where the tile fits (both sides at ranks <= 64)
         if (project_lds(NRB, false, nqb, nterm, 64) <= kMaxLds)
             return launch_project_variant<NRB, false, false, OutT, 64>(X, U, qfrag, nqb, nterm, sl, G, Xt, err, Xh,
+                                                                       stream);
+    }
+    if constexpr (sizeof(OutT) == 4 && NRB <= 2) {
+        // fp32 score launches: K~ rows staged whole, one column block at a time
+        // (3.9-4.3 -> 3.75 ms at 1024 slices x 32768; the V side's 128-byte row
+        // segments gain nothing from it)
+        if (nqb > 0 && project_lds(NRB, false, nqb, nterm, 32) <= kMaxLds)
+            return launch_project_variant<NRB, false, false, OutT, 32>(X, U, qfrag, nqb, nterm, sl, G, Xt, err, Xh,
                                                                        stream);
     }
     return nqb > 0
