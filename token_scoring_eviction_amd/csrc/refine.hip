@@ -9,10 +9,11 @@
 //   d_C = ||q|| radius_C / sqrt(D)  (Cauchy-Schwarz on q . (k - mu_C)),
 //   Vmax = the largest value norm of the slice.
 //
-// cluster_summary_kernel: one wave per cluster, 2 channels per lane (a 256-byte
-//   key row per load across the wave), up to 16 (c <= 16) or 32 rows of K and V in
-//   flight at once; sums in token order, 64-lane sums for the norms; the first
-//   chunk's key rows stay in registers for the radius pass, later ones are read again.
+// cluster_summary_kernel: one wave per cluster, four 256-byte rows per 16-byte load
+//   (16 lanes per row, 8 channels per lane), up to 16 (c <= 16) or 32 rows of K and V
+//   in flight at once; per-lane sums in token order, the four row slots added in a
+//   fixed order, 16-lane sums for the row norms; the first chunk's key rows stay in
+//   registers for the radius pass, later ones are read again.
 // refine_risk_kernel: one 1024-thread workgroup per slice and its queries; 16
 //   lanes per cluster (8 channels each) for the logits z, written into the RC
 //   buffer and read back for the normalisation passes; block reductions in a
@@ -28,70 +29,134 @@ constexpr int kSumWaves = 4;       // clusters per summary workgroup
 constexpr int kRiskThreads = 1024;
 constexpr int kMaxRiskQueries = 8;
 
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) x += __shfl_xor(x, d, 64);
-    return x;
+// Exchanges inside a row of 16 lanes (DPP, gfx9 encodings): partner = lane ^ m for
+// m = 15 (row_mirror), 7 (row_half_mirror), 3 and 1 (quad_perm).
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), kCtrl, 0xf, 0xf, false));
+}
+// Sum over a row of 16 lanes; every lane of the row gets the same bits.
+__device__ __forceinline__ float sum16(float a) {
+    a += dpp_f<0x140>(a);
+    a += dpp_f<0x141>(a);
+    a += dpp_f<0x1b>(a);
+    a += dpp_f<0xb1>(a);
+    return a;
 }
 
-template <int kKeepRows>
+__device__ __forceinline__ void widen8(const uint4 &v, float *x) {
+    x[0] = bf16_lo(v.x); x[1] = bf16_hi(v.x);
+    x[2] = bf16_lo(v.y); x[3] = bf16_hi(v.y);
+    x[4] = bf16_lo(v.z); x[5] = bf16_hi(v.z);
+    x[6] = bf16_lo(v.w); x[7] = bf16_hi(v.w);
+}
+
+// One wave per cluster.  Lane (slot, l) = (lane / 16, lane % 16) holds channels
+// 8l .. 8l + 7 of the rows t0 + slot, t0 + slot + 4, ...: one 16-byte load per lane
+// covers four 256-byte rows.  NR loads of K and of V (4 NR rows) are in flight per
+// chunk; the first chunk's key rows stay in registers for the radius pass (later
+// chunks are read again).  Channel sums run over a lane's rows in token order and
+// the four slots are then added in a fixed order ((0 + 1) + (2 + 3)); row norms
+// are 16-lane sums.
+template <int NR>
 __global__ __launch_bounds__(64 * kSumWaves) void cluster_summary_kernel(
     const uint16_t *__restrict__ K, const uint16_t *__restrict__ V, int64_t G, int64_t S, int64_t c,
     int64_t nC, float *__restrict__ mu_k, float *__restrict__ mu_v, float *__restrict__ radius,
     float *__restrict__ vnorm) {
     const int64_t cl = static_cast<int64_t>(blockIdx.x) * kSumWaves + (threadIdx.x >> 6);
-    const int lane = threadIdx.x & 63;
+    const int lane = threadIdx.x & 63, slot = lane >> 4, l16 = lane & 15;
     if (cl >= G * nC) return;  // whole waves leave together
     const int64_t g = cl / nC, j = cl - g * nC;
     const int64_t t0 = j * c, t1 = min(t0 + c, S);
-    const uint32_t *kr = reinterpret_cast<const uint32_t *>(K + (g * S) * kHeadDim) + lane;
-    const uint32_t *vr = reinterpret_cast<const uint32_t *>(V + (g * S) * kHeadDim) + lane;
-    float sk0 = 0.f, sk1 = 0.f, sv0 = 0.f, sv1 = 0.f, vmax2 = 0.f;
-    // rows in chunks of kKeepRows, every load of a chunk in flight before any use;
-    // the first chunk's key rows stay in registers for the radius pass
-    uint32_t kw[kKeepRows];
-    for (int64_t base = t0; base < t1; base += kKeepRows) {
-        uint32_t kc[kKeepRows], vc[kKeepRows];
+    const uint4 *kr = reinterpret_cast<const uint4 *>(K + (g * S) * kHeadDim) + l16;
+    const uint4 *vr = reinterpret_cast<const uint4 *>(V + (g * S) * kHeadDim) + l16;
+    float sk[8], sv[8];
 #pragma unroll
-        for (int r = 0; r < kKeepRows; ++r) {
-            const bool ok = base + r < t1;
-            kc[r] = ok ? kr[(base + r) * (kHeadDim / 2)] : 0u;
-            vc[r] = ok ? vr[(base + r) * (kHeadDim / 2)] : 0u;
+    for (int e = 0; e < 8; ++e) sk[e] = sv[e] = 0.f;
+    float vmax2 = 0.f;
+    uint4 kw[NR];
+    for (int64_t base = t0; base < t1; base += 4 * NR) {
+        uint4 kc[NR], vc[NR];
+#pragma unroll
+        for (int i = 0; i < NR; ++i) {
+            const int64_t t = base + 4 * i + slot;
+            const bool ok = t < t1;
+            const int64_t ts = ok ? t : t0;  // rows past the cluster are never read
+            const uint4 a = kr[ts * (kHeadDim / 8)], b = vr[ts * (kHeadDim / 8)];
+            kc[i] = ok ? a : make_uint4(0u, 0u, 0u, 0u);
+            vc[i] = ok ? b : make_uint4(0u, 0u, 0u, 0u);
         }
 #pragma unroll
-        for (int r = 0; r < kKeepRows; ++r) {
-            if (base + r < t1) {  // token order
-                sk0 += bf16_lo(kc[r]);
-                sk1 += bf16_hi(kc[r]);
-                const float a = bf16_lo(vc[r]), b = bf16_hi(vc[r]);
-                sv0 += a;
-                sv1 += b;
-                vmax2 = fmaxf(vmax2, wave_sum(a * a + b * b));
+        for (int i = 0; i < NR; ++i) {
+            // rows past the cluster are zeros: they add nothing, and their norm is 0
+            float x[8], y[8];
+            widen8(kc[i], x);
+            widen8(vc[i], y);
+            float n2 = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                sk[e] += x[e];
+                sv[e] += y[e];
+                n2 += y[e] * y[e];
             }
+            vmax2 = fmaxf(vmax2, sum16(n2));
         }
         if (base == t0) {
 #pragma unroll
-            for (int r = 0; r < kKeepRows; ++r) kw[r] = kc[r];
+            for (int i = 0; i < NR; ++i) kw[i] = kc[i];
         }
     }
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+        sk[e] += __shfl_xor(sk[e], 16, 64);
+        sk[e] += __shfl_xor(sk[e], 32, 64);
+        sv[e] += __shfl_xor(sv[e], 16, 64);
+        sv[e] += __shfl_xor(sv[e], 32, 64);
+    }
+    vmax2 = fmaxf(vmax2, __shfl_xor(vmax2, 16, 64));
+    vmax2 = fmaxf(vmax2, __shfl_xor(vmax2, 32, 64));
     const float n = static_cast<float>(t1 - t0);
-    const float m0 = sk0 / n, m1 = sk1 / n;
+    float m[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) m[e] = sk[e] / n;
     float rmax2 = 0.f;
-    for (int64_t base = t0; base < t1; base += kKeepRows) {
-        uint32_t kc[kKeepRows];
+    for (int64_t base = t0; base < t1; base += 4 * NR) {
+        uint4 kc[NR];
 #pragma unroll
-        for (int r = 0; r < kKeepRows; ++r)
-            kc[r] = base == t0 ? kw[r] : (base + r < t1 ? kr[(base + r) * (kHeadDim / 2)] : 0u);
-#pragma unroll
-        for (int r = 0; r < kKeepRows; ++r) {
-            if (base + r < t1) {
-                const float d0 = bf16_lo(kc[r]) - m0, d1 = bf16_hi(kc[r]) - m1;
-                rmax2 = fmaxf(rmax2, wave_sum(d0 * d0 + d1 * d1));
+        for (int i = 0; i < NR; ++i) {
+            const int64_t t = base + 4 * i + slot;
+            const bool ok = t < t1;
+            if (base == t0) {
+                kc[i] = kw[i];
+            } else {
+                const uint4 a = kr[(ok ? t : t0) * (kHeadDim / 8)];
+                kc[i] = ok ? a : make_uint4(0u, 0u, 0u, 0u);
             }
         }
+#pragma unroll
+        for (int i = 0; i < NR; ++i) {
+            float x[8];
+            widen8(kc[i], x);
+            float d2 = 0.f;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) {
+                const float d = x[e] - m[e];
+                d2 += d * d;
+            }
+            d2 = sum16(d2);
+            if (base + 4 * i + slot < t1) rmax2 = fmaxf(rmax2, d2);  // uniform within a row
+        }
     }
-    reinterpret_cast<float2 *>(mu_k + cl * kHeadDim)[lane] = make_float2(m0, m1);
-    reinterpret_cast<float2 *>(mu_v + cl * kHeadDim)[lane] = make_float2(sv0 / n, sv1 / n);
+    rmax2 = fmaxf(rmax2, __shfl_xor(rmax2, 16, 64));
+    rmax2 = fmaxf(rmax2, __shfl_xor(rmax2, 32, 64));
+    if (slot == 0) {
+        float4 *mk = reinterpret_cast<float4 *>(mu_k + cl * kHeadDim + 8 * l16);
+        float4 *mv = reinterpret_cast<float4 *>(mu_v + cl * kHeadDim + 8 * l16);
+        mk[0] = make_float4(m[0], m[1], m[2], m[3]);
+        mk[1] = make_float4(m[4], m[5], m[6], m[7]);
+        mv[0] = make_float4(sv[0] / n, sv[1] / n, sv[2] / n, sv[3] / n);
+        mv[1] = make_float4(sv[4] / n, sv[5] / n, sv[6] / n, sv[7] / n);
+    }
     if (lane == 0) {
         radius[cl] = sqrtf(rmax2);
         vnorm[cl] = sqrtf(vmax2);
@@ -209,11 +274,14 @@ extern "C" kvc_status kvc_cluster_summaries(const uint16_t *K, const uint16_t *V
     const int64_t blocks = (G * nC + kSumWaves - 1) / kSumWaves;
     if (blocks > INT32_MAX) return KVC_ERR_UNSUPPORTED;
     // rows per chunk (in flight together, the first chunk kept for the radius pass)
-    if (c <= 16)
-        hipLaunchKernelGGL(cluster_summary_kernel<16>, dim3(static_cast<unsigned>(blocks)), dim3(64 * kSumWaves),
+    if (c <= 12)
+        hipLaunchKernelGGL(cluster_summary_kernel<3>, dim3(static_cast<unsigned>(blocks)), dim3(64 * kSumWaves),
+                           0, stream, K, V, G, S, c, nC, mu_k, mu_v, radius, vnorm);
+    else if (c <= 16)
+        hipLaunchKernelGGL(cluster_summary_kernel<4>, dim3(static_cast<unsigned>(blocks)), dim3(64 * kSumWaves),
                            0, stream, K, V, G, S, c, nC, mu_k, mu_v, radius, vnorm);
     else
-        hipLaunchKernelGGL(cluster_summary_kernel<32>, dim3(static_cast<unsigned>(blocks)), dim3(64 * kSumWaves),
+        hipLaunchKernelGGL(cluster_summary_kernel<8>, dim3(static_cast<unsigned>(blocks)), dim3(64 * kSumWaves),
                            0, stream, K, V, G, S, c, nC, mu_k, mu_v, radius, vnorm);
     return launch_status();
 }
