@@ -602,16 +602,14 @@ kvc_status score_windowed_impl(const uint16_t *K, int64_t G, int64_t S, int32_t 
         uint64_t *mu_pub = cur.take<uint64_t>(static_cast<size_t>(f.teams) * kHeadDim);
         uint32_t *words = cur.take<uint32_t>(static_cast<size_t>(f.teams + 1));
         uint32_t *counters = words, *status = words + f.teams;
-        // clear the centroid tags, the counters and the status word (a kernel,
-        // not a memset, so the sequence can be captured in a graph)
-        const int64_t n_mu = f.teams * kHeadDim * 2, n_w = f.teams + 1;
-        auto zero_blocks = [](int64_t n) {
-            const int64_t b = (n + kFuseThreads - 1) / kFuseThreads;
-            return static_cast<unsigned>(b < 1024 ? b : 1024);
-        };
-        hipLaunchKernelGGL(zero_words, dim3(zero_blocks(n_mu)), dim3(kFuseThreads), 0, stream,
-                           reinterpret_cast<uint32_t *>(mu_pub), n_mu);
-        hipLaunchKernelGGL(zero_words, dim3(zero_blocks(n_w)), dim3(kFuseThreads), 0, stream, words, n_w);
+        // clear the centroid tags, the counters and the status word in one launch
+        // (they are adjacent in the workspace; a kernel, not a memset, so the
+        // sequence can be captured in a graph)
+        uint32_t *clear_from = reinterpret_cast<uint32_t *>(mu_pub);
+        const int64_t n_clear = (words + f.teams + 1) - clear_from;
+        const int64_t zb = (n_clear + kFuseThreads - 1) / kFuseThreads;
+        hipLaunchKernelGGL(zero_words, dim3(static_cast<unsigned>(zb < 1024 ? zb : 1024)), dim3(kFuseThreads), 0,
+                           stream, clear_from, n_clear);
         FuseGeom fa = f;
         float *mu_user = centroids;
         int64_t grid = capacity / f.members * f.members;
