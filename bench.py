@@ -176,7 +176,12 @@ def manifold_workload(cfg, dev, metric="l2", budgets="uniform"):
         score, score_name = (lambda: kvc.kvc_score_l2(K, scores=buf.scores)), "kvc_score_l2"
     else:
         score, score_name = (lambda: kvc.kvc_score_l2_windowed(K, W, scores=buf.scores)), "kvc_score_l2_windowed"
-    ops = [Op(score_name, score, G * S * (256 + 4), kernel="l2_fused")]
+    # caches under 160 MiB of keys take the three-launch scoring path (second read from
+    # the last-level cache); larger ones the single-read cooperative kernel
+    small = G * S * 256 < (160 << 20)
+    score_kernel = ("centroid_partial+centroid_final+" + ("cosine_distance" if metric == "cosine" else "l2_distance")
+                    if small else "l2_fused")
+    ops = [Op(score_name, score, G * S * (256 + 4), kernel=score_kernel)]
     if budgets == "ripple":
         # per-layer budgets from a seeded sensitivity profile, same total as keep per slice
         import numpy as np

@@ -26,8 +26,10 @@ def _check(K, s, W=None):
     return ora, mu
 
 
+@pytest.mark.parametrize("path", ["0", "1"])
 @pytest.mark.parametrize("G,S", [(1, 1), (3, 257), (2, 1000), (4, 4096), (1, 16384 + 77)])
-def test_cosine_global_small(gpu_lib, G, S):
+def test_cosine_global_small(gpu_lib, monkeypatch, G, S, path):
+    monkeypatch.setenv("KVC_SCORE_UNFUSED", path)
     K, _, _ = synth.manifold_global(1, 1, G, S, planted=min(4, S), seed=S + 1, device=DEV)
     mu_gpu = torch.empty((G, 128), dtype=torch.float32, device=DEV)
     s = gpu_lib.kvc_score_centroid(K, metric="cosine", centroids=mu_gpu)
@@ -37,8 +39,10 @@ def test_cosine_global_small(gpu_lib, G, S):
     np.testing.assert_allclose(mu_gpu.cpu().numpy(), mu, rtol=1e-5, atol=1e-5)
 
 
+@pytest.mark.parametrize("path", ["0", "1"])
 @pytest.mark.parametrize("S,W", [(1000, 1), (1000, 300), (4096 * 3 + 5, 4096), (8192, 512)])
-def test_cosine_windowed_small(gpu_lib, S, W):
+def test_cosine_windowed_small(gpu_lib, monkeypatch, S, W, path):
+    monkeypatch.setenv("KVC_SCORE_UNFUSED", path)
     K, _ = synth.manifold_drifting(1, 1, 2, S, segment=max(1, S // 3), seed=W + 7, device=DEV)
     s = gpu_lib.kvc_score_centroid(K, W=W, metric="cosine")
     torch.cuda.synchronize()
@@ -60,9 +64,8 @@ def test_cosine_degenerate_and_nearly_parallel(gpu_lib, monkeypatch):
     base = rng.normal(0.0, 1.0, 128)
     K[2] = base[None] * rng.uniform(0.5, 2.0, (S, 1)) + rng.normal(0.0, 4e-3, (S, 128))
     Kt = torch.from_numpy(K).to(torch.bfloat16).to(DEV)
-    for unfused in (False, True):
-        if unfused:
-            monkeypatch.setenv("KVC_SCORE_UNFUSED", "1")
+    for path in ("0", "1"):
+        monkeypatch.setenv("KVC_SCORE_UNFUSED", path)
         s = gpu_lib.kvc_score_centroid(Kt, metric="cosine")
         torch.cuda.synchronize()
         ora, _ = _check(Kt, s)
@@ -74,6 +77,7 @@ def test_cosine_degenerate_and_nearly_parallel(gpu_lib, monkeypatch):
 @pytest.mark.parametrize("W", [None, 4096, 1000])
 def test_cosine_fused_and_three_launch_paths_agree(gpu_lib, monkeypatch, W):
     K, _, _ = synth.manifold_global(4, 1, 8, 12288 + 100, planted=8, seed=5, device=DEV)
+    monkeypatch.setenv("KVC_SCORE_UNFUSED", "0")
     f = gpu_lib.kvc_score_centroid(K, W=W, metric="cosine").clone()
     monkeypatch.setenv("KVC_SCORE_UNFUSED", "1")
     u = gpu_lib.kvc_score_centroid(K, W=W, metric="cosine")

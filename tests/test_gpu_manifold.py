@@ -25,8 +25,12 @@ def _scores_vs_oracle(K, gpu_scores, W=None):
     return ora, mu
 
 
+# path "0": the cooperative single-read kernel, "1": the three-launch path (small
+# caches take the latter by default)
+@pytest.mark.parametrize("path", ["0", "1"])
 @pytest.mark.parametrize("G,S", [(1, 1), (3, 257), (2, 1000), (4, 4096), (1, 16384 + 77)])
-def test_score_l2_small(gpu_lib, G, S):
+def test_score_l2_small(gpu_lib, monkeypatch, G, S, path):
+    monkeypatch.setenv("KVC_SCORE_UNFUSED", path)
     K, _, _ = synth.manifold_global(1, 1, G, S, planted=min(4, S), seed=S, device=DEV)
     mu_gpu = torch.empty((G, 128), dtype=torch.float32, device=DEV)
     s = gpu_lib.kvc_score_l2(K, centroid=mu_gpu)
@@ -37,7 +41,9 @@ def test_score_l2_small(gpu_lib, G, S):
 
 @pytest.mark.parametrize("S,W", [(1000, 1), (1000, 1000), (1000, 5000), (1000, 300), (4096 * 3 + 5, 4096),
                                  (8192, 512)])
-def test_score_l2_windowed_small(gpu_lib, S, W):
+@pytest.mark.parametrize("path", ["0", "1"])
+def test_score_l2_windowed_small(gpu_lib, monkeypatch, S, W, path):
+    monkeypatch.setenv("KVC_SCORE_UNFUSED", path)
     K, _ = synth.manifold_drifting(1, 1, 2, S, segment=max(1, S // 3), seed=W, device=DEV)
     nwin = -(-S // W)
     mu_gpu = torch.empty((2, nwin, 128), dtype=torch.float32, device=DEV)
@@ -166,6 +172,7 @@ def test_determinism(gpu_lib):
 def test_fused_and_three_launch_paths_agree(gpu_lib, monkeypatch, W):
     # the cooperative single-read path and the three-launch path compute the same scores
     K, _, _ = synth.manifold_global(4, 1, 8, 12288 + 100, planted=8, seed=3, device=DEV)
+    monkeypatch.setenv("KVC_SCORE_UNFUSED", "0")
     f = gpu_lib.kvc_score_l2(K) if W is None else gpu_lib.kvc_score_l2_windowed(K, W)
     f = f.clone()
     monkeypatch.setenv("KVC_SCORE_UNFUSED", "1")

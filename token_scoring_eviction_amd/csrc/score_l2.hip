@@ -563,11 +563,20 @@ size_t score_bytes(int64_t G, int64_t S, int64_t W) {
     return a.bytes() > b.bytes() ? a.bytes() : b.bytes();
 }
 
-// KVC_SCORE_UNFUSED=1 in the environment selects the three-launch path
-// (read at every call, so a process can compare both paths).
-bool force_unfused() {
+// Caches smaller than this take the three-launch path: its second read of K comes
+// from the 256 MB last-level cache, and it has no cooperative launch or team
+// exchange to wait for.  Measured on MI355X: 8 MB of keys 15 vs 30 us, 134 MB
+// even, 268 MB 113 vs 98 us, 1 GB 426 vs 258 us (three-launch vs single-read).
+constexpr int64_t kSmallCacheBytes = 160ll << 20;
+
+// KVC_SCORE_UNFUSED in the environment overrides the choice: 1 selects the
+// three-launch path, 0 the single-read kernel (read at every call, so a process
+// can compare both paths).  Returns true for the three-launch path.
+bool take_unfused(int64_t G, int64_t S) {
     const char *e = getenv("KVC_SCORE_UNFUSED");
-    return e && e[0] == '1';
+    if (e && e[0] == '1') return true;
+    if (e && e[0] == '0') return false;
+    return G * S * kHeadDim * 2 < kSmallCacheBytes;
 }
 
 kvc_status score_windowed_impl(const uint16_t *K, int64_t G, int64_t S, int32_t D, int64_t W,
@@ -596,7 +605,7 @@ kvc_status score_windowed_impl(const uint16_t *K, int64_t G, int64_t S, int32_t 
         known[metric][dev] = true;
     }
     const int64_t capacity = capacity_by_dev[metric][dev];
-    if (capacity >= f.members && f.tiles <= INT32_MAX && !force_unfused()) {
+    if (capacity >= f.members && f.tiles <= INT32_MAX && !take_unfused(G, S)) {
         WsCursor cur(ws);
         float *partial = cur.take<float>(static_cast<size_t>(f.tiles) * kHeadDim);
         uint64_t *mu_pub = cur.take<uint64_t>(static_cast<size_t>(f.teams) * kHeadDim);
