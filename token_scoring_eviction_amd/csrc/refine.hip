@@ -28,6 +28,7 @@ namespace {
 constexpr int kSumWaves = 4;       // clusters per summary workgroup
 constexpr int kRiskThreads = 1024;
 constexpr int kMaxRiskQueries = 8;
+constexpr int kRiskUnroll = 4;     // clusters in flight per 16-lane group in the logit pass
 
 // Exchanges inside a row of 16 lanes (DPP, gfx9 encodings): partner = lane ^ m for
 // m = 15 (row_mirror), 7 (row_half_mirror), 3 and 1 (quad_perm).
@@ -203,22 +204,38 @@ __global__ __launch_bounds__(kRiskThreads) void refine_risk_kernel(
     // pass 1: logits z into the output rows; running maxima; the slice's value bound
     float zmax[kMaxRiskQueries], vm = 0.f;
     for (int i = 0; i < kMaxRiskQueries; ++i) zmax[i] = -INFINITY;
-    for (int64_t j = grp; j < nC; j += kRiskThreads / 16) {
-        const float4 *m4 = reinterpret_cast<const float4 *>(mu_k + (g * nC + j) * kHeadDim + lane16 * 8);
-        const float4 a = m4[0], b = m4[1];
-        for (int i = 0; i < nq; ++i) {
-            const float *q = &qs[i][lane16 * 8];
-            float z = a.x * q[0] + a.y * q[1] + a.z * q[2] + a.w * q[3] + b.x * q[4] + b.y * q[5] +
-                      b.z * q[6] + b.w * q[7];
-            z += __shfl_xor(z, 8, 16);
-            z += __shfl_xor(z, 4, 16);
-            z += __shfl_xor(z, 2, 16);
-            z += __shfl_xor(z, 1, 16);
-            z *= rs;
-            zmax[i] = fmaxf(zmax[i], z);
-            if (lane16 == i) rcg[i * nC + j] = z;
+    // kRiskUnroll clusters per 16-lane group are loaded before any is used
+    constexpr int kGroups = kRiskThreads / 16;
+    for (int64_t j0 = grp; j0 < nC; j0 += kRiskUnroll * kGroups) {
+        float4 a[kRiskUnroll], b[kRiskUnroll];
+        float vn[kRiskUnroll];
+#pragma unroll
+        for (int u = 0; u < kRiskUnroll; ++u) {
+            const int64_t j = j0 + u * kGroups;
+            const int64_t js = j < nC ? j : j0;  // never past the slice's clusters
+            const float4 *m4 = reinterpret_cast<const float4 *>(mu_k + (g * nC + js) * kHeadDim + lane16 * 8);
+            a[u] = m4[0];
+            b[u] = m4[1];
+            vn[u] = vnorm[g * nC + js];
         }
-        vm = fmaxf(vm, vnorm[g * nC + j]);
+#pragma unroll
+        for (int u = 0; u < kRiskUnroll; ++u) {
+            const int64_t j = j0 + u * kGroups;
+            if (j >= nC) break;  // uniform within the 16-lane group
+            for (int i = 0; i < nq; ++i) {
+                const float *q = &qs[i][lane16 * 8];
+                float z = a[u].x * q[0] + a[u].y * q[1] + a[u].z * q[2] + a[u].w * q[3] + b[u].x * q[4] +
+                          b[u].y * q[5] + b[u].z * q[6] + b[u].w * q[7];
+                z += __shfl_xor(z, 8, 16);
+                z += __shfl_xor(z, 4, 16);
+                z += __shfl_xor(z, 2, 16);
+                z += __shfl_xor(z, 1, 16);
+                z *= rs;
+                zmax[i] = fmaxf(zmax[i], z);
+                if (lane16 == i) rcg[i * nC + j] = z;
+            }
+            vm = fmaxf(vm, vn[u]);
+        }
     }
     const float vmax = block_reduce<1>(vm, scratch);
     for (int i = 0; i < nq; ++i) zmax[i] = block_reduce<1>(zmax[i], scratch);
