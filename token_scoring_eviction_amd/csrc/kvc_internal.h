@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "kvc.h"
 
 namespace kvc {
@@ -43,31 +45,35 @@ inline kvc_status launch_status() {
     return hipGetLastError() == hipSuccess ? KVC_OK : KVC_ERR_HIP;
 }
 
+// Per-device values cached by host code are atomics: host threads that call the
+// library at once may both fill an entry, which is harmless (they compute the same
+// value), and no access races.
+
 // Lets `kernel` take up to 160 KB of dynamic LDS on the current device (the
 // default cap is 64 KB); done once per device, `done` is the caller's per-kernel flag array.
-inline kvc_status allow_large_lds(const void *kernel, bool (&done)[64]) {
+inline kvc_status allow_large_lds(const void *kernel, std::atomic<bool> (&done)[64]) {
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return KVC_ERR_HIP;
-    if (!done[dev]) {
+    if (!done[dev].load(std::memory_order_acquire)) {
         if (hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) != hipSuccess)
             return KVC_ERR_HIP;
-        done[dev] = true;
+        done[dev].store(true, std::memory_order_release);
     }
     return KVC_OK;
 }
 
 // Compute units of the current device (cached per device; 0 if it cannot be queried).
 inline int device_cu_count() {
-    static int cus_by_dev[64];
+    static std::atomic<int> cus_by_dev[64];
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-    if (cus_by_dev[dev] == 0) {
-        int cus = 0;
+    int cus = cus_by_dev[dev].load(std::memory_order_relaxed);
+    if (cus == 0) {
         if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
             return 0;
-        cus_by_dev[dev] = cus;
+        cus_by_dev[dev].store(cus, std::memory_order_relaxed);
     }
-    return cus_by_dev[dev];
+    return cus;
 }
 
 // ------------------------------------------------------------ device helpers

@@ -994,7 +994,7 @@ kvc_status launch_project_variant(const uint16_t *X, const float *U, const u32x4
                                   OutT *Xh, hipStream_t stream) {
     constexpr int HB = KVC_PROJECT_HB;
     const size_t lds = project_lds(NRB, kRebuild, nqb, nterm, kStageRows);
-    static bool lds_ok[64];
+    static std::atomic<bool> lds_ok[64];
     if (allow_large_lds(
             reinterpret_cast<const void *>(&project_kernel<NRB, HB, kRowStores, kRebuild, OutT, kStageRows>),
             lds_ok) != KVC_OK)
@@ -1174,7 +1174,7 @@ kvc_status compress_impl(const kvc_dims *d, const uint16_t *K, const uint16_t *V
         nterm = query_terms(nq);
         qfrag = cur.take<u32x4>(static_cast<size_t>(G * nqb * 8 * nterm * 64));
         const double scale = 1.0 / (static_cast<double>(nq) * sqrt(static_cast<double>(d->D)));
-        static bool lds_ok[64];
+        static std::atomic<bool> lds_ok[64];
         if (allow_large_lds(reinterpret_cast<const void *>(&prep_query_kernel<kPrepThreads>), lds_ok) != KVC_OK)
             return KVC_ERR_HIP;
         if (G > INT32_MAX) return KVC_ERR_UNSUPPORTED;

@@ -426,7 +426,7 @@ extern "C" kvc_status kvc_oja_update(const kvc_dims *d, float *U, const uint16_t
     hipLaunchKernelGGL(cov_partial_kernel, dim3(static_cast<unsigned>(o.LH * o.nchunk)), dim3(256), 0,
                        stream, Xp, d->B, d->H_kv, o.np, o.rows_per_chunk, o.nchunk, Cpart);
     if (d->R <= 64) {
-        static bool lds_ok[2][64];
+        static std::atomic<bool> lds_ok[2][64];
         const void *fn = d->R == 32 ? reinterpret_cast<const void *>(&oja_step_qr_lds_kernel<32>)
                                     : reinterpret_cast<const void *>(&oja_step_qr_lds_kernel<64>);
         if (allow_large_lds(fn, lds_ok[d->R == 32 ? 0 : 1]) != KVC_OK) return KVC_ERR_HIP;
@@ -440,7 +440,7 @@ extern "C" kvc_status kvc_oja_update(const kvc_dims *d, float *U, const uint16_t
         return launch_status();
     }
     const size_t lds = (static_cast<size_t>(kHeadDim) * (d->R + 1) + 2 * kHeadDim + 2) * sizeof(double);
-    static bool lds_ok[64];
+    static std::atomic<bool> lds_ok[64];
     if (allow_large_lds(reinterpret_cast<const void *>(&oja_step_qr_kernel), lds_ok) != KVC_OK)
         return KVC_ERR_HIP;
     hipLaunchKernelGGL(oja_step_qr_kernel, dim3(static_cast<unsigned>(o.LH)), dim3(256), lds, stream, U,

@@ -596,15 +596,15 @@ kvc_status score_windowed_impl(const uint16_t *K, int64_t G, int64_t S, int32_t 
     const FuseGeom f = make_fuse_geom(G, S, W, metric);
     const void *fused = metric == kMetricCosine ? reinterpret_cast<const void *>(&l2_fused<kMetricCosine>)
                                                 : reinterpret_cast<const void *>(&l2_fused<kMetricL2>);
-    static int64_t capacity_by_dev[2][64];
-    static bool known[2][64];
+    static std::atomic<int64_t> capacity_by_dev[2][64];  // capacity + 1; 0: not queried yet
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return KVC_ERR_HIP;
-    if (!known[metric][dev]) {
-        capacity_by_dev[metric][dev] = fused_capacity(fused);
-        known[metric][dev] = true;
+    int64_t cap1 = capacity_by_dev[metric][dev].load(std::memory_order_relaxed);
+    if (cap1 == 0) {
+        cap1 = fused_capacity(fused) + 1;
+        capacity_by_dev[metric][dev].store(cap1, std::memory_order_relaxed);
     }
-    const int64_t capacity = capacity_by_dev[metric][dev];
+    const int64_t capacity = cap1 - 1;
     if (capacity >= f.members && f.tiles <= INT32_MAX && !take_unfused(G, S)) {
         WsCursor cur(ws);
         float *partial = cur.take<float>(static_cast<size_t>(f.tiles) * kHeadDim);
