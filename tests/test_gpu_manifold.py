@@ -182,3 +182,15 @@ def test_fused_and_three_launch_paths_agree(gpu_lib, monkeypatch, W):
     for x in (f, u):
         ok, rel, nbad = score_close(x.cpu().numpy(), ora)
         assert ok, (rel, nbad)
+
+
+def test_binding_refuses_strided_and_host_tensors(gpu_lib):
+    # the C ABI reads dense rows: a strided view or a host tensor is refused, not misread
+    K = torch.zeros((4, 256, 128), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(ValueError):
+        gpu_lib.kvc_score_l2(K[:, ::2])
+    s = torch.rand((4, 256), device=DEV)
+    with pytest.raises(ValueError):
+        gpu_lib.kvc_topk_compact(s.t().contiguous().t(), 10)
+    with pytest.raises(ValueError):
+        gpu_lib.kvc_topk_compact(s, 10, K.cpu(), K.cpu())

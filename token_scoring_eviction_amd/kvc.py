@@ -85,7 +85,17 @@ def load(path: str = LIB_PATH):
 
 
 def _ptr(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    """Device address of a dense row-major device tensor (None passes through): the
+    library reads every buffer as contiguous rows, so views with other strides and
+    host tensors are refused here rather than misread."""
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("libkvc takes device tensors, got one on %s" % t.device)
+    if not t.is_contiguous():
+        raise ValueError("libkvc takes dense row-major tensors, got strides %s for shape %s"
+                         % (t.stride(), tuple(t.shape)))
+    return ctypes.c_void_p(t.data_ptr())
 
 
 def _stream():
