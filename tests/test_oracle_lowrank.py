@@ -167,3 +167,40 @@ def test_invalid_arguments():
         oracle.lowrank_compress(K, V, Q, Uk, Uv, inp.L, inp.B, inp.Hkv, 7)
     with pytest.raises(ValueError):  # V without its basis
         oracle.lowrank_compress(K, V, Q, Uk, None, inp.L, inp.B, inp.Hkv, inp.Hq)
+
+
+def _softmax(z):
+    e = np.exp(z - z.max())
+    return e / e.sum()
+
+
+def test_attention_error_chain_on_hybrid_reconstruction():
+    # appendix A.2's chain on the oracle's hybrid cache of one slice (anchors = the
+    # top 5% of e_t, kept exact): for every query, |z^_t - z_t| <= ||q|| ||e_t|| / sqrt(d),
+    # ||a^ - a||_1 <= 2 ||z^ - z||_inf, and ||o^ - o||_2 <= V ||a^ - a||_1 <= 2 V Q E / sqrt(d),
+    # with exact values V; softmax attention in fp64.  A consistency check of the
+    # reconstruction against the pages' bound (it holds for any residual); the
+    # reconstruction itself is pinned by the library-form test above.
+    K, V, Q, Uk, Uv, inp = _small(L=1, B=1, Hkv=1, Hq=4, S=300, D=128, R=16, Wq=8, seed=5)
+    Kt, _, err = oracle.lowrank_compress(K, None, Q, Uk, None, 1, 1, 1, 4)
+    k = oracle.n_anchors(300)
+    idx = oracle.topk(err.astype(np.float32), k)
+    Kh = oracle.reconstruct(Kt, Uk, idx, oracle.gather(K, idx), 1, 1, 1)[0]
+    Kf = oracle.bf16_to_f64(K[0])
+    Vf = oracle.bf16_to_f64(V[0])
+    res = np.linalg.norm(Kh - Kf, axis=1)
+    assert np.all(res[idx[0]] == 0.0)                       # anchors are exact
+    E = res.max()
+    Vb = np.linalg.norm(Vf, axis=1).max()
+    d = 128
+    rng = np.random.default_rng(9)
+    for q in rng.normal(0.0, 1.0, (6, d)) * np.array([0.1, 1.0, 3.0, 10.0, 1.0, 0.5])[:, None]:
+        z, zh = Kf @ q / np.sqrt(d), Kh @ q / np.sqrt(d)
+        Qn = np.linalg.norm(q)
+        assert np.all(np.abs(zh - z) <= Qn * res / np.sqrt(d) * (1 + 1e-12) + 1e-15)
+        a, ah = _softmax(z), _softmax(zh)
+        l1 = np.abs(ah - a).sum()
+        assert l1 <= 2 * np.abs(zh - z).max() * (1 + 1e-9) + 1e-15
+        do = np.linalg.norm(ah @ Vf - a @ Vf)
+        assert do <= Vb * l1 * (1 + 1e-9) + 1e-15
+        assert do <= 2 * Vb * Qn * E / np.sqrt(d) * (1 + 1e-9) + 1e-15
