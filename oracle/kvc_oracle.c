@@ -33,9 +33,13 @@
  *          "method details", and appendix A.1 (Algorithm 1), A.4, A.9.
  *
  * Parity status: every function here is pinned by CPU tests against closed
- * forms, invariants, exact-rational brute force or a library routine, except
- * the decode-time re-projection reading used by the full-loop driver, which
- * lives in the Python wrapper and is marked "parity unpinned" there.
+ * forms, invariants, exact-rational brute force or a library routine, with two
+ * exceptions.  The decode-time re-projection reading used by the full-loop
+ * driver lives in the Python wrapper and is marked "parity unpinned" there.
+ * ora_refine_risk is "parity unpinned" relative to the page beyond its closed
+ * forms: the page names the attention-mass and logit-deviation terms without
+ * formulas, and under the readings taken here RC is not an upper bound of the
+ * single-cluster replacement error in general.
  */
 #include <math.h>
 #include <stdint.h>
