@@ -135,3 +135,40 @@ def test_pipeline_fused_equals_unfused(gpu_lib):
             assert _same(x[:, :3000], y[:, :3000]), storage
         n = G * pipeline.anchor_count(3000)  # a pass's anchors: the first G*k entries
         assert torch.equal(a.idx.view(-1)[:n], b.idx.view(-1)[:n])
+
+
+def test_fused_bf16_loop_shape_sampled(gpu_lib):
+    # the bf16 loop's launch configuration: 32 layers x 8 kv heads (32 query heads), S = 131072,
+    # r = 64, a 32-query window (16-row staging tile on the K side, 32-row tile with K~ staged
+    # on the V side); two slices checked against the oracle
+    from concurrent.futures import ThreadPoolExecutor
+    S = 131072
+    inp = synth.oja_inputs(32, 1, 8, 32, S, R=64, Wq=32, seed=31, device=DEV)
+    Kt, Vt, err, Kh, Vh = gpu_lib.kvc_lowrank_compress_reconstruct_bf16(inp.K, inp.V, inp.Q, inp.Uk, inp.Uv,
+                                                                        32, 1, 8)
+    torch.cuda.synchronize()
+    Uk, Uv = inp.Uk.cpu().numpy(), inp.Uv.cpu().numpy()
+    host = {}
+    for g in (3, 250):
+        l, h = g // 8, g % 8
+        host[g] = (_bits(inp.K[g:g + 1]), _bits(inp.V[g:g + 1]), _bits(inp.Q[l:l + 1, 0:1, h * 4:(h + 1) * 4]),
+                   _bits(Kt[g:g + 1]), _bits(Vt[g:g + 1]), Kt[g:g + 1].float().cpu().numpy(),
+                   Vt[g:g + 1].float().cpu().numpy(), _bits(Kh[g:g + 1]), _bits(Vh[g:g + 1]),
+                   err[g:g + 1].cpu().numpy())
+
+    def check(g):
+        l, h = g // 8, g % 8
+        kb, vb, Q, ktb, vtb, ktf, vtf, khb, vhb, eg = host[g]
+        okt, ovt, oerr = oracle.lowrank_compress(kb, vb, Q, Uk[l:l + 1, h:h + 1], Uv[l:l + 1, h:h + 1], 1, 1, 1, 4)
+        for got, ref, name in ((ktb, okt, "K~"), (vtb, ovt, "V~")):
+            ok, ulp = bf16_close(got, ref)
+            assert ok, "%s slice %d: %d ulps" % (name, g, ulp)
+        ok, rel, nbad = score_close(eg, oerr)
+        assert ok, "err slice %d: %d off, max rel %.3g" % (g, nbad, rel)
+        for xt, U, gh, name in ((ktf, Uk, khb, "K^"), (vtf, Uv, vhb, "V^")):
+            ref = oracle.reconstruct(xt, U[l:l + 1, h:h + 1], None, None, 1, 1, 1)
+            ok, ulp = bf16_close(gh, ref)
+            assert ok, "%s slice %d: %d ulps" % (name, g, ulp)
+
+    with ThreadPoolExecutor(max_workers=2) as ex:
+        list(ex.map(check, host))

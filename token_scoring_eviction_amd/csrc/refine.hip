@@ -17,7 +17,9 @@
 // refine_risk_kernel: one 1024-thread workgroup per slice and its queries; 16
 //   lanes per cluster (8 channels each) for the logits z, written into the RC
 //   buffer and read back for the normalisation passes; block reductions in a
-//   fixed order (deterministic).
+//   fixed order (deterministic).  The normaliser's terms are shifted by their
+//   largest exponent max_C (z_C + d_C), so no cosh overflows fp32 however far
+//   apart a cluster's keys lie.
 #include <math.h>
 
 #include "kvc_internal.h"
@@ -202,13 +204,14 @@ __global__ __launch_bounds__(kRiskThreads) void refine_risk_kernel(
     }
     float *rcg = rc + g * nq * nC;
     // pass 1: logits z into the output rows; running maxima; the slice's value bound
-    float zmax[kMaxRiskQueries], vm = 0.f;
-    for (int i = 0; i < kMaxRiskQueries; ++i) zmax[i] = -INFINITY;
+    // zdmax = max_C (z_C + d_C), the largest exponent of n_C e^{z_C} cosh d_C
+    float zmax[kMaxRiskQueries], zdmax[kMaxRiskQueries], vm = 0.f;
+    for (int i = 0; i < kMaxRiskQueries; ++i) zmax[i] = zdmax[i] = -INFINITY;
     // kRiskUnroll clusters per 16-lane group are loaded before any is used
     constexpr int kGroups = kRiskThreads / 16;
     for (int64_t j0 = grp; j0 < nC; j0 += kRiskUnroll * kGroups) {
         float4 a[kRiskUnroll], b[kRiskUnroll];
-        float vn[kRiskUnroll];
+        float vn[kRiskUnroll], rd[kRiskUnroll];
 #pragma unroll
         for (int u = 0; u < kRiskUnroll; ++u) {
             const int64_t j = j0 + u * kGroups;
@@ -217,6 +220,7 @@ __global__ __launch_bounds__(kRiskThreads) void refine_risk_kernel(
             a[u] = m4[0];
             b[u] = m4[1];
             vn[u] = vnorm[g * nC + js];
+            rd[u] = radius[g * nC + js];
         }
 #pragma unroll
         for (int u = 0; u < kRiskUnroll; ++u) {
@@ -232,15 +236,22 @@ __global__ __launch_bounds__(kRiskThreads) void refine_risk_kernel(
                 z += __shfl_xor(z, 1, 16);
                 z *= rs;
                 zmax[i] = fmaxf(zmax[i], z);
+                zdmax[i] = fmaxf(zdmax[i], z + qn[i] * rd[u] * rs);
                 if (lane16 == i) rcg[i * nC + j] = z;
             }
             vm = fmaxf(vm, vn[u]);
         }
     }
     const float vmax = block_reduce<1>(vm, scratch);
-    for (int i = 0; i < nq; ++i) zmax[i] = block_reduce<1>(zmax[i], scratch);
+    for (int i = 0; i < nq; ++i) {
+        zmax[i] = block_reduce<1>(zmax[i], scratch);
+        zdmax[i] = block_reduce<1>(zdmax[i], scratch);
+    }
     __syncthreads();  // the logits written by other threads are visible
-    // pass 2: masses n_C exp(z - zmax) and the sums over clusters
+    // pass 2: masses n_C e^{z - zmax} and their sum psum; the normaliser as
+    // dsum = sum_C n_C e^{z_C - zdmax} cosh d_C, every exponent <= 0 (cosh d overflows
+    // fp32 past d ~ 89; here the largest term is >= n_C / 2 and none overflows), so
+    // Dn = e^{zdmax - zmax} dsum / psum
     float psum[kMaxRiskQueries], dsum[kMaxRiskQueries];
     for (int i = 0; i < nq; ++i) {
         psum[i] = 0.f;
@@ -250,25 +261,27 @@ __global__ __launch_bounds__(kRiskThreads) void refine_risk_kernel(
         const float n = static_cast<float>(min((j + 1) * c, S) - j * c);
         const float r = radius[g * nC + j];
         for (int i = 0; i < nq; ++i) {
-            const float p = n * expf(rcg[i * nC + j] - zmax[i]);
-            psum[i] += p;
-            dsum[i] += p * coshf(qn[i] * r * rs);
+            const float z = rcg[i * nC + j], dl = qn[i] * r * rs;
+            psum[i] += n * expf(z - zmax[i]);
+            dsum[i] += n * 0.5f * (expf(z + dl - zdmax[i]) + expf(z - dl - zdmax[i]));
         }
     }
     for (int i = 0; i < nq; ++i) {
         psum[i] = block_reduce<0>(psum[i], scratch);
         dsum[i] = block_reduce<0>(dsum[i], scratch);
     }
-    // pass 3: RC = 2 p Vmax [ (cosh d - 1) / Dn + tanh(d / 2) ], cosh d - 1 = 2 sinh^2(d / 2)
+    // pass 3: RC = 2 p Vmax [ (cosh d - 1) / Dn + tanh(d / 2) ]; with cosh d - 1 =
+    // 2 sinh^2(d / 2) = e^d expm1(-d)^2 / 2 the first term is
+    // n e^{z + d - zdmax} expm1(-d)^2 / (2 dsum): an exponent <= 0 and no cancellation
     for (int64_t j = tid; j < nC; j += kRiskThreads) {
         const float n = static_cast<float>(min((j + 1) * c, S) - j * c);
         const float r = radius[g * nC + j];
         for (int i = 0; i < nq; ++i) {
-            const float p = n * expf(rcg[i * nC + j] - zmax[i]) / psum[i];
-            const float dl = qn[i] * r * rs;
-            const float sh = sinhf(0.5f * dl);
-            const float Dn = dsum[i] / psum[i];
-            rcg[i * nC + j] = 2.f * p * vmax * (2.f * sh * sh / Dn + tanhf(0.5f * dl));
+            const float z = rcg[i * nC + j], dl = qn[i] * r * rs;
+            const float p = n * expf(z - zmax[i]) / psum[i];
+            const float em = expm1f(-dl);
+            const float dev = n * expf(z + dl - zdmax[i]) * em * em / (2.f * dsum[i]);
+            rcg[i * nC + j] = 2.f * vmax * (dev + p * tanhf(0.5f * dl));
         }
     }
 }
