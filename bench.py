@@ -254,7 +254,7 @@ def refine_workload(dev):
     ops = [Op("kvc_cluster_summaries", summaries, G * S * 512 + G * nC * (2 * 512 + 8),
               kernel="cluster_summary_kernel"),
            Op("kvc_refine_risk", lambda: kvc.kvc_refine_risk(summ[0], summ[2], summ[3], S, c, Q, rc=rc),
-              G * nC * (512 + 8 + 3 * nq * 4), kernel="refine_risk_kernel")]
+              G * nC * (512 + 8 + 3 * nq * 4), kernel="risk_partial_kernel + risk_final_kernel")]
     algo = G * S * 512 + G * nC * (2 * 512 + 8) + G * nC * (512 + 8 + nq * 4)
     config = {"workload": "RefineKV cluster summaries (contiguous 10-key clusters: mean key, mean value, "
                           "key radius, value norm) and risk scores of every cluster for the 4 query heads "

@@ -49,7 +49,7 @@
 extern "C" {
 #endif
 
-#define KVC_ABI_VERSION 3
+#define KVC_ABI_VERSION 4
 
 typedef enum kvc_status {
     KVC_OK = 0,
@@ -67,7 +67,8 @@ typedef enum kvc_op {
     KVC_OP_OJA_UPDATE = 4,
     KVC_OP_RECONSTRUCT = 5,
     KVC_OP_SCORE_CENTROID = 6,
-    KVC_OP_TOPK_RAGGED = 7
+    KVC_OP_TOPK_RAGGED = 7,
+    KVC_OP_REFINE_RISK = 8
 } kvc_op;
 
 /* Score of a key against its (global or window) centroid mu, for
@@ -99,6 +100,8 @@ const char *kvc_status_str(kvc_status s);
  *     tokens; W = window (ignored for SCORE_L2).
  *   TOPK_COMPACT: G = L*B*H_kv slices of S tokens; k = tokens kept.
  *   TOPK_RAGGED: G = L*B*H_kv slices (16 bytes per slice).
+ *   REFINE_RISK: G = L*B*H_kv slices of S tokens; k = cluster size c
+ *     (144 bytes per 128 clusters of a slice).
  *   LOWRANK_COMPRESS, OJA_UPDATE, RECONSTRUCT: shapes from `d`; for OJA_UPDATE
  *     d->S is the token count N and W is the pooling window.  The bf16-storage
  *     variants need what LOWRANK_COMPRESS and RECONSTRUCT need.
@@ -194,12 +197,15 @@ kvc_status kvc_cluster_summaries(const uint16_t *K, const uint16_t *V, int64_t G
  *   p_C  = n_C exp(z_C) / sum_C' n_C' exp(z_C'),  z_C = q . mu_k[C] / sqrt(D),
  *   d_C  = ||q|| radius[C] / sqrt(D)   (bounds |q.k - q.mu_C| / sqrt(D) for k in C),
  *   Vmax = max_C vnorm[C] over the slice.
- * Summaries as from kvc_cluster_summaries (same S and c); Q: bf16 [G][nq][D]
- * (the queries served by slice g, nq <= 8); rc: fp32 [G][nq][nC].  A cluster
- * with RC > tau would be expanded to its exact entries (not done here). */
+ * Summaries as from kvc_cluster_summaries (same S and c); Q: bf16 [G][nq][D],
+ * 16-byte aligned (the queries served by slice g, nq <= 8); rc: fp32 [G][nq][nC].
+ * ws: kvc_workspace_bytes(KVC_OP_REFINE_RISK, d, c, 0) bytes, 16-byte aligned,
+ * for per-chunk softmax records.  Evaluated without overflow for any finite d_C
+ * (terms rescaled by the largest exponent).  A cluster with RC > tau would be
+ * expanded to its exact entries (not done here). */
 kvc_status kvc_refine_risk(const float *mu_k, const float *radius, const float *vnorm, int64_t G,
                            int64_t S, int64_t c, int32_t D, const uint16_t *Q, int32_t nq, float *rc,
-                           hipStream_t stream);
+                           void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* Hybrid low-rank compression ([OJA] background: K~ = K U_k, V~ = V U_v;
  * method details: residual r_t = k_t - U_k U_k^T k_t and query-weighted error

@@ -28,7 +28,7 @@ def test_library_exports_every_declared_symbol():
     lib = kvc.load()
     for name in _declared():
         assert hasattr(lib, name), name
-    assert lib.kvc_abi_version() == 3
+    assert lib.kvc_abi_version() == 4
     assert lib.kvc_status_str(kvc.OK) == b"ok"
     assert lib.kvc_status_str(kvc.ERR_WORKSPACE_TOO_SMALL) == b"workspace too small"
     assert lib.kvc_status_str(99) == b"unknown status"

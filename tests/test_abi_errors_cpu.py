@@ -118,6 +118,11 @@ def test_refine_entry_points(lib):
     assert f(A, B, 0, 100, 128, 10, C, D_, E, F, NULL) == OK
     assert f(NULL, B, 2, 100, 128, 10, C, D_, E, F, NULL) == INV
     g = lib.kvc_refine_risk
-    assert g(A, B, C, 2, 100, 10, 128, D_, 9, E, NULL) == UNS      # more than 8 queries
-    assert g(A, B, C, 2, 100, 10, 128, D_, 0, E, NULL) == OK       # no queries
-    assert g(A, B, C, 2, 100, 10, 128, D_, -1, E, NULL) == INV
+    assert g(A, B, C, 2, 100, 10, 128, D_, 9, E, W_, 1 << 20, NULL) == UNS   # more than 8 queries
+    assert g(A, B, C, 2, 100, 10, 128, D_, 0, E, W_, 1 << 20, NULL) == OK    # no queries
+    assert g(A, B, C, 2, 100, 10, 128, D_, -1, E, W_, 1 << 20, NULL) == INV
+    assert g(A, B, C, 2, 100, 10, 128, D_, 4, E, NULL, 1 << 20, NULL) == INV  # no workspace
+    assert g(A, B, C, 2, 100, 10, 128, P(0x400008), 4, E, W_, 1 << 20, NULL) == INV  # Q not 16-byte aligned
+    need = kvc.workspace_bytes(kvc.OP_REFINE_RISK, kvc._dims(1, 1, 2, 0, 100, 0, 128, 0, 0), 10)
+    assert need == 2 * 9 * 16                                     # one chunk record per slice
+    assert g(A, B, C, 2, 100, 10, 128, D_, 4, E, W_, need - 1, NULL) == WS

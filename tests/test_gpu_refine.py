@@ -28,13 +28,16 @@ def test_summaries_vs_oracle(gpu_lib, S, c):
         assert ok, (rel, nbad)
 
 
+@pytest.mark.parametrize("S,c", [(2000, 10), (100, 1000), (5000, 1), (262144 + 7, 33)])
 @pytest.mark.parametrize("rmax", [4.0, 400.0])
 @pytest.mark.parametrize("nq", [1, 4, 8])
-def test_risk_on_given_summaries(gpu_lib, nq, rmax):
+def test_risk_on_given_summaries(gpu_lib, nq, rmax, S, c):
     # identical fp32 summaries and bf16 queries on both sides; radii up to 400 put
-    # d_C = ||q|| radius / sqrt(D) far past where cosh overflows fp32 (d ~ 89)
-    G, S, c = 3, 2000, 10
-    nC = S // c
+    # d_C = ||q|| radius / sqrt(D) far past where cosh overflows fp32 (d ~ 89).  Cluster
+    # counts 200, 1 (a single short cluster), 5000 and 7944 (a short last cluster): one
+    # or many 128-cluster chunks, one or several 2048-cluster final blocks, ragged tails
+    G = 3
+    nC = -(-S // c)
     rng = np.random.default_rng(nq)
     mk = rng.normal(0.0, 1.0, (G, nC, 128)).astype(np.float32)
     rad = rng.uniform(0.0, rmax, (G, nC)).astype(np.float32)
@@ -73,7 +76,9 @@ def test_refine_bench_shape_sampled(gpu_lib):
     Q = torch.randn((L * H, 4, 128), generator=torch.Generator().manual_seed(6)).to(torch.bfloat16)
     mk, mv, rad, vn = gpu_lib.kvc_cluster_summaries(K, V, c)
     rc = gpu_lib.kvc_refine_risk(mk, rad, vn, S, c, Q.to(DEV))
+    rc2 = gpu_lib.kvc_refine_risk(mk, rad, vn, S, c, Q.to(DEV))
     torch.cuda.synchronize()
+    assert torch.equal(rc, rc2)  # the chunk records merge in a fixed order: bit-reproducible
     for g in (0, 137, 255):
         omk, omv, orad, ovn = oracle.cluster_summaries(synth.bf16_bits(K[g:g + 1]), synth.bf16_bits(V[g:g + 1]), c)
         np.testing.assert_allclose(mk[g].cpu().numpy(), omk[0], rtol=1e-5, atol=1e-5)

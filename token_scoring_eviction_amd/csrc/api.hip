@@ -8,6 +8,7 @@ size_t topk_ragged_workspace_bytes(int64_t G);
 size_t compress_workspace_bytes(const kvc_dims *d);
 size_t oja_workspace_bytes(const kvc_dims *d, int64_t pool);
 size_t reconstruct_workspace_bytes(const kvc_dims *d);
+size_t risk_bytes(int64_t G, int64_t S, int64_t c);
 }  // namespace kvc
 
 extern "C" int kvc_abi_version(void) { return KVC_ABI_VERSION; }
@@ -35,6 +36,7 @@ extern "C" size_t kvc_workspace_bytes(kvc_op op, const kvc_dims *d, int64_t k, i
         case KVC_OP_OJA_UPDATE: return kvc::oja_workspace_bytes(d, W);
         case KVC_OP_RECONSTRUCT: return kvc::reconstruct_workspace_bytes(d);
         case KVC_OP_TOPK_RAGGED: return kvc::topk_ragged_workspace_bytes(G);
+        case KVC_OP_REFINE_RISK: return kvc::risk_bytes(G, d->S, k);
     }
     return 0;
 }

@@ -14,12 +14,14 @@
 //   in flight at once; per-lane sums in token order, the four row slots added in a
 //   fixed order, 16-lane sums for the row norms; the first chunk's key rows stay in
 //   registers for the radius pass, later ones are read again.
-// refine_risk_kernel: one 1024-thread workgroup per slice and its queries; 16
-//   lanes per cluster (8 channels each) for the logits z, written into the RC
-//   buffer and read back for the normalisation passes; block reductions in a
-//   fixed order (deterministic).  The normaliser's terms are shifted by their
-//   largest exponent max_C (z_C + d_C), so no cosh overflows fp32 however far
-//   apart a cluster's keys lie.
+// risk_partial_kernel + risk_final_kernel: the slice's clusters are spread over
+//   many workgroups (a single workgroup per slice left the mean-key stream
+//   latency-bound).  The partial pass computes the logits z (16 lanes per cluster,
+//   8 channels each) into the RC rows and, per chunk of clusters, the maxima and
+//   the rescaled sums of the softmax and of the normaliser; the final pass merges
+//   the chunk records in chunk order (deterministic) and turns each logit into RC.
+//   The normaliser's terms are shifted by their largest exponent max_C (z_C + d_C),
+//   so no cosh overflows fp32 however far apart a cluster's keys lie.
 #include <math.h>
 
 #include "kvc_internal.h"
@@ -27,10 +29,14 @@
 namespace kvc {
 namespace {
 
-constexpr int kSumWaves = 4;       // clusters per summary workgroup
-constexpr int kRiskThreads = 1024;
+constexpr int kSumWaves = 4;             // clusters per summary workgroup
+constexpr int kRiskThreads = 256;        // both risk passes
 constexpr int kMaxRiskQueries = 8;
-constexpr int kRiskUnroll = 4;     // clusters in flight per 16-lane group in the logit pass
+constexpr int kRiskBatch = 2;            // clusters per 16-lane row loaded before any is used
+constexpr int kRiskPerRow = 8;           // clusters per 16-lane row in a partial-pass workgroup
+constexpr int kRiskChunk = 16 * kRiskPerRow;     // clusters per partial-pass workgroup
+constexpr int kRiskFinalChunk = 2048;    // clusters per final-pass workgroup
+constexpr int kPartStride = kMaxRiskQueries + 1;  // float4 records per (slice, chunk)
 
 // Exchanges inside a row of 16 lanes (DPP, gfx9 encodings): partner = lane ^ m for
 // m = 15 (row_mirror), 7 (row_half_mirror), 3 and 1 (quad_perm).
@@ -166,127 +172,215 @@ __global__ __launch_bounds__(64 * kSumWaves) void cluster_summary_kernel(
     }
 }
 
-// Block-wide reduction over 1024 threads in a fixed order (op: 0 sum, 1 max).
-template <int kOp>
-__device__ __forceinline__ float block_reduce(float x, float *scratch) {
-    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+// ||q|| of one query row over a row of 16 lanes, 8 channels per lane; every lane
+// of the row gets the same bits, and both risk kernels compute it this way.
+__device__ __forceinline__ float query_norm(const uint16_t *qrow, int lane16) {
+    float x[8];
+    widen8(reinterpret_cast<const uint4 *>(qrow)[lane16], x);
+    float s = 0.f;
 #pragma unroll
-    for (int d = 32; d >= 1; d >>= 1) {
-        const float y = __shfl_xor(x, d, 64);
-        x = kOp == 0 ? x + y : fmaxf(x, y);
-    }
-    __syncthreads();  // scratch is free
-    if (lane == 0) scratch[wave] = x;
-    __syncthreads();
-    float r = kOp == 0 ? 0.f : -INFINITY;
-    for (int w = 0; w < kRiskThreads / 64; ++w) r = kOp == 0 ? r + scratch[w] : fmaxf(r, scratch[w]);
-    return r;
+    for (int e = 0; e < 8; ++e) s += x[e] * x[e];
+    return sqrtf(sum16(s));
 }
 
-__global__ __launch_bounds__(kRiskThreads) void refine_risk_kernel(
+__device__ __forceinline__ float cluster_size(int64_t j, int64_t c, int64_t S) {
+    return static_cast<float>(min((j + 1) * c, S) - j * c);
+}
+
+// Partial pass: one workgroup per (slice, chunk of kRiskChunk clusters).  A 16-lane
+// row takes clusters grp, grp + 16, ... of the chunk (kRiskBatch loaded before any
+// is used); lane i of the row keeps query i's logit z and deviation d of each.
+// The logits go to the RC rows (read back by the final pass); the chunk's record
+// holds, per query, {zmax_c, zdmax_c, psum_c, dsum_c} with
+//   psum_c = sum_C n_C e^{z_C - zmax_c},
+//   dsum_c = sum_C n_C (e^{z_C + d_C - zdmax_c} + e^{z_C - d_C - zdmax_c}) / 2,
+// zdmax_c = max_C (z_C + d_C) (so no exponent is positive), and the chunk's
+// largest value norm.  Rows of the chunk are added in row order.
+__global__ __launch_bounds__(kRiskThreads) void risk_partial_kernel(
     const float *__restrict__ mu_k, const float *__restrict__ radius, const float *__restrict__ vnorm,
-    int64_t S, int64_t c, int64_t nC, const uint16_t *__restrict__ Q, int nq, float *__restrict__ rc) {
+    int64_t S, int64_t c, int64_t nC, int64_t nchunk, const uint16_t *__restrict__ Q, int nq,
+    float *__restrict__ rc, float4 *__restrict__ part) {
     __shared__ float qs[kMaxRiskQueries][kHeadDim];
-    __shared__ float scratch[kRiskThreads / 64];
-    const int64_t g = blockIdx.x;
-    const int tid = threadIdx.x, lane16 = tid & 15, grp = tid >> 4;  // 64 groups of 16 lanes
+    __shared__ float red[4][16][kMaxRiskQueries];
+    __shared__ float vred[kRiskThreads / 64];
+    const int64_t g = blockIdx.x / nchunk, ch = blockIdx.x - g * nchunk;
+    const int tid = threadIdx.x, lane16 = tid & 15, grp = tid >> 4;
     const float rs = 1.f / sqrtf(static_cast<float>(kHeadDim));
-    for (int i = tid; i < nq * kHeadDim; i += kRiskThreads) {
-        const uint16_t h = Q[(g * nq) * kHeadDim + i];
-        qs[i / kHeadDim][i % kHeadDim] = __uint_as_float(static_cast<uint32_t>(h) << 16);
-    }
-    __syncthreads();
-    float qn[kMaxRiskQueries];
+    const uint16_t *Qg = Q + g * nq * kHeadDim;
+    for (int i = tid; i < nq * kHeadDim; i += kRiskThreads)
+        qs[i / kHeadDim][i % kHeadDim] = __uint_as_float(static_cast<uint32_t>(Qg[i]) << 16);
+    float qn = 0.f;  // ||q|| of this lane's query
     for (int i = 0; i < nq; ++i) {
-        float s = 0.f;
-        for (int d = 0; d < kHeadDim; ++d) s += qs[i][d] * qs[i][d];
-        qn[i] = sqrtf(s);  // the same bits in every thread
+        const float n = query_norm(Qg + i * kHeadDim, lane16);
+        if (lane16 == i) qn = n;
     }
-    float *rcg = rc + g * nq * nC;
-    // pass 1: logits z into the output rows; running maxima; the slice's value bound
-    // zdmax = max_C (z_C + d_C), the largest exponent of n_C e^{z_C} cosh d_C
-    float zmax[kMaxRiskQueries], zdmax[kMaxRiskQueries], vm = 0.f;
-    for (int i = 0; i < kMaxRiskQueries; ++i) zmax[i] = zdmax[i] = -INFINITY;
-    // kRiskUnroll clusters per 16-lane group are loaded before any is used
-    constexpr int kGroups = kRiskThreads / 16;
-    for (int64_t j0 = grp; j0 < nC; j0 += kRiskUnroll * kGroups) {
-        float4 a[kRiskUnroll], b[kRiskUnroll];
-        float vn[kRiskUnroll], rd[kRiskUnroll];
+    __syncthreads();  // qs
+    const int64_t j0 = ch * kRiskChunk + grp;
+    float zr[kRiskPerRow], dr[kRiskPerRow];
+    float zmax = -INFINITY, zdmax = -INFINITY, vm = 0.f;
 #pragma unroll
-        for (int u = 0; u < kRiskUnroll; ++u) {
-            const int64_t j = j0 + u * kGroups;
-            const int64_t js = j < nC ? j : j0;  // never past the slice's clusters
+    for (int bt = 0; bt < kRiskPerRow / kRiskBatch; ++bt) {
+        float4 a[kRiskBatch], b[kRiskBatch];
+        float rd[kRiskBatch];
+#pragma unroll
+        for (int u = 0; u < kRiskBatch; ++u) {
+            const int64_t j = j0 + 16 * (bt * kRiskBatch + u);
+            const int64_t js = j < nC ? j : nC - 1;  // never past the slice's clusters
             const float4 *m4 = reinterpret_cast<const float4 *>(mu_k + (g * nC + js) * kHeadDim + lane16 * 8);
             a[u] = m4[0];
             b[u] = m4[1];
-            vn[u] = vnorm[g * nC + js];
             rd[u] = radius[g * nC + js];
+            vm = fmaxf(vm, vnorm[g * nC + js]);  // a repeated cluster leaves the maximum as it is
         }
 #pragma unroll
-        for (int u = 0; u < kRiskUnroll; ++u) {
-            const int64_t j = j0 + u * kGroups;
-            if (j >= nC) break;  // uniform within the 16-lane group
+        for (int u = 0; u < kRiskBatch; ++u) {
+            const int k = bt * kRiskBatch + u;
+            const int64_t j = j0 + 16 * k;
+            float zi = 0.f;
             for (int i = 0; i < nq; ++i) {
                 const float *q = &qs[i][lane16 * 8];
-                float z = a[u].x * q[0] + a[u].y * q[1] + a[u].z * q[2] + a[u].w * q[3] + b[u].x * q[4] +
-                          b[u].y * q[5] + b[u].z * q[6] + b[u].w * q[7];
-                z += __shfl_xor(z, 8, 16);
-                z += __shfl_xor(z, 4, 16);
-                z += __shfl_xor(z, 2, 16);
-                z += __shfl_xor(z, 1, 16);
-                z *= rs;
-                zmax[i] = fmaxf(zmax[i], z);
-                zdmax[i] = fmaxf(zdmax[i], z + qn[i] * rd[u] * rs);
-                if (lane16 == i) rcg[i * nC + j] = z;
+                const float z = a[u].x * q[0] + a[u].y * q[1] + a[u].z * q[2] + a[u].w * q[3] + b[u].x * q[4] +
+                                b[u].y * q[5] + b[u].z * q[6] + b[u].w * q[7];
+                const float zs = sum16(z) * rs;
+                zi = lane16 == i ? zs : zi;
             }
-            vm = fmaxf(vm, vn[u]);
+            const float dl = qn * rd[u] * rs;
+            zr[k] = zi;
+            dr[k] = dl;
+            if (j < nC && lane16 < nq) {
+                rc[(g * nq + lane16) * nC + j] = zi;
+                zmax = fmaxf(zmax, zi);
+                zdmax = fmaxf(zdmax, zi + dl);
+            }
         }
     }
-    const float vmax = block_reduce<1>(vm, scratch);
-    for (int i = 0; i < nq; ++i) {
-        zmax[i] = block_reduce<1>(zmax[i], scratch);
-        zdmax[i] = block_reduce<1>(zdmax[i], scratch);
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) vm = fmaxf(vm, __shfl_xor(vm, d, 64));
+    if ((tid & 63) == 0) vred[tid >> 6] = vm;
+    if (lane16 < kMaxRiskQueries) {
+        red[0][grp][lane16] = zmax;
+        red[1][grp][lane16] = zdmax;
     }
-    __syncthreads();  // the logits written by other threads are visible
-    // pass 2: masses n_C e^{z - zmax} and their sum psum; the normaliser as
-    // dsum = sum_C n_C e^{z_C - zdmax} cosh d_C, every exponent <= 0 (cosh d overflows
-    // fp32 past d ~ 89; here the largest term is >= n_C / 2 and none overflows), so
-    // Dn = e^{zdmax - zmax} dsum / psum
-    float psum[kMaxRiskQueries], dsum[kMaxRiskQueries];
-    for (int i = 0; i < nq; ++i) {
-        psum[i] = 0.f;
-        dsum[i] = 0.f;
-    }
-    for (int64_t j = tid; j < nC; j += kRiskThreads) {
-        const float n = static_cast<float>(min((j + 1) * c, S) - j * c);
-        const float r = radius[g * nC + j];
-        for (int i = 0; i < nq; ++i) {
-            const float z = rcg[i * nC + j], dl = qn[i] * r * rs;
-            psum[i] += n * expf(z - zmax[i]);
-            dsum[i] += n * 0.5f * (expf(z + dl - zdmax[i]) + expf(z - dl - zdmax[i]));
+    __syncthreads();
+    float cz = -INFINITY, czd = -INFINITY, ps = 0.f, ds = 0.f;
+    if (lane16 < nq) {
+        for (int r = 0; r < 16; ++r) {
+            cz = fmaxf(cz, red[0][r][lane16]);
+            czd = fmaxf(czd, red[1][r][lane16]);
         }
+#pragma unroll
+        for (int k = 0; k < kRiskPerRow; ++k) {
+            const int64_t j = j0 + 16 * k;
+            if (j < nC) {
+                const float n = cluster_size(j, c, S);
+                ps += n * expf(zr[k] - cz);
+                ds += n * 0.5f * (expf(zr[k] + dr[k] - czd) + expf(zr[k] - dr[k] - czd));
+            }
+        }
+        red[2][grp][lane16] = ps;
+        red[3][grp][lane16] = ds;
     }
-    for (int i = 0; i < nq; ++i) {
-        psum[i] = block_reduce<0>(psum[i], scratch);
-        dsum[i] = block_reduce<0>(dsum[i], scratch);
+    __syncthreads();
+    float4 *rec = part + (g * nchunk + ch) * kPartStride;
+    if (tid < nq) {  // row 0, lane i: cz, czd are query i's chunk maxima
+        float P = 0.f, D = 0.f;
+        for (int r = 0; r < 16; ++r) {
+            P += red[2][r][tid];
+            D += red[3][r][tid];
+        }
+        rec[tid] = make_float4(cz, czd, P, D);
     }
-    // pass 3: RC = 2 p Vmax [ (cosh d - 1) / Dn + tanh(d / 2) ]; with cosh d - 1 =
-    // 2 sinh^2(d / 2) = e^d expm1(-d)^2 / 2 the first term is
-    // n e^{z + d - zdmax} expm1(-d)^2 / (2 dsum): an exponent <= 0 and no cancellation
-    for (int64_t j = tid; j < nC; j += kRiskThreads) {
-        const float n = static_cast<float>(min((j + 1) * c, S) - j * c);
+    if (tid == 0) {
+        float v = vred[0];
+        for (int w = 1; w < kRiskThreads / 64; ++w) v = fmaxf(v, vred[w]);
+        rec[kMaxRiskQueries] = make_float4(v, 0.f, 0.f, 0.f);
+    }
+}
+
+// Final pass: one workgroup per (slice, kRiskFinalChunk clusters).  The slice's
+// chunk records are merged (maxima, then the sums rescaled to the common maxima:
+// 32 lanes per query, chunks c = lane, lane + 32, ... in order, then a 32-lane
+// butterfly, so every workgroup of the slice holds the same bits); then
+//   RC = 2 Vmax [ n e^{z + d - zdmax} expm1(-d)^2 / (2 dsum) + p tanh(d / 2) ],
+//   p = n e^{z - zmax} / psum,
+// the first term being p (cosh d - 1) / Dn with cosh d - 1 = e^d expm1(-d)^2 / 2
+// and Dn = e^{zdmax - zmax} dsum / psum: no exponent is positive, nothing cancels.
+__global__ __launch_bounds__(kRiskThreads) void risk_final_kernel(
+    const float *__restrict__ radius, int64_t S, int64_t c, int64_t nC, int64_t nchunk, int64_t nfin,
+    const uint16_t *__restrict__ Q, int nq, const float4 *__restrict__ part, float *__restrict__ rc) {
+    __shared__ float4 merged[kMaxRiskQueries];
+    __shared__ float vmax_s;
+    const int64_t g = blockIdx.x / nfin, fc = blockIdx.x - g * nfin;
+    const int tid = threadIdx.x, lane16 = tid & 15;
+    const float rs = 1.f / sqrtf(static_cast<float>(kHeadDim));
+    const uint16_t *Qg = Q + g * nq * kHeadDim;
+    float qn[kMaxRiskQueries];
+#pragma unroll
+    for (int i = 0; i < kMaxRiskQueries; ++i) qn[i] = i < nq ? query_norm(Qg + i * kHeadDim, lane16) : 0.f;
+    {
+        const int mi = tid >> 5, sl = tid & 31;  // query, lane within its 32
+        const float4 *pg = part + g * nchunk * kPartStride;
+        float m = -INFINITY, md = -INFINITY, vm = 0.f, P = 0.f, D = 0.f;
+        if (mi < nq) {
+            for (int64_t k = sl; k < nchunk; k += 32) {
+                const float4 r = pg[k * kPartStride + mi];
+                m = fmaxf(m, r.x);
+                md = fmaxf(md, r.y);
+            }
+        }
+        if (mi == 0)
+            for (int64_t k = sl; k < nchunk; k += 32) vm = fmaxf(vm, pg[k * kPartStride + kMaxRiskQueries].x);
+#pragma unroll
+        for (int d = 16; d >= 1; d >>= 1) {
+            m = fmaxf(m, __shfl_xor(m, d, 32));
+            md = fmaxf(md, __shfl_xor(md, d, 32));
+            vm = fmaxf(vm, __shfl_xor(vm, d, 32));
+        }
+        if (mi < nq) {
+            for (int64_t k = sl; k < nchunk; k += 32) {
+                const float4 r = pg[k * kPartStride + mi];
+                P += r.z * expf(r.x - m);
+                D += r.w * expf(r.y - md);
+            }
+        }
+#pragma unroll
+        for (int d = 16; d >= 1; d >>= 1) {
+            P += __shfl_xor(P, d, 32);
+            D += __shfl_xor(D, d, 32);
+        }
+        if (sl == 0 && mi < nq) merged[mi] = make_float4(m, md, P, D);
+        if (tid == 0) vmax_s = vm;
+    }
+    __syncthreads();
+    const float vmax = vmax_s;
+    const int64_t j1 = min((fc + 1) * kRiskFinalChunk, nC);
+    for (int64_t j = fc * kRiskFinalChunk + tid; j < j1; j += kRiskThreads) {
+        const float n = cluster_size(j, c, S);
         const float r = radius[g * nC + j];
-        for (int i = 0; i < nq; ++i) {
-            const float z = rcg[i * nC + j], dl = qn[i] * r * rs;
-            const float p = n * expf(z - zmax[i]) / psum[i];
+#pragma unroll
+        for (int i = 0; i < kMaxRiskQueries; ++i) {
+            if (i >= nq) break;
+            const float4 M = merged[i];
+            float *o = rc + (g * nq + i) * nC + j;
+            const float z = *o, dl = qn[i] * r * rs;
+            const float p = n * expf(z - M.x) / M.z;
             const float em = expm1f(-dl);
-            const float dev = n * expf(z + dl - zdmax[i]) * em * em / (2.f * dsum[i]);
-            rcg[i * nC + j] = 2.f * vmax * (dev + p * tanhf(0.5f * dl));
+            const float dev = n * expf(z + dl - M.y) * em * em / (2.f * M.w);
+            *o = 2.f * vmax * (dev + p * tanhf(0.5f * dl));
         }
     }
 }
 
 }  // namespace
+
+// Chunk records of the risk passes: kPartStride float4 per (slice, chunk).
+size_t risk_bytes(int64_t G, int64_t S, int64_t c) {
+    if (G < 0 || S < 1 || c < 1) return 0;
+    const int64_t nC = (S + c - 1) / c;
+    const int64_t nchunk = (nC + kRiskChunk - 1) / kRiskChunk;
+    return static_cast<size_t>(G * nchunk) * kPartStride * sizeof(float4);
+}
+
 }  // namespace kvc
 
 extern "C" kvc_status kvc_cluster_summaries(const uint16_t *K, const uint16_t *V, int64_t G, int64_t S,
@@ -318,18 +412,25 @@ extern "C" kvc_status kvc_cluster_summaries(const uint16_t *K, const uint16_t *V
 
 extern "C" kvc_status kvc_refine_risk(const float *mu_k, const float *radius, const float *vnorm,
                                       int64_t G, int64_t S, int64_t c, int32_t D, const uint16_t *Q,
-                                      int32_t nq, float *rc, hipStream_t stream) {
+                                      int32_t nq, float *rc, void *ws, size_t ws_bytes,
+                                      hipStream_t stream) {
     using namespace kvc;
     if (G < 0 || S < 1 || c < 1 || D <= 0 || nq < 0) return KVC_ERR_INVALID_ARGUMENT;
     if (D != kHeadDim || nq > kMaxRiskQueries) return KVC_ERR_UNSUPPORTED;
     if (G == 0 || nq == 0) return KVC_OK;
-    if (!mu_k || !radius || !vnorm || !Q || !rc) return KVC_ERR_INVALID_ARGUMENT;
-    if (!aligned(mu_k, 16) || !aligned(radius, 4) || !aligned(vnorm, 4) || !aligned(Q, 2) ||
-        !aligned(rc, 4))
+    if (!mu_k || !radius || !vnorm || !Q || !rc || !ws) return KVC_ERR_INVALID_ARGUMENT;
+    if (!aligned(mu_k, 16) || !aligned(radius, 4) || !aligned(vnorm, 4) || !aligned(Q, 16) ||
+        !aligned(rc, 4) || !aligned(ws, 16))
         return KVC_ERR_INVALID_ARGUMENT;
-    if (G > INT32_MAX) return KVC_ERR_UNSUPPORTED;
+    if (ws_bytes < risk_bytes(G, S, c)) return KVC_ERR_WORKSPACE_TOO_SMALL;
     const int64_t nC = (S + c - 1) / c;
-    hipLaunchKernelGGL(refine_risk_kernel, dim3(static_cast<unsigned>(G)), dim3(kRiskThreads), 0, stream,
-                       mu_k, radius, vnorm, S, c, nC, Q, nq, rc);
+    const int64_t nchunk = (nC + kRiskChunk - 1) / kRiskChunk;
+    const int64_t nfin = (nC + kRiskFinalChunk - 1) / kRiskFinalChunk;
+    if (G * nchunk > INT32_MAX) return KVC_ERR_UNSUPPORTED;
+    float4 *part = static_cast<float4 *>(ws);
+    hipLaunchKernelGGL(risk_partial_kernel, dim3(static_cast<unsigned>(G * nchunk)), dim3(kRiskThreads), 0,
+                       stream, mu_k, radius, vnorm, S, c, nC, nchunk, Q, nq, rc, part);
+    hipLaunchKernelGGL(risk_final_kernel, dim3(static_cast<unsigned>(G * nfin)), dim3(kRiskThreads), 0, stream,
+                       radius, S, c, nC, nchunk, nfin, Q, nq, part, rc);
     return launch_status();
 }

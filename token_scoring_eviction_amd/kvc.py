@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(_PKG, "libkvc.so")
 
 OK, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_WORKSPACE_TOO_SMALL, ERR_HIP = range(5)
 OP_SCORE_L2, OP_SCORE_L2_WINDOWED, OP_TOPK_COMPACT, OP_LOWRANK_COMPRESS, OP_OJA_UPDATE, \
-    OP_RECONSTRUCT, OP_SCORE_CENTROID, OP_TOPK_RAGGED = range(8)
+    OP_RECONSTRUCT, OP_SCORE_CENTROID, OP_TOPK_RAGGED, OP_REFINE_RISK = range(9)
 METRIC_L2, METRIC_COSINE = 0, 1
 METRICS = {"l2": METRIC_L2, "cosine": METRIC_COSINE}
 
@@ -65,7 +65,7 @@ def load(path: str = LIB_PATH):
                 "kvc_topk_compact_ragged": [P, I64, I64, I64, P, P, P, I32, P, P, P, P, SZ, P],
                 "kvc_layer_budgets": [P, I64, ctypes.c_double, ctypes.c_double, I64, I64, P],
                 "kvc_cluster_summaries": [P, P, I64, I64, I32, I64, P, P, P, P, P],
-                "kvc_refine_risk": [P, P, P, I64, I64, I64, I32, P, I32, P, P],
+                "kvc_refine_risk": [P, P, P, I64, I64, I64, I32, P, I32, P, P, SZ, P],
                 "kvc_lowrank_compress": [DP, P, P, P, P, P, P, P, P, P, SZ, P],
                 "kvc_lowrank_compress_bf16": [DP, P, P, P, P, P, P, P, P, P, SZ, P],
                 "kvc_oja_update": [DP, P, P, I32, ctypes.c_float, P, SZ, P],
@@ -266,8 +266,10 @@ def kvc_refine_risk(mu_k, radius, vnorm, S, c, Q, rc=None):
     nq = Q.shape[1]
     if rc is None:
         rc = torch.empty((G, nq, nC), dtype=torch.float32, device=mu_k.device)
+    nb = workspace_bytes(OP_REFINE_RISK, _dims(1, 1, G, 0, S, 0, D, 0, 0), c)
+    ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=mu_k.device)
     _check("kvc_refine_risk", lib.kvc_refine_risk(_ptr(mu_k), _ptr(radius), _ptr(vnorm), G, S, c, D,
-                                                  _ptr(_bits(Q)), nq, _ptr(rc), _stream()))
+                                                  _ptr(_bits(Q)), nq, _ptr(rc), _ptr(ws), nb, _stream()))
     return rc
 
 
