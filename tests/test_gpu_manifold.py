@@ -194,3 +194,23 @@ def test_binding_refuses_strided_and_host_tensors(gpu_lib):
         gpu_lib.kvc_topk_compact(s.t().contiguous().t(), 10)
     with pytest.raises(ValueError):
         gpu_lib.kvc_topk_compact(s, 10, K.cpu(), K.cpu())
+
+
+def test_binding_workspace_per_stream(gpu_lib):
+    # the binding's cached workspace is one buffer per (device, stream): calls on two
+    # streams may overlap without sharing scratch; results match the default stream's
+    from token_scoring_eviction_amd import kvc
+    K, _, _ = synth.manifold_global(2, 1, 8, 4096, planted=8, seed=9, device=DEV)
+    ref = gpu_lib.kvc_score_l2(K).clone()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    s1.wait_stream(torch.cuda.current_stream())
+    s2.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(s1):
+        w1 = kvc.workspace(1024)
+        a = gpu_lib.kvc_score_l2(K)
+    with torch.cuda.stream(s2):
+        w2 = kvc.workspace(1024)
+        b = gpu_lib.kvc_score_l2(K)
+    torch.cuda.synchronize()
+    assert w1.data_ptr() != w2.data_ptr()
+    assert torch.equal(a, ref) and torch.equal(b, ref)

@@ -108,14 +108,17 @@ def _check(name, st):
 
 
 def workspace(nbytes: int, device=None):
-    """A cached uint8 device buffer of at least nbytes (None when nbytes == 0)."""
+    """A cached uint8 device buffer of at least nbytes (None when nbytes == 0), one per
+    (device, current stream): calls queued on one stream run in order and may share it,
+    calls on different streams get different buffers and may overlap."""
     if nbytes == 0:
         return None
     dev = torch.device("cuda", torch.cuda.current_device() if device is None else device)
-    buf = _ws.get(dev)
+    key = (dev, torch.cuda.current_stream(dev).cuda_stream)
+    buf = _ws.get(key)
     if buf is None or buf.numel() < nbytes:
         buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
-        _ws[dev] = buf
+        _ws[key] = buf
     return buf
 
 
@@ -267,7 +270,7 @@ def kvc_refine_risk(mu_k, radius, vnorm, S, c, Q, rc=None):
     if rc is None:
         rc = torch.empty((G, nq, nC), dtype=torch.float32, device=mu_k.device)
     nb = workspace_bytes(OP_REFINE_RISK, _dims(1, 1, G, 0, S, 0, D, 0, 0), c)
-    ws = torch.empty(max(nb, 1), dtype=torch.uint8, device=mu_k.device)
+    ws = workspace(nb, mu_k.device.index)
     _check("kvc_refine_risk", lib.kvc_refine_risk(_ptr(mu_k), _ptr(radius), _ptr(vnorm), G, S, c, D,
                                                   _ptr(_bits(Q)), nq, _ptr(rc), _ptr(ws), nb, _stream()))
     return rc
