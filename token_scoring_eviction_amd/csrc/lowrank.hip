@@ -63,24 +63,6 @@ __device__ __forceinline__ void split8(const float *x, u32x4 &hi, u32x4 &lo) {
     }
 }
 
-// x (8 fp64) -> three bf16 terms x = t0 + t1 + t2 + O(2^-25 |x|)
-__device__ __forceinline__ void split8x3_f64(const double *x, u32x4 *part) {
-    uint32_t t[3][8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        double rest = x[e];
-#pragma unroll
-        for (int p = 0; p < 3; ++p) {
-            t[p][e] = f32_to_bf16_rne(static_cast<float>(rest));
-            rest -= static_cast<double>(__uint_as_float(t[p][e] << 16));
-        }
-    }
-#pragma unroll
-    for (int p = 0; p < 3; ++p)
-#pragma unroll
-        for (int q = 0; q < 4; ++q) part[p][q] = t[p][2 * q] | (t[p][2 * q + 1] << 16);
-}
-
 // rank carried by operand element e of lane half h at reconstruction k-step ks
 __host__ __device__ constexpr int recon_rank(int ks, int h, int e) {
     return 16 * ks + 8 * (e >> 2) + 4 * h + (e & 3);
@@ -200,25 +182,31 @@ constexpr size_t kPrepLds = static_cast<size_t>(kHeadDim) * kPrepStride * sizeof
                             static_cast<size_t>(kHeadDim) * kPrepStride * sizeof(float) +
                             static_cast<size_t>(kHeadDim) * kPrepQStride * sizeof(uint16_t);
 
-// One workgroup of NT threads per slice, U taken in chunks of 64 columns:
-//   phase 1  T[q][j] = sum_c Q[q][c] U[c][j]        (thread tile 4 queries x JW columns)
-//   phase 2  P[q][c] += sum_j T[q][j] U[c][j]       (thread tile 4 queries x CW channels,
-//                                                    accumulated in registers over chunks)
-// then Q''[q][c] = scale * (Q[q][c] - P[q][c]).  Everything is fp64 (bf16 x fp32
-// products are exact in fp64).  LDS strides are padded so that the rows a wave
-// reads at one column fall in distinct banks.  The LDS footprint allows one
-// workgroup per CU, so NT sets the waves per SIMD: 512 threads (two per SIMD,
-// 128 VGPRs) took 0.37 ms for 1024 slices where 256 threads took 0.52 ms.
-#ifndef KVC_PREP_THREADS
-#define KVC_PREP_THREADS 512
-#endif
-constexpr int kPrepThreads = KVC_PREP_THREADS;
-template <int NT>
-__global__ __launch_bounds__(NT) void prep_query_kernel(const uint16_t *__restrict__ Q,
-                                                         const float *__restrict__ Uk, int64_t B,
-                                                         int64_t Hkv, int64_t Hq, int64_t Wq,
-                                                         int R, int nq, int nqb, int nterm,
-                                                         double scale, u32x4 *__restrict__ qfrag) {
+// fp64 matrix cores, v_mfma_f64_16x16x4f64: A[i][k] comes from lane i + 16k, B[k][j]
+// from lane j + 16k, and element r of lane l receives D[l / 16 + 4r][l % 16].
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ f64x4 mfma_f64(double a, double b, f64x4 c) {
+    return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
+}
+
+// One workgroup of eight waves (two per SIMD) per slice; U is taken in chunks of 64
+// columns and the window in NRB = 2 nqb 16-row blocks (rows past nq zero):
+//   phase 1  T[q][j] = sum_c Q[q][c] U[c][j]    wave w: columns 16 (w % 4) .. + 15 of the
+//                                               chunk, row blocks of half w / 4
+//   phase 2  P[q][c] += sum_j T[q][j] U[c][j]   wave w: channels 16w .. 16w + 15, accumulated
+//                                               over the chunks in registers
+// then Q''[q][c] = scale * (Q[q][c] - P[q][c]), split into bf16 terms and stored
+// two channels per 32-bit word in fragment order.  Every product is fp64 on the
+// matrix cores (bf16 x fp32 products are exact in fp64); T goes through LDS in fp64.
+// With fp64 FMAs on the vector units (a 4 x 4 register tile per thread, operands
+// converted from LDS at every use) the same work took 0.34-0.37 ms at 1024 slices.
+constexpr int kPrepThreads = 512;
+template <int NRB>  // 16-row blocks of the window: 2 nqb (rows past nq are zero)
+__global__ __launch_bounds__(kPrepThreads) void prep_query_kernel(const uint16_t *__restrict__ Q,
+                                                                  const float *__restrict__ Uk, int64_t B,
+                                                                  int64_t Hkv, int64_t Hq, int64_t Wq, int R,
+                                                                  int nq, int nqb, int nterm, double scale,
+                                                                  u32x4 *__restrict__ qfrag) {
     extern __shared__ double lds_prep[];
     double *Ts = lds_prep;                                                     // [128][65]
     float *Uc = reinterpret_cast<float *>(Ts + kHeadDim * kPrepStride);        // [128][65]
@@ -232,94 +220,112 @@ __global__ __launch_bounds__(NT) void prep_query_kernel(const uint16_t *__restri
     const float *U = Uk + (l * Hkv + h) * kHeadDim * R;
     // window rows q = (group head) * Wq + (query); the group's heads are contiguous in Q
     const uint16_t *Qg = Q + ((lb * Hq + h * grp) * Wq) * kHeadDim;
-    for (int i = tid; i < kHeadDim * (kHeadDim / 2); i += blockDim.x) {
-        const int q = i / (kHeadDim / 2), c2 = i % (kHeadDim / 2);  // rows past nq are zero
-        reinterpret_cast<uint32_t *>(Qs + q * kPrepQStride)[c2] =
-            q < nq ? reinterpret_cast<const uint32_t *>(Qg + q * kHeadDim)[c2] : 0u;
+    // staging: every thread issues all its 16-byte loads before storing any to LDS
+    // (one 4-byte load at a time per thread left the prep waiting on memory latency)
+    constexpr int kStageLoads = kHeadDim * kHeadDim / 8 / kPrepThreads;  // 16-byte pieces per thread
+    {
+        uint4 v[kStageLoads];
+#pragma unroll
+        for (int u = 0; u < kStageLoads; ++u) {
+            const int i = tid + u * kPrepThreads, q = i >> 4, c8 = i & 15;  // rows past nq are zero
+            v[u] = q < nq ? reinterpret_cast<const uint4 *>(Qg + q * kHeadDim)[c8] : make_uint4(0u, 0u, 0u, 0u);
+        }
+#pragma unroll
+        for (int u = 0; u < kStageLoads; ++u) {
+            const int i = tid + u * kPrepThreads, q = i >> 4, c8 = i & 15;
+            uint32_t *row = reinterpret_cast<uint32_t *>(Qs + q * kPrepQStride) + 4 * c8;
+            row[0] = v[u].x;
+            row[1] = v[u].y;
+            row[2] = v[u].z;
+            row[3] = v[u].w;
+        }
     }
     auto qval = [&](int q, int c) {
         return static_cast<double>(__uint_as_float(static_cast<uint32_t>(Qs[q * kPrepQStride + c]) << 16));
     };
-    constexpr int GROUPS = NT / 32;             // column / channel groups (32 query groups of 4)
-    constexpr int JW = kPrepJ / GROUPS;         // columns per thread in phase 1
-    constexpr int CW = kHeadDim / GROUPS;       // channels per thread in phase 2
-    // phase-1 tile: columns j = jg + GROUPS jj, queries 4 qg .. 4 qg + 3
-    const int jg = tid % GROUPS, qg1 = tid / GROUPS;
-    // phase-2 tile: channels CW cg .. CW cg + CW - 1, queries 4 qg .. 4 qg + 3
-    const int cg = tid % GROUPS, qg2 = tid / GROUPS;
-    double P[4][CW];
+    const int wave = tid >> 6, lane = tid & 63, l16 = lane & 15, kq = lane >> 4;
+    constexpr int RB1 = NRB / 2;  // row blocks per wave in phase 1
+    const int jb = wave & 3, r0 = (wave >> 2) * RB1;
+    f64x4 pacc[NRB];
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int e = 0; e < CW; ++e) P[a][e] = 0.0;
+    for (int rb = 0; rb < NRB; ++rb) pacc[rb] = f64x4{0.0, 0.0, 0.0, 0.0};
 
     for (int j0 = 0; j0 < R; j0 += kPrepJ) {
         const int jn = min(kPrepJ, R - j0);  // 32 or 64
         __syncthreads();                     // previous chunk's readers are done
-        for (int i = tid; i < kHeadDim * jn; i += blockDim.x) {
-            const int c = i / jn, jj = i % jn;
-            Uc[c * kPrepStride + jj] = U[c * R + j0 + jj];
-        }
-        __syncthreads();
-        if (4 * qg1 < nq) {
-            // columns jg + GROUPS jj for jj < jn / GROUPS
-            double t[4][JW];
+        {
+            const int n4 = jn / 4;  // 16-byte pieces per U row in the chunk
+            float4 v[kStageLoads];
 #pragma unroll
-            for (int a = 0; a < 4; ++a)
-#pragma unroll
-                for (int jj = 0; jj < JW; ++jj) t[a][jj] = 0.0;
-            const int nj = jn / GROUPS;
-            for (int c = 0; c < kHeadDim; ++c) {
-                double qv[4], uv[JW];
-#pragma unroll
-                for (int a = 0; a < 4; ++a) qv[a] = qval(4 * qg1 + a, c);
-#pragma unroll
-                for (int jj = 0; jj < JW; ++jj)
-                    uv[jj] = jj < nj ? static_cast<double>(Uc[c * kPrepStride + jg + GROUPS * jj]) : 0.0;
-#pragma unroll
-                for (int a = 0; a < 4; ++a)
-#pragma unroll
-                    for (int jj = 0; jj < JW; ++jj) t[a][jj] = fma(qv[a], uv[jj], t[a][jj]);
+            for (int u = 0; u < kStageLoads; ++u) {
+                const int i = tid + u * kPrepThreads, c = i / n4, j4 = i % n4;
+                if (c < kHeadDim) v[u] = reinterpret_cast<const float4 *>(U + c * R + j0)[j4];
             }
 #pragma unroll
-            for (int a = 0; a < 4; ++a)
-#pragma unroll
-                for (int jj = 0; jj < JW; ++jj)
-                    if (jj < nj) Ts[(4 * qg1 + a) * kPrepStride + jg + GROUPS * jj] = t[a][jj];
+            for (int u = 0; u < kStageLoads; ++u) {
+                const int i = tid + u * kPrepThreads, c = i / n4, j4 = i % n4;
+                if (c < kHeadDim) {
+                    float *row = Uc + c * kPrepStride + 4 * j4;
+                    row[0] = v[u].x;
+                    row[1] = v[u].y;
+                    row[2] = v[u].z;
+                    row[3] = v[u].w;
+                }
+            }
         }
         __syncthreads();
-        if (4 * qg2 < nq) {
-            for (int j = 0; j < jn; ++j) {
-                double tv[4], uv[CW];
+        if (16 * jb < jn) {
+            f64x4 tacc[RB1];
 #pragma unroll
-                for (int a = 0; a < 4; ++a) tv[a] = Ts[(4 * qg2 + a) * kPrepStride + j];
+            for (int rb = 0; rb < RB1; ++rb) tacc[rb] = f64x4{0.0, 0.0, 0.0, 0.0};
+#pragma unroll 2
+            for (int c0 = 0; c0 < kHeadDim; c0 += 4) {
+                const double b = static_cast<double>(Uc[(c0 + kq) * kPrepStride + 16 * jb + l16]);
+                double a[RB1];
 #pragma unroll
-                for (int e = 0; e < CW; ++e) uv[e] = static_cast<double>(Uc[(CW * cg + e) * kPrepStride + j]);
+                for (int rb = 0; rb < RB1; ++rb) a[rb] = qval(16 * (r0 + rb) + l16, c0 + kq);
 #pragma unroll
-                for (int a = 0; a < 4; ++a)
-#pragma unroll
-                    for (int e = 0; e < CW; ++e) P[a][e] = fma(tv[a], uv[e], P[a][e]);
+                for (int rb = 0; rb < RB1; ++rb) tacc[rb] = mfma_f64(a[rb], b, tacc[rb]);
             }
+#pragma unroll
+            for (int rb = 0; rb < RB1; ++rb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    Ts[(16 * (r0 + rb) + kq + 4 * r) * kPrepStride + 16 * jb + l16] = tacc[rb][r];
+        }
+        __syncthreads();
+#pragma unroll 2
+        for (int j = 0; j < jn; j += 4) {
+            double a[NRB];
+#pragma unroll
+            for (int rb = 0; rb < NRB; ++rb) a[rb] = Ts[(16 * rb + l16) * kPrepStride + j + kq];
+            const double b = static_cast<double>(Uc[(16 * wave + l16) * kPrepStride + j + kq]);
+#pragma unroll
+            for (int rb = 0; rb < NRB; ++rb) pacc[rb] = mfma_f64(a[rb], b, pacc[rb]);
         }
     }
-    // Q'' in fragment order: lane (q % 32) + 32 * ((c0 / 8) % 2) of fragment (q / 32, c0 / 16)
-    // holds channels c0 .. c0 + 7 of query q; queries nq .. 32 nqb - 1 are zero
-    u32x4 *out = qfrag + slice * static_cast<int64_t>(nqb) * 8 * nterm * 64;
+    // Q'' in fragment order: lane (q % 32) + 32 * ((c / 8) % 2) of fragment (q / 32, c / 16)
+    // holds channels 8 (c / 8) .. + 7 of query q (bf16 pairs per 32-bit word); queries
+    // nq .. 32 nqb - 1 are zero.  Lanes l16 and l16 ^ 1 hold channels c and c ^ 1.
+    uint32_t *out = reinterpret_cast<uint32_t *>(qfrag + slice * static_cast<int64_t>(nqb) * 8 * nterm * 64);
 #pragma unroll
-    for (int a = 0; a < 4; ++a) {
-        const int q = 4 * qg2 + a;
-        if (q >= 32 * nqb) continue;
+    for (int rb = 0; rb < NRB; ++rb) {
 #pragma unroll
-        for (int half = 0; half < CW / 8; ++half) {
-            const int c0 = CW * cg + 8 * half;
-            double x[8];
+            for (int r = 0; r < 4; ++r) {
+                const int q = 16 * rb + kq + 4 * r, c = 16 * wave + l16;
+                double rest = q < nq ? scale * (qval(q, c) - pacc[rb][r]) : 0.0;
+                uint32_t t[kQParts];
 #pragma unroll
-            for (int e = 0; e < 8; ++e) x[e] = q < nq ? scale * (qval(q, c0 + e) - P[a][8 * half + e]) : 0.0;
-            u32x4 part[kQParts];
-            split8x3_f64(x, part);
-            const int lane = (q & 31) + 32 * ((c0 >> 3) & 1), s = c0 >> 4;
-            for (int t = 0; t < nterm; ++t) out[(((q >> 5) * 8 + s) * nterm + t) * 64 + lane] = part[t];
-        }
+                for (int p = 0; p < kQParts; ++p) {
+                    t[p] = f32_to_bf16_rne(static_cast<float>(rest));
+                    rest -= static_cast<double>(__uint_as_float(t[p] << 16));
+                }
+                const int64_t word = (((q >> 5) * 8 + (c >> 4)) * nterm) * 64 + (q & 31) + 32 * ((c >> 3) & 1);
+                for (int p = 0; p < nterm; ++p) {
+                    const uint32_t nb = __shfl_xor(t[p], 1, 64);
+                    if (!(l16 & 1)) out[(word + p * 64) * 4 + ((c & 7) >> 1)] = t[p] | (nb << 16);
+                }
+            }
     }
 }
 
@@ -1174,17 +1180,22 @@ kvc_status compress_impl(const kvc_dims *d, const uint16_t *K, const uint16_t *V
         nterm = query_terms(nq);
         qfrag = cur.take<u32x4>(static_cast<size_t>(G * nqb * 8 * nterm * 64));
         const double scale = 1.0 / (static_cast<double>(nq) * sqrt(static_cast<double>(d->D)));
-        static std::atomic<bool> lds_ok[64];
-        if (allow_large_lds(reinterpret_cast<const void *>(&prep_query_kernel<kPrepThreads>), lds_ok) != KVC_OK)
-            return KVC_ERR_HIP;
         if (G > INT32_MAX) return KVC_ERR_UNSUPPORTED;
-        const size_t prep_lds = kPrepLds;
-        hipLaunchKernelGGL(prep_query_kernel<kPrepThreads>, dim3(static_cast<unsigned>(G)), dim3(kPrepThreads),
-                           prep_lds, stream,
-                           Q_win, U_k,
-                           d->B, d->H_kv, d->H_q, d->W_q, static_cast<int>(d->R),
-                           static_cast<int>(nq), nqb, nterm, scale, qfrag);
-        if ((st = launch_status()) != KVC_OK) return st;
+        static std::atomic<bool> lds_ok[4][64];
+        auto prep = [&](auto kernel, std::atomic<bool>(&ok)[64]) -> kvc_status {
+            if (allow_large_lds(reinterpret_cast<const void *>(kernel), ok) != KVC_OK) return KVC_ERR_HIP;
+            hipLaunchKernelGGL(kernel, dim3(static_cast<unsigned>(G)), dim3(kPrepThreads), kPrepLds, stream,
+                               Q_win, U_k, d->B, d->H_kv, d->H_q, d->W_q, static_cast<int>(d->R),
+                               static_cast<int>(nq), nqb, nterm, scale, qfrag);
+            return launch_status();
+        };
+        switch (nqb) {  // nq <= 128 was checked
+            case 1: st = prep(&prep_query_kernel<2>, lds_ok[0]); break;
+            case 2: st = prep(&prep_query_kernel<4>, lds_ok[1]); break;
+            case 3: st = prep(&prep_query_kernel<6>, lds_ok[2]); break;
+            default: st = prep(&prep_query_kernel<8>, lds_ok[3]); break;
+        }
+        if (st != KVC_OK) return st;
     }
     // one side (K with its error score, or V): projection, then X^ fused or separate
     auto side = [&](const uint16_t *X, const float *U, const u32x4 *qf, int nb, int nt, OutT *Xt,
