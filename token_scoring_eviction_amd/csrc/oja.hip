@@ -186,59 +186,91 @@ __global__ __launch_bounds__(256) void oja_step_qr_kernel(float *__restrict__ U,
     for (int e = tid; e < kHeadDim * R; e += blockDim.x) Ug[e] = static_cast<float>(Ul[(e / R) * ld + e % R]);
 }
 
+// fp64 matrix cores, v_mfma_f64_16x16x4f64: A[i][k] comes from lane i + 16k, B[k][j]
+// from lane j + 16k, and element r of lane l receives D[l / 16 + 4r][l % 16].
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ f64x4 mfma_f64(double a, double b, f64x4 c) {
+    return __builtin_amdgcn_mfma_f64_16x16x4f64(a, b, c, 0, 0, 0);
+}
+
+// X^T Y for two [128][R] fp64 matrices in LDS (row strides ldx, ldy) into out [R][ldo],
+// on the matrix cores: the (R/16)^2 16 x 16 blocks are shared by the four waves,
+// each summed over the 128 rows in 32 steps of 4.  Every element of the result is
+// the same sequence of fp64 products in the same order wherever its block sits.
+template <int R, typename OutT>
+__device__ __forceinline__ void gram128(const double *X, int ldx, const double *Y, int ldy, OutT *out, int ldo) {
+    constexpr int NB = R / 16, kPer = NB * NB / 4;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, l16 = lane & 15, kq = lane >> 4;
+    f64x4 acc[kPer];
+#pragma unroll
+    for (int t = 0; t < kPer; ++t) acc[t] = f64x4{0.0, 0.0, 0.0, 0.0};
+#pragma unroll 4
+    for (int k0 = 0; k0 < kHeadDim; k0 += 4) {
+        double a[kPer], b[kPer];
+#pragma unroll
+        for (int t = 0; t < kPer; ++t) {
+            const int blk = wave * kPer + t, ib = blk / NB, jb = blk % NB;
+            a[t] = X[(k0 + kq) * ldx + 16 * ib + l16];
+            b[t] = Y[(k0 + kq) * ldy + 16 * jb + l16];
+        }
+#pragma unroll
+        for (int t = 0; t < kPer; ++t) acc[t] = mfma_f64(a[t], b[t], acc[t]);
+    }
+#pragma unroll
+    for (int t = 0; t < kPer; ++t) {
+        const int blk = wave * kPer + t, ib = blk / NB, jb = blk % NB;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) out[(16 * ib + kq + 4 * r) * ldo + 16 * jb + l16] = static_cast<OutT>(acc[t][r]);
+    }
+}
+
 // Cholesky QR of W [128][R] (fp64, LDS, row-major) applied twice: G = W^T W =
 // R_^T R_ with R_ upper triangular and a positive diagonal, then W <- W R_^{-1}.
 // One pass leaves an orthogonality error of about cond(W)^2 eps; the second
 // pass, on a W that is already orthonormal to that level, brings it to eps.  The
 // Q factor with a positive diagonal of R is unique, so this is the same Q as any
-// other QR with that convention.  256 threads; G [R][R+1] and dg [R] are scratch.
+// other QR with that convention.  256 threads; G [R][R+1] is scratch.
 template <int R>
-__device__ void cholesky_qr2(double *W, double *G, double *dg) {
-    constexpr int TS = R / 16;  // Gram tile per thread (16 x 16 threads)
+__device__ void cholesky_qr2(double *W, double *G) {
     constexpr int ldg = R + 1;
     const int tid = threadIdx.x;
     for (int pass = 0; pass < 2; ++pass) {
-        {  // G = W^T W, a TS x TS tile per thread (exactly symmetric: same products, same order)
-            const int ti = tid >> 4, tj = tid & 15;
-            double acc[TS][TS];
+        gram128<R>(W, R, W, R, G, ldg);  // G = W^T W (only the upper triangle is read)
+        __syncthreads();
+        // Cholesky factor by rows, on one wave (no workgroup barriers): lane j keeps
+        // column j of R_ in registers; at step k every lane forms
+        //   v_j = G_kj - sum_{i<k} R_ik R_ij
+        // (R_ik read from the rows already stored), R_kk = sqrt(v_k) comes from lane k,
+        // and R_kj = v_j / R_kk overwrites G_kj.  (Right-looking on the whole
+        // workgroup, with a barrier per step, this took 45 us of a 0.37 ms call;
+        // right-looking on one wave, with every lane's trailing column in registers,
+        // it spilled.)
+        if (tid < 64) {
+            const int j = tid;
+            double col[R];
 #pragma unroll
-            for (int x = 0; x < TS; ++x)
+            for (int i = 0; i < R; ++i) col[i] = 0.0;
 #pragma unroll
-                for (int y = 0; y < TS; ++y) acc[x][y] = 0.0;
-            for (int r = 0; r < kHeadDim; ++r) {
-                double a[TS], b[TS];
+            for (int k = 0; k < R; ++k) {
+                double s0 = 0.0, s1 = 0.0;
 #pragma unroll
-                for (int x = 0; x < TS; ++x) {
-                    a[x] = W[r * R + ti * TS + x];
-                    b[x] = W[r * R + tj * TS + x];
+                for (int i = 0; i < k; ++i) {
+                    const double rik = G[i * ldg + k];
+                    if (i & 1) s1 = fma(rik, col[i], s1);
+                    else s0 = fma(rik, col[i], s0);
                 }
-#pragma unroll
-                for (int x = 0; x < TS; ++x)
-#pragma unroll
-                    for (int y = 0; y < TS; ++y) acc[x][y] = fma(a[x], b[y], acc[x][y]);
+                const double v = (j < R ? G[k * ldg + (j < R ? j : 0)] : 0.0) - (s0 + s1);
+                const double rkk = sqrt(__shfl(v, k, 64));
+                const double rkj = j == k ? rkk : v / rkk;
+                if (j >= k && j < R) {
+                    col[k] = rkj;
+                    G[k * ldg + j] = rkj;
+                }
+                // row k is read back by the next steps of this wave
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
             }
-#pragma unroll
-            for (int x = 0; x < TS; ++x)
-#pragma unroll
-                for (int y = 0; y < TS; ++y) G[(ti * TS + x) * ldg + tj * TS + y] = acc[x][y];
-        }
-        __syncthreads();
-        // right-looking Cholesky on the unscaled rows: step k removes row k from the
-        // trailing block; the rows are scaled by 1/sqrt(G_kk) at the end
-        for (int k = 0; k < R - 1; ++k) {
-            const int n = R - 1 - k;
-            const double inv = 1.0 / G[k * ldg + k];
-            for (int e = tid; e < n * n; e += blockDim.x) {
-                const int i = k + 1 + e / n, j = k + 1 + e % n;
-                G[i * ldg + j] -= G[k * ldg + i] * G[k * ldg + j] * inv;
-            }
-            __syncthreads();
-        }
-        if (tid < R) dg[tid] = sqrt(G[tid * ldg + tid]);
-        __syncthreads();
-        for (int e = tid; e < R * R; e += blockDim.x) {
-            const int k = e / R, j = e % R;
-            if (j >= k) G[k * ldg + j] /= dg[k];
         }
         __syncthreads();
         // W <- W R_^{-1}: one row per thread, forward substitution in registers
@@ -263,10 +295,12 @@ __device__ void cholesky_qr2(double *W, double *G, double *dg) {
     }
 }
 
-// Fast path for R <= 64: everything per head stays in LDS.
+// Fast path for R <= 64: everything per head stays in LDS, and the products
+// (CU, U^T CU, U M and the Gram matrices of the QR) run on the fp64 matrix cores.
 //   Ud [128][R+1] fp64: U, later the Gram matrix of the QR;  Wd [128][R] fp64: C
-//   column chunks, then CU, then U', then Q;  Mf [R][R+1] fp32: U^T C U;  vs: scratch.
-// Each thread owns row a = tid / 2 and half of the columns of CU and U'.
+//   column chunks, then CU, then U', then Q;  Mf [R][R+1] fp32: U^T C U.
+// (With fp64 vector FMAs, one row and half the columns of CU and U' per thread,
+// and a workgroup-wide right-looking Cholesky, a call took 0.37 ms at 256 heads.)
 constexpr int kCChunk = 16;  // C columns staged per step
 
 template <int R>
@@ -278,19 +312,23 @@ __global__ __launch_bounds__(256) void oja_step_qr_lds_kernel(float *__restrict_
     double *Ud = lds;                                  // [128][R+1]
     double *Wd = Ud + kHeadDim * ld;                   // [128][R] (>= [128][kCChunk])
     float *Mf = reinterpret_cast<float *>(Wd + kHeadDim * R);  // [R][R+1]
-    double *vs = reinterpret_cast<double *>(Mf + R * ld + (R * ld) % 2);  // [128]
     const int64_t lh = blockIdx.x;
     const int tid = threadIdx.x;
     float *Ug = U + lh * kHeadDim * R;
     const int DD = kHeadDim * kHeadDim;
     const double inv_n = 1.0 / static_cast<double>(n);
-    const int a = tid >> 1, jh = (tid & 1) * (R / 2), nj = R / 2;
 
     for (int e = tid; e < kHeadDim * R; e += blockDim.x) Ud[(e / R) * ld + e % R] = static_cast<double>(Ug[e]);
-    // CU = C U, C staged kCChunk columns at a time (chunk partials added in order)
-    double acc[32];
+    // CU = C U on the matrix cores: wave w takes row blocks 2w and 2w + 1 and every
+    // column block; C is staged kCChunk columns at a time (row stride kCChunk + 1),
+    // the chunk partials of each entry added in chunk order
+    constexpr int NB = R / 16, kCs = kCChunk + 1;
+    const int wave = tid >> 6, lane = tid & 63, l16 = lane & 15, kq = lane >> 4;
+    f64x4 cu[2][NB];
 #pragma unroll
-    for (int q = 0; q < 32; ++q) acc[q] = 0.0;
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int cb = 0; cb < NB; ++cb) cu[hh][cb] = f64x4{0.0, 0.0, 0.0, 0.0};
     for (int c0 = 0; c0 < kHeadDim; c0 += kCChunk) {
         __syncthreads();
         for (int e = tid; e < kHeadDim * kCChunk; e += blockDim.x) {
@@ -298,51 +336,73 @@ __global__ __launch_bounds__(256) void oja_step_qr_lds_kernel(float *__restrict_
             double sum = 0.0;
             for (int64_t ch = 0; ch < nchunk; ++ch)
                 sum += static_cast<double>(Cpart[(lh * nchunk + ch) * DD + r * kHeadDim + c]);
-            Wd[r * kCChunk + e % kCChunk] = sum * inv_n;
+            Wd[r * kCs + e % kCChunk] = sum * inv_n;
         }
         __syncthreads();
-        for (int c = 0; c < kCChunk; ++c) {
-            const double cv = Wd[a * kCChunk + c];
 #pragma unroll
-            for (int q = 0; q < 32; ++q)
-                if (q < nj) acc[q] += cv * Ud[(c0 + c) * ld + jh + q];
+        for (int kk = 0; kk < kCChunk; kk += 4) {
+            double av[2], bv[NB];
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) av[hh] = Wd[(16 * (2 * wave + hh) + l16) * kCs + kk + kq];
+#pragma unroll
+            for (int cb = 0; cb < NB; ++cb) bv[cb] = Ud[(c0 + kk + kq) * ld + 16 * cb + l16];
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                for (int cb = 0; cb < NB; ++cb) cu[hh][cb] = mfma_f64(av[hh], bv[cb], cu[hh][cb]);
         }
     }
     __syncthreads();
 #pragma unroll
-    for (int q = 0; q < 32; ++q)
-        if (q < nj) Wd[a * R + jh + q] = acc[q];
-    __syncthreads();
-    // M = U^T (C U)
-    for (int e = tid; e < R * R; e += blockDim.x) {
-        const int i = e / R, j = e % R;
-        double sum = 0.0;
-        for (int r = 0; r < kHeadDim; ++r) sum += Ud[r * ld + i] * Wd[r * R + j];
-        Mf[i * ld + j] = static_cast<float>(sum);
-    }
-    __syncthreads();
-    // U' = U + eta (CU - U M), each thread on its own entries of Wd
+    for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-    for (int q = 0; q < 32; ++q) {
-        if (q < nj) {
-            const int j = jh + q;
-            double um = 0.0;
-            for (int i = 0; i < R; ++i) um += Ud[a * ld + i] * static_cast<double>(Mf[i * ld + j]);
-            Wd[a * R + j] = Ud[a * ld + j] + eta * (Wd[a * R + j] - um);
+        for (int cb = 0; cb < NB; ++cb)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) Wd[(16 * (2 * wave + hh) + kq + 4 * r) * R + 16 * cb + l16] = cu[hh][cb][r];
+    __syncthreads();
+    // M = U^T (C U), kept in fp32
+    gram128<R>(Ud, ld, Wd, R, Mf, ld);
+    __syncthreads();
+    // U' = U + eta (CU - U M): U M on the matrix cores in the blocks of CU; each lane
+    // updates the entries of Wd that its accumulators hold
+    {
+        f64x4 um[2][NB];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+            for (int cb = 0; cb < NB; ++cb) um[hh][cb] = f64x4{0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+        for (int k0 = 0; k0 < R; k0 += 4) {
+            double av[2], bv[NB];
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) av[hh] = Ud[(16 * (2 * wave + hh) + l16) * ld + k0 + kq];
+#pragma unroll
+            for (int cb = 0; cb < NB; ++cb) bv[cb] = static_cast<double>(Mf[(k0 + kq) * ld + 16 * cb + l16]);
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                for (int cb = 0; cb < NB; ++cb) um[hh][cb] = mfma_f64(av[hh], bv[cb], um[hh][cb]);
         }
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+            for (int cb = 0; cb < NB; ++cb)
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const int row = 16 * (2 * wave + hh) + kq + 4 * r, col = 16 * cb + l16;
+                    Wd[row * R + col] = Ud[row * ld + col] + eta * (Wd[row * R + col] - um[hh][cb][r]);
+                }
     }
     __syncthreads();
     // QR of U' (in Wd) by Cholesky QR twice; U is no longer needed, so its
     // storage holds the Gram matrix
-    cholesky_qr2<R>(Wd, Ud, vs);
+    cholesky_qr2<R>(Wd, Ud);
     for (int e = tid; e < kHeadDim * R; e += blockDim.x) Ug[e] = static_cast<float>(Wd[e]);
 }
 
 size_t oja_lds_bytes(int R) {
     const size_t ld = R + 1;
-    size_t b = (kHeadDim * ld + kHeadDim * R) * sizeof(double) + R * ld * sizeof(float);
-    b = (b + 7) / 8 * 8 + (2 * kHeadDim + 2) * sizeof(double);
-    return b;
+    return (kHeadDim * ld + kHeadDim * R) * sizeof(double) + R * ld * sizeof(float);
 }
 
 struct OjaGeom {
