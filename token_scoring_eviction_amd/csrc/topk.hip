@@ -96,8 +96,22 @@ __global__ __launch_bounds__(kSelThreads) void select_compact(const float *__res
         const int shift = 24 - 8 * pass;
         for (int i = threadIdx.x; i < kSelWaves * 256; i += kSelThreads) (&hist[0][0])[i] = 0u;
         __syncthreads();
+        // Keys that match the prefix add to their digit's bin.  The lanes holding the
+        // digit of the wave's first matching lane are counted with one atomic (in the
+        // first passes most keys share a few digits -- the top byte is the sign and
+        // exponent -- and 64 atomics on one LDS address serialise); the others add
+        // one each.  The bin counts are the same either way.
         auto count = [&](uint32_t key) {
-            if ((key & mask) == prefix) atomicAdd(&hist[wave][(key >> shift) & 255u], 1u);
+            const bool m = (key & mask) == prefix;
+            const uint32_t dig = (key >> shift) & 255u;
+            const uint64_t act = __ballot(m);
+            if (act == 0) return;  // uniform across the wave
+            const int first = __ffsll(static_cast<unsigned long long>(act)) - 1;
+            const uint32_t d0 = __shfl(dig, first, 64);
+            const bool same = m && dig == d0;
+            const uint64_t agg = __ballot(same);
+            if (lane == first) atomicAdd(&hist[wave][d0], static_cast<uint32_t>(__popcll(agg)));
+            else if (m && !same) atomicAdd(&hist[wave][dig], 1u);
         };
         // four 16-byte loads per thread in flight per step
         constexpr int64_t kStep = static_cast<int64_t>(kSelThreads) * 4;
