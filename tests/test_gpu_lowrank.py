@@ -60,9 +60,10 @@ def test_compress_small(gpu_lib, R):
     _compress_check(gpu_lib, inp)
 
 
-@pytest.mark.parametrize("Hq,Wq", [(2, 1), (4, 7), (16, 8)])
+@pytest.mark.parametrize("Hq,Wq", [(2, 1), (4, 7), (16, 8), (12, 14)])
 def test_compress_window_shapes(gpu_lib, Hq, Wq):
-    # |W| = g*Wq from 1 to 64 queries; ragged token tail; strided cache (S < S_stride)
+    # |W| = g*Wq of 1, 14, 64 and 84 queries (one to three 32-query blocks of the folded
+    # query); ragged token tail; strided cache (S < S_stride)
     inp = synth.oja_inputs(1, 1, 2, Hq, 333, R=64, Wq=Wq, S_cap=400, seed=Hq * 100 + Wq, device=DEV)
     _compress_check(gpu_lib, inp, S=333)
 
@@ -121,7 +122,7 @@ def test_reconstruct_small(gpu_lib, R, k):
 
 @pytest.mark.parametrize("B,N,pool,eta,R", [(1, 4096, 32, 1e-3, 64), (2, 700, 7, 0.05, 64),
                                             (1, 32, 1, 1e-3, 64), (3, 64, 1, 0.1, 64),
-                                            (1, 500, 4, 0.02, 32), (2, 300, 3, 0.02, 96),
+                                            (1, 500, 4, 0.02, 32), (2, 64, 1, 0.1, 32), (2, 300, 3, 0.02, 96),
                                             (1, 256, 1, 0.02, 128)])
 def test_oja_update_small(gpu_lib, B, N, pool, eta, R):
     # R <= 64 runs the LDS-resident step + QR, larger R the workspace-backed one
