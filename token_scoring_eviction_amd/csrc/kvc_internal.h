@@ -89,6 +89,29 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
     return u >> 16;
 }
 
+// Streaming 16-byte loads and stores (the non-temporal hint of the vector memory
+// instructions) for data touched once: on MI355X a 1 GiB copy moves 5.9-6.1 TB/s with
+// them and 5.2-5.4 TB/s without, a read-only stream 6.1-6.7 against 5.6-6.0 TB/s.
+// Data read again soon (scores, partial sums, rows re-read from the cache) keeps plain
+// accesses.
+typedef uint32_t u32x4_nt __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint4 ld_stream(const uint4 *p) {
+    const u32x4_nt t = __builtin_nontemporal_load(reinterpret_cast<const u32x4_nt *>(p));
+    return make_uint4(t.x, t.y, t.z, t.w);
+}
+__device__ __forceinline__ void st_stream(uint4 *p, const uint4 &v) {
+    const u32x4_nt t = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(t, reinterpret_cast<u32x4_nt *>(p));
+}
+__device__ __forceinline__ float4 ld_stream(const float4 *p) {
+    const uint4 u = ld_stream(reinterpret_cast<const uint4 *>(p));
+    return make_float4(__uint_as_float(u.x), __uint_as_float(u.y), __uint_as_float(u.z), __uint_as_float(u.w));
+}
+__device__ __forceinline__ void st_stream(float4 *p, const float4 &v) {
+    st_stream(reinterpret_cast<uint4 *>(p),
+              make_uint4(__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z), __float_as_uint(v.w)));
+}
+
 // Order-preserving map of an fp32 value to an unsigned key: a > b <=> key(a) > key(b).
 // -0.0 is folded onto +0.0 so that the two compare equal, as in IEEE arithmetic.
 __device__ __forceinline__ uint32_t order_key(float f) {

@@ -317,7 +317,8 @@ __global__ __launch_bounds__(kFuseThreads, KVC_FUSE_MINBLOCKS) void l2_fused(con
 #pragma unroll
         for (int r = 0; r < kFuseRows; ++r) {
             const int64_t row = t.t0 + 16 * r;
-            v[r] = row < t.w1 ? base[row * (kHeadDim / 8)] : make_uint4(0u, 0u, 0u, 0u);
+            // keys are read once (streaming loads)
+            v[r] = row < t.w1 ? ld_stream(base + row * (kHeadDim / 8)) : make_uint4(0u, 0u, 0u, 0u);
         }
     };
     // Column sums of the tile -> the team's partial slot; the last arrival of

@@ -241,21 +241,22 @@ __global__ __launch_bounds__(kSelThreads) void select_compact(const float *__res
         fetch(1, src1, ok1);
         fetch(2, src2, ok2);
         fetch(3, src3, ok3);
+        // rows are read and written once: streaming loads and stores
         if (Ks) {
-            const uint4 a0 = Ks[src0 * 16 + lane16], a1 = Ks[src1 * 16 + lane16];
-            const uint4 a2 = Ks[src2 * 16 + lane16], a3 = Ks[src3 * 16 + lane16];
-            if (ok0) Ko[(i0 + 0 * kRowsPerPass + rsub) * 16 + lane16] = a0;
-            if (ok1) Ko[(i0 + 1 * kRowsPerPass + rsub) * 16 + lane16] = a1;
-            if (ok2) Ko[(i0 + 2 * kRowsPerPass + rsub) * 16 + lane16] = a2;
-            if (ok3) Ko[(i0 + 3 * kRowsPerPass + rsub) * 16 + lane16] = a3;
+            const uint4 a0 = ld_stream(Ks + src0 * 16 + lane16), a1 = ld_stream(Ks + src1 * 16 + lane16);
+            const uint4 a2 = ld_stream(Ks + src2 * 16 + lane16), a3 = ld_stream(Ks + src3 * 16 + lane16);
+            if (ok0) st_stream(Ko + (i0 + 0 * kRowsPerPass + rsub) * 16 + lane16, a0);
+            if (ok1) st_stream(Ko + (i0 + 1 * kRowsPerPass + rsub) * 16 + lane16, a1);
+            if (ok2) st_stream(Ko + (i0 + 2 * kRowsPerPass + rsub) * 16 + lane16, a2);
+            if (ok3) st_stream(Ko + (i0 + 3 * kRowsPerPass + rsub) * 16 + lane16, a3);
         }
         if (Vs) {
-            const uint4 b0 = Vs[src0 * 16 + lane16], b1 = Vs[src1 * 16 + lane16];
-            const uint4 b2 = Vs[src2 * 16 + lane16], b3 = Vs[src3 * 16 + lane16];
-            if (ok0) Vo[(i0 + 0 * kRowsPerPass + rsub) * 16 + lane16] = b0;
-            if (ok1) Vo[(i0 + 1 * kRowsPerPass + rsub) * 16 + lane16] = b1;
-            if (ok2) Vo[(i0 + 2 * kRowsPerPass + rsub) * 16 + lane16] = b2;
-            if (ok3) Vo[(i0 + 3 * kRowsPerPass + rsub) * 16 + lane16] = b3;
+            const uint4 b0 = ld_stream(Vs + src0 * 16 + lane16), b1 = ld_stream(Vs + src1 * 16 + lane16);
+            const uint4 b2 = ld_stream(Vs + src2 * 16 + lane16), b3 = ld_stream(Vs + src3 * 16 + lane16);
+            if (ok0) st_stream(Vo + (i0 + 0 * kRowsPerPass + rsub) * 16 + lane16, b0);
+            if (ok1) st_stream(Vo + (i0 + 1 * kRowsPerPass + rsub) * 16 + lane16, b1);
+            if (ok2) st_stream(Vo + (i0 + 2 * kRowsPerPass + rsub) * 16 + lane16, b2);
+            if (ok3) st_stream(Vo + (i0 + 3 * kRowsPerPass + rsub) * 16 + lane16, b3);
         }
     }
 }
@@ -276,17 +277,31 @@ __global__ __launch_bounds__(kGatherThreads) void gather_rows(
     const int32_t *idx = idx_all + base;
     const int lane16 = threadIdx.x & 15;
     const int rsub = threadIdx.x >> 4;  // 0..15
+    constexpr int kRows = kGatherRows / 16;  // rows per thread
+    // all indices, then all row loads, then the stores: a thread keeps 2 kRows 16-byte
+    // loads in flight (issued one row at a time, each waited on its index and its load)
+    int64_t src[kRows], dst[kRows];
+    bool ok[kRows];
 #pragma unroll
-    for (int r = 0; r < kGatherRows / 16; ++r) {
+    for (int r = 0; r < kRows; ++r) {
         const int64_t i = r0 + r * 16 + rsub;
-        if (i < k) {
-            const int64_t t = idx[i];
-            if (t < 0 || t >= S) continue;  // indices come from select_compact; never read outside
-            const int64_t src = (g * s_stride + t) * (kHeadDim / 8) + lane16;
-            const int64_t dst = (base + i) * (kHeadDim / 8) + lane16;
-            if (K) reinterpret_cast<uint4 *>(K_out)[dst] = reinterpret_cast<const uint4 *>(K)[src];
-            if (V) reinterpret_cast<uint4 *>(V_out)[dst] = reinterpret_cast<const uint4 *>(V)[src];
-        }
+        const int64_t t = i < k ? idx[i] : -1;
+        ok[r] = t >= 0 && t < S;  // indices come from select_compact; never read outside
+        src[r] = (g * s_stride + (ok[r] ? t : 0)) * (kHeadDim / 8) + lane16;
+        dst[r] = (base + i) * (kHeadDim / 8) + lane16;
+    }
+    const uint4 *Ks = reinterpret_cast<const uint4 *>(K), *Vs = reinterpret_cast<const uint4 *>(V);
+    uint4 kv[kRows], vv[kRows];
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) {
+        if (K) kv[r] = ld_stream(Ks + src[r]);
+        if (V) vv[r] = ld_stream(Vs + src[r]);
+    }
+#pragma unroll
+    for (int r = 0; r < kRows; ++r) {
+        if (!ok[r]) continue;
+        if (K) st_stream(reinterpret_cast<uint4 *>(K_out) + dst[r], kv[r]);
+        if (V) st_stream(reinterpret_cast<uint4 *>(V_out) + dst[r], vv[r]);
     }
 }
 
