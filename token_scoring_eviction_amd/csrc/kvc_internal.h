@@ -92,8 +92,11 @@ __device__ __forceinline__ uint32_t f32_to_bf16_rne(float f) {
 // Streaming 16-byte loads and stores (the non-temporal hint of the vector memory
 // instructions) for data touched once: on MI355X a 1 GiB copy moves 5.9-6.1 TB/s with
 // them and 5.2-5.4 TB/s without, a read-only stream 6.1-6.7 against 5.6-6.0 TB/s.
-// Data read again soon (scores, partial sums, rows re-read from the cache) keeps plain
-// accesses.
+// Only where each instruction covers whole 128-byte lines (16 lanes x 16 bytes of a
+// row): the lines are not kept, so an access pattern that takes a line in pieces over
+// several instructions fetches it again (the projection kernel's key loads, 32 bytes
+// of a row per instruction, went 7.4 -> 8.6 ms) and partial-line stores reach HBM
+// unmerged.  Data read again soon (scores, partial sums) keeps plain accesses.
 typedef uint32_t u32x4_nt __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ uint4 ld_stream(const uint4 *p) {
     const u32x4_nt t = __builtin_nontemporal_load(reinterpret_cast<const u32x4_nt *>(p));

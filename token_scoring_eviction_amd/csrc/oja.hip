@@ -34,7 +34,7 @@ __global__ __launch_bounds__(256) void pool_kernel(const uint16_t *__restrict__ 
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     const uint4 *src = reinterpret_cast<const uint4 *>(X + slice * S_stride * kHeadDim) + lane16;
     for (int64_t t = t0; t < t1; ++t) {
-        const uint4 v = src[t * (kHeadDim / 8)];
+        const uint4 v = ld_stream(src + t * (kHeadDim / 8));  // whole rows, read once
         acc[0] += bf16_lo(v.x); acc[1] += bf16_hi(v.x);
         acc[2] += bf16_lo(v.y); acc[3] += bf16_hi(v.y);
         acc[4] += bf16_lo(v.z); acc[5] += bf16_hi(v.z);

@@ -89,11 +89,13 @@ __global__ __launch_bounds__(64 * kSumWaves) void cluster_summary_kernel(
 #pragma unroll
         for (int i = 0; i < NR; ++i) {
             const int64_t t = base + 4 * i + slot;
-            const bool ok = t < t1;
-            const int64_t ts = ok ? t : t0;  // rows past the cluster are never read
-            const uint4 a = kr[ts * (kHeadDim / 8)], b = vr[ts * (kHeadDim / 8)];
-            kc[i] = ok ? a : make_uint4(0u, 0u, 0u, 0u);
-            vc[i] = ok ? b : make_uint4(0u, 0u, 0u, 0u);
+            kc[i] = vc[i] = make_uint4(0u, 0u, 0u, 0u);
+            if (t < t1) {  // rows past the cluster are not read
+                // whole rows per 16 lanes: V is read once (streaming), and so are the
+                // keys of the first chunk (later chunks are read again for the radius)
+                kc[i] = base == t0 ? ld_stream(kr + t * (kHeadDim / 8)) : kr[t * (kHeadDim / 8)];
+                vc[i] = ld_stream(vr + t * (kHeadDim / 8));
+            }
         }
 #pragma unroll
         for (int i = 0; i < NR; ++i) {
@@ -226,9 +228,11 @@ __global__ __launch_bounds__(kRiskThreads) void risk_partial_kernel(
         for (int u = 0; u < kRiskBatch; ++u) {
             const int64_t j = j0 + 16 * (bt * kRiskBatch + u);
             const int64_t js = j < nC ? j : nC - 1;  // never past the slice's clusters
-            const float4 *m4 = reinterpret_cast<const float4 *>(mu_k + (g * nC + js) * kHeadDim + lane16 * 8);
-            a[u] = m4[0];
-            b[u] = m4[1];
+            // lane l16 holds channels 4 l16 .. + 3 and 64 + 4 l16 .. + 3: each load covers
+            // 256 contiguous bytes of the mean key (streaming: read once)
+            const float4 *m4 = reinterpret_cast<const float4 *>(mu_k + (g * nC + js) * kHeadDim) + lane16;
+            a[u] = ld_stream(m4);
+            b[u] = ld_stream(m4 + 16);
             rd[u] = radius[g * nC + js];
             vm = fmaxf(vm, vnorm[g * nC + js]);  // a repeated cluster leaves the maximum as it is
         }
@@ -238,9 +242,9 @@ __global__ __launch_bounds__(kRiskThreads) void risk_partial_kernel(
             const int64_t j = j0 + 16 * k;
             float zi = 0.f;
             for (int i = 0; i < nq; ++i) {
-                const float *q = &qs[i][lane16 * 8];
-                const float z = a[u].x * q[0] + a[u].y * q[1] + a[u].z * q[2] + a[u].w * q[3] + b[u].x * q[4] +
-                                b[u].y * q[5] + b[u].z * q[6] + b[u].w * q[7];
+                const float *q = &qs[i][lane16 * 4], *q2 = q + 64;
+                const float z = a[u].x * q[0] + a[u].y * q[1] + a[u].z * q[2] + a[u].w * q[3] + b[u].x * q2[0] +
+                                b[u].y * q2[1] + b[u].z * q2[2] + b[u].w * q2[3];
                 const float zs = sum16(z) * rs;
                 zi = lane16 == i ? zs : zi;
             }
