@@ -108,7 +108,8 @@ __device__ __forceinline__ void recon_store(OutT *xh, int64_t t0, int64_t t_end,
                 *reinterpret_cast<uint32_t *>(xh + tj * kHeadDim + cb * 32 + col) =
                     f32_to_bf16_rne(acc[j]) | (f32_to_bf16_rne(nb) << 16);
         } else {
-            if (tj < t_end) xh[tj * kHeadDim + cb * 32 + col] = acc[j];
+            // 32 lanes write one whole 128-byte line of a row: streaming store
+            if (tj < t_end) __builtin_nontemporal_store(acc[j], xh + tj * kHeadDim + cb * 32 + col);
         }
     }
 }
@@ -147,7 +148,7 @@ struct Bf16RowTile {
             const int r = (lane >> 4) + 4 * part, c = lane & 15;
             const uint4 v = *reinterpret_cast<const uint4 *>(tile + r * 256 + (((c ^ r) & 15) << 4));
             const int64_t tok = t0 + r;
-            if (tok < t_end) *reinterpret_cast<uint4 *>(xh + tok * kHeadDim + c * 8) = v;
+            if (tok < t_end) st_stream(reinterpret_cast<uint4 *>(xh + tok * kHeadDim + c * 8), v);
         }
         __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
         __builtin_amdgcn_wave_barrier();
@@ -525,7 +526,7 @@ __global__ __launch_bounds__(HB == 1 ? 1024 : 512) void project_kernel(
                     const float4 v =
                         *reinterpret_cast<const float4 *>(tile + r * kFRowB + (((c ^ r) & (kFChunks - 1)) << 4));
                     const int64_t tok = t0 + hb * 32 + r;
-                    if (tok < t_end) *reinterpret_cast<float4 *>(xt + tok * R + c * 4) = v;
+                    if (tok < t_end) st_stream(reinterpret_cast<float4 *>(xt + tok * R + c * 4), v);
                 }
                 __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
                 __builtin_amdgcn_wave_barrier();
@@ -636,7 +637,7 @@ __global__ __launch_bounds__(HB == 1 ? 1024 : 512) void project_kernel(
                 const uint4 v =
                     *reinterpret_cast<const uint4 *>(kt_tile + r * kKtRowB + (((c ^ r) & (kKtChunks - 1)) << 4));
                 const int64_t tok = t0 + r;  // row hb*32 + col is token t0 + hb*32 + col
-                if (tok < t_end) *reinterpret_cast<uint4 *>(xt + tok * R + c * 8) = v;
+                if (tok < t_end) st_stream(reinterpret_cast<uint4 *>(xt + tok * R + c * 8), v);
             }
             __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
             __builtin_amdgcn_wave_barrier();
@@ -668,7 +669,7 @@ __global__ __launch_bounds__(HB == 1 ? 1024 : 512) void project_kernel(
                     const int r = lane / kChunks + (64 / kChunks) * part, c = lane % kChunks;
                     const uint4 v = *reinterpret_cast<const uint4 *>(tile + r * kRowB + (((c ^ r) & (kChunks - 1)) << 4));
                     const int64_t tok = t0 + hb * 32 + r;
-                    if (tok < t_end) *reinterpret_cast<uint4 *>(xt + tok * R + c * 8) = v;
+                    if (tok < t_end) st_stream(reinterpret_cast<uint4 *>(xt + tok * R + c * 8), v);
                 }
                 __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
                 __builtin_amdgcn_wave_barrier();
