@@ -915,8 +915,9 @@ __global__ __launch_bounds__(256) void anchor_copy_bf16_kernel(const int32_t *__
     if (i >= k) return;
     const int64_t t = idx[g * k + i];
     if (t < 0 || t >= S) return;  // documented precondition; never write outside the slice
-    reinterpret_cast<uint4 *>(Xh + (g * S_stride + t) * kHeadDim)[lane16] =
-        reinterpret_cast<const uint4 *>(rows + (g * k + i) * kHeadDim)[lane16];
+    // whole rows per 16 lanes, touched once: streaming load and store
+    st_stream(reinterpret_cast<uint4 *>(Xh + (g * S_stride + t) * kHeadDim) + lane16,
+              ld_stream(reinterpret_cast<const uint4 *>(rows + (g * k + i) * kHeadDim) + lane16));
 }
 
 // Anchor rows back into X^: 16 lanes per row, bf16 widened exactly.
@@ -931,10 +932,14 @@ __global__ __launch_bounds__(256) void anchor_scatter_kernel(const int32_t *__re
     if (i >= k) return;
     const int64_t t = idx[g * k + i];
     if (t < 0 || t >= S) return;  // documented precondition; never write outside the slice
-    const uint4 v = reinterpret_cast<const uint4 *>(rows + (g * k + i) * kHeadDim)[lane16];
-    float4 *dst = reinterpret_cast<float4 *>(Xh + (g * S_stride + t) * kHeadDim + lane16 * 8);
-    dst[0] = make_float4(bf16_lo(v.x), bf16_hi(v.x), bf16_lo(v.y), bf16_hi(v.y));
-    dst[1] = make_float4(bf16_lo(v.z), bf16_hi(v.z), bf16_lo(v.w), bf16_hi(v.w));
+    // lane l16 takes channels 4 l16 .. + 3 and 64 + 4 l16 .. + 3, so each load covers a
+    // contiguous 128-byte line of the bf16 row and each store 256 contiguous bytes of the
+    // fp32 row (streaming: the rows are touched once)
+    const uint2 *src = reinterpret_cast<const uint2 *>(rows + (g * k + i) * kHeadDim);
+    const uint2 v0 = src[lane16], v1 = src[16 + lane16];
+    float4 *dst = reinterpret_cast<float4 *>(Xh + (g * S_stride + t) * kHeadDim);
+    st_stream(dst + lane16, make_float4(bf16_lo(v0.x), bf16_hi(v0.x), bf16_lo(v0.y), bf16_hi(v0.y)));
+    st_stream(dst + 16 + lane16, make_float4(bf16_lo(v1.x), bf16_hi(v1.x), bf16_lo(v1.y), bf16_hi(v1.y)));
 }
 
 // ------------------------------------------------------------------- host
