@@ -196,14 +196,14 @@ def manifold_workload(cfg, dev, metric="l2", budgets="uniform"):
                       lambda: kvc.kvc_topk_compact_ragged(buf.scores, ks, K, V, idx_out=rbuf[0],
                                                           K_out=rbuf[1], V_out=rbuf[2]),
                       G * S * 4 + total * (2 * 256 * 2 + 4),
-                      kernel="select_compact" if ks.max() <= 8192 and G >= 256 else "select_compact+gather_rows"))
+                      kernel=compaction_kernels(ks.max(), G)))
         desc += "; RippleKV per-layer budgets %d..%d (r=8, gamma=4)" % (kl.min(), kl.max())
     else:
         ops.append(Op("kvc_topk_compact",
                       lambda: kvc.kvc_topk_compact(buf.scores, keep, K, V, idx_out=buf.idx, K_out=buf.K_out,
                                                    V_out=buf.V_out),
                       G * S * 4 + G * keep * (2 * 256 * 2 + 4),
-                      kernel="select_compact" if keep <= 8192 and G >= 256 else "select_compact+gather_rows"))
+                      kernel=compaction_kernels(keep, G)))
     algo = G * S * 256 + G * keep * 256 + 2 * G * keep * 256 + G * S * 4 + G * keep * 4
     config = {"workload": desc, "slices": G, "seq_len": S, "keep": keep, "head_dim": 128,
               "window": W, "metric": metric, "budgets": budgets}
@@ -230,6 +230,15 @@ def manifold_workload(cfg, dev, metric="l2", budgets="uniform"):
             done, S, G)
 
     return ops, G * S, algo, config, cpu
+
+
+def compaction_kernels(k, G):
+    """Kernels behind kvc_topk_compact: the selection, then the wide gather of the kept rows
+    (the selecting workgroups copy the rows themselves only with KVC_GATHER_SEPARATE=0,
+    k <= 8192 and a slice per compute unit or more)."""
+    if os.environ.get("KVC_GATHER_SEPARATE") == "0" and k <= 8192 and G >= 256:
+        return "select_compact"
+    return "select_compact+gather_rows"
 
 
 def refine_workload(dev):
@@ -298,7 +307,7 @@ def oja_workload(dev, storage="fp32"):
         Op("kvc_topk_compact",
            lambda: kvc.kvc_topk_compact(st.err, k, inp.K, inp.V, idx_out=st.idx, K_out=st.K_anchor,
                                         V_out=st.V_anchor),
-           G * S * 4 + G * k * (2 * 256 * 2 + 4), kernel="select_compact"),
+           G * S * 4 + G * k * (2 * 256 * 2 + 4), kernel=compaction_kernels(k, G)),
     ]
     algo = G * S * (2 * 256 + 2 * R * ob + 4) + G * k * (2 * 256 * 2 + 4)
     config = {"workload": "OjaKV hybrid low-rank prefill compression, 32 layers x batch 4 x 8 KV heads "

@@ -83,12 +83,11 @@ def test_topk_strided_and_gather_bit_exact(gpu_lib):
 
 @pytest.mark.parametrize("separate", [False, True])
 def test_gather_paths_bit_exact(gpu_lib, monkeypatch, separate):
-    # 300 slices (more than one per compute unit, so the selecting workgroup copies the
-    # rows itself unless the separate launch is forced), ragged S, strided cache,
-    # k from 1 to S including the 8192-row boundary of the in-workgroup copy
+    # 300 slices (more than one per compute unit, so KVC_GATHER_SEPARATE=0 has the selecting
+    # workgroup copy the rows itself; 1 selects the wide gather, the default), ragged S,
+    # strided cache, k from 1 to S including the 8192-row boundary of the in-workgroup copy
     G, S, stride = 300, 8197, 8200
-    if separate:
-        monkeypatch.setenv("KVC_GATHER_SEPARATE", "1")
+    monkeypatch.setenv("KVC_GATHER_SEPARATE", "1" if separate else "0")
     K = torch.randint(-32768, 32767, (G, stride, 128), dtype=torch.int16, device=DEV).view(torch.bfloat16)
     V = torch.randint(-32768, 32767, (G, stride, 128), dtype=torch.int16, device=DEV).view(torch.bfloat16)
     s = synth.random_scores(G, stride, seed=11, kind="ties", device="cpu")

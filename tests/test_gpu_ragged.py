@@ -34,8 +34,7 @@ def _check_packed(idx, Ko, Vo, ks, s_host, Kb, Vb, S=None):
 def test_ragged_layer_budgets_bit_exact(gpu_lib, monkeypatch, separate):
     # 30 layers x 10 slices, S = 5000 with a ragged stride; budgets from a sensitivity
     # profile (some layers pinned at S, none empty) and ties in the scores
-    if separate:
-        monkeypatch.setenv("KVC_GATHER_SEPARATE", "1")
+    monkeypatch.setenv("KVC_GATHER_SEPARATE", "1" if separate else "0")
     L, per, S, stride = 30, 10, 5000, 5003
     G = L * per
     rng = np.random.default_rng(21)
