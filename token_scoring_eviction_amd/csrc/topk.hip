@@ -261,8 +261,11 @@ __global__ __launch_bounds__(kSelThreads) void select_compact(const float *__res
     }
 }
 
-constexpr int kGatherThreads = 256;
-constexpr int kGatherRows = 16;  // rows per block: one per thread (more, smaller workgroups move rows faster)
+// one wave per workgroup, one row per 16 lanes: many small workgroups move the rows
+// fastest (256 x 16384, keep 8192: 0.369 ms with 64 threads, 0.377-0.382 with 256 and
+// one row per thread, 0.410-0.414 with 256 and four rows per thread)
+constexpr int kGatherThreads = 64;
+constexpr int kGatherRows = 4;  // rows per workgroup
 
 // kg / koff as for select_compact (nullable: k_all rows per slice at g * k_all).
 __global__ __launch_bounds__(kGatherThreads) void gather_rows(
@@ -276,15 +279,16 @@ __global__ __launch_bounds__(kGatherThreads) void gather_rows(
     const int64_t base = koff ? koff[g] : g * k_all;
     const int32_t *idx = idx_all + base;
     const int lane16 = threadIdx.x & 15;
-    const int rsub = threadIdx.x >> 4;  // 0..15
-    constexpr int kRows = kGatherRows / 16;  // rows per thread
+    const int rsub = threadIdx.x >> 4;  // row of the pass
+    constexpr int kPass = kGatherThreads / 16;  // rows per pass of the workgroup
+    constexpr int kRows = kGatherRows / kPass;  // rows per thread
     // all indices, then all row loads, then the stores: a thread keeps 2 kRows 16-byte
     // loads in flight (issued one row at a time, each waited on its index and its load)
     int64_t src[kRows], dst[kRows];
     bool ok[kRows];
 #pragma unroll
     for (int r = 0; r < kRows; ++r) {
-        const int64_t i = r0 + r * 16 + rsub;
+        const int64_t i = r0 + r * kPass + rsub;
         const int64_t t = i < k ? idx[i] : -1;
         ok[r] = t >= 0 && t < S;  // indices come from select_compact; never read outside
         src[r] = (g * s_stride + (ok[r] ? t : 0)) * (kHeadDim / 8) + lane16;
