@@ -903,14 +903,19 @@ __global__ __launch_bounds__(256) void reconstruct_bf16_kernel(const uint16_t *_
 #undef KVC_LOAD_XB
 }
 
+// Row kernels (anchor rows): one wave per workgroup, 16 lanes per 256-byte row; many
+// small workgroups move rows fastest (as measured for the compaction gather).
+constexpr int kRowThreads = 64;
+constexpr int kRowsPerBlock = kRowThreads / 16;
+
 // Anchor rows of a bf16 X^: a bit-exact copy, 16 lanes per row.
-__global__ __launch_bounds__(256) void anchor_copy_bf16_kernel(const int32_t *__restrict__ idx,
+__global__ __launch_bounds__(kRowThreads) void anchor_copy_bf16_kernel(const int32_t *__restrict__ idx,
                                                                const uint16_t *__restrict__ rows,
                                                                int64_t k, int64_t blocks_per_slice,
                                                                int64_t S, int64_t S_stride,
                                                                uint16_t *__restrict__ Xh) {
     const int64_t g = blockIdx.x / blocks_per_slice;
-    const int64_t i = (blockIdx.x % blocks_per_slice) * 16 + (threadIdx.x >> 4);
+    const int64_t i = (blockIdx.x % blocks_per_slice) * kRowsPerBlock + (threadIdx.x >> 4);
     const int lane16 = threadIdx.x & 15;
     if (i >= k) return;
     const int64_t t = idx[g * k + i];
@@ -921,13 +926,13 @@ __global__ __launch_bounds__(256) void anchor_copy_bf16_kernel(const int32_t *__
 }
 
 // Anchor rows back into X^: 16 lanes per row, bf16 widened exactly.
-__global__ __launch_bounds__(256) void anchor_scatter_kernel(const int32_t *__restrict__ idx,
+__global__ __launch_bounds__(kRowThreads) void anchor_scatter_kernel(const int32_t *__restrict__ idx,
                                                              const uint16_t *__restrict__ rows,
                                                              int64_t k, int64_t blocks_per_slice,
                                                              int64_t S, int64_t S_stride,
                                                              float *__restrict__ Xh) {
     const int64_t g = blockIdx.x / blocks_per_slice;
-    const int64_t i = (blockIdx.x % blocks_per_slice) * 16 + (threadIdx.x >> 4);
+    const int64_t i = (blockIdx.x % blocks_per_slice) * kRowsPerBlock + (threadIdx.x >> 4);
     const int lane16 = threadIdx.x & 15;
     if (i >= k) return;
     const int64_t t = idx[g * k + i];
@@ -1129,18 +1134,18 @@ kvc_status reconstruct_dispatch(const kvc_dims *d, const OutT *Xt, const float *
 // checked by the caller; out-of-slice indices are skipped by the kernels.
 kvc_status launch_anchors(const int32_t *idx, const uint16_t *rows, int64_t k, int64_t G, int64_t S,
                           int64_t S_stride, float *Xh, hipStream_t stream) {
-    const int64_t bps = (k + 15) / 16;
+    const int64_t bps = (k + kRowsPerBlock - 1) / kRowsPerBlock;
     if (G * bps > INT32_MAX) return KVC_ERR_UNSUPPORTED;
-    hipLaunchKernelGGL(anchor_scatter_kernel, dim3(static_cast<unsigned>(G * bps)), dim3(256), 0, stream,
+    hipLaunchKernelGGL(anchor_scatter_kernel, dim3(static_cast<unsigned>(G * bps)), dim3(kRowThreads), 0, stream,
                        idx, rows, k, bps, S, S_stride, Xh);
     return launch_status();
 }
 
 kvc_status launch_anchors(const int32_t *idx, const uint16_t *rows, int64_t k, int64_t G, int64_t S,
                           int64_t S_stride, uint16_t *Xh, hipStream_t stream) {
-    const int64_t bps = (k + 15) / 16;
+    const int64_t bps = (k + kRowsPerBlock - 1) / kRowsPerBlock;
     if (G * bps > INT32_MAX) return KVC_ERR_UNSUPPORTED;
-    hipLaunchKernelGGL(anchor_copy_bf16_kernel, dim3(static_cast<unsigned>(G * bps)), dim3(256), 0, stream,
+    hipLaunchKernelGGL(anchor_copy_bf16_kernel, dim3(static_cast<unsigned>(G * bps)), dim3(kRowThreads), 0, stream,
                        idx, rows, k, bps, S, S_stride, Xh);
     return launch_status();
 }

@@ -23,10 +23,11 @@ namespace {
 
 constexpr int kCovStage = 64;  // pooled rows staged in LDS per step
 
-__global__ __launch_bounds__(256) void pool_kernel(const uint16_t *__restrict__ X, int64_t rows,
+constexpr int kPoolThreads = 64;  // one wave, four pooled rows per workgroup
+__global__ __launch_bounds__(kPoolThreads) void pool_kernel(const uint16_t *__restrict__ X, int64_t rows,
                                                    int64_t N, int64_t S_stride, int p, int64_t np,
                                                    float *__restrict__ Xp) {
-    const int64_t r = static_cast<int64_t>(blockIdx.x) * 16 + (threadIdx.x >> 4);
+    const int64_t r = static_cast<int64_t>(blockIdx.x) * (kPoolThreads / 16) + (threadIdx.x >> 4);
     const int lane16 = threadIdx.x & 15;
     if (r >= rows) return;
     const int64_t slice = r / np, i = r % np;
@@ -479,9 +480,9 @@ extern "C" kvc_status kvc_oja_update(const kvc_dims *d, float *U, const uint16_t
     double *M64 = cur.take<double>(static_cast<size_t>(o.LH * d->R * d->R));
 
     const int64_t rows = o.G * o.np;
-    const int64_t pb = (rows + 15) / 16;
+    const int64_t pb = (rows + kPoolThreads / 16 - 1) / (kPoolThreads / 16);
     if (pb > INT32_MAX || o.LH * o.nchunk > INT32_MAX) return KVC_ERR_UNSUPPORTED;
-    hipLaunchKernelGGL(pool_kernel, dim3(static_cast<unsigned>(pb)), dim3(256), 0, stream, X, rows,
+    hipLaunchKernelGGL(pool_kernel, dim3(static_cast<unsigned>(pb)), dim3(kPoolThreads), 0, stream, X, rows,
                        o.N, o.S_stride, pool, o.np, Xp);
     hipLaunchKernelGGL(cov_partial_kernel, dim3(static_cast<unsigned>(o.LH * o.nchunk)), dim3(256), 0,
                        stream, Xp, d->B, d->H_kv, o.np, o.rows_per_chunk, o.nchunk, Cpart);

@@ -29,7 +29,7 @@
 namespace kvc {
 namespace {
 
-constexpr int kSumWaves = 4;             // clusters per summary workgroup
+constexpr int kSumWaves = 1;             // clusters per summary workgroup (one wave: 3.39 -> 3.15 ms for 32-key clusters at 256 x 131072)
 constexpr int kRiskThreads = 256;        // both risk passes
 constexpr int kMaxRiskQueries = 8;
 constexpr int kRiskBatch = 2;            // clusters per 16-lane row loaded before any is used
