@@ -627,9 +627,11 @@ kvc_status score_windowed_impl(const uint16_t *K, int64_t G, int64_t S, int32_t 
         void *args[] = {&K, &fa, &partial, &mu_pub, &counters, &status, &scores, &mu_user};
         if (hipLaunchCooperativeKernel(fused,
                                        dim3(static_cast<unsigned>(grid)), dim3(kFuseThreads), args, 0,
-                                       stream) != hipSuccess)
-            return KVC_ERR_HIP;
-        return launch_status();
+                                       stream) == hipSuccess)
+            return launch_status();
+        // the runtime refused the co-resident grid: the three-launch path below computes
+        // the same scores without it (its workspace layout fits the same buffer)
+        (void)hipGetLastError();
     }
 
     const WinGeom geo = make_geom(G, S, W, metric);
