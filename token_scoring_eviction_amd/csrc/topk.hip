@@ -11,6 +11,9 @@
 //     the keys that still match the prefix, then a 256-bin suffix scan finds
 //     the digit holding the k-th largest key; after 4 passes the threshold
 //     key T is exact and `need` = how many keys equal to T are kept;
+//   - slices of up to 16 x 4096 scores are read once: each thread keeps its
+//     keys in registers for the four passes and the ordered pass (longer
+//     slices read the scores again at every pass);
 //   - one ordered pass in 4096-key tiles: a packed (greater, equal) count
 //     scan gives every kept key its output slot, equal keys taken lowest
 //     index first until `need` are taken.
@@ -60,8 +63,16 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t *w
     return excl;
 }
 
+// Longest slice whose keys are held in registers: 16 tiles of 4096 keys, 64 keys
+// (64 VGPRs) per thread.
+constexpr int kMaxHeldTiles = 16;
+
 // kg / koff (device, nullable): per-slice budget and output offset (packed
 // outputs); otherwise every slice keeps k and its outputs start at g * k.
+// NT > 0: the slice holds at most NT * kTile scores; key t * kTile + 4 * thread + j
+// is read once into held[t][j] and every pass reads it there.  NT == 0: each pass
+// reads the scores again.
+template <int NT>
 __global__ __launch_bounds__(kSelThreads) void select_compact(const float *__restrict__ scores,
                                                               int64_t S, int64_t s_stride,
                                                               int64_t k_all,
@@ -92,6 +103,25 @@ __global__ __launch_bounds__(kSelThreads) void select_compact(const float *__res
     const bool vec = (reinterpret_cast<uintptr_t>(s) & 15u) == 0;
     const int64_t S4 = vec ? S / 4 * 4 : 0;
 
+    uint32_t held[NT > 0 ? NT : 1][kPerThread];
+    if constexpr (NT > 0) {
+        // every thread's loads in flight at once
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            const int64_t i0 = static_cast<int64_t>(t) * kTile + static_cast<int64_t>(threadIdx.x) * kPerThread;
+            if (vec && i0 + kPerThread <= S) {
+                const float4 x = *reinterpret_cast<const float4 *>(s + i0);
+                held[t][0] = order_key(x.x);
+                held[t][1] = order_key(x.y);
+                held[t][2] = order_key(x.z);
+                held[t][3] = order_key(x.w);
+            } else {
+#pragma unroll
+                for (int j = 0; j < kPerThread; ++j) held[t][j] = i0 + j < S ? order_key(s[i0 + j]) : 0u;
+            }
+        }
+    }
+
     for (int pass = 0; pass < 4; ++pass) {
         const int shift = 24 - 8 * pass;
         for (int i = threadIdx.x; i < kSelWaves * 256; i += kSelThreads) (&hist[0][0])[i] = 0u;
@@ -100,9 +130,12 @@ __global__ __launch_bounds__(kSelThreads) void select_compact(const float *__res
         // digit of the wave's first matching lane are counted with one atomic (in the
         // first passes most keys share a few digits -- the top byte is the sign and
         // exponent -- and 64 atomics on one LDS address serialise); the others add
-        // one each.  The bin counts are the same either way.
-        auto count = [&](uint32_t key) {
-            const bool m = (key & mask) == prefix;
+        // one each.  The bin counts are the same either way.  (Further rounds of this
+        // aggregation measured slower on the eviction workloads: 0.030 -> 0.033 ms at
+        // 256 x 16384, 0.086 -> 0.096 ms at 256 x 65536; faster only on concentrated
+        // error scores, 0.175 -> 0.165 ms at 1024 x 32768.)
+        auto count = [&](uint32_t key, bool valid) {
+            const bool m = valid && (key & mask) == prefix;
             const uint32_t dig = (key >> shift) & 255u;
             const uint64_t act = __ballot(m);
             if (act == 0) return;  // uniform across the wave
@@ -113,23 +146,31 @@ __global__ __launch_bounds__(kSelThreads) void select_compact(const float *__res
             if (lane == first) atomicAdd(&hist[wave][d0], static_cast<uint32_t>(__popcll(agg)));
             else if (m && !same) atomicAdd(&hist[wave][dig], 1u);
         };
-        // four 16-byte loads per thread in flight per step
-        constexpr int64_t kStep = static_cast<int64_t>(kSelThreads) * 4;
-        for (int64_t i = static_cast<int64_t>(threadIdx.x) * 4; i < S4; i += 4 * kStep) {
-            float4 x[4];
+        if constexpr (NT > 0) {
 #pragma unroll
-            for (int u = 0; u < 4; ++u)
-                if (i + u * kStep < S4) x[u] = *reinterpret_cast<const float4 *>(s + i + u * kStep);
+            for (int t = 0; t < NT; ++t)
 #pragma unroll
-            for (int u = 0; u < 4; ++u)
-                if (i + u * kStep < S4) {
-                    count(order_key(x[u].x));
-                    count(order_key(x[u].y));
-                    count(order_key(x[u].z));
-                    count(order_key(x[u].w));
-                }
+                for (int j = 0; j < kPerThread; ++j)
+                    count(held[t][j], static_cast<int64_t>(t) * kTile + static_cast<int64_t>(threadIdx.x) * kPerThread + j < S);
+        } else {
+            // four 16-byte loads per thread in flight per step
+            constexpr int64_t kStep = static_cast<int64_t>(kSelThreads) * 4;
+            for (int64_t i = static_cast<int64_t>(threadIdx.x) * 4; i < S4; i += 4 * kStep) {
+                float4 x[4];
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    if (i + u * kStep < S4) x[u] = *reinterpret_cast<const float4 *>(s + i + u * kStep);
+#pragma unroll
+                for (int u = 0; u < 4; ++u)
+                    if (i + u * kStep < S4) {
+                        count(order_key(x[u].x), true);
+                        count(order_key(x[u].y), true);
+                        count(order_key(x[u].z), true);
+                        count(order_key(x[u].w), true);
+                    }
+            }
+            for (int64_t i = S4 + threadIdx.x; i < S; i += kSelThreads) count(order_key(s[i]), true);
         }
-        for (int64_t i = S4 + threadIdx.x; i < S; i += kSelThreads) count(order_key(s[i]));
         __syncthreads();
         // suffix sums over bins, suffix[b] = count of matching keys with digit >= b:
         // a 64-lane suffix scan per wave over its 64 bins, then the waves above added
@@ -170,20 +211,10 @@ __global__ __launch_bounds__(kSelThreads) void select_compact(const float *__res
 
     uint32_t out_pos = 0;  // kept so far (uniform across the block)
     uint32_t eq_seen = 0;  // keys equal to T seen so far
-    for (int64_t base = 0; base < S; base += kTile) {
+    // one 4096-key tile of the ordered pass, keys[j] = key of index base + 4 * thread + j
+    auto ordered_tile = [&](int64_t base, const uint32_t (&keys)[kPerThread]) {
         const int64_t i0 = base + static_cast<int64_t>(threadIdx.x) * kPerThread;
-        uint32_t keys[kPerThread];
         uint32_t n_gt = 0, n_eq = 0;
-        if (vec && i0 + kPerThread <= S) {
-            const float4 x = *reinterpret_cast<const float4 *>(s + i0);
-            keys[0] = order_key(x.x);
-            keys[1] = order_key(x.y);
-            keys[2] = order_key(x.z);
-            keys[3] = order_key(x.w);
-        } else {
-#pragma unroll
-            for (int j = 0; j < kPerThread; ++j) keys[j] = i0 + j < S ? order_key(s[i0 + j]) : 0u;
-        }
 #pragma unroll
         for (int j = 0; j < kPerThread; ++j) {
             const int64_t i = i0 + j;
@@ -215,6 +246,29 @@ __global__ __launch_bounds__(kSelThreads) void select_compact(const float *__res
         }
         out_pos += tile_gt + (min(eq_seen + tile_eq, need) - min(eq_seen, need));
         eq_seen += tile_eq;
+    };
+    if constexpr (NT > 0) {
+#pragma unroll
+        for (int t = 0; t < NT; ++t) {
+            if (static_cast<int64_t>(t) * kTile >= S) break;  // uniform across the block
+            ordered_tile(static_cast<int64_t>(t) * kTile, held[t]);
+        }
+    } else {
+        for (int64_t base = 0; base < S; base += kTile) {
+            const int64_t i0 = base + static_cast<int64_t>(threadIdx.x) * kPerThread;
+            uint32_t keys[kPerThread];
+            if (vec && i0 + kPerThread <= S) {
+                const float4 x = *reinterpret_cast<const float4 *>(s + i0);
+                keys[0] = order_key(x.x);
+                keys[1] = order_key(x.y);
+                keys[2] = order_key(x.z);
+                keys[3] = order_key(x.w);
+            } else {
+#pragma unroll
+                for (int j = 0; j < kPerThread; ++j) keys[j] = i0 + j < S ? order_key(s[i0 + j]) : 0u;
+            }
+            ordered_tile(base, keys);
+        }
     }
     if (!K && !V) return;
     // Compaction of the slice's rows by the same workgroup, as soon as its
@@ -319,6 +373,24 @@ bool fused_gather() {
     return e && e[0] == '0';
 }
 
+// select_compact for a slice length S: the register-held instance with the fewest
+// tiles that covers S, else the instance that reads the scores at every pass.
+void launch_select(int64_t G, int64_t S, hipStream_t stream, const float *scores, int64_t s_stride,
+                   int64_t k_all, const int64_t *kg, const int64_t *koff, int32_t *idx_out,
+                   const uint16_t *K, const uint16_t *V, uint16_t *K_out, uint16_t *V_out) {
+    const dim3 grid(static_cast<unsigned>(G)), block(kSelThreads);
+#define KVC_SELECT(nt)                                                                            \
+    hipLaunchKernelGGL(select_compact<nt>, grid, block, 0, stream, scores, S, s_stride, k_all, kg, \
+                       koff, idx_out, K, V, K_out, V_out)
+    if (S <= 1 * kTile) KVC_SELECT(1);
+    else if (S <= 2 * kTile) KVC_SELECT(2);
+    else if (S <= 4 * kTile) KVC_SELECT(4);
+    else if (S <= 8 * kTile) KVC_SELECT(8);
+    else if (S <= kMaxHeldTiles * kTile) KVC_SELECT(kMaxHeldTiles);
+    else KVC_SELECT(0);
+#undef KVC_SELECT
+}
+
 }  // namespace
 
 size_t topk_workspace_bytes(int64_t, int64_t, int64_t) { return 0; }
@@ -351,13 +423,11 @@ extern "C" kvc_status kvc_topk_compact(const float *scores, int64_t G, int64_t S
     // (k <= 8192 rows per slice) and there are enough slices to occupy every compute
     // unit; otherwise the copy goes to a wide gather launch
     if ((K || V) && k <= 8192 && G >= device_cu_count() && fused_gather()) {
-        hipLaunchKernelGGL(select_compact, dim3(static_cast<unsigned>(G)), dim3(kSelThreads), 0, stream,
-                           scores, S, s_stride, k, nullptr, nullptr, idx_out, K, V, K_out, V_out);
+        launch_select(G, S, stream, scores, s_stride, k, nullptr, nullptr, idx_out, K, V, K_out, V_out);
         return launch_status();
     }
-    hipLaunchKernelGGL(select_compact, dim3(static_cast<unsigned>(G)), dim3(kSelThreads), 0, stream,
-                       scores, S, s_stride, k, nullptr, nullptr, idx_out, nullptr, nullptr, nullptr,
-                       nullptr);
+    launch_select(G, S, stream, scores, s_stride, k, nullptr, nullptr, idx_out, nullptr, nullptr, nullptr,
+                  nullptr);
     if (K || V) {
         const int64_t bps = (k + kGatherRows - 1) / kGatherRows;
         if (G * bps > INT32_MAX) return KVC_ERR_UNSUPPORTED;
@@ -407,12 +477,11 @@ extern "C" kvc_status kvc_topk_compact_ragged(const float *scores, int64_t G, in
         hipSuccess)
         return KVC_ERR_HIP;
     if ((K || V) && kmax <= 8192 && G >= device_cu_count() && fused_gather()) {
-        hipLaunchKernelGGL(select_compact, dim3(static_cast<unsigned>(G)), dim3(kSelThreads), 0, stream,
-                           scores, S, s_stride, int64_t{0}, kg, koff, idx_out, K, V, K_out, V_out);
+        launch_select(G, S, stream, scores, s_stride, int64_t{0}, kg, koff, idx_out, K, V, K_out, V_out);
         return launch_status();
     }
-    hipLaunchKernelGGL(select_compact, dim3(static_cast<unsigned>(G)), dim3(kSelThreads), 0, stream,
-                       scores, S, s_stride, int64_t{0}, kg, koff, idx_out, nullptr, nullptr, nullptr, nullptr);
+    launch_select(G, S, stream, scores, s_stride, int64_t{0}, kg, koff, idx_out, nullptr, nullptr, nullptr,
+                  nullptr);
     if (K || V) {
         const int64_t bps = (kmax + kGatherRows - 1) / kGatherRows;
         if (G * bps > INT32_MAX) return KVC_ERR_UNSUPPORTED;
