@@ -1,0 +1,307 @@
+"""Writes the worked-example fixtures in tests/golden/ from the definitions on the
+pages, with exact rational arithmetic (fractions) and 60-digit decimals.  It
+uses neither the oracle nor the HIP library, so the stored values pin both.
+
+    python tests/golden/make_golden.py
+
+Every input is integer-valued (exact in bf16) and every basis is a signed
+selection of coordinate columns (exactly orthonormal in fp32), so each
+expected value is an exact rational, or a 60-digit decimal where the
+definition takes a square root or an exponential.  D = 128 throughout, the
+head size the GPU library is built for, and R = 32, its smallest rank.
+
+Fixtures (each names the passage it follows in its "source" field):
+  manifold_tiny.json  Euclidean distance of every key to the slice centroid
+                      and to its contiguous window's centroid; the kept set.
+  lowrank_tiny.json   K~ = K U_k, V~ = V U_v, the query-weighted error score,
+                      the full-rank anchors and the reconstruction.
+  oja_tiny.json       average pooling, one Oja step on the pooled empirical
+                      covariance, then QR with a positive diagonal.
+  refine_tiny.json    contiguous-cluster summaries and the Figure 2 risk score.
+  pages_figures.json  figures the pages print, with the passage of each.
+"""
+from __future__ import annotations
+
+import json
+import os
+import random
+from decimal import Decimal, getcontext
+from fractions import Fraction as Fr
+
+getcontext().prec = 60
+D = 128
+HERE = os.path.dirname(os.path.abspath(__file__))
+
+OJA_PAGE = "OjaKV: Context-Aware Online Low-Rank KV Cache Compression (deep-notes page)"
+MKV_PAGE = "ManifoldKV: Training-Free KV Cache Compression via Euclidean Outlier Detection (ICML 2026 poster page)"
+RFK_PAGE = "RefineKV (project page)"
+
+
+def fs(x: Fr) -> str:
+    return str(x)
+
+
+def dec(x: Fr) -> Decimal:
+    return Decimal(x.numerator) / Decimal(x.denominator)
+
+
+def ds(x: Decimal) -> str:
+    return format(x, ".18e")
+
+
+def dsqrt(x: Fr) -> Decimal:
+    return dec(x).sqrt()
+
+
+def keep_top(values, k):
+    """Indices of the k largest values (ties: lower index first), ascending."""
+    order = sorted(range(len(values)), key=lambda t: (-values[t], t))
+    return sorted(order[:k])
+
+
+def ints(rnd, lo, hi, *shape):
+    if len(shape) == 1:
+        return [rnd.randint(lo, hi) for _ in range(shape[0])]
+    return [ints(rnd, lo, hi, *shape[1:]) for _ in range(shape[0])]
+
+
+def signed_selection(rnd, R):
+    """Columns cols[j] of the identity with signs sign[j]: an exactly orthonormal D x R basis."""
+    return rnd.sample(range(D), R), [rnd.choice((-1, 1)) for _ in range(R)]
+
+
+# --------------------------------------------------------------- ManifoldKV
+
+def manifold(seed=1):
+    rnd = random.Random(seed)
+    G, S, W, k = 2, 20, 8, 7
+    K = ints(rnd, -8, 8, G, S, D)
+    for g in range(G):  # two far keys per slice (x4, still exact in bf16)
+        for t in rnd.sample(range(S), 2):
+            K[g][t] = [4 * x for x in K[g][t]]
+
+    def part(lo, hi, Kg):
+        mu = [Fr(sum(Kg[t][c] for t in range(lo, hi)), hi - lo) for c in range(D)]
+        s2 = [sum((Kg[t][c] - mu[c]) ** 2 for c in range(D)) for t in range(lo, hi)]
+        return mu, s2
+
+    out = {}
+    for name, win in (("global", S), ("windowed", W)):
+        mus, s2s, keeps = [], [], []
+        for g in range(G):
+            mu_g, s2_g = [], []
+            for lo in range(0, S, win):
+                mu, s2 = part(lo, min(lo + win, S), K[g])
+                mu_g.append([fs(x) for x in mu])
+                s2_g += s2
+            # the kept set is unique under a 1e-4 score tolerance
+            srt = sorted(s2_g, reverse=True)
+            assert srt[k - 1] > srt[k] * Fr(10021, 10000), "margin at the k-th score"
+            mus.append(mu_g)
+            s2s.append([fs(x) for x in s2_g])
+            keeps.append(keep_top(s2_g, k))
+        out[name] = {"W": win, "centroids": mus, "squared_scores": s2s, "keep_idx": keeps}
+    return {
+        "source": MKV_PAGE + ", abstract: each key is scored by its Euclidean distance to the key "
+                  "centroid (WindowedManifoldKV: to its window's centroid); the farthest keys are kept. "
+                  "Centroids are exact rationals, scores are the square roots of the stored squared "
+                  "scores; keep_idx are the k largest, ascending.",
+        "G": G, "S": S, "keep": k, "K": K, **out,
+    }
+
+
+# ------------------------------------------------------------------- OjaKV
+
+def lowrank(seed=2):
+    rnd = random.Random(seed)
+    L, B, Hkv, Hq, Wq, S, R, k = 1, 1, 2, 4, 3, 24, 32, 3
+    g = Hq // Hkv
+    G = L * B * Hkv
+    Uk = [signed_selection(rnd, R) for _ in range(Hkv)]
+    Uv = [signed_selection(rnd, R) for _ in range(Hkv)]
+    K = ints(rnd, -6, 6, G, S, D)
+    V = ints(rnd, -6, 6, G, S, D)
+    Q = ints(rnd, -4, 4, L, B, Hq, Wq, D)
+
+    def project(X, sel):
+        cols, sign = sel
+        return [[sign[j] * X[t][cols[j]] for j in range(R)] for t in range(S)]
+
+    Kt, Vt, esum, anchors, khat, vhat = [], [], [], [], [], []
+    for gi in range(G):
+        h = gi % Hkv
+        Kt.append(project(K[gi], Uk[h]))
+        Vt.append(project(V[gi], Uv[h]))
+        inside = set(Uk[h][0])
+        # r_t = k_t - U U^T k_t: the key with the basis' channels removed
+        res = [[0 if c in inside else K[gi][t][c] for c in range(D)] for t in range(S)]
+        e = []
+        for t in range(S):
+            tot = 0
+            for hq in range(h * g, (h + 1) * g):
+                for q in range(Wq):
+                    tot += abs(sum(Q[0][0][hq][q][c] * res[t][c] for c in range(D)))
+            e.append(tot)
+        esum.append(e)
+        idx = keep_top(e, k)
+        anchors.append(idx)
+        # K^ = K~ U^T (the key restricted to the basis' channels) except at anchors (the full key)
+        kin, vin = set(Uk[h][0]), set(Uv[h][0])
+        khat.append([K[gi][t] if t in idx else [K[gi][t][c] if c in kin else 0 for c in range(D)]
+                     for t in range(S)])
+        vhat.append([V[gi][t] if t in idx else [V[gi][t][c] if c in vin else 0 for c in range(D)]
+                     for t in range(S)])
+    return {
+        "source": OJA_PAGE + ", background on low-rank attention (K~ = K U_k, K^ = K~ U_k^T), method "
+                  "details (r_t = k_t - U_k U_k^T k_t; e_t = (1/|W_t|) sum_{h,q} |q_{h,q} . r_t| / sqrt(d_h); "
+                  "the top-k tokens by e_t stay full rank).  err_sum[t] = |W_t| sqrt(d_h) e_t with "
+                  "|W_t| = g * W_q; anchors are the k largest, ascending; K_hat/V_hat include the anchors.",
+        "L": L, "B": B, "Hkv": Hkv, "Hq": Hq, "Wq": Wq, "S": S, "R": R, "anchors_k": k,
+        "Uk_cols": [s[0] for s in Uk], "Uk_signs": [s[1] for s in Uk],
+        "Uv_cols": [s[0] for s in Uv], "Uv_signs": [s[1] for s in Uv],
+        "K": K, "V": V, "Q": Q, "K_tilde": Kt, "V_tilde": Vt, "err_sum": esum,
+        "anchor_idx": anchors, "K_hat": khat, "V_hat": vhat,
+    }
+
+
+def oja(seed=3):
+    rnd = random.Random(seed)
+    L, B, Hkv, N, pool, R = 1, 2, 1, 12, 4, 32
+    eta = Fr(1, 64)
+    cols, sign = signed_selection(rnd, R)
+    U = [[Fr(sign[j]) if c == cols[j] else Fr(0) for j in range(R)] for c in range(D)]
+    X = ints(rnd, -5, 5, B, N, D)
+    # average pooling with kernel = stride = pool, rows of all batch entries together
+    Xp = []
+    for b in range(B):
+        for i in range(0, N, pool):
+            rows = X[b][i:i + pool]
+            Xp.append([Fr(sum(r[c] for r in rows), len(rows)) for c in range(D)])
+    n = len(Xp)
+    # C = Xp^T Xp / n;  U' = U + eta (C U - U (U^T C U))
+    XpU = [[sum(x[c] * U[c][j] for c in range(D)) for j in range(R)] for x in Xp]
+    CU = [[sum(Xp[i][c] * XpU[i][j] for i in range(n)) / n for j in range(R)] for c in range(D)]
+    M = [[sum(U[c][a] * CU[c][j] for c in range(D)) for j in range(R)] for a in range(R)]
+    U1 = [[U[c][j] + eta * (CU[c][j] - sum(U[c][a] * M[a][j] for a in range(R))) for j in range(R)]
+          for c in range(D)]
+    # thin QR with a positive diagonal, modified Gram-Schmidt in 60-digit decimals
+    A = [[dec(U1[c][j]) for c in range(D)] for j in range(R)]  # columns
+    Qc = []
+    for j in range(R):
+        v = A[j][:]
+        for q in Qc:
+            p = sum(q[c] * v[c] for c in range(D))
+            v = [v[c] - p * q[c] for c in range(D)]
+        nrm = sum(x * x for x in v).sqrt()
+        Qc.append([x / nrm for x in v])
+    Qm = [[ds(Qc[j][c]) for j in range(R)] for c in range(D)]
+    return {
+        "source": OJA_PAGE + ", how it works / method details (Oja's rule U <- U + eta (x x^T U - U U^T "
+                  "x x^T U); prefill: average pooling X_p = AvgPool(X, b), then the update with the "
+                  "empirical covariance C of the pooled rows, then re-orthonormalisation by QR) and "
+                  "appendix A.1.  C = X_p^T X_p / n (uncentred, n pooled rows over the batch); U_step is "
+                  "the update before QR (exact), U_new its Q factor with a positive diagonal.",
+        "L": L, "B": B, "Hkv": Hkv, "N": N, "pool": pool, "R": R, "eta": fs(eta),
+        "U_cols": cols, "U_signs": sign, "X": X,
+        "X_pooled": [[fs(x) for x in row] for row in Xp],
+        "U_step": [[fs(x) for x in row] for row in U1], "U_new": Qm,
+    }
+
+
+# ----------------------------------------------------------------- RefineKV
+
+def refine(seed=4):
+    rnd = random.Random(seed)
+    S, c, nq = 52, 10, 2
+    K = ints(rnd, -3, 3, S, D)
+    V = ints(rnd, -3, 3, S, D)
+    Qs = ints(rnd, -3, 3, nq, D)
+    nC = -(-S // c)
+    mus_k, mus_v, radius, vnorm, sizes = [], [], [], [], []
+    for j in range(nC):
+        t0, t1 = j * c, min((j + 1) * c, S)
+        mk = [Fr(sum(K[t][d] for t in range(t0, t1)), t1 - t0) for d in range(D)]
+        mv = [Fr(sum(V[t][d] for t in range(t0, t1)), t1 - t0) for d in range(D)]
+        rk = max(sum((K[t][d] - mk[d]) ** 2 for d in range(D)) for t in range(t0, t1))
+        nv = max(sum(V[t][d] ** 2 for d in range(D)) for t in range(t0, t1))
+        mus_k.append(mk)
+        mus_v.append(mv)
+        radius.append(dsqrt(rk))
+        vnorm.append(dsqrt(Fr(nv)))
+        sizes.append(t1 - t0)
+    vmax = max(vnorm)
+    rs = Decimal(1) / Decimal(D).sqrt()
+
+    def cosh(x):
+        return (x.exp() + (-x).exp()) / 2
+
+    def tanh(x):
+        e2 = (2 * x).exp()
+        return (e2 - 1) / (e2 + 1)
+
+    RC = []
+    for q in Qs:
+        qn = Decimal(sum(x * x for x in q)).sqrt()
+        z = [dec(sum(q[d] * mus_k[j][d] for d in range(D))) * rs for j in range(nC)]
+        w = [sizes[j] * z[j].exp() for j in range(nC)]
+        p = [x / sum(w) for x in w]
+        dl = [qn * radius[j] * rs for j in range(nC)]
+        Dn = sum(p[j] * cosh(dl[j]) for j in range(nC))
+        RC.append([ds(2 * p[j] * vmax * ((cosh(dl[j]) - 1) / Dn + tanh(dl[j] / 2))) for j in range(nC)])
+    return {
+        "source": RFK_PAGE + ", 'Summarize' (contiguous clusters; cached mean keys, mean values and "
+                  "metadata) and 'Select' with the Figure 2 formula RC = 2 p_C Vmax [(cosh d_C - 1)/Dn + "
+                  "tanh(d_C / 2)], Dn = sum_C' p_C' cosh d_C'.  The page names p_C, d_C and Vmax without "
+                  "formulas; read as p_C = n_C e^{z_C} / sum n e^{z}, z_C = q . mu_C / sqrt(d), d_C = "
+                  "||q|| radius_C / sqrt(d) (radius_C = the largest ||k - mu_C|| in the cluster), Vmax = "
+                  "the largest ||v|| of the slice.  Clusters hold c keys, the last the remainder.",
+        "S": S, "c": c, "K": K, "V": V, "Q": Qs,
+        "mu_k": [[fs(x) for x in m] for m in mus_k], "mu_v": [[fs(x) for x in m] for m in mus_v],
+        "radius": [ds(x) for x in radius], "vnorm": [ds(x) for x in vnorm], "RC": RC,
+    }
+
+
+# ------------------------------------------------------ figures the pages print
+
+def pages_figures():
+    return {
+        "kv_cache_llama31_8b_32k_batch4": {
+            "source": OJA_PAGE + ", quick read ('what problem') and main contributions: Llama-3.1-8B "
+                      "with a 32K-token prompt at batch size 4 needs about 16 GB of KV cache.",
+            "printed_GB": 16, "layers": 32, "kv_heads": 8, "head_dim": 128, "tokens": 32768,
+            "batch": 4, "bytes_per_element": 2,
+        },
+        "rank_and_token_compression_compose": {
+            "source": OJA_PAGE + ", appendix A.9: OjaKV at 0.6x rank combined with SnapKV keeping 50% "
+                      "of the tokens brings KV memory down to 30%; U_k^T (K S) = (U_k^T K) S and the "
+                      "compression ratio is (d / r) (n / m).",
+            "rank_fraction": 0.6, "token_fraction": 0.5, "printed_memory_fraction": 0.30,
+        },
+        "low_rank_memory_saving": {
+            "source": OJA_PAGE + ", appendix A.4: the memory saving is 1 - (r_k + r_v) / (2 d_h).",
+            "r_k": 64, "r_v": 64, "d_h": 128, "saving": 0.5,
+        },
+        "refinekv_figure2_clusters": {
+            "source": RFK_PAGE + ", Figure 2 caption: a 512-token prefix in clusters of 10 keys gives "
+                      "51 complete clusters, and the remaining two keys still count in the normalisation.",
+            "tokens": 512, "cluster": 10, "complete_clusters": 51, "remaining_keys": 2,
+        },
+        "ojakv_defaults": {
+            "source": OJA_PAGE + ", appendix A.5 & A.8: default Oja learning rate 0.10, decode update "
+                      "period T = 32 steps, importance window W = 32 queries.",
+            "eta": 0.10, "T": 32, "W": 32,
+        },
+    }
+
+
+def main():
+    for name, fn in (("manifold_tiny", manifold), ("lowrank_tiny", lowrank), ("oja_tiny", oja),
+                     ("refine_tiny", refine), ("pages_figures", pages_figures)):
+        with open(os.path.join(HERE, name + ".json"), "w") as f:
+            json.dump(fn(), f, separators=(",", ":"))
+            f.write("\n")
+        print("wrote", name)
+
+
+if __name__ == "__main__":
+    main()

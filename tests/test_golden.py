@@ -1,0 +1,250 @@
+"""Worked examples in tests/golden/ against the oracle (CPU) and the HIP library
+(GPU, through the C ABI).  The stored values come from tests/golden/make_golden.py,
+which computes them from the pages' definitions with exact fractions and
+60-digit decimals, using neither the oracle nor the library; pages_figures.json
+holds figures the pages print, each with its passage.
+
+Sources, by page and section:
+  * "ManifoldKV: Training-Free KV Cache Compression via Euclidean Outlier
+    Detection", abstract (distance to the key centroid, windowed variant).
+  * "OjaKV: Context-Aware Online Low-Rank KV Cache Compression" (deep-notes
+    page): background on low-rank attention, method details (residual,
+    error score, anchors, Oja's rule with pooling and QR), appendices A.4, A.5
+    & A.8, A.9, and the quick read's memory figure.
+  * "RefineKV" (project page): "Summarize", "Select", Figure 2 and its caption.
+
+GPU tolerances are the parity rules: scores rel 1e-4 (+1e-6 rms), low-rank and
+Oja outputs rel 2e-3 of (|x| + rms), index sets exact outside the 1e-4 band."""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+
+import oracle
+from tests.helpers import index_sets_agree, int_bf16, lowrank_close, score_close
+
+GOLD = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+D = 128
+
+
+def load(name):
+    with open(os.path.join(GOLD, name + ".json")) as f:
+        return json.load(f)
+
+
+def fr(a):
+    """Nested lists of fraction strings -> float64 array (each the nearest double)."""
+    return np.vectorize(lambda s: float(Fraction(s)), otypes=[np.float64])(np.asarray(a, dtype=object))
+
+
+def dc(a):
+    return np.asarray(a, dtype=object).astype(np.float64)
+
+
+def basis(cols, signs):
+    """[H][D][R] fp32 bases, column j = signs[h][j] * e_{cols[h][j]}."""
+    H, R = len(cols), len(cols[0])
+    U = np.zeros((H, D, R), np.float32)
+    for h in range(H):
+        for j in range(R):
+            U[h, cols[h][j], j] = signs[h][j]
+    return U
+
+
+# ------------------------------------------------------------------ CPU: oracle
+
+def test_manifold_worked_example_oracle():
+    d = load("manifold_tiny")
+    K = int_bf16(np.array(d["K"]))
+    k = d["keep"]
+    for name in ("global", "windowed"):
+        e = d[name]
+        if name == "global":
+            s, mu = oracle.score_l2(K)
+            mu = mu[:, None, :]
+        else:
+            s, mu = oracle.score_l2_windowed(K, e["W"])
+        np.testing.assert_allclose(mu, fr(e["centroids"]), rtol=1e-15, atol=1e-15)
+        np.testing.assert_allclose(s, np.sqrt(fr(e["squared_scores"])), rtol=1e-14)
+        assert oracle.topk(s.astype(np.float32), k).tolist() == e["keep_idx"]
+
+
+def test_lowrank_worked_example_oracle():
+    d = load("lowrank_tiny")
+    L, B, Hkv, Hq, Wq, S, k = (d[x] for x in ("L", "B", "Hkv", "Hq", "Wq", "S", "anchors_k"))
+    K, V, Q = (int_bf16(np.array(d[x])) for x in ("K", "V", "Q"))
+    Uk = basis(d["Uk_cols"], d["Uk_signs"])[None]
+    Uv = basis(d["Uv_cols"], d["Uv_signs"])[None]
+    Kt, Vt, err = oracle.lowrank_compress(K, V, Q, Uk, Uv, L, B, Hkv, Hq)
+    assert np.array_equal(Kt, np.array(d["K_tilde"], np.float64))
+    assert np.array_equal(Vt, np.array(d["V_tilde"], np.float64))
+    want = np.array(d["err_sum"], np.float64) / ((Hq // Hkv) * Wq * math.sqrt(D))
+    np.testing.assert_allclose(err, want, rtol=1e-14)
+    idx = oracle.topk(err.astype(np.float32), k)
+    assert idx.tolist() == d["anchor_idx"]
+    Kh = oracle.reconstruct(Kt, Uk, idx, oracle.gather(K, idx), L, B, Hkv)
+    Vh = oracle.reconstruct(Vt, Uv, idx, oracle.gather(V, idx), L, B, Hkv)
+    assert np.array_equal(Kh, np.array(d["K_hat"], np.float64))
+    assert np.array_equal(Vh, np.array(d["V_hat"], np.float64))
+
+
+def test_oja_worked_example_oracle():
+    d = load("oja_tiny")
+    L, B, Hkv, N, pool = (d[x] for x in ("L", "B", "Hkv", "N", "pool"))
+    eta = float(Fraction(d["eta"]))
+    X = int_bf16(np.array(d["X"]))  # [B, N, D]: slices of the one (layer, kv head)
+    U0 = basis([d["U_cols"]], [d["U_signs"]])  # [1, D, R]
+    Xp = np.concatenate([oracle.avgpool(X[b], pool) for b in range(B)])
+    np.testing.assert_array_equal(Xp, fr(d["X_pooled"]))
+    step = oracle.oja_step(Xp, U0[0].astype(np.float64), eta)
+    np.testing.assert_allclose(step, fr(d["U_step"]), rtol=1e-14, atol=1e-16)
+    np.testing.assert_allclose(oracle.qr(step), dc(d["U_new"]), rtol=0, atol=1e-14)
+    Un = oracle.oja_update(U0[None], X, pool, eta, L, B, Hkv)
+    np.testing.assert_allclose(Un[0, 0], dc(d["U_new"]), rtol=0, atol=1e-14)
+
+
+def test_refine_worked_example_oracle():
+    d = load("refine_tiny")
+    S, c = d["S"], d["c"]
+    K, V, Q = (int_bf16(np.array(d[x]))[None] for x in ("K", "V", "Q"))
+    mk, mv, rad, vn = oracle.cluster_summaries(K, V, c)
+    np.testing.assert_allclose(mk[0], fr(d["mu_k"]), rtol=1e-15, atol=1e-15)
+    np.testing.assert_allclose(mv[0], fr(d["mu_v"]), rtol=1e-15, atol=1e-15)
+    np.testing.assert_allclose(rad[0], dc(d["radius"]), rtol=1e-14)
+    np.testing.assert_allclose(vn[0], dc(d["vnorm"]), rtol=1e-14)
+    rc = oracle.refine_risk(mk, rad, vn, S, c, Q)
+    np.testing.assert_allclose(rc[0], dc(d["RC"]), rtol=1e-12)
+
+
+def test_figures_the_pages_print():
+    f = load("pages_figures")
+    # about 16 GB of K and V at 32K tokens x batch 4 (16-bit elements; 16 GiB = 17.2 GB)
+    m = f["kv_cache_llama31_8b_32k_batch4"]
+    nbytes = 2 * m["layers"] * m["kv_heads"] * m["head_dim"] * m["tokens"] * m["batch"] * m["bytes_per_element"]
+    assert nbytes == 16 * 2 ** 30
+    assert abs(nbytes / 1e9 - m["printed_GB"]) / m["printed_GB"] < 0.1
+    # A.9: keeping half of the tokens, then projecting onto 0.6 of the dimensions, stores 30%;
+    # selection and projection commute, U^T (K S) = (U^T K) S, on the oracle's outputs
+    a = f["rank_and_token_compression_compose"]
+    Dm, Rm, n = 10, 6, 40
+    m_keep = int(a["token_fraction"] * n)
+    assert Rm / Dm == a["rank_fraction"]
+    rng = np.random.default_rng(9)
+    K = int_bf16(rng.integers(-8, 9, (1, n, Dm)))
+    U = np.linalg.qr(rng.normal(size=(Dm, Rm)))[0].astype(np.float32)[None, None]
+    idx = oracle.topk(rng.random((1, n)).astype(np.float32), m_keep)
+    kept = oracle.gather(K, idx)
+    Kt_kept, _, _ = oracle.lowrank_compress(kept, None, None, U, None, 1, 1, 1, 0)
+    Kt_all, _, _ = oracle.lowrank_compress(K, None, None, U, None, 1, 1, 1, 0)
+    np.testing.assert_array_equal(Kt_kept[0], Kt_all[0][idx[0]])
+    assert Kt_kept.size / K.size == pytest.approx(a["printed_memory_fraction"], abs=1e-12)
+    # A.4: saving 1 - (r_k + r_v) / (2 d_h) on the oracle's outputs
+    s = f["low_rank_memory_saving"]
+    K2 = int_bf16(rng.integers(-8, 9, (1, 8, s["d_h"])))
+    Ub = np.linalg.qr(rng.normal(size=(s["d_h"], s["r_k"])))[0].astype(np.float32)[None, None]
+    Kt2, Vt2, _ = oracle.lowrank_compress(K2, K2, None, Ub, Ub, 1, 1, 1, 0)
+    assert 1 - (Kt2.size + Vt2.size) / (2 * K2.size) == s["saving"] == 1 - (s["r_k"] + s["r_v"]) / (2 * s["d_h"])
+    # Figure 2: 512 keys in clusters of 10 -> 51 complete clusters and a last one of 2 keys
+    r = f["refinekv_figure2_clusters"]
+    Kc = rng.integers(-4, 5, (1, r["tokens"], D))
+    mk, _, _, _ = oracle.cluster_summaries(int_bf16(Kc), int_bf16(Kc), r["cluster"])
+    assert mk.shape[1] == r["complete_clusters"] + 1
+    assert r["tokens"] - r["complete_clusters"] * r["cluster"] == r["remaining_keys"]
+    np.testing.assert_allclose(mk[0, -1], Kc[0, -r["remaining_keys"]:].mean(axis=0), rtol=0, atol=1e-15)
+    # A.5 & A.8: the decode update period and the query window are the workload's 32
+    dflt = f["ojakv_defaults"]
+    assert (dflt["T"], dflt["W"]) == (32, 32)
+
+
+# ------------------------------------------------------------- GPU: the library
+
+@pytest.mark.gpu
+def test_manifold_worked_example_gpu(gpu_lib):
+    import torch
+    d = load("manifold_tiny")
+    K = torch.from_numpy(int_bf16(np.array(d["K"])).view(np.int16)).view(torch.bfloat16).cuda()
+    V = K.flip(1).contiguous()
+    k = d["keep"]
+    for name in ("global", "windowed"):
+        e = d[name]
+        want = np.sqrt(fr(e["squared_scores"]))
+        if name == "global":
+            s = gpu_lib.kvc_score_l2(K)
+        else:
+            s = gpu_lib.kvc_score_l2_windowed(K, e["W"])
+        idx, Ko, Vo = gpu_lib.kvc_topk_compact(s, k, K, V)
+        torch.cuda.synchronize()
+        ok, rel, nbad = score_close(s.cpu().numpy(), want)
+        assert ok, (name, rel, nbad)
+        ok, nb = index_sets_agree(idx.cpu().numpy(), np.array(e["keep_idx"]), want.astype(np.float32), k)
+        assert ok and nb == 0, name
+        ii = idx.long()
+        assert torch.equal(Ko, K.gather(1, ii[..., None].expand(-1, -1, D)))
+        assert torch.equal(Vo, V.gather(1, ii[..., None].expand(-1, -1, D)))
+
+
+@pytest.mark.gpu
+def test_lowrank_worked_example_gpu(gpu_lib):
+    import torch
+    d = load("lowrank_tiny")
+    L, B, Hkv, Hq, Wq, S, k = (d[x] for x in ("L", "B", "Hkv", "Hq", "Wq", "S", "anchors_k"))
+
+    def bf(a):
+        return torch.from_numpy(int_bf16(np.array(a)).view(np.int16)).view(torch.bfloat16).cuda()
+
+    K, V, Q = bf(d["K"]), bf(d["V"]), bf(d["Q"])
+    Uk = torch.from_numpy(basis(d["Uk_cols"], d["Uk_signs"])[None]).cuda()
+    Uv = torch.from_numpy(basis(d["Uv_cols"], d["Uv_signs"])[None]).cuda()
+    Kt, Vt, err = gpu_lib.kvc_lowrank_compress(K, V, Q, Uk, Uv, L, B, Hkv)
+    idx, Ka, Va = gpu_lib.kvc_topk_compact(err, k, K, V)
+    Kh = gpu_lib.kvc_reconstruct(Kt, Uk, idx, Ka, L, B, Hkv)
+    Vh = gpu_lib.kvc_reconstruct(Vt, Uv, idx, Va, L, B, Hkv)
+    torch.cuda.synchronize()
+    for got, key in ((Kt, "K_tilde"), (Vt, "V_tilde"), (Kh, "K_hat"), (Vh, "V_hat")):
+        ok, rel = lowrank_close(got.cpu().numpy(), np.array(d[key], np.float64))
+        assert ok, (key, rel)
+    want = np.array(d["err_sum"], np.float64) / ((Hq // Hkv) * Wq * math.sqrt(D))
+    ok, rel, nbad = score_close(err.cpu().numpy(), want)
+    assert ok, (rel, nbad)
+    ok, _ = index_sets_agree(idx.cpu().numpy(), np.array(d["anchor_idx"]), want.astype(np.float32), k)
+    assert ok
+
+
+@pytest.mark.gpu
+def test_oja_worked_example_gpu(gpu_lib):
+    import torch
+    d = load("oja_tiny")
+    L, B, Hkv, pool = (d[x] for x in ("L", "B", "Hkv", "pool"))
+    X = torch.from_numpy(int_bf16(np.array(d["X"])).view(np.int16)).view(torch.bfloat16).cuda()
+    U = torch.from_numpy(basis([d["U_cols"]], [d["U_signs"]])[None]).cuda()
+    gpu_lib.kvc_oja_update(U, X, pool, float(Fraction(d["eta"])), L, B, Hkv)
+    torch.cuda.synchronize()
+    got = U[0, 0].double().cpu().numpy()
+    ok, rel = lowrank_close(got[None], dc(d["U_new"])[None])
+    assert ok, rel
+    assert np.abs(got.T @ got - np.eye(got.shape[1])).max() <= 1e-5
+
+
+@pytest.mark.gpu
+def test_refine_worked_example_gpu(gpu_lib):
+    import torch
+    d = load("refine_tiny")
+    S, c = d["S"], d["c"]
+
+    def bf(a):
+        return torch.from_numpy(int_bf16(np.array(a)).view(np.int16)).view(torch.bfloat16)[None].cuda()
+
+    K, V, Q = bf(d["K"]), bf(d["V"]), bf(d["Q"])
+    mk, mv, rad, vn = gpu_lib.kvc_cluster_summaries(K, V, c)
+    rc = gpu_lib.kvc_refine_risk(mk, rad, vn, S, c, Q)
+    torch.cuda.synchronize()
+    np.testing.assert_allclose(mk[0].cpu().numpy(), fr(d["mu_k"]), rtol=1e-6, atol=1e-6)
+    np.testing.assert_allclose(mv[0].cpu().numpy(), fr(d["mu_v"]), rtol=1e-6, atol=1e-6)
+    for got, key in ((rad, "radius"), (vn, "vnorm")):
+        ok, rel, nbad = score_close(got[0].cpu().numpy(), dc(d[key]))
+        assert ok, (key, rel, nbad)
+    ok, rel, nbad = score_close(rc[0].cpu().numpy(), dc(d["RC"]))
+    assert ok, (rel, nbad)
