@@ -113,7 +113,11 @@ size_t kvc_workspace_bytes(kvc_op op, const kvc_dims *d, int64_t k, int64_t W);
  *   mu_g       = (1/S) sum_t K[g][t][:]           (the key centroid)
  *   scores[g][t] = || K[g][t][:] - mu_g ||_2      (Euclidean distance)
  * K: bf16 [G][S][D].  scores: fp32 [G][S].  centroid: fp32 [G][D] or NULL.
- * Accumulation is fp32.  G >= 0, S >= 1 (G = 0 is a no-op). */
+ * Accumulation is fp32.  G >= 0, S >= 1 (G = 0 is a no-op).
+ * Large caches are scored by one cooperative launch whose workgroups exchange
+ * each window's centroid; every wait in it is bounded.  A wait that expires
+ * (it cannot while the grid stays resident, as the cooperative launch
+ * guarantees) leaves the affected scores NaN rather than wrong finite values. */
 kvc_status kvc_score_l2(const uint16_t *K, int64_t G, int64_t S, int32_t D, float *scores,
                         float *centroid, void *ws, size_t ws_bytes, hipStream_t stream);
 

@@ -213,3 +213,29 @@ def test_binding_workspace_per_stream(gpu_lib):
     torch.cuda.synchronize()
     assert w1.data_ptr() != w2.data_ptr()
     assert torch.equal(a, ref) and torch.equal(b, ref)
+
+
+@pytest.mark.parametrize("metric", ["l2", "cosine"])
+def test_expired_centroid_wait_gives_nan_not_wrong_scores(gpu_lib, monkeypatch, metric):
+    # the single-read kernel's centroid waits are bounded; a spin limit of 0 set from the
+    # host makes nearly every wait expire at its first poll.  Those tiles must come out NaN
+    # (whole 256-token tiles), every other score exactly as in a normal run, the kernel must
+    # end normally, and a normal call afterwards must be unaffected
+    K, _, _ = synth.manifold_global(4, 1, 8, 16384, planted=8, seed=5, device=DEV)
+    monkeypatch.setenv("KVC_SCORE_UNFUSED", "0")
+
+    def score():
+        return gpu_lib.kvc_score_centroid(K, W=None, metric=metric)
+
+    ref = score().clone()
+    monkeypatch.setenv("KVC_SCORE_SPIN_LIMIT", "0")
+    bad = score().clone()
+    monkeypatch.delenv("KVC_SCORE_SPIN_LIMIT")
+    again = score()
+    torch.cuda.synchronize()
+    nan = torch.isnan(bad)
+    assert nan.any()
+    assert torch.equal(bad[~nan], ref[~nan])
+    tiles = nan.view(-1, 256)
+    assert torch.equal(tiles.any(1), tiles.all(1))
+    assert not torch.isnan(ref).any() and torch.equal(again, ref)

@@ -213,6 +213,7 @@ struct FuseGeom {
     int64_t members;  // tiles per window
     int64_t teams;    // G * nwin
     int64_t tiles;    // teams * members
+    uint32_t spin_limit;  // polls of a centroid wait before it gives up (kSpinLimit)
 };
 
 __device__ __forceinline__ void widen8(const uint4 &v, float *x) {
@@ -397,8 +398,10 @@ __global__ __launch_bounds__(kFuseThreads, KVC_FUSE_MINBLOCKS) void l2_fused(con
         __syncthreads();  // red is reused by the caller
     };
     // The team's centroid into mu_s: each channel's tagged word is polled
-    // until ready, with back-off (bounded; past the limit a status bit is set).
-    auto fetch_mu = [&](const TileGeo &t) {
+    // until ready, with back-off.  The wait is bounded: past the limit a status
+    // bit is set and false is returned (the caller then writes NaN scores for
+    // the tile rather than scores against an unpublished centroid).
+    auto fetch_mu = [&](const TileGeo &t) -> bool {
         uint32_t spins = 0;
         int nap = 1;
         for (;;) {
@@ -409,10 +412,10 @@ __global__ __launch_bounds__(kFuseThreads, KVC_FUSE_MINBLOCKS) void l2_fused(con
                 ready = (w >> 32) == kReady;
                 mu_s[tid] = __uint_as_float(static_cast<uint32_t>(w));
             }
-            if (__syncthreads_and(ready)) break;
-            if (++spins > kSpinLimit) {
+            if (__syncthreads_and(ready)) return true;
+            if (++spins > geo.spin_limit) {
                 if (tid == 0) atomicOr(status, 1u);
-                break;
+                return false;
             }
             // back-off: a team polls the same few lines; hammering them costs
             // the data loads bandwidth on those memory channels
@@ -425,7 +428,11 @@ __global__ __launch_bounds__(kFuseThreads, KVC_FUSE_MINBLOCKS) void l2_fused(con
 
     // Scores tile `t` (held in v) once its team's centroid is published.
     auto score_tile = [&](const TileGeo &t, const uint4 *v) {
-        fetch_mu(t);
+        // a centroid that never arrived (the bounded wait expired) makes every
+        // score of the tile a quiet NaN, so the failure shows in the output
+        // instead of as plausible wrong distances (uniform across the workgroup)
+        const bool ok = fetch_mu(t);
+        const float nan = __int_as_float(0x7fc00000);
         float m[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) m[j] = mu_s[lane16 * 8 + j];
@@ -459,7 +466,7 @@ __global__ __launch_bounds__(kFuseThreads, KVC_FUSE_MINBLOCKS) void l2_fused(con
                 if (lane16 == r) mine = (kk > 0.f && mm > 0.f) ? 0.5f * e : 1.f;
             }
             const int64_t row = t.t0 + 16 * lane16;
-            if (lane16 < kFuseRows && row < t.w1) scores[t.g * geo.S + row] = mine;
+            if (lane16 < kFuseRows && row < t.w1) scores[t.g * geo.S + row] = ok ? mine : nan;
         } else {
             float d2[kFuseRows];
 #pragma unroll
@@ -478,7 +485,7 @@ __global__ __launch_bounds__(kFuseThreads, KVC_FUSE_MINBLOCKS) void l2_fused(con
             const int r = kFuseRows == 16 ? lane16 : (lane16 >> 1);
             const int64_t row = t.t0 + 16 * r;
             if ((kFuseRows == 16 || (lane16 & 1) == 0) && row < t.w1)
-                scores[t.g * geo.S + row] = sqrtf(d2[0]);
+                scores[t.g * geo.S + row] = ok ? sqrtf(d2[0]) : nan;
         }
         __syncthreads();  // mu_s is rewritten by the next fetch
     };
@@ -519,6 +526,7 @@ FuseGeom make_fuse_geom(int64_t G, int64_t S, int64_t W, int metric = kMetricL2)
     f.members = (f.W + kFuseTile - 1) / kFuseTile;
     f.teams = G * f.nwin;
     f.tiles = f.teams * f.members;
+    f.spin_limit = kSpinLimit;
     return f;
 }
 
@@ -621,6 +629,10 @@ kvc_status score_windowed_impl(const uint16_t *K, int64_t G, int64_t S, int32_t 
         hipLaunchKernelGGL(zero_words, dim3(static_cast<unsigned>(zb < 1024 ? zb : 1024)), dim3(kFuseThreads), 0,
                            stream, clear_from, n_clear);
         FuseGeom fa = f;
+        // KVC_SCORE_SPIN_LIMIT in the environment shortens the bounded waits (read at
+        // every call), so that tests can force the expired-wait path from the host
+        const char *lim = getenv("KVC_SCORE_SPIN_LIMIT");
+        fa.spin_limit = lim ? static_cast<uint32_t>(strtoul(lim, nullptr, 10)) : kSpinLimit;
         float *mu_user = centroids;
         int64_t grid = capacity / f.members * f.members;
         if (grid > f.tiles) grid = f.tiles;
