@@ -444,8 +444,9 @@ def base_line(args, metric, value, ms_step, steps, config):
 def main():
     args = parse()
     if args.gpus != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (every slice is "
-              "independent; sharding is described in DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU: the library has no multi-GPU path (every slice is "
+              "independent, so slices would shard across GPUs without communication). Run with --gpus 1.",
+              file=sys.stderr)
         sys.exit(2)
     import torch
 

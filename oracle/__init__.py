@@ -18,7 +18,7 @@ Sources, by page title and section:
 
 Every function is pinned by the ``-m "not gpu"`` tests, except
 ``full_loop_slice``'s decode-time re-projection and re-selection over the whole
-cache, which is this build's reading of the full-loop workload and is
+cache, which is the reading adopted here for the full-loop workload and is
 **parity unpinned** relative to the pages.
 """
 from __future__ import annotations
@@ -307,7 +307,7 @@ def full_loop_slice(K, V, Qprompt, Qdec, Uk, Uv, S0, steps, T, pool, eta, anchor
 
     The re-projection, re-scoring and re-selection over the whole cache at each
     decode update (and the use of the T decode queries as the query window) is
-    this build's reading of the full-loop workload: the pages' decode phase
+    the reading adopted here for the full-loop workload: the pages' decode phase
     re-projects nothing.  Parity unpinned relative to the pages.
 
     K, V: uint16 [S0+steps, D] (the full-rank rows the caller keeps);

@@ -79,7 +79,7 @@ def test_compress_without_query_or_values(gpu_lib):
     assert ok, rel
 
 
-def test_config3_sampled(gpu_lib):
+def test_prefill_1024x32768_r64_sampled(gpu_lib):
     # 32 layers x batch 4 x 8 kv heads x 32 query heads, S=32768, r=64, 32-query window,
     # 5% anchors, launched at full size; 40 slices (every layer, every batch row and kv
     # head at least once) checked against the oracle

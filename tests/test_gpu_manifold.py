@@ -134,7 +134,7 @@ def _evict_and_check(gpu_lib, K, V, keep, W=None, slices=None, threads=8):
     return idx, nb_total
 
 
-def test_config0_global_full(gpu_lib):
+def test_global_8x4096_keep3277_full(gpu_lib):
     # 1 layer x 8 kv heads, S=4096, drop 20% -> keep 3277; every slice checked
     K, V, plant = synth.manifold_global(1, 1, 8, 4096, planted=16, device=DEV)
     idx, _ = _evict_and_check(gpu_lib, K, V, oracle.keep_count(4096, 20))
@@ -142,7 +142,7 @@ def test_config0_global_full(gpu_lib):
         assert set(plant[g].tolist()) <= set(idx[g].cpu().tolist())
 
 
-def test_config1_global_full(gpu_lib):
+def test_global_256x16384_keep8192(gpu_lib):
     # 32 layers x 8 kv heads, S=16384, keep 8192, in the launch configuration the
     # benchmark times; every one of the 256 slices checked against the oracle
     K, V, plant = synth.manifold_global(32, 1, 8, 16384, planted=64, device=DEV)
@@ -151,7 +151,7 @@ def test_config1_global_full(gpu_lib):
         assert set(plant[g].tolist()) <= set(idx[g].cpu().tolist())
 
 
-def test_config2_windowed_full(gpu_lib):
+def test_windowed_256x65536_w4096_keep49152(gpu_lib):
     # 32 layers x 8 kv heads, S=65536, W=4096, keep 49152; every slice checked
     K, V = synth.manifold_drifting(32, 1, 8, 65536, device=DEV)
     _evict_and_check(gpu_lib, K, V, 49152, W=4096)

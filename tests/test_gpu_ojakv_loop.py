@@ -5,7 +5,7 @@ orthonormal to 1e-5), error scores (rel 1e-4), anchor sets (threshold band)
 and reconstructions (rel 2e-3, anchor rows exact) agree.
 
 The loop's decode-time re-projection and re-selection over the whole cache is
-this build's reading of the full-loop workload (parity unpinned relative to
+the reading adopted for the full-loop workload (parity unpinned relative to
 the pages); both sides implement that same reading."""
 import threading
 
@@ -106,7 +106,7 @@ def test_loop_small_all_slices(gpu_lib):
             _compare(snaps[j][g], ora, ora["S"])
 
 
-def test_loop_config4_sampled(gpu_lib):
+def test_loop_256x131072_sampled(gpu_lib):
     # 32 layers x batch 1 x 8 kv heads (32 query heads), 131072-token prompt pooled by 32 for
     # the prefill update, eta 1e-3, 256 decode steps with an update every 32, all at full
     # size on the GPU.  Two slices are checked against independent oracle runs (one thread
