@@ -38,13 +38,14 @@ def source_digest(path):
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def measured_traffic(entry_point, config):
-    """Scaled FETCH_SIZE + WRITE_SIZE bytes per launch of an entry point, as
-    recorded from rocprofv3 counter runs (profiles/hbm_traffic.json); None when
-    absent or when the kernel source changed since the counters were taken."""
+def measured_traffic(entry_point, workload):
+    """Scaled FETCH_SIZE + WRITE_SIZE bytes per launch of an entry point on a
+    workload ("config<N>" or "refine"), as recorded from rocprofv3 counter runs
+    (profiles/hbm_traffic.json); None when absent or when the kernel source
+    changed since the counters were taken."""
     try:
         with open(TRAFFIC_FILE) as f:
-            rec = json.load(f)["entries"]["%s/config%d" % (entry_point, config)]
+            rec = json.load(f)["entries"]["%s/%s" % (entry_point, workload)]
     except (OSError, KeyError, ValueError):
         return None
     if any(source_digest(p) != h for p, h in rec["sources"].items()):
@@ -429,7 +430,8 @@ def run_loop_config(args, dev):
     achieved = fused_bytes / fused_ms / 1e6
     line["roofline"] = {"bound": "hbm", "entry_point": fused_name, "kernel": "project_kernel (fused reconstruction)",
                         "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                        "traffic": None, "algorithmic_bytes": fused_bytes / max(1, len(fused_calls)),
+                        "traffic": measured_traffic(fused_name, "config4"),
+                        "algorithmic_bytes": fused_bytes / max(1, len(fused_calls)),
                         "ms_per_call": fused_ms / max(1, len(fused_calls)), "calls": len(fused_calls)}
     print(json.dumps(line), flush=True)
 
@@ -502,7 +504,7 @@ def main():
                      ms_step, args.steps, config)
     line["roofline"] = {"bound": "hbm", "entry_point": dom, "kernel": per_op[dom]["kernel"],
                         "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                        "traffic": measured_traffic(dom, args.config),
+                        "traffic": measured_traffic(dom, "refine" if args.refine else "config%d" % args.config),
                         "algorithmic_bytes": per_op[dom]["bytes"]}
     if "TFLOPs" in per_op[dom]:
         line["roofline"]["mfma_TFLOPs"] = per_op[dom]["TFLOPs"]
