@@ -36,10 +36,12 @@
  * forms, invariants, exact-rational brute force or a library routine, with two
  * exceptions.  The decode-time re-projection reading used by the full-loop
  * driver lives in the Python wrapper and is marked "parity unpinned" there.
- * ora_refine_risk is "parity unpinned" relative to the page beyond its closed
- * forms: the page names the attention-mass and logit-deviation terms without
- * formulas, and under the readings taken here RC is not an upper bound of the
- * single-cluster replacement error in general.
+ * ora_refine_risk is "parity unpinned" relative to the page in its readings:
+ * the page names the attention-mass and logit-deviation terms without formulas,
+ * and under the readings taken here RC is not an upper bound of the
+ * single-cluster replacement error in general.  Its arithmetic is pinned: closed
+ * forms, and a worked example of the printed Figure 2 formula evaluated in
+ * 60-digit decimals under the same readings.
  */
 #include <math.h>
 #include <stdint.h>
