@@ -80,6 +80,9 @@ def manifold(seed=1):
         for t in rnd.sample(range(S), 2):
             K[g][t] = [4 * x for x in K[g][t]]
 
+    def mu_of(mus_g, t, win):
+        return mus_g[t // win]
+
     def part(lo, hi, Kg):
         mu = [Fr(sum(Kg[t][c] for t in range(lo, hi)), hi - lo) for c in range(D)]
         s2 = [sum((Kg[t][c] - mu[c]) ** 2 for c in range(D)) for t in range(lo, hi)]
@@ -100,10 +103,27 @@ def manifold(seed=1):
             mus.append(mu_g)
             s2s.append([fs(x) for x in s2_g])
             keeps.append(keep_top(s2_g, k))
-        out[name] = {"W": win, "centroids": mus, "squared_scores": s2s, "keep_idx": keeps}
+        # cosine dissimilarity to the same centroid (the baseline the abstract compares
+        # against), 1 - k.mu / (||k|| ||mu||) in 60-digit decimals (1 where k or mu is zero)
+        cos = []
+        for g in range(G):
+            row = []
+            for t in range(S):
+                mu = [Fr(x) for x in mu_of(mus[g], t, win)]
+                kk = sum(Fr(x) ** 2 for x in K[g][t])
+                mm = sum(x * x for x in mu)
+                if kk == 0 or mm == 0:
+                    row.append(ds(Decimal(1)))
+                    continue
+                dot = sum(K[g][t][c] * mu[c] for c in range(D))
+                row.append(ds(1 - dec(dot) / (dec(kk).sqrt() * dec(mm).sqrt())))
+            cos.append(row)
+        out[name] = {"W": win, "centroids": mus, "squared_scores": s2s, "keep_idx": keeps,
+                     "cosine_scores": cos}
     return {
         "source": MKV_PAGE + ", abstract: each key is scored by its Euclidean distance to the key "
-                  "centroid (WindowedManifoldKV: to its window's centroid); the farthest keys are kept. "
+                  "centroid (WindowedManifoldKV: to its window's centroid); the farthest keys are kept; "
+                  "cosine_scores are the cosine-to-centroid baseline the abstract contrasts it with. "
                   "Centroids are exact rationals, scores are the square roots of the stored squared "
                   "scores; keep_idx are the k largest, ascending.",
         "G": G, "S": S, "keep": k, "K": K, **out,

@@ -6,7 +6,8 @@ holds figures the pages print, each with its passage.
 
 Sources, by page and section:
   * "ManifoldKV: Training-Free KV Cache Compression via Euclidean Outlier
-    Detection", abstract (distance to the key centroid, windowed variant).
+    Detection", abstract (distance to the key centroid, windowed variant, and
+    the cosine-to-centroid baseline it is compared with).
   * "OjaKV: Context-Aware Online Low-Rank KV Cache Compression" (deep-notes
     page): background on low-rank attention, method details (residual,
     error score, anchors, Oja's rule with pooling and QR), appendices A.4, A.5
@@ -70,6 +71,8 @@ def test_manifold_worked_example_oracle():
         np.testing.assert_allclose(mu, fr(e["centroids"]), rtol=1e-15, atol=1e-15)
         np.testing.assert_allclose(s, np.sqrt(fr(e["squared_scores"])), rtol=1e-14)
         assert oracle.topk(s.astype(np.float32), k).tolist() == e["keep_idx"]
+        c, _ = oracle.score_cosine_windowed(K, e["W"])
+        np.testing.assert_allclose(c, dc(e["cosine_scores"]), rtol=1e-13)
 
 
 def test_lowrank_worked_example_oracle():
@@ -184,6 +187,10 @@ def test_manifold_worked_example_gpu(gpu_lib):
         ii = idx.long()
         assert torch.equal(Ko, K.gather(1, ii[..., None].expand(-1, -1, D)))
         assert torch.equal(Vo, V.gather(1, ii[..., None].expand(-1, -1, D)))
+        c = gpu_lib.kvc_score_centroid(K, W=e["W"], metric="cosine")
+        torch.cuda.synchronize()
+        ok, rel, nbad = score_close(c.cpu().numpy(), dc(e["cosine_scores"]))
+        assert ok, (name, "cosine", rel, nbad)
 
 
 @pytest.mark.gpu
@@ -211,6 +218,13 @@ def test_lowrank_worked_example_gpu(gpu_lib):
     assert ok, (rel, nbad)
     ok, _ = index_sets_agree(idx.cpu().numpy(), np.array(d["anchor_idx"]), want.astype(np.float32), k)
     assert ok
+    # bf16 storage: every stored value here is a small integer, exact in bf16
+    Kt16, Vt16, _ = gpu_lib.kvc_lowrank_compress_bf16(K, V, Q, Uk, Uv, L, B, Hkv)
+    Kh16 = gpu_lib.kvc_reconstruct_bf16(Kt16, Uk, idx, Ka, L, B, Hkv)
+    Vh16 = gpu_lib.kvc_reconstruct_bf16(Vt16, Uv, idx, Va, L, B, Hkv)
+    torch.cuda.synchronize()
+    for got, key in ((Kt16, "K_tilde"), (Vt16, "V_tilde"), (Kh16, "K_hat"), (Vh16, "V_hat")):
+        np.testing.assert_array_equal(got.float().cpu().numpy(), np.array(d[key], np.float32), err_msg=key)
 
 
 @pytest.mark.gpu
