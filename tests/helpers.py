@@ -96,3 +96,16 @@ def bf16_close(gpu_bits, ora, ulps=1, abs_frac=2.0 ** -14):
     rms = np.sqrt(np.mean(ora ** 2, axis=axes, keepdims=True))
     ok = (dist <= ulps) | (np.abs(g - ora) <= abs_frac * rms)
     return bool(ok.all()), int(dist[~ok].max()) if (~ok).any() else int(dist.max())
+
+
+def built_library():
+    """True once libkvc.so exists: it is compiled here (hipcc, gfx950) when a fresh
+    checkout has none; False only where hipcc is not installed."""
+    import os
+    import shutil
+    from token_scoring_eviction_amd import build, kvc
+    if not os.path.exists(kvc.LIB_PATH):
+        if shutil.which(build.HIPCC) is None and not os.path.exists(build.HIPCC):
+            return False
+        build.build(verbose=False)
+    return os.path.exists(kvc.LIB_PATH)

@@ -10,9 +10,10 @@ import os
 import numpy as np
 import pytest
 
+from tests.helpers import built_library
 from token_scoring_eviction_amd import kvc
 
-pytestmark = pytest.mark.skipif(not os.path.exists(kvc.LIB_PATH), reason="libkvc.so not built here")
+pytestmark = pytest.mark.skipif(not built_library(), reason="hipcc is not installed here")
 
 OK, INV, UNS, WS = kvc.OK, kvc.ERR_INVALID_ARGUMENT, kvc.ERR_UNSUPPORTED, kvc.ERR_WORKSPACE_TOO_SMALL
 NULL = None
