@@ -16,10 +16,15 @@ Sources, by page title and section:
     query-weighted error score, top-k full-rank anchors, pooled prefill Oja
     update with QR, decode-time buffered updates (method details; appendix A.1).
 
-Every function is pinned by the ``-m "not gpu"`` tests, except
-``full_loop_slice``'s decode-time re-projection and re-selection over the whole
-cache, which is the reading adopted here for the full-loop workload and is
-**parity unpinned** relative to the pages.
+Every function is pinned by the ``-m "not gpu"`` tests.  ``full_loop_slice`` is
+pinned by a worked example of the whole loop (tests/golden/oja_loop_tiny.json:
+pooled prefill update, QR, scoring with the updated bases, anchors, then two
+decode updates with re-projection, re-scoring and re-selection, computed with
+exact rationals and 60-digit decimals) that also tells apart planted mistakes
+in the order of the steps, the pooling, the buffer and the query window.  What
+stays a reading is its decode-time re-projection and re-selection over the
+whole cache (the pages' decode phase re-projects nothing): that reading is
+**parity unpinned relative to the pages**, though its arithmetic is pinned.
 """
 from __future__ import annotations
 
@@ -308,7 +313,8 @@ def full_loop_slice(K, V, Qprompt, Qdec, Uk, Uv, S0, steps, T, pool, eta, anchor
     The re-projection, re-scoring and re-selection over the whole cache at each
     decode update (and the use of the T decode queries as the query window) is
     the reading adopted here for the full-loop workload: the pages' decode phase
-    re-projects nothing.  Parity unpinned relative to the pages.
+    re-projects nothing.  Parity unpinned relative to the pages; the arithmetic
+    and the order of the steps are pinned by the loop's worked example.
 
     K, V: uint16 [S0+steps, D] (the full-rank rows the caller keeps);
     Qprompt: uint16 [g, Wq, D]; Qdec: uint16 [steps, g, D];

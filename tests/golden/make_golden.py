@@ -2,7 +2,7 @@
 pages, with exact rational arithmetic (fractions) and 60-digit decimals.  It
 uses neither the oracle nor the HIP library, so the stored values pin both.
 
-    python tests/golden/make_golden.py
+    python tests/golden/make_golden.py [fixture names...]
 
 Every input is integer-valued (exact in bf16) and every basis is a signed
 selection of coordinate columns (exactly orthonormal in fp32), so each
@@ -17,6 +17,11 @@ Fixtures (each names the passage it follows in its "source" field):
                       the full-rank anchors and the reconstruction.
   oja_tiny.json       average pooling, one Oja step on the pooled empirical
                       covariance, then QR with a positive diagonal.
+  oja_loop_tiny.json  the hybrid loop on one slice: the pooled prefill update,
+                      QR, scoring with the updated bases and anchors, then two
+                      decode updates on the buffered tokens, each followed by
+                      re-projection, re-scoring with the decode queries and
+                      re-selection (bases stored in fp32 between steps).
   refine_tiny.json    contiguous-cluster summaries and the Figure 2 risk score.
   pages_figures.json  figures the pages print, with the passage of each.
 """
@@ -25,6 +30,8 @@ from __future__ import annotations
 import json
 import os
 import random
+import struct
+import sys
 from decimal import Decimal, getcontext
 from fractions import Fraction as Fr
 
@@ -68,6 +75,66 @@ def ints(rnd, lo, hi, *shape):
 def signed_selection(rnd, R):
     """Columns cols[j] of the identity with signs sign[j]: an exactly orthonormal D x R basis."""
     return rnd.sample(range(D), R), [rnd.choice((-1, 1)) for _ in range(R)]
+
+
+def selection_matrix(sel):
+    cols, sign = sel
+    return [[Fr(sign[j]) if c == cols[j] else Fr(0) for j in range(len(cols))] for c in range(D)]
+
+
+def oja_step(U, X, eta):
+    """Oja's rule with the empirical (uncentred) covariance of the rows X, exactly:
+    C = X^T X / n;  U' = U + eta (C U - U (U^T C U))."""
+    n, R = len(X), len(U[0])
+    XU = [[sum(x[c] * U[c][j] for c in range(D) if x[c]) for j in range(R)] for x in X]
+    CU = [[sum(X[i][c] * XU[i][j] for i in range(n)) / n for j in range(R)] for c in range(D)]
+    M = [[sum(U[c][a] * CU[c][j] for c in range(D) if U[c][a]) for j in range(R)] for a in range(R)]
+    return [[U[c][j] + eta * (CU[c][j] - sum(U[c][a] * M[a][j] for a in range(R) if U[c][a]))
+             for j in range(R)] for c in range(D)]
+
+
+def mgs_columns(A):
+    """Thin QR with a positive diagonal of A (D x R exact rationals), modified
+    Gram-Schmidt in 60-digit decimals; returns the R columns of Q."""
+    R = len(A[0])
+    cols = [[dec(A[c][j]) for c in range(D)] for j in range(R)]
+    Qc = []
+    for j in range(R):
+        v = cols[j][:]
+        for q in Qc:
+            p = sum(q[c] * v[c] for c in range(D))
+            v = [v[c] - p * q[c] for c in range(D)]
+        nrm = sum(x * x for x in v).sqrt()
+        Qc.append([x / nrm for x in v])
+    return Qc
+
+
+def f32_nearest(x: Decimal):
+    """The fp32 value nearest to x (ties to even; normal range), as an exact
+    rational, and how far x sits from the rounding midpoint in units of the fp32
+    spacing (0.5: on a representable value, 0: on a midpoint)."""
+    a = abs(Fr(x))
+    if a == 0:
+        return Fr(0), Fr(1, 2)
+    e = a.numerator.bit_length() - a.denominator.bit_length()
+    while Fr(2) ** e > a:
+        e -= 1
+    while Fr(2) ** (e + 1) <= a:
+        e += 1
+    assert e >= -126, "subnormal"
+    ulp = Fr(2) ** (e - 23)
+    q = a / ulp
+    m = q.numerator // q.denominator
+    frac = q - m
+    if frac > Fr(1, 2) or (frac == Fr(1, 2) and m % 2):
+        m += 1
+    v = m * ulp
+    return (v if x > 0 else -v), abs(frac - Fr(1, 2))
+
+
+def f32_hex(values):
+    """Big-endian fp32 bit patterns of exactly representable values, as one hex string."""
+    return struct.pack(">%df" % len(values), *[float(v) for v in values]).hex()
 
 
 # --------------------------------------------------------------- ManifoldKV
@@ -197,23 +264,8 @@ def oja(seed=3):
         for i in range(0, N, pool):
             rows = X[b][i:i + pool]
             Xp.append([Fr(sum(r[c] for r in rows), len(rows)) for c in range(D)])
-    n = len(Xp)
-    # C = Xp^T Xp / n;  U' = U + eta (C U - U (U^T C U))
-    XpU = [[sum(x[c] * U[c][j] for c in range(D)) for j in range(R)] for x in Xp]
-    CU = [[sum(Xp[i][c] * XpU[i][j] for i in range(n)) / n for j in range(R)] for c in range(D)]
-    M = [[sum(U[c][a] * CU[c][j] for c in range(D)) for j in range(R)] for a in range(R)]
-    U1 = [[U[c][j] + eta * (CU[c][j] - sum(U[c][a] * M[a][j] for a in range(R))) for j in range(R)]
-          for c in range(D)]
-    # thin QR with a positive diagonal, modified Gram-Schmidt in 60-digit decimals
-    A = [[dec(U1[c][j]) for c in range(D)] for j in range(R)]  # columns
-    Qc = []
-    for j in range(R):
-        v = A[j][:]
-        for q in Qc:
-            p = sum(q[c] * v[c] for c in range(D))
-            v = [v[c] - p * q[c] for c in range(D)]
-        nrm = sum(x * x for x in v).sqrt()
-        Qc.append([x / nrm for x in v])
+    U1 = oja_step(U, Xp, eta)
+    Qc = mgs_columns(U1)
     Qm = [[ds(Qc[j][c]) for j in range(R)] for c in range(D)]
     return {
         "source": OJA_PAGE + ", how it works / method details (Oja's rule U <- U + eta (x x^T U - U U^T "
@@ -225,6 +277,117 @@ def oja(seed=3):
         "U_cols": cols, "U_signs": sign, "X": X,
         "X_pooled": [[fs(x) for x in row] for row in Xp],
         "U_step": [[fs(x) for x in row] for row in U1], "U_new": Qm,
+    }
+
+
+def hybrid_exact(Krows, Vrows, Qwin, Uk, Uv, k_anchor):
+    """One hybrid pass over the rows with fp32 bases given exactly: K~ = K U_k,
+    V~ = V U_v, r_t = k_t - U_k K~_t, err_sum_t = sum over the window of |q . r_t|
+    (= |W_t| sqrt(d_h) e_t), the k_anchor largest as anchors (ascending; a 1e-4
+    margin at the threshold), K^ = K~ U_k^T and V^ = V~ U_v^T with the anchor
+    rows full rank."""
+    R = len(Uk[0])
+    Kt = [[sum(k[c] * Uk[c][j] for c in range(D) if k[c]) for j in range(R)] for k in Krows]
+    Vt = [[sum(v[c] * Uv[c][j] for c in range(D) if v[c]) for j in range(R)] for v in Vrows]
+    err = []
+    for k, kt in zip(Krows, Kt):
+        r = [k[c] - sum(Uk[c][j] * kt[j] for j in range(R)) for c in range(D)]
+        err.append(sum(abs(sum(q[c] * r[c] for c in range(D) if q[c])) for q in Qwin))
+    srt = sorted(err, reverse=True)
+    assert srt[k_anchor - 1] > srt[k_anchor] * Fr(10021, 10000), "margin at the anchor threshold"
+    anchors = keep_top(err, k_anchor)
+    Kh = [Krows[t] if t in anchors else [sum(Kt[t][j] * Uk[c][j] for j in range(R)) for c in range(D)]
+          for t in range(len(Krows))]
+    Vh = [Vrows[t] if t in anchors else [sum(Vt[t][j] * Uv[c][j] for j in range(R)) for c in range(D)]
+          for t in range(len(Vrows))]
+    return Kt, Vt, err, anchors, Kh, Vh
+
+
+def stored_f32(U1):
+    """QR of the Oja step's result, then the basis as it is stored between updates:
+    each entry rounded to the nearest fp32 value (asserted to sit at least 1e-6 of
+    the fp32 spacing away from a rounding midpoint, so that a double-precision QR
+    rounds to the same fp32 value)."""
+    Qc = mgs_columns(U1)
+    R = len(Qc)
+    U = [[None] * R for _ in range(D)]
+    for j in range(R):
+        for c in range(D):
+            U[c][j], margin = f32_nearest(Qc[j][c])
+            assert margin > Fr(1, 10 ** 6), "fp32 rounding midpoint"
+    return U
+
+
+def oja_loop(seed=5):
+    """The first seed from `seed` on whose inputs every margin assertion holds."""
+    while True:
+        try:
+            return oja_loop_seeded(seed)
+        except AssertionError:
+            seed += 1
+
+
+def oja_loop_seeded(seed):
+    """Prefill and two decode updates of the hybrid loop on one slice (batch 1,
+    one kv head with g query heads).  Prefill: pool the S0 prompt keys (values)
+    by p, one Oja step on the pooled rows, QR, basis stored in fp32; then the
+    hybrid pass over the S0 tokens with the prompt's W_q queries.  Decode: every
+    T steps, one Oja step on the T buffered tokens (no pooling), QR, fp32; then
+    the hybrid pass over all S0 + jT tokens with the T decode queries of the
+    g heads since the last update."""
+    rnd = random.Random(seed)
+    S0, T, steps, pool, g, Wq, R = 24, 4, 8, 4, 2, 4, 32
+    eta = Fr(1, 256)
+    n_end = S0 + steps
+    sel_k, sel_v = signed_selection(rnd, R), signed_selection(rnd, R)
+    K = ints(rnd, -5, 5, n_end, D)
+    V = ints(rnd, -5, 5, n_end, D)
+    Qp = ints(rnd, -4, 4, g, Wq, D)        # the prompt's last W_q queries of each head
+    Qd = ints(rnd, -4, 4, steps, g, D)     # one query per head per decode step
+    Uk, Uv = selection_matrix(sel_k), selection_matrix(sel_v)
+
+    def pooled(rows):
+        return [[Fr(sum(r[c] for r in rows[i:i + pool]), len(rows[i:i + pool])) for c in range(D)]
+                for i in range(0, len(rows), pool)]
+
+    phases = []
+    for j in range(steps // T + 1):
+        if j == 0:
+            S, Xk, Xv = S0, pooled(K[:S0]), pooled(V[:S0])
+            qwin = [q for h in range(g) for q in Qp[h]]
+        else:
+            S = S0 + j * T
+            Xk, Xv = K[S - T:S], V[S - T:S]
+            qwin = [Qd[s][h] for h in range(g) for s in range(S - T - S0, S - S0)]
+        Uk = stored_f32(oja_step(Uk, Xk, eta))
+        Uv = stored_f32(oja_step(Uv, Xv, eta))
+        k_anchor = -(-5 * S // 100)
+        Kt, Vt, err, anchors, Kh, Vh = hybrid_exact(K[:S], V[:S], qwin, Uk, Uv, k_anchor)
+        rows = sorted(set([0, S - 1] + anchors))
+        phases.append({
+            "S": S, "window_queries": len(qwin), "anchors_k": k_anchor,
+            "Uk_f32": f32_hex([Uk[c][i] for c in range(D) for i in range(R)]),
+            "Uv_f32": f32_hex([Uv[c][i] for c in range(D) for i in range(R)]),
+            "err_sum": [ds(dec(x)) for x in err], "anchor_idx": anchors, "rows": rows,
+            "K_tilde": [[ds(dec(x)) for x in Kt[t]] for t in rows],
+            "V_tilde": [[ds(dec(x)) for x in Vt[t]] for t in rows],
+            "K_hat": [[ds(dec(Fr(x))) for x in Kh[t]] for t in rows],
+            "V_hat": [[ds(dec(Fr(x))) for x in Vh[t]] for t in rows],
+        })
+    return {
+        "source": OJA_PAGE + ", appendix A.1 (Algorithm 1: prefill pools the prompt's keys and values, "
+                  "takes an Oja step with their empirical covariance, re-orthonormalises by QR, then "
+                  "scores every token with the updated bases and keeps the top-k at full rank; decoding "
+                  "buffers T tokens and updates the bases on them every T steps), method details "
+                  "(two-phase online update; e_t over the recent query window) and background on "
+                  "low-rank attention.  Readings: C = X^T X / n uncentred; pooling kernel = stride = p; "
+                  "bases stored in fp32 between updates (U_f32 are their big-endian fp32 bits, [D][R]); "
+                  "at each decode update the whole cache is re-projected, re-scored with the T decode "
+                  "queries of the group's g heads and its ceil(5% S) anchors re-selected.  err_sum[t] = "
+                  "|W_t| sqrt(d_h) e_t; K_tilde .. V_hat are given at the listed rows.",
+        "seed": seed, "S0": S0, "T": T, "steps": steps, "pool": pool, "g": g, "Wq": Wq, "R": R,
+        "eta": fs(eta), "Uk0_cols": sel_k[0], "Uk0_signs": sel_k[1], "Uv0_cols": sel_v[0], "Uv0_signs": sel_v[1],
+        "K": K, "V": V, "Q_prompt": Qp, "Q_decode": Qd, "phases": phases,
     }
 
 
@@ -315,8 +478,12 @@ def pages_figures():
 
 
 def main():
+    only = set(sys.argv[1:])
     for name, fn in (("manifold_tiny", manifold), ("lowrank_tiny", lowrank), ("oja_tiny", oja),
-                     ("refine_tiny", refine), ("pages_figures", pages_figures)):
+                     ("oja_loop_tiny", oja_loop), ("refine_tiny", refine),
+                     ("pages_figures", pages_figures)):
+        if only and name not in only:
+            continue
         with open(os.path.join(HERE, name + ".json"), "w") as f:
             json.dump(fn(), f, separators=(",", ":"))
             f.write("\n")

@@ -262,3 +262,176 @@ def test_refine_worked_example_gpu(gpu_lib):
         assert ok, (key, rel, nbad)
     ok, rel, nbad = score_close(rc[0].cpu().numpy(), dc(d["RC"]))
     assert ok, (rel, nbad)
+
+
+# ------------------------------------------- the hybrid loop (prefill + updates)
+
+def _loop_inputs(d):
+    """The fixture's inputs in the oracle's and the pipeline's shapes."""
+    K, V = (int_bf16(np.array(d[x])) for x in ("K", "V"))              # [S0 + steps, D]
+    Qp = int_bf16(np.array(d["Q_prompt"]))                              # [g, Wq, D]
+    Qd = int_bf16(np.array(d["Q_decode"]))                              # [steps, g, D]
+    Uk = basis([d["Uk0_cols"]], [d["Uk0_signs"]])[0]
+    Uv = basis([d["Uv0_cols"]], [d["Uv0_signs"]])[0]
+    return K, V, Qp, Qd, Uk, Uv
+
+
+def _f32_of(hexstr, R):
+    return np.frombuffer(bytes.fromhex(hexstr), dtype=">f4").astype(np.float32).reshape(D, R)
+
+
+def _loop_matches(d, phases, rtol=1e-12):
+    """Compares a loop's phases (dicts with Uk, Uv, err, idx, Kt, Vt, Khat, Vhat over
+    all S rows) with the fixture; returns the first mismatch or None."""
+    if len(phases) != len(d["phases"]):
+        return "phase count"
+    for j, (got, want) in enumerate(zip(phases, d["phases"])):
+        R = d["R"]
+        for key in ("Uk", "Uv"):
+            if not np.array_equal(np.asarray(got[key], np.float32), _f32_of(want[key + "_f32"], R)):
+                return "phase %d: %s" % (j, key)
+        e = dc(want["err_sum"]) / (want["window_queries"] * math.sqrt(D))
+        if not np.allclose(np.asarray(got["err"]).reshape(-1), e, rtol=rtol, atol=0):
+            return "phase %d: err" % j
+        if np.asarray(got["idx"]).reshape(-1).tolist() != want["anchor_idx"]:
+            return "phase %d: anchors" % j
+        rows = want["rows"]
+        for key, name in (("Kt", "K_tilde"), ("Vt", "V_tilde"), ("Khat", "K_hat"), ("Vhat", "V_hat")):
+            ref = dc(want[name])
+            scale = np.sqrt(np.mean(ref ** 2))
+            val = np.asarray(got[key]).reshape(-1, ref.shape[1])[rows]
+            if not np.allclose(val, ref, rtol=rtol, atol=rtol * scale):
+                return "phase %d: %s" % (j, key)
+    return None
+
+
+def _oracle_phases(res):
+    return [dict(Uk=st["Uk"], Uv=st["Uv"], err=st["err"], idx=st["idx"], Kt=st["Kt"][0],
+                 Vt=st["Vt"][0], Khat=st["Khat"][0], Vhat=st["Vhat"][0]) for st in res]
+
+
+def test_oja_loop_worked_example_oracle():
+    d = load("oja_loop_tiny")
+    K, V, Qp, Qd, Uk, Uv = _loop_inputs(d)
+    res = oracle.full_loop_slice(K, V, Qp, Qd, Uk, Uv, d["S0"], d["steps"], d["T"], d["pool"],
+                                 float(Fraction(d["eta"])))
+    assert [st["S"] for st in res] == [p["S"] for p in d["phases"]]
+    assert _loop_matches(d, _oracle_phases(res)) is None, _loop_matches(d, _oracle_phases(res))
+
+
+def _mutant_loop(K, V, Qp, Qd, Uk, Uv, S0, steps, T, pool, eta, mutation):
+    """The loop of oracle.full_loop_slice rebuilt from the oracle's steps with one
+    planted mistake, to show that the fixture tells each of them apart."""
+    D_ = K.shape[1]
+    Uk = Uk.reshape(1, 1, D_, -1).astype(np.float32)
+    Uv = Uv.reshape(1, 1, D_, -1).astype(np.float32)
+    out = []
+    for j in range(steps // T + 1):
+        if j == 0:
+            S, Xk, Xv, p = S0, K[None, :S0], V[None, :S0], pool
+            qwin = Qp
+            if mutation == "prefill_unpooled":
+                p = 1
+        else:
+            S = S0 + j * T
+            lo = S - T - (T if mutation == "decode_buffer_stale" else 0)
+            Xk, Xv, p = K[None, lo:lo + T], V[None, lo:lo + T], 1
+            q0 = S - T - S0 - (T if mutation == "decode_window_stale" and j > 1 else 0)
+            qwin = np.ascontiguousarray(Qd[q0:q0 + T].transpose(1, 0, 2))
+            if mutation == "decode_window_prompt":
+                qwin = Qp
+        Uk_new = oracle.oja_update(Uk, Xk, p, eta, 1, 1, 1).astype(np.float32)
+        Uv_new = oracle.oja_update(Uv, Xv, p, eta, 1, 1, 1).astype(np.float32)
+        # scoring with the basis from before the update is the planted order mistake
+        Us_k, Us_v = (Uk, Uv) if mutation == "score_before_update" else (Uk_new, Uv_new)
+        k_anchor = 5 * S // 100 if mutation == "anchor_count_floor" else oracle.n_anchors(S)
+        st = oracle.hybrid_compress_slice(K[None, :S], V[None, :S], qwin[None, None], Us_k, Us_v,
+                                          k_anchor)
+        Uk, Uv = Uk_new, Uv_new
+        out.append(dict(Uk=Uk[0, 0], Uv=Uv[0, 0], err=st["err"], idx=st["idx"], Kt=st["Kt"][0],
+                        Vt=st["Vt"][0], Khat=st["Khat"][0], Vhat=st["Vhat"][0]))
+    return out
+
+
+@pytest.mark.parametrize("mutation", [None, "score_before_update", "prefill_unpooled", "decode_buffer_stale",
+                                      "decode_window_stale", "decode_window_prompt",
+                                      "anchor_count_floor"])
+def test_oja_loop_worked_example_detects_planted_mistakes(mutation):
+    # the rebuilt loop without a mutation matches the fixture; each planted mistake
+    # in the order of the steps, the pooling, the buffer, the query window or the
+    # anchor count makes it differ
+    d = load("oja_loop_tiny")
+    K, V, Qp, Qd, Uk, Uv = _loop_inputs(d)
+    got = _mutant_loop(K, V, Qp, Qd, Uk, Uv, d["S0"], d["steps"], d["T"], d["pool"],
+                       float(Fraction(d["eta"])), mutation)
+    miss = _loop_matches(d, got)
+    if mutation is None:
+        assert miss is None, miss
+    else:
+        assert miss is not None, mutation
+
+
+@pytest.mark.gpu
+def test_oja_loop_worked_example_gpu(gpu_lib):
+    # the pipeline's prefill and decode steps through the C ABI (the append, the Oja
+    # updates with QR, the fused compression + reconstruction, the anchor selection)
+    # against the fixture, to the parity rules
+    import torch
+    from token_scoring_eviction_amd import pipeline
+    d = load("oja_loop_tiny")
+    K, V, Qp, Qd, Uk0, Uv0 = _loop_inputs(d)
+    S0, T, steps, pool, g, R = (d[x] for x in ("S0", "T", "steps", "pool", "g", "R"))
+    eta = float(Fraction(d["eta"]))
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+
+    Kc = torch.zeros((1, S0 + steps, D), dtype=torch.bfloat16, device="cuda")
+    Vc = torch.zeros_like(Kc)
+    Kc[0, :S0] = bf(K[:S0])
+    Vc[0, :S0] = bf(V[:S0])
+    Uk = torch.from_numpy(Uk0[None, None].copy()).cuda()
+    Uv = torch.from_numpy(Uv0[None, None].copy()).cuda()
+    st = pipeline.ojakv_prefill(Kc, Vc, bf(Qp)[None, None], Uk, Uv, 1, 1, 1, S0, T=T, pool=pool, eta=eta)
+    snaps = []
+
+    def snap():
+        torch.cuda.synchronize()
+        S = st.S
+        k = pipeline.anchor_count(S)
+        snaps.append(dict(S=S, Uk=st.U_k[0, 0].cpu().numpy(), Uv=st.U_v[0, 0].cpu().numpy(),
+                          err=st.hybrid.err[0, :S].cpu().numpy(),
+                          idx=st.hybrid.idx.view(-1)[:k].cpu().numpy(),
+                          Kt=st.hybrid.Kt[0, :S].cpu().numpy(), Vt=st.hybrid.Vt[0, :S].cpu().numpy(),
+                          Khat=st.hybrid.Khat[0, :S].cpu().numpy(), Vhat=st.hybrid.Vhat[0, :S].cpu().numpy()))
+
+    snap()
+    for s in range(steps):
+        if pipeline.ojakv_decode_step(st, Kc, Vc, bf(K[S0 + s])[None], bf(V[S0 + s])[None],
+                                      bf(Qd[s])[None, None], 1, 1, 1, T=T, eta=eta):
+            snap()
+    assert [s["S"] for s in snaps] == [p["S"] for p in d["phases"]]
+    for got, want in zip(snaps, d["phases"]):
+        for key in ("Uk", "Uv"):
+            ref = _f32_of(want[key + "_f32"], R).astype(np.float64)
+            ok, rel = lowrank_close(got[key][None], ref[None])
+            assert ok, (want["S"], key, rel)
+            U = got[key].astype(np.float64)
+            assert np.abs(U.T @ U - np.eye(R)).max() <= 1e-5
+        e = dc(want["err_sum"]) / (want["window_queries"] * math.sqrt(D))
+        ok, rel, nbad = score_close(got["err"][None], e[None])
+        assert ok, (want["S"], "err", rel, nbad)
+        ok, nb = index_sets_agree(got["idx"][None], np.array([want["anchor_idx"]]), e[None].astype(np.float32),
+                                  want["anchors_k"])
+        assert ok and nb == 0, (want["S"], got["idx"], want["anchor_idx"])
+        rows = want["rows"]
+        for key, name in (("Kt", "K_tilde"), ("Vt", "V_tilde"), ("Khat", "K_hat"), ("Vhat", "V_hat")):
+            ok, rel = lowrank_close(got[key][rows][None], dc(want[name])[None])
+            assert ok, (want["S"], key, rel)
+        for t in want["anchor_idx"]:  # anchor rows are the full-rank rows, exactly
+            assert np.array_equal(got["Khat"][t], bf16_widen(K[t]))
+            assert np.array_equal(got["Vhat"][t], bf16_widen(V[t]))
+
+
+def bf16_widen(bits):
+    return (np.asarray(bits, np.uint16).astype(np.uint32) << 16).view(np.float32)
