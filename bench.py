@@ -12,9 +12,12 @@ score every key + select + compact.
 --config 0..4 measures the other synthetic workloads instead (0: 8 slices at
 S=4096 keep 3277; 2: windowed W=4096 at S=65536 keep 49152; 3: OjaKV prefill
 compression B=4, S=32768, r=64 with 5% anchors; 4: the OjaKV prefill + 256
-decode-step loop at S=131072).  Prints one JSON line: head-tokens/s, the
-roofline of the dominant entry point (algorithmic bytes / its average time,
-HIP events on the launch stream), and the CPU oracle on a bounded sample.
+decode-step loop at S=131072).  Prints one JSON line: head-tokens/s; the
+roofline of the whole step (its algorithmic bytes -- K read once, kept V rows
+read, kept K/V written, scores and indices written, low-rank outputs written --
+over the step's time, HIP events on the launch stream), with the dominant
+kernel named; per entry point, its share of those bytes and its time; and the
+CPU oracle on a bounded sample.
 """
 from __future__ import annotations
 
@@ -51,6 +54,13 @@ def measured_traffic(entry_point, workload):
     if any(source_digest(p) != h for p, h in rec["sources"].items()):
         return None
     return rec["bytes_per_launch"]
+
+
+def step_traffic(ops, workload):
+    """Counter bytes of one step: the sum over its entry points, or None unless every
+    one of them has a current record."""
+    parts = [measured_traffic(op.name, workload) for op in ops]
+    return None if any(x is None for x in parts) else sum(parts)
 
 
 def parse():
@@ -140,11 +150,17 @@ def run_cpu_baseline(cpu, seconds):
 
 
 class Op:
-    """An entry-point call inside a step, with its algorithmic bytes and flops."""
+    """An entry-point call inside a step.  nbytes: its share of the step's
+    algorithmic bytes (what the method must move: K once, kept V rows, kept K/V
+    written, scores, indices, low-rank outputs); moved: the bytes this
+    implementation has to move for it (adds re-reads, e.g. the selection's read of
+    the scores and the copy's read of the kept K rows); flops: the method's own
+    dense-contraction flops (no split-operand passes)."""
 
-    def __init__(self, name, fn, nbytes, flops=0, kernel=None):
+    def __init__(self, name, fn, nbytes, flops=0, kernel=None, moved=None):
         self.name, self.fn, self.nbytes, self.flops = name, fn, nbytes, flops
         self.kernel = kernel or name
+        self.moved = nbytes if moved is None else moved
         self.ms = []
 
 
@@ -182,6 +198,9 @@ def manifold_workload(cfg, dev, metric="l2", budgets="uniform"):
     small = G * S * 256 < (160 << 20)
     score_kernel = ("centroid_partial+centroid_final+" + ("cosine_distance" if metric == "cosine" else "l2_distance")
                     if small else "l2_fused")
+    # algorithmic bytes: K read once and the scores written (scoring); kept V rows read,
+    # kept K and V rows written, indices written (compaction).  The selection's read of
+    # the scores and the copy's read of the kept K rows are the implementation's own.
     ops = [Op(score_name, score, G * S * (256 + 4), kernel=score_kernel)]
     if budgets == "ripple":
         # per-layer budgets from a seeded sensitivity profile, same total as keep per slice
@@ -190,22 +209,26 @@ def manifold_workload(cfg, dev, metric="l2", budgets="uniform"):
         kl = kvc.kvc_layer_budgets(sens, 8.0, 4.0, L * keep, S)
         ks = np.repeat(kl, H)
         total = int(ks.sum())
+        kd = torch.from_numpy(ks.astype(np.int64)).to(dev)  # the budgets live on the device
         rbuf = (torch.empty(total, dtype=torch.int32, device=dev),
                 torch.empty((total, 128), dtype=torch.bfloat16, device=dev),
                 torch.empty((total, 128), dtype=torch.bfloat16, device=dev))
         ops.append(Op("kvc_topk_compact_ragged",
-                      lambda: kvc.kvc_topk_compact_ragged(buf.scores, ks, K, V, idx_out=rbuf[0],
-                                                          K_out=rbuf[1], V_out=rbuf[2]),
-                      G * S * 4 + total * (2 * 256 * 2 + 4),
-                      kernel=compaction_kernels(ks.max(), G)))
+                      lambda: kvc.kvc_topk_compact_ragged(buf.scores, kd, K, V, idx_out=rbuf[0],
+                                                          K_out=rbuf[1], V_out=rbuf[2], k_max=int(ks.max()),
+                                                          k_total=total),
+                      total * (3 * 256 + 4), moved=G * S * 4 + total * (4 * 256 + 4),
+                      kernel="ragged_offsets+select_compact+gather_rows"))
         desc += "; RippleKV per-layer budgets %d..%d (r=8, gamma=4)" % (kl.min(), kl.max())
+        kept = total
     else:
         ops.append(Op("kvc_topk_compact",
                       lambda: kvc.kvc_topk_compact(buf.scores, keep, K, V, idx_out=buf.idx, K_out=buf.K_out,
                                                    V_out=buf.V_out),
-                      G * S * 4 + G * keep * (2 * 256 * 2 + 4),
-                      kernel=compaction_kernels(keep, G)))
-    algo = G * S * 256 + G * keep * 256 + 2 * G * keep * 256 + G * S * 4 + G * keep * 4
+                      G * keep * (3 * 256 + 4), moved=G * S * 4 + G * keep * (4 * 256 + 4),
+                      kernel="select_compact+gather_rows"))
+        kept = G * keep
+    algo = G * S * (256 + 4) + kept * (3 * 256 + 4)
     config = {"workload": desc, "slices": G, "seq_len": S, "keep": keep, "head_dim": 128,
               "window": W, "metric": metric, "budgets": budgets}
 
@@ -233,15 +256,6 @@ def manifold_workload(cfg, dev, metric="l2", budgets="uniform"):
     return ops, G * S, algo, config, cpu
 
 
-def compaction_kernels(k, G):
-    """Kernels behind kvc_topk_compact: the selection, then the wide gather of the kept rows
-    (the selecting workgroups copy the rows themselves only with KVC_GATHER_SEPARATE=0,
-    k <= 8192 and a slice per compute unit or more)."""
-    if os.environ.get("KVC_GATHER_SEPARATE") == "0" and k <= 8192 and G >= 256:
-        return "select_compact"
-    return "select_compact+gather_rows"
-
-
 def refine_workload(dev):
     import torch
 
@@ -261,11 +275,14 @@ def refine_workload(dev):
         kvc._check("kvc_cluster_summaries", lib.kvc_cluster_summaries(
             kvc._ptr(K), kvc._ptr(V), G, S, 128, c, *[kvc._ptr(t) for t in summ], kvc._stream()))
 
+    # algorithmic bytes: K and V read once, summaries written; the risk pass reads the
+    # mean keys, radii and value norms and writes one score per (query, cluster)
     ops = [Op("kvc_cluster_summaries", summaries, G * S * 512 + G * nC * (2 * 512 + 8),
               kernel="cluster_summary_kernel"),
            Op("kvc_refine_risk", lambda: kvc.kvc_refine_risk(summ[0], summ[2], summ[3], S, c, Q, rc=rc),
-              G * nC * (512 + 8 + 3 * nq * 4), kernel="risk_partial_kernel + risk_final_kernel")]
-    algo = G * S * 512 + G * nC * (2 * 512 + 8) + G * nC * (512 + 8 + nq * 4)
+              G * nC * (512 + 8 + nq * 4), moved=G * nC * (512 + 8 + 3 * nq * 4),
+              kernel="risk_partial_kernel+risk_final_kernel")]
+    algo = sum(op.nbytes for op in ops)
     config = {"workload": "RefineKV cluster summaries (contiguous 10-key clusters: mean key, mean value, "
                           "key radius, value norm) and risk scores of every cluster for the 4 query heads "
                           "of each kv head, 32 layers x 8 KV heads x d_h 128, S=131072",
@@ -298,19 +315,23 @@ def oja_workload(dev, storage="fp32"):
     st = pipeline.alloc_hybrid(G, S, R, device=dev, max_anchor=k, with_hat=False, storage=storage)
     ob = 2 if storage == "bf16" else 4  # bytes per stored K~ / V~ element
     compress = kvc.kvc_lowrank_compress_bf16 if storage == "bf16" else kvc.kvc_lowrank_compress
+    # the method's dense contractions per head-token: K~ = K U_k (2*128*R), the residual
+    # r = k - U_k K~ (2*R*128), the window's products q.r over g*W_q queries
+    # (2*128*g*W_q), V~ = V U_v (2*128*R): 81,920 flop at R = 64, g*W_q = 128
+    flops_per_token = 2 * 128 * R + 2 * R * 128 + 2 * 128 * (Hq // Hkv) * Wq + 2 * 128 * R
     ops = [
         Op("kvc_lowrank_compress" + ("_bf16" if storage == "bf16" else ""),
            lambda: compress(inp.K, inp.V, inp.Q, inp.Uk, inp.Uv, L, B, Hkv,
                             K_tilde=st.Kt, V_tilde=st.Vt, err=st.err),
-           G * S * (2 * 256 + 2 * R * ob + 4),
-           flops=G * S * (2 * 2 * 128 * R + 3 * 2 * 128 * (Hq // Hkv) * Wq + 2 * 2 * 128 * R),
-           kernel="project_kernel"),
+           G * S * (2 * 256 + 2 * R * ob + 4), flops=G * S * flops_per_token,
+           kernel="prep_query_kernel+project_kernel"),
         Op("kvc_topk_compact",
            lambda: kvc.kvc_topk_compact(st.err, k, inp.K, inp.V, idx_out=st.idx, K_out=st.K_anchor,
                                         V_out=st.V_anchor),
-           G * S * 4 + G * k * (2 * 256 * 2 + 4), kernel=compaction_kernels(k, G)),
+           G * k * (3 * 256 + 4), moved=G * S * 4 + G * k * (4 * 256 + 4),
+           kernel="select_compact+gather_rows"),
     ]
-    algo = G * S * (2 * 256 + 2 * R * ob + 4) + G * k * (2 * 256 * 2 + 4)
+    algo = sum(op.nbytes for op in ops)
     config = {"workload": "OjaKV hybrid low-rank prefill compression, 32 layers x batch 4 x 8 KV heads "
                           "(32 query heads), d_h 128, S=32768, r=64, 32-query window, 5% anchors",
               "slices": G, "seq_len": S, "rank": R, "anchors": k, "storage": storage}
@@ -422,24 +443,72 @@ def run_loop_config(args, dev):
                       "slices": G, "seq_len": S0, "decode_steps": steps, "updates": 8,
                       "storage": args.storage})
     line["phases_ms"] = {"prefill": pre, "per_update": upd, "whole_loop": ms}
-    line["step_hbm"] = {"algorithmic_bytes": algo, "GBs": algo / ms / 1e6,
-                        "frac": algo / ms / 1e6 / HBM_PEAK_GBS}
     # algorithmic bytes of one fused call: K and V read, K~/V~ and K^/V^ written, e written
     fused_ms = sum(a.elapsed_time(b) for a, b, _ in fused_calls)
     fused_bytes = sum(n * (2 * 256 + 2 * R * ob + 2 * 128 * ob + 4) for _, _, n in fused_calls)
-    achieved = fused_bytes / fused_ms / 1e6
-    line["roofline"] = {"bound": "hbm", "entry_point": fused_name, "kernel": "project_kernel (fused reconstruction)",
-                        "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                        "traffic": measured_traffic(fused_name, "config4"),
-                        "algorithmic_bytes": fused_bytes / max(1, len(fused_calls)),
-                        "ms_per_call": fused_ms / max(1, len(fused_calls)), "calls": len(fused_calls)}
+    ncalls = max(1, len(fused_calls))
+    fused_per_loop = fused_bytes / reps
+    # the roofline of the whole loop (pooling pass, 9 compression + reconstruction passes,
+    # anchors, appends); the fused pass is the dominant entry point
+    achieved = algo / ms / 1e6
+    line["roofline"] = {"bound": "hbm", "scope": "step (the whole loop)", "achieved": achieved,
+                        "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
+                        "traffic": None, "algorithmic_bytes": algo,
+                        "dominant": {"entry_point": fused_name, "kernels": "project_kernel (fused reconstruction)",
+                                     "ms": fused_ms / ncalls, "calls_per_loop": len(fused_calls) / reps,
+                                     "frac": fused_bytes / fused_ms / 1e6 / HBM_PEAK_GBS,
+                                     "algorithmic_share": fused_per_loop / algo}}
+    line["ops"] = {fused_name: {"ms": fused_ms / ncalls, "algorithmic_bytes": fused_bytes / ncalls,
+                                "GBs": fused_bytes / fused_ms / 1e6,
+                                "frac": fused_bytes / fused_ms / 1e6 / HBM_PEAK_GBS,
+                                "traffic": measured_traffic(fused_name, "config4"),
+                                "mfma": {"flops_per_head_token": 81920 + 2 * 2 * 128 * R,
+                                         "TFLOPs": sum(n for _, _, n in fused_calls) * (81920 + 4 * 128 * R)
+                                         / fused_ms / 1e9}}}
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = loop_cpu_baseline(inp, toks, S0, T, G, R)
     print(json.dumps(line), flush=True)
 
 
+def loop_cpu_baseline(inp, toks, S0, T, G, R):
+    """The oracle's loop on one slice (layer 0, kv head 0), pinned to one core: the
+    pooled prefill update and pass, then the first decode update and pass (two
+    passes over ~131K tokens).  Reported as oracle scorings/s; the time of the whole
+    workload on one core is extrapolated from it."""
+    import numpy as np
+    import torch
+
+    import oracle
+    import synth
+    grp = inp.Hq // inp.Hkv
+    K = synth.bf16_bits(inp.K[0, :S0 + T])
+    V = synth.bf16_bits(inp.V[0, :S0 + T])
+    Qp = synth.bf16_bits(inp.Q[0, 0, :grp])
+    Qd = synth.bf16_bits(torch.stack([q[0, 0, :grp] for _, _, q in toks[:T]]).to(torch.bfloat16))
+    Uk, Uv = inp.Uk[0, 0].cpu().numpy(), inp.Uv[0, 0].cpu().numpy()
+
+    def cpu(_budget):
+        t0 = time.perf_counter()
+        res = oracle.full_loop_slice(K, V, Qp, Qd, Uk, Uv, S0, T, T, 32, 1e-3)
+        t = time.perf_counter() - t0
+        return sum(st["S"] for st in res), t, ("layer 0 / kv head 0: the pooled prefill update and pass over "
+                                               "%d tokens, then the first decode update and pass over %d" % (S0, S0 + T))
+
+    rec = run_cpu_baseline(cpu, 0.0)
+    rec["unit"] = "scorings/s"
+    scorings = G * sum(S0 + T * j for j in range(9))
+    rec["extrapolated_full_workload_s"] = scorings / rec["value"]
+    rec["extrapolation"] = ("%d scorings (256 slices x 9 passes) at the sample's rate on one core; "
+                            "not measured" % scorings)
+    del np
+    return rec
+
+
 def base_line(args, metric, value, ms_step, steps, config):
+    # the path takes bf16 K/V/Q and computes in fp32 (scores, centroids, low-rank outputs)
     return {"metric": metric, "value": value, "unit": "head-tokens/s", "n_gpus": 1, "steps": steps,
             "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
-            "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+            "scaling": "weak", "vs_baseline": None, "dtype": "fp32 (bf16 inputs)", "data": "synthetic",
             "config": config}
 
 
@@ -491,32 +560,42 @@ def main():
     for i in range(args.steps):
         for op, (a, b) in zip(ops, ev[i]):
             op.ms.append(a.elapsed_time(b))
+    workload = "refine" if args.refine else "config%d" % args.config
     per_op = {}
     for op in ops:
         ms = sum(op.ms) / len(op.ms)
-        per_op[op.name] = {"ms": ms, "bytes": op.nbytes, "GBs": op.nbytes / ms / 1e6,
-                           "kernel": op.kernel}
+        rec = {"ms": ms, "algorithmic_bytes": op.nbytes, "algorithmic_share": op.nbytes / algo,
+               "GBs": op.nbytes / ms / 1e6, "frac": op.nbytes / ms / 1e6 / HBM_PEAK_GBS,
+               "moved_bytes": op.moved, "moved_GBs": op.moved / ms / 1e6, "kernels": op.kernel,
+               "traffic": measured_traffic(op.name, workload)}
         if op.flops:
-            per_op[op.name]["TFLOPs"] = op.flops / ms / 1e9
+            rec["mfma"] = {"flops": op.flops, "TFLOPs": op.flops / ms / 1e9,
+                           "frac": op.flops / ms / 1e9 / MFMA_BF16_PEAK_TFLOPS}
+        per_op[op.name] = rec
     dom = max(per_op, key=lambda n: per_op[n]["ms"])
-    achieved = per_op[dom]["GBs"]
     line = base_line(args, "KV head-tokens scored+compacted/s", head_tokens / (ms_step / 1e3),
                      ms_step, args.steps, config)
-    line["roofline"] = {"bound": "hbm", "entry_point": dom, "kernel": per_op[dom]["kernel"],
-                        "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS,
-                        "traffic": measured_traffic(dom, "refine" if args.refine else "config%d" % args.config),
-                        "algorithmic_bytes": per_op[dom]["bytes"]}
-    if "TFLOPs" in per_op[dom]:
-        line["roofline"]["mfma_TFLOPs"] = per_op[dom]["TFLOPs"]
-        line["roofline"]["mfma_frac"] = per_op[dom]["TFLOPs"] / MFMA_BF16_PEAK_TFLOPS
-    line["step_hbm"] = {"algorithmic_bytes": algo, "GBs": algo / ms_step / 1e6,
-                        "frac": algo / ms_step / 1e6 / HBM_PEAK_GBS}
+    # the roofline of the whole step: its algorithmic bytes over its time; the entry
+    # point that takes longest is named with its kernels and its own fraction
+    achieved = algo / ms_step / 1e6
+    line["roofline"] = {"bound": "hbm", "scope": "step", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                        "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": step_traffic(ops, workload),
+                        "algorithmic_bytes": algo,
+                        "dominant": {"entry_point": dom, "kernels": per_op[dom]["kernels"],
+                                     "ms": per_op[dom]["ms"], "frac": per_op[dom]["frac"],
+                                     "algorithmic_share": per_op[dom]["algorithmic_share"]}}
+    mf = [r["mfma"] for r in per_op.values() if "mfma" in r]
+    if mf:
+        line["roofline"]["mfma"] = mf[0]
     line["ops"] = per_op
     # context for the fraction: what a plain 1 GiB device copy reaches on this GPU
     copy_ms, copy_gbs = time_device_copy(1024, 10)
     line["context"] = {"device_copy_GBs": copy_gbs, "device_copy_frac": copy_gbs / HBM_PEAK_GBS}
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = run_cpu_baseline(cpu, args.cpu_seconds)
+        rec = run_cpu_baseline(cpu, args.cpu_seconds)
+        rec["extrapolated_full_workload_s"] = head_tokens / rec["value"]
+        rec["extrapolation"] = "the whole workload at the sample's rate on one core; not measured"
+        line["cpu_baseline"] = rec
     print(json.dumps(line), flush=True)
 
 

@@ -49,15 +49,31 @@
 extern "C" {
 #endif
 
-#define KVC_ABI_VERSION 4
+#define KVC_ABI_VERSION 5
 
 typedef enum kvc_status {
     KVC_OK = 0,
     KVC_ERR_INVALID_ARGUMENT = 1,   /* null/misaligned pointer, negative or inconsistent size */
     KVC_ERR_UNSUPPORTED = 2,        /* valid but not built: D != 128, R not in {32,64,96,128}, ... */
     KVC_ERR_WORKSPACE_TOO_SMALL = 3,/* ws_bytes < kvc_workspace_bytes(...) */
-    KVC_ERR_HIP = 4                 /* a HIP runtime call or kernel launch failed */
+    KVC_ERR_HIP = 4,                /* a HIP runtime call or kernel launch failed */
+    KVC_ERR_WAIT_EXPIRED = 5        /* reported by kvc_workspace_status: a bounded in-kernel
+                                       wait gave up; the affected scores are NaN */
 } kvc_status;
+
+/* Process-wide options for tests and measurements (kvc_set_option).  The
+ * defaults select the production kernel paths; every path computes the same
+ * results. */
+typedef enum kvc_option {
+    KVC_OPTION_SCORE_PATH = 0,       /* centroid scores: 0 automatic (default), 1 the single-read
+                                        cooperative kernel where its grid fits, 2 the three-launch path */
+    KVC_OPTION_SCORE_SPIN_LIMIT = 1, /* polls of a centroid wait before it gives up: -1 the built-in
+                                        limit (default), 0 .. 2^32-1 (0: the first poll that finds no
+                                        centroid gives up; lets a test force the expired-wait path) */
+    KVC_OPTION_GATHER_PATH = 2       /* kept-row copy: 0 a separate wide gather launch (default),
+                                        1 the selecting workgroup copies its slice's rows when
+                                        k <= 8192 and there are at least as many slices as CUs */
+} kvc_option;
 
 typedef enum kvc_op {
     KVC_OP_SCORE_L2 = 0,
@@ -92,6 +108,23 @@ typedef struct kvc_dims {
 /* ABI version of the loaded library (KVC_ABI_VERSION). */
 int kvc_abi_version(void);
 
+/* Sets a kvc_option for every later call in the process (calls already queued
+ * are not affected).  A value outside the option's range, or an unknown
+ * option: KVC_ERR_INVALID_ARGUMENT, and nothing changes. */
+kvc_status kvc_set_option(kvc_option opt, int64_t value);
+
+/* Failures that only the kernels can see, recorded in the status header at the
+ * start of `ws` by the last call that used this workspace (kvc_score_l2,
+ * kvc_score_l2_windowed, kvc_score_centroid, kvc_topk_compact_ragged; each of
+ * them clears it before its kernels run).  Waits for `stream` to finish, then
+ * reads the header: KVC_OK; KVC_ERR_WAIT_EXPIRED when a centroid wait gave up
+ * (those tiles' scores are NaN, and NaN scores rank below every number in
+ * kvc_topk_compact); KVC_ERR_INVALID_ARGUMENT when a device-side budget of
+ * kvc_topk_compact_ragged was out of bounds (that slice kept nothing);
+ * KVC_ERR_HIP when the wait or the read failed.  ws must be a workspace of one
+ * of those calls, 256-byte aligned. */
+kvc_status kvc_workspace_status(const void *ws, hipStream_t stream);
+
 /* Static, human-readable text for a status code. */
 const char *kvc_status_str(kvc_status s);
 
@@ -99,7 +132,7 @@ const char *kvc_status_str(kvc_status s);
  *   SCORE_L2, SCORE_L2_WINDOWED, SCORE_CENTROID: G = L*B*H_kv slices of S
  *     tokens; W = window (ignored for SCORE_L2).
  *   TOPK_COMPACT: G = L*B*H_kv slices of S tokens; k = tokens kept.
- *   TOPK_RAGGED: G = L*B*H_kv slices (16 bytes per slice).
+ *   TOPK_RAGGED: G = L*B*H_kv slices (a 256-byte status header + 16 bytes per slice).
  *   REFINE_RISK: G = L*B*H_kv slices of S tokens; k = cluster size c
  *     (144 bytes per 128 clusters of a slice).
  *   LOWRANK_COMPRESS, OJA_UPDATE, RECONSTRUCT: shapes from `d`; for OJA_UPDATE
@@ -117,7 +150,8 @@ size_t kvc_workspace_bytes(kvc_op op, const kvc_dims *d, int64_t k, int64_t W);
  * Large caches are scored by one cooperative launch whose workgroups exchange
  * each window's centroid; every wait in it is bounded.  A wait that expires
  * (it cannot while the grid stays resident, as the cooperative launch
- * guarantees) leaves the affected scores NaN rather than wrong finite values. */
+ * guarantees) leaves the affected scores NaN rather than wrong finite values,
+ * and kvc_workspace_status(ws, stream) then returns KVC_ERR_WAIT_EXPIRED. */
 kvc_status kvc_score_l2(const uint16_t *K, int64_t G, int64_t S, int32_t D, float *scores,
                         float *centroid, void *ws, size_t ws_bytes, hipStream_t stream);
 
@@ -172,16 +206,23 @@ kvc_status kvc_layer_budgets(const double *sensitivity, int64_t L, double r, dou
 
 /* Retention and compaction with a budget per slice (e.g. RippleKV's layer
  * budgets, every slice of layer l keeping k_l): as kvc_topk_compact with slice
- * g keeping k[g] tokens, 0 <= k[g] <= S.  k is a HOST array [G], read before the
- * call returns.  Outputs are packed in slice order: slice g's indices are
- * idx_out[o_g .. o_g + k[g]) with o_g = k[0] + ... + k[g-1], and its rows
- * K_out[o_g + i][:] (likewise V_out); idx_out int32 [sum k], K_out, V_out bf16
- * [sum k][D].  The workspace holds the budgets and offsets on the device
- * (kvc_workspace_bytes(KVC_OP_TOPK_RAGGED, ...)). */
+ * g keeping k[g] tokens.  k is a DEVICE array int64 [G] (8-byte aligned), read
+ * by the call's kernels on `stream`.  Outputs are packed in slice order: slice
+ * g's indices are idx_out[o_g .. o_g + k[g]) with o_g = k[0] + ... + k[g-1],
+ * and its rows K_out[o_g + i][:] (likewise V_out).
+ *   k_max:   host bound on every budget, 0 <= k_max <= S (sizes the row copy)
+ *   k_total: capacity of the packed outputs in rows: idx_out int32 [k_total],
+ *            K_out, V_out bf16 [k_total][D]
+ * The budgets are checked on the device: a slice whose budget is negative or
+ * above k_max, or whose rows would end past k_total, keeps nothing, no output
+ * is written outside [0, k_total), and kvc_workspace_status on this workspace
+ * reports KVC_ERR_INVALID_ARGUMENT.  The workspace (kvc_workspace_bytes(
+ * KVC_OP_TOPK_RAGGED, ...)) holds the status header, the checked budgets and
+ * the offsets. */
 kvc_status kvc_topk_compact_ragged(const float *scores, int64_t G, int64_t S, int64_t s_stride,
-                                   const int64_t *k, const uint16_t *K, const uint16_t *V,
-                                   int32_t D, int32_t *idx_out, uint16_t *K_out, uint16_t *V_out,
-                                   void *ws, size_t ws_bytes, hipStream_t stream);
+                                   const int64_t *k, int64_t k_max, int64_t k_total, const uint16_t *K,
+                                   const uint16_t *V, int32_t D, int32_t *idx_out, uint16_t *K_out,
+                                   uint16_t *V_out, void *ws, size_t ws_bytes, hipStream_t stream);
 
 /* RefineKV cluster summaries ([RFK] "Summarize": contiguous clusters with
  * cached mean keys, mean values and metadata).  For slice g and cluster

@@ -21,3 +21,12 @@ def gpu_lib():
     from token_scoring_eviction_amd import kvc
     kvc.load()
     return kvc
+
+
+@pytest.fixture
+def kvc_option(gpu_lib):
+    """Sets libkvc's process-wide options (kvc_set_option) for one test; every option
+    goes back to its default afterwards."""
+    yield gpu_lib.kvc_set_option
+    for name, value in gpu_lib.OPTION_DEFAULTS.items():
+        gpu_lib.kvc_set_option(name, value)

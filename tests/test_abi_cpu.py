@@ -29,7 +29,7 @@ def test_library_exports_every_declared_symbol():
     lib = kvc.load()
     for name in _declared():
         assert hasattr(lib, name), name
-    assert lib.kvc_abi_version() == 4
+    assert lib.kvc_abi_version() == 5
     assert lib.kvc_status_str(kvc.OK) == b"ok"
     assert lib.kvc_status_str(kvc.ERR_WORKSPACE_TOO_SMALL) == b"workspace too small"
     assert lib.kvc_status_str(99) == b"unknown status"
@@ -61,5 +61,8 @@ def test_workspace_sizing():
     assert kvc.workspace_bytes(kvc.OP_OJA_UPDATE, D(1, 1, 1, 0, 10, 0, 128, 48, 0), 0, 1) == 0
     assert kvc.workspace_bytes(kvc.OP_OJA_UPDATE, D(32, 1, 8, 0, 131072, 0, 128, 64, 0), 0, 32) > 0
     assert kvc.workspace_bytes(kvc.OP_TOPK_COMPACT, D(1, 1, 8, 0, 4096, 0, 128, 0, 0), 3277) == 0
+    # ragged selection: the status header, then a budget and an offset per slice
+    assert kvc.workspace_bytes(kvc.OP_TOPK_RAGGED, D(1, 1, 300, 0, 4096, 0, 128, 0, 0)) == \
+        256 + 2560 + 300 * 8  # 2400 bytes of budgets padded to 2560, then the offsets
     assert kvc.workspace_bytes(kvc.OP_RECONSTRUCT, D(1, 1, 8, 0, 4096, 0, 128, 64, 0), 10) == 0
     assert kvc.load().kvc_workspace_bytes(0, None, 0, 0) == 0

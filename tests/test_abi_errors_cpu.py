@@ -59,15 +59,17 @@ def test_topk_entry_points(lib):
     assert f(A, 0, 100, 100, 10, NULL, NULL, 128, B, NULL, NULL, NULL, 0, NULL) == OK   # G = 0
     assert f(NULL, 2, 100, 100, 10, NULL, NULL, 128, B, NULL, NULL, NULL, 0, NULL) == INV
     assert f(A, 2, 100, 100, 10, P(0x100008), NULL, 128, B, D_, NULL, NULL, 0, NULL) == INV  # K misaligned
-    ks = np.array([3, 101], dtype=np.int64)
-    kp = ks.ctypes.data_as(ctypes.c_void_p)
+    # budgets are a device array checked by the call's kernels; the host checks their bound
+    # k_max, the packed capacity k_total, the pointers and the workspace
     g = lib.kvc_topk_compact_ragged
-    assert g(A, 2, 100, 100, kp, NULL, NULL, 128, B, NULL, NULL, W_, 1 << 20, NULL) == INV  # k[1] > S
-    assert g(A, 2, 100, 100, NULL, NULL, NULL, 128, B, NULL, NULL, W_, 1 << 20, NULL) == INV  # no budgets
-    ks[:] = 0
-    assert g(A, 2, 100, 100, kp, NULL, NULL, 128, B, NULL, NULL, NULL, 0, NULL) == OK       # every k = 0
-    ks[:] = 5
-    assert g(A, 2, 100, 100, kp, NULL, NULL, 128, B, NULL, NULL, W_, 0, NULL) == WS
+    assert g(A, 2, 100, 100, C, 101, 10, NULL, NULL, 128, B, NULL, NULL, W_, 1 << 20, NULL) == INV  # k_max > S
+    assert g(A, 2, 100, 100, C, 5, -1, NULL, NULL, 128, B, NULL, NULL, W_, 1 << 20, NULL) == INV    # k_total < 0
+    assert g(A, 2, 100, 100, NULL, 5, 10, NULL, NULL, 128, B, NULL, NULL, W_, 1 << 20, NULL) == INV  # no budgets
+    assert g(A, 2, 100, 100, P(0x300004), 5, 10, NULL, NULL, 128, B, NULL, NULL, W_, 1 << 20,
+             NULL) == INV                                                                     # budgets misaligned
+    assert g(A, 2, 100, 100, C, 5, 10, NULL, NULL, 128, B, NULL, NULL, NULL, 0, NULL) == INV    # no workspace
+    assert g(A, 2, 100, 100, C, 5, 10, NULL, NULL, 128, B, NULL, NULL, W_, 0, NULL) == WS
+    assert g(A, 0, 100, 100, C, 5, 10, NULL, NULL, 128, B, NULL, NULL, NULL, 0, NULL) == OK     # G = 0
 
 
 def test_lowrank_entry_points(lib):
@@ -127,3 +129,21 @@ def test_refine_entry_points(lib):
     need = kvc.workspace_bytes(kvc.OP_REFINE_RISK, kvc._dims(1, 1, 2, 0, 100, 0, 128, 0, 0), 10)
     assert need == 2 * 9 * 16                                     # one chunk record per slice
     assert g(A, B, C, 2, 100, 10, 128, D_, 4, E, W_, need - 1, NULL) == WS
+
+
+def test_options_and_deferred_status(lib):
+    # every option takes its documented range and nothing else (values unchanged on error)
+    for opt, good, bad in ((kvc.OPTION_SCORE_PATH, (0, 1, 2), (-1, 3)),
+                           (kvc.OPTION_SCORE_SPIN_LIMIT, (-1, 0, 2 ** 32 - 1), (-2, 2 ** 32)),
+                           (kvc.OPTION_GATHER_PATH, (0, 1), (-1, 2))):
+        for v in good:
+            assert lib.kvc_set_option(opt, v) == OK
+        for v in bad:
+            assert lib.kvc_set_option(opt, v) == INV
+    assert lib.kvc_set_option(7, 0) == INV
+    for name, v in kvc.OPTION_DEFAULTS.items():
+        assert lib.kvc_set_option(kvc.OPTIONS[name], v) == OK
+    # the status query refuses a missing or misaligned workspace before touching the device
+    assert lib.kvc_workspace_status(NULL, NULL) == INV
+    assert lib.kvc_workspace_status(P(0x100010), NULL) == INV
+    assert lib.kvc_status_str(kvc.ERR_WAIT_EXPIRED).startswith(b"an in-kernel wait expired")

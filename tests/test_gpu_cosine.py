@@ -28,8 +28,8 @@ def _check(K, s, W=None):
 
 @pytest.mark.parametrize("path", ["0", "1"])
 @pytest.mark.parametrize("G,S", [(1, 1), (3, 257), (2, 1000), (4, 4096), (1, 16384 + 77)])
-def test_cosine_global_small(gpu_lib, monkeypatch, G, S, path):
-    monkeypatch.setenv("KVC_SCORE_UNFUSED", path)
+def test_cosine_global_small(gpu_lib, kvc_option, G, S, path):
+    kvc_option("score_path", 1 + int(path))
     K, _, _ = synth.manifold_global(1, 1, G, S, planted=min(4, S), seed=S + 1, device=DEV)
     mu_gpu = torch.empty((G, 128), dtype=torch.float32, device=DEV)
     s = gpu_lib.kvc_score_centroid(K, metric="cosine", centroids=mu_gpu)
@@ -41,15 +41,15 @@ def test_cosine_global_small(gpu_lib, monkeypatch, G, S, path):
 
 @pytest.mark.parametrize("path", ["0", "1"])
 @pytest.mark.parametrize("S,W", [(1000, 1), (1000, 300), (4096 * 3 + 5, 4096), (8192, 512)])
-def test_cosine_windowed_small(gpu_lib, monkeypatch, S, W, path):
-    monkeypatch.setenv("KVC_SCORE_UNFUSED", path)
+def test_cosine_windowed_small(gpu_lib, kvc_option, S, W, path):
+    kvc_option("score_path", 1 + int(path))
     K, _ = synth.manifold_drifting(1, 1, 2, S, segment=max(1, S // 3), seed=W + 7, device=DEV)
     s = gpu_lib.kvc_score_centroid(K, W=W, metric="cosine")
     torch.cuda.synchronize()
     _check(K, s, W)
 
 
-def test_cosine_degenerate_and_nearly_parallel(gpu_lib, monkeypatch):
+def test_cosine_degenerate_and_nearly_parallel(gpu_lib, kvc_option):
     # slice 0: a zero key among keys with a nonzero centroid (score 1);
     # slice 1: integer keys summing exactly to zero (zero centroid: every score 1);
     # slice 2: keys nearly parallel to the centroid (scores ~1e-5, which the evaluation
@@ -65,7 +65,7 @@ def test_cosine_degenerate_and_nearly_parallel(gpu_lib, monkeypatch):
     K[2] = base[None] * rng.uniform(0.5, 2.0, (S, 1)) + rng.normal(0.0, 4e-3, (S, 128))
     Kt = torch.from_numpy(K).to(torch.bfloat16).to(DEV)
     for path in ("0", "1"):
-        monkeypatch.setenv("KVC_SCORE_UNFUSED", path)
+        kvc_option("score_path", 1 + int(path))
         s = gpu_lib.kvc_score_centroid(Kt, metric="cosine")
         torch.cuda.synchronize()
         ora, _ = _check(Kt, s)
@@ -75,11 +75,11 @@ def test_cosine_degenerate_and_nearly_parallel(gpu_lib, monkeypatch):
 
 
 @pytest.mark.parametrize("W", [None, 4096, 1000])
-def test_cosine_fused_and_three_launch_paths_agree(gpu_lib, monkeypatch, W):
+def test_cosine_fused_and_three_launch_paths_agree(gpu_lib, kvc_option, W):
     K, _, _ = synth.manifold_global(4, 1, 8, 12288 + 100, planted=8, seed=5, device=DEV)
-    monkeypatch.setenv("KVC_SCORE_UNFUSED", "0")
+    kvc_option("score_path", 1)
     f = gpu_lib.kvc_score_centroid(K, W=W, metric="cosine").clone()
-    monkeypatch.setenv("KVC_SCORE_UNFUSED", "1")
+    kvc_option("score_path", 2)
     u = gpu_lib.kvc_score_centroid(K, W=W, metric="cosine")
     torch.cuda.synchronize()
     for x in (f, u):

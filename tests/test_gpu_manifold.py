@@ -26,11 +26,11 @@ def _scores_vs_oracle(K, gpu_scores, W=None):
 
 
 # path "0": the cooperative single-read kernel, "1": the three-launch path (small
-# caches take the latter by default)
+# caches take the latter by default); chosen with the score_path option
 @pytest.mark.parametrize("path", ["0", "1"])
 @pytest.mark.parametrize("G,S", [(1, 1), (3, 257), (2, 1000), (4, 4096), (1, 16384 + 77)])
-def test_score_l2_small(gpu_lib, monkeypatch, G, S, path):
-    monkeypatch.setenv("KVC_SCORE_UNFUSED", path)
+def test_score_l2_small(gpu_lib, kvc_option, G, S, path):
+    kvc_option("score_path", 1 + int(path))
     K, _, _ = synth.manifold_global(1, 1, G, S, planted=min(4, S), seed=S, device=DEV)
     mu_gpu = torch.empty((G, 128), dtype=torch.float32, device=DEV)
     s = gpu_lib.kvc_score_l2(K, centroid=mu_gpu)
@@ -42,8 +42,8 @@ def test_score_l2_small(gpu_lib, monkeypatch, G, S, path):
 @pytest.mark.parametrize("S,W", [(1000, 1), (1000, 1000), (1000, 5000), (1000, 300), (4096 * 3 + 5, 4096),
                                  (8192, 512)])
 @pytest.mark.parametrize("path", ["0", "1"])
-def test_score_l2_windowed_small(gpu_lib, monkeypatch, S, W, path):
-    monkeypatch.setenv("KVC_SCORE_UNFUSED", path)
+def test_score_l2_windowed_small(gpu_lib, kvc_option, S, W, path):
+    kvc_option("score_path", 1 + int(path))
     K, _ = synth.manifold_drifting(1, 1, 2, S, segment=max(1, S // 3), seed=W, device=DEV)
     nwin = -(-S // W)
     mu_gpu = torch.empty((2, nwin, 128), dtype=torch.float32, device=DEV)
@@ -85,12 +85,12 @@ def test_topk_strided_and_gather_bit_exact(gpu_lib):
 
 
 @pytest.mark.parametrize("separate", [False, True])
-def test_gather_paths_bit_exact(gpu_lib, monkeypatch, separate):
-    # 300 slices (more than one per compute unit, so KVC_GATHER_SEPARATE=0 has the selecting
-    # workgroup copy the rows itself; 1 selects the wide gather, the default), ragged S,
+def test_gather_paths_bit_exact(gpu_lib, kvc_option, separate):
+    # 300 slices (more than one per compute unit, so gather_path 1 has the selecting
+    # workgroup copy the rows itself; 0 selects the wide gather, the default), ragged S,
     # strided cache, k from 1 to S including the 8192-row boundary of the in-workgroup copy
     G, S, stride = 300, 8197, 8200
-    monkeypatch.setenv("KVC_GATHER_SEPARATE", "1" if separate else "0")
+    kvc_option("gather_path", 0 if separate else 1)
     K = torch.randint(-32768, 32767, (G, stride, 128), dtype=torch.int16, device=DEV).view(torch.bfloat16)
     V = torch.randint(-32768, 32767, (G, stride, 128), dtype=torch.int16, device=DEV).view(torch.bfloat16)
     s = synth.random_scores(G, stride, seed=11, kind="ties", device="cpu")
@@ -171,13 +171,13 @@ def test_determinism(gpu_lib):
 
 
 @pytest.mark.parametrize("W", [None, 4096, 1000])
-def test_fused_and_three_launch_paths_agree(gpu_lib, monkeypatch, W):
+def test_fused_and_three_launch_paths_agree(gpu_lib, kvc_option, W):
     # the cooperative single-read path and the three-launch path compute the same scores
     K, _, _ = synth.manifold_global(4, 1, 8, 12288 + 100, planted=8, seed=3, device=DEV)
-    monkeypatch.setenv("KVC_SCORE_UNFUSED", "0")
+    kvc_option("score_path", 1)
     f = gpu_lib.kvc_score_l2(K) if W is None else gpu_lib.kvc_score_l2_windowed(K, W)
     f = f.clone()
-    monkeypatch.setenv("KVC_SCORE_UNFUSED", "1")
+    kvc_option("score_path", 2)
     u = gpu_lib.kvc_score_l2(K) if W is None else gpu_lib.kvc_score_l2_windowed(K, W)
     torch.cuda.synchronize()
     ora, _ = oracle.score_l2(synth.bf16_bits(K)) if W is None else oracle.score_l2_windowed(synth.bf16_bits(K), W)
@@ -219,24 +219,40 @@ def test_binding_workspace_per_stream(gpu_lib):
 
 
 @pytest.mark.parametrize("metric", ["l2", "cosine"])
-def test_expired_centroid_wait_gives_nan_not_wrong_scores(gpu_lib, monkeypatch, metric):
+def test_expired_centroid_wait_gives_nan_not_wrong_scores(gpu_lib, kvc_option, metric):
     # the single-read kernel's centroid waits are bounded; a spin limit of 0 set from the
     # host makes nearly every wait expire at its first poll.  Those tiles must come out NaN
     # (whole 256-token tiles), every other score exactly as in a normal run, the kernel must
     # end normally, and a normal call afterwards must be unaffected
     K, _, _ = synth.manifold_global(4, 1, 8, 16384, planted=8, seed=5, device=DEV)
-    monkeypatch.setenv("KVC_SCORE_UNFUSED", "0")
+    kvc_option("score_path", 1)
 
     def score():
         return gpu_lib.kvc_score_centroid(K, W=None, metric=metric)
 
     ref = score().clone()
-    monkeypatch.setenv("KVC_SCORE_SPIN_LIMIT", "0")
+    gpu_lib.kvc_workspace_status()  # a normal call reports nothing
+    kvc_option("score_spin_limit", 0)
     bad = score().clone()
-    monkeypatch.delenv("KVC_SCORE_SPIN_LIMIT")
+    # the failure is reported by the status query on the call's workspace
+    with pytest.raises(gpu_lib.KvcError) as err:
+        gpu_lib.kvc_workspace_status()
+    assert err.value.status == gpu_lib.ERR_WAIT_EXPIRED
+    # NaN scores rank below every number: with k no larger than the count of finite
+    # scores in every slice, no NaN token is kept, and the kept set is the top-k of the
+    # finite scores
+    nan = torch.isnan(bad)
+    k = int((~nan).sum(1).min())
+    if k > 0:
+        idx, _, _ = gpu_lib.kvc_topk_compact(bad, k)
+        kept_nan = torch.gather(nan, 1, idx.long())
+        assert not kept_nan.any()
+        fin = torch.where(nan, torch.full_like(bad, -1.0), bad).cpu().numpy()
+        np.testing.assert_array_equal(idx.cpu().numpy(), oracle.topk(fin, k))
+    kvc_option("score_spin_limit", -1)
     again = score()
     torch.cuda.synchronize()
-    nan = torch.isnan(bad)
+    gpu_lib.kvc_workspace_status()  # cleared by the next call
     assert nan.any()
     assert torch.equal(bad[~nan], ref[~nan])
     tiles = nan.view(-1, 256)

@@ -31,10 +31,10 @@ def _check_packed(idx, Ko, Vo, ks, s_host, Kb, Vb, S=None):
 
 
 @pytest.mark.parametrize("separate", [False, True])
-def test_ragged_layer_budgets_bit_exact(gpu_lib, monkeypatch, separate):
+def test_ragged_layer_budgets_bit_exact(gpu_lib, kvc_option, separate):
     # 30 layers x 10 slices, S = 5000 with a ragged stride; budgets from a sensitivity
     # profile (some layers pinned at S, none empty) and ties in the scores
-    monkeypatch.setenv("KVC_GATHER_SEPARATE", "1" if separate else "0")
+    kvc_option("gather_path", 0 if separate else 1)
     L, per, S, stride = 30, 10, 5000, 5003
     G = L * per
     rng = np.random.default_rng(21)
@@ -100,3 +100,37 @@ def test_ripplekv_eviction_llama_shape(gpu_lib):
 
     with ThreadPoolExecutor(max_workers=8) as ex:
         list(ex.map(check, range(L * H)))
+
+
+def test_ragged_device_budgets_checked_on_device(gpu_lib):
+    # budgets handed over as a device array: a budget above k_max, a negative one, and one
+    # whose rows would end past the packed capacity k_total keep nothing (reported by the
+    # status query), nothing is written outside [0, k_total), and every other slice is
+    # exactly the oracle's selection at its offset
+    G, S = 5, 3000
+    s = synth.random_scores(G, S, seed=26, device="cpu")
+    K = torch.randint(-32768, 32767, (G, S, 128), dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    ks = np.array([100, 2500, -3, 700, 400], dtype=np.int64)  # 2500 > k_max; -3 < 0
+    k_max, k_total = 1000, 100 + 700 + 300  # slice 4's 400 rows do not fit after slice 3's
+    pad = 64
+    idx = torch.full((k_total + pad,), -7, dtype=torch.int32, device=DEV)
+    Ko = torch.full((k_total + pad, 128), 0x1234, dtype=torch.int16, device=DEV).view(torch.bfloat16)
+    kd = torch.from_numpy(ks).to(DEV)
+    gpu_lib.kvc_topk_compact_ragged(s.to(DEV), kd, K, None, idx_out=idx[:k_total], K_out=Ko[:k_total],
+                                    k_max=k_max, k_total=k_total)
+    with pytest.raises(gpu_lib.KvcError) as err:
+        gpu_lib.kvc_workspace_status()
+    assert err.value.status == gpu_lib.ERR_INVALID_ARGUMENT
+    ih = idx.cpu().numpy()
+    kept = [(0, 100, 0), (3, 700, 100)]  # (slice, budget, offset) of the slices that fit
+    for g, k, off in kept:
+        np.testing.assert_array_equal(ih[off:off + k], oracle.topk(s[g:g + 1].numpy(), k)[0])
+        np.testing.assert_array_equal(synth.bf16_bits(Ko[off:off + k]),
+                                      synth.bf16_bits(K)[g][ih[off:off + k].astype(np.int64)])
+    assert np.all(ih[800:] == -7)  # rows of the slice that did not fit and the guard stay untouched
+    assert torch.all(Ko[800:].view(torch.int16) == 0x1234)
+    # valid device budgets: the status query reports nothing
+    kd2 = torch.from_numpy(np.array([100, 200, 0, 300, 400], dtype=np.int64)).to(DEV)
+    a, _, _ = gpu_lib.kvc_topk_compact_ragged(s.to(DEV), kd2, k_max=400, k_total=1000)
+    gpu_lib.kvc_workspace_status()
+    np.testing.assert_array_equal(a.cpu().numpy(), oracle.topk_ragged(s.numpy(), [100, 200, 0, 300, 400]))

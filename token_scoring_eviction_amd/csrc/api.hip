@@ -11,7 +11,43 @@ size_t reconstruct_workspace_bytes(const kvc_dims *d);
 size_t risk_bytes(int64_t G, int64_t S, int64_t c);
 }  // namespace kvc
 
+namespace kvc {
+Options &options() {
+    static Options opts;
+    return opts;
+}
+}  // namespace kvc
+
 extern "C" int kvc_abi_version(void) { return KVC_ABI_VERSION; }
+
+extern "C" kvc_status kvc_set_option(kvc_option opt, int64_t value) {
+    kvc::Options &o = kvc::options();
+    switch (opt) {
+        case KVC_OPTION_SCORE_PATH:
+            if (value < 0 || value > 2) return KVC_ERR_INVALID_ARGUMENT;
+            o.score_path.store(value, std::memory_order_relaxed);
+            return KVC_OK;
+        case KVC_OPTION_SCORE_SPIN_LIMIT:
+            if (value < -1 || value > static_cast<int64_t>(UINT32_MAX)) return KVC_ERR_INVALID_ARGUMENT;
+            o.spin_limit.store(value, std::memory_order_relaxed);
+            return KVC_OK;
+        case KVC_OPTION_GATHER_PATH:
+            if (value < 0 || value > 1) return KVC_ERR_INVALID_ARGUMENT;
+            o.gather_path.store(value, std::memory_order_relaxed);
+            return KVC_OK;
+    }
+    return KVC_ERR_INVALID_ARGUMENT;
+}
+
+extern "C" kvc_status kvc_workspace_status(const void *ws, hipStream_t stream) {
+    if (!ws || !kvc::aligned(ws, kvc::kWsAlign)) return KVC_ERR_INVALID_ARGUMENT;
+    if (hipStreamSynchronize(stream) != hipSuccess) return KVC_ERR_HIP;
+    uint32_t word = 0;
+    if (hipMemcpy(&word, ws, sizeof(word), hipMemcpyDeviceToHost) != hipSuccess) return KVC_ERR_HIP;
+    if (word & kvc::kStatusWaitExpired) return KVC_ERR_WAIT_EXPIRED;
+    if (word & kvc::kStatusBadBudget) return KVC_ERR_INVALID_ARGUMENT;
+    return KVC_OK;
+}
 
 extern "C" const char *kvc_status_str(kvc_status s) {
     switch (s) {
@@ -20,6 +56,7 @@ extern "C" const char *kvc_status_str(kvc_status s) {
         case KVC_ERR_UNSUPPORTED: return "unsupported shape or parameter";
         case KVC_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
         case KVC_ERR_HIP: return "HIP runtime error";
+        case KVC_ERR_WAIT_EXPIRED: return "an in-kernel wait expired (affected scores are NaN)";
     }
     return "unknown status";
 }

@@ -41,6 +41,30 @@ struct WsSizer {
     size_t bytes() const { return off; }
 };
 
+// Workspaces that report failures found by the kernels themselves (expired
+// in-kernel waits, invalid device-side budgets) start with this header; its first
+// word holds kStatus* bits, cleared by each call before its kernels run and read
+// by kvc_workspace_status.
+constexpr size_t kStatusBytes = 256;
+constexpr uint32_t kStatusWaitExpired = 1u;  // a bounded centroid wait gave up
+constexpr uint32_t kStatusBadBudget = 2u;    // a per-slice budget outside its bounds
+
+// Process-wide options set by kvc_set_option (tests and measurements choose a
+// kernel path with them; the defaults select the production paths).
+struct Options {
+    std::atomic<int64_t> score_path{0};   // 0 automatic, 1 single-read kernel, 2 three launches
+    std::atomic<int64_t> spin_limit{-1};  // polls of a centroid wait; -1: the built-in limit
+    std::atomic<int64_t> gather_path{0};  // 0 wide gather launch, 1 in-workgroup copy
+};
+Options &options();
+
+// Centroid scoring (kvc_score_centroid) with the caller's workspace of ws_bytes; and
+// the workspace it needs (0 for invalid shapes).
+kvc_status score_centroid_impl(const uint16_t *K, int64_t G, int64_t S, int32_t D, int64_t W, int metric,
+                               float *scores, float *centroids, void *ws, size_t ws_bytes,
+                               hipStream_t stream);
+size_t score_workspace_bytes(int64_t G, int64_t S, int64_t W);
+
 inline kvc_status launch_status() {
     return hipGetLastError() == hipSuccess ? KVC_OK : KVC_ERR_HIP;
 }
@@ -117,8 +141,12 @@ __device__ __forceinline__ void st_stream(float4 *p, const float4 &v) {
 
 // Order-preserving map of an fp32 value to an unsigned key: a > b <=> key(a) > key(b).
 // -0.0 is folded onto +0.0 so that the two compare equal, as in IEEE arithmetic.
+// A NaN (inputs are finite, but a scoring wait that expired leaves NaN scores) maps
+// to 0, below every other key (-inf maps to 0x007fffff), so it is never kept ahead
+// of a number.
 __device__ __forceinline__ uint32_t order_key(float f) {
     uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u) return 0u;
     if (u == 0x80000000u) u = 0u;
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }

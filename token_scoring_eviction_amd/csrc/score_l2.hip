@@ -30,8 +30,6 @@
 //      (deterministic, no float atomics) and divided by the window's length;
 //   3. l2_distance: 16 lanes per key row, each lane 8 channels, a 16-lane
 //      butterfly for the squared norm, fp32 sqrt.
-#include <stdlib.h>
-
 #include "kvc_internal.h"
 
 namespace kvc {
@@ -91,8 +89,10 @@ __global__ __launch_bounds__(kThreads) void centroid_partial(const uint16_t *__r
 
 __global__ __launch_bounds__(kHeadDim) void centroid_final(const float *__restrict__ partial,
                                                            WinGeom geo, float *__restrict__ mu,
-                                                           float *__restrict__ mu_user) {
+                                                           float *__restrict__ mu_user,
+                                                           uint32_t *__restrict__ status) {
     const int64_t gw = blockIdx.x;  // (slice, window)
+    if (gw == 0 && threadIdx.x == 0) *status = 0u;  // this path has no wait that can expire
     const int64_t w = gw % geo.nwin;
     const int64_t w0 = w * geo.W;
     const int64_t len = min(w0 + geo.W, geo.S) - w0;
@@ -414,7 +414,7 @@ __global__ __launch_bounds__(kFuseThreads, KVC_FUSE_MINBLOCKS) void l2_fused(con
             }
             if (__syncthreads_and(ready)) return true;
             if (++spins > geo.spin_limit) {
-                if (tid == 0) atomicOr(status, 1u);
+                if (tid == 0) atomicOr(status, kStatusWaitExpired);
                 return false;
             }
             // back-off: a team polls the same few lines; hammering them costs
@@ -530,11 +530,14 @@ FuseGeom make_fuse_geom(int64_t G, int64_t S, int64_t W, int metric = kMetricL2)
     return f;
 }
 
+// Status header, tagged centroids and counters first (one contiguous range that a
+// single launch clears), then the tile partials.
 template <class Ws>
 void fused_ws_layout(Ws &ws, const FuseGeom &f) {
-    ws.template take<float>(static_cast<size_t>(f.tiles) * kHeadDim);      // tile partials
+    ws.template take<uint32_t>(kStatusBytes / 4);                          // status header
     ws.template take<uint64_t>(static_cast<size_t>(f.teams) * kHeadDim);   // tagged centroids
-    ws.template take<uint32_t>(static_cast<size_t>(f.teams + 1));          // counters, status
+    ws.template take<uint32_t>(static_cast<size_t>(f.teams));              // arrival counters
+    ws.template take<float>(static_cast<size_t>(f.tiles) * kHeadDim);      // tile partials
 }
 
 // Co-resident workgroups of a fused-kernel instance on the current device (0 if unknown).
@@ -561,6 +564,7 @@ WinGeom make_geom(int64_t G, int64_t S, int64_t W, int metric = kMetricL2) {
 
 template <class Ws>
 void score_ws_layout(Ws &ws, const WinGeom &geo) {
+    ws.template take<uint32_t>(kStatusBytes / 4);  // status header
     ws.template take<float>(static_cast<size_t>(geo.G * geo.nwin * geo.nchunk) * kHeadDim);
     ws.template take<float>(static_cast<size_t>(geo.G * geo.nwin) * kHeadDim);
 }
@@ -578,13 +582,13 @@ size_t score_bytes(int64_t G, int64_t S, int64_t W) {
 // even, 268 MB 113 vs 98 us, 1 GB 426 vs 258 us (three-launch vs single-read).
 constexpr int64_t kSmallCacheBytes = 160ll << 20;
 
-// KVC_SCORE_UNFUSED in the environment overrides the choice: 1 selects the
-// three-launch path, 0 the single-read kernel (read at every call, so a process
-// can compare both paths).  Returns true for the three-launch path.
+// The option KVC_OPTION_SCORE_PATH overrides the choice (1: the single-read kernel,
+// 2: the three-launch path), so that tests and measurements can compare both.
+// Returns true for the three-launch path.
 bool take_unfused(int64_t G, int64_t S) {
-    const char *e = getenv("KVC_SCORE_UNFUSED");
-    if (e && e[0] == '1') return true;
-    if (e && e[0] == '0') return false;
+    const int64_t path = options().score_path.load(std::memory_order_relaxed);
+    if (path == 1) return false;
+    if (path == 2) return true;
     return G * S * kHeadDim * 2 < kSmallCacheBytes;
 }
 
@@ -616,23 +620,22 @@ kvc_status score_windowed_impl(const uint16_t *K, int64_t G, int64_t S, int32_t 
     const int64_t capacity = cap1 - 1;
     if (capacity >= f.members && f.tiles <= INT32_MAX && !take_unfused(G, S)) {
         WsCursor cur(ws);
-        float *partial = cur.take<float>(static_cast<size_t>(f.tiles) * kHeadDim);
+        uint32_t *status = cur.take<uint32_t>(kStatusBytes / 4);
         uint64_t *mu_pub = cur.take<uint64_t>(static_cast<size_t>(f.teams) * kHeadDim);
-        uint32_t *words = cur.take<uint32_t>(static_cast<size_t>(f.teams + 1));
-        uint32_t *counters = words, *status = words + f.teams;
-        // clear the centroid tags, the counters and the status word in one launch
+        uint32_t *counters = cur.take<uint32_t>(static_cast<size_t>(f.teams));
+        float *partial = cur.take<float>(static_cast<size_t>(f.tiles) * kHeadDim);
+        // clear the status word, the centroid tags and the counters in one launch
         // (they are adjacent in the workspace; a kernel, not a memset, so the
         // sequence can be captured in a graph)
-        uint32_t *clear_from = reinterpret_cast<uint32_t *>(mu_pub);
-        const int64_t n_clear = (words + f.teams + 1) - clear_from;
+        const int64_t n_clear = (counters + f.teams) - status;
         const int64_t zb = (n_clear + kFuseThreads - 1) / kFuseThreads;
         hipLaunchKernelGGL(zero_words, dim3(static_cast<unsigned>(zb < 1024 ? zb : 1024)), dim3(kFuseThreads), 0,
-                           stream, clear_from, n_clear);
+                           stream, status, n_clear);
         FuseGeom fa = f;
-        // KVC_SCORE_SPIN_LIMIT in the environment shortens the bounded waits (read at
-        // every call), so that tests can force the expired-wait path from the host
-        const char *lim = getenv("KVC_SCORE_SPIN_LIMIT");
-        fa.spin_limit = lim ? static_cast<uint32_t>(strtoul(lim, nullptr, 10)) : kSpinLimit;
+        // KVC_OPTION_SCORE_SPIN_LIMIT shortens the bounded waits, so that a test can
+        // force the expired-wait path from the host
+        const int64_t lim = options().spin_limit.load(std::memory_order_relaxed);
+        fa.spin_limit = lim >= 0 ? static_cast<uint32_t>(lim) : kSpinLimit;
         float *mu_user = centroids;
         int64_t grid = capacity / f.members * f.members;
         if (grid > f.tiles) grid = f.tiles;
@@ -648,6 +651,7 @@ kvc_status score_windowed_impl(const uint16_t *K, int64_t G, int64_t S, int32_t 
 
     const WinGeom geo = make_geom(G, S, W, metric);
     WsCursor cur(ws);
+    uint32_t *status = cur.take<uint32_t>(kStatusBytes / 4);
     float *partial = cur.take<float>(static_cast<size_t>(geo.G * geo.nwin * geo.nchunk) * kHeadDim);
     float *mu = cur.take<float>(static_cast<size_t>(geo.G * geo.nwin) * kHeadDim);
 
@@ -656,7 +660,7 @@ kvc_status score_windowed_impl(const uint16_t *K, int64_t G, int64_t S, int32_t 
     hipLaunchKernelGGL(centroid_partial, dim3(static_cast<unsigned>(nitems)), dim3(kThreads), 0,
                        stream, K, geo, partial);
     hipLaunchKernelGGL(centroid_final, dim3(static_cast<unsigned>(geo.G * geo.nwin)),
-                       dim3(kHeadDim), 0, stream, partial, geo, mu, centroids);
+                       dim3(kHeadDim), 0, stream, partial, geo, mu, centroids, status);
     const int64_t nblk = (geo.G * geo.S + (kThreads / 16) - 1) / (kThreads / 16);
     if (nblk > INT32_MAX) return KVC_ERR_UNSUPPORTED;
     if (metric == kMetricCosine)
@@ -673,6 +677,12 @@ kvc_status score_windowed_impl(const uint16_t *K, int64_t G, int64_t S, int32_t 
 size_t score_workspace_bytes(int64_t G, int64_t S, int64_t W) {
     if (G < 0 || S < 1 || W < 1) return 0;
     return score_bytes(G, S, W);
+}
+
+kvc_status score_centroid_impl(const uint16_t *K, int64_t G, int64_t S, int32_t D, int64_t W, int metric,
+                               float *scores, float *centroids, void *ws, size_t ws_bytes,
+                               hipStream_t stream) {
+    return score_windowed_impl(K, G, S, D, W, metric, scores, centroids, ws, ws_bytes, stream);
 }
 
 }  // namespace kvc

@@ -18,10 +18,6 @@
 //     scan gives every kept key its output slot, equal keys taken lowest
 //     index first until `need` are taken.
 // gather_rows: 16 lanes per 256-byte row, 16-byte loads and stores.
-#include <stdlib.h>
-
-#include <vector>
-
 #include "kvc_internal.h"
 
 namespace kvc {
@@ -86,7 +82,7 @@ __global__ __launch_bounds__(kSelThreads) void select_compact(const float *__res
     const int64_t g = blockIdx.x;
     const int64_t k = kg ? kg[g] : k_all;
     const int64_t base = koff ? koff[g] : g * k_all;
-    if (k <= 0 || k > S) return;  // the host validated every budget; uniform per block
+    if (k <= 0 || k > S) return;  // budgets were validated (host or device); uniform per block
     const float *s = scores + g * s_stride;
     int32_t *out = idx_out + base;
 
@@ -366,11 +362,62 @@ __global__ __launch_bounds__(kGatherThreads) void gather_rows(
 // The kept rows are copied by the separate wide launch: with one row per thread and
 // many small workgroups it moves them faster than the selecting workgroups can
 // (256 x 16384, keep 8192: 0.385 against 0.419 ms for select + copy; 1024 x 32768,
-// keep 1639: 0.467 against 0.484 ms).  KVC_GATHER_SEPARATE=0 in the environment
-// selects the in-workgroup copy instead (read at every call).
-bool fused_gather() {
-    const char *e = getenv("KVC_GATHER_SEPARATE");
-    return e && e[0] == '0';
+// keep 1639: 0.467 against 0.484 ms).  The option KVC_OPTION_GATHER_PATH = 1 selects
+// the in-workgroup copy instead.
+bool fused_gather() { return options().gather_path.load(std::memory_order_relaxed) == 1; }
+
+// Per-slice budgets of kvc_topk_compact_ragged, checked and packed on the device:
+// one workgroup reads the caller's budgets k[g], keeps a budget only if it lies in
+// [0, k_max] and its rows fit before k_total (else the slice keeps nothing and the
+// status word says so), and writes each slice's effective budget and output offset
+// (an exclusive scan in slice order) to the workspace.
+constexpr int kScanThreads = 1024;
+__global__ __launch_bounds__(kScanThreads) void ragged_offsets(const int64_t *__restrict__ k, int64_t G,
+                                                               int64_t k_max, int64_t k_total,
+                                                               uint32_t *__restrict__ status,
+                                                               int64_t *__restrict__ keff,
+                                                               int64_t *__restrict__ koff) {
+    __shared__ int64_t wsum[kScanThreads / 64];
+    __shared__ uint32_t bad;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    if (threadIdx.x == 0) bad = 0u;
+    __syncthreads();
+    int64_t carry = 0;  // rows packed by the slices before this chunk (uniform)
+    for (int64_t g0 = 0; g0 < G; g0 += kScanThreads) {
+        const int64_t g = g0 + threadIdx.x;
+        int64_t v = g < G ? k[g] : 0;
+        if (v < 0 || v > k_max) {
+            bad = 1u;
+            v = 0;
+        }
+        // inclusive scan of the chunk: within each wave, then across the waves
+        int64_t x = v;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const int64_t y = __shfl_up(x, d, 64);
+            if (lane >= d) x += y;
+        }
+        if (lane == 63) wsum[wave] = x;
+        __syncthreads();
+        int64_t before = 0, chunk = 0;
+        for (int w = 0; w < kScanThreads / 64; ++w) {
+            if (w < wave) before += wsum[w];
+            chunk += wsum[w];
+        }
+        int64_t off = carry + before + x - v;
+        if (off + v > k_total) {  // outputs sized for fewer rows: this slice keeps none
+            bad = 1u;
+            v = 0;
+        }
+        if (g < G) {
+            keff[g] = v;
+            koff[g] = off < k_total ? off : k_total;
+        }
+        carry += chunk;
+        __syncthreads();  // wsum is rewritten by the next chunk
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) *status = bad ? kStatusBadBudget : 0u;
 }
 
 // select_compact for a slice length S: the register-held instance with the fewest
@@ -395,9 +442,20 @@ void launch_select(int64_t G, int64_t S, hipStream_t stream, const float *scores
 
 size_t topk_workspace_bytes(int64_t, int64_t, int64_t) { return 0; }
 
-// Per-slice budgets and output offsets of kvc_topk_compact_ragged.
+// Status header, then the per-slice effective budgets and output offsets of
+// kvc_topk_compact_ragged.
+template <class Ws>
+void ragged_ws_layout(Ws &ws, int64_t G) {
+    ws.template take<uint32_t>(kStatusBytes / 4);
+    ws.template take<int64_t>(static_cast<size_t>(G));
+    ws.template take<int64_t>(static_cast<size_t>(G));
+}
+
 size_t topk_ragged_workspace_bytes(int64_t G) {
-    return G > 0 ? align_up(static_cast<size_t>(2 * G) * sizeof(int64_t), kWsAlign) : 0;
+    if (G <= 0) return 0;
+    WsSizer z;
+    ragged_ws_layout(z, G);
+    return z.bytes();
 }
 
 }  // namespace kvc
@@ -438,52 +496,41 @@ extern "C" kvc_status kvc_topk_compact(const float *scores, int64_t G, int64_t S
 }
 
 extern "C" kvc_status kvc_topk_compact_ragged(const float *scores, int64_t G, int64_t S,
-                                              int64_t s_stride, const int64_t *k, const uint16_t *K,
-                                              const uint16_t *V, int32_t D, int32_t *idx_out,
-                                              uint16_t *K_out, uint16_t *V_out, void *ws,
-                                              size_t ws_bytes, hipStream_t stream) {
+                                              int64_t s_stride, const int64_t *k, int64_t k_max,
+                                              int64_t k_total, const uint16_t *K, const uint16_t *V,
+                                              int32_t D, int32_t *idx_out, uint16_t *K_out,
+                                              uint16_t *V_out, void *ws, size_t ws_bytes,
+                                              hipStream_t stream) {
     using namespace kvc;
-    if (G < 0 || S < 0 || s_stride < S) return KVC_ERR_INVALID_ARGUMENT;
+    if (G < 0 || S < 0 || s_stride < S || k_max < 0 || k_max > S || k_total < 0)
+        return KVC_ERR_INVALID_ARGUMENT;
     if ((K == nullptr) != (K_out == nullptr) || (V == nullptr) != (V_out == nullptr))
         return KVC_ERR_INVALID_ARGUMENT;
     if ((K || V) && D != kHeadDim) return D <= 0 ? KVC_ERR_INVALID_ARGUMENT : KVC_ERR_UNSUPPORTED;
     if (S > INT32_MAX || G > INT32_MAX) return KVC_ERR_UNSUPPORTED;
     if (G == 0) return KVC_OK;
-    if (!k) return KVC_ERR_INVALID_ARGUMENT;
-    // budgets (host) -> validated, packed offsets
-    int64_t total = 0, kmax = 0;
-    for (int64_t g = 0; g < G; ++g) {
-        if (k[g] < 0 || k[g] > S) return KVC_ERR_INVALID_ARGUMENT;
-        total += k[g];
-        kmax = k[g] > kmax ? k[g] : kmax;
-    }
-    if (total == 0) return KVC_OK;
-    if (!scores || !idx_out || !aligned(scores, 4) || !aligned(idx_out, 4)) return KVC_ERR_INVALID_ARGUMENT;
+    if (!k || !aligned(k, 8) || !ws || !aligned(ws, kWsAlign)) return KVC_ERR_INVALID_ARGUMENT;
+    if (ws_bytes < topk_ragged_workspace_bytes(G)) return KVC_ERR_WORKSPACE_TOO_SMALL;
+    if (k_total > 0 && (!scores || !idx_out || !aligned(scores, 4) || !aligned(idx_out, 4)))
+        return KVC_ERR_INVALID_ARGUMENT;
     if ((K && (!aligned(K, 16) || !aligned(K_out, 16))) || (V && (!aligned(V, 16) || !aligned(V_out, 16))))
         return KVC_ERR_INVALID_ARGUMENT;
-    if (!ws || !aligned(ws, kWsAlign)) return KVC_ERR_INVALID_ARGUMENT;
-    if (ws_bytes < topk_ragged_workspace_bytes(G)) return KVC_ERR_WORKSPACE_TOO_SMALL;
-    std::vector<int64_t> host(static_cast<size_t>(2 * G));
-    for (int64_t g = 0, off = 0; g < G; ++g) {
-        host[g] = k[g];
-        host[G + g] = off;
-        off += k[g];
-    }
-    int64_t *kg = static_cast<int64_t *>(ws);
-    int64_t *koff = kg + G;
-    // the copy is ordered before the kernels on the stream; the host vector is read
-    // before hipMemcpyAsync returns (pageable source)
-    if (hipMemcpyAsync(kg, host.data(), host.size() * sizeof(int64_t), hipMemcpyHostToDevice, stream) !=
-        hipSuccess)
-        return KVC_ERR_HIP;
-    if ((K || V) && kmax <= 8192 && G >= device_cu_count() && fused_gather()) {
+    WsCursor cur(ws);
+    uint32_t *status = cur.take<uint32_t>(kStatusBytes / 4);
+    int64_t *kg = cur.take<int64_t>(static_cast<size_t>(G));
+    int64_t *koff = cur.take<int64_t>(static_cast<size_t>(G));
+    // the budgets are checked and packed by a kernel on the stream (no host copy)
+    hipLaunchKernelGGL(ragged_offsets, dim3(1), dim3(kScanThreads), 0, stream, k, G, k_max, k_total,
+                       status, kg, koff);
+    if (k_max == 0 || k_total == 0) return launch_status();
+    if ((K || V) && k_max <= 8192 && G >= device_cu_count() && fused_gather()) {
         launch_select(G, S, stream, scores, s_stride, int64_t{0}, kg, koff, idx_out, K, V, K_out, V_out);
         return launch_status();
     }
     launch_select(G, S, stream, scores, s_stride, int64_t{0}, kg, koff, idx_out, nullptr, nullptr, nullptr,
                   nullptr);
     if (K || V) {
-        const int64_t bps = (kmax + kGatherRows - 1) / kGatherRows;
+        const int64_t bps = (k_max + kGatherRows - 1) / kGatherRows;
         if (G * bps > INT32_MAX) return KVC_ERR_UNSUPPORTED;
         hipLaunchKernelGGL(gather_rows, dim3(static_cast<unsigned>(G * bps)), dim3(kGatherThreads), 0,
                            stream, K, V, S, s_stride, idx_out, int64_t{0}, kg, koff, bps, K_out, V_out);

@@ -15,14 +15,20 @@ import torch
 _PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_PKG, "libkvc.so")
 
-OK, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_WORKSPACE_TOO_SMALL, ERR_HIP = range(5)
+OK, ERR_INVALID_ARGUMENT, ERR_UNSUPPORTED, ERR_WORKSPACE_TOO_SMALL, ERR_HIP, ERR_WAIT_EXPIRED = range(6)
+OPTION_SCORE_PATH, OPTION_SCORE_SPIN_LIMIT, OPTION_GATHER_PATH = range(3)
+OPTIONS = {"score_path": OPTION_SCORE_PATH, "score_spin_limit": OPTION_SCORE_SPIN_LIMIT,
+           "gather_path": OPTION_GATHER_PATH}
+OPTION_DEFAULTS = {"score_path": 0, "score_spin_limit": -1, "gather_path": 0}
 OP_SCORE_L2, OP_SCORE_L2_WINDOWED, OP_TOPK_COMPACT, OP_LOWRANK_COMPRESS, OP_OJA_UPDATE, \
     OP_RECONSTRUCT, OP_SCORE_CENTROID, OP_TOPK_RAGGED, OP_REFINE_RISK = range(9)
 METRIC_L2, METRIC_COSINE = 0, 1
 METRICS = {"l2": METRIC_L2, "cosine": METRIC_COSINE}
 
-EXPORTED = ("kvc_abi_version", "kvc_status_str", "kvc_workspace_bytes", "kvc_score_l2",
-            "kvc_score_l2_windowed", "kvc_score_centroid", "kvc_layer_budgets", "kvc_topk_compact",
+EXPORTED = ("kvc_abi_version", "kvc_status_str", "kvc_set_option", "kvc_workspace_status",
+            "kvc_workspace_bytes", "kvc_score_l2",
+            "kvc_score_l2_windowed", "kvc_score_centroid",
+            "kvc_layer_budgets", "kvc_topk_compact",
             "kvc_topk_compact_ragged", "kvc_cluster_summaries", "kvc_refine_risk", "kvc_lowrank_compress",
             "kvc_lowrank_compress_bf16", "kvc_oja_update", "kvc_reconstruct", "kvc_reconstruct_bf16",
             "kvc_decode_append", "kvc_lowrank_compress_reconstruct",
@@ -57,12 +63,14 @@ def load(path: str = LIB_PATH):
             lib.kvc_abi_version.argtypes, lib.kvc_abi_version.restype = [], ctypes.c_int
             lib.kvc_status_str.argtypes, lib.kvc_status_str.restype = [ctypes.c_int], ctypes.c_char_p
             lib.kvc_workspace_bytes.argtypes, lib.kvc_workspace_bytes.restype = [ctypes.c_int, DP, I64, I64], SZ
+            lib.kvc_set_option.argtypes, lib.kvc_set_option.restype = [ctypes.c_int, I64], ctypes.c_int
+            lib.kvc_workspace_status.argtypes, lib.kvc_workspace_status.restype = [P, P], ctypes.c_int
             sigs = {
                 "kvc_score_l2": [P, I64, I64, I32, P, P, P, SZ, P],
                 "kvc_score_l2_windowed": [P, I64, I64, I32, I64, P, P, P, SZ, P],
                 "kvc_score_centroid": [P, I64, I64, I32, I64, I32, P, P, P, SZ, P],
                 "kvc_topk_compact": [P, I64, I64, I64, I64, P, P, I32, P, P, P, P, SZ, P],
-                "kvc_topk_compact_ragged": [P, I64, I64, I64, P, P, P, I32, P, P, P, P, SZ, P],
+                "kvc_topk_compact_ragged": [P, I64, I64, I64, P, I64, I64, P, P, I32, P, P, P, P, SZ, P],
                 "kvc_layer_budgets": [P, I64, ctypes.c_double, ctypes.c_double, I64, I64, P],
                 "kvc_cluster_summaries": [P, P, I64, I64, I32, I64, P, P, P, P, P],
                 "kvc_refine_risk": [P, P, P, I64, I64, I64, I32, P, I32, P, P, SZ, P],
@@ -124,6 +132,24 @@ def workspace(nbytes: int, device=None):
 
 def workspace_bytes(op, dims: Dims, k=0, W=0) -> int:
     return int(load().kvc_workspace_bytes(op, ctypes.byref(dims), k, W))
+
+
+def kvc_set_option(name, value):
+    """Sets a process-wide kvc_option by name ("score_path", "score_spin_limit",
+    "gather_path"); the defaults are OPTION_DEFAULTS."""
+    _check("kvc_set_option", load().kvc_set_option(OPTIONS[name], int(value)))
+
+
+def kvc_workspace_status(device=None):
+    """kvc_workspace_status on the cached workspace of the current stream: waits for
+    the stream, then raises KvcError if the last scoring or ragged-selection call on
+    it recorded a failure in its kernels (an expired centroid wait, a device budget
+    out of bounds)."""
+    dev = torch.device("cuda", torch.cuda.current_device() if device is None else device)
+    buf = _ws.get((dev, torch.cuda.current_stream(dev).cuda_stream))
+    if buf is None:
+        raise ValueError("no workspace has been used on this stream")
+    _check("kvc_workspace_status", load().kvc_workspace_status(ctypes.c_void_p(buf.data_ptr()), _stream()))
 
 
 def _bits(t):
@@ -220,28 +246,41 @@ def kvc_layer_budgets(sensitivity, r, gamma, B, S):
     return k
 
 
-def kvc_topk_compact_ragged(scores, ks, K=None, V=None, S=None, idx_out=None, K_out=None, V_out=None):
-    """scores: fp32 [G, S_stride]; ks: per-slice budgets (int sequence [G]).
-    Returns (idx int32 [sum ks], K_out, V_out bf16 [sum ks, D] or None), packed
-    in slice order."""
+def kvc_topk_compact_ragged(scores, ks, K=None, V=None, S=None, idx_out=None, K_out=None, V_out=None,
+                            k_max=None, k_total=None):
+    """scores: fp32 [G, S_stride]; ks: per-slice budgets, a host sequence [G] (copied
+    to the device here) or an int64 device tensor [G] (then k_max and k_total are
+    needed).  Returns (idx int32 [k_total], K_out, V_out bf16 [k_total, D] or None),
+    packed in slice order; k_total defaults to sum(ks)."""
     import numpy as np
     lib = load()
     G, stride = scores.shape
     S = stride if S is None else S
-    k = np.ascontiguousarray(ks, dtype=np.int64)
-    total = int(k.sum())
-    D = K.shape[2] if K is not None else (V.shape[2] if V is not None else 128)
     dev = scores.device
+    if torch.is_tensor(ks) and ks.is_cuda:
+        kd = ks
+        if k_max is None or k_total is None:
+            raise ValueError("device budgets need k_max and k_total")
+    else:
+        k = np.ascontiguousarray(ks, dtype=np.int64)
+        if k_max is None:
+            k_max = int(k.max()) if k.size else 0
+        if k_total is None:
+            k_total = int(k.sum())
+        # a stream-ordered device copy: the caching allocator reuses its memory only
+        # for work queued after the call's kernels
+        kd = torch.from_numpy(k).to(dev)
+    D = K.shape[2] if K is not None else (V.shape[2] if V is not None else 128)
     if idx_out is None:
-        idx_out = torch.empty(total, dtype=torch.int32, device=dev)
+        idx_out = torch.empty(k_total, dtype=torch.int32, device=dev)
     if K is not None and K_out is None:
-        K_out = torch.empty((total, D), dtype=torch.bfloat16, device=dev)
+        K_out = torch.empty((k_total, D), dtype=torch.bfloat16, device=dev)
     if V is not None and V_out is None:
-        V_out = torch.empty((total, D), dtype=torch.bfloat16, device=dev)
+        V_out = torch.empty((k_total, D), dtype=torch.bfloat16, device=dev)
     nb = workspace_bytes(OP_TOPK_RAGGED, _dims(1, 1, G, 0, S, stride, D, 0, 0))
     ws = workspace(nb, dev.index)
     _check("kvc_topk_compact_ragged",
-           lib.kvc_topk_compact_ragged(_ptr(scores), G, S, stride, k.ctypes.data_as(ctypes.c_void_p),
+           lib.kvc_topk_compact_ragged(_ptr(scores), G, S, stride, _ptr(kd), int(k_max), int(k_total),
                                        _ptr(K), _ptr(V), D, _ptr(idx_out), _ptr(K_out), _ptr(V_out),
                                        _ptr(ws), nb, _stream()))
     return idx_out, K_out, V_out
