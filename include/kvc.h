@@ -176,6 +176,24 @@ kvc_status kvc_score_centroid(const uint16_t *K, int64_t G, int64_t S, int32_t D
                               int32_t metric, float *scores, float *centroids, void *ws,
                               size_t ws_bytes, hipStream_t stream);
 
+/* For callers that cannot allocate device memory (code under stream capture,
+ * tight serving loops, harnesses that forbid allocation): kvc_score_centroid
+ * with no workspace argument.  Its scratch is a device array of
+ * KVC_NOALLOC_SCRATCH_BYTES inside the library, one per device, held until the
+ * process ends; the call allocates nothing.  It accepts the shapes whose
+ * kvc_workspace_bytes(KVC_OP_SCORE_CENTROID, ...) fits that size (e.g. 256
+ * slices of 65536 tokens with 4096-token windows; 2 bytes per token plus a few
+ * KiB per window) and returns KVC_ERR_WORKSPACE_TOO_SMALL for larger ones,
+ * before launching anything.  Results are bit-identical to kvc_score_centroid.
+ * Every call on a device shares that device's scratch, so calls that may overlap
+ * on one device (different streams or threads) race; calls queued in order on
+ * one stream do not.  An expired centroid wait shows only as NaN scores (there
+ * is no workspace to query). */
+#define KVC_NOALLOC_SCRATCH_BYTES (48ull << 20)
+kvc_status kvc_score_centroid_noalloc(const uint16_t *K, int64_t G, int64_t S, int32_t D, int64_t W,
+                                      int32_t metric, float *scores, float *centroids,
+                                      hipStream_t stream);
+
 /* Retention and compaction ([MKV] abstract: the keys farthest from the
  * centroid are retained; [OJA] method details: the top-k error scores are kept
  * at full rank).  For each slice g, selects the k largest scores[g][0..S)

@@ -27,7 +27,7 @@ METRICS = {"l2": METRIC_L2, "cosine": METRIC_COSINE}
 
 EXPORTED = ("kvc_abi_version", "kvc_status_str", "kvc_set_option", "kvc_workspace_status",
             "kvc_workspace_bytes", "kvc_score_l2",
-            "kvc_score_l2_windowed", "kvc_score_centroid",
+            "kvc_score_l2_windowed", "kvc_score_centroid", "kvc_score_centroid_noalloc",
             "kvc_layer_budgets", "kvc_topk_compact",
             "kvc_topk_compact_ragged", "kvc_cluster_summaries", "kvc_refine_risk", "kvc_lowrank_compress",
             "kvc_lowrank_compress_bf16", "kvc_oja_update", "kvc_reconstruct", "kvc_reconstruct_bf16",
@@ -69,6 +69,7 @@ def load(path: str = LIB_PATH):
                 "kvc_score_l2": [P, I64, I64, I32, P, P, P, SZ, P],
                 "kvc_score_l2_windowed": [P, I64, I64, I32, I64, P, P, P, SZ, P],
                 "kvc_score_centroid": [P, I64, I64, I32, I64, I32, P, P, P, SZ, P],
+                "kvc_score_centroid_noalloc": [P, I64, I64, I32, I64, I32, P, P, P],
                 "kvc_topk_compact": [P, I64, I64, I64, I64, P, P, I32, P, P, P, P, SZ, P],
                 "kvc_topk_compact_ragged": [P, I64, I64, I64, P, I64, I64, P, P, I32, P, P, P, P, SZ, P],
                 "kvc_layer_budgets": [P, I64, ctypes.c_double, ctypes.c_double, I64, I64, P],
@@ -205,6 +206,22 @@ def kvc_score_centroid(K, W=None, metric="l2", scores=None, centroids=None):
     _check("kvc_score_centroid",
            lib.kvc_score_centroid(_ptr(_bits(K)), G, S, D, W, m, _ptr(scores), _ptr(centroids),
                                   _ptr(ws), nb, _stream()))
+    return scores
+
+
+def kvc_score_centroid_noalloc(K, W=None, metric="l2", scores=None, centroids=None):
+    """kvc_score_centroid with the library's own scratch instead of a workspace (the
+    call allocates nothing; `scores` may be passed in to keep this side allocation-free
+    too).  K: bf16 [G, S, D] -> scores fp32 [G, S]."""
+    lib = load()
+    G, S, D = K.shape
+    W = S if W is None else W
+    m = METRICS[metric] if isinstance(metric, str) else int(metric)
+    if scores is None:
+        scores = torch.empty((G, S), dtype=torch.float32, device=K.device)
+    _check("kvc_score_centroid_noalloc",
+           lib.kvc_score_centroid_noalloc(_ptr(_bits(K)), G, S, D, W, m, _ptr(scores), _ptr(centroids),
+                                          _stream()))
     return scores
 
 
