@@ -202,9 +202,15 @@ __global__ __launch_bounds__(kThreads) void cosine_distance(const uint16_t *__re
 #ifndef KVC_FUSE_MINBLOCKS
 #define KVC_FUSE_MINBLOCKS 3
 #endif
-constexpr int kFuseThreads = 256;
+#ifndef KVC_FUSE_THREADS
+#define KVC_FUSE_THREADS 256
+#endif
+constexpr int kFuseThreads = KVC_FUSE_THREADS;                // a multiple of 64
+constexpr int kRowGroups = kFuseThreads / 16;                 // 16 lanes per key row
 constexpr int kFuseRows = KVC_FUSE_ROWS;                      // rows per thread (8 or 16)
-constexpr int kFuseTile = (kFuseThreads / 16) * kFuseRows;    // 256 tokens per tile
+constexpr int kFuseTile = kRowGroups * kFuseRows;             // tokens per tile
+constexpr int kMemberGroups = kFuseThreads / 32;              // 32 channel groups of 4 each
+static_assert(kFuseThreads % 64 == 0 && kMemberGroups <= kRowGroups, "fused tile shape");
 constexpr uint32_t kSpinLimit = 1u << 16;  // ~0.1 s of polling: far above any real wait
 
 struct FuseGeom {
@@ -272,7 +278,8 @@ __device__ __forceinline__ float sum16(float a) {
     return a;
 }
 
-__global__ __launch_bounds__(kFuseThreads) void zero_words(uint32_t *p, int64_t n) {
+constexpr int kZeroThreads = 256;
+__global__ __launch_bounds__(kZeroThreads) void zero_words(uint32_t *p, int64_t n) {
     for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
          i += static_cast<int64_t>(gridDim.x) * blockDim.x)
         p[i] = 0u;
@@ -294,8 +301,8 @@ __global__ __launch_bounds__(kFuseThreads, KVC_FUSE_MINBLOCKS) void l2_fused(con
                                                          float *__restrict__ mu_user) {
     const int tid = threadIdx.x;
     const int lane16 = tid & 15;
-    const int rowg = tid >> 4;  // 0..15
-    __shared__ float red[16][kHeadDim + 4];
+    const int rowg = tid >> 4;  // 0 .. kRowGroups-1
+    __shared__ float red[kRowGroups][kHeadDim + 4];
     __shared__ float mu_s[kHeadDim];
     __shared__ uint32_t last_s;
 
@@ -317,7 +324,7 @@ __global__ __launch_bounds__(kFuseThreads, KVC_FUSE_MINBLOCKS) void l2_fused(con
         const uint4 *base = reinterpret_cast<const uint4 *>(K + t.g * geo.S * kHeadDim) + lane16;
 #pragma unroll
         for (int r = 0; r < kFuseRows; ++r) {
-            const int64_t row = t.t0 + 16 * r;
+            const int64_t row = t.t0 + static_cast<int64_t>(kRowGroups) * r;
             // keys are read once (streaming loads)
             v[r] = row < t.w1 ? ld_stream(base + row * (kHeadDim / 8)) : make_uint4(0u, 0u, 0u, 0u);
         }
@@ -339,7 +346,7 @@ __global__ __launch_bounds__(kFuseThreads, KVC_FUSE_MINBLOCKS) void l2_fused(con
         if (tid < kHeadDim) {
             float sum = 0.f;
 #pragma unroll
-            for (int r = 0; r < 16; ++r) sum += red[r][tid];
+            for (int r = 0; r < kRowGroups; ++r) sum += red[r][tid];
             __hip_atomic_store(partial + tile * kHeadDim + tid, sum, __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
         }
@@ -349,34 +356,40 @@ __global__ __launch_bounds__(kFuseThreads, KVC_FUSE_MINBLOCKS) void l2_fused(con
             last_s = atomicAdd(&counters[t.team], 1u) == static_cast<uint32_t>(geo.members - 1);
         __syncthreads();
         if (!last_s) return;
-        // 32 channel groups of 4 x 8 member groups; each thread sums its members
-        // (all loads in flight), then member groups are added in order
+        // 32 channel groups of 4 x kMemberGroups member groups; each thread sums its
+        // members (8 of them in flight at a time, two 64-bit coherent loads per member),
+        // then the member groups are added in order
         {
             const int cg = tid & 31, mg = tid >> 5;
-            const int64_t per = (geo.members + 7) / 8;
+            const int64_t per = (geo.members + kMemberGroups - 1) / kMemberGroups;
             const int64_t m0 = mg * per, m1 = min(geo.members, m0 + per);
-            const float *p = partial + t.team * geo.members * kHeadDim + cg * 4;
+            const uint64_t *p = reinterpret_cast<const uint64_t *>(partial + t.team * geo.members * kHeadDim) +
+                                cg * 2;
             float sx = 0.f, sy = 0.f, sz = 0.f, sw = 0.f;
+            auto add = [&](uint64_t a, uint64_t b) {
+                sx += __uint_as_float(static_cast<uint32_t>(a));
+                sy += __uint_as_float(static_cast<uint32_t>(a >> 32));
+                sz += __uint_as_float(static_cast<uint32_t>(b));
+                sw += __uint_as_float(static_cast<uint32_t>(b >> 32));
+            };
             int64_t m = m0;
             for (; m + 8 <= m1; m += 8) {
-                float x[8][4];
+                uint64_t x[8][2];
 #pragma unroll
                 for (int u = 0; u < 8; ++u)
 #pragma unroll
-                    for (int c = 0; c < 4; ++c)
-                        x[u][c] = __hip_atomic_load(p + (m + u) * kHeadDim + c, __ATOMIC_RELAXED,
+                    for (int c = 0; c < 2; ++c)
+                        x[u][c] = __hip_atomic_load(p + (m + u) * (kHeadDim / 2) + c, __ATOMIC_RELAXED,
                                                     __HIP_MEMORY_SCOPE_AGENT);
 #pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    sx += x[u][0]; sy += x[u][1]; sz += x[u][2]; sw += x[u][3];
-                }
+                for (int u = 0; u < 8; ++u) add(x[u][0], x[u][1]);
             }
             for (; m < m1; ++m) {
-                const float *q = p + m * kHeadDim;
-                sx += __hip_atomic_load(q + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                sy += __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                sz += __hip_atomic_load(q + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                sw += __hip_atomic_load(q + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+                const uint64_t a = __hip_atomic_load(p + m * (kHeadDim / 2), __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
+                const uint64_t b = __hip_atomic_load(p + m * (kHeadDim / 2) + 1, __ATOMIC_RELAXED,
+                                                     __HIP_MEMORY_SCOPE_AGENT);
+                add(a, b);
             }
             red[mg][cg * 4 + 0] = sx;
             red[mg][cg * 4 + 1] = sy;
@@ -388,7 +401,7 @@ __global__ __launch_bounds__(kFuseThreads, KVC_FUSE_MINBLOCKS) void l2_fused(con
         if (tid < kHeadDim) {
             float sum = 0.f;
 #pragma unroll
-            for (int q = 0; q < 8; ++q) sum += red[q][tid];
+            for (int q = 0; q < kMemberGroups; ++q) sum += red[q][tid];
             mu = sum / static_cast<float>(t.w1 - t.w0);
             if (mu_user) mu_user[t.team * kHeadDim + tid] = mu;
         }
@@ -465,7 +478,7 @@ __global__ __launch_bounds__(kFuseThreads, KVC_FUSE_MINBLOCKS) void l2_fused(con
                 e = sum16(e);
                 if (lane16 == r) mine = (kk > 0.f && mm > 0.f) ? 0.5f * e : 1.f;
             }
-            const int64_t row = t.t0 + 16 * lane16;
+            const int64_t row = t.t0 + static_cast<int64_t>(kRowGroups) * lane16;
             if (lane16 < kFuseRows && row < t.w1) scores[t.g * geo.S + row] = ok ? mine : nan;
         } else {
             float d2[kFuseRows];
@@ -483,7 +496,7 @@ __global__ __launch_bounds__(kFuseThreads, KVC_FUSE_MINBLOCKS) void l2_fused(con
             }
             row_transpose_reduce<kFuseRows>(d2, lane16);
             const int r = kFuseRows == 16 ? lane16 : (lane16 >> 1);
-            const int64_t row = t.t0 + 16 * r;
+            const int64_t row = t.t0 + static_cast<int64_t>(kRowGroups) * r;
             if ((kFuseRows == 16 || (lane16 & 1) == 0) && row < t.w1)
                 scores[t.g * geo.S + row] = ok ? sqrtf(d2[0]) : nan;
         }
@@ -628,8 +641,8 @@ kvc_status score_windowed_impl(const uint16_t *K, int64_t G, int64_t S, int32_t 
         // (they are adjacent in the workspace; a kernel, not a memset, so the
         // sequence can be captured in a graph)
         const int64_t n_clear = (counters + f.teams) - status;
-        const int64_t zb = (n_clear + kFuseThreads - 1) / kFuseThreads;
-        hipLaunchKernelGGL(zero_words, dim3(static_cast<unsigned>(zb < 1024 ? zb : 1024)), dim3(kFuseThreads), 0,
+        const int64_t zb = (n_clear + kZeroThreads - 1) / kZeroThreads;
+        hipLaunchKernelGGL(zero_words, dim3(static_cast<unsigned>(zb < 1024 ? zb : 1024)), dim3(kZeroThreads), 0,
                            stream, status, n_clear);
         FuseGeom fa = f;
         // KVC_OPTION_SCORE_SPIN_LIMIT shortens the bounded waits, so that a test can
