@@ -57,8 +57,10 @@ typedef enum kvc_status {
     KVC_ERR_UNSUPPORTED = 2,        /* valid but not built: D != 128, R not in {32,64,96,128}, ... */
     KVC_ERR_WORKSPACE_TOO_SMALL = 3,/* ws_bytes < kvc_workspace_bytes(...) */
     KVC_ERR_HIP = 4,                /* a HIP runtime call or kernel launch failed */
-    KVC_ERR_WAIT_EXPIRED = 5        /* reported by kvc_workspace_status: a bounded in-kernel
+    KVC_ERR_WAIT_EXPIRED = 5,       /* reported by kvc_workspace_status: a bounded in-kernel
                                        wait gave up; the affected scores are NaN */
+    KVC_STATUS_MAX_ENUM = 0x7fffffff /* not a status: makes every int32 value a valid
+                                        kvc_status, so callers may pass any code */
 } kvc_status;
 
 /* Process-wide options for tests and measurements (kvc_set_option).  The
@@ -70,9 +72,10 @@ typedef enum kvc_option {
     KVC_OPTION_SCORE_SPIN_LIMIT = 1, /* polls of a centroid wait before it gives up: -1 the built-in
                                         limit (default), 0 .. 2^32-1 (0: the first poll that finds no
                                         centroid gives up; lets a test force the expired-wait path) */
-    KVC_OPTION_GATHER_PATH = 2       /* kept-row copy: 0 a separate wide gather launch (default),
+    KVC_OPTION_GATHER_PATH = 2,      /* kept-row copy: 0 a separate wide gather launch (default),
                                         1 the selecting workgroup copies its slice's rows when
                                         k <= 8192 and there are at least as many slices as CUs */
+    KVC_OPTION_MAX_ENUM = 0x7fffffff /* not an option: every int32 value is a valid kvc_option */
 } kvc_option;
 
 typedef enum kvc_op {
@@ -84,16 +87,18 @@ typedef enum kvc_op {
     KVC_OP_RECONSTRUCT = 5,
     KVC_OP_SCORE_CENTROID = 6,
     KVC_OP_TOPK_RAGGED = 7,
-    KVC_OP_REFINE_RISK = 8
+    KVC_OP_REFINE_RISK = 8,
+    KVC_OP_MAX_ENUM = 0x7fffffff    /* not an op: every int32 value is a valid kvc_op */
 } kvc_op;
 
 /* Score of a key against its (global or window) centroid mu, for
  * kvc_score_centroid. */
 typedef enum kvc_metric {
     KVC_METRIC_L2 = 0,     /* || k_t - mu ||_2: ManifoldKV ([MKV] abstract) */
-    KVC_METRIC_COSINE = 1  /* 1 - cos(k_t, mu): the cosine-to-centroid baseline the [MKV]
+    KVC_METRIC_COSINE = 1, /* 1 - cos(k_t, mu): the cosine-to-centroid baseline the [MKV]
                               abstract compares against (scale-invariant); taken as 1 where
                               k_t or mu is the zero vector */
+    KVC_METRIC_MAX_ENUM = 0x7fffffff
 } kvc_metric;
 
 /* Shapes of a multi-layer KV cache.

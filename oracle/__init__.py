@@ -37,7 +37,9 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "kvc_oracle.c")
-_LIB = os.path.join(_HERE, "liboracle.so")
+# KVC_ORACLE_LIB names another build of the same source to load instead (the
+# sanitizer test runs the pins against an AddressSanitizer/UBSan build this way)
+_LIB = os.environ.get("KVC_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
 _lock = threading.Lock()
 _lib = None
 
@@ -60,7 +62,8 @@ def _load():
     global _lib
     with _lock:
         if _lib is None:
-            build(force=False)
+            if not os.environ.get("KVC_ORACLE_LIB"):
+                build(force=False)
             lib = ctypes.CDLL(_LIB)
             P = ctypes.c_void_p
             I = ctypes.c_int64

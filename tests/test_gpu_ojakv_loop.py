@@ -106,30 +106,50 @@ def test_loop_small_all_slices(gpu_lib):
             _compare(snaps[j][g], ora, ora["S"])
 
 
-def test_loop_256x131072_sampled(gpu_lib):
+def test_loop_256x131072_every_update(gpu_lib):
     # 32 layers x batch 1 x 8 kv heads (32 query heads), 131072-token prompt pooled by 32 for
     # the prefill update, eta 1e-3, 256 decode steps with an update every 32, all at full
-    # size on the GPU.  Two slices are checked against independent oracle runs (one thread
-    # each) after the prefill and the first two updates; every update of the loop is
-    # checked on all slices at a 4096-token prompt by test_loop_small_all_slices.
-    S0, steps, checked = 131072, 256, 2
+    # size on the GPU.  One slice in each of layers 0, 15 and 31 is compared with an
+    # independent oracle run of the whole loop after the prefill and after every one of
+    # the 8 updates (bases, error scores, anchor sets, K^/V^ on 4096 sampled tokens plus
+    # the anchors).  The three oracle loops run on their own threads; each phase is
+    # compared as soon as the oracle reaches it and its arrays are then dropped.
+    S0, steps, T = 131072, 256, 32
     inp = synth.oja_inputs(32, 1, 8, 32, S0, R=64, Wq=32, S_cap=S0 + steps, device=DEV)
-    sl = [137, 250]
+    sl = [3, 15 * 8 + 7, 31 * 8 + 0]  # (layer 0, kv head 3), (15, 7), (31, 0)
     rng = np.random.default_rng(0)
-    snaps, qdec = _run_gpu_loop(inp, steps, 32, 32, 1e-3, slices=sl,
+    snaps, qdec = _run_gpu_loop(inp, steps, T, 32, 1e-3, slices=sl,
                                 token_sample=lambda S: np.sort(rng.choice(S, 4096, replace=False)))
     assert len(snaps) == 9 and snaps[-1]["S"] == S0 + steps
-    result = {}
-    threads = [threading.Thread(target=lambda g=g: result.__setitem__(
-        g, _oracle_loop(inp, g, 32 * checked, 32, 32, 1e-3, qdec))) for g in sl]
+    checked = {g: [] for g in sl}
+    errors = []
+
+    def prepare(g):
+        def on_update(j, st):
+            try:
+                _compare(snaps[j][g], st, st["S"])
+                checked[g].append(j)
+            except AssertionError as e:  # reported on the main thread
+                errors.append("slice %d, phase %d: %s" % (g, j, e))
+            for key in ("Kt", "Vt", "Khat", "Vhat"):
+                st.pop(key, None)
+        l, b, h = g // (inp.B * inp.Hkv), (g // inp.Hkv) % inp.B, g % inp.Hkv
+        grp = inp.Hq // inp.Hkv
+        K = synth.bf16_bits(inp.K[g, :S0 + steps])
+        V = synth.bf16_bits(inp.V[g, :S0 + steps])
+        Qp = synth.bf16_bits(inp.Q[l, b, h * grp:(h + 1) * grp])
+        Qd = synth.bf16_bits(qdec[:, l, b, h * grp:(h + 1) * grp].to(torch.bfloat16))
+        return K, V, Qp, Qd, inp.Uk[l, h].cpu().numpy(), inp.Uv[l, h].cpu().numpy(), on_update
+
+    args = {g: prepare(g) for g in sl}  # host copies on this thread
+    threads = [threading.Thread(target=lambda g=g: oracle.full_loop_slice(
+        *args[g][:6], S0, steps, T, 32, 1e-3, on_update=args[g][6])) for g in sl]
     for th in threads:
         th.start()
     for th in threads:
         th.join()
-    for g in sl:
-        assert len(result[g]) == checked + 1
-        for j, ora in enumerate(result[g]):
-            _compare(snaps[j][g], ora, ora["S"])
+    assert not errors, errors
+    assert all(checked[g] == list(range(9)) for g in sl), checked
 
 
 def test_decode_append_places_rows(gpu_lib):

@@ -35,6 +35,8 @@ extern "C" kvc_status kvc_set_option(kvc_option opt, int64_t value) {
             if (value < 0 || value > 1) return KVC_ERR_INVALID_ARGUMENT;
             o.gather_path.store(value, std::memory_order_relaxed);
             return KVC_OK;
+        default:
+            break;
     }
     return KVC_ERR_INVALID_ARGUMENT;
 }
@@ -57,6 +59,8 @@ extern "C" const char *kvc_status_str(kvc_status s) {
         case KVC_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
         case KVC_ERR_HIP: return "HIP runtime error";
         case KVC_ERR_WAIT_EXPIRED: return "an in-kernel wait expired (affected scores are NaN)";
+        default:
+            break;
     }
     return "unknown status";
 }
@@ -74,6 +78,8 @@ extern "C" size_t kvc_workspace_bytes(kvc_op op, const kvc_dims *d, int64_t k, i
         case KVC_OP_RECONSTRUCT: return kvc::reconstruct_workspace_bytes(d);
         case KVC_OP_TOPK_RAGGED: return kvc::topk_ragged_workspace_bytes(G);
         case KVC_OP_REFINE_RISK: return kvc::risk_bytes(G, d->S, k);
+        default:
+            break;
     }
     return 0;
 }
