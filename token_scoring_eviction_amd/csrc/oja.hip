@@ -10,10 +10,13 @@
 //                      8x8 register tiles over LDS-staged rows
 //   oja_step_qr_*      per (layer, kv head), fp64 arithmetic: C = sum of
 //                      partials / n in chunk order; CU = C U; M = U^T CU;
-//                      U' = U + eta (CU - U M); classical Gram-Schmidt applied
-//                      twice per column (a reorthogonalised QR, positive
-//                      diagonal); U <- fp32(Q).  R <= 64 runs entirely in LDS
-//                      (M stored in fp32); larger R keeps C, CU, M in the workspace.
+//                      U' = U + eta (CU - U M); then a QR with a positive
+//                      diagonal, U <- fp32(Q).  R <= 64 (oja_step_qr_lds_kernel)
+//                      runs entirely in LDS with the products on the fp64
+//                      matrix cores and Cholesky QR applied twice (the Gram
+//                      matrix factored by rows on one wave); R = 96 and 128
+//                      (oja_step_qr_kernel) keep C, CU, M in the workspace and
+//                      use classical Gram-Schmidt applied twice per column.
 #include <cmath>
 
 #include "kvc_internal.h"
