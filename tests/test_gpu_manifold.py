@@ -57,9 +57,10 @@ def test_score_l2_windowed_small(gpu_lib, kvc_option, S, W, path):
 
 @pytest.mark.parametrize("kind", ["normal", "ties", "signed"])
 # slice lengths for every register-held select instance (up to 1, 2, 4, 8 and 16 tiles of
-# 4096 keys) and both sides of the longest one (65536 held, 65537 read at every pass)
+# 4096 keys) and both sides of the longest one (65536 held; 65537 and the decode loop's
+# 131104 hold the first 49152 and read the rest at every pass)
 @pytest.mark.parametrize("G,S", [(1, 1), (3, 100), (2, 4096), (2, 4097), (2, 16384), (5, 20000),
-                                 (1, 65536), (1, 65537)])
+                                 (1, 65536), (1, 65537), (2, 131104)])
 def test_topk_bit_exact_on_same_scores(gpu_lib, kind, G, S):
     s = synth.random_scores(G, S, seed=S * 7 + G, kind=kind, device="cpu")
     s_gpu = s.to(DEV)

@@ -65,10 +65,11 @@ constexpr int kMaxHeldTiles = 16;
 
 // kg / koff (device, nullable): per-slice budget and output offset (packed
 // outputs); otherwise every slice keeps k and its outputs start at g * k.
-// NT > 0: the slice holds at most NT * kTile scores; key t * kTile + 4 * thread + j
-// is read once into held[t][j] and every pass reads it there.  NT == 0: each pass
-// reads the scores again.
-template <int NT>
+// NT > 0: key t * kTile + 4 * thread + j (t < NT) is read once into held[t][j] and
+// every pass reads it there; without kTail the slice holds at most NT * kTile
+// scores, with kTail the scores past NT * kTile are read again at every pass.
+// NT == 0: each pass reads all the scores again.
+template <int NT, bool kTail = false>
 __global__ __launch_bounds__(kSelThreads) void select_compact(const float *__restrict__ scores,
                                                               int64_t S, int64_t s_stride,
                                                               int64_t k_all,
@@ -100,6 +101,7 @@ __global__ __launch_bounds__(kSelThreads) void select_compact(const float *__res
     const int64_t S4 = vec ? S / 4 * 4 : 0;
 
     uint32_t held[NT > 0 ? NT : 1][kPerThread];
+    constexpr int64_t kTail0 = static_cast<int64_t>(NT) * kTile;  // first score not held
     if constexpr (NT > 0) {
         // every thread's loads in flight at once
 #pragma unroll
@@ -148,10 +150,11 @@ __global__ __launch_bounds__(kSelThreads) void select_compact(const float *__res
 #pragma unroll
                 for (int j = 0; j < kPerThread; ++j)
                     count(held[t][j], static_cast<int64_t>(t) * kTile + static_cast<int64_t>(threadIdx.x) * kPerThread + j < S);
-        } else {
-            // four 16-byte loads per thread in flight per step
+        }
+        if constexpr (NT == 0 || kTail) {
+            // the scores past the held ones: four 16-byte loads per thread in flight per step
             constexpr int64_t kStep = static_cast<int64_t>(kSelThreads) * 4;
-            for (int64_t i = static_cast<int64_t>(threadIdx.x) * 4; i < S4; i += 4 * kStep) {
+            for (int64_t i = kTail0 + static_cast<int64_t>(threadIdx.x) * 4; i < S4; i += 4 * kStep) {
                 float4 x[4];
 #pragma unroll
                 for (int u = 0; u < 4; ++u)
@@ -249,8 +252,9 @@ __global__ __launch_bounds__(kSelThreads) void select_compact(const float *__res
             if (static_cast<int64_t>(t) * kTile >= S) break;  // uniform across the block
             ordered_tile(static_cast<int64_t>(t) * kTile, held[t]);
         }
-    } else {
-        for (int64_t base = 0; base < S; base += kTile) {
+    }
+    if constexpr (NT == 0 || kTail) {
+        for (int64_t base = kTail0; base < S; base += kTile) {
             const int64_t i0 = base + static_cast<int64_t>(threadIdx.x) * kPerThread;
             uint32_t keys[kPerThread];
             if (vec && i0 + kPerThread <= S) {
@@ -421,7 +425,10 @@ __global__ __launch_bounds__(kScanThreads) void ragged_offsets(const int64_t *__
 }
 
 // select_compact for a slice length S: the register-held instance with the fewest
-// tiles that covers S, else the instance that reads the scores at every pass.
+// tiles that covers S, else the instance that holds the first 12 tiles (49152
+// scores; holding 14 or 16 next to the tail's loads spilled) and reads the rest at
+// every pass (the decode loop's 131072 + 32j scores: 172 us per call when every
+// score was read at each of the five passes).
 void launch_select(int64_t G, int64_t S, hipStream_t stream, const float *scores, int64_t s_stride,
                    int64_t k_all, const int64_t *kg, const int64_t *koff, int32_t *idx_out,
                    const uint16_t *K, const uint16_t *V, uint16_t *K_out, uint16_t *V_out) {
@@ -434,7 +441,9 @@ void launch_select(int64_t G, int64_t S, hipStream_t stream, const float *scores
     else if (S <= 4 * kTile) KVC_SELECT(4);
     else if (S <= 8 * kTile) KVC_SELECT(8);
     else if (S <= kMaxHeldTiles * kTile) KVC_SELECT(kMaxHeldTiles);
-    else KVC_SELECT(0);
+    else
+        hipLaunchKernelGGL((select_compact<12, true>), grid, block, 0, stream, scores, S, s_stride, k_all,
+                           kg, koff, idx_out, K, V, K_out, V_out);
 #undef KVC_SELECT
 }
 
