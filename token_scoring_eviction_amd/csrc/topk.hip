@@ -124,17 +124,23 @@ __global__ __launch_bounds__(kSelThreads) void select_compact(const float *__res
         const int shift = 24 - 8 * pass;
         for (int i = threadIdx.x; i < kSelWaves * 256; i += kSelThreads) (&hist[0][0])[i] = 0u;
         __syncthreads();
-        // Keys that match the prefix add to their digit's bin.  The lanes holding the
-        // digit of the wave's first matching lane are counted with one atomic (in the
-        // first passes most keys share a few digits -- the top byte is the sign and
-        // exponent -- and 64 atomics on one LDS address serialise); the others add
-        // one each.  The bin counts are the same either way.  (Further rounds of this
-        // aggregation measured slower on the eviction workloads: 0.030 -> 0.033 ms at
-        // 256 x 16384, 0.086 -> 0.096 ms at 256 x 65536; faster only on concentrated
-        // error scores, 0.175 -> 0.165 ms at 1024 x 32768.)
+        // Keys that match the prefix add to their digit's bin.  In the first pass the
+        // digit is the top byte -- the sign and exponent -- so most keys share a few
+        // digits and 64 atomics on one LDS address would serialise: the lanes holding
+        // the digit of the wave's first matching lane add with one atomic and the
+        // others one each.  The later passes' digits are mantissa bits, spread over
+        // many bins, and every key adds its own atomic: the ballots of an aggregation
+        // round cost more than the conflicts they save there (one round in every pass
+        // -> in the first pass only: 21.4 -> 19.9 us at 256 x 16384, 72.4 -> 65.6 us at
+        // 256 x 65536, 164 -> 153 us for 1024 x 32768 error scores; two or more rounds
+        // in the first pass: 47 us at 256 x 16384).  The bin counts are the same either way.
         auto count = [&](uint32_t key, bool valid) {
             const bool m = valid && (key & mask) == prefix;
             const uint32_t dig = (key >> shift) & 255u;
+            if (pass > 0) {
+                if (m) atomicAdd(&hist[wave][dig], 1u);
+                return;
+            }
             const uint64_t act = __ballot(m);
             if (act == 0) return;  // uniform across the wave
             const int first = __ffsll(static_cast<unsigned long long>(act)) - 1;
