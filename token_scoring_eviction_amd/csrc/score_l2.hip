@@ -14,14 +14,18 @@
 //     are co-resident (cooperative launch), so a team's tiles run in the same
 //     round.  Each workgroup keeps its tile in registers (16 rows x 8 channels
 //     per thread, 16-byte coalesced loads).
-//   - Each workgroup publishes its tile's fp32 column sums; the last one to
-//     arrive (device-scope counter) adds the team's partials in tile order --
-//     deterministic whichever arrives last -- divides by the window length and
-//     publishes the centroid and a flag; the others poll the flag (bounded:
-//     past the limit a status bit is set and the kernel still ends).
+//   - Each workgroup publishes its tile's fp32 column sums with coherent stores
+//     and goes on without waiting for them.  One member of the team (member
+//     team mod members, so the role rotates) polls the team's partial words
+//     until all are written -- they are cleared to a pattern no sum can take
+//     before the launch -- adds them in tile order (deterministic), divides by
+//     the window length and publishes the centroid words; the others poll those
+//     (every wait bounded: past the limit a status bit is set and the kernel
+//     still ends).
 //   - Every workgroup then scores its rows from registers.  Two tiles are in
-//     flight per workgroup: the next tile is loaded and its partial published
-//     before the workgroup waits for the current tile's centroid.
+//     flight per workgroup: every load of the next tile is issued before the
+//     workgroup waits for the current tile's centroid, and the next tile's
+//     partial is published right after the current tile is scored.
 //
 // Fallback path, three launches on the caller's stream:
 //   1. centroid_partial: column sums of bf16 keys over fixed 256-token chunks
@@ -30,6 +34,8 @@
 //      (deterministic, no float atomics) and divided by the window's length;
 //   3. l2_distance: 16 lanes per key row, each lane 8 channels, a 16-lane
 //      butterfly for the squared norm, fp32 sqrt.
+#include <type_traits>
+
 #include "kvc_internal.h"
 
 namespace kvc {
@@ -279,24 +285,26 @@ __device__ __forceinline__ float sum16(float a) {
 }
 
 constexpr int kZeroThreads = 256;
-__global__ __launch_bounds__(kZeroThreads) void zero_words(uint32_t *p, int64_t n) {
+// Words [0, n_zero) of p become 0, words [n_zero, n) become `value`.
+__global__ __launch_bounds__(kZeroThreads) void fill_words(uint32_t *p, int64_t n_zero, int64_t n,
+                                                           uint32_t value) {
     for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
          i += static_cast<int64_t>(gridDim.x) * blockDim.x)
-        p[i] = 0u;
+        p[i] = i < n_zero ? 0u : value;
 }
 
-// Centroid words are published as 64-bit {fp32 bits, ready tag}, so a reader
-// learns availability and value in one coherent load.
-constexpr uint32_t kReady = 1u;
-
-__device__ __forceinline__ uint64_t tagged(float mu) {
-    return (static_cast<uint64_t>(kReady) << 32) | __float_as_uint(mu);
-}
+// Exchange words (tile partials and published centroids) are 32-bit fp32 bit
+// patterns, cleared to kPending before the launch.  kPending and kFailed are NaNs
+// whose low 16 bits are set: widened bf16 keys have those bits clear, and sums and
+// quotients of them either keep a NaN operand's payload or produce the default NaN,
+// so no computed value equals either pattern.
+constexpr uint32_t kPending = 0x7fffffffu;  // not written yet
+constexpr uint32_t kFailed = 0xffffffffu;   // the team's gather gave up (bounded wait)
 
 template <int kMetric>
 __global__ __launch_bounds__(kFuseThreads, KVC_FUSE_MINBLOCKS) void l2_fused(const uint16_t *__restrict__ K, FuseGeom geo,
-                                                         float *partial, uint64_t *mu_pub,
-                                                         uint32_t *counters, uint32_t *status,
+                                                         uint32_t *partial, uint32_t *mu_pub,
+                                                         uint32_t *status,
                                                          float *__restrict__ scores,
                                                          float *__restrict__ mu_user) {
     const int tid = threadIdx.x;
@@ -304,7 +312,6 @@ __global__ __launch_bounds__(kFuseThreads, KVC_FUSE_MINBLOCKS) void l2_fused(con
     const int rowg = tid >> 4;  // 0 .. kRowGroups-1
     __shared__ float red[kRowGroups][kHeadDim + 4];
     __shared__ float mu_s[kHeadDim];
-    __shared__ uint32_t last_s;
 
     struct TileGeo {
         int64_t team, member, g, w0, w1, t0;
@@ -320,18 +327,110 @@ __global__ __launch_bounds__(kFuseThreads, KVC_FUSE_MINBLOCKS) void l2_fused(con
         t.t0 = t.w0 + t.member * kFuseTile + rowg;  // this thread's first row
         return t;
     };
-    auto load_rows = [&](const TileGeo &t, uint4 *v, int r0, int r1) {
+    auto load_tile = [&](const TileGeo &t, uint4 *v) {
         const uint4 *base = reinterpret_cast<const uint4 *>(K + t.g * geo.S * kHeadDim) + lane16;
 #pragma unroll
-        for (int r = r0; r < r1; ++r) {
+        for (int r = 0; r < kFuseRows; ++r) {
             const int64_t row = t.t0 + static_cast<int64_t>(kRowGroups) * r;
             // keys are read once (streaming loads)
             v[r] = row < t.w1 ? ld_stream(base + row * (kHeadDim / 8)) : make_uint4(0u, 0u, 0u, 0u);
         }
     };
-    auto load_tile = [&](const TileGeo &t, uint4 *v) { load_rows(t, v, 0, kFuseRows); };
-    // Column sums of the tile -> the team's partial slot; the last arrival of
-    // the team adds the team's partials in tile order and publishes the centroid.
+    bool agg_ok = false;  // the last gather's outcome (its centroid is in mu_s)
+    auto nap_for = [](int &nap) {
+        // back-off: a team polls the same few lines; hammering them costs the data
+        // loads bandwidth on those memory channels
+        if (nap <= 1) __builtin_amdgcn_s_sleep(1);
+        else if (nap <= 4) __builtin_amdgcn_s_sleep(4);
+        else __builtin_amdgcn_s_sleep(16);
+        nap = nap < 16 ? nap * 2 : 16;
+    };
+    // The aggregator of a team polls the team's partials
+    // until every word is written, adds them in tile order (32 channel groups of 4 x
+    // kMemberGroups member groups, 8 members of a group in flight per thread, then
+    // the groups in order), divides by the window's length and publishes the
+    // centroid.  The wait is bounded: past the limit it publishes kFailed in every
+    // channel, sets the status bit and returns false.  The centroid is left in mu_s
+    // for the aggregator's own scoring of the tile.
+    auto gather_mu = [&](const TileGeo &t) -> bool {
+        const int cg = tid & 31, mg = tid >> 5;
+        const int64_t per = (geo.members + kMemberGroups - 1) / kMemberGroups;
+        const int64_t m0 = mg * per, m1 = min(geo.members, m0 + per);
+        const uint64_t *p = reinterpret_cast<const uint64_t *>(partial + t.team * geo.members * kHeadDim) + cg * 2;
+        float sx = 0.f, sy = 0.f, sz = 0.f, sw = 0.f;
+        bool failed = false;
+        uint32_t spins = 0;
+        // Polls members [m, m + n) until all their words are written, then adds them in
+        // order.  Each poll loads only the words not yet seen written (a written
+        // partial never changes).
+        auto take = [&](int64_t m, auto n_const) {
+            constexpr int n = decltype(n_const)::value;
+            uint64_t x[n][2];
+            uint32_t pending = (1u << (2 * n)) - 1u;
+            int nap = 1;
+            for (;;) {
+#pragma unroll
+                for (int u = 0; u < n; ++u)
+#pragma unroll
+                    for (int c = 0; c < 2; ++c)
+                        if (pending & (1u << (2 * u + c)))
+                            x[u][c] = __hip_atomic_load(p + (m + u) * (kHeadDim / 2) + c, __ATOMIC_RELAXED,
+                                                        __HIP_MEMORY_SCOPE_AGENT);
+#pragma unroll
+                for (int u = 0; u < n; ++u)
+#pragma unroll
+                    for (int c = 0; c < 2; ++c)
+                        if (static_cast<uint32_t>(x[u][c]) != kPending &&
+                            static_cast<uint32_t>(x[u][c] >> 32) != kPending)
+                            pending &= ~(1u << (2 * u + c));
+                if (!pending) break;
+                if (++spins > geo.spin_limit) {
+                    failed = true;
+                    return;
+                }
+                nap_for(nap);
+            }
+#pragma unroll
+            for (int u = 0; u < n; ++u) {
+                sx += __uint_as_float(static_cast<uint32_t>(x[u][0]));
+                sy += __uint_as_float(static_cast<uint32_t>(x[u][0] >> 32));
+                sz += __uint_as_float(static_cast<uint32_t>(x[u][1]));
+                sw += __uint_as_float(static_cast<uint32_t>(x[u][1] >> 32));
+            }
+        };
+        // chunks of 8, 4, 2, 1 members: every member of a thread's range is requested in
+        // one poll when the range is 8 long or a power of two below 8
+        int64_t m = m0;
+        for (; m + 8 <= m1 && !failed; m += 8) take(m, std::integral_constant<int, 8>());
+        if (m + 4 <= m1 && !failed) { take(m, std::integral_constant<int, 4>()); m += 4; }
+        if (m + 2 <= m1 && !failed) { take(m, std::integral_constant<int, 2>()); m += 2; }
+        if (m < m1 && !failed) take(m, std::integral_constant<int, 1>());
+        red[mg][cg * 4 + 0] = sx;
+        red[mg][cg * 4 + 1] = sy;
+        red[mg][cg * 4 + 2] = sz;
+        red[mg][cg * 4 + 3] = sw;
+        const bool any_failed = __syncthreads_or(failed);
+        if (tid < kHeadDim) {
+            uint32_t w = kFailed;
+            float mu = __int_as_float(0x7fc00000);
+            if (!any_failed) {
+                float sum = 0.f;
+#pragma unroll
+                for (int q = 0; q < kMemberGroups; ++q) sum += red[q][tid];
+                mu = sum / static_cast<float>(t.w1 - t.w0);
+                w = __float_as_uint(mu);
+            }
+            if (mu_user) mu_user[t.team * kHeadDim + tid] = mu;
+            __hip_atomic_store(mu_pub + t.team * kHeadDim + tid, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            mu_s[tid] = __uint_as_float(w);
+        }
+        if (any_failed && tid == 0) atomicOr(status, kStatusWaitExpired);
+        __syncthreads();  // red and mu_s
+        return !any_failed;
+    };
+    // Column sums of the tile -> the tile's partial words (32-bit coherent stores,
+    // nothing waited for).  The team's aggregator (member team mod members) then
+    // gathers the team's centroid, while it holds only this tile.
     auto publish = [&](int64_t tile, const TileGeo &t, const uint4 *v) {
         float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -348,96 +447,35 @@ __global__ __launch_bounds__(kFuseThreads, KVC_FUSE_MINBLOCKS) void l2_fused(con
             float sum = 0.f;
 #pragma unroll
             for (int r = 0; r < kRowGroups; ++r) sum += red[r][tid];
-            __hip_atomic_store(partial + tile * kHeadDim + tid, sum, __ATOMIC_RELAXED,
+            __hip_atomic_store(partial + tile * kHeadDim + tid, __float_as_uint(sum), __ATOMIC_RELAXED,
                                __HIP_MEMORY_SCOPE_AGENT);
         }
-        __builtin_amdgcn_s_waitcnt(0);  // partial stored at the coherence point
-        __syncthreads();
-        if (tid == 0)
-            last_s = atomicAdd(&counters[t.team], 1u) == static_cast<uint32_t>(geo.members - 1);
-        __syncthreads();
-        if (!last_s) return;
-        // 32 channel groups of 4 x kMemberGroups member groups; each thread sums its
-        // members (8 of them in flight at a time, two 64-bit coherent loads per member),
-        // then the member groups are added in order
-        {
-            const int cg = tid & 31, mg = tid >> 5;
-            const int64_t per = (geo.members + kMemberGroups - 1) / kMemberGroups;
-            const int64_t m0 = mg * per, m1 = min(geo.members, m0 + per);
-            const uint64_t *p = reinterpret_cast<const uint64_t *>(partial + t.team * geo.members * kHeadDim) +
-                                cg * 2;
-            float sx = 0.f, sy = 0.f, sz = 0.f, sw = 0.f;
-            auto add = [&](uint64_t a, uint64_t b) {
-                sx += __uint_as_float(static_cast<uint32_t>(a));
-                sy += __uint_as_float(static_cast<uint32_t>(a >> 32));
-                sz += __uint_as_float(static_cast<uint32_t>(b));
-                sw += __uint_as_float(static_cast<uint32_t>(b >> 32));
-            };
-            int64_t m = m0;
-            for (; m + 8 <= m1; m += 8) {
-                uint64_t x[8][2];
-#pragma unroll
-                for (int u = 0; u < 8; ++u)
-#pragma unroll
-                    for (int c = 0; c < 2; ++c)
-                        x[u][c] = __hip_atomic_load(p + (m + u) * (kHeadDim / 2) + c, __ATOMIC_RELAXED,
-                                                    __HIP_MEMORY_SCOPE_AGENT);
-#pragma unroll
-                for (int u = 0; u < 8; ++u) add(x[u][0], x[u][1]);
-            }
-            for (; m < m1; ++m) {
-                const uint64_t a = __hip_atomic_load(p + m * (kHeadDim / 2), __ATOMIC_RELAXED,
-                                                     __HIP_MEMORY_SCOPE_AGENT);
-                const uint64_t b = __hip_atomic_load(p + m * (kHeadDim / 2) + 1, __ATOMIC_RELAXED,
-                                                     __HIP_MEMORY_SCOPE_AGENT);
-                add(a, b);
-            }
-            red[mg][cg * 4 + 0] = sx;
-            red[mg][cg * 4 + 1] = sy;
-            red[mg][cg * 4 + 2] = sz;
-            red[mg][cg * 4 + 3] = sw;
-        }
-        __syncthreads();
-        float mu = 0.f;
-        if (tid < kHeadDim) {
-            float sum = 0.f;
-#pragma unroll
-            for (int q = 0; q < kMemberGroups; ++q) sum += red[q][tid];
-            mu = sum / static_cast<float>(t.w1 - t.w0);
-            if (mu_user) mu_user[t.team * kHeadDim + tid] = mu;
-        }
-        if (tid < kHeadDim)
-            __hip_atomic_store(mu_pub + t.team * kHeadDim + tid, tagged(mu), __ATOMIC_RELAXED,
-                               __HIP_MEMORY_SCOPE_AGENT);
-        __syncthreads();  // red is reused by the caller
+        __syncthreads();  // red is reused
+        if (t.member == t.team % geo.members) agg_ok = gather_mu(t);
     };
-    // The team's centroid into mu_s: each channel's tagged word is polled
-    // until ready, with back-off.  The wait is bounded: past the limit a status
-    // bit is set and false is returned (the caller then writes NaN scores for
-    // the tile rather than scores against an unpublished centroid).
-    auto fetch_mu = [&](const TileGeo &t) -> bool {
+    // The other members poll the published centroid (bounded like the gather).
+    auto poll_mu = [&](const TileGeo &t) -> bool {
         uint32_t spins = 0;
         int nap = 1;
         for (;;) {
             bool ready = true;
             if (tid < kHeadDim) {
-                const uint64_t w = __hip_atomic_load(mu_pub + t.team * kHeadDim + tid, __ATOMIC_RELAXED,
+                const uint32_t w = __hip_atomic_load(mu_pub + t.team * kHeadDim + tid, __ATOMIC_RELAXED,
                                                      __HIP_MEMORY_SCOPE_AGENT);
-                ready = (w >> 32) == kReady;
-                mu_s[tid] = __uint_as_float(static_cast<uint32_t>(w));
+                ready = w != kPending;
+                mu_s[tid] = __uint_as_float(w);
             }
-            if (__syncthreads_and(ready)) return true;
+            if (__syncthreads_and(ready)) break;
             if (++spins > geo.spin_limit) {
                 if (tid == 0) atomicOr(status, kStatusWaitExpired);
                 return false;
             }
-            // back-off: a team polls the same few lines; hammering them costs
-            // the data loads bandwidth on those memory channels
-            if (nap <= 1) __builtin_amdgcn_s_sleep(1);
-            else if (nap <= 4) __builtin_amdgcn_s_sleep(4);
-            else __builtin_amdgcn_s_sleep(16);
-            nap = nap < 16 ? nap * 2 : 16;
+            nap_for(nap);
         }
+        return !__syncthreads_or(tid < kHeadDim && __float_as_uint(mu_s[tid]) == kFailed);
+    };
+    auto fetch_mu = [&](const TileGeo &t) -> bool {
+        return t.member == t.team % geo.members ? agg_ok : poll_mu(t);
     };
 
     // Scores tile `t` (held in v) once its team's centroid is published.
@@ -505,9 +543,10 @@ __global__ __launch_bounds__(kFuseThreads, KVC_FUSE_MINBLOCKS) void l2_fused(con
 
     const int64_t step = gridDim.x;
     int64_t tile = blockIdx.x;
-    // Two tiles per workgroup: while tile `tile` waits for its team's centroid
-    // and is scored, the next tile's loads are already in flight; its partial
-    // is published right after.
+    // Two tiles per workgroup: while tile `tile` waits for its team's centroid and is
+    // scored, every load of the next tile is already in flight; its partial is
+    // published right after.  (Requesting half of the next tile before the wait and
+    // half after it: 0.273 vs 0.267 ms per scoring call at 256 x 16384.)
     uint4 v[kFuseRows], vn[kFuseRows];
     if (tile < geo.tiles) {
         const TileGeo t = geo_of(tile);
@@ -518,17 +557,11 @@ __global__ __launch_bounds__(kFuseThreads, KVC_FUSE_MINBLOCKS) void l2_fused(con
         const TileGeo t = geo_of(tile);
         const int64_t next = tile + step;
         TileGeo tn;
-        // half of the next tile's rows are requested before the centroid wait, the
-        // rest after it: the chip's burst of key loads at the start of a step is
-        // halved, so the exchange's coherent accesses queue behind fewer of them
-        // (scoring call at 256 x 65536, W = 4096: 0.937 -> 0.910 ms; requesting 0, 4
-        // or 12 of the 16 rows first: 0.916-0.920 ms; at 256 x 16384 within 1%)
         if (next < geo.tiles) {
             tn = geo_of(next);
-            load_rows(tn, vn, 0, kFuseRows / 2);
+            load_tile(tn, vn);
         }
         const bool ok = fetch_mu(t);
-        if (next < geo.tiles) load_rows(tn, vn, kFuseRows / 2, kFuseRows);
         score_tile(t, v, ok);
         if (next < geo.tiles) publish(next, tn, vn);
 #pragma unroll
@@ -550,14 +583,13 @@ FuseGeom make_fuse_geom(int64_t G, int64_t S, int64_t W, int metric = kMetricL2)
     return f;
 }
 
-// Status header, tagged centroids and counters first (one contiguous range that a
-// single launch clears), then the tile partials.
+// Status header, published centroid words, then the tile partials: one contiguous
+// range that a single launch prepares.
 template <class Ws>
 void fused_ws_layout(Ws &ws, const FuseGeom &f) {
     ws.template take<uint32_t>(kStatusBytes / 4);                          // status header
-    ws.template take<uint64_t>(static_cast<size_t>(f.teams) * kHeadDim);   // tagged centroids
-    ws.template take<uint32_t>(static_cast<size_t>(f.teams));              // arrival counters
-    ws.template take<float>(static_cast<size_t>(f.tiles) * kHeadDim);      // tile partials
+    ws.template take<uint32_t>(static_cast<size_t>(f.teams) * kHeadDim);   // published centroids
+    ws.template take<uint32_t>(static_cast<size_t>(f.tiles) * kHeadDim);   // tile partials
 }
 
 // Co-resident workgroups of a fused-kernel instance on the current device (0 if unknown).
@@ -641,16 +673,17 @@ kvc_status score_windowed_impl(const uint16_t *K, int64_t G, int64_t S, int32_t 
     if (capacity >= f.members && f.tiles <= INT32_MAX && !take_unfused(G, S)) {
         WsCursor cur(ws);
         uint32_t *status = cur.take<uint32_t>(kStatusBytes / 4);
-        uint64_t *mu_pub = cur.take<uint64_t>(static_cast<size_t>(f.teams) * kHeadDim);
-        uint32_t *counters = cur.take<uint32_t>(static_cast<size_t>(f.teams));
-        float *partial = cur.take<float>(static_cast<size_t>(f.tiles) * kHeadDim);
-        // clear the status word, the centroid tags and the counters in one launch
-        // (they are adjacent in the workspace; a kernel, not a memset, so the
-        // sequence can be captured in a graph)
-        const int64_t n_clear = (counters + f.teams) - status;
+        uint32_t *mu_pub = cur.take<uint32_t>(static_cast<size_t>(f.teams) * kHeadDim);
+        uint32_t *partial = cur.take<uint32_t>(static_cast<size_t>(f.tiles) * kHeadDim);
+        // the status word cleared, the centroid and partial words set to kPending, in
+        // one launch (they are adjacent in the workspace; a kernel, not a memset, so
+        // the sequence can be captured in a graph)
+        const int64_t n_zero = kStatusBytes / 4;
+        const int64_t n_clear = (partial + f.tiles * kHeadDim) - status;
+        const uint32_t fill = kPending;
         const int64_t zb = (n_clear + kZeroThreads - 1) / kZeroThreads;
-        hipLaunchKernelGGL(zero_words, dim3(static_cast<unsigned>(zb < 1024 ? zb : 1024)), dim3(kZeroThreads), 0,
-                           stream, status, n_clear);
+        hipLaunchKernelGGL(fill_words, dim3(static_cast<unsigned>(zb < 1024 ? zb : 1024)), dim3(kZeroThreads), 0,
+                           stream, status, n_zero, n_clear, fill);
         FuseGeom fa = f;
         // KVC_OPTION_SCORE_SPIN_LIMIT shortens the bounded waits, so that a test can
         // force the expired-wait path from the host
@@ -659,7 +692,7 @@ kvc_status score_windowed_impl(const uint16_t *K, int64_t G, int64_t S, int32_t 
         float *mu_user = centroids;
         int64_t grid = capacity / f.members * f.members;
         if (grid > f.tiles) grid = f.tiles;
-        void *args[] = {&K, &fa, &partial, &mu_pub, &counters, &status, &scores, &mu_user};
+        void *args[] = {&K, &fa, &partial, &mu_pub, &status, &scores, &mu_user};
         if (hipLaunchCooperativeKernel(fused,
                                        dim3(static_cast<unsigned>(grid)), dim3(kFuseThreads), args, 0,
                                        stream) == hipSuccess)
