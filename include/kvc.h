@@ -57,8 +57,8 @@ typedef enum kvc_status {
     KVC_ERR_UNSUPPORTED = 2,        /* valid but not built: D != 128, R not in {32,64,96,128}, ... */
     KVC_ERR_WORKSPACE_TOO_SMALL = 3,/* ws_bytes < kvc_workspace_bytes(...) */
     KVC_ERR_HIP = 4,                /* a HIP runtime call or kernel launch failed */
-    KVC_ERR_WAIT_EXPIRED = 5,       /* reported by kvc_workspace_status: a bounded in-kernel
-                                       wait gave up; the affected scores are NaN */
+    KVC_ERR_WAIT_EXPIRED = 5,       /* no longer reported (a centroid wait that gives up is
+                                       repaired within the call); kept so codes stay stable */
     KVC_STATUS_MAX_ENUM = 0x7fffffff /* not a status: makes every int32 value a valid
                                         kvc_status, so callers may pass any code */
 } kvc_status;
@@ -68,10 +68,12 @@ typedef enum kvc_status {
  * results. */
 typedef enum kvc_option {
     KVC_OPTION_SCORE_PATH = 0,       /* centroid scores: 0 automatic (default), 1 the single-read
-                                        cooperative kernel where its grid fits, 2 the three-launch path */
-    KVC_OPTION_SCORE_SPIN_LIMIT = 1, /* polls of a centroid wait before it gives up: -1 the built-in
-                                        limit (default), 0 .. 2^32-1 (0: the first poll that finds no
-                                        centroid gives up; lets a test force the expired-wait path) */
+                                        kernel where a window's tiles fit the GPU at once, 2 the
+                                        three-launch path */
+    KVC_OPTION_SCORE_SPIN_LIMIT = 1, /* polls of a centroid wait before it gives up and leaves its
+                                        team to the call's repair launch: -1 the built-in limit
+                                        (default), 0 .. 2^32-1 (0: the first poll that finds no
+                                        centroid gives up; lets a test force the repair path) */
     KVC_OPTION_GATHER_PATH = 2,      /* kept-row copy: 0 a separate wide gather launch (default),
                                         1 the selecting workgroup copies its slice's rows when
                                         k <= 8192 and there are at least as many slices as CUs */
@@ -122,12 +124,12 @@ kvc_status kvc_set_option(kvc_option opt, int64_t value);
  * start of `ws` by the last call that used this workspace (kvc_score_l2,
  * kvc_score_l2_windowed, kvc_score_centroid, kvc_topk_compact_ragged; each of
  * them clears it before its kernels run).  Waits for `stream` to finish, then
- * reads the header: KVC_OK; KVC_ERR_WAIT_EXPIRED when a centroid wait gave up
- * (those tiles' scores are NaN, and NaN scores rank below every number in
- * kvc_topk_compact); KVC_ERR_INVALID_ARGUMENT when a device-side budget of
- * kvc_topk_compact_ragged was out of bounds (that slice kept nothing);
- * KVC_ERR_HIP when the wait or the read failed.  ws must be a workspace of one
- * of those calls, 256-byte aligned. */
+ * reads the header: KVC_OK; KVC_ERR_INVALID_ARGUMENT when a device-side budget
+ * of kvc_topk_compact_ragged was out of bounds (that slice kept nothing);
+ * KVC_ERR_HIP when the wait or the read failed.  The scoring calls have no
+ * failure to report (a centroid wait that gives up is repaired within the
+ * call), so for them it returns KVC_OK.  ws must be a workspace of one of those
+ * calls, 256-byte aligned. */
 kvc_status kvc_workspace_status(const void *ws, hipStream_t stream);
 
 /* Static, human-readable text for a status code. */
@@ -152,11 +154,12 @@ size_t kvc_workspace_bytes(kvc_op op, const kvc_dims *d, int64_t k, int64_t W);
  *   scores[g][t] = || K[g][t][:] - mu_g ||_2      (Euclidean distance)
  * K: bf16 [G][S][D].  scores: fp32 [G][S].  centroid: fp32 [G][D] or NULL.
  * Accumulation is fp32.  G >= 0, S >= 1 (G = 0 is a no-op).
- * Large caches are scored by one cooperative launch whose workgroups exchange
- * each window's centroid; every wait in it is bounded.  A wait that expires
- * (it cannot while the grid stays resident, as the cooperative launch
- * guarantees) leaves the affected scores NaN rather than wrong finite values,
- * and kvc_workspace_status(ws, stream) then returns KVC_ERR_WAIT_EXPIRED. */
+ * Large caches are scored by one persistent launch whose workgroups exchange
+ * each window's centroid; every wait in it is bounded.  A wait that runs past
+ * its limit (a team's workgroups not all resident, e.g. while another kernel
+ * holds part of the GPU) flags its window, and a repair launch queued in the
+ * same call recomputes the flagged windows from the keys with the same bits, so
+ * the results never depend on residency.  Results are deterministic. */
 kvc_status kvc_score_l2(const uint16_t *K, int64_t G, int64_t S, int32_t D, float *scores,
                         float *centroid, void *ws, size_t ws_bytes, hipStream_t stream);
 
@@ -192,8 +195,7 @@ kvc_status kvc_score_centroid(const uint16_t *K, int64_t G, int64_t S, int32_t D
  * before launching anything.  Results are bit-identical to kvc_score_centroid.
  * Every call on a device shares that device's scratch, so calls that may overlap
  * on one device (different streams or threads) race; calls queued in order on
- * one stream do not.  An expired centroid wait shows only as NaN scores (there
- * is no workspace to query). */
+ * one stream do not. */
 #define KVC_NOALLOC_SCRATCH_BYTES (48ull << 20)
 kvc_status kvc_score_centroid_noalloc(const uint16_t *K, int64_t G, int64_t S, int32_t D, int64_t W,
                                       int32_t metric, float *scores, float *centroids,

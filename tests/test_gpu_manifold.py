@@ -219,43 +219,48 @@ def test_binding_workspace_per_stream(gpu_lib):
     assert torch.equal(a, ref) and torch.equal(b, ref)
 
 
+@pytest.mark.parametrize("W", [None, 1000])
 @pytest.mark.parametrize("metric", ["l2", "cosine"])
-def test_expired_centroid_wait_gives_nan_not_wrong_scores(gpu_lib, kvc_option, metric):
+def test_expired_centroid_waits_are_repaired_bit_exactly(gpu_lib, kvc_option, metric, W):
     # the single-read kernel's centroid waits are bounded; a spin limit of 0 set from the
-    # host makes nearly every wait expire at its first poll.  Those tiles must come out NaN
-    # (whole 256-token tiles), every other score exactly as in a normal run, the kernel must
-    # end normally, and a normal call afterwards must be unaffected
+    # host makes nearly every wait give up at its first poll.  Those teams are flagged,
+    # and the repair launch queued after the kernel recomputes their centroids and
+    # scores from the keys: every score and centroid must come out bit-identical to a
+    # run whose waits succeed, and the workspace status must report nothing
     K, _, _ = synth.manifold_global(4, 1, 8, 16384, planted=8, seed=5, device=DEV)
     kvc_option("score_path", 1)
+    G, S = K.shape[0], K.shape[1]
+    nwin = 1 if W is None else -(-S // W)
 
     def score():
-        return gpu_lib.kvc_score_centroid(K, W=None, metric=metric)
+        mu = torch.empty((G, nwin, 128), dtype=torch.float32, device=DEV)
+        sc = gpu_lib.kvc_score_centroid(K, W=W, metric=metric, centroids=mu)
+        return sc.clone(), mu
 
-    ref = score().clone()
-    gpu_lib.kvc_workspace_status()  # a normal call reports nothing
+    ref, ref_mu = score()
+    gpu_lib.kvc_workspace_status()
     kvc_option("score_spin_limit", 0)
-    bad = score().clone()
-    # the failure is reported by the status query on the call's workspace
-    with pytest.raises(gpu_lib.KvcError) as err:
-        gpu_lib.kvc_workspace_status()
-    assert err.value.status == gpu_lib.ERR_WAIT_EXPIRED
-    # NaN scores rank below every number: with k no larger than the count of finite
-    # scores in every slice, no NaN token is kept, and the kept set is the top-k of the
-    # finite scores
-    nan = torch.isnan(bad)
-    k = int((~nan).sum(1).min())
-    if k > 0:
-        idx, _, _ = gpu_lib.kvc_topk_compact(bad, k)
-        kept_nan = torch.gather(nan, 1, idx.long())
-        assert not kept_nan.any()
-        fin = torch.where(nan, torch.full_like(bad, -1.0), bad).cpu().numpy()
-        np.testing.assert_array_equal(idx.cpu().numpy(), oracle.topk(fin, k))
+    rep, rep_mu = score()
+    gpu_lib.kvc_workspace_status()  # a repaired call reports no failure
     kvc_option("score_spin_limit", -1)
-    again = score()
+    again, _ = score()
     torch.cuda.synchronize()
-    gpu_lib.kvc_workspace_status()  # cleared by the next call
-    assert nan.any()
-    assert torch.equal(bad[~nan], ref[~nan])
-    tiles = nan.view(-1, 256)
-    assert torch.equal(tiles.any(1), tiles.all(1))
-    assert not torch.isnan(ref).any() and torch.equal(again, ref)
+    assert not torch.isnan(ref).any()
+    assert torch.equal(rep, ref) and torch.equal(rep_mu, ref_mu)
+    assert torch.equal(again, ref)
+
+
+def test_topk_ranks_nan_scores_below_every_number(gpu_lib):
+    # order keys map NaN below -inf: with k no larger than the count of numbers in
+    # every slice no NaN is kept, and the kept set is the top-k of the numbers
+    G, S = 24, 5000
+    s = synth.random_scores(G, S, seed=40, device=DEV)
+    rng = np.random.default_rng(41)
+    nan = torch.from_numpy(rng.random((G, S)) < 0.3).to(DEV)
+    nan[:, :256] = True  # whole leading tile as well
+    s = torch.where(nan, torch.full_like(s, float("nan")), s)
+    k = int((~nan).sum(1).min())
+    idx, _, _ = gpu_lib.kvc_topk_compact(s, k)
+    assert not torch.gather(nan, 1, idx.long()).any()
+    fin = torch.where(nan, torch.full_like(s, -1.0), s).cpu().numpy()  # the scores are >= 0
+    np.testing.assert_array_equal(idx.cpu().numpy(), oracle.topk(fin, k))

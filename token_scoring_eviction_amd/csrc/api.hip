@@ -46,7 +46,6 @@ extern "C" kvc_status kvc_workspace_status(const void *ws, hipStream_t stream) {
     if (hipStreamSynchronize(stream) != hipSuccess) return KVC_ERR_HIP;
     uint32_t word = 0;
     if (hipMemcpy(&word, ws, sizeof(word), hipMemcpyDeviceToHost) != hipSuccess) return KVC_ERR_HIP;
-    if (word & kvc::kStatusWaitExpired) return KVC_ERR_WAIT_EXPIRED;
     if (word & kvc::kStatusBadBudget) return KVC_ERR_INVALID_ARGUMENT;
     return KVC_OK;
 }
@@ -58,7 +57,7 @@ extern "C" const char *kvc_status_str(kvc_status s) {
         case KVC_ERR_UNSUPPORTED: return "unsupported shape or parameter";
         case KVC_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
         case KVC_ERR_HIP: return "HIP runtime error";
-        case KVC_ERR_WAIT_EXPIRED: return "an in-kernel wait expired (affected scores are NaN)";
+        case KVC_ERR_WAIT_EXPIRED: return "an in-kernel wait expired (no longer reported)";
         default:
             break;
     }

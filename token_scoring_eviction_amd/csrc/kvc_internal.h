@@ -46,8 +46,9 @@ struct WsSizer {
 // word holds kStatus* bits, cleared by each call before its kernels run and read
 // by kvc_workspace_status.
 constexpr size_t kStatusBytes = 256;
-constexpr uint32_t kStatusWaitExpired = 1u;  // a bounded centroid wait gave up
-constexpr uint32_t kStatusBadBudget = 2u;    // a per-slice budget outside its bounds
+constexpr uint32_t kStatusBadBudget = 2u;  // a per-slice budget outside its bounds
+constexpr uint32_t kStatusRepair = 4u;     // a centroid wait ran past its limit; the call's
+                                           // repair launch recomputed those teams (not a failure)
 
 // Process-wide options set by kvc_set_option (tests and measurements choose a
 // kernel path with them; the defaults select the production paths).

@@ -8,24 +8,28 @@
 // relative accuracy.
 //
 // Fused path (used whenever a window's tiles fit on the GPU at once): one
-// cooperative launch of a persistent grid reads every key exactly once.
+// launch of a persistent grid reads every key exactly once.
 //   - A window (the whole slice for the global score) is a team of 256-token
-//     tiles; the grid is a multiple of the team size and all its workgroups
-//     are co-resident (cooperative launch), so a team's tiles run in the same
-//     round.  Each workgroup keeps its tile in registers (16 rows x 8 channels
-//     per thread, 16-byte coalesced loads).
+//     tiles; the grid is a multiple of the team size, sized to the workgroups the
+//     GPU holds at once, so a team's tiles run in the same round.  Each workgroup
+//     keeps its tile in registers (16 rows x 8 channels per thread, 16-byte
+//     coalesced loads).
 //   - Each workgroup publishes its tile's fp32 column sums with coherent stores
 //     and goes on without waiting for them.  One member of the team (member
 //     team mod members, so the role rotates) polls the team's partial words
-//     until all are written -- they are cleared to a pattern no sum can take
-//     before the launch -- adds them in tile order (deterministic), divides by
-//     the window length and publishes the centroid words; the others poll those
-//     (every wait bounded: past the limit a status bit is set and the kernel
-//     still ends).
+//     until all are written -- they are set before the launch to a pattern no
+//     sum can take -- adds them in tile order (deterministic), divides by the
+//     window length and publishes the centroid words; the others poll those.
 //   - Every workgroup then scores its rows from registers.  Two tiles are in
 //     flight per workgroup: every load of the next tile is issued before the
 //     workgroup waits for the current tile's centroid, and the next tile's
 //     partial is published right after the current tile is scored.
+//   - Every wait is bounded.  One that runs past its limit (possible only when a
+//     team's workgroups are not all resident, e.g. another kernel holds part of
+//     the GPU) flags the team; a repair launch queued right after recomputes the
+//     flagged teams' centroids and scores from the keys, with the same bits, and
+//     returns at once when nothing is flagged.  So the launch needs no
+//     co-residency guarantee and is an ordinary launch.
 //
 // Fallback path, three launches on the caller's stream:
 //   1. centroid_partial: column sums of bf16 keys over fixed 256-token chunks
@@ -217,7 +221,10 @@ constexpr int kFuseRows = KVC_FUSE_ROWS;                      // rows per thread
 constexpr int kFuseTile = kRowGroups * kFuseRows;             // tokens per tile
 constexpr int kMemberGroups = kFuseThreads / 32;              // 32 channel groups of 4 each
 static_assert(kFuseThreads % 64 == 0 && kMemberGroups <= kRowGroups, "fused tile shape");
-constexpr uint32_t kSpinLimit = 1u << 16;  // ~0.1 s of polling: far above any real wait
+// Polls of a centroid wait before it gives up and leaves the team to the repair
+// launch: ~28 ms with the back-off, far above a wait among resident workgroups (~10 us).
+constexpr uint32_t kSpinLimit = 1u << 16;
+constexpr int64_t kRepairGrid = 1024;  // workgroups of the repair launch
 
 struct FuseGeom {
     int64_t G, S, W, nwin;
@@ -284,6 +291,49 @@ __device__ __forceinline__ float sum16(float a) {
     return a;
 }
 
+// Per-lane arithmetic of a key row (its 128 channels spread over the 16 lanes of a
+// row group, 8 per lane), shared by the scoring kernel and its repair launch so that
+// both give the same bits.  lane_d2: the lane's part of ||k - mu||^2.  row_cos: the
+// row's cosine score ||k/||k|| - mu/||mu||||^2 / 2 (1 where k or mu is zero) in every
+// lane of the row group, with ||mu||^2 (mm) formed by the same lane split and
+// butterfly as each key's ||k||^2, so that a key equal to the centroid scores 0.
+__device__ __forceinline__ float lane_d2(const uint4 &w, const float *m) {
+    float x[8];
+    widen8(w, x);
+    float acc = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const float d = x[j] - m[j];
+        acc += d * d;
+    }
+    return acc;
+}
+__device__ __forceinline__ float row_cos(const uint4 &w, const float *m, float mm, float inv_m) {
+    float x[8];
+    widen8(w, x);
+    float kk = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) kk += x[j] * x[j];
+    kk = sum16(kk);
+    const float inv = kk > 0.f ? 1.f / sqrtf(kk) : 0.f;
+    float e = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+        const float d = diff_of_products(x[j], inv, m[j], inv_m);
+        e += d * d;
+    }
+    e = sum16(e);
+    return (kk > 0.f && mm > 0.f) ? 0.5f * e : 1.f;
+}
+// ||mu||^2 over the row group's lanes (channels lane16*8 .. +8 in m) and 1/||mu||.
+__device__ __forceinline__ void centroid_norm(const float *m, float &mm, float &inv_m) {
+    mm = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) mm += m[j] * m[j];
+    mm = sum16(mm);
+    inv_m = mm > 0.f ? 1.f / sqrtf(mm) : 0.f;
+}
+
 constexpr int kZeroThreads = 256;
 // Words [0, n_zero) of p become 0, words [n_zero, n) become `value`.
 __global__ __launch_bounds__(kZeroThreads) void fill_words(uint32_t *p, int64_t n_zero, int64_t n,
@@ -304,7 +354,7 @@ constexpr uint32_t kFailed = 0xffffffffu;   // the team's gather gave up (bounde
 template <int kMetric>
 __global__ __launch_bounds__(kFuseThreads, KVC_FUSE_MINBLOCKS) void l2_fused(const uint16_t *__restrict__ K, FuseGeom geo,
                                                          uint32_t *partial, uint32_t *mu_pub,
-                                                         uint32_t *status,
+                                                         uint32_t *repair, uint32_t *status,
                                                          float *__restrict__ scores,
                                                          float *__restrict__ mu_user) {
     const int tid = threadIdx.x;
@@ -337,6 +387,15 @@ __global__ __launch_bounds__(kFuseThreads, KVC_FUSE_MINBLOCKS) void l2_fused(con
         }
     };
     bool agg_ok = false;  // the last gather's outcome (its centroid is in mu_s)
+    // A wait that ran past its limit marks its team for the repair launch that follows
+    // this kernel on the stream, which recomputes the team's centroid and scores from
+    // the keys (the tile's scores are NaN until then).
+    auto flag_repair = [&](const TileGeo &t) {
+        if (tid == 0) {
+            __hip_atomic_store(repair + t.team, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            atomicOr(status, kStatusRepair);
+        }
+    };
     auto nap_for = [](int &nap) {
         // back-off: a team polls the same few lines; hammering them costs the data
         // loads bandwidth on those memory channels
@@ -424,7 +483,7 @@ __global__ __launch_bounds__(kFuseThreads, KVC_FUSE_MINBLOCKS) void l2_fused(con
             __hip_atomic_store(mu_pub + t.team * kHeadDim + tid, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             mu_s[tid] = __uint_as_float(w);
         }
-        if (any_failed && tid == 0) atomicOr(status, kStatusWaitExpired);
+        if (any_failed) flag_repair(t);
         __syncthreads();  // red and mu_s
         return !any_failed;
     };
@@ -467,7 +526,7 @@ __global__ __launch_bounds__(kFuseThreads, KVC_FUSE_MINBLOCKS) void l2_fused(con
             }
             if (__syncthreads_and(ready)) break;
             if (++spins > geo.spin_limit) {
-                if (tid == 0) atomicOr(status, kStatusWaitExpired);
+                flag_repair(t);
                 return false;
             }
             nap_for(nap);
@@ -488,50 +547,22 @@ __global__ __launch_bounds__(kFuseThreads, KVC_FUSE_MINBLOCKS) void l2_fused(con
 #pragma unroll
         for (int j = 0; j < 8; ++j) m[j] = mu_s[lane16 * 8 + j];
         if (kMetric == kMetricCosine) {
-            // ||k/||k|| - mu/||mu||||^2 / 2 per row: the 16 lanes of a row group hold its
-            // 128 channels; lane r keeps row r's score (1 where k or mu is zero)
-            // ||mu||^2 with the same lane split and butterfly as each key's ||k||^2, so a
-            // key equal to the centroid gets the same scale and scores exactly 0
-            float mm = 0.f;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) mm += m[j] * m[j];
-            mm = sum16(mm);
-            const float inv_m = mm > 0.f ? 1.f / sqrtf(mm) : 0.f;
+            float mm, inv_m;
+            centroid_norm(m, mm, inv_m);
             float mine = 0.f;
 #pragma unroll
             for (int r = 0; r < kFuseRows; ++r) {
-                float x[8];
-                widen8(v[r], x);
-                float kk = 0.f;
-#pragma unroll
-                for (int j = 0; j < 8; ++j) kk += x[j] * x[j];
-                kk = sum16(kk);
-                const float inv = kk > 0.f ? 1.f / sqrtf(kk) : 0.f;
-                float e = 0.f;
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const float d = diff_of_products(x[j], inv, m[j], inv_m);
-                    e += d * d;
-                }
-                e = sum16(e);
-                if (lane16 == r) mine = (kk > 0.f && mm > 0.f) ? 0.5f * e : 1.f;
+                const float c = row_cos(v[r], m, mm, inv_m);
+                if (lane16 == r) mine = c;
             }
             const int64_t row = t.t0 + static_cast<int64_t>(kRowGroups) * lane16;
             if (lane16 < kFuseRows && row < t.w1) scores[t.g * geo.S + row] = ok ? mine : nan;
         } else {
+            // the 16 rows' lane parts reduced across the row group at once (DPP
+            // transpose-reduce, the same pairing as a 16-lane butterfly per row)
             float d2[kFuseRows];
 #pragma unroll
-            for (int r = 0; r < kFuseRows; ++r) {
-                float x[8];
-                widen8(v[r], x);
-                float acc = 0.f;
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const float d = x[j] - m[j];
-                    acc += d * d;
-                }
-                d2[r] = acc;
-            }
+            for (int r = 0; r < kFuseRows; ++r) d2[r] = lane_d2(v[r], m);
             row_transpose_reduce<kFuseRows>(d2, lane16);
             const int r = kFuseRows == 16 ? lane16 : (lane16 >> 1);
             const int64_t row = t.t0 + static_cast<int64_t>(kRowGroups) * r;
@@ -569,6 +600,100 @@ __global__ __launch_bounds__(kFuseThreads, KVC_FUSE_MINBLOCKS) void l2_fused(con
     }
 }
 
+// Repair launch, queued right after l2_fused on the same stream.  When no centroid
+// wait of that launch ran past its limit (the status bit is clear) every workgroup
+// returns at once.  Otherwise each flagged team's centroid is computed from its
+// keys -- every member tile's column sums formed as l2_fused's publish forms them,
+// added in its aggregator's order -- and every tile of the team is scored from its
+// keys read again, with the scoring kernel's per-row arithmetic.  The results are
+// the bits l2_fused produces when its waits succeed.  With this launch the fused
+// path needs no co-residency guarantee: a team whose workgroups are not all
+// resident at once only costs a second read of its keys.
+template <int kMetric>
+__global__ __launch_bounds__(kFuseThreads) void l2_repair(const uint16_t *__restrict__ K, FuseGeom geo,
+                                                          const uint32_t *__restrict__ repair,
+                                                          const uint32_t *__restrict__ status,
+                                                          float *__restrict__ scores,
+                                                          float *__restrict__ mu_user) {
+    if ((*status & kStatusRepair) == 0u) return;
+    const int tid = threadIdx.x;
+    const int lane16 = tid & 15;
+    const int rowg = tid >> 4;
+    __shared__ float red[kRowGroups][kHeadDim + 4];
+    __shared__ float mu_s[kHeadDim];
+    const int64_t per = (geo.members + kMemberGroups - 1) / kMemberGroups;
+    for (int64_t team = blockIdx.x; team < geo.teams; team += gridDim.x) {
+        if (repair[team] == 0u) continue;
+        const int64_t g = team / geo.nwin;
+        const int64_t w0 = (team - g * geo.nwin) * geo.W;
+        const int64_t w1 = min(w0 + geo.W, geo.S);
+        const uint4 *base = reinterpret_cast<const uint4 *>(K + g * geo.S * kHeadDim) + lane16;
+        // the centroid: tile column sums (rows t0 + 16 r of the thread's row group,
+        // then the 16 row groups in order), member groups of `per` tiles added in
+        // order, then the groups in order
+        float gs[kMemberGroups];
+#pragma unroll
+        for (int q = 0; q < kMemberGroups; ++q) gs[q] = 0.f;
+        for (int64_t j = 0; j < geo.members; ++j) {
+            const int64_t t0 = w0 + j * kFuseTile + rowg;
+            float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int r = 0; r < kFuseRows; ++r) {
+                const int64_t row = t0 + static_cast<int64_t>(kRowGroups) * r;
+                const uint4 w = row < w1 ? ld_stream(base + row * (kHeadDim / 8)) : make_uint4(0u, 0u, 0u, 0u);
+                float x[8];
+                widen8(w, x);
+#pragma unroll
+                for (int c = 0; c < 8; ++c) acc[c] += x[c];
+            }
+#pragma unroll
+            for (int c = 0; c < 8; ++c) red[rowg][lane16 * 8 + c] = acc[c];
+            __syncthreads();
+            if (tid < kHeadDim) {
+                float sum = 0.f;
+#pragma unroll
+                for (int r = 0; r < kRowGroups; ++r) sum += red[r][tid];
+                const int64_t q = j / per;
+#pragma unroll
+                for (int qq = 0; qq < kMemberGroups; ++qq)
+                    if (qq == q) gs[qq] += sum;
+            }
+            __syncthreads();  // red is reused
+        }
+        if (tid < kHeadDim) {
+            float sum = 0.f;
+#pragma unroll
+            for (int q = 0; q < kMemberGroups; ++q) sum += gs[q];
+            const float mu = sum / static_cast<float>(w1 - w0);
+            mu_s[tid] = mu;
+            if (mu_user) mu_user[team * kHeadDim + tid] = mu;
+        }
+        __syncthreads();
+        float m[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c) m[c] = mu_s[lane16 * 8 + c];
+        float mm = 0.f, inv_m = 0.f;
+        if (kMetric == kMetricCosine) centroid_norm(m, mm, inv_m);
+        // every tile of the team: lane r of a row group keeps row r's score; a row's
+        // lane parts are added by a 16-lane butterfly, the pairing of the scoring
+        // kernel's transpose-reduce
+        for (int64_t j = 0; j < geo.members; ++j) {
+            const int64_t t0 = w0 + j * kFuseTile + rowg;
+            float mine = 0.f;
+#pragma unroll
+            for (int r = 0; r < kFuseRows; ++r) {
+                const int64_t row = t0 + static_cast<int64_t>(kRowGroups) * r;
+                const uint4 w = row < w1 ? ld_stream(base + row * (kHeadDim / 8)) : make_uint4(0u, 0u, 0u, 0u);
+                const float c = kMetric == kMetricCosine ? row_cos(w, m, mm, inv_m) : sqrtf(sum16(lane_d2(w, m)));
+                if (lane16 == r) mine = c;
+            }
+            const int64_t row = t0 + static_cast<int64_t>(kRowGroups) * lane16;
+            if (lane16 < kFuseRows && row < w1) scores[g * geo.S + row] = mine;
+        }
+        __syncthreads();  // mu_s is rewritten for the next team
+    }
+}
+
 FuseGeom make_fuse_geom(int64_t G, int64_t S, int64_t W, int metric = kMetricL2) {
     FuseGeom f;
     f.metric = metric;
@@ -588,16 +713,16 @@ FuseGeom make_fuse_geom(int64_t G, int64_t S, int64_t W, int metric = kMetricL2)
 template <class Ws>
 void fused_ws_layout(Ws &ws, const FuseGeom &f) {
     ws.template take<uint32_t>(kStatusBytes / 4);                          // status header
+    ws.template take<uint32_t>(static_cast<size_t>(f.teams));              // repair flags
     ws.template take<uint32_t>(static_cast<size_t>(f.teams) * kHeadDim);   // published centroids
     ws.template take<uint32_t>(static_cast<size_t>(f.tiles) * kHeadDim);   // tile partials
 }
 
 // Co-resident workgroups of a fused-kernel instance on the current device (0 if unknown).
 int64_t fused_capacity(const void *kernel) {
-    int dev = 0, cus = 0, per_cu = 0, coop = 0;
+    int dev = 0, cus = 0, per_cu = 0;
     if (hipGetDevice(&dev) != hipSuccess) return 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-    if (hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) != hipSuccess || !coop) return 0;
     if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kFuseThreads, 0) != hipSuccess)
         return 0;
     return static_cast<int64_t>(cus) * per_cu;
@@ -629,8 +754,7 @@ size_t score_bytes(int64_t G, int64_t S, int64_t W) {
 }
 
 // Caches smaller than this take the three-launch path: its second read of K comes
-// from the 256 MB last-level cache, and it has no cooperative launch or team
-// exchange to wait for.  Measured on MI355X: 8 MB of keys 15 vs 30 us, 134 MB
+// from the 256 MB last-level cache, and it has no team exchange to wait for.  Measured on MI355X: 8 MB of keys 15 vs 30 us, 134 MB
 // even, 268 MB 113 vs 98 us, 1 GB 426 vs 258 us (three-launch vs single-read).
 constexpr int64_t kSmallCacheBytes = 160ll << 20;
 
@@ -673,33 +797,41 @@ kvc_status score_windowed_impl(const uint16_t *K, int64_t G, int64_t S, int32_t 
     if (capacity >= f.members && f.tiles <= INT32_MAX && !take_unfused(G, S)) {
         WsCursor cur(ws);
         uint32_t *status = cur.take<uint32_t>(kStatusBytes / 4);
+        uint32_t *repair = cur.take<uint32_t>(static_cast<size_t>(f.teams));
         uint32_t *mu_pub = cur.take<uint32_t>(static_cast<size_t>(f.teams) * kHeadDim);
         uint32_t *partial = cur.take<uint32_t>(static_cast<size_t>(f.tiles) * kHeadDim);
-        // the status word cleared, the centroid and partial words set to kPending, in
-        // one launch (they are adjacent in the workspace; a kernel, not a memset, so
-        // the sequence can be captured in a graph)
-        const int64_t n_zero = kStatusBytes / 4;
+        // the status word and the repair flags cleared, the centroid and partial words
+        // set to kPending, in one launch (they are adjacent in the workspace; a kernel,
+        // not a memset, so the sequence can be captured in a graph)
+        const int64_t n_zero = (repair + f.teams) - status;
         const int64_t n_clear = (partial + f.tiles * kHeadDim) - status;
-        const uint32_t fill = kPending;
         const int64_t zb = (n_clear + kZeroThreads - 1) / kZeroThreads;
         hipLaunchKernelGGL(fill_words, dim3(static_cast<unsigned>(zb < 1024 ? zb : 1024)), dim3(kZeroThreads), 0,
-                           stream, status, n_zero, n_clear, fill);
+                           stream, status, n_zero, n_clear, kPending);
         FuseGeom fa = f;
-        // KVC_OPTION_SCORE_SPIN_LIMIT shortens the bounded waits, so that a test can
-        // force the expired-wait path from the host
+        // KVC_OPTION_SCORE_SPIN_LIMIT shortens the waits, so that a test can force the
+        // repair path from the host
         const int64_t lim = options().spin_limit.load(std::memory_order_relaxed);
         fa.spin_limit = lim >= 0 ? static_cast<uint32_t>(lim) : kSpinLimit;
         float *mu_user = centroids;
         int64_t grid = capacity / f.members * f.members;
         if (grid > f.tiles) grid = f.tiles;
-        void *args[] = {&K, &fa, &partial, &mu_pub, &status, &scores, &mu_user};
-        if (hipLaunchCooperativeKernel(fused,
-                                       dim3(static_cast<unsigned>(grid)), dim3(kFuseThreads), args, 0,
-                                       stream) == hipSuccess)
-            return launch_status();
-        // the runtime refused the co-resident grid: the three-launch path below computes
-        // the same scores without it (its workspace layout fits the same buffer)
-        (void)hipGetLastError();
+        // Plain launches: no co-residency is needed (a team whose waits run long is
+        // recomputed by the repair launch), and a cooperative launch costs ~16 us more
+        // per call (scoring call at 256 x 16384: 0.264 vs 0.248 ms).
+        const int64_t rgrid = f.teams < kRepairGrid ? f.teams : kRepairGrid;
+        if (metric == kMetricCosine) {
+            hipLaunchKernelGGL(l2_fused<kMetricCosine>, dim3(static_cast<unsigned>(grid)), dim3(kFuseThreads), 0,
+                               stream, K, fa, partial, mu_pub, repair, status, scores, mu_user);
+            hipLaunchKernelGGL(l2_repair<kMetricCosine>, dim3(static_cast<unsigned>(rgrid)), dim3(kFuseThreads), 0,
+                               stream, K, fa, repair, status, scores, mu_user);
+        } else {
+            hipLaunchKernelGGL(l2_fused<kMetricL2>, dim3(static_cast<unsigned>(grid)), dim3(kFuseThreads), 0,
+                               stream, K, fa, partial, mu_pub, repair, status, scores, mu_user);
+            hipLaunchKernelGGL(l2_repair<kMetricL2>, dim3(static_cast<unsigned>(rgrid)), dim3(kFuseThreads), 0,
+                               stream, K, fa, repair, status, scores, mu_user);
+        }
+        return launch_status();
     }
 
     const WinGeom geo = make_geom(G, S, W, metric);

@@ -143,9 +143,9 @@ def kvc_set_option(name, value):
 
 def kvc_workspace_status(device=None):
     """kvc_workspace_status on the cached workspace of the current stream: waits for
-    the stream, then raises KvcError if the last scoring or ragged-selection call on
-    it recorded a failure in its kernels (an expired centroid wait, a device budget
-    out of bounds)."""
+    the stream, then raises KvcError if the last ragged-selection call on it recorded
+    a failure in its kernels (a device budget out of bounds; scoring calls have none
+    to report)."""
     dev = torch.device("cuda", torch.cuda.current_device() if device is None else device)
     buf = _ws.get((dev, torch.cuda.current_stream(dev).cuda_stream))
     if buf is None:
