@@ -753,10 +753,12 @@ size_t score_bytes(int64_t G, int64_t S, int64_t W) {
     return a.bytes() > b.bytes() ? a.bytes() : b.bytes();
 }
 
-// Caches smaller than this take the three-launch path: its second read of K comes
-// from the 256 MB last-level cache, and it has no team exchange to wait for.  Measured on MI355X: 8 MB of keys 15 vs 30 us, 134 MB
-// even, 268 MB 113 vs 98 us, 1 GB 426 vs 258 us (three-launch vs single-read).
-constexpr int64_t kSmallCacheBytes = 160ll << 20;
+// Caches smaller than this take the three-launch path (its second read of K comes
+// from the caches, and it has no team exchange to wait for).  Measured on MI355X,
+// scoring call three-launch vs single-read: 8 MB of keys 16.6 vs 17.4 us, 17 MB 28.3
+// vs 17.1, 67 MB 42.1 vs 24.4, 134 MB 64.0 vs 39.7, 268 MB 112.0 vs 67.9, 1 GB 449.9
+// vs 240.9 us.
+constexpr int64_t kSmallCacheBytes = 12ll << 20;
 
 // The option KVC_OPTION_SCORE_PATH overrides the choice (1: the single-read kernel,
 // 2: the three-launch path), so that tests and measurements can compare both.
