@@ -224,7 +224,7 @@ static_assert(kFuseThreads % 64 == 0 && kMemberGroups <= kRowGroups, "fused tile
 // Polls of a centroid wait before it gives up and leaves the team to the repair
 // launch: ~28 ms with the back-off, far above a wait among resident workgroups (~10 us).
 constexpr uint32_t kSpinLimit = 1u << 16;
-constexpr int64_t kRepairGrid = 1024;  // workgroups of the repair launch
+constexpr int64_t kRepairGrid = 256;  // workgroups of the repair launch
 
 struct FuseGeom {
     int64_t G, S, W, nwin;
@@ -338,9 +338,16 @@ constexpr int kZeroThreads = 256;
 // Words [0, n_zero) of p become 0, words [n_zero, n) become `value`.
 __global__ __launch_bounds__(kZeroThreads) void fill_words(uint32_t *p, int64_t n_zero, int64_t n,
                                                            uint32_t value) {
-    for (int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x; i < n;
-         i += static_cast<int64_t>(gridDim.x) * blockDim.x)
-        p[i] = i < n_zero ? 0u : value;
+    // 16-byte stores over whole groups of 4 words (p is 16-byte aligned), then the tail
+    const int64_t n4 = n / 4;
+    const int64_t stride = static_cast<int64_t>(gridDim.x) * blockDim.x;
+    const int64_t first = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+    for (int64_t i = first; i < n4; i += stride) {
+        const int64_t w = 4 * i;
+        reinterpret_cast<uint4 *>(p)[i] = make_uint4(w < n_zero ? 0u : value, w + 1 < n_zero ? 0u : value,
+                                                     w + 2 < n_zero ? 0u : value, w + 3 < n_zero ? 0u : value);
+    }
+    for (int64_t i = 4 * n4 + first; i < n; i += stride) p[i] = i < n_zero ? 0u : value;
 }
 
 // Exchange words (tile partials and published centroids) are 32-bit fp32 bit
@@ -807,8 +814,8 @@ kvc_status score_windowed_impl(const uint16_t *K, int64_t G, int64_t S, int32_t 
         // not a memset, so the sequence can be captured in a graph)
         const int64_t n_zero = (repair + f.teams) - status;
         const int64_t n_clear = (partial + f.tiles * kHeadDim) - status;
-        const int64_t zb = (n_clear + kZeroThreads - 1) / kZeroThreads;
-        hipLaunchKernelGGL(fill_words, dim3(static_cast<unsigned>(zb < 1024 ? zb : 1024)), dim3(kZeroThreads), 0,
+        const int64_t zb = (n_clear / 4 + kZeroThreads - 1) / kZeroThreads + 1;
+        hipLaunchKernelGGL(fill_words, dim3(static_cast<unsigned>(zb < 2048 ? zb : 2048)), dim3(kZeroThreads), 0,
                            stream, status, n_zero, n_clear, kPending);
         FuseGeom fa = f;
         // KVC_OPTION_SCORE_SPIN_LIMIT shortens the waits, so that a test can force the
