@@ -25,8 +25,8 @@ def _scores_vs_oracle(K, gpu_scores, W=None):
     return ora, mu
 
 
-# path "0": the cooperative single-read kernel, "1": the three-launch path (small
-# caches take the latter by default); chosen with the score_path option
+# path "0": the single-read kernel, "1": the three-launch path (caches under 12 MiB
+# take the latter by default); chosen with the score_path option
 @pytest.mark.parametrize("path", ["0", "1"])
 @pytest.mark.parametrize("G,S", [(1, 1), (3, 257), (2, 1000), (4, 4096), (1, 16384 + 77)])
 def test_score_l2_small(gpu_lib, kvc_option, G, S, path):
@@ -173,7 +173,7 @@ def test_determinism(gpu_lib):
 
 @pytest.mark.parametrize("W", [None, 4096, 1000])
 def test_fused_and_three_launch_paths_agree(gpu_lib, kvc_option, W):
-    # the cooperative single-read path and the three-launch path compute the same scores
+    # the single-read path and the three-launch path compute the same scores
     K, _, _ = synth.manifold_global(4, 1, 8, 12288 + 100, planted=8, seed=3, device=DEV)
     kvc_option("score_path", 1)
     f = gpu_lib.kvc_score_l2(K) if W is None else gpu_lib.kvc_score_l2_windowed(K, W)
@@ -248,6 +248,38 @@ def test_expired_centroid_waits_are_repaired_bit_exactly(gpu_lib, kvc_option, me
     assert not torch.isnan(ref).any()
     assert torch.equal(rep, ref) and torch.equal(rep_mu, ref_mu)
     assert torch.equal(again, ref)
+
+
+def test_scoring_beside_another_kernel_is_bit_identical(gpu_lib, kvc_option):
+    # the single-read kernel is an ordinary launch: while a GEMM on a second stream holds
+    # part of the GPU, a team's workgroups need not be resident together, and with a
+    # short poll limit the waits that run long leave their teams to the repair launch.
+    # Scores and centroids must equal those of a run on an otherwise idle GPU, bit for bit
+    K, _, _ = synth.manifold_global(4, 1, 8, 16384, planted=8, seed=61, device=DEV)
+    kvc_option("score_path", 1)
+    G = K.shape[0]
+
+    def score():
+        mu = torch.empty((G, 128), dtype=torch.float32, device=DEV)
+        return gpu_lib.kvc_score_l2(K, centroid=mu).clone(), mu
+
+    ref, ref_mu = score()
+    torch.cuda.synchronize()
+    a = torch.randn(6144, 6144, device=DEV)
+    b = torch.randn(6144, 6144, device=DEV)
+    side = torch.cuda.Stream()  # default priority
+    kvc_option("score_spin_limit", 256)
+    outs = []
+    for _ in range(3):
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            for _ in range(4):
+                c = a @ b
+        outs.append(score())
+    torch.cuda.synchronize()
+    del c
+    for sc, mu in outs:
+        assert torch.equal(sc, ref) and torch.equal(mu, ref_mu)
 
 
 def test_topk_ranks_nan_scores_below_every_number(gpu_lib):

@@ -28,8 +28,8 @@ def _both(gpu_lib, K, W, metric):
 
 @pytest.mark.parametrize("metric", ["l2", "cosine"])
 def test_noalloc_matches_workspace_entry_point(gpu_lib, metric):
-    # first call: 64 slices x 16384 tokens (256 MiB of keys: the single-read cooperative
-    # kernel); second call: 8 slices x 3000 tokens with 700-token windows (the
+    # first call: 64 slices x 16384 tokens (256 MiB of keys: the single-read kernel);
+    # second call: 8 slices x 3000 tokens with 700-token windows (the
     # three-launch path), after the first left its scratch filled
     K1, _, _ = synth.manifold_global(8, 1, 8, 16384, planted=16, seed=51, device=DEV)
     K2, _ = synth.manifold_drifting(1, 1, 8, 3000, segment=1000, seed=52, device=DEV)
