@@ -351,12 +351,13 @@ __global__ __launch_bounds__(kZeroThreads) void fill_words(uint32_t *p, int64_t 
 }
 
 // Exchange words (tile partials and published centroids) are 32-bit fp32 bit
-// patterns, cleared to kPending before the launch.  kPending and kFailed are NaNs
-// whose low 16 bits are set: widened bf16 keys have those bits clear, and sums and
+// patterns, set to kPending before the launch.  kPending and kFailed are NaNs whose
+// low 16 bits are set: widened bf16 keys have those bits clear, and sums and
 // quotients of them either keep a NaN operand's payload or produce the default NaN,
 // so no computed value equals either pattern.
 constexpr uint32_t kPending = 0x7fffffffu;  // not written yet
-constexpr uint32_t kFailed = 0xffffffffu;   // the team's gather gave up (bounded wait)
+constexpr uint32_t kFailed = 0xffffffffu;   // the team's gather gave up; the repair launch
+                                            // recomputes the team
 
 template <int kMetric>
 __global__ __launch_bounds__(kFuseThreads, KVC_FUSE_MINBLOCKS) void l2_fused(const uint16_t *__restrict__ K, FuseGeom geo,
@@ -416,8 +417,8 @@ __global__ __launch_bounds__(kFuseThreads, KVC_FUSE_MINBLOCKS) void l2_fused(con
     // kMemberGroups member groups, 8 members of a group in flight per thread, then
     // the groups in order), divides by the window's length and publishes the
     // centroid.  The wait is bounded: past the limit it publishes kFailed in every
-    // channel, sets the status bit and returns false.  The centroid is left in mu_s
-    // for the aggregator's own scoring of the tile.
+    // channel, flags the team for the repair launch and returns false.  The centroid
+    // is left in mu_s for the aggregator's own scoring of the tile.
     auto gather_mu = [&](const TileGeo &t) -> bool {
         const int cg = tid & 31, mg = tid >> 5;
         const int64_t per = (geo.members + kMemberGroups - 1) / kMemberGroups;
@@ -544,11 +545,10 @@ __global__ __launch_bounds__(kFuseThreads, KVC_FUSE_MINBLOCKS) void l2_fused(con
         return t.member == t.team % geo.members ? agg_ok : poll_mu(t);
     };
 
-    // Scores tile `t` (held in v) once its team's centroid is published.
+    // Scores tile `t` (held in v) once its team's centroid is published.  Without a
+    // centroid (a wait that gave up: the team is flagged) the tile's scores are
+    // written as quiet NaN, which the repair launch then overwrites.
     auto score_tile = [&](const TileGeo &t, const uint4 *v, bool ok) {
-        // a centroid that never arrived (the bounded wait expired) makes every
-        // score of the tile a quiet NaN, so the failure shows in the output
-        // instead of as plausible wrong distances (uniform across the workgroup)
         const float nan = __int_as_float(0x7fc00000);
         float m[8];
 #pragma unroll
