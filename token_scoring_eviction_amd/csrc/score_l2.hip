@@ -225,6 +225,7 @@ static_assert(kFuseThreads % 64 == 0 && kMemberGroups <= kRowGroups, "fused tile
 // launch: ~28 ms with the back-off, far above a wait among resident workgroups (~10 us).
 constexpr uint32_t kSpinLimit = 1u << 16;
 constexpr int64_t kRepairGrid = 256;  // workgroups of the repair launch
+constexpr int64_t kEarlyMembers = 32;  // teams of this many tiles or more publish early
 
 struct FuseGeom {
     int64_t G, S, W, nwin;
@@ -359,7 +360,7 @@ constexpr uint32_t kPending = 0x7fffffffu;  // not written yet
 constexpr uint32_t kFailed = 0xffffffffu;   // the team's gather gave up; the repair launch
                                             // recomputes the team
 
-template <int kMetric>
+template <int kMetric, bool kEarly>
 __global__ __launch_bounds__(kFuseThreads, KVC_FUSE_MINBLOCKS) void l2_fused(const uint16_t *__restrict__ K, FuseGeom geo,
                                                          uint32_t *partial, uint32_t *mu_pub,
                                                          uint32_t *repair, uint32_t *status,
@@ -518,7 +519,7 @@ __global__ __launch_bounds__(kFuseThreads, KVC_FUSE_MINBLOCKS) void l2_fused(con
                                __HIP_MEMORY_SCOPE_AGENT);
         }
         __syncthreads();  // red is reused
-        if (t.member == t.team % geo.members) agg_ok = gather_mu(t);
+        if (!kEarly && t.member == t.team % geo.members) agg_ok = gather_mu(t);
     };
     // The other members poll the published centroid (bounded like the gather).
     auto poll_mu = [&](const TileGeo &t) -> bool {
@@ -581,29 +582,62 @@ __global__ __launch_bounds__(kFuseThreads, KVC_FUSE_MINBLOCKS) void l2_fused(con
 
     const int64_t step = gridDim.x;
     int64_t tile = blockIdx.x;
-    // Two tiles per workgroup: while tile `tile` waits for its team's centroid and is
-    // scored, every load of the next tile is already in flight; its partial is
-    // published right after.  (Requesting half of the next tile before the wait and
-    // half after it: 0.273 vs 0.267 ms per scoring call at 256 x 16384.)
+    // Two tiles per workgroup (the current one and the next).
     uint4 v[kFuseRows], vn[kFuseRows];
-    if (tile < geo.tiles) {
-        const TileGeo t = geo_of(tile);
-        load_tile(t, v);
-        publish(tile, t, v);
-    }
-    for (; tile < geo.tiles; tile += step) {
-        const TileGeo t = geo_of(tile);
-        const int64_t next = tile + step;
-        TileGeo tn;
-        if (next < geo.tiles) {
-            tn = geo_of(next);
-            load_tile(tn, vn);
+    if constexpr (kEarly) {
+        // Large teams: a tile's partial is published as soon as its keys are in, before
+        // the workgroup waits for the current tile's centroid, and the aggregator
+        // gathers after scoring (holding one tile).  Rounds overlap: the next
+        // centroid no longer waits for the current one to be scored first
+        // (scoring call at 256 x 16384: 0.248 -> 0.239 ms; with 16-tile teams,
+        // 256 x 65536 in 4096-token windows, 0.893 -> 0.934 ms, so smaller teams
+        // keep the order below).
+        if (tile < geo.tiles) {
+            const TileGeo t = geo_of(tile);
+            load_tile(t, v);
+            publish(tile, t, v);
+            if (t.member == t.team % geo.members) agg_ok = gather_mu(t);
         }
-        const bool ok = fetch_mu(t);
-        score_tile(t, v, ok);
-        if (next < geo.tiles) publish(next, tn, vn);
+        for (; tile < geo.tiles; tile += step) {
+            const TileGeo t = geo_of(tile);
+            const int64_t next = tile + step;
+            TileGeo tn;
+            if (next < geo.tiles) {
+                tn = geo_of(next);
+                load_tile(tn, vn);
+                publish(next, tn, vn);
+            }
+            const bool ok = fetch_mu(t);
+            score_tile(t, v, ok);
+            if (next < geo.tiles && tn.member == tn.team % geo.members) agg_ok = gather_mu(tn);
 #pragma unroll
-        for (int r = 0; r < kFuseRows; ++r) v[r] = vn[r];
+            for (int r = 0; r < kFuseRows; ++r) v[r] = vn[r];
+        }
+    } else {
+        // While tile `tile` waits for its team's centroid and is scored, every load of
+        // the next tile is already in flight; its partial is published right after
+        // (the aggregator gathers in publish).  Requesting half of the next tile
+        // before the wait and half after it: 0.273 vs 0.267 ms per scoring call at
+        // 256 x 16384.
+        if (tile < geo.tiles) {
+            const TileGeo t = geo_of(tile);
+            load_tile(t, v);
+            publish(tile, t, v);
+        }
+        for (; tile < geo.tiles; tile += step) {
+            const TileGeo t = geo_of(tile);
+            const int64_t next = tile + step;
+            TileGeo tn;
+            if (next < geo.tiles) {
+                tn = geo_of(next);
+                load_tile(tn, vn);
+            }
+            const bool ok = fetch_mu(t);
+            score_tile(t, v, ok);
+            if (next < geo.tiles) publish(next, tn, vn);
+#pragma unroll
+            for (int r = 0; r < kFuseRows; ++r) v[r] = vn[r];
+        }
     }
 }
 
@@ -792,8 +826,9 @@ kvc_status score_windowed_impl(const uint16_t *K, int64_t G, int64_t S, int32_t 
     if (ws_bytes < score_bytes(G, S, W)) return KVC_ERR_WORKSPACE_TOO_SMALL;
 
     const FuseGeom f = make_fuse_geom(G, S, W, metric);
-    const void *fused = metric == kMetricCosine ? reinterpret_cast<const void *>(&l2_fused<kMetricCosine>)
-                                                : reinterpret_cast<const void *>(&l2_fused<kMetricL2>);
+    // occupancy of the single-read kernel (both loop orders compile to the same budget)
+    const void *fused = metric == kMetricCosine ? reinterpret_cast<const void *>(&l2_fused<kMetricCosine, false>)
+                                                : reinterpret_cast<const void *>(&l2_fused<kMetricL2, false>);
     static std::atomic<int64_t> capacity_by_dev[2][64];  // capacity + 1; 0: not queried yet
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return KVC_ERR_HIP;
@@ -829,14 +864,27 @@ kvc_status score_windowed_impl(const uint16_t *K, int64_t G, int64_t S, int32_t 
         // recomputed by the repair launch), and a cooperative launch costs ~16 us more
         // per call (scoring call at 256 x 16384: 0.264 vs 0.248 ms).
         const int64_t rgrid = f.teams < kRepairGrid ? f.teams : kRepairGrid;
+        const bool early = f.members >= kEarlyMembers;
         if (metric == kMetricCosine) {
-            hipLaunchKernelGGL(l2_fused<kMetricCosine>, dim3(static_cast<unsigned>(grid)), dim3(kFuseThreads), 0,
-                               stream, K, fa, partial, mu_pub, repair, status, scores, mu_user);
+            if (early)
+                hipLaunchKernelGGL((l2_fused<kMetricCosine, true>), dim3(static_cast<unsigned>(grid)),
+                                   dim3(kFuseThreads), 0, stream, K, fa, partial, mu_pub, repair, status, scores,
+                                   mu_user);
+            else
+                hipLaunchKernelGGL((l2_fused<kMetricCosine, false>), dim3(static_cast<unsigned>(grid)),
+                                   dim3(kFuseThreads), 0, stream, K, fa, partial, mu_pub, repair, status, scores,
+                                   mu_user);
             hipLaunchKernelGGL(l2_repair<kMetricCosine>, dim3(static_cast<unsigned>(rgrid)), dim3(kFuseThreads), 0,
                                stream, K, fa, repair, status, scores, mu_user);
         } else {
-            hipLaunchKernelGGL(l2_fused<kMetricL2>, dim3(static_cast<unsigned>(grid)), dim3(kFuseThreads), 0,
-                               stream, K, fa, partial, mu_pub, repair, status, scores, mu_user);
+            if (early)
+                hipLaunchKernelGGL((l2_fused<kMetricL2, true>), dim3(static_cast<unsigned>(grid)),
+                                   dim3(kFuseThreads), 0, stream, K, fa, partial, mu_pub, repair, status, scores,
+                                   mu_user);
+            else
+                hipLaunchKernelGGL((l2_fused<kMetricL2, false>), dim3(static_cast<unsigned>(grid)),
+                                   dim3(kFuseThreads), 0, stream, K, fa, partial, mu_pub, repair, status, scores,
+                                   mu_user);
             hipLaunchKernelGGL(l2_repair<kMetricL2>, dim3(static_cast<unsigned>(rgrid)), dim3(kFuseThreads), 0,
                                stream, K, fa, repair, status, scores, mu_user);
         }
