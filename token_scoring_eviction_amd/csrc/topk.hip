@@ -10,7 +10,9 @@
 //   - radix select, 8 bits per pass from the top: per-wave LDS histograms of
 //     the keys that still match the prefix, then a 256-bin suffix scan finds
 //     the digit holding the k-th largest key; after 4 passes the threshold
-//     key T is exact and `need` = how many keys equal to T are kept;
+//     key T is exact and `need` = how many keys equal to T are kept.  The
+//     passes stop early when the chosen bin holds exactly the keys still
+//     needed: all of them are kept, and the lower digits cannot change the set;
 //   - slices of up to 16 x 4096 scores are read once: each thread keeps its
 //     keys in registers for the four passes and the ordered pass (longer
 //     slices read the scores again at every pass);
@@ -89,7 +91,7 @@ __global__ __launch_bounds__(kSelThreads) void select_compact(const float *__res
 
     __shared__ uint32_t hist[kSelWaves][256];
     __shared__ uint32_t suffix[257];
-    __shared__ uint32_t sel[2];
+    __shared__ uint32_t sel[3];
     __shared__ uint32_t wtot[2 * kSelWaves];
 
     const int wave = threadIdx.x >> 6;
@@ -202,6 +204,7 @@ __global__ __launch_bounds__(kSelThreads) void select_compact(const float *__res
             if (here >= remaining && above < remaining) {
                 sel[0] = threadIdx.x;
                 sel[1] = above;
+                sel[2] = here - above;  // keys in the chosen bin
             }
         }
         __syncthreads();
@@ -209,10 +212,19 @@ __global__ __launch_bounds__(kSelThreads) void select_compact(const float *__res
         remaining -= sel[1];
         prefix |= digit << shift;
         mask |= 255u << shift;
+        const bool whole_bin = sel[2] == remaining;
         __syncthreads();
+        // every key of the chosen bin is kept: the lower digits cannot change the set
+        // (the k-th largest key is the bin's smallest, and keys equal to it share the
+        // bin), so the passes left are skipped (uniform across the block)
+        if (whole_bin) break;
     }
-    const uint32_t T = prefix;      // key of the k-th largest score
-    const uint32_t need = remaining;  // keys equal to T that are kept (>= 1)
+    // The kept keys are those whose masked key is above the prefix, and of the keys
+    // whose masked key equals it the first `need` in index order (all of them when
+    // the passes stopped at a whole bin).  With all four passes the mask covers the
+    // whole key and the prefix is the key of the k-th largest score.
+    const uint32_t T = prefix;
+    const uint32_t need = remaining;  // keys at the prefix that are kept (>= 1)
 
     uint32_t out_pos = 0;  // kept so far (uniform across the block)
     uint32_t eq_seen = 0;  // keys equal to T seen so far
@@ -223,8 +235,8 @@ __global__ __launch_bounds__(kSelThreads) void select_compact(const float *__res
 #pragma unroll
         for (int j = 0; j < kPerThread; ++j) {
             const int64_t i = i0 + j;
-            n_gt += (i < S && keys[j] > T);
-            n_eq += (i < S && keys[j] == T);
+            n_gt += (i < S && (keys[j] & mask) > T);
+            n_eq += (i < S && (keys[j] & mask) == T);
         }
         uint32_t tot;
         const uint32_t excl = block_exclusive_scan((n_gt << 16) | n_eq, wtot, &tot);
@@ -238,10 +250,10 @@ __global__ __launch_bounds__(kSelThreads) void select_compact(const float *__res
             if (i >= S) break;
             // pos < k holds by construction (exactly k keys are kept); the
             // test only keeps a write inside the slice's output row regardless
-            if (keys[j] > T) {
+            if ((keys[j] & mask) > T) {
                 if (pos < k) out[pos] = static_cast<int32_t>(i);
                 ++pos;
-            } else if (keys[j] == T) {
+            } else if ((keys[j] & mask) == T) {
                 if (eq_rank < need) {
                     if (pos < k) out[pos] = static_cast<int32_t>(i);
                     ++pos;
