@@ -33,15 +33,18 @@
  *          "method details", and appendix A.1 (Algorithm 1), A.4, A.9.
  *
  * Parity status: every function here is pinned by CPU tests against closed
- * forms, invariants, exact-rational brute force or a library routine, with two
- * exceptions.  The decode-time re-projection reading used by the full-loop
- * driver lives in the Python wrapper and is marked "parity unpinned" there.
- * ora_refine_risk is "parity unpinned" relative to the page in its readings:
- * the page names the attention-mass and logit-deviation terms without formulas,
- * and under the readings taken here RC is not an upper bound of the
- * single-cluster replacement error in general.  Its arithmetic is pinned: closed
- * forms, and a worked example of the printed Figure 2 formula evaluated in
- * 60-digit decimals under the same readings.
+ * forms, invariants, exact-rational brute force or a library routine.  The
+ * decode-time re-projection reading used by the full-loop driver lives in the
+ * Python wrapper and is marked "parity unpinned" there.  ora_refine_risk takes
+ * readings of the attention-mass and logit-deviation terms, which the page names
+ * without formulas; they are pinned by what the page says the scores are, the
+ * cluster-wise terms of an upper bound on the attention-output error: the sum of
+ * the clusters' RC bounds the error of attending with every cluster replaced by
+ * its size-weighted representative (random and adversarial instances; a reading
+ * that makes RC too small fails).  RC is not a bound of a single cluster's
+ * replacement error, which the page only correlates with it.  Its arithmetic is
+ * pinned by closed forms and a worked example of the printed Figure 2 formula
+ * evaluated in 60-digit decimals.
  */
 #include <math.h>
 #include <stdint.h>

@@ -2,10 +2,13 @@
 project page: "Summarize" -- contiguous clusters with mean keys, mean values and
 metadata -- and the Figure 2 formula RC = 2 p Vmax [(cosh d - 1)/Dn + tanh(d/2)]).
 Summaries are pinned against numpy (means, norms); the risk score against closed
-forms.  The page leaves p (share of attention mass) and d (logit-deviation bound)
-without formulas: their readings are the oracle's, so RC is parity unpinned
-relative to the pages beyond these closed forms (in particular RC is not checked
-to bound the single-cluster replacement error)."""
+forms, and against what the page says the scores are: the cluster-wise terms of an
+upper bound on the attention-output error.  The page leaves p (share of attention
+mass) and d (logit-deviation bound) without formulas; under the oracle's readings
+the sum of the clusters' RC bounds the error of attending with every cluster
+replaced by its size-weighted representative (mean key, mean value), checked on
+random and adversarial instances (not proven here).  RC is not checked to bound the
+single-cluster replacement error, which the page only correlates with it."""
 import numpy as np
 import pytest
 from scipy.special import softmax
@@ -82,3 +85,74 @@ def test_equal_radii_share_the_mass_by_softmax():
         scale = 2.0 * vmax * ((np.cosh(d) - 1.0) / np.cosh(d) + np.tanh(d / 2.0))
         np.testing.assert_allclose(rc[0, i], p * scale, rtol=1e-11)
         assert rc[0, i].sum() == pytest.approx(scale, rel=1e-12)
+
+
+def _bf16_rne(a):
+    u = np.ascontiguousarray(a, np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def _representative_error(K, V, Q, mk, mv, S, c):
+    """||o - o'|| per query: exact attention output against the output with every
+    cluster replaced by its mean key and mean value, weighted by its size."""
+    Kf, Vf, Qf = oracle.bf16_to_f64(K)[0], oracle.bf16_to_f64(V)[0], oracle.bf16_to_f64(Q)[0]
+    D = Kf.shape[1]
+    n = np.array([min(c, S - j * c) for j in range(mk.shape[1])], np.float64)
+    out = []
+    for q in Qf:
+        o = softmax(Kf @ q / np.sqrt(D)) @ Vf
+        o2 = softmax(mk[0] @ q / np.sqrt(D) + np.log(n)) @ mv[0]
+        out.append(np.linalg.norm(o - o2))
+    return np.array(out)
+
+
+def test_risk_scores_sum_to_a_bound_of_the_representative_error():
+    # the page derives RC from an upper bound on attention-output error and uses its
+    # cluster-wise terms as risk scores: with every cluster replaced by its
+    # representative, the error must not exceed sum_C RC_C.  Random caches, and
+    # adversarial ones where the bound is nearly attained: two-point clusters, values
+    # following the key deviations, a query along the deviations, and one cluster of
+    # large values beside spread-out clusters of small values.  A reading that makes
+    # RC too small fails here: d with an extra 1/sqrt(d) or halved, Vmax taken per
+    # cluster or as the mean value norm (checked when this test was written)
+    rng = np.random.default_rng(2026)
+    worst = 0.0
+    for trial in range(1500):
+        D = 16
+        nC = int(rng.integers(1, 6))
+        c = int(rng.integers(2, 12))
+        S = max(1, nC * c - int(rng.integers(0, c)))
+        kind = trial % 5
+        base = rng.normal(0.0, float(rng.choice([0.5, 2.0, 6.0])), (nC, D))
+        big = int(rng.integers(0, nC))
+        K = np.zeros((1, S, D))
+        V = np.zeros((1, S, D))
+        for t in range(S):
+            C, sign = t // c, (1.0 if t % 2 == 0 else -1.0)
+            if kind == 0:
+                K[0, t] = base[C] + sign * rng.normal(0.0, 1.0, D) * float(rng.choice([0.5, 2.0, 5.0]))
+            elif kind == 1:
+                K[0, t] = base[C] + rng.normal(0.0, float(rng.choice([0.1, 1.0, 4.0])), D)
+            elif kind == 4:
+                K[0, t] = base[C] + (0.0 if C == big else sign * float(rng.choice([1.0, 3.0])))
+            else:
+                K[0, t] = base[C] + sign * float(rng.choice([0.3, 1.0, 3.0]))
+            if kind == 4:
+                V[0, t] = (20.0 if C == big else 0.05) * rng.normal(0.0, 1.0, D)
+            else:
+                V[0, t] = (K[0, t] - base[C]) if kind >= 2 else rng.normal(0.0, 1.0, D)
+        Q = rng.normal(0.0, float(rng.choice([0.1, 0.5, 1.5])), (1, 2, D))
+        if kind in (3, 4):
+            Q[0, 0] = float(rng.choice([0.2, 1.0]))
+        Kb, Vb, Qb = _bf16_rne(K), _bf16_rne(V), _bf16_rne(Q)
+        mk, mv, rad, vn = oracle.cluster_summaries(Kb, Vb, c)
+        bound = oracle.refine_risk(mk, rad, vn, S, c, Qb)[0].sum(axis=1)
+        err = _representative_error(Kb, Vb, Qb, mk, mv, S, c)
+        # a bound of 0 (no spread) leaves only rounding in the error
+        tol = 1e-12 * vn.max()
+        assert np.all(err <= bound * (1 + 1e-12) + tol), (trial, err, bound)
+        ratio = np.where(bound > 1e-9 * vn.max(), err / np.maximum(bound, 1e-300), 0.0)
+        worst = max(worst, float(ratio.max()))
+    # the check is tight enough to see a risk score half as large (a dropped factor,
+    # or d or Vmax read too small by that much)
+    assert worst > 0.5
