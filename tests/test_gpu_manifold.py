@@ -26,9 +26,12 @@ def _scores_vs_oracle(K, gpu_scores, W=None):
 
 
 # path "0": the single-read kernel, "1": the three-launch path (caches under 12 MiB
-# take the latter by default); chosen with the score_path option
+# take the latter by default); chosen with the score_path option.  Slices of more
+# than 64 tiles (16384 tokens) split the centroid gather over 2, 4, ... aggregators:
+# 40000 tokens are 157 tiles (4 aggregators), 131149 are 513 (16)
 @pytest.mark.parametrize("path", ["0", "1"])
-@pytest.mark.parametrize("G,S", [(1, 1), (3, 257), (2, 1000), (4, 4096), (1, 16384 + 77)])
+@pytest.mark.parametrize("G,S", [(1, 1), (3, 257), (2, 1000), (4, 4096), (1, 16384 + 77), (2, 40000),
+                                 (1, 131072 + 77)])
 def test_score_l2_small(gpu_lib, kvc_option, G, S, path):
     kvc_option("score_path", 1 + int(path))
     K, _, _ = synth.manifold_global(1, 1, G, S, planted=min(4, S), seed=S, device=DEV)
@@ -250,6 +253,36 @@ def test_expired_centroid_waits_are_repaired_bit_exactly(gpu_lib, kvc_option, me
     assert not torch.isnan(ref).any()
     assert torch.equal(rep, ref) and torch.equal(rep_mu, ref_mu)
     assert torch.equal(again, ref)
+
+
+@pytest.mark.parametrize("G,S,W,metric", [(4, 40000, None, "l2"), (4, 40000, None, "cosine"),
+                                          (2, 131072 + 300, None, "l2"), (4, 70000, 33000, "l2")])
+def test_multi_aggregator_teams_repair_bit_exactly(gpu_lib, kvc_option, G, S, W, metric):
+    # teams of more than 64 tiles gather their centroid with several aggregators, each
+    # owning a block of channels (4 for the 157-tile slices of 40000 tokens and the
+    # 129-tile windows of 33000, 16 for the 514-tile slices of 131372).  The scores match
+    # the oracle, and a run whose waits all give up is repaired to the same bits: the
+    # repair launch adds the tile sums in the member groups the aggregators use
+    K, _, _ = synth.manifold_global(1, 1, G, S, planted=8, seed=S % 1000, device=DEV)
+    kvc_option("score_path", 1)
+    nwin = 1 if W is None else -(-S // W)
+
+    def score():
+        mu = torch.empty((G, nwin, 128), dtype=torch.float32, device=DEV)
+        sc = gpu_lib.kvc_score_centroid(K, W=W, metric=metric, centroids=mu)
+        return sc.clone(), mu
+
+    ref, ref_mu = score()
+    torch.cuda.synchronize()
+    if metric == "l2":
+        _scores_vs_oracle(K, ref, W)
+    kvc_option("score_spin_limit", 0)
+    rep, rep_mu = score()
+    gpu_lib.kvc_workspace_status()
+    kvc_option("score_spin_limit", -1)
+    torch.cuda.synchronize()
+    assert not torch.isnan(ref).any()
+    assert torch.equal(rep, ref) and torch.equal(rep_mu, ref_mu)
 
 
 def test_scoring_beside_another_kernel_is_bit_identical(gpu_lib, kvc_option):

@@ -15,11 +15,13 @@
 //     keeps its tile in registers (16 rows x 8 channels per thread, 16-byte
 //     coalesced loads).
 //   - Each workgroup publishes its tile's fp32 column sums with coherent stores
-//     and goes on without waiting for them.  One member of the team (member
-//     team mod members, so the role rotates) polls the team's partial words
-//     until all are written -- they are set before the launch to a pattern no
-//     sum can take -- adds them in tile order (deterministic), divides by the
-//     window length and publishes the centroid words; the others poll those.
+//     and goes on without waiting for them.  An aggregator of the team (one per
+//     64 tiles, rounded up to a power of two, each owning a block of channels;
+//     the roles rotate over the team's workgroups) polls its channels of the
+//     team's partial words until all are written -- they are set before the
+//     launch to a pattern no sum can take -- adds them in a fixed order of tile
+//     groups (deterministic), divides by the window length and publishes its
+//     centroid words; the members poll those.
 //   - Every workgroup then scores its rows from registers.  Two tiles are in
 //     flight per workgroup: every load of the next tile is issued before the
 //     workgroup waits for the current tile's centroid, and the next tile's
@@ -219,8 +221,13 @@ constexpr int kFuseThreads = KVC_FUSE_THREADS;                // a multiple of 6
 constexpr int kRowGroups = kFuseThreads / 16;                 // 16 lanes per key row
 constexpr int kFuseRows = KVC_FUSE_ROWS;                      // rows per thread (8 or 16)
 constexpr int kFuseTile = kRowGroups * kFuseRows;             // tokens per tile
-constexpr int kMemberGroups = kFuseThreads / 32;              // 32 channel groups of 4 each
+constexpr int kMemberGroups = kFuseThreads / 32;              // member groups per aggregator with
+                                                              // all 32 channel groups of 4
+constexpr int kGatherDepth = 8;                               // members in flight per gathering thread
+constexpr int kMaxAggShift = 5;                               // at most 32 aggregators per team
 static_assert(kFuseThreads % 64 == 0 && kMemberGroups <= kRowGroups, "fused tile shape");
+static_assert(kRowGroups * (kHeadDim + 4) >= (kMemberGroups << kMaxAggShift) * ((kHeadDim >> kMaxAggShift) + 4),
+              "the gather's group sums fit the reduction buffer");
 // Polls of a centroid wait before it gives up and leaves the team to the repair
 // launch: ~28 ms with the back-off, far above a wait among resident workgroups (~10 us).
 constexpr uint32_t kSpinLimit = 1u << 16;
@@ -233,6 +240,8 @@ struct FuseGeom {
     int64_t members;  // tiles per window
     int64_t teams;    // G * nwin
     int64_t tiles;    // teams * members
+    int agg_shift;    // log2 of the aggregators per team (each owns 128 >> agg_shift channels)
+    int64_t per;      // members per member group: kMemberGroups << agg_shift groups per team
     uint32_t spin_limit;  // polls of a centroid wait before it gives up (kSpinLimit)
 };
 
@@ -413,18 +422,34 @@ __global__ __launch_bounds__(kFuseThreads, KVC_FUSE_MINBLOCKS) void l2_fused(con
         else __builtin_amdgcn_s_sleep(16);
         nap = nap < 16 ? nap * 2 : 16;
     };
-    // The aggregator of a team polls the team's partials
-    // until every word is written, adds them in tile order (32 channel groups of 4 x
-    // kMemberGroups member groups, 8 members of a group in flight per thread, then
-    // the groups in order), divides by the window's length and publishes the
-    // centroid.  The wait is bounded: past the limit it publishes kFailed in every
-    // channel, flags the team for the repair launch and returns false.  The centroid
-    // is left in mu_s for the aggregator's own scoring of the tile.
-    auto gather_mu = [&](const TileGeo &t) -> bool {
-        const int cg = tid & 31, mg = tid >> 5;
-        const int64_t per = (geo.members + kMemberGroups - 1) / kMemberGroups;
-        const int64_t m0 = mg * per, m1 = min(geo.members, m0 + per);
-        const uint64_t *p = reinterpret_cast<const uint64_t *>(partial + t.team * geo.members * kHeadDim) + cg * 2;
+    // A team has A = 1 << agg_shift aggregators (one while the team has at most 64
+    // tiles): members (team + a * members / A) mod members, a = 0 .. A-1, so the roles
+    // rotate over the team's workgroups from round to round.  Returns a, or -1.
+    auto agg_of = [&](const TileGeo &t) -> int {
+        const int64_t d = (t.member - t.team % geo.members + geo.members) % geo.members;
+        const int64_t step = geo.members >> geo.agg_shift;
+        if (d % step != 0) return -1;
+        const int64_t a = d / step;
+        return a < (1 << geo.agg_shift) ? static_cast<int>(a) : -1;
+    };
+    // Aggregator a owns channels [a, a + 1) * 128 / A of the centroid.  It polls those
+    // channels of the team's partials until every word is written and adds them in
+    // tile order: the team's tiles fall into kMemberGroups * A member groups of `per`
+    // consecutive tiles (per <= 8, so each thread requests its whole group in one
+    // poll), a group's tiles are added in order, then the groups in order.  It divides
+    // by the window's length and publishes its channels.  The wait is bounded: past
+    // the limit it publishes kFailed in its channels, flags the team for the repair
+    // launch and returns false.  Its channels of the centroid are left in mu_s (all of
+    // it when A = 1, for the aggregator's own scoring of the tile).
+    auto gather_mu = [&](const TileGeo &t, int a) -> bool {
+        const int sh = geo.agg_shift;
+        const int chans = kHeadDim >> sh;      // this aggregator's channels
+        const int stride = chans + 4;          // of a member group's row in red
+        const int cg = tid & ((32 >> sh) - 1);  // channel group of 4
+        const int mg = tid >> (5 - sh);         // member group, 0 .. kMemberGroups * A - 1
+        const int64_t m0 = mg * geo.per, m1 = min(geo.members, m0 + geo.per);
+        const uint64_t *p =
+            reinterpret_cast<const uint64_t *>(partial + t.team * geo.members * kHeadDim + a * chans) + cg * 2;
         float sx = 0.f, sy = 0.f, sz = 0.f, sw = 0.f;
         bool failed = false;
         uint32_t spins = 0;
@@ -466,39 +491,41 @@ __global__ __launch_bounds__(kFuseThreads, KVC_FUSE_MINBLOCKS) void l2_fused(con
                 sw += __uint_as_float(static_cast<uint32_t>(x[u][1] >> 32));
             }
         };
-        // chunks of 8, 4, 2, 1 members: every member of a thread's range is requested in
-        // one poll when the range is 8 long or a power of two below 8
+        // chunks of 8, 4, 2, 1 members: a group of 8 or of a power of two below 8 is
+        // requested in one poll
+        static_assert(kGatherDepth == 8, "the chunk ladder below starts at 8");
         int64_t m = m0;
         for (; m + 8 <= m1 && !failed; m += 8) take(m, std::integral_constant<int, 8>());
         if (m + 4 <= m1 && !failed) { take(m, std::integral_constant<int, 4>()); m += 4; }
         if (m + 2 <= m1 && !failed) { take(m, std::integral_constant<int, 2>()); m += 2; }
         if (m < m1 && !failed) take(m, std::integral_constant<int, 1>());
-        red[mg][cg * 4 + 0] = sx;
-        red[mg][cg * 4 + 1] = sy;
-        red[mg][cg * 4 + 2] = sz;
-        red[mg][cg * 4 + 3] = sw;
+        float *rf = &red[0][0];
+        rf[mg * stride + cg * 4 + 0] = sx;
+        rf[mg * stride + cg * 4 + 1] = sy;
+        rf[mg * stride + cg * 4 + 2] = sz;
+        rf[mg * stride + cg * 4 + 3] = sw;
         const bool any_failed = __syncthreads_or(failed);
-        if (tid < kHeadDim) {
+        if (tid < chans) {
             uint32_t w = kFailed;
             float mu = __int_as_float(0x7fc00000);
             if (!any_failed) {
                 float sum = 0.f;
-#pragma unroll
-                for (int q = 0; q < kMemberGroups; ++q) sum += red[q][tid];
+                for (int q = 0; q < (kMemberGroups << sh); ++q) sum += rf[q * stride + tid];
                 mu = sum / static_cast<float>(t.w1 - t.w0);
                 w = __float_as_uint(mu);
             }
-            if (mu_user) mu_user[t.team * kHeadDim + tid] = mu;
-            __hip_atomic_store(mu_pub + t.team * kHeadDim + tid, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            mu_s[tid] = __uint_as_float(w);
+            const int ch = a * chans + tid;
+            if (mu_user) mu_user[t.team * kHeadDim + ch] = mu;
+            __hip_atomic_store(mu_pub + t.team * kHeadDim + ch, w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            mu_s[ch] = __uint_as_float(w);
         }
         if (any_failed) flag_repair(t);
         __syncthreads();  // red and mu_s
         return !any_failed;
     };
     // Column sums of the tile -> the tile's partial words (32-bit coherent stores,
-    // nothing waited for).  The team's aggregator (member team mod members) then
-    // gathers the team's centroid, while it holds only this tile.
+    // nothing waited for).  A team's aggregator then gathers its channels of the
+    // centroid, while it holds only this tile.
     auto publish = [&](int64_t tile, const TileGeo &t, const uint4 *v) {
         float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -519,9 +546,13 @@ __global__ __launch_bounds__(kFuseThreads, KVC_FUSE_MINBLOCKS) void l2_fused(con
                                __HIP_MEMORY_SCOPE_AGENT);
         }
         __syncthreads();  // red is reused
-        if (!kEarly && t.member == t.team % geo.members) agg_ok = gather_mu(t);
+        if constexpr (!kEarly) {
+            const int a = agg_of(t);
+            if (a >= 0) agg_ok = gather_mu(t, a);
+        }
     };
-    // The other members poll the published centroid (bounded like the gather).
+    // The other members, and every member when a team has several aggregators, poll
+    // the published centroid (bounded like the gather).
     auto poll_mu = [&](const TileGeo &t) -> bool {
         uint32_t spins = 0;
         int nap = 1;
@@ -543,7 +574,7 @@ __global__ __launch_bounds__(kFuseThreads, KVC_FUSE_MINBLOCKS) void l2_fused(con
         return !__syncthreads_or(tid < kHeadDim && __float_as_uint(mu_s[tid]) == kFailed);
     };
     auto fetch_mu = [&](const TileGeo &t) -> bool {
-        return t.member == t.team % geo.members ? agg_ok : poll_mu(t);
+        return geo.agg_shift == 0 && agg_of(t) == 0 ? agg_ok : poll_mu(t);
     };
 
     // Scores tile `t` (held in v) once its team's centroid is published.  Without a
@@ -596,7 +627,8 @@ __global__ __launch_bounds__(kFuseThreads, KVC_FUSE_MINBLOCKS) void l2_fused(con
             const TileGeo t = geo_of(tile);
             load_tile(t, v);
             publish(tile, t, v);
-            if (t.member == t.team % geo.members) agg_ok = gather_mu(t);
+            const int a = agg_of(t);
+            if (a >= 0) agg_ok = gather_mu(t, a);
         }
         for (; tile < geo.tiles; tile += step) {
             const TileGeo t = geo_of(tile);
@@ -609,7 +641,10 @@ __global__ __launch_bounds__(kFuseThreads, KVC_FUSE_MINBLOCKS) void l2_fused(con
             }
             const bool ok = fetch_mu(t);
             score_tile(t, v, ok);
-            if (next < geo.tiles && tn.member == tn.team % geo.members) agg_ok = gather_mu(tn);
+            if (next < geo.tiles) {
+                const int a = agg_of(tn);
+                if (a >= 0) agg_ok = gather_mu(tn, a);
+            }
 #pragma unroll
             for (int r = 0; r < kFuseRows; ++r) v[r] = vn[r];
         }
@@ -662,7 +697,6 @@ __global__ __launch_bounds__(kFuseThreads) void l2_repair(const uint16_t *__rest
     const int rowg = tid >> 4;
     __shared__ float red[kRowGroups][kHeadDim + 4];
     __shared__ float mu_s[kHeadDim];
-    const int64_t per = (geo.members + kMemberGroups - 1) / kMemberGroups;
     for (int64_t team = blockIdx.x; team < geo.teams; team += gridDim.x) {
         if (repair[team] == 0u) continue;
         const int64_t g = team / geo.nwin;
@@ -672,9 +706,7 @@ __global__ __launch_bounds__(kFuseThreads) void l2_repair(const uint16_t *__rest
         // the centroid: tile column sums (rows t0 + 16 r of the thread's row group,
         // then the 16 row groups in order), member groups of `per` tiles added in
         // order, then the groups in order
-        float gs[kMemberGroups];
-#pragma unroll
-        for (int q = 0; q < kMemberGroups; ++q) gs[q] = 0.f;
+        float total = 0.f, group = 0.f;
         for (int64_t j = 0; j < geo.members; ++j) {
             const int64_t t0 = w0 + j * kFuseTile + rowg;
             float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
@@ -694,18 +726,16 @@ __global__ __launch_bounds__(kFuseThreads) void l2_repair(const uint16_t *__rest
                 float sum = 0.f;
 #pragma unroll
                 for (int r = 0; r < kRowGroups; ++r) sum += red[r][tid];
-                const int64_t q = j / per;
-#pragma unroll
-                for (int qq = 0; qq < kMemberGroups; ++qq)
-                    if (qq == q) gs[qq] += sum;
+                group += sum;
+                if ((j + 1) % geo.per == 0 || j + 1 == geo.members) {
+                    total += group;
+                    group = 0.f;
+                }
             }
             __syncthreads();  // red is reused
         }
         if (tid < kHeadDim) {
-            float sum = 0.f;
-#pragma unroll
-            for (int q = 0; q < kMemberGroups; ++q) sum += gs[q];
-            const float mu = sum / static_cast<float>(w1 - w0);
+            const float mu = total / static_cast<float>(w1 - w0);
             mu_s[tid] = mu;
             if (mu_user) mu_user[team * kHeadDim + tid] = mu;
         }
@@ -745,6 +775,12 @@ FuseGeom make_fuse_geom(int64_t G, int64_t S, int64_t W, int metric = kMetricL2)
     f.members = (f.W + kFuseTile - 1) / kFuseTile;
     f.teams = G * f.nwin;
     f.tiles = f.teams * f.members;
+    // one aggregator per 64 tiles of a team, rounded up to a power of two: each
+    // gathering thread then polls at most kGatherDepth tiles, in one request
+    int sh = 0;
+    while (sh < kMaxAggShift && f.members > (static_cast<int64_t>(kMemberGroups * kGatherDepth) << sh)) ++sh;
+    f.agg_shift = sh;
+    f.per = (f.members + (kMemberGroups << sh) - 1) / (kMemberGroups << sh);
     f.spin_limit = kSpinLimit;
     return f;
 }
