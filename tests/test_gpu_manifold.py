@@ -256,11 +256,13 @@ def test_expired_centroid_waits_are_repaired_bit_exactly(gpu_lib, kvc_option, me
 
 
 @pytest.mark.parametrize("G,S,W,metric", [(4, 40000, None, "l2"), (4, 40000, None, "cosine"),
-                                          (2, 131072 + 300, None, "l2"), (4, 70000, 33000, "l2")])
+                                          (2, 131072 + 300, None, "l2"), (3, 118016, None, "l2"),
+                                          (4, 70000, 33000, "l2")])
 def test_multi_aggregator_teams_repair_bit_exactly(gpu_lib, kvc_option, G, S, W, metric):
     # teams of more than 64 tiles gather their centroid with several aggregators, each
     # owning a block of channels (4 for the 157-tile slices of 40000 tokens and the
-    # 129-tile windows of 33000, 16 for the 514-tile slices of 131372).  The scores match
+    # 129-tile windows of 33000, 8 for the 461-tile slices of 118016, 16 for the
+    # 514-tile slices of 131372).  The scores match
     # the oracle, and a run whose waits all give up is repaired to the same bits: the
     # repair launch adds the tile sums in the member groups the aggregators use
     K, _, _ = synth.manifold_global(1, 1, G, S, planted=8, seed=S % 1000, device=DEV)
