@@ -291,6 +291,22 @@ __device__ __forceinline__ void row_transpose_reduce(float *v, int lane16) {
     }
 }
 
+// Lane r's value in every lane of its row group of 16 (a swizzle in bitmask mode:
+// lane' = (lane & 0x10) | r within each 32 lanes).
+template <int r>
+__device__ __forceinline__ float row_bcast(float a) {
+    return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(a), 0x10 | (r << 5)));
+}
+
+// f(integral_constant<int, r>) for r = R .. N-1, in order.
+template <int R, int N, class F>
+__device__ __forceinline__ void for_rows(F &&f) {
+    if constexpr (R < N) {
+        f(std::integral_constant<int, R>());
+        for_rows<R + 1, N>(f);
+    }
+}
+
 // Sum over the 16 lanes of a row group, the same bits in every lane (each
 // butterfly step adds a commuted pair).
 __device__ __forceinline__ float sum16(float a) {
@@ -318,22 +334,33 @@ __device__ __forceinline__ float lane_d2(const uint4 &w, const float *m) {
     }
     return acc;
 }
-__device__ __forceinline__ float row_cos(const uint4 &w, const float *m, float mm, float inv_m) {
+// The lane's part of ||k||^2 and, given the row's 1 / ||k||, of ||k/||k|| - mu/||mu||||^2.
+__device__ __forceinline__ float lane_kk(const uint4 &w) {
     float x[8];
     widen8(w, x);
     float kk = 0.f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) kk += x[j] * x[j];
-    kk = sum16(kk);
-    const float inv = kk > 0.f ? 1.f / sqrtf(kk) : 0.f;
+    return kk;
+}
+__device__ __forceinline__ float lane_e(const uint4 &w, float inv, const float *m, float inv_m) {
+    float x[8];
+    widen8(w, x);
     float e = 0.f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
         const float d = diff_of_products(x[j], inv, m[j], inv_m);
         e += d * d;
     }
-    e = sum16(e);
+    return e;
+}
+__device__ __forceinline__ float inv_norm(float kk) { return kk > 0.f ? 1.f / sqrtf(kk) : 0.f; }
+__device__ __forceinline__ float cos_score(float kk, float e, float mm) {
     return (kk > 0.f && mm > 0.f) ? 0.5f * e : 1.f;
+}
+__device__ __forceinline__ float row_cos(const uint4 &w, const float *m, float mm, float inv_m) {
+    const float kk = sum16(lane_kk(w));
+    return cos_score(kk, sum16(lane_e(w, inv_norm(kk), m, inv_m)), mm);
 }
 // ||mu||^2 over the row group's lanes (channels lane16*8 .. +8 in m) and 1/||mu||.
 __device__ __forceinline__ void centroid_norm(const float *m, float &mm, float &inv_m) {
@@ -585,7 +612,32 @@ __global__ __launch_bounds__(kFuseThreads, KVC_FUSE_MINBLOCKS) void l2_fused(con
         float m[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) m[j] = mu_s[lane16 * 8 + j];
-        if (kMetric == kMetricCosine) {
+        if (kMetric == kMetricCosine && kFuseRows == 16) {
+            // The 16 rows' ||k||^2 by one transpose-reduce (lane r holds row r's),
+            // 1 / ||k|| formed once per row in its lane and broadcast to the row
+            // group, then the 16 rows' ||k/||k|| - mu/||mu||||^2 by a second
+            // transpose-reduce.  The same pairings and per-row arithmetic as row_cos:
+            // the same bits.
+            float mm, inv_m;
+            centroid_norm(m, mm, inv_m);
+            float part[kFuseRows];
+#pragma unroll
+            for (int r = 0; r < kFuseRows; ++r) part[r] = lane_kk(v[r]);
+            row_transpose_reduce<kFuseRows>(part, lane16);
+            const float kk = part[0];
+            const float inv_mine = inv_norm(kk);
+            for_rows<0, kFuseRows>([&](auto rc) {
+                constexpr int r = decltype(rc)::value;
+                // widened again rather than kept from the first pass (128 more live
+                // registers otherwise): the empty asm hides that the bits are the same
+                uint4 w = v[r];
+                asm volatile("" : "+v"(w.x), "+v"(w.y), "+v"(w.z), "+v"(w.w));
+                part[r] = lane_e(w, row_bcast<r>(inv_mine), m, inv_m);
+            });
+            row_transpose_reduce<kFuseRows>(part, lane16);
+            const int64_t row = t.t0 + static_cast<int64_t>(kRowGroups) * lane16;
+            if (row < t.w1) scores[t.g * geo.S + row] = ok ? cos_score(kk, part[0], mm) : nan;
+        } else if (kMetric == kMetricCosine) {
             float mm, inv_m;
             centroid_norm(m, mm, inv_m);
             float mine = 0.f;
