@@ -27,8 +27,9 @@ def _scores_vs_oracle(K, gpu_scores, W=None):
 
 # path "0": the single-read kernel, "1": the three-launch path (caches under 12 MiB
 # take the latter by default); chosen with the score_path option.  Slices of more
-# than 64 tiles (16384 tokens) split the centroid gather over 2, 4, ... aggregators:
-# 40000 tokens are 157 tiles (4 aggregators), 131149 are 513 (16)
+# than 32 tiles (8192 tokens) split the centroid gather over 2, 4, ... aggregators:
+# 16461 tokens are 65 tiles (4 aggregators), 40000 are 157 (8), 131149 are 513 (16,
+# with 8 tiles per poll above 256 tiles)
 @pytest.mark.parametrize("path", ["0", "1"])
 @pytest.mark.parametrize("G,S", [(1, 1), (3, 257), (2, 1000), (4, 4096), (1, 16384 + 77), (2, 40000),
                                  (1, 131072 + 77)])
@@ -259,10 +260,11 @@ def test_expired_centroid_waits_are_repaired_bit_exactly(gpu_lib, kvc_option, me
                                           (2, 131072 + 300, None, "l2"), (3, 118016, None, "l2"),
                                           (4, 70000, 33000, "l2")])
 def test_multi_aggregator_teams_repair_bit_exactly(gpu_lib, kvc_option, G, S, W, metric):
-    # teams of more than 64 tiles gather their centroid with several aggregators, each
-    # owning a block of channels (4 for the 157-tile slices of 40000 tokens and the
-    # 129-tile windows of 33000, 8 for the 461-tile slices of 118016, 16 for the
-    # 514-tile slices of 131372).  The scores match
+    # teams of more than 32 tiles gather their centroid with several aggregators, each
+    # owning a block of channels (8 for the 157-tile slices of 40000 tokens and the
+    # 129-tile windows of 33000; above 256 tiles one per 64 tiles: 8 for the 461-tile
+    # slices of 118016, 16 for the 514-tile slices of 131372, whose member groups are
+    # 5 tiles long).  The scores match
     # the oracle, and a run whose waits all give up is repaired to the same bits: the
     # repair launch adds the tile sums in the member groups the aggregators use
     K, _, _ = synth.manifold_global(1, 1, G, S, planted=8, seed=S % 1000, device=DEV)

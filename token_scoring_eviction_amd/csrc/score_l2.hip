@@ -16,7 +16,7 @@
 //     coalesced loads).
 //   - Each workgroup publishes its tile's fp32 column sums with coherent stores
 //     and goes on without waiting for them.  An aggregator of the team (one per
-//     64 tiles, rounded up to a power of two, each owning a block of channels;
+//     32 tiles, rounded up to a power of two, each owning a block of channels;
 //     the roles rotate over the team's workgroups) polls its channels of the
 //     team's partial words until all are written -- they are set before the
 //     launch to a pattern no sum can take -- adds them in a fixed order of tile
@@ -223,7 +223,13 @@ constexpr int kFuseRows = KVC_FUSE_ROWS;                      // rows per thread
 constexpr int kFuseTile = kRowGroups * kFuseRows;             // tokens per tile
 constexpr int kMemberGroups = kFuseThreads / 32;              // member groups per aggregator with
                                                               // all 32 channel groups of 4
-constexpr int kGatherDepth = 8;                               // members in flight per gathering thread
+// Tiles a gathering thread requests per poll: 4 for teams of up to kDeepTeam tiles,
+// 8 above (fewer aggregators for large teams).  Scoring call, depth 4 vs 8 on one
+// box: 256 x 16384 0.238-0.240 vs 0.244-0.249 ms, 256 x 32768 0.445 vs 0.458 ms,
+// 256 x 65536 tied at 0.94 ms, 256 x 98304 1.63-1.64 vs 1.54-1.56 ms, 256 x 131072
+// 2.50 vs 2.37-2.40 ms.  (Depth 2: 0.240 ms and 0.452 ms at the first two.)
+constexpr int kGatherDepthSmall = 4, kGatherDepthLarge = 8;
+constexpr int64_t kDeepTeam = 256;
 constexpr int kMaxAggShift = 5;                               // at most 32 aggregators per team
 static_assert(kFuseThreads % 64 == 0 && kMemberGroups <= kRowGroups, "fused tile shape");
 static_assert(kRowGroups * (kHeadDim + 4) >= (kMemberGroups << kMaxAggShift) * ((kHeadDim >> kMaxAggShift) + 4),
@@ -242,6 +248,7 @@ struct FuseGeom {
     int64_t tiles;    // teams * members
     int agg_shift;    // log2 of the aggregators per team (each owns 128 >> agg_shift channels)
     int64_t per;      // members per member group: kMemberGroups << agg_shift groups per team
+    int depth;        // tiles per gathering poll (kGatherDepthSmall or kGatherDepthLarge)
     uint32_t spin_limit;  // polls of a centroid wait before it gives up (kSpinLimit)
 };
 
@@ -396,7 +403,7 @@ constexpr uint32_t kPending = 0x7fffffffu;  // not written yet
 constexpr uint32_t kFailed = 0xffffffffu;   // the team's gather gave up; the repair launch
                                             // recomputes the team
 
-template <int kMetric, bool kEarly>
+template <int kMetric, bool kEarly, int kGatherDepth>
 __global__ __launch_bounds__(kFuseThreads, KVC_FUSE_MINBLOCKS) void l2_fused(const uint16_t *__restrict__ K, FuseGeom geo,
                                                          uint32_t *partial, uint32_t *mu_pub,
                                                          uint32_t *repair, uint32_t *status,
@@ -449,7 +456,7 @@ __global__ __launch_bounds__(kFuseThreads, KVC_FUSE_MINBLOCKS) void l2_fused(con
         else __builtin_amdgcn_s_sleep(16);
         nap = nap < 16 ? nap * 2 : 16;
     };
-    // A team has A = 1 << agg_shift aggregators (one while the team has at most 64
+    // A team has A = 1 << agg_shift aggregators (one while the team has at most 32
     // tiles): members (team + a * members / A) mod members, a = 0 .. A-1, so the roles
     // rotate over the team's workgroups from round to round.  Returns a, or -1.
     auto agg_of = [&](const TileGeo &t) -> int {
@@ -462,8 +469,8 @@ __global__ __launch_bounds__(kFuseThreads, KVC_FUSE_MINBLOCKS) void l2_fused(con
     // Aggregator a owns channels [a, a + 1) * 128 / A of the centroid.  It polls those
     // channels of the team's partials until every word is written and adds them in
     // tile order: the team's tiles fall into kMemberGroups * A member groups of `per`
-    // consecutive tiles (per <= 8, so each thread requests its whole group in one
-    // poll), a group's tiles are added in order, then the groups in order.  It divides
+    // consecutive tiles (per <= kGatherDepth, so each thread requests its whole group
+    // in one poll), a group's tiles are added in order, then the groups in order.  It divides
     // by the window's length and publishes its channels.  The wait is bounded: past
     // the limit it publishes kFailed in its channels, flags the team for the repair
     // launch and returns false.  Its channels of the centroid are left in mu_s (all of
@@ -520,10 +527,14 @@ __global__ __launch_bounds__(kFuseThreads, KVC_FUSE_MINBLOCKS) void l2_fused(con
         };
         // chunks of 8, 4, 2, 1 members: a group of 8 or of a power of two below 8 is
         // requested in one poll
-        static_assert(kGatherDepth == 8, "the chunk ladder below starts at 8");
+        static_assert(kGatherDepth == 8 || kGatherDepth == 4, "gather depth");
         int64_t m = m0;
-        for (; m + 8 <= m1 && !failed; m += 8) take(m, std::integral_constant<int, 8>());
-        if (m + 4 <= m1 && !failed) { take(m, std::integral_constant<int, 4>()); m += 4; }
+        if constexpr (kGatherDepth == 8) {
+            for (; m + 8 <= m1 && !failed; m += 8) take(m, std::integral_constant<int, 8>());
+            if (m + 4 <= m1 && !failed) { take(m, std::integral_constant<int, 4>()); m += 4; }
+        } else {
+            for (; m + 4 <= m1 && !failed; m += 4) take(m, std::integral_constant<int, 4>());
+        }
         if (m + 2 <= m1 && !failed) { take(m, std::integral_constant<int, 2>()); m += 2; }
         if (m < m1 && !failed) take(m, std::integral_constant<int, 1>());
         float *rf = &red[0][0];
@@ -827,10 +838,12 @@ FuseGeom make_fuse_geom(int64_t G, int64_t S, int64_t W, int metric = kMetricL2)
     f.members = (f.W + kFuseTile - 1) / kFuseTile;
     f.teams = G * f.nwin;
     f.tiles = f.teams * f.members;
-    // one aggregator per 64 tiles of a team, rounded up to a power of two: each
-    // gathering thread then polls at most kGatherDepth tiles, in one request
+    // one aggregator per kMemberGroups * depth tiles of a team, rounded up to a power
+    // of two: each gathering thread then polls at most `depth` tiles, in one request
+    // (a 64-tile team has 2 aggregators, a 512-tile team 8)
+    f.depth = f.members > kDeepTeam ? kGatherDepthLarge : kGatherDepthSmall;
     int sh = 0;
-    while (sh < kMaxAggShift && f.members > (static_cast<int64_t>(kMemberGroups * kGatherDepth) << sh)) ++sh;
+    while (sh < kMaxAggShift && f.members > (static_cast<int64_t>(kMemberGroups * f.depth) << sh)) ++sh;
     f.agg_shift = sh;
     f.per = (f.members + (kMemberGroups << sh) - 1) / (kMemberGroups << sh);
     f.spin_limit = kSpinLimit;
@@ -915,8 +928,9 @@ kvc_status score_windowed_impl(const uint16_t *K, int64_t G, int64_t S, int32_t 
 
     const FuseGeom f = make_fuse_geom(G, S, W, metric);
     // occupancy of the single-read kernel (both loop orders compile to the same budget)
-    const void *fused = metric == kMetricCosine ? reinterpret_cast<const void *>(&l2_fused<kMetricCosine, false>)
-                                                : reinterpret_cast<const void *>(&l2_fused<kMetricL2, false>);
+    const void *fused = metric == kMetricCosine
+                            ? reinterpret_cast<const void *>(&l2_fused<kMetricCosine, false, kGatherDepthSmall>)
+                            : reinterpret_cast<const void *>(&l2_fused<kMetricL2, false, kGatherDepthSmall>);
     static std::atomic<int64_t> capacity_by_dev[2][64];  // capacity + 1; 0: not queried yet
     int dev = 0;
     if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return KVC_ERR_HIP;
@@ -953,26 +967,23 @@ kvc_status score_windowed_impl(const uint16_t *K, int64_t G, int64_t S, int32_t 
         // per call (scoring call at 256 x 16384: 0.264 vs 0.248 ms).
         const int64_t rgrid = f.teams < kRepairGrid ? f.teams : kRepairGrid;
         const bool early = f.members >= kEarlyMembers;
+        // the teams' order (early publish or not) and gather depth pick the instance
+        auto fused_kernel = [&](auto metric_c) -> decltype(&l2_fused<kMetricL2, false, kGatherDepthSmall>) {
+            constexpr int kM = decltype(metric_c)::value;
+            if (!early) return &l2_fused<kM, false, kGatherDepthSmall>;
+            return f.depth == kGatherDepthLarge ? &l2_fused<kM, true, kGatherDepthLarge>
+                                                : &l2_fused<kM, true, kGatherDepthSmall>;
+        };
         if (metric == kMetricCosine) {
-            if (early)
-                hipLaunchKernelGGL((l2_fused<kMetricCosine, true>), dim3(static_cast<unsigned>(grid)),
-                                   dim3(kFuseThreads), 0, stream, K, fa, partial, mu_pub, repair, status, scores,
-                                   mu_user);
-            else
-                hipLaunchKernelGGL((l2_fused<kMetricCosine, false>), dim3(static_cast<unsigned>(grid)),
-                                   dim3(kFuseThreads), 0, stream, K, fa, partial, mu_pub, repair, status, scores,
-                                   mu_user);
+            hipLaunchKernelGGL(fused_kernel(std::integral_constant<int, kMetricCosine>()),
+                               dim3(static_cast<unsigned>(grid)), dim3(kFuseThreads), 0, stream, K, fa, partial,
+                               mu_pub, repair, status, scores, mu_user);
             hipLaunchKernelGGL(l2_repair<kMetricCosine>, dim3(static_cast<unsigned>(rgrid)), dim3(kFuseThreads), 0,
                                stream, K, fa, repair, status, scores, mu_user);
         } else {
-            if (early)
-                hipLaunchKernelGGL((l2_fused<kMetricL2, true>), dim3(static_cast<unsigned>(grid)),
-                                   dim3(kFuseThreads), 0, stream, K, fa, partial, mu_pub, repair, status, scores,
-                                   mu_user);
-            else
-                hipLaunchKernelGGL((l2_fused<kMetricL2, false>), dim3(static_cast<unsigned>(grid)),
-                                   dim3(kFuseThreads), 0, stream, K, fa, partial, mu_pub, repair, status, scores,
-                                   mu_user);
+            hipLaunchKernelGGL(fused_kernel(std::integral_constant<int, kMetricL2>()),
+                               dim3(static_cast<unsigned>(grid)), dim3(kFuseThreads), 0, stream, K, fa, partial,
+                               mu_pub, repair, status, scores, mu_user);
             hipLaunchKernelGGL(l2_repair<kMetricL2>, dim3(static_cast<unsigned>(rgrid)), dim3(kFuseThreads), 0,
                                stream, K, fa, repair, status, scores, mu_user);
         }
