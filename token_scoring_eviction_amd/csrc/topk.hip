@@ -349,7 +349,6 @@ __global__ __launch_bounds__(kGatherThreads) void gather_rows(
     // part of them is still in the last-level cache when the copy starts (windowed
     // step at 256 x 65536: 3.045 -> 3.005 ms; global step unchanged)
     const int64_t g = (gridDim.x / blocks_per_slice) - 1 - blockIdx.x / blocks_per_slice;
-    const int64_t r0 = (blockIdx.x % blocks_per_slice) * kGatherRows;
     const int64_t k = kg ? kg[g] : k_all;
     const int64_t base = koff ? koff[g] : g * k_all;
     const int32_t *idx = idx_all + base;
@@ -357,30 +356,41 @@ __global__ __launch_bounds__(kGatherThreads) void gather_rows(
     const int rsub = threadIdx.x >> 4;  // row of the pass
     constexpr int kPass = kGatherThreads / 16;  // rows per pass of the workgroup
     constexpr int kRows = kGatherRows / kPass;  // rows per thread
-    // all indices, then all row loads, then the stores: a thread keeps 2 kRows 16-byte
-    // loads in flight (issued one row at a time, each waited on its index and its load)
-    int64_t src[kRows], dst[kRows];
-    bool ok[kRows];
-#pragma unroll
-    for (int r = 0; r < kRows; ++r) {
-        const int64_t i = r0 + r * kPass + rsub;
-        const int64_t t = i < k ? idx[i] : -1;
-        ok[r] = t >= 0 && t < S;  // indices come from select_compact; never read outside
-        src[r] = (g * s_stride + (ok[r] ? t : 0)) * (kHeadDim / 8) + lane16;
-        dst[r] = (base + i) * (kHeadDim / 8) + lane16;
-    }
     const uint4 *Ks = reinterpret_cast<const uint4 *>(K), *Vs = reinterpret_cast<const uint4 *>(V);
-    uint4 kv[kRows], vv[kRows];
+    // Block b of a slice copies rows [4 b, 4 b + 4), then, with per-slice budgets
+    // (the grid sized for the mean budget), the blocks b + blocks_per_slice, ... that
+    // the slice's budget reaches: as many workgroups as with one budget, and none
+    // launched only to find nothing to copy (a grid sized for the largest budget left
+    // half its one-wave workgroups empty: 366.6 against 342.5 us at 256 x 16384 with
+    // budgets from 3976 to 15906 rows; block j of every slice before block j + 1
+    // instead: 0.48 ms, the copy's reads no longer walking a slice in order).
+    for (int64_t r0 = (blockIdx.x % blocks_per_slice) * kGatherRows; r0 < k;
+         r0 += blocks_per_slice * kGatherRows) {
+        // all indices, then all row loads, then the stores: a thread keeps 2 kRows
+        // 16-byte loads in flight (issued one row at a time, each waited on its index
+        // and its load)
+        int64_t src[kRows], dst[kRows];
+        bool ok[kRows];
 #pragma unroll
-    for (int r = 0; r < kRows; ++r) {
-        if (K) kv[r] = ld_stream(Ks + src[r]);
-        if (V) vv[r] = ld_stream(Vs + src[r]);
-    }
+        for (int r = 0; r < kRows; ++r) {
+            const int64_t i = r0 + r * kPass + rsub;
+            const int64_t t = i < k ? idx[i] : -1;
+            ok[r] = t >= 0 && t < S;  // indices come from select_compact; never read outside
+            src[r] = (g * s_stride + (ok[r] ? t : 0)) * (kHeadDim / 8) + lane16;
+            dst[r] = (base + i) * (kHeadDim / 8) + lane16;
+        }
+        uint4 kv[kRows], vv[kRows];
 #pragma unroll
-    for (int r = 0; r < kRows; ++r) {
-        if (!ok[r]) continue;
-        if (K) st_stream(reinterpret_cast<uint4 *>(K_out) + dst[r], kv[r]);
-        if (V) st_stream(reinterpret_cast<uint4 *>(V_out) + dst[r], vv[r]);
+        for (int r = 0; r < kRows; ++r) {
+            if (K) kv[r] = ld_stream(Ks + src[r]);
+            if (V) vv[r] = ld_stream(Vs + src[r]);
+        }
+#pragma unroll
+        for (int r = 0; r < kRows; ++r) {
+            if (!ok[r]) continue;
+            if (K) st_stream(reinterpret_cast<uint4 *>(K_out) + dst[r], kv[r]);
+            if (V) st_stream(reinterpret_cast<uint4 *>(V_out) + dst[r], vv[r]);
+        }
     }
 }
 
@@ -560,7 +570,11 @@ extern "C" kvc_status kvc_topk_compact_ragged(const float *scores, int64_t G, in
     launch_select(G, S, stream, scores, s_stride, int64_t{0}, kg, koff, idx_out, nullptr, nullptr, nullptr,
                   nullptr);
     if (K || V) {
-        const int64_t bps = (k_max + kGatherRows - 1) / kGatherRows;
+        // blocks for the mean budget (the packed outputs hold k_total rows); a slice
+        // with more rows loops over its further blocks
+        const int64_t mean = (k_total + G - 1) / G;
+        const int64_t rows = mean < k_max ? mean : k_max;
+        const int64_t bps = (rows + kGatherRows - 1) / kGatherRows;
         if (G * bps > INT32_MAX) return KVC_ERR_UNSUPPORTED;
         hipLaunchKernelGGL(gather_rows, dim3(static_cast<unsigned>(G * bps)), dim3(kGatherThreads), 0,
                            stream, K, V, S, s_stride, idx_out, int64_t{0}, kg, koff, bps, K_out, V_out);
