@@ -335,3 +335,41 @@ def test_topk_ranks_nan_scores_below_every_number(gpu_lib):
     assert not torch.gather(nan, 1, idx.long()).any()
     fin = torch.where(nan, torch.full_like(s, -1.0), s).cpu().numpy()  # the scores are >= 0
     np.testing.assert_array_equal(idx.cpu().numpy(), oracle.topk(fin, k))
+
+
+def test_random_team_sizes_single_read_matches_three_launch_and_repair(gpu_lib, kvc_option):
+    # 30 seeded shapes whose teams (slices or windows) have 33 to 700 tiles and often a
+    # ragged last tile, global and windowed, L2 and cosine: the single-read kernel agrees
+    # with the three-launch path (rel 1e-4) and, on the smaller ones, with the oracle;
+    # a run whose every centroid wait gives up is repaired to the same bits
+    rng = np.random.default_rng(2024)
+    for _ in range(30):
+        M = int(rng.choice([33, 40, 63, 65, 97, 129, 200, 257, 300, 385, 513, 700]))
+        if rng.random() < 0.4:
+            W = M * 256 - int(rng.integers(0, 255))
+            S = int(W * rng.uniform(1.0, 3.5))
+        else:
+            S, W = M * 256 - int(rng.integers(0, 255)), None
+        G = int(rng.integers(1, max(1, min(12, 1_500_000 // S)) + 1))
+        metric = "cosine" if rng.random() < 0.3 else "l2"
+        K, _, _ = synth.manifold_global(1, 1, G, S, planted=4, seed=int(rng.integers(1 << 30)), device=DEV)
+        nwin = 1 if W is None else -(-S // W)
+
+        def score(path, spin=-1):
+            kvc_option("score_path", path)
+            kvc_option("score_spin_limit", spin)
+            mu = torch.empty((G, nwin, 128), dtype=torch.float32, device=DEV)
+            return gpu_lib.kvc_score_centroid(K, W=W, metric=metric, centroids=mu).clone(), mu
+
+        f, fmu = score(1)
+        r, rmu = score(1, 0)
+        u, _ = score(2)
+        kvc_option("score_spin_limit", -1)
+        torch.cuda.synchronize()
+        case = (G, S, W, metric)
+        assert not torch.isnan(f).any(), case
+        assert torch.equal(f, r) and torch.equal(fmu, rmu), case
+        rel = ((f - u).abs() / u.abs().clamp_min(1e-6)).max().item()
+        assert rel < 1e-4, (rel, case)
+        if metric == "l2" and G * S <= 400_000:
+            _scores_vs_oracle(K, f, W)
