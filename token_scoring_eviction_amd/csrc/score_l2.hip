@@ -564,14 +564,33 @@ __global__ __launch_bounds__(kFuseThreads, KVC_FUSE_MINBLOCKS) void l2_fused(con
     // Column sums of the tile -> the tile's partial words (32-bit coherent stores,
     // nothing waited for).  A team's aggregator then gathers its channels of the
     // centroid, while it holds only this tile.
+    // Cosine metric with the small teams' order: the tile's ||k||^2 of row lane16 (its
+    // 16 rows by one transpose-reduce) is formed in publish, which runs in the shadow of
+    // the next centroid wait, and carried with the tile to its scoring (windowed
+    // scoring call at 256 x 65536, W 4096: 1.082 -> 0.993 ms).  In the early-publish
+    // order the carried value costs more register spills than it saves (256 x 16384:
+    // 0.297 -> 0.307 ms), so the scoring forms it there.
+    constexpr bool kNorms = kMetric == kMetricCosine && kFuseRows == 16 && !kEarly;
+    float kk_pub = 0.f;
     auto publish = [&](int64_t tile, const TileGeo &t, const uint4 *v) {
         float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        float part[kFuseRows];  // cosine: each row's lane part of ||k||^2 (lane_kk's sum)
 #pragma unroll
         for (int r = 0; r < kFuseRows; ++r) {
             float x[8];
             widen8(v[r], x);
 #pragma unroll
             for (int j = 0; j < 8; ++j) acc[j] += x[j];
+            if constexpr (kNorms) {
+                float kk = 0.f;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) kk += x[j] * x[j];
+                part[r] = kk;
+            }
+        }
+        if constexpr (kNorms) {
+            row_transpose_reduce<kFuseRows>(part, lane16);
+            kk_pub = part[0];
         }
 #pragma unroll
         for (int j = 0; j < 8; ++j) red[rowg][lane16 * 8 + j] = acc[j];
@@ -618,24 +637,27 @@ __global__ __launch_bounds__(kFuseThreads, KVC_FUSE_MINBLOCKS) void l2_fused(con
     // Scores tile `t` (held in v) once its team's centroid is published.  Without a
     // centroid (a wait that gave up: the team is flagged) the tile's scores are
     // written as quiet NaN, which the repair launch then overwrites.
-    auto score_tile = [&](const TileGeo &t, const uint4 *v, bool ok) {
+    auto score_tile = [&](const TileGeo &t, const uint4 *v, bool ok, float kk_row) {
         const float nan = __int_as_float(0x7fc00000);
         float m[8];
 #pragma unroll
         for (int j = 0; j < 8; ++j) m[j] = mu_s[lane16 * 8 + j];
         if (kMetric == kMetricCosine && kFuseRows == 16) {
-            // The 16 rows' ||k||^2 by one transpose-reduce (lane r holds row r's),
-            // 1 / ||k|| formed once per row in its lane and broadcast to the row
-            // group, then the 16 rows' ||k/||k|| - mu/||mu||||^2 by a second
-            // transpose-reduce.  The same pairings and per-row arithmetic as row_cos:
-            // the same bits.
+            // The 16 rows' ||k||^2 by one transpose-reduce (lane r holds row r's;
+            // formed in publish when kNorms), 1 / ||k|| formed once per row in its
+            // lane and broadcast to the row group, then the 16 rows'
+            // ||k/||k|| - mu/||mu||||^2 by a second transpose-reduce.  The same
+            // pairings and per-row arithmetic as row_cos: the same bits.
             float mm, inv_m;
             centroid_norm(m, mm, inv_m);
             float part[kFuseRows];
+            float kk = kk_row;
+            if constexpr (!kNorms) {
 #pragma unroll
-            for (int r = 0; r < kFuseRows; ++r) part[r] = lane_kk(v[r]);
-            row_transpose_reduce<kFuseRows>(part, lane16);
-            const float kk = part[0];
+                for (int r = 0; r < kFuseRows; ++r) part[r] = lane_kk(v[r]);
+                row_transpose_reduce<kFuseRows>(part, lane16);
+                kk = part[0];
+            }
             const float inv_mine = inv_norm(kk);
             for_rows<0, kFuseRows>([&](auto rc) {
                 constexpr int r = decltype(rc)::value;
@@ -686,10 +708,12 @@ __global__ __launch_bounds__(kFuseThreads, KVC_FUSE_MINBLOCKS) void l2_fused(con
         // (scoring call at 256 x 16384: 0.248 -> 0.239 ms; with 16-tile teams,
         // 256 x 65536 in 4096-token windows, 0.893 -> 0.934 ms, so smaller teams
         // keep the order below).
+        float kk_cur = 0.f;  // the current tile's row norms (cosine)
         if (tile < geo.tiles) {
             const TileGeo t = geo_of(tile);
             load_tile(t, v);
             publish(tile, t, v);
+            kk_cur = kk_pub;
             const int a = agg_of(t);
             if (a >= 0) agg_ok = gather_mu(t, a);
         }
@@ -703,13 +727,14 @@ __global__ __launch_bounds__(kFuseThreads, KVC_FUSE_MINBLOCKS) void l2_fused(con
                 publish(next, tn, vn);
             }
             const bool ok = fetch_mu(t);
-            score_tile(t, v, ok);
+            score_tile(t, v, ok, kk_cur);
             if (next < geo.tiles) {
                 const int a = agg_of(tn);
                 if (a >= 0) agg_ok = gather_mu(tn, a);
             }
 #pragma unroll
             for (int r = 0; r < kFuseRows; ++r) v[r] = vn[r];
+            kk_cur = kk_pub;
         }
     } else {
         // While tile `tile` waits for its team's centroid and is scored, every load of
@@ -717,10 +742,12 @@ __global__ __launch_bounds__(kFuseThreads, KVC_FUSE_MINBLOCKS) void l2_fused(con
         // (the aggregator gathers in publish).  Requesting half of the next tile
         // before the wait and half after it: 0.273 vs 0.267 ms per scoring call at
         // 256 x 16384.
+        float kk_cur = 0.f;  // the current tile's row norms (cosine)
         if (tile < geo.tiles) {
             const TileGeo t = geo_of(tile);
             load_tile(t, v);
             publish(tile, t, v);
+            kk_cur = kk_pub;
         }
         for (; tile < geo.tiles; tile += step) {
             const TileGeo t = geo_of(tile);
@@ -731,10 +758,11 @@ __global__ __launch_bounds__(kFuseThreads, KVC_FUSE_MINBLOCKS) void l2_fused(con
                 load_tile(tn, vn);
             }
             const bool ok = fetch_mu(t);
-            score_tile(t, v, ok);
+            score_tile(t, v, ok, kk_cur);
             if (next < geo.tiles) publish(next, tn, vn);
 #pragma unroll
             for (int r = 0; r < kFuseRows; ++r) v[r] = vn[r];
+            kk_cur = kk_pub;
         }
     }
 }
