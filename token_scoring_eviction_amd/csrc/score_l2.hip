@@ -564,13 +564,16 @@ __global__ __launch_bounds__(kFuseThreads, KVC_FUSE_MINBLOCKS) void l2_fused(con
     // Column sums of the tile -> the tile's partial words (32-bit coherent stores,
     // nothing waited for).  A team's aggregator then gathers its channels of the
     // centroid, while it holds only this tile.
-    // Cosine metric with the small teams' order: the tile's ||k||^2 of row lane16 (its
-    // 16 rows by one transpose-reduce) is formed in publish, which runs in the shadow of
-    // the next centroid wait, and carried with the tile to its scoring (windowed
-    // scoring call at 256 x 65536, W 4096: 1.082 -> 0.993 ms).  In the early-publish
-    // order the carried value costs more register spills than it saves (256 x 16384:
-    // 0.297 -> 0.307 ms), so the scoring forms it there.
+    // Cosine metric: the tile's ||k||^2 of row lane16 (its 16 rows by one
+    // transpose-reduce) is formed before the tile's centroid arrives and carried with
+    // the tile to its scoring.  With the small teams' order it is formed in publish, in
+    // the shadow of the next centroid wait (windowed scoring call at 256 x 65536, W
+    // 4096: 1.082 -> 0.993 ms).  In the early-publish order publish runs while two
+    // tiles are held (formed there: 0.297 -> 0.307 ms, more spills), so it is formed at
+    // the end of the iteration, when only the next tile is held (256 x 16384: 0.293 ->
+    // 0.276 ms, 25 -> 8 registers spilled).
     constexpr bool kNorms = kMetric == kMetricCosine && kFuseRows == 16 && !kEarly;
+    constexpr bool kNormsEnd = kMetric == kMetricCosine && kFuseRows == 16 && kEarly;
     float kk_pub = 0.f;
     auto publish = [&](int64_t tile, const TileGeo &t, const uint4 *v) {
         float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
@@ -644,15 +647,15 @@ __global__ __launch_bounds__(kFuseThreads, KVC_FUSE_MINBLOCKS) void l2_fused(con
         for (int j = 0; j < 8; ++j) m[j] = mu_s[lane16 * 8 + j];
         if (kMetric == kMetricCosine && kFuseRows == 16) {
             // The 16 rows' ||k||^2 by one transpose-reduce (lane r holds row r's;
-            // formed in publish when kNorms), 1 / ||k|| formed once per row in its
-            // lane and broadcast to the row group, then the 16 rows'
-            // ||k/||k|| - mu/||mu||||^2 by a second transpose-reduce.  The same
-            // pairings and per-row arithmetic as row_cos: the same bits.
+            // formed before the centroid wait and carried in kk_row), 1 / ||k||
+            // formed once per row in its lane and broadcast to the row group, then
+            // the 16 rows' ||k/||k|| - mu/||mu||||^2 by a second transpose-reduce.
+            // The same pairings and per-row arithmetic as row_cos: the same bits.
             float mm, inv_m;
             centroid_norm(m, mm, inv_m);
             float part[kFuseRows];
             float kk = kk_row;
-            if constexpr (!kNorms) {
+            if constexpr (!kNorms && !kNormsEnd) {
 #pragma unroll
                 for (int r = 0; r < kFuseRows; ++r) part[r] = lane_kk(v[r]);
                 row_transpose_reduce<kFuseRows>(part, lane16);
@@ -709,11 +712,19 @@ __global__ __launch_bounds__(kFuseThreads, KVC_FUSE_MINBLOCKS) void l2_fused(con
         // 256 x 65536 in 4096-token windows, 0.893 -> 0.934 ms, so smaller teams
         // keep the order below).
         float kk_cur = 0.f;  // the current tile's row norms (cosine)
+        auto norms_of = [&](const uint4 *w) -> float {
+            float part[kFuseRows];
+#pragma unroll
+            for (int r = 0; r < kFuseRows; ++r) part[r] = lane_kk(w[r]);
+            row_transpose_reduce<kFuseRows>(part, lane16);
+            return part[0];
+        };
         if (tile < geo.tiles) {
             const TileGeo t = geo_of(tile);
             load_tile(t, v);
             publish(tile, t, v);
             kk_cur = kk_pub;
+            if constexpr (kNormsEnd) kk_cur = norms_of(v);
             const int a = agg_of(t);
             if (a >= 0) agg_ok = gather_mu(t, a);
         }
@@ -735,6 +746,8 @@ __global__ __launch_bounds__(kFuseThreads, KVC_FUSE_MINBLOCKS) void l2_fused(con
 #pragma unroll
             for (int r = 0; r < kFuseRows; ++r) v[r] = vn[r];
             kk_cur = kk_pub;
+            if constexpr (kNormsEnd)
+                if (next < geo.tiles) kk_cur = norms_of(v);
         }
     } else {
         // While tile `tile` waits for its team's centroid and is scored, every load of
