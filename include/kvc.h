@@ -210,7 +210,8 @@ kvc_status kvc_score_centroid_noalloc(const uint16_t *K, int64_t G, int64_t S, i
  *   scores: fp32, slice stride s_stride floats (s_stride >= S)
  *   K, V:   bf16, slice stride s_stride rows of D, or NULL
  *   idx_out: int32 [G][k];  K_out, V_out: bf16 [G][k][D] (NULL iff K / V NULL)
- * 0 <= k <= S. */
+ * 0 <= k <= S.  With k == 0 (or G == 0) nothing is written and every output may
+ * be NULL. */
 kvc_status kvc_topk_compact(const float *scores, int64_t G, int64_t S, int64_t s_stride, int64_t k,
                             const uint16_t *K, const uint16_t *V, int32_t D, int32_t *idx_out,
                             uint16_t *K_out, uint16_t *V_out, void *ws, size_t ws_bytes,
@@ -237,7 +238,8 @@ kvc_status kvc_layer_budgets(const double *sensitivity, int64_t L, double r, dou
  * and its rows K_out[o_g + i][:] (likewise V_out).
  *   k_max:   host bound on every budget, 0 <= k_max <= S (sizes the row copy)
  *   k_total: capacity of the packed outputs in rows: idx_out int32 [k_total],
- *            K_out, V_out bf16 [k_total][D]
+ *            K_out, V_out bf16 [k_total][D] (any of them may be NULL when
+ *            k_total == 0: no row is written)
  * The budgets are checked on the device: a slice whose budget is negative or
  * above k_max, or whose rows would end past k_total, keeps nothing, no output
  * is written outside [0, k_total), and kvc_workspace_status on this workspace

@@ -56,6 +56,7 @@ def test_topk_entry_points(lib):
     assert f(A, 2, 100, 100, 10, C, NULL, 128, B, NULL, NULL, NULL, 0, NULL) == INV     # K without K_out
     assert f(A, 2, 100, 100, 10, C, NULL, 64, B, D_, NULL, NULL, 0, NULL) == UNS        # D != 128
     assert f(A, 2, 100, 100, 0, NULL, NULL, 128, B, NULL, NULL, NULL, 0, NULL) == OK    # k = 0
+    assert f(A, 2, 100, 100, 0, C, C, 128, B, NULL, NULL, NULL, 0, NULL) == OK          # k = 0: no row outputs needed
     assert f(A, 0, 100, 100, 10, NULL, NULL, 128, B, NULL, NULL, NULL, 0, NULL) == OK   # G = 0
     assert f(NULL, 2, 100, 100, 10, NULL, NULL, 128, B, NULL, NULL, NULL, 0, NULL) == INV
     assert f(A, 2, 100, 100, 10, P(0x100008), NULL, 128, B, D_, NULL, NULL, 0, NULL) == INV  # K misaligned

@@ -63,6 +63,20 @@ def test_ragged_zero_full_and_large_budgets(gpu_lib):
     assert torch.equal(idx, idx2)
 
 
+def test_empty_selections_with_rows_given(gpu_lib):
+    # nothing to keep (k = 0, or every budget 0): the empty outputs the binding passes
+    # have no storage, and the calls succeed without writing anything
+    G, S = 5, 700
+    s = synth.random_scores(G, S, seed=31, device=DEV)
+    K = torch.zeros((G, S, 128), dtype=torch.bfloat16, device=DEV)
+    idx, Ko, Vo = gpu_lib.kvc_topk_compact(s, 0, K, K)
+    assert idx.numel() == 0 and Ko.numel() == 0 and Vo.numel() == 0
+    idx, Ko, Vo = gpu_lib.kvc_topk_compact_ragged(s, [0] * G, K, K)
+    torch.cuda.synchronize()
+    gpu_lib.kvc_workspace_status()
+    assert idx.numel() == 0 and Ko.numel() == 0 and Vo.numel() == 0
+
+
 def test_ragged_with_uniform_budgets_equals_topk(gpu_lib):
     G, S, k = 40, 3000, 777
     s = synth.random_scores(G, S, seed=24, device="cpu").to(DEV)

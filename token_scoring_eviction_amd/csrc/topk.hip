@@ -508,11 +508,11 @@ extern "C" kvc_status kvc_topk_compact(const float *scores, int64_t G, int64_t S
     (void)ws;
     (void)ws_bytes;
     if (G < 0 || S < 0 || k < 0 || k > S || s_stride < S) return KVC_ERR_INVALID_ARGUMENT;
+    if (G == 0 || k == 0) return KVC_OK;  // nothing to write: the outputs may be NULL
     if ((K == nullptr) != (K_out == nullptr) || (V == nullptr) != (V_out == nullptr))
         return KVC_ERR_INVALID_ARGUMENT;
     if ((K || V) && D != kHeadDim) return D <= 0 ? KVC_ERR_INVALID_ARGUMENT : KVC_ERR_UNSUPPORTED;
     if (S > INT32_MAX || G > INT32_MAX) return KVC_ERR_UNSUPPORTED;
-    if (G == 0 || k == 0) return KVC_OK;
     if (!scores || !idx_out || !aligned(scores, 4) || !aligned(idx_out, 4))
         return KVC_ERR_INVALID_ARGUMENT;
     if ((K && (!aligned(K, 16) || !aligned(K_out, 16))) || (V && (!aligned(V, 16) || !aligned(V_out, 16))))
@@ -544,16 +544,18 @@ extern "C" kvc_status kvc_topk_compact_ragged(const float *scores, int64_t G, in
     using namespace kvc;
     if (G < 0 || S < 0 || s_stride < S || k_max < 0 || k_max > S || k_total < 0)
         return KVC_ERR_INVALID_ARGUMENT;
-    if ((K == nullptr) != (K_out == nullptr) || (V == nullptr) != (V_out == nullptr))
+    // with k_total == 0 no row is written: the row outputs may then be NULL
+    if (k_total > 0 && ((K == nullptr) != (K_out == nullptr) || (V == nullptr) != (V_out == nullptr)))
         return KVC_ERR_INVALID_ARGUMENT;
-    if ((K || V) && D != kHeadDim) return D <= 0 ? KVC_ERR_INVALID_ARGUMENT : KVC_ERR_UNSUPPORTED;
+    if (k_total > 0 && (K || V) && D != kHeadDim) return D <= 0 ? KVC_ERR_INVALID_ARGUMENT : KVC_ERR_UNSUPPORTED;
     if (S > INT32_MAX || G > INT32_MAX) return KVC_ERR_UNSUPPORTED;
     if (G == 0) return KVC_OK;
     if (!k || !aligned(k, 8) || !ws || !aligned(ws, kWsAlign)) return KVC_ERR_INVALID_ARGUMENT;
     if (ws_bytes < topk_ragged_workspace_bytes(G)) return KVC_ERR_WORKSPACE_TOO_SMALL;
     if (k_total > 0 && (!scores || !idx_out || !aligned(scores, 4) || !aligned(idx_out, 4)))
         return KVC_ERR_INVALID_ARGUMENT;
-    if ((K && (!aligned(K, 16) || !aligned(K_out, 16))) || (V && (!aligned(V, 16) || !aligned(V_out, 16))))
+    if (k_total > 0 &&
+        ((K && (!aligned(K, 16) || !aligned(K_out, 16))) || (V && (!aligned(V, 16) || !aligned(V_out, 16)))))
         return KVC_ERR_INVALID_ARGUMENT;
     WsCursor cur(ws);
     uint32_t *status = cur.take<uint32_t>(kStatusBytes / 4);
