@@ -192,3 +192,42 @@ def test_compress_determinism(gpu_lib):
     torch.cuda.synchronize()
     for x, y in zip(a, b):
         assert torch.equal(x, y)
+
+
+def test_random_shapes_compress_and_fused_rebuild(gpu_lib):
+    # 20 seeded shapes: ranks 32-128, 1-2 KV heads with 1, 2 or 4 query heads each, 1-32
+    # window queries, odd lengths and strided caches, the fused reconstruction at ranks
+    # <= 64 on about half -- K~, V~, e_t (and K^, V^) against the oracle
+    rng = np.random.default_rng(77)
+    for _ in range(20):
+        R = int(rng.choice([32, 64, 96, 128]))
+        Hkv, grp = int(rng.integers(1, 3)), int(rng.choice([1, 2, 4]))
+        L, B = int(rng.integers(1, 3)), int(rng.integers(1, 3))
+        S = int(rng.integers(1, 1500))
+        Wq = int(rng.integers(1, 33))
+        fused = R <= 64 and rng.random() < 0.5
+        inp = synth.oja_inputs(L, B, Hkv, Hkv * grp, S, R=R, Wq=Wq, S_cap=S + int(rng.integers(0, 40)),
+                               seed=int(rng.integers(1 << 30)), device=DEV)
+        if fused:
+            Kt, Vt, err, Kh, Vh = gpu_lib.kvc_lowrank_compress_reconstruct(inp.K, inp.V, inp.Q, inp.Uk, inp.Uv,
+                                                                           L, B, Hkv, S=S)
+        else:
+            Kt, Vt, err = gpu_lib.kvc_lowrank_compress(inp.K, inp.V, inp.Q, inp.Uk, inp.Uv, L, B, Hkv, S=S)
+        torch.cuda.synchronize()
+        Uk, Uv = inp.Uk.cpu().numpy(), inp.Uv.cpu().numpy()
+        case = (R, Hkv, grp, L, B, S, Wq, fused)
+        for g in range(L * B * Hkv):
+            l, b, h = g // (B * Hkv), (g // Hkv) % B, g % Hkv
+            Q = synth.bf16_bits(inp.Q[l:l + 1, b:b + 1, h * grp:(h + 1) * grp])
+            okt, ovt, oerr = oracle.lowrank_compress(synth.bf16_bits(inp.K[g:g + 1, :S]),
+                                                     synth.bf16_bits(inp.V[g:g + 1, :S]), Q,
+                                                     Uk[l:l + 1, h:h + 1], Uv[l:l + 1, h:h + 1], 1, 1, 1, grp)
+            pairs = [(Kt, okt), (Vt, ovt)]
+            if fused:
+                pairs += [(Kh, oracle.reconstruct(okt, Uk[l:l + 1, h:h + 1], None, None, 1, 1, 1)),
+                          (Vh, oracle.reconstruct(ovt, Uv[l:l + 1, h:h + 1], None, None, 1, 1, 1))]
+            for gpu, ora in pairs:
+                ok, rel = lowrank_close(gpu[g:g + 1, :S].cpu().numpy(), ora)
+                assert ok, (rel, g, case)
+            ok, rel, nbad = score_close(err[g:g + 1, :S].cpu().numpy(), oerr)
+            assert ok, (rel, nbad, g, case)
