@@ -355,9 +355,15 @@ __global__ __launch_bounds__(HB == 1 ? 1024 : 512) void project_kernel(
     constexpr int KS = R / 16;  // reconstruction k-steps
     constexpr int TOK = 32 * HB;
 #ifndef KVC_FUSED_LATE_PREFETCH
-#define KVC_FUSED_LATE_PREFETCH 1
+#define KVC_FUSED_LATE_PREFETCH 0
 #endif
-    constexpr bool kLatePrefetch = kRebuild && KVC_FUSED_LATE_PREFETCH;
+    // The fused kernel's next keys: requested at the start of a step for fp32 storage
+    // (256 VGPRs, 2 spilled; the loop's fused pass at S = 131072, five A/B pairs on two
+    // boxes: 13.30-14.20 against 13.63-14.10 ms, mean 13.67 against 14.00, the early
+    // request faster in four; requested after the projection it needs 194 VGPRs),
+    // after the projection for bf16 storage (requested early its variants spill 11
+    // and 26).  The same bits either way.
+    constexpr bool kLatePrefetch = kRebuild && (kBf16 || KVC_FUSED_LATE_PREFETCH);
     extern __shared__ u32x4 lds[];
     u32x4 *ufr = lds;
     u32x4 *rfr = lds + NRB * 16 * 64;                            // reconstruction fragments
