@@ -413,7 +413,11 @@ def run_loop_config(args, dev):
             times.append((e, upd))
         return st
 
+    # each loop allocates the hybrid state (about 70 GB at this size) in its prefill; the
+    # previous loop's state is released first, so the caching allocator hands back the same
+    # blocks instead of mapping new memory inside the timed region
     for _ in range(max(1, args.warmup // 5)):
+        st = None
         st = loop()
     torch.cuda.synchronize()
     reps = max(1, args.steps // 25)
@@ -421,8 +425,10 @@ def run_loop_config(args, dev):
     t0 = torch.cuda.Event(enable_timing=True)
     t1 = torch.cuda.Event(enable_timing=True)
     recording[0] = True
+    st = None
     t0.record()
     for _ in range(reps):
+        st = None
         st = loop(times)
     t1.record()
     torch.cuda.synchronize()
